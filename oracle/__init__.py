@@ -1,0 +1,154 @@
+"""CPU oracle for the WFST Viterbi beam search -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package. The decoder (``wfst_beam_search_amd``) never does,
+and the two share no code: this binding loads ``wfst_oracle.c`` (plain C, built
+with gcc) and nothing else.
+
+The oracle is a single-threaded token-passing search written from the page
+"GPU WFST Beam-Search Decoder", sections 1, 3, 5.3 and 5.5 (see the C file's
+header for the readings it takes). Every function below is argument marshalling.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wfst_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libwfst_oracle.so")
+
+FIELDS = ("n", "beam", "max", "cutoff", "arcs", "admitted", "distinct", "eps_arcs",
+          "eps_admitted", "eps_distinct", "eps_new", "eps_replaced", "eps_passes",
+          "n_next", "phase", "_pad")
+NFIELDS = 16
+PHASE_REAL, PHASE_FINAL, PHASE_REDIRECT, PHASE_DEAD = 0, 1, 2, 3
+
+
+class _Graph(ctypes.Structure):
+    _fields_ = [("num_states", ctypes.c_int32), ("num_arcs", ctypes.c_int32),
+                ("start", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("epsilon_id", ctypes.c_int32),
+                ("row_splits", ctypes.c_void_p), ("dest", ctypes.c_void_p),
+                ("ilabel", ctypes.c_void_p), ("olabel", ctypes.c_void_p),
+                ("weight", ctypes.c_void_p)]
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("beam", ctypes.c_float), ("min_active", ctypes.c_int32),
+                ("max_active", ctypes.c_int32), ("allow_partial", ctypes.c_int32),
+                ("eps_iterations", ctypes.c_int32)]
+
+
+class _Result(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_float), ("reached_final", ctypes.c_int32),
+                ("dead", ctypes.c_int32), ("n_arcs", ctypes.c_int32),
+                ("n_words", ctypes.c_int32), ("n_steps", ctypes.c_int32),
+                ("log_entries", ctypes.c_int64), ("start_closure", ctypes.c_int64 * 8)]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (binary32 arithmetic, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def _load():
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            lib.wo_decode.restype = ctypes.c_int
+            lib.wo_decode.argtypes = [ctypes.POINTER(_Graph), ctypes.POINTER(_Config),
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.POINTER(_Result)]
+            _lib = lib
+    return _lib
+
+
+class OracleGraph:
+    """Holds contiguous copies of a graph's arrays for the oracle."""
+
+    def __init__(self, g):
+        self.rs = np.ascontiguousarray(g.row_splits, dtype=np.int32)
+        self.dest = np.ascontiguousarray(g.dest, dtype=np.int32)
+        self.il = np.ascontiguousarray(g.ilabel, dtype=np.int32)
+        self.ol = np.ascontiguousarray(g.olabel, dtype=np.int32)
+        self.w = np.ascontiguousarray(g.weight, dtype=np.float32)
+        self.num_states = int(g.num_states)
+        self.num_arcs = int(self.dest.shape[0])
+        self.c = _Graph(self.num_states, self.num_arcs, int(g.start), int(g.vocab),
+                        int(g.epsilon_id), self.rs.ctypes.data, self.dest.ctypes.data,
+                        self.il.ctypes.data, self.ol.ctypes.data, self.w.ctypes.data)
+
+
+def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active: int,
+                min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0):
+    """Decode one utterance. ``lp_lane`` is [T, V] (float32, or float16 widened exactly).
+
+    Returns a dict: score (float32), reached_final, dead, arcs, words (int32 arrays),
+    steps (int64 [n_steps, 16], fields ``FIELDS``), start_closure, log_entries.
+    """
+    lib = _load()
+    og = graph if isinstance(graph, OracleGraph) else OracleGraph(graph)
+    lp = np.ascontiguousarray(lp_lane, dtype=np.float32)    # f16 -> f32 is exact
+    if lp.ndim != 2:
+        raise ValueError("lp_lane must be [T, V]")
+    length = int(length)
+    if length < 0 or length > lp.shape[0]:
+        raise ValueError("length outside [0, T]")
+    cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
+                  int(eps_iterations))
+    arcs_cap = (length + 2) * (1 + max(0, int(eps_iterations))) + 8
+    steps_cap = length + 2
+    arcs = np.zeros(arcs_cap, dtype=np.int32)
+    words = np.zeros(arcs_cap, dtype=np.int32)
+    steps = np.zeros((steps_cap, NFIELDS), dtype=np.int64)
+    res = _Result()
+    rc = lib.wo_decode(ctypes.byref(og.c), ctypes.byref(cfg), lp.ctypes.data if lp.size else None,
+                       length, int(lp.shape[1]), arcs.ctypes.data, arcs_cap, words.ctypes.data,
+                       arcs_cap, steps.ctypes.data, steps_cap, ctypes.byref(res))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed (rc={rc})")
+    if res.n_arcs > arcs_cap or res.n_steps > steps_cap:
+        raise RuntimeError("oracle output larger than its buffers")
+    return dict(score=np.float32(res.score), reached_final=int(res.reached_final),
+                dead=int(res.dead), arcs=arcs[:res.n_arcs].copy(),
+                words=words[:res.n_words].copy(), steps=steps[:res.n_steps].copy(),
+                start_closure=np.array(res.start_closure[:], dtype=np.int64),
+                log_entries=int(res.log_entries))
+
+
+def decode_batch(graph, lp: np.ndarray, lengths, beam: float, max_active: int,
+                 min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0,
+                 lanes=None, threads: int = 1):
+    """Decode lanes of a batch independently (each lane on one thread of a pool)."""
+    og = graph if isinstance(graph, OracleGraph) else OracleGraph(graph)
+    lanes = list(range(lp.shape[0])) if lanes is None else list(lanes)
+
+    def one(b):
+        return decode_lane(og, lp[b], int(lengths[b]), beam, max_active, min_active,
+                           allow_partial, eps_iterations)
+
+    if threads <= 1:
+        return [one(b) for b in lanes]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(one, lanes))

@@ -1,0 +1,282 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+* hand-traced golden cases (tests/golden/*.json, each citing its passage);
+* the exact Viterbi score of a full trellis DP and exhaustive path enumeration on
+  tiny graphs at infinite beam (the beam search reduces to them exactly);
+* closed forms: greedy CTC on a one-state graph (numpy argmax / running sum) and
+  forced alignment on a linear chain;
+* invariants of every returned path on the five workloads.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from bruteforce import enumerate_paths, viterbi_exact
+from cases import check_path, f32_value, graph_from_states, load_golden
+
+F32 = np.float32
+IDX = {name: i for i, name in enumerate(oracle.FIELDS)}
+
+
+def _bits(x):
+    return int(np.array(F32(x)).view(np.uint32))
+
+
+def _decode(g, lp, T, beam, max_active, min_active=0, allow_partial=False, eps=0):
+    return oracle.decode_lane(g, lp, T, beam, max_active, min_active, allow_partial, eps)
+
+
+def _const_lp(frames, vocab, value):
+    return np.full((frames, vocab), value, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- golden cases
+
+@pytest.mark.parametrize("case", load_golden("beam_schedule.json")["cases"], ids=lambda c: c["name"])
+def test_golden_beam_schedule(case):
+    spec = load_golden("beam_schedule.json")["graphs"][case["graph"]]
+    g = graph_from_states(spec)
+    lp = _const_lp(case["frames"], g.vocab, case["lp_value"])
+    r = _decode(g, lp, case["frames"], case["beam"], case["max_active"], case["min_active"])
+    st = r["steps"]
+    assert list(st[:, IDX["n"]]) == case["expect_n"]
+    assert [hex(int(x)) for x in st[:, IDX["beam"]]] == case["expect_beam_hex"]
+    got_max = np.array(st[:, IDX["max"]], dtype=np.uint32).view(np.float32)
+    assert list(got_max) == [F32(x) for x in case["expect_max"]]
+    assert list(r["arcs"]) == case["expect_arcs"]
+    assert r["score"] == F32(case["expect_score"])
+    assert r["reached_final"] == 1
+
+
+def test_golden_tie_chain():
+    case = load_golden("tie_chain.json")
+    g = graph_from_states(case["graph"])
+    lp = _const_lp(case["frames"], g.vocab, case["lp_value"])
+    r = _decode(g, lp, case["frames"], case["beam"], case["max_active"], case["min_active"])
+    assert list(r["arcs"]) == case["expect_arcs"]
+    assert list(r["words"]) == case["expect_words"]
+    assert r["score"] == F32(case["expect_score"])
+    assert r["reached_final"] == case["expect_reached_final"]
+
+
+def test_golden_eps_closure():
+    case = load_golden("eps_closure.json")
+    g = graph_from_states(case["graph"])
+    lp = np.array(case["lp_rows"], dtype=np.float32)
+    r = _decode(g, lp, case["frames"], case["beam"], case["max_active"], case["min_active"],
+                eps=case["eps_iterations"])
+    assert list(r["arcs"]) == case["expect_arcs"]
+    assert list(r["words"]) == case["expect_words"]
+    assert r["score"] == F32(case["expect_score"])
+    sc = case["expect_start_closure"]
+    assert list(r["start_closure"][:7]) == [sc["eps_arcs"], sc["admitted"], sc["distinct"], sc["new"],
+                                            sc["replaced"], sc["passes"], sc["n_after"]]
+    s0 = r["steps"][0]
+    for k, v in case["expect_step0"].items():
+        got = s0[IDX[k]]
+        if k in ("beam", "max", "cutoff"):
+            assert got == _bits(v), k
+        else:
+            assert got == v, k
+
+
+@pytest.mark.parametrize("case", load_golden("edge_cases.json")["cases"], ids=lambda c: c["name"])
+def test_golden_edge_cases(case):
+    g = graph_from_states(case["graph"])
+    lp = np.array(case["lp_rows"], dtype=np.float32).reshape(case["frames"], g.vocab)
+    r = _decode(g, lp, case["frames"], case["beam"], case["max_active"], case["min_active"],
+                allow_partial=bool(case["allow_partial"]))
+    assert list(r["arcs"]) == case["expect_arcs"]
+    assert list(r["words"]) == case["expect_words"]
+    exp = f32_value(case["expect_score"])
+    assert (r["score"] == exp) or (np.isneginf(exp) and np.isneginf(r["score"]))
+    assert r["reached_final"] == case["expect_reached_final"]
+    assert r["dead"] == case["expect_dead"]
+    for k, v in case.get("expect_step0", {}).items():
+        assert r["steps"][0][IDX[k]] == v, k
+
+
+# ----------------------------------------------------- exact search at infinite beam
+
+INF_BEAM = 1e10
+
+
+def _tiny(seed, eps):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 9))
+    vocab = int(rng.integers(2, 6))
+    g = synth.random_graph(seed, n=n, deg=(1, 3), vocab=vocab, epsilon=eps, eps_levels=3,
+                           self_loop=0.3 if seed % 2 else 0.0)
+    T = int(rng.integers(0, 7))
+    lp = synth.random_logprobs(seed + 7, 1, max(T, 1), vocab)[0]
+    return g, lp, T
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_infinite_beam_equals_exact_viterbi(eps):
+    compared_paths = 0
+    for seed in range(120):
+        g, lp, T = _tiny(seed, eps)
+        P = 2 if eps else 0
+        r = _decode(g, lp, T, INF_BEAM, 1 << 20, eps=P)
+        best, path, tied = viterbi_exact(g, lp, T)
+        assert r["reached_final"] == 1
+        assert r["score"] == best, (seed, r["score"], best)
+        if not tied:
+            assert list(r["arcs"]) == path, seed
+            compared_paths += 1
+        check_path(g, lp, T, r["arcs"], r["words"], r["score"], 1)
+    assert compared_paths > 80
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_infinite_beam_equals_path_enumeration(eps):
+    unique = 0
+    for seed in range(200, 260):
+        rng = np.random.default_rng(seed)
+        n = int(rng.integers(2, 7))
+        vocab = int(rng.integers(2, 5))
+        g = synth.random_graph(seed, n=n, deg=(1, 3), vocab=vocab, epsilon=eps, eps_levels=3)
+        T = int(rng.integers(0, 6))
+        lp = synth.random_logprobs(seed, 1, max(T, 1), vocab)[0]
+        P = 2 if eps else 0
+        r = _decode(g, lp, T, INF_BEAM, 1 << 20, eps=P)
+        best, path, count = enumerate_paths(g, lp, T, P)
+        assert r["score"] == best, seed
+        if count == 1:
+            assert list(r["arcs"]) == path, seed
+            unique += 1
+    assert unique > 40
+
+
+def test_deeper_closure_needs_more_passes():
+    """A 3-arc epsilon chain 0 -> 1 -> 2 -> 3 (only state 3 final) is closed by
+    3 passes and not by 2: each pass extends chains by one arc."""
+    spec = {"start": 0, "vocab": 2, "epsilon_id": 0,
+            "states": [[[1, 0, 0, -0.5]], [[2, 0, 0, -0.25]], [[3, 0, 0, -0.125]],
+                       [[3, 1, 0, 0.0], [4, -1, 0, 0.0]], []]}
+    g = graph_from_states(spec)
+    for T in (0, 1, 3):
+        lp = synth.random_logprobs(T, 1, max(T, 1), 2)[0]
+        best, path, _ = viterbi_exact(g, lp, T)
+        r3 = _decode(g, lp, T, 10.0, 100, eps=3)
+        assert r3["score"] == best and list(r3["arcs"]) == path
+        r2 = _decode(g, lp, T, 10.0, 100, eps=2)
+        if T == 0:
+            assert r2["reached_final"] == 0 and np.isneginf(r2["score"])
+        else:
+            assert r2["score"] <= best
+
+
+def test_pruned_score_never_beats_exact():
+    for seed in range(400, 480):
+        g, lp, T = _tiny(seed, seed % 3 == 0)
+        best, _, _ = viterbi_exact(g, lp, T)
+        r = _decode(g, lp, T, 1.5, 2, eps=2 if seed % 3 == 0 else 0)
+        if r["reached_final"]:
+            assert r["score"] <= best
+            check_path(g, lp, T, r["arcs"], r["words"], r["score"], 1)
+
+
+# ------------------------------------------------------------------ closed forms
+
+def _greedy_graph(vocab):
+    """One state with a self-loop per label (arc id = label, weight 0) and a final arc."""
+    spec = {"start": 0, "vocab": vocab, "epsilon_id": -1,
+            "states": [[[0, v, v + 1, 0.0] for v in range(vocab)] + [[1, -1, 0, 0.0]], []]}
+    return graph_from_states(spec)
+
+
+@pytest.mark.parametrize("vocab,frames", [(5, 12), (32, 50), (500, 30)])
+def test_greedy_ctc_closed_form(vocab, frames):
+    g = _greedy_graph(vocab)
+    lp = synth.random_logprobs(vocab * 7 + frames, 1, frames, vocab, sigma=3.0)[0]
+    r = _decode(g, lp, frames, 10.0, 100)
+    expect_arcs = list(np.argmax(lp, axis=1)) + [vocab]
+    s = F32(0.0)
+    for t in range(frames):
+        s = F32(s + lp[t].max())
+    assert list(r["arcs"]) == expect_arcs
+    assert r["score"] == s
+    assert list(r["words"]) == [a + 1 for a in expect_arcs[:-1]]
+
+
+def test_greedy_ctc_ties_take_smallest_label():
+    g = _greedy_graph(6)
+    lp = _const_lp(9, 6, -1.75)
+    r = _decode(g, lp, 9, 10.0, 100)
+    assert list(r["arcs"]) == [0] * 9 + [6]
+
+
+def test_forced_alignment_closed_form():
+    rng = np.random.default_rng(5)
+    T, V = 40, 17
+    labels = rng.integers(0, V, size=T)
+    w = np.log(rng.uniform(0.1, 1.0, size=T)).astype(np.float32)
+    states = [[[k + 1, int(labels[k]), k + 1, float(w[k])]] for k in range(T)]
+    states.append([[T + 1, -1, 0, 0.0]])
+    states.append([])
+    g = graph_from_states({"start": 0, "vocab": V, "epsilon_id": -1, "states": states})
+    lp = synth.random_logprobs(9, 1, T, V)[0]
+    r = _decode(g, lp, T, 10.0, 100)
+    s = F32(0.0)
+    for k in range(T):
+        s = F32(F32(s + w[k]) + lp[k, labels[k]])
+    assert r["score"] == s
+    assert list(r["arcs"]) == list(range(T)) + [T]
+
+
+# ------------------------------------------------------ dynamic beam consistency
+
+def _recompute_beams(steps, length, beam, max_active, min_active):
+    out, bp = [], F32(beam)
+    for t, n in enumerate(steps[:, IDX["n"]]):
+        if t == length:
+            out.append(F32(1e10)); continue
+        mina = max(min_active, max_active // 2) if length - t <= 5 else min_active
+        if n > max_active:
+            b = F32(min(bp, F32(beam)) * F32(0.8))
+        elif n < mina:
+            b = F32(max(bp, F32(beam)) * F32(1.25))
+        else:
+            b = F32(F32(F32(0.8) * bp) + F32(F32(0.2) * F32(beam)))
+        out.append(b); bp = b
+    return np.array(out, dtype=np.float32)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_logged_beams_follow_the_update_rule(cid):
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    for b in range(min(wl.batch, 3)):
+        r = _decode(g, lp[b], int(L[b]), wl.beam, wl.max_active)
+        st = r["steps"]
+        got = np.array(st[:, IDX["beam"]], dtype=np.uint32).view(np.float32)
+        assert np.array_equal(got, _recompute_beams(st, int(L[b]), wl.beam, wl.max_active, 0))
+        # soft cap: the frontier is allowed to exceed max_active
+        cut = np.array(st[:, IDX["cutoff"]], dtype=np.uint32).view(np.float32)
+        mx = np.array(st[:, IDX["max"]], dtype=np.uint32).view(np.float32)
+        assert np.array_equal(cut[:-1], (mx - got)[:-1])
+
+
+# ------------------------------------------------------ invariants on workloads
+
+@pytest.mark.parametrize("cid,lanes", [(1, [0]), (2, list(range(8))), (5, [0, 1]), (4, [0]), (3, [0])])
+def test_workload_paths_are_consistent(cid, lanes):
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    og = oracle.OracleGraph(g)
+    rs = oracle.decode_batch(og, lp, L, wl.beam, wl.max_active, eps_iterations=wl.eps_iterations,
+                             lanes=lanes, threads=len(lanes))
+    for b, r in zip(lanes, rs):
+        assert r["reached_final"] == 1 and r["dead"] == 0
+        check_path(g, lp[b].astype(np.float32), int(L[b]), r["arcs"], r["words"], r["score"], 1)
+        st = r["steps"]
+        assert st.shape[0] == int(L[b]) + 1
+        assert np.all(st[:, IDX["distinct"]] <= st[:, IDX["admitted"]])
+        assert np.all(st[:, IDX["admitted"]] <= st[:, IDX["arcs"]])
+        if not wl.epsilon:
+            assert np.array_equal(st[:-1, IDX["n_next"]], st[1:, IDX["n"]])
+            assert np.array_equal(st[:, IDX["n_next"]], st[:, IDX["distinct"]])
