@@ -1,0 +1,225 @@
+/*
+ * wfst.h -- C ABI of the MI355X (gfx950) WFST Viterbi beam-search decoder.
+ *
+ * The decoder takes per-frame CTC log-posteriors log_prob[B, T, V] and a CSR
+ * decoding graph (epsilon-free HLG-style, or TLG-style with epsilon arcs) and
+ * returns, per utterance, the best word sequence, the arc ids of the best path
+ * and its score. Semantics follow the page "GPU WFST Beam-Search Decoder" (OASR
+ * docs): section 1 "Purpose and Responsibilities" (relaxation
+ * end = score[src] + arc_weight + log_prob[t][ilabel], recombination by
+ * destination, backtrack through arc ids to words), section 3 "Decoding
+ * Semantics" (dynamic beam, soft max_active, exact admit test, final step,
+ * allow_partial), section 5.3 (fp32 addition order (score + weight) + log_prob),
+ * section 5.5 (epsilon closure), section 7 (outputs, overflow bits) and
+ * section 10 "Public C API" (load graph / create decoder / decode batch / free,
+ * out_meta = {ok, reached_final, overflow}). Among equal scores the smallest arc
+ * id wins, so results are deterministic.
+ *
+ * Conventions for every call: the return value is 0 (WFST_OK) or a negative
+ * status; on failure wfst_last_error() returns a message for the calling
+ * thread. Host pointers are only read during the call unless stated.
+ */
+#ifndef WFST_H
+#define WFST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WFST_OK        0
+#define WFST_EINVAL   -1   /* an argument is out of range or a pointer is null       */
+#define WFST_ECORRUPT -2   /* the graph fails validation (nothing was uploaded)      */
+#define WFST_ENOMEM   -3   /* a device or host allocation failed                     */
+#define WFST_EDEVICE  -4   /* a HIP runtime call failed (no device, launch failure)  */
+
+#define WFST_LP_F32 0      /* log_prob elements are binary32                          */
+#define WFST_LP_F16 1      /* log_prob elements are binary16, widened exactly to fp32 */
+
+/* out_meta[b * 3 + 2] bits (section 7 of the page): a non-zero value means the
+ * lane's result may be degraded; such a lane also reports ok = 0. */
+#define WFST_OVF_HASH     2   /* a destination found no hash slot within the probe bound   */
+#define WFST_OVF_ARENA    4   /* the lane's winners-log region is full                     */
+#define WFST_OVF_CLAIMS   8   /* more distinct destinations in one pass than claims_cap    */
+#define WFST_OVF_FRONTIER 16  /* more surviving tokens than frontier_cap                   */
+#define WFST_OVF_PATH     32  /* best path longer than the device path buffer              */
+
+typedef struct wfst_graph_s *wfst_graph_t;
+typedef struct wfst_decoder_s *wfst_decoder_t;
+
+/*
+ * A decoding graph in CSR form, as host arrays (page section 4 "Graph Image":
+ * row_splits, per-arc destination, ilabel, word label and weight; arc order is
+ * identity: arc id = CSR index, never reordered).
+ *
+ *  num_states   states including the super-final state, which must be the last
+ *               state (num_states - 1) and have no out-arcs; >= 2.
+ *  num_arcs     total arcs, including final arcs; in [0, 2^31 - 1).
+ *  start_state  in [0, num_states - 1).
+ *  vocab_size   V: width of a log_prob row; in [1, 65535) (ilabels are stored as
+ *               u16 on the device, page section 4).
+ *  epsilon_id   -1 when the graph has no epsilon arcs; otherwise the ilabel that
+ *               marks an epsilon arc, in [0, V) (0 on TLG graphs); that column
+ *               of log_prob is then never read.
+ *  row_splits   [num_states + 1], row_splits[0] = 0, non-decreasing,
+ *               row_splits[num_states] = num_arcs.
+ *  dest         [num_arcs], in [0, num_states).
+ *  ilabel       [num_arcs]: -1 for a final arc, epsilon_id for an epsilon arc,
+ *               else an emitting label in [0, V).
+ *  olabel       [num_arcs]: word id, 0 = no word; >= 0.
+ *  weight       [num_arcs]: log-score added to the path score; NaN and +inf are
+ *               rejected.
+ * Per state the arcs must come as [epsilon arcs][emitting arcs][final arcs];
+ * an arc enters the super-final state iff it is a final arc.
+ */
+typedef struct wfst_graph_desc {
+    int32_t num_states;
+    int32_t num_arcs;
+    int32_t start_state;
+    int32_t vocab_size;
+    int32_t epsilon_id;
+    const int32_t *row_splits;
+    const int32_t *dest;
+    const int32_t *ilabel;
+    const int32_t *olabel;
+    const float *weight;
+} wfst_graph_desc;
+
+/*
+ * Search settings (page section 10, wfst_create_decoder; section 3 for the
+ * meaning of beam, min_active, max_active and allow_partial).
+ *
+ *  beam            search beam (> 0, finite).
+ *  min_active      lower frontier target of the dynamic beam (>= 0; 0 default).
+ *  max_active      upper frontier target, enforced only through beam decay (>= 1).
+ *  allow_partial   1: when no frontier state has a final arc on the last step,
+ *                  the best-scoring token ends the path (reached_final = 0).
+ *  max_lanes       largest batch B a decode may use; in [1, 64].
+ *  max_frames      largest T a decode may use; >= 1.
+ *  lp_dtype        WFST_LP_F32 or WFST_LP_F16.
+ *  eps_iterations  epsilon-closure passes after each real step (and once on the
+ *                  start frontier); ignored on graphs without epsilon arcs;
+ *                  in [0, 16].
+ *  use_graphs      1: each decode replays one captured hipGraph of the whole
+ *                  frame loop; 0: plain launches (same kernels, same results).
+ *  frontier_cap    tokens per lane per step (0: 64 * max_active).
+ *  claims_cap      distinct destinations per lane per pass (0: frontier_cap);
+ *                  claims_cap * (1 + eps passes) * (largest out-degree of one
+ *                  arc class) must stay below 2^32.
+ *  arena_entries   winners-log entries per lane per decode
+ *                  (0: 4 * max_active * (max_frames + 2) * (1 + eps passes),
+ *                  at least 2^20); max_lanes * arena_entries < 2^31.
+ *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
+ */
+typedef struct wfst_decoder_config {
+    float beam;
+    int32_t min_active;
+    int32_t max_active;
+    int32_t allow_partial;
+    int32_t max_lanes;
+    int32_t max_frames;
+    int32_t lp_dtype;
+    int32_t eps_iterations;
+    int32_t use_graphs;
+    int32_t frontier_cap;
+    int32_t claims_cap;
+    int32_t grid_blocks;
+    int64_t arena_entries;
+} wfst_decoder_config;
+
+/* Message of the last failed call on this thread ("" if none). The pointer stays
+ * valid until the next call on the same thread. */
+const char *wfst_last_error(void);
+
+/*
+ * Validate a host CSR graph and upload it to `device` (page section 4: the
+ * loader validates every index the decoder later follows; the device copy is
+ * split into per-arc columns, ilabel as u16, and per-state arc ranges and the
+ * largest emitting / final weight of each state are computed once here).
+ * The host arrays are copied; the caller may free them when the call returns.
+ * On success *out holds one reference; release it with wfst_graph_release.
+ * Errors: WFST_EINVAL (null pointer, bad device), WFST_ECORRUPT (any rule of
+ * wfst_graph_desc broken; checked before any device work), WFST_ENOMEM,
+ * WFST_EDEVICE.
+ */
+int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_graph_t *out);
+
+/* Drop one reference (page section 10: a decoder co-owns its graph, so the
+ * graph may be released before its decoders). Null is a no-op. */
+int wfst_graph_release(wfst_graph_t g);
+
+/*
+ * Create a decoder on the graph's device: allocates every workspace buffer once
+ * (frontiers, per-lane hash tables, claims lists, winners-log regions, result
+ * buffers) and takes a graph reference (page section 6.1 "Workspace", section
+ * 10). Errors: WFST_EINVAL (bad config), WFST_ENOMEM, WFST_EDEVICE.
+ */
+int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *c, wfst_decoder_t *out);
+
+/*
+ * Decode a batch (page section 10 wfst_decode_batch, section 7 outputs).
+ *
+ *  log_prob      device pointer to a packed [B, T, V] tensor of lp_dtype on the
+ *                decoder's device (row (b, t) at log_prob + (b*T + t)*V); owned
+ *                by the caller and left untouched; must stay valid until the
+ *                call returns.
+ *  B, T, V       1 <= B <= max_lanes, 0 <= T <= max_frames, V = graph vocab_size.
+ *  lengths_host  [B] host int32, each in [0, T]; frames t >= lengths[b] of lane b
+ *                are never read.
+ *  stream        the caller's HIP stream (hipStream_t; null = the null stream):
+ *                the decode is ordered after work already queued on it, and the
+ *                call returns after synchronising it once, when the results
+ *                have been copied back.
+ *  out_words     [B * words_cap] host: lane b's word ids at b*words_cap.
+ *  out_word_lens [B] host: TRUE word counts (may exceed words_cap; the first
+ *                words_cap words are written).
+ *  out_arcs      [B * arcs_cap] host: arc ids of the best path in forward order,
+ *                epsilon and final arcs included.
+ *  out_arc_lens  [B] host: TRUE path lengths (may exceed arcs_cap).
+ *  out_scores    [B] host: best path score (binary32); -inf when the lane has no
+ *                path.
+ *  out_meta      [B * 3] host: {ok, reached_final, overflow bits}.
+ * out_words / out_arcs may be null when their cap is 0. A lane with no path
+ * (every candidate of a real step pruned or no arc to expand, or no final arc on
+ * the last step without allow_partial) reports ok = 1, reached_final = 0,
+ * score -inf and no arcs. The call is idempotent and serial per decoder (an
+ * internal mutex); other decoders may run concurrently.
+ * Errors: WFST_EINVAL (ranges above, null pointers, V mismatch), WFST_EDEVICE.
+ */
+int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
+                const int32_t *lengths_host, void *stream,
+                int32_t *out_words, int32_t words_cap, int32_t *out_word_lens,
+                int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
+                float *out_scores, int32_t *out_meta);
+
+/* Free the decoder's workspace and its graph reference. Null is a no-op. */
+int wfst_decoder_destroy(wfst_decoder_t d);
+
+/*
+ * Counters of the last decode, summed over its lanes (n up to 12 values):
+ *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
+ *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
+ *  frontier sizes), [4] epsilon arcs relaxed, [5] epsilon candidates admitted,
+ *  [6] epsilon destinations claimed, [7] tokens appended or replaced by the
+ *  closure, [8] winners-log entries written, [9] steps run (frame loop length),
+ *  [10] largest frontier, [11] device bytes reserved by the decoder.
+ */
+int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
+
+/*
+ * Per-step records of lane `lane` in the last decode, 16 int64 each:
+ *  {n, beam bits, max bits, arcs, admitted, distinct, eps arcs, eps admitted,
+ *   eps distinct, eps new, eps replaced, eps passes, phase, 0, 0, 0}
+ * record 0 describes the start frontier's closure (only the eps fields), record
+ * t + 1 step t. phase: 0 real, 1 final, 2 redirect, 3 dead, -1 not run.
+ * Writes min(steps_cap, lengths[lane] + 2) records; returns how many it wrote
+ * or a negative status.
+ */
+int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_t steps_cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WFST_H */

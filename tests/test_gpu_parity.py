@@ -1,0 +1,227 @@
+"""GPU parity: the HIP decoder (through the C ABI) against the CPU oracle on the
+same seeded inputs. Arc ids and words must be bit-exact, scores within 1e-4
+(they come out bit-equal), and every per-step counter (frontier size, beam,
+exact max, arcs expanded, admitted, distinct, epsilon counters) equal."""
+
+import numpy as np
+import pytest
+
+import synth
+import wfst_beam_search_amd as wb
+from cases import check_path, graph_from_states, load_golden
+from gpu_util import compare_batch, compare_lane, gpu_decode, oracle_lanes
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ golden
+
+def _golden_cases():
+    out = []
+    bs = load_golden("beam_schedule.json")
+    for c in bs["cases"]:
+        out.append(("beam_" + c["name"], graph_from_states(bs["graphs"][c["graph"]]),
+                    np.full((c["frames"], 1), c["lp_value"], np.float32), c, 0, 0))
+    tc = load_golden("tie_chain.json")
+    g = graph_from_states(tc["graph"])
+    out.append(("tie_chain", g, np.full((tc["frames"], g.vocab), tc["lp_value"], np.float32), tc, 0, 0))
+    ec = load_golden("eps_closure.json")
+    out.append(("eps_closure", graph_from_states(ec["graph"]), np.array(ec["lp_rows"], np.float32), ec,
+                ec["eps_iterations"], 0))
+    for c in load_golden("edge_cases.json")["cases"]:
+        g = graph_from_states(c["graph"])
+        out.append(("edge_" + c["name"], g,
+                    np.array(c["lp_rows"], np.float32).reshape(c["frames"], g.vocab), c, 0, c["allow_partial"]))
+    return out
+
+
+@pytest.mark.parametrize("name,g,lp,case,eps,ap", _golden_cases(), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("use_graphs", [True, False])
+def test_golden(name, g, lp, case, eps, ap, use_graphs):
+    _say("golden", name, use_graphs)
+    T = lp.shape[0]
+    lpb = lp.reshape(1, T, g.vocab)
+    r, steps, _ = gpu_decode(g, lpb, [T], case["beam"], case["max_active"], case.get("min_active", 0),
+                             bool(ap), eps, use_graphs=use_graphs)
+    assert list(r.arcs[0]) == case["expect_arcs"]
+    if "expect_words" in case:
+        assert list(r.words[0]) == case["expect_words"]
+    exp = case["expect_score"]
+    if exp == "-inf":
+        assert np.isneginf(r.scores[0])
+    else:
+        assert r.scores[0] == np.float32(exp)
+    o = oracle_lanes(g, lpb, [T], case["beam"], case["max_active"], case.get("min_active", 0), bool(ap), eps)
+    compare_lane(0, r, steps, o[0])
+
+
+# --------------------------------------------------------- random small graphs
+
+def _random_case(seed, eps):
+    rng = np.random.default_rng(10_000 + seed)
+    n = int(rng.integers(3, 60))
+    vocab = int(rng.integers(2, 12))
+    g = synth.random_graph(seed, n=n, deg=(1, int(rng.integers(2, 9))), vocab=vocab, epsilon=eps,
+                           eps_levels=int(rng.integers(2, 5)), self_loop=float(rng.choice([0.0, 0.3])))
+    B = int(rng.integers(1, 6))
+    T = int(rng.integers(0, 24))
+    lp = synth.random_logprobs(seed, B, max(T, 1), vocab, sigma=float(rng.uniform(0.5, 3.0)))
+    if T == 0:
+        lp = lp[:, :0, :]
+    lengths = rng.integers(0, T + 1, size=B).astype(np.int32)
+    beam = float(rng.choice([0.5, 2.0, 5.0, 12.0, 1e10]))
+    max_active = int(rng.choice([1, 2, 5, 20, 1000]))
+    min_active = int(rng.choice([0, 0, 3]))
+    allow_partial = bool(rng.integers(0, 2))
+    P = int(rng.integers(1, 5)) if eps else 0
+    return g, lp, lengths, beam, max_active, min_active, allow_partial, P
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_random_small_graphs(eps):
+    for seed in range(150):
+        g, lp, L, beam, ma, mi, ap, P = _random_case(seed + (1000 if eps else 0), eps)
+        _say("random", eps, seed, lp.shape, beam, ma, mi, ap, P)
+        r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, use_graphs=bool(seed % 2))
+        o = oracle_lanes(g, lp, L, beam, ma, mi, ap, P)
+        compare_batch(r, steps, o)
+
+
+def test_greedy_closed_form_gpu():
+    V, T = 500, 60
+    spec = {"start": 0, "vocab": V, "epsilon_id": -1,
+            "states": [[[0, v, v + 1, 0.0] for v in range(V)] + [[1, -1, 0, 0.0]], []]}
+    g = graph_from_states(spec)
+    lp = synth.random_logprobs(77, 3, T, V, sigma=3.0)
+    r, _, _ = gpu_decode(g, lp, [T, T - 7, 0], 10.0, 100)
+    for b, Tb in enumerate([T, T - 7, 0]):
+        exp = list(np.argmax(lp[b, :Tb], axis=1)) + [V]
+        s = np.float32(0.0)
+        for t in range(Tb):
+            s = np.float32(s + lp[b, t].max())
+        assert list(r.arcs[b]) == exp
+        assert r.scores[b] == s
+
+
+# ------------------------------------------------------------- workloads
+
+WORKLOAD_IDS = [1, 2, 5, 4, 3]
+
+
+@pytest.fixture(scope="module")
+def workload_graphs():
+    return {}
+
+
+@pytest.mark.parametrize("cid", WORKLOAD_IDS)
+def test_workload_parity(cid, workload_graphs):
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    _say("workload", cid, lp.shape, lp.dtype)
+    dg = wb.Graph(g)
+    try:
+        r, steps, stats = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
+                                     dgraph=dg)
+    finally:
+        dg.release()
+    _say("  gpu done; stats", stats)
+    o = oracle_lanes(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations)
+    _say("  oracle done")
+    compare_batch(r, steps, o)
+    for b in range(lp.shape[0]):
+        check_path(g, lp[b].astype(np.float32), int(L[b]), r.arcs[b], r.words[b], r.scores[b], 1)
+    assert stats["arcs"] == sum(int(x["steps"][:, 4].sum()) for x in o)
+
+
+def test_graph_replay_equals_eager_and_is_idempotent():
+    cid = 2
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    import torch
+    dg = wb.Graph(g)
+    dec_g = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames, use_graphs=True)
+    dec_e = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames, use_graphs=False)
+    x = torch.from_numpy(lp).cuda()
+    runs = [dec_g.decode(x, L), dec_g.decode(x, L), dec_e.decode(x, L), dec_g.decode(x, L)]
+    for rr in runs[1:]:
+        for b in range(wl.batch):
+            assert np.array_equal(rr.arcs[b], runs[0].arcs[b])
+            assert np.array_equal(rr.words[b], runs[0].words[b])
+        assert np.array_equal(rr.scores.view(np.uint32), runs[0].scores.view(np.uint32))
+        assert np.array_equal(rr.meta, runs[0].meta)
+    dec_g.close(); dec_e.close(); dg.release()
+
+
+def test_lane_result_independent_of_batchmates():
+    cid = 2
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    import torch
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames)
+    full = dec.decode(torch.from_numpy(lp).cuda(), L)
+    for b in (0, 5):
+        one = dec.decode(torch.from_numpy(np.ascontiguousarray(lp[b:b + 1])).cuda(), L[b:b + 1])
+        assert np.array_equal(one.arcs[0], full.arcs[b])
+        assert one.scores[0].view(np.uint32) == full.scores[b].view(np.uint32)
+    # a shorter batch after a longer one reuses the same decoder
+    part = dec.decode(torch.from_numpy(np.ascontiguousarray(lp[2:5, :100])).cuda(), np.minimum(L[2:5], 100))
+    o = oracle_lanes(g, np.ascontiguousarray(lp[2:5, :100]), np.minimum(L[2:5], 100), wl.beam, wl.max_active)
+    for b in range(3):
+        compare_lane(b, part, None, o[b], check_steps=False)
+    dec.close(); dg.release()
+
+
+# ------------------------------------------------------------ errors, overflow
+
+def test_decode_argument_errors():
+    import torch
+    g = graph_from_states(load_golden("tie_chain.json")["graph"])
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, 10.0, 100, max_lanes=2, max_frames=4)
+    x = torch.zeros((2, 4, g.vocab), device="cuda")
+    with pytest.raises(wb.WfstError):
+        dec.decode(x, [5, 1])                      # length > T
+    with pytest.raises(wb.WfstError):
+        dec.decode(torch.zeros((3, 4, g.vocab), device="cuda"), [1, 1, 1])   # B > max_lanes
+    with pytest.raises(wb.WfstError):
+        dec.decode(torch.zeros((1, 5, g.vocab), device="cuda"), [1])         # T > max_frames
+    with pytest.raises(wb.WfstError):
+        dec.decode(torch.zeros((1, 4, g.vocab + 1), device="cuda"), [1])     # V mismatch
+    r = dec.decode(x, [0, 3])
+    assert r.meta[0, 0] == 1
+    dec.close(); dg.release()
+    with pytest.raises(wb.WfstError):
+        wb.Decoder(wb.Graph(g), -1.0, 10)
+
+
+@pytest.mark.parametrize("cid,cap,bit", [(2, "frontier_cap", 16), (2, "arena_entries", 4),
+                                         (2, "claims_cap", 8), (4, "frontier_cap", 16),
+                                         (4, "arena_entries", 4)])
+def test_capacity_overflow_is_flagged(cid, cap, bit):
+    import torch
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    _say("overflow", cid, cap)
+    caps = {"frontier_cap": {"frontier_cap": 2000 if cid == 4 else 64, "claims_cap": 1000000},
+            "arena_entries": {"arena_entries": 40000 if cid == 4 else 4096},
+            "claims_cap": {"frontier_cap": 100000, "claims_cap": 64}}[cap]
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=2, max_frames=wl.frames,
+                     eps_iterations=wl.eps_iterations, **caps)
+    x = torch.from_numpy(np.ascontiguousarray(lp[:2])).cuda()
+    r = dec.decode(x, L[:2])
+    assert all(int(r.meta[b, 2]) & bit for b in range(2))
+    assert all(int(r.meta[b, 0]) == 0 for b in range(2))
+    # the same decoder recovers on a decode that fits (a claims overflow leaves
+    # stale hash slots that the next decode clears first)
+    short = np.array([1, 2], dtype=np.int32)
+    r2 = dec.decode(x, short)
+    o = oracle_lanes(g, lp[:2], short, wl.beam, wl.max_active, eps_iterations=wl.eps_iterations)
+    for b in range(2):
+        compare_lane(b, r2, None, o[b], check_steps=False)
+    dec.close(); dg.release()

@@ -1,0 +1,240 @@
+"""MI355X (gfx950) WFST Viterbi beam-search decoder: thin Python binding.
+
+Every step of the decode runs in the HIP library ``libwfst_mi355x.so`` (C ABI in
+``include/wfst.h``); this module only marshals arguments through ctypes. PyTorch
+is used for device memory and the current stream, nothing else. There is no CPU
+fallback: importing works without a GPU, but every call needs the built library
+and a device, and fails loudly otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = ["Graph", "Decoder", "DecodeResult", "WfstError", "library_path", "load_library",
+           "EXPORTED_SYMBOLS", "LP_F32", "LP_F16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libwfst_mi355x.so")
+
+LP_F32, LP_F16 = 0, 1
+EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release",
+                    "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
+                    "wfst_decoder_stats", "wfst_decoder_step_stats")
+STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
+               "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "_13", "_14", "_15")
+STAT_FIELDS = ("arcs", "admitted", "distinct", "tokens", "eps_arcs", "eps_admitted",
+               "eps_distinct", "eps_changed", "log_entries", "steps", "max_frontier", "bytes_reserved")
+
+
+class WfstError(RuntimeError):
+    """A call into the decoder library failed (the message is the library's)."""
+
+    def __init__(self, code, msg):
+        super().__init__(f"wfst error {code}: {msg}")
+        self.code = code
+
+
+class _GraphDesc(ctypes.Structure):
+    _fields_ = [("num_states", ctypes.c_int32), ("num_arcs", ctypes.c_int32),
+                ("start_state", ctypes.c_int32), ("vocab_size", ctypes.c_int32),
+                ("epsilon_id", ctypes.c_int32),
+                ("row_splits", ctypes.c_void_p), ("dest", ctypes.c_void_p),
+                ("ilabel", ctypes.c_void_p), ("olabel", ctypes.c_void_p), ("weight", ctypes.c_void_p)]
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("beam", ctypes.c_float), ("min_active", ctypes.c_int32),
+                ("max_active", ctypes.c_int32), ("allow_partial", ctypes.c_int32),
+                ("max_lanes", ctypes.c_int32), ("max_frames", ctypes.c_int32),
+                ("lp_dtype", ctypes.c_int32), ("eps_iterations", ctypes.c_int32),
+                ("use_graphs", ctypes.c_int32), ("frontier_cap", ctypes.c_int32),
+                ("claims_cap", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
+                ("arena_entries", ctypes.c_int64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise WfstError(-4, f"{_LIB_PATH} is missing: build it with "
+                                "`python -m wfst_beam_search_amd.build` (there is no CPU fallback)")
+        # PyTorch bundles its own HIP runtime under the same soname
+        # (libamdhip64.so.7). Loading torch first makes the library bind to that
+        # copy, so the process holds one HIP/HSA runtime; loading the system copy
+        # first would leave torch unable to open the GPU.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+        lib.wfst_last_error.restype = ctypes.c_char_p
+        lib.wfst_graph_upload.argtypes = [ctypes.POINTER(_GraphDesc), ctypes.c_int, ctypes.POINTER(vp)]
+        lib.wfst_graph_release.argtypes = [vp]
+        lib.wfst_decoder_create.argtypes = [vp, ctypes.POINTER(_Config), ctypes.POINTER(vp)]
+        lib.wfst_decoder_destroy.argtypes = [vp]
+        lib.wfst_decode.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+        lib.wfst_decoder_stats.argtypes = [vp, vp, i32]
+        lib.wfst_decoder_step_stats.argtypes = [vp, i32, vp, i32]
+        for name in EXPORTED_SYMBOLS:
+            if name != "wfst_last_error":
+                getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(rc):
+    if rc < 0:
+        msg = _lib.wfst_last_error().decode(errors="replace")
+        raise WfstError(rc, msg)
+    return rc
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data if a.size else None
+
+
+class Graph:
+    """A decoding graph uploaded to one device.
+
+    ``g`` has the attributes num_states (including the super-final state, the
+    last one), start, vocab, epsilon_id and the arrays row_splits, dest, ilabel,
+    olabel, weight (see include/wfst.h for the rules).
+    """
+
+    def __init__(self, g, device: int = 0):
+        lib = load_library()
+        self._arrays = [np.ascontiguousarray(g.row_splits, dtype=np.int32),
+                        np.ascontiguousarray(g.dest, dtype=np.int32),
+                        np.ascontiguousarray(g.ilabel, dtype=np.int32),
+                        np.ascontiguousarray(g.olabel, dtype=np.int32),
+                        np.ascontiguousarray(g.weight, dtype=np.float32)]
+        rs, dest, il, ol, w = self._arrays
+        desc = _GraphDesc(int(g.num_states), int(dest.shape[0]), int(g.start), int(g.vocab),
+                          int(g.epsilon_id), _ptr(rs), _ptr(dest), _ptr(il), _ptr(ol), _ptr(w))
+        h = ctypes.c_void_p()
+        _check(lib.wfst_graph_upload(ctypes.byref(desc), int(device), ctypes.byref(h)))
+        self._arrays = None
+        self.handle = h
+        self.device = device
+        self.vocab = int(g.vocab)
+        self.epsilon_id = int(g.epsilon_id)
+
+    def release(self):
+        if self.handle:
+            _lib.wfst_graph_release(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+@dataclass
+class DecodeResult:
+    words: list          # per lane: int32 array of word ids
+    arcs: list           # per lane: int32 array of arc ids (forward order)
+    scores: np.ndarray   # float32 [B]
+    meta: np.ndarray     # int32 [B, 3]: ok, reached_final, overflow bits
+    word_lens: np.ndarray
+    arc_lens: np.ndarray
+
+
+class Decoder:
+    """A decoder instance (workspace on the graph's device)."""
+
+    def __init__(self, graph: Graph, beam: float, max_active: int, min_active: int = 0,
+                 allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
+                 lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
+                 frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
+                 grid_blocks: int = 0):
+        lib = load_library()
+        cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
+                      int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
+                      int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
+                      int(claims_cap), int(grid_blocks), int(arena_entries))
+        h = ctypes.c_void_p()
+        _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
+        self.handle = h
+        self.graph = graph
+        self.max_lanes = int(max_lanes)
+        self.max_frames = int(max_frames)
+        self.lp_dtype = lp_dtype
+        self.eps_iterations = int(eps_iterations)
+
+    def decode(self, log_prob, lengths, stream=None, words_cap: int | None = None,
+               arcs_cap: int | None = None) -> DecodeResult:
+        """Decode ``log_prob`` ([B, T, V] torch tensor on the decoder's device, packed,
+        in the decoder's dtype) with per-lane ``lengths``; returns host results."""
+        import torch
+        if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda:
+            raise TypeError("log_prob must be a torch tensor on the GPU")
+        if not log_prob.is_contiguous():
+            raise ValueError("log_prob must be packed (contiguous)")
+        want = torch.float16 if self.lp_dtype == "f16" else torch.float32
+        if log_prob.dtype != want:
+            raise TypeError(f"log_prob must be {want}")
+        B, T, V = (int(x) for x in log_prob.shape)
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
+        if lens.shape[0] != B:
+            raise ValueError("lengths must have B entries")
+        if stream is None:
+            stream = torch.cuda.current_stream(log_prob.device).cuda_stream
+        wcap = int(words_cap) if words_cap is not None else T + 2
+        acap = int(arcs_cap) if arcs_cap is not None else (T + 2) * (1 + max(0, self.eps_iterations))
+        out_words = np.zeros((B, max(wcap, 1)), dtype=np.int32)
+        out_arcs = np.zeros((B, max(acap, 1)), dtype=np.int32)
+        wl = np.zeros(B, dtype=np.int32)
+        al = np.zeros(B, dtype=np.int32)
+        sc = np.zeros(B, dtype=np.float32)
+        meta = np.zeros((B, 3), dtype=np.int32)
+        _check(_lib.wfst_decode(self.handle, ctypes.c_void_p(log_prob.data_ptr()), B, T, V,
+                                _ptr(lens), ctypes.c_void_p(int(stream)),
+                                _ptr(out_words), wcap, _ptr(wl), _ptr(out_arcs), acap, _ptr(al),
+                                _ptr(sc), _ptr(meta)))
+        words = [out_words[b, :min(int(wl[b]), wcap)].copy() for b in range(B)]
+        arcs = [out_arcs[b, :min(int(al[b]), acap)].copy() for b in range(B)]
+        return DecodeResult(words, arcs, sc, meta, wl, al)
+
+    def stats(self) -> dict:
+        out = np.zeros(len(STAT_FIELDS), dtype=np.int64)
+        _check(_lib.wfst_decoder_stats(self.handle, _ptr(out), len(STAT_FIELDS)))
+        return dict(zip(STAT_FIELDS, (int(x) for x in out)))
+
+    def step_stats(self, lane: int) -> np.ndarray:
+        """Per-step records of ``lane`` in the last decode: int64 [n, 16]
+        (record 0: start closure; record t + 1: step t)."""
+        cap = self.max_frames + 2
+        out = np.zeros((cap, len(STEP_FIELDS)), dtype=np.int64)
+        n = _check(_lib.wfst_decoder_step_stats(self.handle, int(lane), _ptr(out), cap))
+        return out[:n]
+
+    def close(self):
+        if self.handle:
+            _lib.wfst_decoder_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

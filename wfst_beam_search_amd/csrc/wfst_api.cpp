@@ -1,0 +1,529 @@
+// C ABI of the MI355X WFST decoder: graph validation and upload, decoder
+// workspace, hipGraph capture of the frame loop, decode, statistics.
+// Page "GPU WFST Beam-Search Decoder" (OASR docs): section 4 (validation, SoA
+// split, per-state upper-bound weights), section 6.1 (workspace), section 9
+// (whole-decode graph replay, plain launches when disabled), section 10 (API).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "wfst.h"
+#include "wfst_internal.h"
+
+using namespace wfst;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg)
+{
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(e == hipErrorOutOfMemory ? WFST_ENOMEM : WFST_EDEVICE,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr)                                              \
+    do {                                                           \
+        hipError_t _e = (expr);                                    \
+        if (_e != hipSuccess) return hip_fail(_e, #expr);          \
+    } while (0)
+
+template <typename T>
+int dalloc(T **p, size_t count, std::vector<void *> *owned, size_t *bytes)
+{
+    *p = nullptr;
+    const size_t nb = std::max<size_t>(count, 1) * sizeof(T);
+    hipError_t e = hipMalloc((void **)p, nb);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+    owned->push_back(*p);
+    *bytes += nb;
+    return WFST_OK;
+}
+
+uint64_t next_pow2(uint64_t x)
+{
+    uint64_t p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+struct wfst_graph_s {
+    std::atomic<int> refs{1};
+    int device = 0;
+    int32_t num_states = 0, num_arcs = 0, start = 0, vocab = 0, eps_id = -1;
+    uint32_t max_class_deg = 0;   // most arcs of one class leaving one state
+    std::vector<void *> owned;
+    size_t bytes = 0;
+    StateInfo *sinfo = nullptr;
+    uint16_t *ilabel = nullptr;
+    float *weight = nullptr;
+    int32_t *dest = nullptr, *olabel = nullptr, *arc_src = nullptr;
+
+    ~wfst_graph_s()
+    {
+        if (!owned.empty()) {
+            (void)hipSetDevice(device);
+            for (void *p : owned) (void)hipFree(p);
+        }
+    }
+};
+
+struct wfst_decoder_s {
+    std::mutex mu;
+    wfst_graph_s *g = nullptr;
+    wfst_decoder_config cfg{};
+    Work w{};
+    int grid = 0;
+    int passes = 0;                 // closure passes run per step (0 without epsilon arcs)
+    std::vector<void *> owned;
+    size_t bytes = 0;
+    LaneCtl *ctl = nullptr;
+    LpDesc *d_desc = nullptr;
+    int32_t *d_lengths = nullptr;
+    void *h_in = nullptr;           // pinned: LpDesc + lengths
+    int32_t *h_res = nullptr;       // pinned: results
+    hipStream_t cap_stream = nullptr;
+    std::map<int, hipGraphExec_t> graphs;
+    int last_B = 0;
+    std::vector<int32_t> last_len;
+    int last_steps = 0;
+
+    ~wfst_decoder_s()
+    {
+        (void)hipSetDevice(g ? g->device : 0);
+        for (auto &kv : graphs) (void)hipGraphExecDestroy(kv.second);
+        if (cap_stream) (void)hipStreamDestroy(cap_stream);
+        if (h_in) (void)hipHostFree(h_in);
+        if (h_res) (void)hipHostFree(h_res);
+        for (void *p : owned) (void)hipFree(p);
+        if (g && g->refs.fetch_sub(1) == 1) delete g;
+    }
+};
+
+// ------------------------------------------------------------- validation
+
+// Checks every rule of wfst_graph_desc (page section 4: every index the decoder
+// later follows without a check) and derives the per-state ranges and
+// upper-bound weights. Pure host code: no device call.
+static int validate_graph(const wfst_graph_desc *g, std::vector<StateInfo> *info, uint32_t *max_deg)
+{
+    if (!g) return fail(WFST_EINVAL, "graph descriptor is null");
+    const int32_t S = g->num_states, A = g->num_arcs;
+    if (S < 2) return fail(WFST_ECORRUPT, "corrupt graph: num_states must be >= 2 (a real state and the super-final state)");
+    if (A < 0 || A == INT32_MAX) return fail(WFST_ECORRUPT, "corrupt graph: num_arcs out of range");
+    if (!g->row_splits || (A > 0 && (!g->dest || !g->ilabel || !g->olabel || !g->weight)))
+        return fail(WFST_EINVAL, "graph array pointer is null");
+    if (g->vocab_size < 1 || g->vocab_size >= 65535)
+        return fail(WFST_ECORRUPT, "corrupt graph: vocab_size must lie in [1, 65535)");
+    if (g->epsilon_id < -1 || g->epsilon_id >= g->vocab_size)
+        return fail(WFST_ECORRUPT, "corrupt graph: epsilon_id must be -1 or lie in [0, vocab_size)");
+    if (g->start_state < 0 || g->start_state >= S - 1)
+        return fail(WFST_ECORRUPT, "corrupt graph: start_state must be a real state");
+    const int32_t *rs = g->row_splits;
+    if (rs[0] != 0 || rs[S] != A) return fail(WFST_ECORRUPT, "corrupt graph: row_splits must start at 0 and end at num_arcs");
+    for (int32_t s = 0; s < S; ++s)
+        if (rs[s + 1] < rs[s]) return fail(WFST_ECORRUPT, "corrupt graph: row_splits decreases at state " + std::to_string(s));
+    if (rs[S - 1] != rs[S]) return fail(WFST_ECORRUPT, "corrupt graph: the super-final state (last) must have no out-arcs");
+    const int32_t sf = S - 1, V = g->vocab_size, eps = g->epsilon_id;
+    info->assign((size_t)S, StateInfo{});
+    uint32_t md = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        int32_t a = rs[s];
+        const int32_t e = rs[s + 1];
+        StateInfo si{};
+        si.eps_b = a;
+        if (eps >= 0)
+            while (a < e && g->ilabel[a] == eps) ++a;
+        si.emit_b = a;
+        float emax = -INFINITY, fmax = -INFINITY;
+        while (a < e && g->ilabel[a] >= 0 && g->ilabel[a] < V && g->ilabel[a] != eps) {
+            emax = std::max(emax, g->weight[a]);
+            ++a;
+        }
+        si.fin_b = a;
+        while (a < e && g->ilabel[a] == -1) {
+            fmax = std::max(fmax, g->weight[a]);
+            ++a;
+        }
+        si.end = e;
+        if (a != e) {
+            const int32_t il = g->ilabel[a];
+            if (il == -1 || il == eps || (il >= 0 && il < V))
+                return fail(WFST_ECORRUPT, "corrupt graph: arcs of state " + std::to_string(s) +
+                                               " are not ordered [epsilon][emitting][final] (arc " + std::to_string(a) + ")");
+            return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) + " has ilabel " + std::to_string(il) +
+                                           " outside {-1, epsilon_id} and [0, vocab_size)");
+        }
+        si.emit_maxw = emax;
+        si.fin_maxw = fmax;
+        md = std::max(md, (uint32_t)(si.fin_b - si.emit_b));
+        md = std::max(md, (uint32_t)(si.end - si.fin_b));
+        md = std::max(md, (uint32_t)(si.emit_b - si.eps_b));
+        (*info)[(size_t)s] = si;
+    }
+    for (int32_t a = 0; a < A; ++a) {
+        const int32_t d = g->dest[a];
+        if (d < 0 || d >= S) return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) + " has dest outside [0, num_states)");
+        if ((g->ilabel[a] == -1) != (d == sf))
+            return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) +
+                                           ": an arc must enter the super-final state iff its ilabel is -1");
+        if (g->olabel[a] < 0) return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) + " has a negative olabel");
+        const float w = g->weight[a];
+        if (std::isnan(w) || (std::isinf(w) && w > 0)) return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) + " has a NaN or +inf weight");
+    }
+    *max_deg = md;
+    return WFST_OK;
+}
+
+extern "C" const char *wfst_last_error(void) { return g_err.c_str(); }
+
+extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_graph_t *out)
+{
+    if (!out) return fail(WFST_EINVAL, "out is null");
+    *out = nullptr;
+    std::vector<StateInfo> info;
+    uint32_t md = 0;
+    int rc = validate_graph(g, &info, &md);
+    if (rc != WFST_OK) return rc;
+    int ndev = 0;
+    HIP_TRY(hipGetDeviceCount(&ndev));
+    if (device < 0 || device >= ndev) return fail(WFST_EINVAL, "device index out of range");
+    HIP_TRY(hipSetDevice(device));
+
+    const int32_t S = g->num_states, A = g->num_arcs;
+    std::vector<uint16_t> il16((size_t)A);
+    std::vector<int32_t> src((size_t)A);
+    for (int32_t s = 0; s < S; ++s)
+        for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) src[(size_t)a] = s;
+    for (int32_t a = 0; a < A; ++a) il16[(size_t)a] = g->ilabel[a] == -1 ? kFinalLabel : (uint16_t)g->ilabel[a];
+
+    wfst_graph_s *h = new wfst_graph_s();
+    h->device = device;
+    h->num_states = S;
+    h->num_arcs = A;
+    h->start = g->start_state;
+    h->vocab = g->vocab_size;
+    h->eps_id = g->epsilon_id;
+    h->max_class_deg = md;
+    int r = WFST_OK;
+    if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->ilabel, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->weight, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->dest, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->olabel, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->arc_src, (size_t)A, &h->owned, &h->bytes))) {
+        delete h;
+        return r;
+    }
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = hipMemcpy(h->sinfo, info.data(), sizeof(StateInfo) * (size_t)S, hipMemcpyHostToDevice);
+    if (A > 0) {
+        if (e == hipSuccess) e = hipMemcpy(h->ilabel, il16.data(), 2 * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->weight, g->weight, 4 * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->dest, g->dest, 4 * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->olabel, g->olabel, 4 * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->arc_src, src.data(), 4 * (size_t)A, hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "graph upload");
+    }
+    *out = h;
+    return WFST_OK;
+}
+
+extern "C" int wfst_graph_release(wfst_graph_t g)
+{
+    if (g && g->refs.fetch_sub(1) == 1) delete g;
+    return WFST_OK;
+}
+
+// ---------------------------------------------------------------- decoder
+
+extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp, wfst_decoder_t *out)
+{
+    if (!out) return fail(WFST_EINVAL, "out is null");
+    *out = nullptr;
+    if (!g || !cp) return fail(WFST_EINVAL, "graph or config is null");
+    wfst_decoder_config c = *cp;
+    if (!(c.beam > 0.0f) || std::isinf(c.beam)) return fail(WFST_EINVAL, "beam must be positive and finite");
+    if (c.max_active < 1 || c.min_active < 0) return fail(WFST_EINVAL, "max_active must be >= 1 and min_active >= 0");
+    if (c.max_lanes < 1 || c.max_lanes > kMaxLanes) return fail(WFST_EINVAL, "max_lanes must lie in [1, 64]");
+    if (c.max_frames < 1 || c.max_frames > (1 << 20)) return fail(WFST_EINVAL, "max_frames must lie in [1, 2^20]");
+    if (c.lp_dtype != WFST_LP_F32 && c.lp_dtype != WFST_LP_F16) return fail(WFST_EINVAL, "lp_dtype must be WFST_LP_F32 or WFST_LP_F16");
+    if (c.eps_iterations < 0 || c.eps_iterations > 16) return fail(WFST_EINVAL, "eps_iterations must lie in [0, 16]");
+    if (c.frontier_cap < 0 || c.claims_cap < 0 || c.arena_entries < 0 || c.grid_blocks < 0)
+        return fail(WFST_EINVAL, "capacities must be >= 0");
+    const int P = (g->eps_id >= 0) ? c.eps_iterations : 0;
+
+    const uint64_t Q = c.frontier_cap ? (uint64_t)c.frontier_cap : std::min<uint64_t>(64ull * (uint64_t)c.max_active, 1ull << 28);
+    const uint64_t CC = c.claims_cap ? (uint64_t)c.claims_cap : Q;
+    if (Q < 1 || Q > (1ull << 28)) return fail(WFST_EINVAL, "frontier_cap must lie in [1, 2^28]");
+    if (CC < 1 || CC > (1ull << 28)) return fail(WFST_EINVAL, "claims_cap must lie in [1, 2^28]");
+    const uint64_t maxdeg = std::max<uint32_t>(g->max_class_deg, 1);
+    // a step counts at most claims_cap tokens per pass (main expand + closure
+    // passes), and their arcs must fit the 32-bit slot space of one lane
+    if (CC * (uint64_t)(1 + P) * maxdeg >= (1ull << 32))
+        return fail(WFST_EINVAL, "claims_cap * (1 + eps passes) * (largest out-degree of one arc class) must stay below 2^32 (32-bit slot offsets)");
+    const uint64_t HC = std::max<uint64_t>(next_pow2(2 * CC), 64);
+    uint64_t arena = c.arena_entries ? (uint64_t)c.arena_entries
+                                     : std::max<uint64_t>(1ull << 20, 4ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P));
+    if ((uint64_t)c.max_lanes * arena >= (1ull << 31)) {
+        if (c.arena_entries) return fail(WFST_EINVAL, "max_lanes * arena_entries must stay below 2^31");
+        arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
+    }
+    const uint64_t path_cap = (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
+
+    HIP_TRY(hipSetDevice(g->device));
+    wfst_decoder_s *d = new wfst_decoder_s();
+    d->g = g;
+    g->refs.fetch_add(1);
+    d->cfg = c;
+    d->passes = P;
+    int ncu = 256;
+    {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, g->device) == hipSuccess && prop.multiProcessorCount > 0)
+            ncu = prop.multiProcessorCount;
+    }
+    const long long want = ((long long)c.max_lanes * c.max_active + 255) / 256;
+    d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 8LL * ncu);
+
+    Work &w = d->w;
+    w.sinfo = g->sinfo; w.ilabel = g->ilabel; w.weight = g->weight; w.dest = g->dest;
+    w.olabel = g->olabel; w.arc_src = g->arc_src;
+    w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
+    w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
+    w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
+    w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
+    w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
+    w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC; w.hash_mask = (uint32_t)(HC - 1);
+    w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap;
+    w.res_stride = (uint32_t)(kResHeader + 2 * path_cap);
+
+    const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
+    int r = WFST_OK;
+    auto A = [&](auto **p, size_t n) { if (r == WFST_OK) r = dalloc(p, n, &d->owned, &d->bytes); };
+    A(&d->ctl, L);
+    A(&d->d_desc, 1);
+    A(&d->d_lengths, L);
+    A(&w.lpmax, L * (size_t)c.max_frames);
+    for (int p = 0; p < 2; ++p) {
+        A(&w.tok_state[p], L * Q); A(&w.tok_score[p], L * Q); A(&w.tok_entry[p], L * Q);
+        A(&w.tok_last[p], L * Q); A(&w.tok_off[p], L * Q); A(&w.tok_abeg[p], L * Q);
+        A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S);
+        if (P > 0) A(&w.changed[p], L * CC);
+    }
+    A(&w.hash, L * HC);
+    A(&w.claims, L * CC);
+    if (P > 0) { A(&w.dec, L * CC); A(&w.dec_dest, L * CC); }
+    A(&w.wlog, L * arena);
+    A(&w.res, L * (size_t)w.res_stride);
+    A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
+    if (r != WFST_OK) { delete d; return r; }
+    w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths;
+
+    hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
+    if (e == hipSuccess) e = hipMemset(w.hash, 0, sizeof(HashSlot) * L * HC);
+    for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
+    if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) { delete d; return hip_fail(e, "decoder workspace"); }
+    *out = d;
+    return WFST_OK;
+}
+
+extern "C" int wfst_decoder_destroy(wfst_decoder_t d)
+{
+    delete d;
+    return WFST_OK;
+}
+
+// Queue one whole decode of `steps` frame-loop steps on stream s.
+static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
+{
+    const Work &w = d->w;
+    hipError_t e;
+    if ((e = launch_clear_dirty(w, d->grid, s)) != hipSuccess) return e;
+    if ((e = launch_init(w, d->grid, s)) != hipSuccess) return e;
+    if (d->passes > 0 && (e = launch_closure(w, -1, d->grid, s)) != hipSuccess) return e;
+    if ((e = launch_lpmax(w, d->grid, s)) != hipSuccess) return e;
+    for (int t = 0; t < steps; ++t) {
+        if ((e = launch_step(w, t, d->grid, s)) != hipSuccess) return e;
+        if (d->passes > 0 && (e = launch_closure(w, t, d->grid, s)) != hipSuccess) return e;
+    }
+    return launch_backtrack(w, s);
+}
+
+static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)
+{
+    auto it = d->graphs.find(steps);
+    if (it != d->graphs.end()) { *exec = it->second; return WFST_OK; }
+    hipGraph_t graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(d->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipError_t e = enqueue_decode(d, steps, d->cap_stream);
+    hipError_t e2 = hipStreamEndCapture(d->cap_stream, &graph);
+    if (e != hipSuccess) { if (graph) (void)hipGraphDestroy(graph); return hip_fail(e, "kernel launch during capture"); }
+    if (e2 != hipSuccess) return hip_fail(e2, "hipStreamEndCapture");
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+    d->graphs[steps] = ex;
+    *exec = ex;
+    return WFST_OK;
+}
+
+extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
+                           const int32_t *lengths_host, void *stream, int32_t *out_words, int32_t words_cap,
+                           int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
+                           float *out_scores, int32_t *out_meta)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    const wfst_decoder_config &c = d->cfg;
+    if (B < 1 || B > c.max_lanes) return fail(WFST_EINVAL, "B must lie in [1, max_lanes]");
+    if (T < 0 || T > c.max_frames) return fail(WFST_EINVAL, "T must lie in [0, max_frames]");
+    if (V != d->g->vocab) return fail(WFST_EINVAL, "V differs from the graph's vocab_size");
+    if (!lengths_host || !out_word_lens || !out_arc_lens || !out_scores || !out_meta)
+        return fail(WFST_EINVAL, "an output or lengths pointer is null");
+    if (words_cap < 0 || arcs_cap < 0 || (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs))
+        return fail(WFST_EINVAL, "bad words/arcs buffer");
+    int32_t maxlen = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (lengths_host[b] < 0 || lengths_host[b] > T) return fail(WFST_EINVAL, "lengths must lie in [0, T]");
+        maxlen = std::max(maxlen, lengths_host[b]);
+    }
+    if (maxlen > 0 && !log_prob) return fail(WFST_EINVAL, "log_prob is null");
+
+    std::lock_guard<std::mutex> lock(d->mu);
+    HIP_TRY(hipSetDevice(d->g->device));
+    hipStream_t s = (hipStream_t)stream;
+    const size_t L = (size_t)c.max_lanes;
+    LpDesc *hd = (LpDesc *)d->h_in;
+    hd->base = log_prob;
+    hd->stride_t = V;
+    hd->stride_b = (long long)T * V;
+    hd->B = B;
+    hd->dtype = c.lp_dtype;
+    int32_t *hl = (int32_t *)((char *)d->h_in + sizeof(LpDesc));
+    for (size_t b = 0; b < L; ++b) hl[b] = (int32_t)b < B ? lengths_host[b] : 0;
+    HIP_TRY(hipMemcpyAsync(d->d_desc, hd, sizeof(LpDesc), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(d->d_lengths, hl, 4 * L, hipMemcpyHostToDevice, s));
+
+    const int steps = maxlen + 1;
+    if (c.use_graphs) {
+        int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
+        bucket = std::min(bucket, c.max_frames + 1);
+        hipGraphExec_t ex = nullptr;
+        int rc = graph_for(d, bucket, &ex);
+        if (rc != WFST_OK) return rc;
+        HIP_TRY(hipGraphLaunch(ex, s));
+        d->last_steps = bucket;
+    } else {
+        hipError_t e = enqueue_decode(d, steps, s);
+        if (e != hipSuccess) return hip_fail(e, "kernel launch");
+        d->last_steps = steps;
+    }
+    const size_t rs = d->w.res_stride;
+    HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+
+    d->last_B = B;
+    d->last_len.assign(lengths_host, lengths_host + B);
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t *R = d->h_res + rs * (size_t)b;
+        const int32_t *arcs = R + kResHeader;
+        const int32_t *words = arcs + d->w.path_cap;
+        const int32_t alen = R[kResArcLen], wlen = R[kResWordLen];
+        const int32_t astored = std::min<int32_t>(alen, (int32_t)d->w.path_cap);
+        out_meta[3 * b + 0] = R[kResOk];
+        out_meta[3 * b + 1] = R[kResReached];
+        out_meta[3 * b + 2] = R[kResOverflow];
+        uint32_t sb = (uint32_t)R[kResScore];
+        float sc;
+        std::memcpy(&sc, &sb, 4);
+        out_scores[b] = sc;
+        out_arc_lens[b] = alen;
+        out_word_lens[b] = wlen;
+        if (arcs_cap > 0) std::memcpy(out_arcs + (size_t)b * arcs_cap, arcs, 4 * (size_t)std::min(astored, arcs_cap));
+        if (words_cap > 0) std::memcpy(out_words + (size_t)b * words_cap, words, 4 * (size_t)std::min(wlen, words_cap));
+    }
+    return WFST_OK;
+}
+
+static int fetch_records(wfst_decoder_s *d, std::vector<uint32_t> *rec)
+{
+    const size_t per = (size_t)(d->cfg.max_frames + 2) * kStepFields;
+    rec->resize(per * (size_t)d->cfg.max_lanes);
+    HIP_TRY(hipSetDevice(d->g->device));
+    HIP_TRY(hipMemcpy(rec->data(), d->w.steps, 4 * rec->size(), hipMemcpyDeviceToHost));
+    return WFST_OK;
+}
+
+extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
+{
+    if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
+    std::lock_guard<std::mutex> lock(d->mu);
+    int64_t v[12] = {0};
+    if (d->last_B > 0) {
+        std::vector<uint32_t> rec;
+        int rc = fetch_records(d, &rec);
+        if (rc != WFST_OK) return rc;
+        const size_t per = (size_t)(d->cfg.max_frames + 2);
+        for (int b = 0; b < d->last_B; ++b) {
+            for (size_t r = 0; r < per; ++r) {
+                const uint32_t *x = rec.data() + ((size_t)b * per + r) * kStepFields;
+                v[0] += x[kRecArcs]; v[1] += x[kRecAdmitted]; v[2] += x[kRecDistinct]; v[3] += x[kRecN];
+                v[4] += x[kRecEpsArcs]; v[5] += x[kRecEpsAdmitted]; v[6] += x[kRecEpsDistinct];
+                v[7] += (int64_t)x[kRecEpsNew] + x[kRecEpsReplaced];
+                v[10] = std::max<int64_t>(v[10], x[kRecN]);
+            }
+        }
+        std::vector<LaneCtl> ctl((size_t)d->cfg.max_lanes);
+        HIP_TRY(hipMemcpy(ctl.data(), d->ctl, sizeof(LaneCtl) * ctl.size(), hipMemcpyDeviceToHost));
+        for (int b = 0; b < d->last_B; ++b) v[8] += ctl[(size_t)b].log_cursor;
+    }
+    v[9] = d->last_steps;
+    v[11] = (int64_t)(d->bytes + d->g->bytes);
+    for (int32_t i = 0; i < n && i < 12; ++i) out[i] = v[i];
+    return WFST_OK;
+}
+
+extern "C" int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_t steps_cap)
+{
+    if (!d || !out || steps_cap < 0) return fail(WFST_EINVAL, "bad arguments");
+    std::lock_guard<std::mutex> lock(d->mu);
+    if (lane < 0 || lane >= d->last_B) return fail(WFST_EINVAL, "lane outside the last decode's batch");
+    std::vector<uint32_t> rec;
+    int rc = fetch_records(d, &rec);
+    if (rc != WFST_OK) return rc;
+    const int32_t *R = d->h_res + (size_t)d->w.res_stride * (size_t)lane;
+    const int32_t last = R[7];
+    const size_t per = (size_t)(d->cfg.max_frames + 2);
+    const int32_t nrec = std::min<int32_t>(steps_cap, d->last_len[(size_t)lane] + 2);
+    for (int32_t r = 0; r < nrec; ++r) {
+        const uint32_t *x = rec.data() + ((size_t)lane * per + (size_t)r) * kStepFields;
+        for (int f = 0; f < kStepFields; ++f) out[(size_t)r * kStepFields + f] = x[f];
+        if (r >= 1 && r - 1 > last) out[(size_t)r * kStepFields + kRecPhase] = -1;
+        if (r == 0) out[kRecPhase] = -1;
+    }
+    return nrec;
+}

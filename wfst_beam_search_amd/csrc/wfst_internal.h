@@ -1,0 +1,142 @@
+// Internal layout shared by the host orchestration (wfst_api.cpp) and the
+// gfx950 kernels (wfst_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wfst {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kBlock = 256;         // threads per workgroup of the frame-loop kernels
+constexpr int kMaxLanes = 64;       // one wavefront scans the per-lane table
+constexpr int kMaxProbes = 256;     // linear-probe bound of the recombination hash
+constexpr int kStepFields = 16;     // u32 fields of one per-step record
+constexpr uint16_t kFinalLabel = 0xFFFF;
+
+// Lane status.
+enum : int32_t { kActive = 0, kDone = 1 };
+
+// Step phase of a lane.
+enum : int32_t { kPhNone = -1, kPhReal = 0, kPhFinal = 1, kPhRedirect = 2, kPhDead = 3 };
+
+// Overflow bits (same values as the public WFST_OVF_*).
+enum : uint32_t {
+    kOvfHash = 2, kOvfArena = 4, kOvfClaims = 8, kOvfFrontier = 16, kOvfPath = 32
+};
+
+// Per-step record fields (u32).
+enum : int {
+    kRecN = 0, kRecBeam, kRecMax, kRecArcs, kRecAdmitted, kRecDistinct, kRecEpsArcs,
+    kRecEpsAdmitted, kRecEpsDistinct, kRecEpsNew, kRecEpsReplaced, kRecEpsPasses, kRecPhase
+};
+
+// Per-state arc ranges and upper-bound weights, one 32-byte line per state:
+// arcs [eps_b, emit_b) are epsilon, [emit_b, fin_b) emitting, [fin_b, end) final.
+struct alignas(32) StateInfo {
+    int32_t eps_b, emit_b, fin_b, end;
+    float emit_maxw;   // largest weight over the emitting arcs (-inf if none)
+    float fin_maxw;    // largest weight over the final arcs (-inf if none)
+    int32_t pad0, pad1;
+};
+
+// Recombination hash slot: key = destination state + 1 (0 = empty) and the
+// packed (ordered score << 32 | ~arc) payload resolved by one u64 atomicMax.
+struct alignas(16) HashSlot {
+    uint32_t key;
+    uint32_t pad;
+    unsigned long long payload;
+};
+
+// Per-lane control block (one 128-byte line per lane).
+struct alignas(128) LaneCtl {
+    int32_t T;                 // frames of this lane
+    int32_t status;            // kActive / kDone
+    uint32_t overflow;         // kOvf* bits
+    int32_t reached_final;
+    unsigned long long cnt[2]; // frontier counter by parity: tokens | (arcs of the step's class) << 32
+    float beam[2];             // b_t by step parity (beam[1] = search beam before step 0)
+    uint32_t maxkey[2];        // ordered exact maximum M_t by step parity
+    float cutoff;              // cutoff of the latest real step (closure passes use it)
+    uint32_t nclaims;          // claims of the main expand of the current step
+    uint32_t log_cursor;       // winners-log entries used in this lane's region
+    int32_t final_entry;       // winners-log entry of the result (-1 none)
+    unsigned long long final_key;  // best final candidate key of the final step
+    float final_score;
+    uint32_t nclaims_eps[2];   // claims of closure pass k at [k & 1]
+    uint32_t nchanged[2];      // changed-token list sizes of closure pass k at [k & 1]
+    uint32_t dirty;            // hash table may hold stale slots (claims overflow)
+    int32_t last_step;         // last step this lane ran
+    int32_t phase_final;       // phase code of the lane's last step
+    uint32_t pad[8];
+};
+
+// Device-resident description of the caller's log_prob tensor, rewritten before
+// every decode so that a captured graph stays valid across decodes.
+struct LpDesc {
+    const void *base;
+    long long stride_b;   // elements between lanes
+    long long stride_t;   // elements between frames
+    int32_t B;
+    int32_t dtype;        // 0 f32, 1 f16
+};
+
+// Everything a kernel needs, passed by value.
+struct Work {
+    // graph (read-only)
+    const StateInfo *sinfo;
+    const uint16_t *ilabel;
+    const float *weight;
+    const int32_t *dest;
+    const int32_t *olabel;
+    const int32_t *arc_src;
+    int32_t num_states, num_arcs, start_state, vocab, super_final;
+    int32_t has_eps;
+    // search settings
+    float beam;
+    int32_t min_active, max_active, allow_partial, eps_iterations;
+    int32_t lp_dtype;         // 0 f32, 1 f16
+    // capacities
+    int32_t max_lanes;        // lanes held by the workspace
+    int32_t max_frames;
+    uint32_t frontier_cap;    // Q
+    uint32_t claims_cap;      // CC
+    uint32_t hash_mask;       // HC - 1 (HC power of two)
+    uint32_t arena;           // winners-log entries per lane
+    uint32_t path_cap;        // device path buffer per lane
+    uint32_t res_stride;      // int32 per lane in the result buffer
+    // workspace
+    LaneCtl *ctl;             // [L]
+    const LpDesc *lp;         // device descriptor
+    const int32_t *lengths;   // [L] device copy of the batch lengths
+    float *lpmax;             // [L][max_frames]
+    int32_t *tok_state[2];    // [L][Q] by parity
+    float *tok_score[2];
+    int32_t *tok_entry[2];
+    int32_t *tok_last[2];
+    uint32_t *tok_off[2];     // exclusive arc offset of the token in the step's slot space
+    int32_t *tok_abeg[2];     // first arc of the step's class
+    float *tok_ub[2];         // score + largest weight of the step's class
+    int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
+    HashSlot *hash;           // [L][HC]
+    uint32_t *claims;         // [L][CC]
+    int4 *dec;                // [L][CC] closure decisions {token or -1/-2, score bits, arc, src entry}
+    int32_t *dec_dest;        // [L][CC]
+    uint32_t *changed[2];     // [L][CC] closure change lists by pass parity
+    int2 *wlog;               // [L][arena] winners log {prev entry, arc}
+    int32_t *res;             // [L][res_stride] results
+    uint32_t *steps;          // [L][max_frames + 2][kStepFields]
+};
+
+// Host-side launchers (wfst_kernels.hip).
+hipError_t launch_init(const Work &w, int grid, hipStream_t s);
+hipError_t launch_lpmax(const Work &w, int grid, hipStream_t s);
+hipError_t launch_step(const Work &w, int t, int grid, hipStream_t s);
+hipError_t launch_closure(const Work &w, int t, int grid, hipStream_t s);
+hipError_t launch_backtrack(const Work &w, hipStream_t s);
+hipError_t launch_clear_dirty(const Work &w, int grid, hipStream_t s);
+
+// Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
+enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };
+
+}  // namespace wfst

@@ -1,0 +1,1026 @@
+// gfx950 (CDNA4) kernels of the WFST Viterbi beam search.
+//
+// Semantics: page "GPU WFST Beam-Search Decoder" (OASR docs), sections 1, 3,
+// 5.1-5.5 and 7. Design (ours, for 64-wide wavefronts):
+//  * every frontier token owns a contiguous range of "slots" (its arcs of the
+//    step's class); the ranges of all lanes form one flattened slot space cut
+//    into 64-slot strips, and each wavefront walks a contiguous run of strips
+//    with a forward token cursor resolved by a 6-shuffle search over a
+//    register-held window of 64 token offsets (section 5.2/5.3 problem, wave64
+//    solution);
+//  * pass 1 (k_max) takes the exact per-lane maximum with the per-token upper
+//    bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds in IEEE fp32);
+//  * pass 2 (k_expand) admits end > M - b and recombines per destination in an
+//    open-addressing hash with one u64 atomicMax of (ordered score << 32 | ~arc)
+//    per candidate, so the greatest score wins and, among equal scores, the
+//    smallest arc id; the first claimer of a slot appends it to the claims list;
+//  * pass 3 (k_finalize) compacts the claims into the next frontier: one
+//    64-bit atomicAdd per wavefront allocates token positions and arc offsets
+//    together (tokens in the low half, arcs in the high half), which is the
+//    exclusive degree scan of the next step, done as the frontier is built; the
+//    winners-log entry {source entry, arc} is written and the hash slot cleared;
+//  * epsilon closure passes (expand / resolve / apply) on TLG graphs.
+// All fp32 arithmetic is single operations in the order the page fixes; the
+// file is compiled with -ffp-contract=off.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "wfst_internal.h"
+
+namespace wfst {
+
+constexpr uint32_t kOrdNegInf = 0x007FFFFFu;  // ordered code of -inf
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t f2ord(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;  // -0.0 orders as +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float ord2f(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ unsigned long long cand_key(float score, int32_t arc)
+{
+    return ((unsigned long long)f2ord(score) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)arc);
+}
+
+__device__ __forceinline__ int wlane() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ unsigned long long mask_lt() { return (1ull << wlane()) - 1ull; }
+
+__device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t *total)
+{
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, kWave);
+        if (wlane() >= d) x += y;
+    }
+    *total = __shfl(x, kWave - 1, kWave);
+    return x - v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float lp_at(const float *row, uint32_t i) { return row[i]; }
+__device__ __forceinline__ float lp_at(const __half *row, uint32_t i) { return __half2float(row[i]); }
+
+__device__ __forceinline__ uint32_t hash_state(uint32_t s) { return s * 0x9E3779B1u; }
+
+__device__ __forceinline__ uint32_t *step_rec(const Work &w, int L, int t)
+{
+    return w.steps + ((size_t)L * (size_t)(w.max_frames + 2) + (size_t)(t + 1)) * kStepFields;
+}
+
+// Phase of lane c at step t: real for t < T, final at t == T.
+__device__ __forceinline__ int lane_phase(const LaneCtl &c, int t)
+{
+    if (c.status != kActive) return kPhNone;
+    if (t < c.T) return kPhReal;
+    if (t == c.T) return kPhFinal;
+    return kPhNone;
+}
+
+// Per-workgroup view of the lanes, built by wavefront 0 of every workgroup.
+struct LaneTab {
+    uint32_t base[kMaxLanes + 1];  // exclusive prefix of work units per lane
+    uint32_t n[kMaxLanes];         // items (tokens / claims / sources)
+    uint32_t arcs[kMaxLanes];      // slots of the step
+    int32_t ph[kMaxLanes];
+    int32_t T[kMaxLanes];
+    float f0[kMaxLanes];           // max log-prob of the lane's row (0 on the final step)
+    float f1[kMaxLanes];           // cutoff, or the running max
+};
+
+__device__ __forceinline__ void tab_publish(LaneTab &tab, int nl, uint32_t units)
+{
+    uint32_t tot;
+    uint32_t ex = wave_excl_sum(units, &tot);
+    const int L = (int)threadIdx.x;
+    if (L < nl) tab.base[L] = ex;
+    if (L == 0) tab.base[nl] = tot;
+}
+
+__device__ __forceinline__ int find_lane(const uint32_t *base, int nl, uint32_t s)
+{
+    int lo = 0, hi = nl - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (base[mid] <= s) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Next-step class of a token at state s: [abeg, abeg + deg) and its upper bound.
+__device__ __forceinline__ void class_of(const StateInfo &si, bool final_step, float score,
+                                         int32_t *abeg, uint32_t *deg, float *ub)
+{
+    if (final_step) {
+        *abeg = si.fin_b; *deg = (uint32_t)(si.end - si.fin_b); *ub = score + si.fin_maxw;
+    } else {
+        *abeg = si.emit_b; *deg = (uint32_t)(si.fin_b - si.emit_b); *ub = score + si.emit_maxw;
+    }
+}
+
+// ------------------------------------------------------------ hash insert
+// Returns the slot of `dest` in the lane's table (claiming it if empty) or -1
+// when the probe bound is exceeded. *first is set for the claiming thread.
+__device__ __forceinline__ int hash_claim(HashSlot *tbl, uint32_t mask, int32_t dest, bool *first)
+{
+    const uint32_t want = (uint32_t)dest + 1u;
+    uint32_t h = hash_state((uint32_t)dest) & mask;
+    *first = false;
+    for (int probe = 0; probe < kMaxProbes; ++probe) {
+        uint32_t k = __hip_atomic_load(&tbl[h].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (k == want) return (int)h;
+        if (k == 0u) {
+            uint32_t old = atomicCAS(&tbl[h].key, 0u, want);
+            if (old == 0u) { *first = true; return (int)h; }
+            if (old == want) return (int)h;
+        }
+        h = (h + 1u) & mask;
+    }
+    return -1;
+}
+
+__device__ __forceinline__ void payload_max(unsigned long long *p, unsigned long long key)
+{
+    unsigned long long cur = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (key > cur) atomicMax(p, key);
+}
+
+// Wave-aggregated append of the claiming threads' slots to a claims list.
+__device__ __forceinline__ void append_claims(const Work &w, int L, uint32_t *counter, bool first,
+                                              int slot)
+{
+    unsigned long long m = __ballot(first);
+    if (m == 0ull) return;
+    const int leader = __ffsll((long long)m) - 1;
+    uint32_t base = 0;
+    if (wlane() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(base, leader, kWave);
+    if (first) {
+        uint32_t idx = base + (uint32_t)__popcll(m & mask_lt());
+        if (idx < w.claims_cap) w.claims[(size_t)L * w.claims_cap + idx] = (uint32_t)slot;
+    }
+}
+
+// ---------------------------------------------------------------- k_clear
+// Clears the per-step records and the hash tables of lanes whose claims list
+// overflowed in an earlier decode (the targeted clear cannot see those slots).
+__global__ __launch_bounds__(kBlock) void k_clear(Work w)
+{
+    const size_t nrec = (size_t)w.max_lanes * (size_t)(w.max_frames + 2) * kStepFields;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nrec; i += stride) w.steps[i] = 0u;
+    const size_t hc = (size_t)w.hash_mask + 1;
+    for (int L = 0; L < w.max_lanes; ++L) {
+        if (!w.ctl[L].dirty) continue;
+        HashSlot *tbl = w.hash + (size_t)L * hc;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < hc; i += stride) {
+            tbl[i].key = 0u;
+            tbl[i].payload = 0ull;
+        }
+    }
+}
+
+// ----------------------------------------------------------------- k_init
+// Lane control blocks and the start token (page section 2: InitKernel resets all
+// state, so a decode is idempotent).
+__global__ __launch_bounds__(kWave) void k_init(Work w)
+{
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    const LpDesc d = *w.lp;
+    LaneCtl &c = w.ctl[L];
+    const bool on = L < d.B;
+    const int T = on ? w.lengths[L] : 0;
+    c.T = T;
+    c.status = on ? kActive : kDone;
+    c.overflow = 0u;
+    c.reached_final = 0;
+    c.beam[0] = w.beam;
+    c.beam[1] = w.beam;
+    c.maxkey[0] = kOrdNegInf;
+    c.maxkey[1] = kOrdNegInf;
+    c.cutoff = 0.0f - w.beam;
+    c.nclaims = 0u;
+    c.log_cursor = 0u;
+    c.final_entry = -1;
+    c.final_key = 0ull;
+    c.final_score = -__builtin_inff();
+    c.nclaims_eps[0] = 0u;
+    c.nclaims_eps[1] = 0u;
+    c.nchanged[0] = 0u;
+    c.nchanged[1] = 0u;
+    c.dirty = 0u;
+    c.last_step = -1;
+    c.phase_final = kPhNone;
+    c.cnt[1] = 0ull;
+    if (!on) { c.cnt[0] = 0ull; return; }
+    const int32_t s = w.start_state;
+    const StateInfo si = w.sinfo[s];
+    int32_t abeg; uint32_t deg; float ub;
+    class_of(si, T == 0, 0.0f, &abeg, &deg, &ub);
+    const size_t q = (size_t)L * w.frontier_cap;
+    w.tok_state[0][q] = s;
+    w.tok_score[0][q] = 0.0f;
+    w.tok_entry[0][q] = -1;
+    w.tok_last[0][q] = -1;
+    w.tok_off[0][q] = 0u;
+    w.tok_abeg[0][q] = abeg;
+    w.tok_ub[0][q] = ub;
+    w.pos[0][(size_t)L * w.num_states + s] = 0;
+    c.cnt[0] = 1ull | ((unsigned long long)deg << 32);
+}
+
+// ---------------------------------------------------------------- k_lpmax
+// Max log-prob of every (lane, frame) row, for the upper-bound skip.
+template <typename LPT>
+__global__ __launch_bounds__(kBlock) void k_lpmax(Work w)
+{
+    const LpDesc d = *w.lp;
+    const int wpb = kBlock / kWave;
+    const long long rows = (long long)d.B * w.max_frames;
+    for (long long r = (long long)blockIdx.x * wpb + threadIdx.x / kWave; r < rows;
+         r += (long long)gridDim.x * wpb) {
+        const int L = (int)(r / w.max_frames), t = (int)(r % w.max_frames);
+        if (t >= w.lengths[L]) continue;
+        const LPT *row = (const LPT *)d.base + (long long)L * d.stride_b + (long long)t * d.stride_t;
+        float m = -__builtin_inff();
+        for (int v = wlane(); v < w.vocab; v += kWave) m = fmaxf(m, lp_at(row, (uint32_t)v));
+        m = wave_max(m);
+        if (wlane() == 0) w.lpmax[(size_t)L * w.max_frames + t] = m;
+    }
+}
+
+// ------------------------------------------------- slot walk (max / expand)
+
+enum { kModeMax = 0, kModeExpand = 1 };
+
+template <int MODE, typename LPT>
+__device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d)
+{
+    const int p = t & 1;
+    const int nl = w.max_lanes;
+    const uint32_t total = tab.base[nl];
+    if (total == 0u) return;
+    const int lane = wlane();
+    const uint32_t wpb = kBlock / kWave;
+    const uint32_t nwaves = gridDim.x * wpb;
+    const uint32_t wid = blockIdx.x * wpb + threadIdx.x / kWave;
+    uint32_t s = (uint32_t)(((unsigned long long)total * wid) / nwaves);
+    const uint32_t s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
+    const uint32_t Q = w.frontier_cap;
+
+    while (s < s_end) {
+        const int L = find_lane(tab.base, nl, s);
+        const uint32_t seg_end = min(s_end, tab.base[L + 1]);
+        const uint32_t n = tab.n[L], arcs = tab.arcs[L];
+        const int ph = tab.ph[L];
+        const size_t qo = (size_t)L * Q;
+        const uint32_t *off = w.tok_off[p] + qo;
+        const int32_t *abeg = w.tok_abeg[p] + qo;
+        const float *score = w.tok_score[p] + qo;
+        const float *ubv = w.tok_ub[p] + qo;
+        const LPT *row = (ph == kPhReal)
+            ? (const LPT *)d.base + (long long)L * d.stride_b + (long long)t * d.stride_t : nullptr;
+        const float lpm = tab.f0[L];
+        const float cut = tab.f1[L];
+        LaneCtl &c = w.ctl[L];
+        uint32_t j0 = (s - tab.base[L]) * (uint32_t)kWave;
+
+        // first token of the run: largest i with off[i] <= j0
+        uint32_t cur;
+        {
+            uint32_t lo = 0, hi = n - 1;
+            while (lo < hi) {
+                uint32_t mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= j0) lo = mid; else hi = mid - 1;
+            }
+            cur = lo;
+        }
+        float run = -__builtin_inff();
+        if (MODE == kModeMax)
+            run = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        uint32_t admitted = 0;
+        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
+
+        for (; s < seg_end; ++s, j0 += kWave) {
+            const uint32_t j = j0 + (uint32_t)lane;
+            const bool valid = j < arcs;
+            bool resolved = !valid;
+            uint32_t tok = cur, toff = 0;
+            int32_t ab = 0;
+            float sc = 0.0f, ub = 0.0f;
+            uint32_t wb = cur;
+            for (;;) {
+                const uint32_t idx = wb + (uint32_t)lane;
+                const bool in = idx < n;
+                const uint32_t o = in ? off[idx] : 0xFFFFFFFFu;
+                const int32_t ab_l = in ? abeg[idx] : 0;
+                const float sc_l = in ? score[idx] : 0.0f;
+                const float ub_l = in ? ubv[idx] : 0.0f;
+                const uint32_t o_next = (wb + kWave < n) ? off[wb + kWave] : 0xFFFFFFFFu;
+                int i = 0;
+#pragma unroll
+                for (int st = 32; st >= 1; st >>= 1) {
+                    const uint32_t v = __shfl(o, i + st, kWave);
+                    if (v <= j) i += st;
+                }
+                const uint32_t g_o = __shfl(o, i, kWave);
+                const int32_t g_ab = __shfl(ab_l, i, kWave);
+                const float g_sc = __shfl(sc_l, i, kWave);
+                const float g_ub = __shfl(ub_l, i, kWave);
+                if (!resolved && (i < kWave - 1 || j < o_next)) {
+                    tok = wb + (uint32_t)i; toff = g_o; ab = g_ab; sc = g_sc; ub = g_ub;
+                    resolved = true;
+                }
+                if (__ballot(!resolved) == 0ull) break;
+                wb += kWave;
+            }
+            cur = __shfl(tok, kWave - 1, kWave);
+            const uint32_t arc = (uint32_t)ab + (j - toff);
+            const bool live = valid && tok < n && arc < (uint32_t)w.num_arcs;
+
+            if (MODE == kModeMax) {
+                float m = -__builtin_inff();
+                if (live && ub + lpm > run) {
+                    float e = sc + w.weight[arc];
+                    if (row) e = e + lp_at(row, w.ilabel[arc]);
+                    m = e;
+                }
+                m = wave_max(m);
+                if (m > run) {
+                    if (lane == 0) atomicMax(&c.maxkey[p], f2ord(m));
+                    run = m;
+                }
+                run = fmaxf(run, ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)));
+            } else {
+                bool first = false;
+                int slot = -1;
+                if (live && ub + lpm > cut) {
+                    float e = sc + w.weight[arc];
+                    if (row) e = e + lp_at(row, w.ilabel[arc]);
+                    if (e > cut) {
+                        ++admitted;
+                        const unsigned long long key = cand_key(e, (int32_t)arc);
+                        if (ph == kPhReal) {
+                            const int32_t dst = w.dest[arc];
+                            slot = hash_claim(tbl, w.hash_mask, dst, &first);
+                            if (slot < 0) atomicOr(&c.overflow, kOvfHash);
+                            else payload_max(&tbl[slot].payload, key);
+                        } else {
+                            payload_max(&c.final_key, key);
+                        }
+                    }
+                }
+                append_claims(w, L, &c.nclaims, first, slot);
+            }
+        }
+        if (MODE == kModeExpand) {
+            const uint32_t a = wave_sum(admitted);
+            if (lane == 0 && a) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
+        }
+    }
+}
+
+// Per-lane table for the two slot passes of step t.
+template <int MODE>
+__device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t)
+{
+    if (threadIdx.x >= kWave) return;
+    const int L = (int)threadIdx.x;
+    const int p = t & 1;
+    uint32_t units = 0;
+    if (L < w.max_lanes) {
+        const LaneCtl &c = w.ctl[L];
+        int ph = lane_phase(c, t);
+        const unsigned long long cn = c.cnt[p];
+        const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
+        if (ph != kPhNone && (n > w.frontier_cap || c.log_cursor > w.arena)) ph = kPhNone;
+        float lpm = 0.0f, f1 = 0.0f;
+        if (ph == kPhReal) lpm = w.lpmax[(size_t)L * w.max_frames + t];
+        if (MODE == kModeExpand && ph != kPhNone) f1 = ord2f(c.maxkey[p]) - c.beam[p];
+        if (ph != kPhNone && n > 0u && arcs > 0u) units = (arcs + kWave - 1) / kWave;
+        tab.n[L] = n;
+        tab.arcs[L] = arcs;
+        tab.ph[L] = ph;
+        tab.T[L] = c.T;
+        tab.f0[L] = lpm;
+        tab.f1[L] = f1;
+    }
+    tab_publish(tab, w.max_lanes, units);
+}
+
+// Step bookkeeping done once per step by thread L of workgroup 0 of k_max:
+// retire overflowed / dead lanes, the dynamic beam, the redirect, resets.
+__device__ void step_begin_lane(const Work &w, int t, int L)
+{
+    LaneCtl &c = w.ctl[L];
+    const int ph = lane_phase(c, t);
+    if (ph == kPhNone) return;
+    const int p = t & 1;
+    const unsigned long long cn = c.cnt[p];
+    const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
+    uint32_t *rec = step_rec(w, L, t);
+    c.last_step = t;
+    rec[kRecN] = n;
+    rec[kRecArcs] = arcs;
+    if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    if (c.log_cursor > w.arena) { c.overflow |= kOvfArena; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    // dynamic beam (page section 3), every operation one fp32 rounding
+    float b;
+    if (ph == kPhFinal) {
+        b = 1e10f;
+    } else {
+        int mina = w.min_active;
+        if (c.T - t <= 5 && w.max_active / 2 > mina) mina = w.max_active / 2;
+        const float bp = c.beam[p ^ 1];
+        if ((long long)n > (long long)w.max_active) {
+            b = __fmul_rn(fminf(bp, w.beam), 0.8f);
+        } else if ((long long)n < (long long)mina) {
+            b = __fmul_rn(fmaxf(bp, w.beam), 1.25f);
+        } else {
+            b = __fadd_rn(__fmul_rn(0.8f, bp), __fmul_rn(0.2f, w.beam));
+        }
+    }
+    c.beam[p] = b;
+    rec[kRecBeam] = __float_as_uint(b);
+    rec[kRecPhase] = ph;
+    c.phase_final = ph;
+    c.nclaims = 0u;
+    c.cnt[p ^ 1] = 0ull;
+    c.maxkey[p ^ 1] = kOrdNegInf;
+    if (arcs == 0u) {
+        if (ph == kPhReal) {
+            c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead;
+        } else {
+            if (w.allow_partial) {
+                // redirect: each token offers a virtual weight-0 arc num_arcs + state
+                const size_t qo = (size_t)L * w.frontier_cap;
+                unsigned long long bk = 0ull;
+                uint32_t bi = 0;
+                for (uint32_t i = 0; i < n; ++i) {
+                    const float e = w.tok_score[p][qo + i] + 0.0f;
+                    const unsigned long long k =
+                        cand_key(e, (int32_t)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + i]));
+                    if (i == 0 || k > bk) { bk = k; bi = i; }
+                }
+                c.final_entry = w.tok_entry[p][qo + bi];
+                c.final_score = w.tok_score[p][qo + bi] + 0.0f;
+                c.reached_final = 0;
+                rec[kRecPhase] = kPhRedirect;
+                c.phase_final = kPhRedirect;
+            }
+            c.status = kDone;
+        }
+    }
+}
+
+template <typename LPT>
+__global__ __launch_bounds__(kBlock) void k_max(Work w, int t)
+{
+    __shared__ LaneTab tab;
+    slot_prologue<kModeMax>(w, tab, t);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
+    const LpDesc d = *w.lp;
+    walk_slots<kModeMax, LPT>(w, tab, t, d);
+}
+
+template <typename LPT>
+__global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
+{
+    __shared__ LaneTab tab;
+    slot_prologue<kModeExpand>(w, tab, t);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        if (tab.ph[L] != kPhNone) {
+            LaneCtl &c = w.ctl[L];
+            const int p = t & 1;
+            uint32_t *rec = step_rec(w, L, t);
+            rec[kRecMax] = __float_as_uint(ord2f(c.maxkey[p]));
+            if (tab.ph[L] == kPhReal) c.cutoff = tab.f1[L];
+        }
+    }
+    const LpDesc d = *w.lp;
+    walk_slots<kModeExpand, LPT>(w, tab, t, d);
+}
+
+// -------------------------------------------------------------- k_finalize
+
+__global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
+{
+    __shared__ LaneTab tab;
+    const int p = t & 1, np = p ^ 1;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            const int ph = lane_phase(c, t);
+            const uint32_t nc = c.nclaims;
+            if (ph == kPhReal && nc <= w.claims_cap && c.log_cursor <= w.arena &&
+                (uint32_t)c.cnt[p] <= w.frontier_cap)
+                units = (nc + kWave - 1) / kWave;
+            tab.n[L] = nc;
+            tab.ph[L] = ph;
+            tab.T[L] = c.T;
+            tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        LaneCtl &c = w.ctl[L];
+        const int ph = tab.ph[L];
+        if (ph == kPhReal) {
+            step_rec(w, L, t)[kRecDistinct] = tab.n[L];
+            if (tab.n[L] > w.claims_cap) {
+                c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
+            }
+            c.nclaims_eps[1] = 0u;
+        } else if (ph == kPhFinal) {
+            const unsigned long long fk = c.final_key;
+            step_rec(w, L, t)[kRecDistinct] = fk ? 1u : 0u;
+            if (fk) {
+                const float end = ord2f((uint32_t)(fk >> 32));
+                const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)fk);
+                const int32_t src = w.arc_src[arc];
+                const int32_t stok = w.pos[p][(size_t)L * w.num_states + src];
+                const int32_t esrc = (uint32_t)stok < w.frontier_cap
+                    ? w.tok_entry[p][(size_t)L * w.frontier_cap + stok] : -1;
+                const uint32_t le = c.log_cursor;
+                if (le < w.arena) {
+                    const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
+                    w.wlog[e] = make_int2(esrc, arc);
+                    c.log_cursor = le + 1u;
+                    c.final_entry = e;
+                    c.final_score = end;
+                    c.reached_final = 1;
+                } else {
+                    c.overflow |= kOvfArena;
+                }
+            }
+            c.status = kDone;
+        }
+    }
+
+    const int nl = w.max_lanes;
+    const uint32_t total = tab.base[nl];
+    const uint32_t wpb = kBlock / kWave;
+    const uint32_t nwaves = gridDim.x * wpb;
+    const int lane = wlane();
+    const uint32_t Q = w.frontier_cap;
+    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t nc = tab.n[L];
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const bool valid = i < nc;
+        const float cutoff = tab.f1[L];
+        const bool next_final = (t + 1 == tab.T[L]);
+        LaneCtl &c = w.ctl[L];
+        bool keep = false;
+        int32_t dst = 0, arc = 0, esrc = -1, abeg = 0;
+        uint32_t deg = 0;
+        float end = 0.0f, ub = 0.0f;
+        if (valid) {
+            const uint32_t h = w.claims[(size_t)L * w.claims_cap + i];
+            HashSlot *sl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1) + h;
+            const uint32_t key = sl->key;
+            const unsigned long long K = sl->payload;
+            sl->key = 0u;
+            sl->payload = 0ull;
+            dst = (int32_t)key - 1;
+            end = ord2f((uint32_t)(K >> 32));
+            arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
+            keep = (K != 0ull) && key != 0u && (end > cutoff);
+            if (keep) {
+                const int32_t src = w.arc_src[arc];
+                const int32_t stok = w.pos[p][(size_t)L * w.num_states + src];
+                keep = (uint32_t)stok < Q;
+                if (keep) {
+                    esrc = w.tok_entry[p][(size_t)L * Q + stok];
+                    class_of(w.sinfo[dst], next_final, end, &abeg, &deg, &ub);
+                }
+            }
+        }
+        const unsigned long long m = __ballot(keep);
+        if (m == 0ull) continue;
+        const uint32_t nkeep = (uint32_t)__popcll(m);
+        const uint32_t rank = (uint32_t)__popcll(m & mask_lt());
+        uint32_t dsum;
+        const uint32_t dpre = wave_excl_sum(keep ? deg : 0u, &dsum);
+        const int leader = __ffsll((long long)m) - 1;
+        unsigned long long old = 0ull;
+        uint32_t lb = 0u;
+        if (lane == leader) {
+            old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
+            lb = atomicAdd(&c.log_cursor, nkeep);
+        }
+        old = __shfl(old, leader, kWave);
+        lb = __shfl(lb, leader, kWave);
+        if (keep) {
+            const uint32_t pi = (uint32_t)old + rank;
+            const uint32_t le = lb + rank;
+            if (pi < Q && le < w.arena) {
+                const size_t q = (size_t)L * Q + pi;
+                const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
+                w.wlog[e] = make_int2(esrc, arc);
+                w.tok_state[np][q] = dst;
+                w.tok_score[np][q] = end;
+                w.tok_entry[np][q] = e;
+                w.tok_last[np][q] = arc;
+                w.tok_off[np][q] = (uint32_t)(old >> 32) + dpre;
+                w.tok_abeg[np][q] = abeg;
+                w.tok_ub[np][q] = ub;
+                w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------- epsilon closure
+// Pass k of the closure that follows step t (t = -1: the start frontier). The
+// frontier being closed has parity fp = (t + 1) & 1 and feeds step t + 1.
+
+// A lane whose winners log or frontier overflowed holds tokens that were
+// counted but never written; it is skipped until the next step retires it.
+__device__ __forceinline__ bool closure_lane(const Work &w, const LaneCtl &c, int t)
+{
+    return c.status == kActive && (t < 0 || t < c.T) && c.log_cursor <= w.arena;
+}
+
+__global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
+{
+    __shared__ LaneTab tab;
+    const int fp = (t + 1) & 1;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            uint32_t ns = 0;
+            if (closure_lane(w, c, t)) {
+                const uint32_t n = (uint32_t)c.cnt[fp];
+                if (n <= w.frontier_cap) ns = (k == 1) ? n : c.nchanged[k & 1];
+            }
+            units = (ns + kWave - 1) / kWave;
+            tab.n[L] = ns;
+            tab.f1[L] = c.cutoff;
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
+    }
+    const int nl = w.max_lanes;
+    const uint32_t total = tab.base[nl];
+    const uint32_t wpb = kBlock / kWave;
+    const uint32_t nwaves = gridDim.x * wpb;
+    const int lane = wlane();
+    const uint32_t Q = w.frontier_cap;
+    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const float cutoff = tab.f1[L];
+        LaneCtl &c = w.ctl[L];
+        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
+        uint32_t n_arcs = 0, n_adm = 0;
+        const uint32_t tok = (i < tab.n[L])
+            ? ((k == 1) ? i : w.changed[k & 1][(size_t)L * w.claims_cap + i]) : 0xFFFFFFFFu;
+        if (tok < Q) {
+            const size_t q = (size_t)L * Q + tok;
+            const int32_t s = w.tok_state[fp][q];
+            const float sc = w.tok_score[fp][q];
+            const StateInfo si = w.sinfo[s];
+            for (int32_t a = si.eps_b; a < si.emit_b; ++a) {
+                const float e = sc + w.weight[a];
+                ++n_arcs;
+                if (e > cutoff) {
+                    ++n_adm;
+                    bool first = false;
+                    const int slot = hash_claim(tbl, w.hash_mask, w.dest[a], &first);
+                    if (slot < 0) {
+                        atomicOr(&c.overflow, kOvfHash);
+                    } else {
+                        payload_max(&tbl[slot].payload, cand_key(e, a));
+                        if (first) {
+                            const uint32_t idx = atomicAdd(&c.nclaims_eps[k & 1], 1u);
+                            if (idx < w.claims_cap) w.claims[(size_t)L * w.claims_cap + idx] = (uint32_t)slot;
+                        }
+                    }
+                }
+            }
+        }
+        const uint32_t sa = wave_sum(n_arcs), sd = wave_sum(n_adm);
+        if (lane == 0 && sa) {
+            uint32_t *rec = step_rec(w, L, t);
+            atomicAdd(rec + kRecEpsArcs, sa);
+            if (sd) atomicAdd(rec + kRecEpsAdmitted, sd);
+        }
+    }
+}
+
+// Decides, per claimed destination, append / replace / nothing (reads only).
+__global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
+{
+    __shared__ LaneTab tab;
+    const int fp = (t + 1) & 1;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            uint32_t nc = 0;
+            const uint32_t n = (uint32_t)c.cnt[fp];
+            if (closure_lane(w, c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
+            if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
+            tab.n[L] = nc;
+            tab.arcs[L] = n;
+            tab.f1[L] = c.cutoff;
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        LaneCtl &c = w.ctl[L];
+        if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsDistinct] += tab.n[L];
+        if (tab.n[L] > w.claims_cap) {
+            c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
+        }
+        c.nchanged[(k + 1) & 1] = 0u;
+    }
+    const int nl = w.max_lanes;
+    const uint32_t total = tab.base[nl];
+    const uint32_t wpb = kBlock / kWave;
+    const uint32_t nwaves = gridDim.x * wpb;
+    const uint32_t Q = w.frontier_cap;
+    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+        const int L = (int)find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (i >= tab.n[L]) continue;
+        const size_t ci = (size_t)L * w.claims_cap + i;
+        const uint32_t h = w.claims[ci];
+        HashSlot *sl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1) + h;
+        const uint32_t key = sl->key;
+        const unsigned long long K = sl->payload;
+        sl->key = 0u;
+        sl->payload = 0ull;
+        const int32_t dst = (int32_t)key - 1;
+        const float end = ord2f((uint32_t)(K >> 32));
+        const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
+        int32_t code = -2;
+        int32_t esrc = -1;
+        if (K != 0ull && key != 0u && end > tab.f1[L]) {
+            const int32_t src = w.arc_src[arc];
+            const int32_t stok = w.pos[fp][(size_t)L * w.num_states + src];
+            esrc = (uint32_t)stok < Q ? w.tok_entry[fp][(size_t)L * Q + stok] : -1;
+            const int32_t pd = w.pos[fp][(size_t)L * w.num_states + dst];
+            const bool exists = (uint32_t)pd < tab.arcs[L] && w.tok_state[fp][(size_t)L * Q + pd] == dst;
+            if (!exists) {
+                code = -1;
+            } else {
+                const size_t q = (size_t)L * Q + pd;
+                if (K > cand_key(w.tok_score[fp][q], w.tok_last[fp][q])) code = pd;
+            }
+        }
+        w.dec[ci] = make_int4(code, (int)__float_as_uint(end), arc, esrc);
+        w.dec_dest[ci] = dst;
+    }
+}
+
+// Applies the decisions: fresh winners-log entries, appended tokens (with their
+// next-step class and arc offsets), replaced tokens, the next pass's sources.
+__global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
+{
+    __shared__ LaneTab tab;
+    const int fp = (t + 1) & 1;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            uint32_t nc = 0;
+            const uint32_t n = (uint32_t)c.cnt[fp];
+            if (closure_lane(w, c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
+            if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
+            tab.n[L] = nc;
+            tab.T[L] = c.T;
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) w.ctl[threadIdx.x].nclaims_eps[(k + 1) & 1] = 0u;
+    const int nl = w.max_lanes;
+    const uint32_t total = tab.base[nl];
+    const uint32_t wpb = kBlock / kWave;
+    const uint32_t nwaves = gridDim.x * wpb;
+    const int lane = wlane();
+    const uint32_t Q = w.frontier_cap;
+    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+        const int L = (int)find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const bool valid = i < tab.n[L];
+        const bool next_final = (t + 1 == tab.T[L]);
+        LaneCtl &c = w.ctl[L];
+        int4 dd = make_int4(-2, 0, 0, -1);
+        int32_t dst = 0;
+        if (valid) {
+            const size_t ci = (size_t)L * w.claims_cap + i;
+            dd = w.dec[ci];
+            dst = w.dec_dest[ci];
+        }
+        const bool any = dd.x != -2;
+        const bool isnew = dd.x == -1;
+        const float end = __uint_as_float((uint32_t)dd.y);
+        int32_t abeg = 0;
+        uint32_t deg = 0;
+        float ub = 0.0f;
+        if (any) class_of(w.sinfo[dst], next_final, end, &abeg, &deg, &ub);
+        const unsigned long long ma = __ballot(any);
+        if (ma == 0ull) continue;
+        const unsigned long long mn = __ballot(isnew);
+        const int leader = __ffsll((long long)ma) - 1;
+        uint32_t dsum;
+        const uint32_t dpre = wave_excl_sum(isnew ? deg : 0u, &dsum);
+        unsigned long long old = 0ull;
+        uint32_t lb = 0u, cb = 0u;
+        if (lane == leader) {
+            lb = atomicAdd(&c.log_cursor, (uint32_t)__popcll(ma));
+            cb = atomicAdd(&c.nchanged[(k + 1) & 1], (uint32_t)__popcll(ma));
+            if (mn) old = atomicAdd(&c.cnt[fp], (unsigned long long)__popcll(mn) | ((unsigned long long)dsum << 32));
+            uint32_t *rec = step_rec(w, L, t);
+            if (mn) atomicAdd(rec + kRecEpsNew, (uint32_t)__popcll(mn));
+            if (ma & ~mn) atomicAdd(rec + kRecEpsReplaced, (uint32_t)__popcll(ma & ~mn));
+        }
+        old = __shfl(old, leader, kWave);
+        lb = __shfl(lb, leader, kWave);
+        cb = __shfl(cb, leader, kWave);
+        if (!any) continue;
+        const uint32_t ra = (uint32_t)__popcll(ma & mask_lt());
+        const uint32_t le = lb + ra;
+        if (le >= w.arena) continue;   // the next step retires the lane (arena bit)
+        const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
+        w.wlog[e] = make_int2(dd.w, dd.z);
+        uint32_t pi;
+        if (isnew) {
+            pi = (uint32_t)old + (uint32_t)__popcll(mn & mask_lt());
+            if (pi >= Q) continue;     // the next step retires the lane (frontier bit)
+            const size_t q = (size_t)L * Q + pi;
+            w.tok_state[fp][q] = dst;
+            w.tok_off[fp][q] = (uint32_t)(old >> 32) + dpre;
+            w.tok_abeg[fp][q] = abeg;
+            w.pos[fp][(size_t)L * w.num_states + dst] = (int32_t)pi;
+        } else {
+            pi = (uint32_t)dd.x;
+        }
+        const size_t q = (size_t)L * Q + pi;
+        w.tok_score[fp][q] = end;
+        w.tok_entry[fp][q] = e;
+        w.tok_last[fp][q] = dd.z;
+        w.tok_ub[fp][q] = ub;
+        const uint32_t ci = cb + ra;
+        if (ci < w.claims_cap) w.changed[(k + 1) & 1][(size_t)L * w.claims_cap + ci] = pi;
+    }
+}
+
+// -------------------------------------------------------------- k_backtrack
+// One wavefront per lane: lane 0 walks the winners chain from the result entry
+// (newest arc first), then the wavefront reverses it in place and gathers the
+// word ids (page section 7).
+__global__ __launch_bounds__(kWave) void k_backtrack(Work w)
+{
+    const int L = (int)blockIdx.x;
+    const LpDesc d = *w.lp;
+    if (L >= d.B) return;
+    const LaneCtl &c = w.ctl[L];
+    int32_t *R = w.res + (size_t)L * w.res_stride;
+    int32_t *arcs = R + kResHeader;
+    int32_t *words = arcs + w.path_cap;
+    const int lane = wlane();
+    uint32_t len = 0;
+    uint32_t ovf = c.overflow;
+    const bool has_path = c.final_entry >= 0;
+    if (lane == 0 && has_path) {
+        const long long limit = (long long)w.max_lanes * w.arena;
+        int32_t e = c.final_entry;
+        while (e >= 0 && e < limit) {
+            const int2 r = w.wlog[e];
+            if (len < w.path_cap) arcs[len] = r.y;
+            ++len;
+            e = r.x;
+            if (len > (uint32_t)w.arena) break;
+        }
+        if (len > w.path_cap) ovf |= kOvfPath;
+    }
+    len = __shfl(len, 0, kWave);
+    ovf = __shfl(ovf, 0, kWave);
+    const uint32_t ns = min(len, w.path_cap);
+    __syncthreads();
+    for (uint32_t i = (uint32_t)lane; i < ns / 2; i += kWave) {
+        const int32_t a = arcs[i], b = arcs[ns - 1 - i];
+        arcs[i] = b;
+        arcs[ns - 1 - i] = a;
+    }
+    __syncthreads();
+    uint32_t nw = 0;
+    for (uint32_t i0 = 0; i0 < ns; i0 += kWave) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        int32_t ol = 0;
+        if (i < ns) ol = w.olabel[arcs[i]];
+        const unsigned long long m = __ballot(ol != 0);
+        if (ol != 0) words[nw + (uint32_t)__popcll(m & mask_lt())] = ol;
+        nw += (uint32_t)__popcll(m);
+    }
+    if (lane == 0) {
+        R[kResOk] = ovf == 0u ? 1 : 0;
+        R[kResReached] = c.reached_final;
+        R[kResOverflow] = (int32_t)ovf;
+        R[kResArcLen] = (int32_t)len;
+        R[kResWordLen] = (int32_t)nw;
+        R[kResScore] = (int32_t)__float_as_uint(has_path ? c.final_score : -__builtin_inff());
+        R[6] = c.phase_final;
+        R[7] = c.last_step;
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_clear_dirty(const Work &w, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_clear, dim3(grid), dim3(kBlock), 0, s, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_init(const Work &w, int grid, hipStream_t s)
+{
+    (void)grid;
+    hipLaunchKernelGGL(k_init, dim3(1), dim3(kWave), 0, s, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_lpmax(const Work &w, int grid, hipStream_t s)
+{
+    if (w.lp_dtype == 1) hipLaunchKernelGGL(k_lpmax<__half>, dim3(grid), dim3(kBlock), 0, s, w);
+    else hipLaunchKernelGGL(k_lpmax<float>, dim3(grid), dim3(kBlock), 0, s, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const Work &w, int t, int grid, hipStream_t s)
+{
+    if (w.lp_dtype == 1) {
+        hipLaunchKernelGGL(k_max<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        hipLaunchKernelGGL(k_expand<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
+    } else {
+        hipLaunchKernelGGL(k_max<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        hipLaunchKernelGGL(k_expand<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+    }
+    hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kBlock), 0, s, w, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_closure(const Work &w, int t, int grid, hipStream_t s)
+{
+    for (int k = 1; k <= w.eps_iterations; ++k) {
+        hipLaunchKernelGGL(k_eps_expand, dim3(grid), dim3(kBlock), 0, s, w, t, k);
+        hipLaunchKernelGGL(k_eps_resolve, dim3(grid), dim3(kBlock), 0, s, w, t, k);
+        hipLaunchKernelGGL(k_eps_apply, dim3(grid), dim3(kBlock), 0, s, w, t, k);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_backtrack(const Work &w, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_backtrack, dim3(w.max_lanes), dim3(kWave), 0, s, w);
+    return hipGetLastError();
+}
+
+}  // namespace wfst
