@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X WFST beam-search decoder on one GPU.
+
+A step is one whole decode (wfst_decode) of the synthetic HLG-scale batch: 32
+utterances of 300-500 frames (fp16 log-probs [32, 500, 5000]) over a 2M-state,
+21M-arc power-law graph, beam 20, max_active 10000. Inputs are resident in HBM
+before the timed region; a decode's host work (one 24-byte descriptor copy in,
+one result copy out) is inside it.
+
+Prints one JSON line: decoded frames/s (value), arcs expanded/s, the achieved
+fraction of the HBM roofline for the dominant kernel (algorithmic bytes per
+launch over its average launch time, from hipEvents recorded between the
+decoder's launches in a second, instrumented pass of the same K decodes), and
+the CPU oracle's frames/s on a bounded sample of lanes (test infrastructure,
+single thread).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(st, elem_bytes, vocab):
+    """Bytes the method must move per decode, per kernel, from the device counters.
+
+    Per-unit figures (n tokens expanded, S candidate arcs, C admitted candidates,
+    D distinct destinations, n' survivors = D without epsilon arcs, F lane-frames,
+    E epsilon arcs, e*V log-prob row bytes):
+      max      12 n + 6 S + e V F       (token score + arc range, ilabel u16 + weight f32, one row per lane-frame)
+      expand   12 n + 6 S + 12 C + 8 D + e V F   (+ dest i32 and u64 payload atomic per admitted, hash key + claim per distinct)
+      finalize 28 D + 20 n'             (claim + payload read-back + targeted clear; next-frontier token 12 B + winners-log entry 8 B)
+      eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, claims, changed tokens)
+      path     20 n + 6 S + 12 C + 28 D + 20 n' + e V F (+ eps terms): the whole step, counted once
+    """
+    n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
+    E, De, Ne = st["eps_arcs"], st["eps_distinct"], st["eps_changed"]
+    row = elem_bytes * vocab * F
+    per = {
+        "max": 12 * n + 6 * S + row,
+        "expand": 12 * n + 6 * S + 12 * C + 8 * D + row,
+        "finalize": 28 * D + 20 * D,
+        "eps_expand": 16 * E,
+        "eps_resolve": 28 * De,
+        "eps_apply": 20 * Ne,
+    }
+    path = 20 * n + 6 * S + 12 * C + 28 * D + 20 * D + row + 16 * E + 28 * De + 20 * Ne
+    return per, path
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("wfst_kernels.hip", "wfst_internal.h"):
+        with open(os.path.join(ROOT, "wfst_beam_search_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload_name):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    when it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload_name, {}).get(kernel)
+    if not ent or ent.get("kernel_source") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(graph, lp, lengths, wl, seconds):
+    import numpy as np
+
+    import oracle
+    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    og = oracle.OracleGraph(graph)
+    frames = arcs = 0
+    lanes = 0
+    t0 = time.perf_counter()
+    for b in range(lp.shape[0]):
+        r = oracle.decode_lane(og, lp[b], int(lengths[b]), wl.beam, wl.max_active,
+                               eps_iterations=wl.eps_iterations)
+        frames += int(lengths[b])
+        arcs += int(r["steps"][:, 4].sum() + r["steps"][:, 7].sum())
+        lanes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": frames / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "arcs_per_s": arcs / dt,
+            "sample": f"lanes 0..{lanes - 1} of the {wl.name} batch ({frames} frames, {dt:.1f} s, "
+                      f"single-threaded C oracle pinned to one core; host nproc {os.cpu_count()}, {model})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (1-5); 3 = HLG-scale")
+    ap.add_argument("--eager", action="store_true", help="plain launches instead of the captured graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
+    ap.add_argument("--no-profile-pass", action="store_true")
+    ap.add_argument("--report", default="", help="also write a detailed JSON report here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this decoder runs on one GPU; utterances shard across GPUs with no "
+              "exchange, so there is no multi-GPU step to time (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import wfst_beam_search_amd as wb
+
+    wl = synth.WORKLOADS[args.workload]
+    graph, lp, lengths = synth.workload_inputs(args.workload)
+    B, T, V = lp.shape
+    dev = torch.device("cuda:0")
+    dg = wb.Graph(graph, device=0)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
+                     eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
+                     grid_blocks=args.grid)
+    x = torch.from_numpy(lp).to(dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        dec.decode(x, lengths)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = dec.decode(x, lengths)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = dec.stats()
+
+    frames = int(np.asarray(lengths).sum())
+    ms_per_step = dt / args.steps * 1e3
+    fps = frames * args.steps / dt
+    arcs_ps = (st["arcs"] + st["eps_arcs"]) * args.steps / dt
+    ok = bool((res.meta[:, 0] == 1).all() and (res.meta[:, 2] == 0).all())
+    elem = 2 if wl.dtype == "f16" else 4
+    per_kernel_bytes, path_bytes = algorithmic_bytes(st, elem, V)
+
+    roofline = None
+    ktimes = {}
+    prof_ms = None
+    if not args.no_profile_pass:
+        dec.profile(True)
+        dec.decode(x, lengths)            # capture the instrumented graph
+        torch.cuda.synchronize()
+        acc = {}
+        tp = time.perf_counter()
+        for _ in range(args.steps):
+            dec.decode(x, lengths)
+            for k, (ms, cnt) in dec.kernel_times().items():
+                a = acc.setdefault(k, [0.0, 0])
+                a[0] += ms
+                a[1] += cnt
+        torch.cuda.synchronize()
+        prof_ms = (time.perf_counter() - tp) / args.steps * 1e3
+        dec.profile(False)
+        ktimes = {k: {"total_ms_per_decode": v[0] / args.steps, "launches_per_decode": v[1] // args.steps,
+                      "avg_launch_us": (v[0] / v[1] * 1e3) if v[1] else 0.0} for k, v in acc.items()}
+        dom = max((k for k in ktimes if k in per_kernel_bytes), key=lambda k: ktimes[k]["total_ms_per_decode"])
+        launches = ktimes[dom]["launches_per_decode"]
+        avg_s = ktimes[dom]["avg_launch_us"] * 1e-6
+        bpl = per_kernel_bytes[dom] / max(launches, 1)
+        achieved = bpl / avg_s / 1e9 if avg_s > 0 else 0.0
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                    "traffic": traffic_from_profiles(dom, wl.name),
+                    "bytes_per_launch": int(bpl), "avg_launch_us": round(ktimes[dom]["avg_launch_us"], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds)
+
+    line = {
+        "metric": "decoded frames/sec and arcs expanded/sec at 1 GPU; % of HBM peak",
+        "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: synthetic HLG-scale graph ({graph.num_states - 1} states, "
+                               f"{graph.num_arcs} arcs, power-law out-degree), log_prob {wl.dtype} "
+                               f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
+                   "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
+                   "graph_replay": not args.eager},
+        "arcs_expanded_per_s": round(arcs_ps, 1),
+        "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
+        "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
+        "parity_meta_ok": ok,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump({"line": line, "stats": st, "kernels": ktimes, "per_kernel_bytes": per_kernel_bytes,
+                       "path_bytes": path_bytes, "profiled_ms_per_step": prof_ms,
+                       "kernel_source": kernel_source_hash()}, f, indent=1)
+    dec.close()
+    dg.release()
+
+
+if __name__ == "__main__":
+    main()

@@ -39,6 +39,7 @@ extern "C" {
 
 /* out_meta[b * 3 + 2] bits (section 7 of the page): a non-zero value means the
  * lane's result may be degraded; such a lane also reports ok = 0. */
+#define WFST_OVF_SLOTS    1   /* a lane's candidate arcs in one step exceed slot_cap       */
 #define WFST_OVF_HASH     2   /* a destination found no hash slot within the probe bound   */
 #define WFST_OVF_ARENA    4   /* the lane's winners-log region is full                     */
 #define WFST_OVF_CLAIMS   8   /* more distinct destinations in one pass than claims_cap    */
@@ -111,6 +112,8 @@ typedef struct wfst_graph_desc {
  *                  (0: 4 * max_active * (max_frames + 2) * (1 + eps passes),
  *                  at least 2^20); max_lanes * arena_entries < 2^31.
  *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
+ *  slot_cap        candidate arcs (slots) per lane per step (0: 512 * max_active,
+ *                  at least 2^16); at most 2^31.
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -126,6 +129,7 @@ typedef struct wfst_decoder_config {
     int32_t claims_cap;
     int32_t grid_blocks;
     int64_t arena_entries;
+    int64_t slot_cap;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -197,13 +201,14 @@ int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, in
 int wfst_decoder_destroy(wfst_decoder_t d);
 
 /*
- * Counters of the last decode, summed over its lanes (n up to 12 values):
+ * Counters of the last decode, summed over its lanes (n up to 13 values):
  *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
  *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
  *  frontier sizes), [4] epsilon arcs relaxed, [5] epsilon candidates admitted,
  *  [6] epsilon destinations claimed, [7] tokens appended or replaced by the
  *  closure, [8] winners-log entries written, [9] steps run (frame loop length),
- *  [10] largest frontier, [11] device bytes reserved by the decoder.
+ *  [10] largest frontier, [11] device bytes reserved by the decoder,
+ *  [12] real (frame) steps run, summed over lanes.
  */
 int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 
@@ -217,6 +222,37 @@ int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
  * or a negative status.
  */
 int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_t steps_cap);
+
+/* Kernel ids of wfst_decoder_kernel_times, in launch order within a step. */
+#define WFST_K_CLEAR        0  /* per-decode clear of records and stale hash tables        */
+#define WFST_K_INIT         1  /* lane control blocks and start tokens                     */
+#define WFST_K_LPMAX        2  /* max log-prob per (lane, frame) row for the bound skip    */
+#define WFST_K_MAX          3  /* exact per-lane maximum of the step                       */
+#define WFST_K_EXPAND       4  /* admit + recombination                                    */
+#define WFST_K_FINALIZE     5  /* compaction into the next frontier, winners log           */
+#define WFST_K_EPS_EXPAND   6  /* closure pass: relax epsilon arcs                         */
+#define WFST_K_EPS_RESOLVE  7  /* closure pass: append / replace decisions                 */
+#define WFST_K_EPS_APPLY    8  /* closure pass: apply them                                 */
+#define WFST_K_BACKTRACK    9  /* best path to arc ids and words                           */
+#define WFST_K_COUNT       10
+
+/*
+ * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its
+ * kernels as plain launches (no graph replay, as the page's sections 9 and 12
+ * profile) and records a hipEvent on the decode's stream before every launch
+ * and after the last one, so the time between consecutive events bounds each
+ * launch. Results are identical with timing on or off.
+ * Errors: WFST_EINVAL, WFST_EDEVICE.
+ */
+int wfst_decoder_profile(wfst_decoder_t d, int32_t enable);
+
+/*
+ * Per-kernel times of the last decode, which must have run with timing on:
+ * out[2*k] = total milliseconds and out[2*k + 1] = launches of kernel id k
+ * (WFST_K_*), for k < min(n / 2, WFST_K_COUNT). Errors: WFST_EINVAL (null, or
+ * the last decode was not profiled), WFST_EDEVICE.
+ */
+int wfst_decoder_kernel_times(wfst_decoder_t d, double *out, int32_t n);
 
 #ifdef __cplusplus
 }

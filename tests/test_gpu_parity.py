@@ -200,8 +200,8 @@ def test_decode_argument_errors():
 
 
 @pytest.mark.parametrize("cid,cap,bit", [(2, "frontier_cap", 16), (2, "arena_entries", 4),
-                                         (2, "claims_cap", 8), (4, "frontier_cap", 16),
-                                         (4, "arena_entries", 4)])
+                                         (2, "claims_cap", 8), (2, "slot_cap", 1),
+                                         (4, "frontier_cap", 16), (4, "arena_entries", 4)])
 def test_capacity_overflow_is_flagged(cid, cap, bit):
     import torch
     g, lp, L = synth.workload_inputs(cid)
@@ -209,7 +209,8 @@ def test_capacity_overflow_is_flagged(cid, cap, bit):
     _say("overflow", cid, cap)
     caps = {"frontier_cap": {"frontier_cap": 2000 if cid == 4 else 64, "claims_cap": 1000000},
             "arena_entries": {"arena_entries": 40000 if cid == 4 else 4096},
-            "claims_cap": {"frontier_cap": 100000, "claims_cap": 64}}[cap]
+            "claims_cap": {"frontier_cap": 100000, "claims_cap": 64},
+            "slot_cap": {"slot_cap": 256}}[cap]
     dg = wb.Graph(g)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=2, max_frames=wl.frames,
                      eps_iterations=wl.eps_iterations, **caps)

@@ -25,11 +25,15 @@ _LIB_PATH = os.path.join(_HERE, "libwfst_mi355x.so")
 LP_F32, LP_F16 = 0, 1
 EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release",
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
-                    "wfst_decoder_stats", "wfst_decoder_step_stats")
+                    "wfst_decoder_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
+                    "wfst_decoder_kernel_times")
+KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
+           "eps_apply", "backtrack")
 STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
                "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "_13", "_14", "_15")
 STAT_FIELDS = ("arcs", "admitted", "distinct", "tokens", "eps_arcs", "eps_admitted",
-               "eps_distinct", "eps_changed", "log_entries", "steps", "max_frontier", "bytes_reserved")
+               "eps_distinct", "eps_changed", "log_entries", "steps", "max_frontier", "bytes_reserved",
+               "lane_frames")
 
 
 class WfstError(RuntimeError):
@@ -55,7 +59,7 @@ class _Config(ctypes.Structure):
                 ("lp_dtype", ctypes.c_int32), ("eps_iterations", ctypes.c_int32),
                 ("use_graphs", ctypes.c_int32), ("frontier_cap", ctypes.c_int32),
                 ("claims_cap", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
-                ("arena_entries", ctypes.c_int64)]
+                ("arena_entries", ctypes.c_int64), ("slot_cap", ctypes.c_int64)]
 
 
 _lib = None
@@ -93,6 +97,8 @@ def load_library():
         lib.wfst_decode.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_decoder_stats.argtypes = [vp, vp, i32]
         lib.wfst_decoder_step_stats.argtypes = [vp, i32, vp, i32]
+        lib.wfst_decoder_profile.argtypes = [vp, i32]
+        lib.wfst_decoder_kernel_times.argtypes = [vp, vp, i32]
         for name in EXPORTED_SYMBOLS:
             if name != "wfst_last_error":
                 getattr(lib, name).restype = ctypes.c_int
@@ -166,12 +172,12 @@ class Decoder:
                  allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
                  lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
-                 grid_blocks: int = 0):
+                 grid_blocks: int = 0, slot_cap: int = 0):
         lib = load_library()
         cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                       int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                       int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
-                      int(claims_cap), int(grid_blocks), int(arena_entries))
+                      int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap))
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h
@@ -227,6 +233,16 @@ class Decoder:
         out = np.zeros((cap, len(STEP_FIELDS)), dtype=np.int64)
         n = _check(_lib.wfst_decoder_step_stats(self.handle, int(lane), _ptr(out), cap))
         return out[:n]
+
+    def profile(self, enable: bool = True):
+        """Record hipEvents between this decoder's kernel launches (see kernel_times)."""
+        _check(_lib.wfst_decoder_profile(self.handle, int(bool(enable))))
+
+    def kernel_times(self) -> dict:
+        """{kernel: (total ms, launches)} of the last decode (run with profile on)."""
+        out = np.zeros(2 * len(KERNELS), dtype=np.float64)
+        _check(_lib.wfst_decoder_kernel_times(self.handle, _ptr(out), out.shape[0]))
+        return {k: (float(out[2 * i]), int(out[2 * i + 1])) for i, k in enumerate(KERNELS)}
 
     def close(self):
         if self.handle:

@@ -103,11 +103,17 @@ struct wfst_decoder_s {
     int last_B = 0;
     std::vector<int32_t> last_len;
     int last_steps = 0;
+    bool prof_on = false;            // record hipEvents between launches
+    bool last_profiled = false;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> ev_kind;
+    size_t ev_used = 0;
 
     ~wfst_decoder_s()
     {
         (void)hipSetDevice(g ? g->device : 0);
         for (auto &kv : graphs) (void)hipGraphExecDestroy(kv.second);
+        for (hipEvent_t e : ev) (void)hipEventDestroy(e);
         if (cap_stream) (void)hipStreamDestroy(cap_stream);
         if (h_in) (void)hipHostFree(h_in);
         if (h_res) (void)hipHostFree(h_res);
@@ -268,7 +274,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.max_frames < 1 || c.max_frames > (1 << 20)) return fail(WFST_EINVAL, "max_frames must lie in [1, 2^20]");
     if (c.lp_dtype != WFST_LP_F32 && c.lp_dtype != WFST_LP_F16) return fail(WFST_EINVAL, "lp_dtype must be WFST_LP_F32 or WFST_LP_F16");
     if (c.eps_iterations < 0 || c.eps_iterations > 16) return fail(WFST_EINVAL, "eps_iterations must lie in [0, 16]");
-    if (c.frontier_cap < 0 || c.claims_cap < 0 || c.arena_entries < 0 || c.grid_blocks < 0)
+    if (c.frontier_cap < 0 || c.claims_cap < 0 || c.arena_entries < 0 || c.grid_blocks < 0 ||
+        c.slot_cap < 0 || c.slot_cap > (1ll << 31))
         return fail(WFST_EINVAL, "capacities must be >= 0");
     const int P = (g->eps_id >= 0) ? c.eps_iterations : 0;
 
@@ -289,6 +296,9 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
     }
     const uint64_t path_cap = (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
+    const uint64_t slots = c.slot_cap ? (uint64_t)c.slot_cap
+                                      : std::min<uint64_t>(std::max<uint64_t>(512ull * (uint64_t)c.max_active, 1ull << 16), 1ull << 31);
+    const uint64_t strip_cap = (slots + kWave - 1) / kWave;
 
     HIP_TRY(hipSetDevice(g->device));
     wfst_decoder_s *d = new wfst_decoder_s();
@@ -302,8 +312,10 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         if (hipGetDeviceProperties(&prop, g->device) == hipSuccess && prop.multiProcessorCount > 0)
             ncu = prop.multiProcessorCount;
     }
-    const long long want = ((long long)c.max_lanes * c.max_active + 255) / 256;
-    d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 8LL * ncu);
+    const long long want = ((long long)c.max_lanes * c.max_active + 127) / 128;
+    // every workgroup of a frame-loop kernel first builds the lane table, so a
+    // grid of 4 workgroups per CU (16 wavefronts) is measured best on MI355X
+    d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
 
     Work &w = d->w;
     w.sinfo = g->sinfo; w.ilabel = g->ilabel; w.weight = g->weight; w.dest = g->dest;
@@ -314,7 +326,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
     w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
     w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC; w.hash_mask = (uint32_t)(HC - 1);
-    w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap;
+    w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap; w.strip_cap = (uint32_t)strip_cap;
     w.res_stride = (uint32_t)(kResHeader + 2 * path_cap);
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
@@ -327,7 +339,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     for (int p = 0; p < 2; ++p) {
         A(&w.tok_state[p], L * Q); A(&w.tok_score[p], L * Q); A(&w.tok_entry[p], L * Q);
         A(&w.tok_last[p], L * Q); A(&w.tok_off[p], L * Q); A(&w.tok_abeg[p], L * Q);
-        A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S);
+        A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S); A(&w.strip_tok[p], L * strip_cap);
         if (P > 0) A(&w.changed[p], L * CC);
     }
     A(&w.hash, L * HC);
@@ -357,25 +369,55 @@ extern "C" int wfst_decoder_destroy(wfst_decoder_t d)
     return WFST_OK;
 }
 
+// One launch of the decode; with profiling on, an event is recorded before it
+// (events between consecutive launches bound each kernel's time).
+static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
+{
+    if (d->prof_on) {
+        if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
+        hipError_t e = hipEventRecord(d->ev[d->ev_used], s);
+        if (e != hipSuccess) return e;
+        d->ev_kind[d->ev_used++] = id;
+    }
+    return launch_kernel(id, d->w, t, k, d->grid, s);
+}
+
 // Queue one whole decode of `steps` frame-loop steps on stream s.
 static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
 {
-    const Work &w = d->w;
     hipError_t e;
-    if ((e = launch_clear_dirty(w, d->grid, s)) != hipSuccess) return e;
-    if ((e = launch_init(w, d->grid, s)) != hipSuccess) return e;
-    if (d->passes > 0 && (e = launch_closure(w, -1, d->grid, s)) != hipSuccess) return e;
-    if ((e = launch_lpmax(w, d->grid, s)) != hipSuccess) return e;
-    for (int t = 0; t < steps; ++t) {
-        if ((e = launch_step(w, t, d->grid, s)) != hipSuccess) return e;
-        if (d->passes > 0 && (e = launch_closure(w, t, d->grid, s)) != hipSuccess) return e;
+    d->ev_used = 0;
+    if ((e = launch(d, kKClear, 0, 0, s)) != hipSuccess) return e;
+    if ((e = launch(d, kKInit, 0, 0, s)) != hipSuccess) return e;
+    for (int k = 1; k <= d->passes; ++k) {
+        if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
+        if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
+        if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
     }
-    return launch_backtrack(w, s);
+    if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
+    for (int t = 0; t < steps; ++t) {
+        if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
+        if ((e = launch(d, kKExpand, t, 0, s)) != hipSuccess) return e;
+        if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
+        for (int k = 1; k <= d->passes; ++k) {
+            if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
+        }
+    }
+    if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
+    if (d->prof_on) {
+        if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
+        if ((e = hipEventRecord(d->ev[d->ev_used], s)) != hipSuccess) return e;
+        d->ev_kind[d->ev_used++] = -1;
+    }
+    return hipSuccess;
 }
 
 static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)
 {
-    auto it = d->graphs.find(steps);
+    const int key = steps * 2 + (d->prof_on ? 1 : 0);
+    auto it = d->graphs.find(key);
     if (it != d->graphs.end()) { *exec = it->second; return WFST_OK; }
     hipGraph_t graph = nullptr;
     HIP_TRY(hipStreamBeginCapture(d->cap_stream, hipStreamCaptureModeThreadLocal));
@@ -387,7 +429,7 @@ static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)
     e = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
-    d->graphs[steps] = ex;
+    d->graphs[key] = ex;
     *exec = ex;
     return WFST_OK;
 }
@@ -429,7 +471,9 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     HIP_TRY(hipMemcpyAsync(d->d_lengths, hl, 4 * L, hipMemcpyHostToDevice, s));
 
     const int steps = maxlen + 1;
-    if (c.use_graphs) {
+    // timing events cannot be read back from a replayed graph: a profiled decode
+    // runs the same kernels as plain launches
+    if (c.use_graphs && !d->prof_on) {
         int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
         bucket = std::min(bucket, c.max_frames + 1);
         hipGraphExec_t ex = nullptr;
@@ -442,6 +486,7 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
         d->last_steps = steps;
     }
+    d->last_profiled = d->prof_on;
     const size_t rs = d->w.res_stride;
     HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
@@ -482,7 +527,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
 {
     if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
     std::lock_guard<std::mutex> lock(d->mu);
-    int64_t v[12] = {0};
+    int64_t v[13] = {0};
     if (d->last_B > 0) {
         std::vector<uint32_t> rec;
         int rc = fetch_records(d, &rec);
@@ -495,6 +540,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
                 v[4] += x[kRecEpsArcs]; v[5] += x[kRecEpsAdmitted]; v[6] += x[kRecEpsDistinct];
                 v[7] += (int64_t)x[kRecEpsNew] + x[kRecEpsReplaced];
                 v[10] = std::max<int64_t>(v[10], x[kRecN]);
+                if (r >= 1 && x[kRecPhase] == (uint32_t)kPhReal && x[kRecN] > 0) v[12] += 1;
             }
         }
         std::vector<LaneCtl> ctl((size_t)d->cfg.max_lanes);
@@ -503,7 +549,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
     }
     v[9] = d->last_steps;
     v[11] = (int64_t)(d->bytes + d->g->bytes);
-    for (int32_t i = 0; i < n && i < 12; ++i) out[i] = v[i];
+    for (int32_t i = 0; i < n && i < 13; ++i) out[i] = v[i];
     return WFST_OK;
 }
 
@@ -526,4 +572,36 @@ extern "C" int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *
         if (r == 0) out[kRecPhase] = -1;
     }
     return nrec;
+}
+
+extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    std::lock_guard<std::mutex> lock(d->mu);
+    HIP_TRY(hipSetDevice(d->g->device));
+    if (enable && d->ev.empty()) {
+        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(3 + 3 * d->passes);
+        d->ev.resize(n, nullptr);
+        d->ev_kind.assign(n, -1);
+        for (size_t i = 0; i < n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));
+    }
+    d->prof_on = enable != 0;
+    return WFST_OK;
+}
+
+extern "C" int wfst_decoder_kernel_times(wfst_decoder_t d, double *out, int32_t n)
+{
+    if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
+    std::lock_guard<std::mutex> lock(d->mu);
+    if (!d->last_profiled) return fail(WFST_EINVAL, "the last decode was not profiled");
+    HIP_TRY(hipSetDevice(d->g->device));
+    std::vector<double> v(2 * kKCount, 0.0);
+    for (size_t i = 0; i + 1 < d->ev_used; ++i) {
+        float ms = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&ms, d->ev[i], d->ev[i + 1]));
+        const int id = d->ev_kind[i];
+        if (id >= 0 && id < kKCount) { v[2 * id] += ms; v[2 * id + 1] += 1.0; }
+    }
+    for (int32_t i = 0; i < n && i < 2 * kKCount; ++i) out[i] = v[(size_t)i];
+    return WFST_OK;
 }

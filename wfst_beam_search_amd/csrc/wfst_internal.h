@@ -22,7 +22,7 @@ enum : int32_t { kPhNone = -1, kPhReal = 0, kPhFinal = 1, kPhRedirect = 2, kPhDe
 
 // Overflow bits (same values as the public WFST_OVF_*).
 enum : uint32_t {
-    kOvfHash = 2, kOvfArena = 4, kOvfClaims = 8, kOvfFrontier = 16, kOvfPath = 32
+    kOvfSlots = 1, kOvfHash = 2, kOvfArena = 4, kOvfClaims = 8, kOvfFrontier = 16, kOvfPath = 32
 };
 
 // Per-step record fields (u32).
@@ -68,7 +68,12 @@ struct alignas(128) LaneCtl {
     uint32_t dirty;            // hash table may hold stale slots (claims overflow)
     int32_t last_step;         // last step this lane ran
     int32_t phase_final;       // phase code of the lane's last step
-    uint32_t pad[8];
+    uint32_t log_pending;      // entries of the last compaction, added to log_cursor by the next kernel
+    uint32_t snap_n;           // frontier size and winners-log cursor as a closure pass's
+    uint32_t snap_log;         //   apply kernel starts (taken by the resolve kernel before it)
+    uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
+                               //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
+    uint32_t pad[3];
 };
 
 // Device-resident description of the caller's log_prob tensor, rewritten before
@@ -104,6 +109,7 @@ struct Work {
     uint32_t hash_mask;       // HC - 1 (HC power of two)
     uint32_t arena;           // winners-log entries per lane
     uint32_t path_cap;        // device path buffer per lane
+    uint32_t strip_cap;       // 64-slot strips per lane and step (slot space = 64 * strip_cap)
     uint32_t res_stride;      // int32 per lane in the result buffer
     // workspace
     LaneCtl *ctl;             // [L]
@@ -115,6 +121,7 @@ struct Work {
     int32_t *tok_entry[2];
     int32_t *tok_last[2];
     uint32_t *tok_off[2];     // exclusive arc offset of the token in the step's slot space
+    uint32_t *strip_tok[2];   // [L][strip_cap] token holding the first slot of each 64-slot strip
     int32_t *tok_abeg[2];     // first arc of the step's class
     float *tok_ub[2];         // score + largest weight of the step's class
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
@@ -128,13 +135,14 @@ struct Work {
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]
 };
 
-// Host-side launchers (wfst_kernels.hip).
-hipError_t launch_init(const Work &w, int grid, hipStream_t s);
-hipError_t launch_lpmax(const Work &w, int grid, hipStream_t s);
-hipError_t launch_step(const Work &w, int t, int grid, hipStream_t s);
-hipError_t launch_closure(const Work &w, int t, int grid, hipStream_t s);
-hipError_t launch_backtrack(const Work &w, hipStream_t s);
-hipError_t launch_clear_dirty(const Work &w, int grid, hipStream_t s);
+// Kernels of a decode, in launch order within a step (ids match WFST_K_*).
+enum : int {
+    kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
+    kKEpsApply, kKBacktrack, kKCount
+};
+
+// Host-side launcher (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.
+hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
 enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };

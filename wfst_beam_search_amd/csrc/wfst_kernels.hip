@@ -108,6 +108,7 @@ struct LaneTab {
     int32_t T[kMaxLanes];
     float f0[kMaxLanes];           // max log-prob of the lane's row (0 on the final step)
     float f1[kMaxLanes];           // cutoff, or the running max
+    uint32_t fb[kMaxLanes];        // winners-log base of the sources' compaction
 };
 
 __device__ __forceinline__ void tab_publish(LaneTab &tab, int nl, uint32_t units)
@@ -148,39 +149,68 @@ __device__ __forceinline__ int hash_claim(HashSlot *tbl, uint32_t mask, int32_t 
     const uint32_t want = (uint32_t)dest + 1u;
     uint32_t h = hash_state((uint32_t)dest) & mask;
     *first = false;
+    // Most admitted candidates reach a destination no other candidate has claimed
+    // yet, so the first probe goes straight to the compare-and-swap (one round
+    // trip claims the slot or reports its owner).
     for (int probe = 0; probe < kMaxProbes; ++probe) {
-        uint32_t k = __hip_atomic_load(&tbl[h].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (k == want) return (int)h;
-        if (k == 0u) {
-            uint32_t old = atomicCAS(&tbl[h].key, 0u, want);
-            if (old == 0u) { *first = true; return (int)h; }
-            if (old == want) return (int)h;
-        }
+        const uint32_t old = atomicCAS(&tbl[h].key, 0u, want);
+        if (old == 0u) { *first = true; return (int)h; }
+        if (old == want) return (int)h;
         h = (h + 1u) & mask;
     }
     return -1;
 }
 
-__device__ __forceinline__ void payload_max(unsigned long long *p, unsigned long long key)
+// Writes the strip map for tokens just allocated by one wavefront: the keepers
+// of this wave got positions p0 + rank and slot offsets a0 + dpre (dpre is the
+// exclusive scan of the keepers' degrees, so over all 64 lanes a0 + dpre is
+// non-decreasing and a non-keeper acts as a token without arcs). For every
+// strip whose first slot lies in [a0, a0 + dsum) the token holding that slot is
+// the last lane whose offset is <= the slot.
+__device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip_cap, uint32_t p0,
+                                             uint32_t a0, uint32_t dpre, uint32_t dsum,
+                                             unsigned long long keep_mask)
 {
-    unsigned long long cur = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (key > cur) atomicMax(p, key);
+    const uint32_t o = a0 + dpre;
+    const uint32_t rank = (uint32_t)__popcll(keep_mask & mask_lt());
+    const uint32_t sb0 = (a0 + kWave - 1) / kWave;
+    const uint32_t sb1 = (a0 + dsum + kWave - 1) / kWave;
+    for (uint32_t sb = sb0 + (uint32_t)wlane(); sb - (uint32_t)wlane() < sb1; sb += kWave) {
+        const uint32_t slot = sb * kWave;
+        int i = 0;
+#pragma unroll
+        for (int st = 32; st >= 1; st >>= 1) {
+            const uint32_t v = __shfl(o, i + st, kWave);
+            if (v <= slot) i += st;
+        }
+        const uint32_t r = __shfl(rank, i, kWave);
+        if (sb < sb1 && sb < strip_cap) strip_tok[sb] = p0 + r;
+    }
 }
 
-// Wave-aggregated append of the claiming threads' slots to a claims list.
-__device__ __forceinline__ void append_claims(const Work &w, int L, uint32_t *counter, bool first,
-                                              int slot)
+// Per-wavefront LDS buffer of claimed slots in the expand pass.
+constexpr uint32_t kClaimBuf = 512;
+
+__device__ __forceinline__ void wave_lds_sync()
 {
-    unsigned long long m = __ballot(first);
-    if (m == 0ull) return;
-    const int leader = __ffsll((long long)m) - 1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Appends the wave's n buffered claims to lane L's list: one atomic, then a
+// coalesced copy out of LDS.
+__device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *counter, uint32_t *cbuf,
+                                             uint32_t n)
+{
+    wave_lds_sync();
     uint32_t base = 0;
-    if (wlane() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader, kWave);
-    if (first) {
-        uint32_t idx = base + (uint32_t)__popcll(m & mask_lt());
-        if (idx < w.claims_cap) w.claims[(size_t)L * w.claims_cap + idx] = (uint32_t)slot;
-    }
+    if (wlane() == 0) base = atomicAdd(counter, n);
+    base = __shfl(base, 0, kWave);
+    uint32_t *dst = w.claims + (size_t)L * w.claims_cap;
+    for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave)
+        if (base + i < w.claims_cap) dst[base + i] = cbuf[i];
+    wave_lds_sync();
 }
 
 // ---------------------------------------------------------------- k_clear
@@ -232,6 +262,9 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
     c.nchanged[0] = 0u;
     c.nchanged[1] = 0u;
     c.dirty = 0u;
+    c.log_pending = 0u;
+    c.front_base[0] = 0xFFFFFFFFu;
+    c.front_base[1] = 0xFFFFFFFFu;
     c.last_step = -1;
     c.phase_final = kPhNone;
     c.cnt[1] = 0ull;
@@ -249,6 +282,8 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
     w.tok_abeg[0][q] = abeg;
     w.tok_ub[0][q] = ub;
     w.pos[0][(size_t)L * w.num_states + s] = 0;
+    uint32_t *st = w.strip_tok[0] + (size_t)L * w.strip_cap;
+    for (uint32_t sb = 0; sb * kWave < deg && sb < w.strip_cap; ++sb) st[sb] = 0u;
     c.cnt[0] = 1ull | ((unsigned long long)deg << 32);
 }
 
@@ -277,8 +312,10 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(Work w)
 enum { kModeMax = 0, kModeExpand = 1 };
 
 template <int MODE, typename LPT>
-__device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d)
+__device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
+                                           uint32_t *cbuf)
 {
+    uint32_t cb_n = 0;
     const int p = t & 1;
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
@@ -308,19 +345,15 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
         LaneCtl &c = w.ctl[L];
         uint32_t j0 = (s - tab.base[L]) * (uint32_t)kWave;
 
-        // first token of the run: largest i with off[i] <= j0
-        uint32_t cur;
-        {
-            uint32_t lo = 0, hi = n - 1;
-            while (lo < hi) {
-                uint32_t mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= j0) lo = mid; else hi = mid - 1;
-            }
-            cur = lo;
-        }
+        // first token of the run, from the strip map built with the frontier
+        uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L])];
+        if (cur >= n) cur = 0;
         float run = -__builtin_inff();
-        if (MODE == kModeMax)
-            run = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float posted = -__builtin_inff();
+        if (MODE == kModeMax) {
+            posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            run = posted;
+        }
         uint32_t admitted = 0;
         HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
 
@@ -369,37 +402,59 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
                     m = e;
                 }
                 m = wave_max(m);
-                if (m > run) {
-                    if (lane == 0) atomicMax(&c.maxkey[p], f2ord(m));
-                    run = m;
-                }
-                run = fmaxf(run, ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)));
+                run = fmaxf(run, m);
             } else {
                 bool first = false;
                 int slot = -1;
+                unsigned long long fkey = 0ull;
                 if (live && ub + lpm > cut) {
-                    float e = sc + w.weight[arc];
+                    // destination fetched with the arc so the hash insert of an
+                    // admitted candidate does not wait for another round trip
+                    const float wt = w.weight[arc];
+                    const int32_t dst = row ? w.dest[arc] : 0;
+                    float e = sc + wt;
                     if (row) e = e + lp_at(row, w.ilabel[arc]);
                     if (e > cut) {
                         ++admitted;
                         const unsigned long long key = cand_key(e, (int32_t)arc);
                         if (ph == kPhReal) {
-                            const int32_t dst = w.dest[arc];
                             slot = hash_claim(tbl, w.hash_mask, dst, &first);
                             if (slot < 0) atomicOr(&c.overflow, kOvfHash);
-                            else payload_max(&tbl[slot].payload, key);
+                            else atomicMax(&tbl[slot].payload, key);
                         } else {
-                            payload_max(&c.final_key, key);
+                            fkey = key;
                         }
                     }
                 }
-                append_claims(w, L, &c.nclaims, first, slot);
+                if (ph == kPhReal) {
+                    // first claimers go to this wavefront's LDS buffer, flushed
+                    // with one atomic on the lane's claims counter
+                    const unsigned long long fm = __ballot(first);
+                    if (fm) {
+                        if (cb_n + kWave > kClaimBuf) {
+                            flush_claims(w, L, &c.nclaims, cbuf, cb_n);
+                            cb_n = 0;
+                        }
+                        if (first) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot;
+                        cb_n += (uint32_t)__popcll(fm);
+                    }
+                } else {
+#pragma unroll
+                    for (int d = kWave / 2; d >= 1; d >>= 1) {
+                        const unsigned long long o = __shfl_xor(fkey, d, kWave);
+                        fkey = o > fkey ? o : fkey;
+                    }
+                    if (lane == 0 && fkey) atomicMax(&c.final_key, fkey);
+                }
             }
         }
         if (MODE == kModeExpand) {
+            if (cb_n) flush_claims(w, L, &c.nclaims, cbuf, cb_n);
+            cb_n = 0;
             const uint32_t a = wave_sum(admitted);
             if (lane == 0 && a) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
+        } else if (run > posted && lane == 0) {
+            atomicMax(&c.maxkey[p], f2ord(run));
         }
     }
 }
@@ -417,7 +472,7 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         int ph = lane_phase(c, t);
         const unsigned long long cn = c.cnt[p];
         const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
-        if (ph != kPhNone && (n > w.frontier_cap || c.log_cursor > w.arena)) ph = kPhNone;
+        if (ph != kPhNone && (n > w.frontier_cap || arcs > w.strip_cap * (uint32_t)kWave)) ph = kPhNone;
         float lpm = 0.0f, f1 = 0.0f;
         if (ph == kPhReal) lpm = w.lpmax[(size_t)L * w.max_frames + t];
         if (MODE == kModeExpand && ph != kPhNone) f1 = ord2f(c.maxkey[p]) - c.beam[p];
@@ -443,11 +498,13 @@ __device__ void step_begin_lane(const Work &w, int t, int L)
     const unsigned long long cn = c.cnt[p];
     const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
     uint32_t *rec = step_rec(w, L, t);
+    c.log_cursor += c.log_pending;   // entries of the previous compaction
+    c.log_pending = 0u;
     c.last_step = t;
     rec[kRecN] = n;
     rec[kRecArcs] = arcs;
     if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
-    if (c.log_cursor > w.arena) { c.overflow |= kOvfArena; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     // dynamic beam (page section 3), every operation one fp32 rounding
     float b;
@@ -506,7 +563,7 @@ __global__ __launch_bounds__(kBlock) void k_max(Work w, int t)
     __syncthreads();
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
     const LpDesc d = *w.lp;
-    walk_slots<kModeMax, LPT>(w, tab, t, d);
+    walk_slots<kModeMax, LPT>(w, tab, t, d, nullptr);
 }
 
 template <typename LPT>
@@ -525,8 +582,9 @@ __global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
             if (tab.ph[L] == kPhReal) c.cutoff = tab.f1[L];
         }
     }
+    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
     const LpDesc d = *w.lp;
-    walk_slots<kModeExpand, LPT>(w, tab, t, d);
+    walk_slots<kModeExpand, LPT>(w, tab, t, d, cbufs[threadIdx.x / kWave]);
 }
 
 // -------------------------------------------------------------- k_finalize
@@ -542,13 +600,18 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
             const LaneCtl &c = w.ctl[L];
             const int ph = lane_phase(c, t);
             const uint32_t nc = c.nclaims;
-            if (ph == kPhReal && nc <= w.claims_cap && c.log_cursor <= w.arena &&
-                (uint32_t)c.cnt[p] <= w.frontier_cap)
-                units = (nc + kWave - 1) / kWave;
+            // every claim becomes a token (the payload is the best admitted
+            // candidate): check the whole compaction fits before writing any
+            const bool fits = nc <= w.claims_cap && nc <= w.frontier_cap &&
+                              (unsigned long long)c.log_cursor + nc <= w.arena;
+            if (ph == kPhReal && fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
+            tab.arcs[L] = c.log_cursor;          // winners-log base of this compaction
             tab.ph[L] = ph;
             tab.T[L] = c.T;
+            tab.f0[L] = fits ? 1.0f : 0.0f;
             tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;
+            tab.fb[L] = c.front_base[p];
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -559,9 +622,18 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
         LaneCtl &c = w.ctl[L];
         const int ph = tab.ph[L];
         if (ph == kPhReal) {
-            step_rec(w, L, t)[kRecDistinct] = tab.n[L];
-            if (tab.n[L] > w.claims_cap) {
-                c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
+            const uint32_t nc = tab.n[L];
+            step_rec(w, L, t)[kRecDistinct] = nc;
+            if (tab.f0[L] == 0.0f) {
+                // the compaction does not fit: retire the lane before writing any
+                // token; its claimed hash slots stay set, so the table is cleared
+                // before the next decode
+                c.overflow |= nc > w.claims_cap ? kOvfClaims
+                            : nc > w.frontier_cap ? kOvfFrontier : kOvfArena;
+                c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
+            } else {
+                c.log_pending = nc;
+                c.front_base[np] = tab.arcs[L];
             }
             c.nclaims_eps[1] = 0u;
         } else if (ph == kPhFinal) {
@@ -621,11 +693,16 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
             keep = (K != 0ull) && key != 0u && (end > cutoff);
             if (keep) {
                 const int32_t src = w.arc_src[arc];
+                const StateInfo si = w.sinfo[dst];
                 const int32_t stok = w.pos[p][(size_t)L * w.num_states + src];
                 keep = (uint32_t)stok < Q;
                 if (keep) {
-                    esrc = w.tok_entry[p][(size_t)L * Q + stok];
-                    class_of(w.sinfo[dst], next_final, end, &abeg, &deg, &ub);
+                    // without epsilon arcs a token's entry is its compaction's base
+                    // plus its position; the closure may give a token a fresh entry
+                    const uint32_t fb = tab.fb[L];
+                    esrc = w.has_eps ? w.tok_entry[p][(size_t)L * Q + stok]
+                         : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
+                    class_of(si, next_final, end, &abeg, &deg, &ub);
                 }
             }
         }
@@ -637,30 +714,26 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
         const uint32_t dpre = wave_excl_sum(keep ? deg : 0u, &dsum);
         const int leader = __ffsll((long long)m) - 1;
         unsigned long long old = 0ull;
-        uint32_t lb = 0u;
-        if (lane == leader) {
+        if (lane == leader)
             old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
-            lb = atomicAdd(&c.log_cursor, nkeep);
-        }
         old = __shfl(old, leader, kWave);
-        lb = __shfl(lb, leader, kWave);
+        const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
         if (keep) {
-            const uint32_t pi = (uint32_t)old + rank;
-            const uint32_t le = lb + rank;
-            if (pi < Q && le < w.arena) {
-                const size_t q = (size_t)L * Q + pi;
-                const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
-                w.wlog[e] = make_int2(esrc, arc);
-                w.tok_state[np][q] = dst;
-                w.tok_score[np][q] = end;
-                w.tok_entry[np][q] = e;
-                w.tok_last[np][q] = arc;
-                w.tok_off[np][q] = (uint32_t)(old >> 32) + dpre;
-                w.tok_abeg[np][q] = abeg;
-                w.tok_ub[np][q] = ub;
-                w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
-            }
+            // position < nclaims <= frontier_cap and log base + nclaims <= arena (prologue)
+            const uint32_t pi = p0 + rank;
+            const size_t q = (size_t)L * Q + pi;
+            const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
+            w.wlog[e] = make_int2(esrc, arc);
+            w.tok_state[np][q] = dst;
+            w.tok_score[np][q] = end;
+            w.tok_entry[np][q] = e;
+            w.tok_last[np][q] = arc;
+            w.tok_off[np][q] = a0 + dpre;
+            w.tok_abeg[np][q] = abeg;
+            w.tok_ub[np][q] = ub;
+            w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
         }
+        write_strips(w.strip_tok[np] + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
 }
 
@@ -670,9 +743,12 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
 
 // A lane whose winners log or frontier overflowed holds tokens that were
 // counted but never written; it is skipped until the next step retires it.
-__device__ __forceinline__ bool closure_lane(const Work &w, const LaneCtl &c, int t)
+// Capacity of the compaction before a closure was checked lane-wide before it
+// wrote anything, and every apply kernel checks its own appends the same way,
+// so an active lane never holds a counted but unwritten token.
+__device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
 {
-    return c.status == kActive && (t < 0 || t < c.T) && c.log_cursor <= w.arena;
+    return c.status == kActive && (t < 0 || t < c.T);
 }
 
 __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
@@ -685,7 +761,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
             uint32_t ns = 0;
-            if (closure_lane(w, c, t)) {
+            if (closure_lane(c, t)) {
                 const uint32_t n = (uint32_t)c.cnt[fp];
                 if (n <= w.frontier_cap) ns = (k == 1) ? n : c.nchanged[k & 1];
             }
@@ -698,6 +774,11 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
     __syncthreads();
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
         const int L = (int)threadIdx.x;
+        LaneCtl &c = w.ctl[L];
+        if (k == 1) {   // entries of the compaction before this closure
+            c.log_cursor += c.log_pending;
+            c.log_pending = 0u;
+        }
         if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
     }
     const int nl = w.max_lanes;
@@ -730,7 +811,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
                     if (slot < 0) {
                         atomicOr(&c.overflow, kOvfHash);
                     } else {
-                        payload_max(&tbl[slot].payload, cand_key(e, a));
+                        atomicMax(&tbl[slot].payload, cand_key(e, a));
                         if (first) {
                             const uint32_t idx = atomicAdd(&c.nclaims_eps[k & 1], 1u);
                             if (idx < w.claims_cap) w.claims[(size_t)L * w.claims_cap + idx] = (uint32_t)slot;
@@ -760,7 +841,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
             const LaneCtl &c = w.ctl[L];
             uint32_t nc = 0;
             const uint32_t n = (uint32_t)c.cnt[fp];
-            if (closure_lane(w, c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
+            if (closure_lane(c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
             if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = n;
@@ -777,6 +858,10 @@ __global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
             c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
         }
         c.nchanged[(k + 1) & 1] = 0u;
+        // nothing changes these during resolve; the apply kernel, which advances
+        // them atomically, reads the snapshot in its prologue
+        c.snap_n = (uint32_t)c.cnt[fp];
+        c.snap_log = c.log_cursor;
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
@@ -829,16 +914,30 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
             uint32_t nc = 0;
-            const uint32_t n = (uint32_t)c.cnt[fp];
-            if (closure_lane(w, c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
-            if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
+            const uint32_t n = c.snap_n;
+            const bool on = closure_lane(c, t) && n <= w.frontier_cap;
+            if (on) nc = c.nclaims_eps[k & 1];
+            // at most nc appends and nc fresh entries: check they fit before writing
+            const bool fits = nc <= w.claims_cap && (unsigned long long)n + nc <= w.frontier_cap &&
+                              (unsigned long long)c.snap_log + nc <= w.arena;
+            if (fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.T[L] = c.T;
+            tab.f0[L] = (on && !fits) ? 1.0f : 0.0f;
         }
         tab_publish(tab, w.max_lanes, units);
     }
     __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) w.ctl[threadIdx.x].nclaims_eps[(k + 1) & 1] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        LaneCtl &c = w.ctl[L];
+        c.nclaims_eps[(k + 1) & 1] = 0u;
+        if (tab.f0[L] != 0.0f) {
+            c.overflow |= tab.n[L] > w.claims_cap ? kOvfClaims
+                        : c.snap_n + tab.n[L] > w.frontier_cap ? kOvfFrontier : kOvfArena;
+            c.status = kDone; c.phase_final = kPhDead;
+        }
+    }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
     const uint32_t wpb = kBlock / kWave;
@@ -884,16 +983,17 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
         old = __shfl(old, leader, kWave);
         lb = __shfl(lb, leader, kWave);
         cb = __shfl(cb, leader, kWave);
+        if (mn) write_strips(w.strip_tok[fp] + (size_t)L * w.strip_cap, w.strip_cap, (uint32_t)old,
+                             (uint32_t)(old >> 32), dpre, dsum, mn);
         if (!any) continue;
+        // positions and entries fit: the prologue checked n + nc and log + nc
         const uint32_t ra = (uint32_t)__popcll(ma & mask_lt());
         const uint32_t le = lb + ra;
-        if (le >= w.arena) continue;   // the next step retires the lane (arena bit)
         const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
         w.wlog[e] = make_int2(dd.w, dd.z);
         uint32_t pi;
         if (isnew) {
             pi = (uint32_t)old + (uint32_t)__popcll(mn & mask_lt());
-            if (pi >= Q) continue;     // the next step retires the lane (frontier bit)
             const size_t q = (size_t)L * Q + pi;
             w.tok_state[fp][q] = dst;
             w.tok_off[fp][q] = (uint32_t)(old >> 32) + dpre;
@@ -974,52 +1074,31 @@ __global__ __launch_bounds__(kWave) void k_backtrack(Work w)
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_clear_dirty(const Work &w, int grid, hipStream_t s)
+hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_clear, dim3(grid), dim3(kBlock), 0, s, w);
-    return hipGetLastError();
-}
-
-hipError_t launch_init(const Work &w, int grid, hipStream_t s)
-{
-    (void)grid;
-    hipLaunchKernelGGL(k_init, dim3(1), dim3(kWave), 0, s, w);
-    return hipGetLastError();
-}
-
-hipError_t launch_lpmax(const Work &w, int grid, hipStream_t s)
-{
-    if (w.lp_dtype == 1) hipLaunchKernelGGL(k_lpmax<__half>, dim3(grid), dim3(kBlock), 0, s, w);
-    else hipLaunchKernelGGL(k_lpmax<float>, dim3(grid), dim3(kBlock), 0, s, w);
-    return hipGetLastError();
-}
-
-hipError_t launch_step(const Work &w, int t, int grid, hipStream_t s)
-{
-    if (w.lp_dtype == 1) {
-        hipLaunchKernelGGL(k_max<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
-        hipLaunchKernelGGL(k_expand<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
-    } else {
-        hipLaunchKernelGGL(k_max<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
-        hipLaunchKernelGGL(k_expand<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+    const bool f16 = w.lp_dtype == 1;
+    switch (id) {
+    case kKClear: hipLaunchKernelGGL(k_clear, dim3(grid), dim3(kBlock), 0, s, w); break;
+    case kKInit: hipLaunchKernelGGL(k_init, dim3(1), dim3(kWave), 0, s, w); break;
+    case kKLpmax:
+        if (f16) hipLaunchKernelGGL(k_lpmax<__half>, dim3(grid), dim3(kBlock), 0, s, w);
+        else hipLaunchKernelGGL(k_lpmax<float>, dim3(grid), dim3(kBlock), 0, s, w);
+        break;
+    case kKMax:
+        if (f16) hipLaunchKernelGGL(k_max<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        else hipLaunchKernelGGL(k_max<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        break;
+    case kKExpand:
+        if (f16) hipLaunchKernelGGL(k_expand<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        else hipLaunchKernelGGL(k_expand<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        break;
+    case kKFinalize: hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kBlock), 0, s, w, t); break;
+    case kKEpsExpand: hipLaunchKernelGGL(k_eps_expand, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
+    case kKEpsResolve: hipLaunchKernelGGL(k_eps_resolve, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
+    case kKEpsApply: hipLaunchKernelGGL(k_eps_apply, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
+    case kKBacktrack: hipLaunchKernelGGL(k_backtrack, dim3(w.max_lanes), dim3(kWave), 0, s, w); break;
+    default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kBlock), 0, s, w, t);
-    return hipGetLastError();
-}
-
-hipError_t launch_closure(const Work &w, int t, int grid, hipStream_t s)
-{
-    for (int k = 1; k <= w.eps_iterations; ++k) {
-        hipLaunchKernelGGL(k_eps_expand, dim3(grid), dim3(kBlock), 0, s, w, t, k);
-        hipLaunchKernelGGL(k_eps_resolve, dim3(grid), dim3(kBlock), 0, s, w, t, k);
-        hipLaunchKernelGGL(k_eps_apply, dim3(grid), dim3(kBlock), 0, s, w, t, k);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_backtrack(const Work &w, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_backtrack, dim3(w.max_lanes), dim3(kWave), 0, s, w);
     return hipGetLastError();
 }
 
