@@ -125,7 +125,21 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (scales rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1:
         print("bench.py: this decoder runs on one GPU; utterances shard across GPUs with no "
               "exchange, so there is no multi-GPU step to time (use --gpus 1)", file=sys.stderr)

@@ -189,7 +189,7 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
 }
 
 // Per-wavefront LDS buffer of claimed slots in the expand pass.
-constexpr uint32_t kClaimBuf = 512;
+constexpr uint32_t kClaimBuf = 1024;
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -311,6 +311,13 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(Work w)
 
 enum { kModeMax = 0, kModeExpand = 1 };
 
+// A wavefront walks its run of the flattened slot space in units of kUnit slots:
+// lane l owns slots j0 + r*64 + l for r < kR, so one window of token offsets and
+// one round of independent arc loads serve kR strips (memory-level parallelism
+// for the latency-bound gathers).
+constexpr int kR = 4;
+constexpr uint32_t kUnit = kWave * kR;
+
 template <int MODE, typename LPT>
 __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            uint32_t *cbuf)
@@ -343,27 +350,33 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
         const float lpm = tab.f0[L];
         const float cut = tab.f1[L];
         LaneCtl &c = w.ctl[L];
-        uint32_t j0 = (s - tab.base[L]) * (uint32_t)kWave;
+        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
 
         // first token of the run, from the strip map built with the frontier
-        uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L])];
+        uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
         if (cur >= n) cur = 0;
         float run = -__builtin_inff();
         float posted = -__builtin_inff();
+        uint32_t admitted = 0;
         if (MODE == kModeMax) {
             posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
             run = posted;
         }
-        uint32_t admitted = 0;
-        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
 
-        for (; s < seg_end; ++s, j0 += kWave) {
-            const uint32_t j = j0 + (uint32_t)lane;
-            const bool valid = j < arcs;
-            bool resolved = !valid;
-            uint32_t tok = cur, toff = 0;
-            int32_t ab = 0;
-            float sc = 0.0f, ub = 0.0f;
+        for (; s < seg_end; ++s) {
+            const uint32_t j0 = (s - tab.base[L]) * kUnit;
+            uint32_t j[kR], tok[kR], toff[kR];
+            int32_t ab[kR];
+            float sc[kR], ub[kR];
+            bool valid[kR], resolved[kR];
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                j[r] = j0 + (uint32_t)(r * kWave + lane);
+                valid[r] = j[r] < arcs;
+                resolved[r] = !valid[r];
+                tok[r] = cur; toff[r] = 0; ab[r] = 0; sc[r] = 0.0f; ub[r] = 0.0f;
+            }
+            // resolve slot -> token against register-held windows of 64 offsets
             uint32_t wb = cur;
             for (;;) {
                 const uint32_t idx = wb + (uint32_t)lane;
@@ -373,75 +386,122 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
                 const float sc_l = in ? score[idx] : 0.0f;
                 const float ub_l = in ? ubv[idx] : 0.0f;
                 const uint32_t o_next = (wb + kWave < n) ? off[wb + kWave] : 0xFFFFFFFFu;
-                int i = 0;
+                bool pending = false;
 #pragma unroll
-                for (int st = 32; st >= 1; st >>= 1) {
-                    const uint32_t v = __shfl(o, i + st, kWave);
-                    if (v <= j) i += st;
+                for (int r = 0; r < kR; ++r) {
+                    int i = 0;
+#pragma unroll
+                    for (int st = 32; st >= 1; st >>= 1) {
+                        const uint32_t v = __shfl(o, i + st, kWave);
+                        if (v <= j[r]) i += st;
+                    }
+                    const uint32_t g_o = __shfl(o, i, kWave);
+                    const int32_t g_ab = __shfl(ab_l, i, kWave);
+                    const float g_sc = __shfl(sc_l, i, kWave);
+                    const float g_ub = __shfl(ub_l, i, kWave);
+                    if (!resolved[r] && (i < kWave - 1 || j[r] < o_next)) {
+                        tok[r] = wb + (uint32_t)i; toff[r] = g_o; ab[r] = g_ab; sc[r] = g_sc; ub[r] = g_ub;
+                        resolved[r] = true;
+                    }
+                    pending |= !resolved[r];
                 }
-                const uint32_t g_o = __shfl(o, i, kWave);
-                const int32_t g_ab = __shfl(ab_l, i, kWave);
-                const float g_sc = __shfl(sc_l, i, kWave);
-                const float g_ub = __shfl(ub_l, i, kWave);
-                if (!resolved && (i < kWave - 1 || j < o_next)) {
-                    tok = wb + (uint32_t)i; toff = g_o; ab = g_ab; sc = g_sc; ub = g_ub;
-                    resolved = true;
-                }
-                if (__ballot(!resolved) == 0ull) break;
+                if (__ballot(pending) == 0ull) break;
                 wb += kWave;
             }
-            cur = __shfl(tok, kWave - 1, kWave);
-            const uint32_t arc = (uint32_t)ab + (j - toff);
-            const bool live = valid && tok < n && arc < (uint32_t)w.num_arcs;
+            cur = __shfl(tok[kR - 1], kWave - 1, kWave);
+
+            // issue every arc load of the unit before consuming any
+            uint32_t arc[kR];
+            bool go[kR];
+            float wt[kR];
+            uint32_t il[kR];
+            int32_t dst[kR];
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                arc[r] = (uint32_t)ab[r] + (j[r] - toff[r]);
+                const bool live = valid[r] && tok[r] < n && arc[r] < (uint32_t)w.num_arcs;
+                go[r] = live && (MODE == kModeMax ? ub[r] + lpm > run : ub[r] + lpm > cut);
+                wt[r] = go[r] ? w.weight[arc[r]] : 0.0f;
+                il[r] = (go[r] && row) ? (uint32_t)w.ilabel[arc[r]] : 0u;
+                dst[r] = (MODE == kModeExpand && go[r] && row) ? w.dest[arc[r]] : 0;
+            }
+            float e[kR];
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                e[r] = sc[r] + wt[r];
+                if (row) e[r] = e[r] + (go[r] ? lp_at(row, il[r]) : 0.0f);
+            }
 
             if (MODE == kModeMax) {
                 float m = -__builtin_inff();
-                if (live && ub + lpm > run) {
-                    float e = sc + w.weight[arc];
-                    if (row) e = e + lp_at(row, w.ilabel[arc]);
-                    m = e;
-                }
+#pragma unroll
+                for (int r = 0; r < kR; ++r)
+                    if (go[r]) m = fmaxf(m, e[r]);
                 m = wave_max(m);
                 run = fmaxf(run, m);
             } else {
-                bool first = false;
-                int slot = -1;
+                bool adm[kR], first[kR];
+                int slot[kR];
+                uint32_t hh[kR], old[kR];
                 unsigned long long fkey = 0ull;
-                if (live && ub + lpm > cut) {
-                    // destination fetched with the arc so the hash insert of an
-                    // admitted candidate does not wait for another round trip
-                    const float wt = w.weight[arc];
-                    const int32_t dst = row ? w.dest[arc] : 0;
-                    float e = sc + wt;
-                    if (row) e = e + lp_at(row, w.ilabel[arc]);
-                    if (e > cut) {
-                        ++admitted;
-                        const unsigned long long key = cand_key(e, (int32_t)arc);
-                        if (ph == kPhReal) {
-                            slot = hash_claim(tbl, w.hash_mask, dst, &first);
-                            if (slot < 0) atomicOr(&c.overflow, kOvfHash);
-                            else atomicMax(&tbl[slot].payload, key);
-                        } else {
-                            fkey = key;
-                        }
-                    }
+#pragma unroll
+                for (int r = 0; r < kR; ++r) {
+                    adm[r] = go[r] && e[r] > cut;
+                    first[r] = false;
+                    slot[r] = -1;
+                    admitted += adm[r] ? 1u : 0u;
                 }
                 if (ph == kPhReal) {
+                    // first probe of every admitted candidate in flight at once
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        hh[r] = hash_state((uint32_t)dst[r]) & w.hash_mask;
+                        old[r] = adm[r] ? atomicCAS(&tbl[hh[r]].key, 0u, (uint32_t)dst[r] + 1u) : 0u;
+                    }
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        if (!adm[r]) continue;
+                        const uint32_t want = (uint32_t)dst[r] + 1u;
+                        if (old[r] == 0u) { first[r] = true; slot[r] = (int)hh[r]; }
+                        else if (old[r] == want) slot[r] = (int)hh[r];
+                        else {
+                            // collision: continue probing after the first slot
+                            uint32_t h = (hh[r] + 1u) & w.hash_mask;
+                            for (int probe = 1; probe < kMaxProbes; ++probe) {
+                                const uint32_t o2 = atomicCAS(&tbl[h].key, 0u, want);
+                                if (o2 == 0u) { first[r] = true; slot[r] = (int)h; break; }
+                                if (o2 == want) { slot[r] = (int)h; break; }
+                                h = (h + 1u) & w.hash_mask;
+                            }
+                        }
+                        if (slot[r] < 0) atomicOr(&c.overflow, kOvfHash);
+                        else atomicMax(&tbl[slot[r]].payload, cand_key(e[r], (int32_t)arc[r]));
+                    }
                     // first claimers go to this wavefront's LDS buffer, flushed
                     // with one atomic on the lane's claims counter
-                    const unsigned long long fm = __ballot(first);
-                    if (fm) {
-                        if (cb_n + kWave > kClaimBuf) {
-                            flush_claims(w, L, &c.nclaims, cbuf, cb_n);
-                            cb_n = 0;
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) {
+                        const unsigned long long fm = __ballot(first[r]);
+                        if (fm) {
+                            if (cb_n + kWave > kClaimBuf) {
+                                flush_claims(w, L, &c.nclaims, cbuf, cb_n);
+                                cb_n = 0;
+                            }
+                            if (first[r]) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot[r];
+                            cb_n += (uint32_t)__popcll(fm);
                         }
-                        if (first) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot;
-                        cb_n += (uint32_t)__popcll(fm);
                     }
                 } else {
 #pragma unroll
-                    for (int d = kWave / 2; d >= 1; d >>= 1) {
-                        const unsigned long long o = __shfl_xor(fkey, d, kWave);
+                    for (int r = 0; r < kR; ++r) {
+                        if (adm[r]) {
+                            const unsigned long long k = cand_key(e[r], (int32_t)arc[r]);
+                            fkey = k > fkey ? k : fkey;
+                        }
+                    }
+#pragma unroll
+                    for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
+                        const unsigned long long o = __shfl_xor(fkey, dd, kWave);
                         fkey = o > fkey ? o : fkey;
                     }
                     if (lane == 0 && fkey) atomicMax(&c.final_key, fkey);
@@ -476,7 +536,7 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         float lpm = 0.0f, f1 = 0.0f;
         if (ph == kPhReal) lpm = w.lpmax[(size_t)L * w.max_frames + t];
         if (MODE == kModeExpand && ph != kPhNone) f1 = ord2f(c.maxkey[p]) - c.beam[p];
-        if (ph != kPhNone && n > 0u && arcs > 0u) units = (arcs + kWave - 1) / kWave;
+        if (ph != kPhNone && n > 0u && arcs > 0u) units = (arcs + kUnit - 1) / kUnit;
         tab.n[L] = n;
         tab.arcs[L] = arcs;
         tab.ph[L] = ph;
@@ -754,6 +814,7 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
 __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
 {
     __shared__ LaneTab tab;
+    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -787,43 +848,66 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
     const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
+    uint32_t *cbuf = cbufs[threadIdx.x / kWave];
     for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
         LaneCtl &c = w.ctl[L];
         HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
-        uint32_t n_arcs = 0, n_adm = 0;
+        // the 64 sources of this unit and their epsilon ranges
         const uint32_t tok = (i < tab.n[L])
             ? ((k == 1) ? i : w.changed[k & 1][(size_t)L * w.claims_cap + i]) : 0xFFFFFFFFu;
+        int32_t eb = 0;
+        uint32_t ed = 0;
+        float sc = 0.0f;
         if (tok < Q) {
             const size_t q = (size_t)L * Q + tok;
-            const int32_t s = w.tok_state[fp][q];
-            const float sc = w.tok_score[fp][q];
-            const StateInfo si = w.sinfo[s];
-            for (int32_t a = si.eps_b; a < si.emit_b; ++a) {
-                const float e = sc + w.weight[a];
-                ++n_arcs;
+            const StateInfo si = w.sinfo[w.tok_state[fp][q]];
+            sc = w.tok_score[fp][q];
+            eb = si.eps_b;
+            ed = (uint32_t)(si.emit_b - si.eps_b);
+        }
+        uint32_t dsum;
+        const uint32_t dpre = wave_excl_sum(ed, &dsum);
+        // all epsilon arcs of the unit, 64 at a time (balanced within the wave)
+        uint32_t n_adm = 0, cb_n = 0;
+        for (uint32_t x0 = 0; x0 < dsum; x0 += kWave) {
+            const uint32_t x = x0 + (uint32_t)lane;
+            int src = 0;
+#pragma unroll
+            for (int st = 32; st >= 1; st >>= 1) {
+                const uint32_t v = __shfl(dpre, src + st, kWave);
+                if (v <= x) src += st;
+            }
+            const int32_t a = __shfl(eb, src, kWave) + (int32_t)(x - __shfl(dpre, src, kWave));
+            const float ssc = __shfl(sc, src, kWave);
+            bool first = false;
+            int slot = -1;
+            if (x < dsum) {
+                const float e = ssc + w.weight[a];
                 if (e > cutoff) {
                     ++n_adm;
-                    bool first = false;
-                    const int slot = hash_claim(tbl, w.hash_mask, w.dest[a], &first);
-                    if (slot < 0) {
-                        atomicOr(&c.overflow, kOvfHash);
-                    } else {
-                        atomicMax(&tbl[slot].payload, cand_key(e, a));
-                        if (first) {
-                            const uint32_t idx = atomicAdd(&c.nclaims_eps[k & 1], 1u);
-                            if (idx < w.claims_cap) w.claims[(size_t)L * w.claims_cap + idx] = (uint32_t)slot;
-                        }
-                    }
+                    slot = hash_claim(tbl, w.hash_mask, w.dest[a], &first);
+                    if (slot < 0) atomicOr(&c.overflow, kOvfHash);
+                    else atomicMax(&tbl[slot].payload, cand_key(e, a));
                 }
             }
+            const unsigned long long fm = __ballot(first);
+            if (fm) {
+                if (cb_n + kWave > kClaimBuf) {
+                    flush_claims(w, L, &c.nclaims_eps[k & 1], cbuf, cb_n);
+                    cb_n = 0;
+                }
+                if (first) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot;
+                cb_n += (uint32_t)__popcll(fm);
+            }
         }
-        const uint32_t sa = wave_sum(n_arcs), sd = wave_sum(n_adm);
-        if (lane == 0 && sa) {
+        if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], cbuf, cb_n);
+        const uint32_t sd = wave_sum(n_adm);
+        if (lane == 0 && dsum) {
             uint32_t *rec = step_rec(w, L, t);
-            atomicAdd(rec + kRecEpsArcs, sa);
+            atomicAdd(rec + kRecEpsArcs, dsum);
             if (sd) atomicAdd(rec + kRecEpsAdmitted, sd);
         }
     }
