@@ -42,6 +42,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
       finalize 28 D + 20 n'             (claim + payload read-back + targeted clear; next-frontier token 12 B + winners-log entry 8 B)
       eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, claims, changed tokens)
       path     20 n + 6 S + 12 C + 28 D + 20 n' + e V F (+ eps terms): the whole step, counted once
+               (also the persistent kernel's bytes: it runs every phase of the frame loop)
     """
     n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
     E, De, Ne = st["eps_arcs"], st["eps_distinct"], st["eps_changed"]
@@ -55,6 +56,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
         "eps_apply": 20 * Ne,
     }
     path = 20 * n + 6 * S + 12 * C + 28 * D + 20 * D + row + 16 * E + 28 * De + 20 * Ne
+    per["persistent"] = path      # the persistent kernel runs the whole frame loop
     return per, path
 
 
@@ -120,6 +122,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (1-5); 3 = HLG-scale")
     ap.add_argument("--eager", action="store_true", help="plain launches instead of the captured graph")
+    ap.add_argument("--mode", choices=("graph", "persistent"), default="graph",
+                    help="graph: one kernel per phase, captured as a hipGraph; persistent: the frame "
+                         "loop as one cooperative kernel with grid barriers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
@@ -158,7 +163,7 @@ def main():
     dg = wb.Graph(graph, device=0)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
-                     grid_blocks=args.grid)
+                     grid_blocks=args.grid, persistent=args.mode == "persistent")
     x = torch.from_numpy(lp).to(dev)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -223,7 +228,8 @@ def main():
                                f"{graph.num_arcs} arcs, power-law out-degree), log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
-                   "graph_replay": not args.eager},
+                   "execution": "persistent cooperative kernel" if args.mode == "persistent"
+                   else ("per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay")},
         "arcs_expanded_per_s": round(arcs_ps, 1),
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),

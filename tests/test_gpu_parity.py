@@ -39,14 +39,18 @@ def _golden_cases():
     return out
 
 
+MODES = {"graph": dict(use_graphs=True), "eager": dict(use_graphs=False),
+         "persistent": dict(persistent=True)}
+
+
 @pytest.mark.parametrize("name,g,lp,case,eps,ap", _golden_cases(), ids=lambda x: x if isinstance(x, str) else "")
-@pytest.mark.parametrize("use_graphs", [True, False])
-def test_golden(name, g, lp, case, eps, ap, use_graphs):
-    _say("golden", name, use_graphs)
+@pytest.mark.parametrize("mode", list(MODES))
+def test_golden(name, g, lp, case, eps, ap, mode):
+    _say("golden", name, mode)
     T = lp.shape[0]
     lpb = lp.reshape(1, T, g.vocab)
     r, steps, _ = gpu_decode(g, lpb, [T], case["beam"], case["max_active"], case.get("min_active", 0),
-                             bool(ap), eps, use_graphs=use_graphs)
+                             bool(ap), eps, **MODES[mode])
     assert list(r.arcs[0]) == case["expect_arcs"]
     if "expect_words" in case:
         assert list(r.words[0]) == case["expect_words"]
@@ -86,7 +90,8 @@ def test_random_small_graphs(eps):
     for seed in range(150):
         g, lp, L, beam, ma, mi, ap, P = _random_case(seed + (1000 if eps else 0), eps)
         _say("random", eps, seed, lp.shape, beam, ma, mi, ap, P)
-        r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, use_graphs=bool(seed % 2))
+        mode = ("persistent", "graph", "eager")[seed % 3]
+        r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, **MODES[mode])
         o = oracle_lanes(g, lp, L, beam, ma, mi, ap, P)
         compare_batch(r, steps, o)
 
@@ -123,18 +128,22 @@ def test_workload_parity(cid, workload_graphs):
     wl = synth.WORKLOADS[cid]
     _say("workload", cid, lp.shape, lp.dtype)
     dg = wb.Graph(g)
+    runs = {}
     try:
-        r, steps, stats = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
-                                     dgraph=dg)
+        for mode in ("graph", "persistent"):
+            runs[mode] = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
+                                    dgraph=dg, **MODES[mode])
+            _say("  gpu", mode, "done; stats", runs[mode][2])
     finally:
         dg.release()
-    _say("  gpu done; stats", stats)
     o = oracle_lanes(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations)
     _say("  oracle done")
-    compare_batch(r, steps, o)
-    for b in range(lp.shape[0]):
-        check_path(g, lp[b].astype(np.float32), int(L[b]), r.arcs[b], r.words[b], r.scores[b], 1)
-    assert stats["arcs"] == sum(int(x["steps"][:, 4].sum()) for x in o)
+    for mode, (r, steps, stats) in runs.items():
+        _say("  compare", mode)
+        compare_batch(r, steps, o)
+        for b in range(lp.shape[0]):
+            check_path(g, lp[b].astype(np.float32), int(L[b]), r.arcs[b], r.words[b], r.scores[b], 1)
+        assert stats["arcs"] == sum(int(x["steps"][:, 4].sum()) for x in o)
 
 
 def test_graph_replay_equals_eager_and_is_idempotent():

@@ -268,6 +268,10 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
     c.last_step = -1;
     c.phase_final = kPhNone;
     c.cnt[1] = 0ull;
+    if (L == 0 && w.gsync) {
+        w.gsync->count = 0u;
+        w.gsync->abort = 0u;
+    }
     if (!on) { c.cnt[0] = 0ull; return; }
     const int32_t s = w.start_state;
     const StateInfo si = w.sinfo[s];
@@ -318,195 +322,248 @@ enum { kModeMax = 0, kModeExpand = 1 };
 constexpr int kR = 4;
 constexpr uint32_t kUnit = kWave * kR;
 
-template <int MODE, typename LPT>
-__device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
-                                           uint32_t *cbuf)
+// Candidates of one unit as seen by one lane of the wavefront.
+struct UnitData {
+    float e[kR];          // end score (valid where bit r of `live` is set)
+    uint32_t arc[kR];
+    int32_t dst[kR];
+    uint32_t live;        // bit r: slot r is a candidate whose arc was loaded
+};
+
+// The lane of the batch a wavefront is working on.
+struct LaneView {
+    int L, ph;
+    uint32_t n, arcs;
+    const uint32_t *off;
+    const int32_t *abeg;
+    const float *score;
+    const float *ubv;
+    const void *row;      // log-prob row of the step (null on the final step)
+    float lpm;            // its maximum (0 on the final step)
+};
+
+__device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab, int t, const LpDesc &d, int L)
 {
-    uint32_t cb_n = 0;
+    LaneView v;
     const int p = t & 1;
-    const int nl = w.max_lanes;
-    const uint32_t total = tab.base[nl];
-    if (total == 0u) return;
+    const size_t qo = (size_t)L * w.frontier_cap;
+    v.L = L;
+    v.ph = tab.ph[L];
+    v.n = tab.n[L];
+    v.arcs = tab.arcs[L];
+    v.off = w.tok_off[p] + qo;
+    v.abeg = w.tok_abeg[p] + qo;
+    v.score = w.tok_score[p] + qo;
+    v.ubv = w.tok_ub[p] + qo;
+    const long long eoff = (long long)L * d.stride_b + (long long)t * d.stride_t;
+    v.row = (v.ph == kPhReal)
+        ? (const void *)((const char *)d.base + eoff * (w.lp_dtype == 1 ? 2 : 4)) : nullptr;
+    v.lpm = tab.f0[L];
+    return v;
+}
+
+// Loads unit u of lane v.L: lane l of the wavefront resolves slots
+// j0 + r*64 + l against register-held windows of 64 token offsets (start token
+// `cur`, moved forward), then issues every arc load of the unit before using
+// any. Tokens whose bound ub + maxlp <= skip are not expanded (exact: no arc of
+// theirs can end above skip).
+template <typename LPT>
+__device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
+                                          float skip, bool want_dest, UnitData &ud)
+{
     const int lane = wlane();
+    const uint32_t n = v.n;
+    const uint32_t j0 = u * kUnit;
+    uint32_t j[kR], tok[kR], toff[kR];
+    int32_t ab[kR];
+    float sc[kR], ub[kR];
+    bool valid[kR], resolved[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        j[r] = j0 + (uint32_t)(r * kWave + lane);
+        valid[r] = j[r] < v.arcs;
+        resolved[r] = !valid[r];
+        tok[r] = cur; toff[r] = 0; ab[r] = 0; sc[r] = 0.0f; ub[r] = 0.0f;
+    }
+    uint32_t wb = cur;
+    for (;;) {
+        const uint32_t idx = wb + (uint32_t)lane;
+        const bool in = idx < n;
+        const uint32_t o = in ? v.off[idx] : 0xFFFFFFFFu;
+        const int32_t ab_l = in ? v.abeg[idx] : 0;
+        const float sc_l = in ? v.score[idx] : 0.0f;
+        const float ub_l = in ? v.ubv[idx] : 0.0f;
+        const uint32_t o_next = (wb + kWave < n) ? v.off[wb + kWave] : 0xFFFFFFFFu;
+        bool pending = false;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            int i = 0;
+#pragma unroll
+            for (int st = 32; st >= 1; st >>= 1) {
+                const uint32_t x = __shfl(o, i + st, kWave);
+                if (x <= j[r]) i += st;
+            }
+            const uint32_t g_o = __shfl(o, i, kWave);
+            const int32_t g_ab = __shfl(ab_l, i, kWave);
+            const float g_sc = __shfl(sc_l, i, kWave);
+            const float g_ub = __shfl(ub_l, i, kWave);
+            if (!resolved[r] && (i < kWave - 1 || j[r] < o_next)) {
+                tok[r] = wb + (uint32_t)i; toff[r] = g_o; ab[r] = g_ab; sc[r] = g_sc; ub[r] = g_ub;
+                resolved[r] = true;
+            }
+            pending |= !resolved[r];
+        }
+        if (__ballot(pending) == 0ull) break;
+        wb += kWave;
+    }
+    cur = __shfl(tok[kR - 1], kWave - 1, kWave);
+
+    const LPT *row = (const LPT *)v.row;
+    float wt[kR];
+    uint32_t il[kR];
+    ud.live = 0u;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        ud.arc[r] = (uint32_t)ab[r] + (j[r] - toff[r]);
+        const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] + v.lpm > skip;
+        if (go) ud.live |= 1u << r;
+        wt[r] = go ? w.weight[ud.arc[r]] : 0.0f;
+        il[r] = (go && row) ? (uint32_t)w.ilabel[ud.arc[r]] : 0u;
+        ud.dst[r] = (want_dest && go && row) ? w.dest[ud.arc[r]] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        float e = sc[r] + wt[r];
+        if (row) e = e + (((ud.live >> r) & 1u) ? lp_at(row, il[r]) : 0.0f);
+        ud.e[r] = e;
+    }
+}
+
+__device__ __forceinline__ float unit_max(const UnitData &ud)
+{
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        if ((ud.live >> r) & 1u) m = fmaxf(m, ud.e[r]);
+    return wave_max(m);
+}
+
+// Admits a unit's candidates (end > cut, strict) and recombines them: on a real
+// step through the lane's hash (CAS on the first probe of every candidate at
+// once, then a posted u64 atomicMax of the key), on the final step through one
+// wavefront-reduced atomicMax of the lane's final key. First claimers of a slot
+// go to the wavefront's LDS claims buffer.
+__device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, const UnitData &ud,
+                                           uint32_t *cbuf, uint32_t &cb_n, uint32_t &admitted)
+{
+    LaneCtl &c = w.ctl[L];
+    const int lane = wlane();
+    bool adm[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        adm[r] = ((ud.live >> r) & 1u) && ud.e[r] > cut;
+        admitted += adm[r] ? 1u : 0u;
+    }
+    if (ph == kPhReal) {
+        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
+        uint32_t hh[kR], old[kR];
+        bool first[kR];
+        int slot[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            hh[r] = hash_state((uint32_t)ud.dst[r]) & w.hash_mask;
+            old[r] = adm[r] ? atomicCAS(&tbl[hh[r]].key, 0u, (uint32_t)ud.dst[r] + 1u) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            first[r] = false;
+            slot[r] = -1;
+            if (!adm[r]) continue;
+            const uint32_t want = (uint32_t)ud.dst[r] + 1u;
+            if (old[r] == 0u) { first[r] = true; slot[r] = (int)hh[r]; }
+            else if (old[r] == want) slot[r] = (int)hh[r];
+            else {
+                uint32_t h = (hh[r] + 1u) & w.hash_mask;
+                for (int probe = 1; probe < kMaxProbes; ++probe) {
+                    const uint32_t o2 = atomicCAS(&tbl[h].key, 0u, want);
+                    if (o2 == 0u) { first[r] = true; slot[r] = (int)h; break; }
+                    if (o2 == want) { slot[r] = (int)h; break; }
+                    h = (h + 1u) & w.hash_mask;
+                }
+            }
+            if (slot[r] < 0) atomicOr(&c.overflow, kOvfHash);
+            else atomicMax(&tbl[slot[r]].payload, cand_key(ud.e[r], (int32_t)ud.arc[r]));
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const unsigned long long fm = __ballot(first[r]);
+            if (fm) {
+                if (cb_n + kWave > kClaimBuf) {
+                    flush_claims(w, L, &c.nclaims, cbuf, cb_n);
+                    cb_n = 0;
+                }
+                if (first[r]) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot[r];
+                cb_n += (uint32_t)__popcll(fm);
+            }
+        }
+    } else {
+        unsigned long long fkey = 0ull;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            if (adm[r]) {
+                const unsigned long long k = cand_key(ud.e[r], (int32_t)ud.arc[r]);
+                fkey = k > fkey ? k : fkey;
+            }
+        }
+#pragma unroll
+        for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
+            const unsigned long long o = __shfl_xor(fkey, dd, kWave);
+            fkey = o > fkey ? o : fkey;
+        }
+        if (lane == 0 && fkey) atomicMax(&c.final_key, fkey);
+    }
+}
+
+// This wavefront's contiguous, equal share [s, s_end) of `total` units.
+__device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t *s_end)
+{
     const uint32_t wpb = kBlock / kWave;
     const uint32_t nwaves = gridDim.x * wpb;
     const uint32_t wid = blockIdx.x * wpb + threadIdx.x / kWave;
-    uint32_t s = (uint32_t)(((unsigned long long)total * wid) / nwaves);
-    const uint32_t s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
-    const uint32_t Q = w.frontier_cap;
+    *s = (uint32_t)(((unsigned long long)total * wid) / nwaves);
+    *s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
+}
 
+// Units [s, s_end) of the flattened slot space: exact max (MODE max, with the
+// bound skip against the running max) or admit + recombine (MODE expand, with
+// the bound skip against the cutoff).
+template <int MODE, typename LPT>
+__device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
+                                           uint32_t s, uint32_t s_end, uint32_t *cbuf)
+{
+    const int p = t & 1;
+    const int nl = w.max_lanes;
+    const int lane = wlane();
+    uint32_t cb_n = 0;
     while (s < s_end) {
         const int L = find_lane(tab.base, nl, s);
         const uint32_t seg_end = min(s_end, tab.base[L + 1]);
-        const uint32_t n = tab.n[L], arcs = tab.arcs[L];
-        const int ph = tab.ph[L];
-        const size_t qo = (size_t)L * Q;
-        const uint32_t *off = w.tok_off[p] + qo;
-        const int32_t *abeg = w.tok_abeg[p] + qo;
-        const float *score = w.tok_score[p] + qo;
-        const float *ubv = w.tok_ub[p] + qo;
-        const LPT *row = (ph == kPhReal)
-            ? (const LPT *)d.base + (long long)L * d.stride_b + (long long)t * d.stride_t : nullptr;
-        const float lpm = tab.f0[L];
-        const float cut = tab.f1[L];
+        const LaneView v = lane_view(w, tab, t, d, L);
         LaneCtl &c = w.ctl[L];
-        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
-
-        // first token of the run, from the strip map built with the frontier
         uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
-        if (cur >= n) cur = 0;
-        float run = -__builtin_inff();
-        float posted = -__builtin_inff();
-        uint32_t admitted = 0;
+        if (cur >= v.n) cur = 0;
+        float run = -__builtin_inff(), posted = -__builtin_inff();
         if (MODE == kModeMax) {
             posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
             run = posted;
         }
-
+        const float cut = tab.f1[L];
+        uint32_t admitted = 0;
         for (; s < seg_end; ++s) {
-            const uint32_t j0 = (s - tab.base[L]) * kUnit;
-            uint32_t j[kR], tok[kR], toff[kR];
-            int32_t ab[kR];
-            float sc[kR], ub[kR];
-            bool valid[kR], resolved[kR];
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                j[r] = j0 + (uint32_t)(r * kWave + lane);
-                valid[r] = j[r] < arcs;
-                resolved[r] = !valid[r];
-                tok[r] = cur; toff[r] = 0; ab[r] = 0; sc[r] = 0.0f; ub[r] = 0.0f;
-            }
-            // resolve slot -> token against register-held windows of 64 offsets
-            uint32_t wb = cur;
-            for (;;) {
-                const uint32_t idx = wb + (uint32_t)lane;
-                const bool in = idx < n;
-                const uint32_t o = in ? off[idx] : 0xFFFFFFFFu;
-                const int32_t ab_l = in ? abeg[idx] : 0;
-                const float sc_l = in ? score[idx] : 0.0f;
-                const float ub_l = in ? ubv[idx] : 0.0f;
-                const uint32_t o_next = (wb + kWave < n) ? off[wb + kWave] : 0xFFFFFFFFu;
-                bool pending = false;
-#pragma unroll
-                for (int r = 0; r < kR; ++r) {
-                    int i = 0;
-#pragma unroll
-                    for (int st = 32; st >= 1; st >>= 1) {
-                        const uint32_t v = __shfl(o, i + st, kWave);
-                        if (v <= j[r]) i += st;
-                    }
-                    const uint32_t g_o = __shfl(o, i, kWave);
-                    const int32_t g_ab = __shfl(ab_l, i, kWave);
-                    const float g_sc = __shfl(sc_l, i, kWave);
-                    const float g_ub = __shfl(ub_l, i, kWave);
-                    if (!resolved[r] && (i < kWave - 1 || j[r] < o_next)) {
-                        tok[r] = wb + (uint32_t)i; toff[r] = g_o; ab[r] = g_ab; sc[r] = g_sc; ub[r] = g_ub;
-                        resolved[r] = true;
-                    }
-                    pending |= !resolved[r];
-                }
-                if (__ballot(pending) == 0ull) break;
-                wb += kWave;
-            }
-            cur = __shfl(tok[kR - 1], kWave - 1, kWave);
-
-            // issue every arc load of the unit before consuming any
-            uint32_t arc[kR];
-            bool go[kR];
-            float wt[kR];
-            uint32_t il[kR];
-            int32_t dst[kR];
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                arc[r] = (uint32_t)ab[r] + (j[r] - toff[r]);
-                const bool live = valid[r] && tok[r] < n && arc[r] < (uint32_t)w.num_arcs;
-                go[r] = live && (MODE == kModeMax ? ub[r] + lpm > run : ub[r] + lpm > cut);
-                wt[r] = go[r] ? w.weight[arc[r]] : 0.0f;
-                il[r] = (go[r] && row) ? (uint32_t)w.ilabel[arc[r]] : 0u;
-                dst[r] = (MODE == kModeExpand && go[r] && row) ? w.dest[arc[r]] : 0;
-            }
-            float e[kR];
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                e[r] = sc[r] + wt[r];
-                if (row) e[r] = e[r] + (go[r] ? lp_at(row, il[r]) : 0.0f);
-            }
-
-            if (MODE == kModeMax) {
-                float m = -__builtin_inff();
-#pragma unroll
-                for (int r = 0; r < kR; ++r)
-                    if (go[r]) m = fmaxf(m, e[r]);
-                m = wave_max(m);
-                run = fmaxf(run, m);
-            } else {
-                bool adm[kR], first[kR];
-                int slot[kR];
-                uint32_t hh[kR], old[kR];
-                unsigned long long fkey = 0ull;
-#pragma unroll
-                for (int r = 0; r < kR; ++r) {
-                    adm[r] = go[r] && e[r] > cut;
-                    first[r] = false;
-                    slot[r] = -1;
-                    admitted += adm[r] ? 1u : 0u;
-                }
-                if (ph == kPhReal) {
-                    // first probe of every admitted candidate in flight at once
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        hh[r] = hash_state((uint32_t)dst[r]) & w.hash_mask;
-                        old[r] = adm[r] ? atomicCAS(&tbl[hh[r]].key, 0u, (uint32_t)dst[r] + 1u) : 0u;
-                    }
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        if (!adm[r]) continue;
-                        const uint32_t want = (uint32_t)dst[r] + 1u;
-                        if (old[r] == 0u) { first[r] = true; slot[r] = (int)hh[r]; }
-                        else if (old[r] == want) slot[r] = (int)hh[r];
-                        else {
-                            // collision: continue probing after the first slot
-                            uint32_t h = (hh[r] + 1u) & w.hash_mask;
-                            for (int probe = 1; probe < kMaxProbes; ++probe) {
-                                const uint32_t o2 = atomicCAS(&tbl[h].key, 0u, want);
-                                if (o2 == 0u) { first[r] = true; slot[r] = (int)h; break; }
-                                if (o2 == want) { slot[r] = (int)h; break; }
-                                h = (h + 1u) & w.hash_mask;
-                            }
-                        }
-                        if (slot[r] < 0) atomicOr(&c.overflow, kOvfHash);
-                        else atomicMax(&tbl[slot[r]].payload, cand_key(e[r], (int32_t)arc[r]));
-                    }
-                    // first claimers go to this wavefront's LDS buffer, flushed
-                    // with one atomic on the lane's claims counter
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        const unsigned long long fm = __ballot(first[r]);
-                        if (fm) {
-                            if (cb_n + kWave > kClaimBuf) {
-                                flush_claims(w, L, &c.nclaims, cbuf, cb_n);
-                                cb_n = 0;
-                            }
-                            if (first[r]) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot[r];
-                            cb_n += (uint32_t)__popcll(fm);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) {
-                        if (adm[r]) {
-                            const unsigned long long k = cand_key(e[r], (int32_t)arc[r]);
-                            fkey = k > fkey ? k : fkey;
-                        }
-                    }
-#pragma unroll
-                    for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
-                        const unsigned long long o = __shfl_xor(fkey, dd, kWave);
-                        fkey = o > fkey ? o : fkey;
-                    }
-                    if (lane == 0 && fkey) atomicMax(&c.final_key, fkey);
-                }
-            }
+            UnitData ud;
+            load_unit<LPT>(w, v, s - tab.base[L], cur, MODE == kModeMax ? run : cut, MODE == kModeExpand, ud);
+            if (MODE == kModeMax) run = fmaxf(run, unit_max(ud));
+            else admit_unit(w, L, v.ph, cut, ud, cbuf, cb_n, admitted);
         }
         if (MODE == kModeExpand) {
             if (cb_n) flush_claims(w, L, &c.nclaims, cbuf, cb_n);
@@ -517,6 +574,15 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
             atomicMax(&c.maxkey[p], f2ord(run));
         }
     }
+}
+
+template <int MODE, typename LPT>
+__device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
+                                           uint32_t *cbuf)
+{
+    uint32_t s, s_end;
+    wave_share(tab.base[w.max_lanes], &s, &s_end);
+    walk_range<MODE, LPT>(w, tab, t, d, s, s_end, cbuf);
 }
 
 // Per-lane table for the two slot passes of step t.
@@ -549,7 +615,7 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
 
 // Step bookkeeping done once per step by thread L of workgroup 0 of k_max:
 // retire overflowed / dead lanes, the dynamic beam, the redirect, resets.
-__device__ void step_begin_lane(const Work &w, int t, int L)
+__device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
 {
     LaneCtl &c = w.ctl[L];
     const int ph = lane_phase(c, t);
@@ -615,13 +681,42 @@ __device__ void step_begin_lane(const Work &w, int t, int L)
     }
 }
 
+// Start of a step: the lane table of the step's slot space, then workgroup 0
+// runs the per-lane bookkeeping (beam update, retirements, resets).
+__device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
+{
+    slot_prologue<kModeMax>(w, tab, t);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
+}
+
+// After the exact maxima are known: every workgroup refreshes the cutoffs in its
+// table (the slot space is unchanged); workgroup 0 records them.
+__device__ __forceinline__ void step_cutoffs(const Work &w, int t, LaneTab &tab)
+{
+    __syncthreads();
+    if (threadIdx.x < (unsigned)w.max_lanes) {
+        const int L = (int)threadIdx.x;
+        const int p = t & 1;
+        // lanes without candidates (dead, redirected, retired) keep no maximum
+        if (tab.ph[L] != kPhNone && tab.n[L] > 0u && tab.arcs[L] > 0u) {
+            LaneCtl &c = w.ctl[L];
+            const float cut = ord2f(c.maxkey[p]) - c.beam[p];
+            tab.f1[L] = cut;
+            if (blockIdx.x == 0) {
+                step_rec(w, L, t)[kRecMax] = __float_as_uint(ord2f(c.maxkey[p]));
+                if (tab.ph[L] == kPhReal) c.cutoff = cut;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 template <typename LPT>
 __global__ __launch_bounds__(kBlock) void k_max(Work w, int t)
 {
     __shared__ LaneTab tab;
-    slot_prologue<kModeMax>(w, tab, t);
-    __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
+    step_open(w, t, tab);
     const LpDesc d = *w.lp;
     walk_slots<kModeMax, LPT>(w, tab, t, d, nullptr);
 }
@@ -630,18 +725,8 @@ template <typename LPT>
 __global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
 {
     __shared__ LaneTab tab;
-    slot_prologue<kModeExpand>(w, tab, t);
-    __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
-        const int L = (int)threadIdx.x;
-        if (tab.ph[L] != kPhNone) {
-            LaneCtl &c = w.ctl[L];
-            const int p = t & 1;
-            uint32_t *rec = step_rec(w, L, t);
-            rec[kRecMax] = __float_as_uint(ord2f(c.maxkey[p]));
-            if (tab.ph[L] == kPhReal) c.cutoff = tab.f1[L];
-        }
-    }
+    slot_prologue<kModeMax>(w, tab, t);
+    step_cutoffs(w, t, tab);
     __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
     const LpDesc d = *w.lp;
     walk_slots<kModeExpand, LPT>(w, tab, t, d, cbufs[threadIdx.x / kWave]);
@@ -649,9 +734,8 @@ __global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
 
 // -------------------------------------------------------------- k_finalize
 
-__global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
+__device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 {
-    __shared__ LaneTab tab;
     const int p = t & 1, np = p ^ 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -797,6 +881,12 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
     }
 }
 
+__global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
+{
+    __shared__ LaneTab tab;
+    ph_finalize(w, t, tab);
+}
+
 // ---------------------------------------------------------- epsilon closure
 // Pass k of the closure that follows step t (t = -1: the start frontier). The
 // frontier being closed has parity fp = (t + 1) & 1 and feeds step t + 1.
@@ -811,10 +901,8 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
     return c.status == kActive && (t < 0 || t < c.T);
 }
 
-__global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
+__device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, uint32_t *cbuf_wave)
 {
-    __shared__ LaneTab tab;
-    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -848,7 +936,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
     const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    uint32_t *cbuf = cbufs[threadIdx.x / kWave];
+    uint32_t *cbuf = cbuf_wave;
     for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
@@ -913,10 +1001,16 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
     }
 }
 
-// Decides, per claimed destination, append / replace / nothing (reads only).
-__global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
+__global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
 {
     __shared__ LaneTab tab;
+    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
+    ph_eps_expand(w, t, k, tab, cbufs[threadIdx.x / kWave]);
+}
+
+// Decides, per claimed destination, append / replace / nothing (reads only).
+__device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, LaneTab &tab)
+{
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -986,11 +1080,16 @@ __global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
     }
 }
 
-// Applies the decisions: fresh winners-log entries, appended tokens (with their
-// next-step class and arc offsets), replaced tokens, the next pass's sources.
-__global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
+__global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
 {
     __shared__ LaneTab tab;
+    ph_eps_resolve(w, t, k, tab);
+}
+
+// Applies the decisions: fresh winners-log entries, appended tokens (with their
+// next-step class and arc offsets), replaced tokens, the next pass's sources.
+__device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
+{
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -1096,6 +1195,12 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
     }
 }
 
+__global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
+{
+    __shared__ LaneTab tab;
+    ph_eps_apply(w, t, k, tab);
+}
+
 // -------------------------------------------------------------- k_backtrack
 // One wavefront per lane: lane 0 walks the winners chain from the result entry
 // (newest arc first), then the wavefront reverses it in place and gathers the
@@ -1154,6 +1259,189 @@ __global__ __launch_bounds__(kWave) void k_backtrack(Work w)
         R[6] = c.phase_final;
         R[7] = c.last_step;
     }
+}
+
+// ---------------------------------------------------------- persistent mode
+// One cooperatively launched grid (every workgroup resident) runs the whole
+// frame loop. Phases are separated by a grid barrier instead of kernel
+// boundaries, and the score phase keeps up to kHeld units of candidates per
+// wavefront in registers, so the admit phase after the barrier only issues the
+// hash atomics (the page's section 2 needs two device-wide points per step: the
+// exact maximum before the admit test, and the resolved payloads before
+// compaction; the same phases and the same arithmetic as the per-kernel path).
+
+constexpr int kHeld = 2;
+constexpr unsigned long long kSyncTimeoutTicks = 200000000ull;   // 2 s of the 100 MHz clock
+
+// Grid barrier by generation. Arrival is an agent-scope atomic with release
+// fences around it; the wait is bounded in wall-clock time: past the bound the
+// waiter raises `abort`, and every workgroup leaves at its next barrier, so the
+// grid always drains.
+__device__ __forceinline__ bool grid_sync(GridSync *gs, uint32_t &gen)
+{
+    __shared__ int ok_s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t g = gen;
+        const uint32_t arrived = atomicAdd(&gs->count, 1u) + 1u;
+        if (arrived == gridDim.x) {
+            atomicExch(&gs->count, 0u);
+            __threadfence();
+            atomicAdd(&gs->gen, 1u);
+        } else {
+            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
+                if (__hip_atomic_load(&gs->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncTimeoutTicks) {
+                    atomicExch(&gs->abort, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __threadfence();
+        gen = g + 1u;
+        ok_s = __hip_atomic_load(&gs->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+    }
+    __syncthreads();
+    return ok_s != 0;
+}
+
+struct Held {
+    int L, ph;
+    UnitData ud;
+};
+
+// Score phase: the first kHeld units of this wavefront's share are loaded in
+// full (no bound skip: the admit phase needs every candidate) and kept; the
+// rest only contribute to the maximum (with the bound skip) and are loaded
+// again after the barrier.
+template <typename LPT>
+__device__ __forceinline__ void score_phase(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
+                                            Held (&held)[kHeld], int &nh, uint32_t &s_rest, uint32_t &s_end)
+{
+    const int p = t & 1;
+    uint32_t s;
+    wave_share(tab.base[w.max_lanes], &s, &s_end);
+    nh = 0;
+    int vl = -1;
+    uint32_t cur = 0;
+    LaneView v;
+#pragma unroll
+    for (int h = 0; h < kHeld; ++h) {
+        if (s < s_end) {
+            const int L = find_lane(tab.base, w.max_lanes, s);
+            if (L != vl) {
+                v = lane_view(w, tab, t, d, L);
+                cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
+                if (cur >= v.n) cur = 0;
+                vl = L;
+            }
+            load_unit<LPT>(w, v, s - tab.base[L], cur, -__builtin_inff(), true, held[h].ud);
+            held[h].L = L;
+            held[h].ph = v.ph;
+            const float m = unit_max(held[h].ud);
+            if (wlane() == 0 && m > -__builtin_inff()) atomicMax(&w.ctl[L].maxkey[p], f2ord(m));
+            nh = h + 1;
+            ++s;
+        }
+    }
+    s_rest = s;
+    if (s < s_end) walk_range<kModeMax, LPT>(w, tab, t, d, s, s_end, nullptr);
+}
+
+// Admit phase: the kept units admit from registers against the exact cutoff;
+// the others are loaded again (bound skip against the cutoff).
+template <typename LPT>
+__device__ __forceinline__ void admit_phase(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
+                                            const Held (&held)[kHeld], int nh, uint32_t s_rest,
+                                            uint32_t s_end, uint32_t *cbuf)
+{
+    uint32_t cb_n = 0, admitted = 0;
+    int last = -1;
+#pragma unroll
+    for (int h = 0; h < kHeld; ++h) {
+        if (h < nh) {
+            const int L = held[h].L;
+            if (last >= 0 && L != last) {
+                if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, cbuf, cb_n);
+                cb_n = 0;
+                const uint32_t a = wave_sum(admitted);
+                if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
+                admitted = 0;
+            }
+            last = L;
+            admit_unit(w, L, held[h].ph, tab.f1[L], held[h].ud, cbuf, cb_n, admitted);
+        }
+    }
+    if (last >= 0) {
+        if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, cbuf, cb_n);
+        const uint32_t a = wave_sum(admitted);
+        if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
+    }
+    if (s_rest < s_end) walk_range<kModeExpand, LPT>(w, tab, t, d, s_rest, s_end, cbuf);
+}
+
+__device__ __forceinline__ bool closure_phases(const Work &w, int t, LaneTab &tab, uint32_t *cbuf,
+                                               GridSync *gs, uint32_t &gen)
+{
+    for (int k = 1; k <= w.eps_iterations; ++k) {
+        ph_eps_expand(w, t, k, tab, cbuf);
+        if (!grid_sync(gs, gen)) return false;
+        ph_eps_resolve(w, t, k, tab);
+        if (!grid_sync(gs, gen)) return false;
+        ph_eps_apply(w, t, k, tab);
+        if (!grid_sync(gs, gen)) return false;
+    }
+    return true;
+}
+
+template <typename LPT>
+__global__ __launch_bounds__(kBlock, 3) void k_persistent(Work w, int steps, GridSync *gs)
+{
+    __shared__ LaneTab tab;
+    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
+    uint32_t *cbuf = cbufs[threadIdx.x / kWave];
+    uint32_t gen = 0;
+    if (threadIdx.x == 0) gen = __hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const LpDesc d = *w.lp;
+    if (!closure_phases(w, -1, tab, cbuf, gs, gen)) return;
+    for (int t = 0; t < steps; ++t) {
+        step_open(w, t, tab);
+        Held held[kHeld];
+        int nh;
+        uint32_t s_rest, s_end;
+        score_phase<LPT>(w, tab, t, d, held, nh, s_rest, s_end);
+        if (!grid_sync(gs, gen)) return;
+        step_cutoffs(w, t, tab);
+        admit_phase<LPT>(w, tab, t, d, held, nh, s_rest, s_end, cbuf);
+        if (!grid_sync(gs, gen)) return;
+        ph_finalize(w, t, tab);
+        if (!grid_sync(gs, gen)) return;
+        if (!closure_phases(w, t, tab, cbuf, gs, gen)) return;
+    }
+}
+
+hipError_t launch_persistent(const Work &w, int steps, int grid, GridSync *gs, hipStream_t s)
+{
+    Work wc = w;
+    int st = steps;
+    GridSync *g = gs;
+    void *args[] = {&wc, &st, &g};
+    const void *fn = w.lp_dtype == 1 ? (const void *)k_persistent<__half> : (const void *)k_persistent<float>;
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kBlock), args, 0, s);
+}
+
+hipError_t persistent_max_grid(int lp_dtype, int *max_blocks)
+{
+    int dev = 0, ncu = 0, per = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const void *fn = lp_dtype == 1 ? (const void *)k_persistent<__half> : (const void *)k_persistent<float>;
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kBlock, 0);
+    *max_blocks = per * ncu;
+    return e;
 }
 
 // ---------------------------------------------------------------- launchers
