@@ -40,7 +40,7 @@ extern "C" {
 /* out_meta[b * 3 + 2] bits (section 7 of the page): a non-zero value means the
  * lane's result may be degraded; such a lane also reports ok = 0. */
 #define WFST_OVF_SLOTS    1   /* a lane's candidate arcs in one step exceed slot_cap       */
-#define WFST_OVF_HASH     2   /* a destination found no hash slot within the probe bound   */
+#define WFST_OVF_HASH     2   /* reserved: recombination is direct-mapped and never overflows */
 #define WFST_OVF_ARENA    4   /* the lane's winners-log region is full                     */
 #define WFST_OVF_CLAIMS   8   /* more distinct destinations in one pass than claims_cap    */
 #define WFST_OVF_FRONTIER 16  /* more surviving tokens than frontier_cap                   */
@@ -162,9 +162,12 @@ int wfst_graph_release(wfst_graph_t g);
 
 /*
  * Create a decoder on the graph's device: allocates every workspace buffer once
- * (frontiers, per-lane hash tables, claims lists, winners-log regions, result
- * buffers) and takes a graph reference (page section 6.1 "Workspace", section
- * 10). Errors: WFST_EINVAL (bad config), WFST_ENOMEM, WFST_EDEVICE.
+ * (frontiers, per-lane recombination tables, claims lists, winners-log regions,
+ * result buffers) and takes a graph reference (page section 6.1 "Workspace",
+ * section 10). The recombination table holds one 8-byte entry per state and
+ * lane (max_lanes * num_states * 8 bytes), so destinations are resolved with
+ * one atomic each and never overflow. Errors: WFST_EINVAL (bad config),
+ * WFST_ENOMEM, WFST_EDEVICE.
  */
 int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *c, wfst_decoder_t *out);
 
@@ -231,7 +234,7 @@ int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_t steps_cap);
 
 /* Kernel ids of wfst_decoder_kernel_times, in launch order within a step. */
-#define WFST_K_CLEAR        0  /* per-decode clear of records and stale hash tables        */
+#define WFST_K_CLEAR        0  /* per-decode clear of records and stale recombination tables */
 #define WFST_K_INIT         1  /* lane control blocks and start tokens                     */
 #define WFST_K_LPMAX        2  /* max log-prob per (lane, frame) row for the bound skip    */
 #define WFST_K_MAX          3  /* exact per-lane maximum of the step                       */

@@ -54,12 +54,6 @@ int dalloc(T **p, size_t count, std::vector<void *> *owned, size_t *bytes)
     return WFST_OK;
 }
 
-uint64_t next_pow2(uint64_t x)
-{
-    uint64_t p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
 
 }  // namespace
 
@@ -71,9 +65,9 @@ struct wfst_graph_s {
     std::vector<void *> owned;
     size_t bytes = 0;
     StateInfo *sinfo = nullptr;
-    uint16_t *ilabel = nullptr;
-    float *weight = nullptr;
-    int32_t *dest = nullptr, *olabel = nullptr, *arc_src = nullptr;
+    ArcLW *arc_lw = nullptr;
+    ArcDLW *arc_dlw = nullptr;
+    int32_t *olabel = nullptr, *arc_src = nullptr;
 
     ~wfst_graph_s()
     {
@@ -218,11 +212,18 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     HIP_TRY(hipSetDevice(device));
 
     const int32_t S = g->num_states, A = g->num_arcs;
-    std::vector<uint16_t> il16((size_t)A);
+    // interleaved arc records in CSR order (section 4's split, regrouped so that
+    // the fields a pass reads for one arc share a cache line)
     std::vector<int32_t> src((size_t)A);
+    std::vector<ArcLW> lw((size_t)A);
+    std::vector<ArcDLW> dlw((size_t)A);
     for (int32_t s = 0; s < S; ++s)
         for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) src[(size_t)a] = s;
-    for (int32_t a = 0; a < A; ++a) il16[(size_t)a] = g->ilabel[a] == -1 ? kFinalLabel : (uint16_t)g->ilabel[a];
+    for (int32_t a = 0; a < A; ++a) {
+        const uint32_t il = g->ilabel[a] == -1 ? (uint32_t)kFinalLabel : (uint32_t)g->ilabel[a];
+        lw[(size_t)a] = ArcLW{il, g->weight[a]};
+        dlw[(size_t)a] = ArcDLW{g->dest[a], il, g->weight[a]};
+    }
 
     wfst_graph_s *h = new wfst_graph_s();
     h->device = device;
@@ -234,9 +235,8 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     h->max_class_deg = md;
     int r = WFST_OK;
     if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->ilabel, (size_t)A, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->weight, (size_t)A, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->dest, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->arc_lw, (size_t)A, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->arc_dlw, (size_t)A, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->olabel, (size_t)A, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->arc_src, (size_t)A, &h->owned, &h->bytes))) {
         delete h;
@@ -245,9 +245,8 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMemcpy(h->sinfo, info.data(), sizeof(StateInfo) * (size_t)S, hipMemcpyHostToDevice);
     if (A > 0) {
-        if (e == hipSuccess) e = hipMemcpy(h->ilabel, il16.data(), 2 * (size_t)A, hipMemcpyHostToDevice);
-        if (e == hipSuccess) e = hipMemcpy(h->weight, g->weight, 4 * (size_t)A, hipMemcpyHostToDevice);
-        if (e == hipSuccess) e = hipMemcpy(h->dest, g->dest, 4 * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->arc_lw, lw.data(), sizeof(ArcLW) * (size_t)A, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->arc_dlw, dlw.data(), sizeof(ArcDLW) * (size_t)A, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemcpy(h->olabel, g->olabel, 4 * (size_t)A, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemcpy(h->arc_src, src.data(), 4 * (size_t)A, hipMemcpyHostToDevice);
     }
@@ -293,7 +292,6 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     // passes), and their arcs must fit the 32-bit slot space of one lane
     if (CC * (uint64_t)(1 + P) * maxdeg >= (1ull << 32))
         return fail(WFST_EINVAL, "claims_cap * (1 + eps passes) * (largest out-degree of one arc class) must stay below 2^32 (32-bit slot offsets)");
-    const uint64_t HC = std::max<uint64_t>(next_pow2(2 * CC), 64);
     uint64_t arena = c.arena_entries ? (uint64_t)c.arena_entries
                                      : std::max<uint64_t>(1ull << 20, 4ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P));
     if ((uint64_t)c.max_lanes * arena >= (1ull << 31)) {
@@ -323,14 +321,14 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
 
     Work &w = d->w;
-    w.sinfo = g->sinfo; w.ilabel = g->ilabel; w.weight = g->weight; w.dest = g->dest;
+    w.sinfo = g->sinfo; w.arc_lw = g->arc_lw; w.arc_dlw = g->arc_dlw;
     w.olabel = g->olabel; w.arc_src = g->arc_src;
     w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
     w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
     w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
     w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
     w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
-    w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC; w.hash_mask = (uint32_t)(HC - 1);
+    w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC;
     w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap; w.strip_cap = (uint32_t)strip_cap;
     w.res_stride = (uint32_t)(kResHeader + 2 * path_cap);
 
@@ -347,7 +345,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S); A(&w.strip_tok[p], L * strip_cap);
         if (P > 0) A(&w.changed[p], L * CC);
     }
-    A(&w.hash, L * HC);
+    A(&w.best, L * S);
     A(&w.claims, L * CC);
     if (P > 0) { A(&w.dec, L * CC); A(&w.dec_dest, L * CC); }
     A(&w.wlog, L * arena);
@@ -369,7 +367,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     }
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
-    if (e == hipSuccess) e = hipMemset(w.hash, 0, sizeof(HashSlot) * L * HC);
+    if (e == hipSuccess) e = hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
     for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);

@@ -10,7 +10,6 @@ namespace wfst {
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kBlock = 256;         // threads per workgroup of the frame-loop kernels
 constexpr int kMaxLanes = 64;       // one wavefront scans the per-lane table
-constexpr int kMaxProbes = 256;     // linear-probe bound of the recombination hash
 constexpr int kStepFields = 16;     // u32 fields of one per-step record
 constexpr uint16_t kFinalLabel = 0xFFFF;
 
@@ -40,12 +39,28 @@ struct alignas(32) StateInfo {
     int32_t pad0, pad1;
 };
 
-// Recombination hash slot: key = destination state + 1 (0 = empty) and the
-// packed (ordered score << 32 | ~arc) payload resolved by one u64 atomicMax.
-struct alignas(16) HashSlot {
-    uint32_t key;
+// Arc records, one contiguous run per state (the CSR order of the graph), so a
+// token's arcs share cache lines: the maximum pass reads {ilabel, weight}, the
+// admit pass and the closure {dest, ilabel, weight}. Final arcs carry
+// kFinalLabel.
+struct alignas(8) ArcLW {
+    uint32_t ilabel;
+    float weight;
+};
+struct ArcDLW {
+    int32_t dest;
+    uint32_t ilabel;
+    float weight;
+};
+
+// Claim of a destination by its first admitted candidate: the destination, the
+// candidate's arc and its source token (position in the frontier being read).
+// When that candidate is also the winner, the source token needs no lookup.
+struct alignas(16) Claim {
+    int32_t dest;
+    int32_t arc;
+    uint32_t tok;
     uint32_t pad;
-    unsigned long long payload;
 };
 
 // Per-lane control block (one 128-byte line per lane).
@@ -65,7 +80,7 @@ struct alignas(128) LaneCtl {
     float final_score;
     uint32_t nclaims_eps[2];   // claims of closure pass k at [k & 1]
     uint32_t nchanged[2];      // changed-token list sizes of closure pass k at [k & 1]
-    uint32_t dirty;            // hash table may hold stale slots (claims overflow)
+    uint32_t dirty;            // recombination table may hold stale entries (claims overflow)
     int32_t last_step;         // last step this lane ran
     int32_t phase_final;       // phase code of the lane's last step
     uint32_t log_pending;      // entries of the last compaction, added to log_cursor by the next kernel
@@ -98,9 +113,8 @@ struct LpDesc {
 struct Work {
     // graph (read-only)
     const StateInfo *sinfo;
-    const uint16_t *ilabel;
-    const float *weight;
-    const int32_t *dest;
+    const ArcLW *arc_lw;
+    const ArcDLW *arc_dlw;
     const int32_t *olabel;
     const int32_t *arc_src;
     int32_t num_states, num_arcs, start_state, vocab, super_final;
@@ -114,7 +128,6 @@ struct Work {
     int32_t max_frames;
     uint32_t frontier_cap;    // Q
     uint32_t claims_cap;      // CC
-    uint32_t hash_mask;       // HC - 1 (HC power of two)
     uint32_t arena;           // winners-log entries per lane
     uint32_t path_cap;        // device path buffer per lane
     uint32_t strip_cap;       // 64-slot strips per lane and step (slot space = 64 * strip_cap)
@@ -133,8 +146,8 @@ struct Work {
     int32_t *tok_abeg[2];     // first arc of the step's class
     float *tok_ub[2];         // score + largest weight of the step's class
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
-    HashSlot *hash;           // [L][HC]
-    uint32_t *claims;         // [L][CC]
+    unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed)
+    Claim *claims;            // [L][CC]
     int4 *dec;                // [L][CC] closure decisions {token or -1/-2, score bits, arc, src entry}
     int32_t *dec_dest;        // [L][CC]
     uint32_t *changed[2];     // [L][CC] closure change lists by pass parity

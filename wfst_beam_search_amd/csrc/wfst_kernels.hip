@@ -10,15 +10,17 @@
 //    solution);
 //  * pass 1 (k_max) takes the exact per-lane maximum with the per-token upper
 //    bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds in IEEE fp32);
-//  * pass 2 (k_expand) admits end > M - b and recombines per destination in an
-//    open-addressing hash with one u64 atomicMax of (ordered score << 32 | ~arc)
-//    per candidate, so the greatest score wins and, among equal scores, the
-//    smallest arc id; the first claimer of a slot appends it to the claims list;
+//  * pass 2 (k_expand) admits end > M - b and recombines per destination in a
+//    direct-mapped per-lane table best[state] with one returning u64 atomicMax
+//    of (ordered score << 32 | ~arc) per candidate, so the greatest score wins
+//    and, among equal scores, the smallest arc id; the candidate that finds the
+//    entry empty appends a claim {dest, arc, source token} to the claims list;
 //  * pass 3 (k_finalize) compacts the claims into the next frontier: one
 //    64-bit atomicAdd per wavefront allocates token positions and arc offsets
 //    together (tokens in the low half, arcs in the high half), which is the
 //    exclusive degree scan of the next step, done as the frontier is built; the
-//    winners-log entry {source entry, arc} is written and the hash slot cleared;
+//    winners-log entry {source entry, arc} is written and the table entry
+//    cleared;
 //  * epsilon closure passes (expand / resolve / apply) on TLG graphs.
 // All fp32 arithmetic is single operations in the order the page fixes; the
 // file is compiled with -ffp-contract=off.
@@ -83,8 +85,6 @@ __device__ __forceinline__ float wave_max(float v)
 __device__ __forceinline__ float lp_at(const float *row, uint32_t i) { return row[i]; }
 __device__ __forceinline__ float lp_at(const __half *row, uint32_t i) { return __half2float(row[i]); }
 
-__device__ __forceinline__ uint32_t hash_state(uint32_t s) { return s * 0x9E3779B1u; }
-
 __device__ __forceinline__ uint32_t *step_rec(const Work &w, int L, int t)
 {
     return w.steps + ((size_t)L * (size_t)(w.max_frames + 2) + (size_t)(t + 1)) * kStepFields;
@@ -141,26 +141,6 @@ __device__ __forceinline__ void class_of(const StateInfo &si, bool final_step, f
     }
 }
 
-// ------------------------------------------------------------ hash insert
-// Returns the slot of `dest` in the lane's table (claiming it if empty) or -1
-// when the probe bound is exceeded. *first is set for the claiming thread.
-__device__ __forceinline__ int hash_claim(HashSlot *tbl, uint32_t mask, int32_t dest, bool *first)
-{
-    const uint32_t want = (uint32_t)dest + 1u;
-    uint32_t h = hash_state((uint32_t)dest) & mask;
-    *first = false;
-    // Most admitted candidates reach a destination no other candidate has claimed
-    // yet, so the first probe goes straight to the compare-and-swap (one round
-    // trip claims the slot or reports its owner).
-    for (int probe = 0; probe < kMaxProbes; ++probe) {
-        const uint32_t old = atomicCAS(&tbl[h].key, 0u, want);
-        if (old == 0u) { *first = true; return (int)h; }
-        if (old == want) return (int)h;
-        h = (h + 1u) & mask;
-    }
-    return -1;
-}
-
 // Writes the strip map for tokens just allocated by one wavefront: the keepers
 // of this wave got positions p0 + rank and slot offsets a0 + dpre (dpre is the
 // exclusive scan of the keepers' degrees, so over all 64 lanes a0 + dpre is
@@ -188,8 +168,14 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
     }
 }
 
-// Per-wavefront LDS buffer of claimed slots in the expand pass.
-constexpr uint32_t kClaimBuf = 1024;
+// Per-wavefront LDS buffer of the claims made by the expand passes.
+constexpr uint32_t kClaimBuf = 512;
+
+struct ClaimBuf {
+    int32_t dest[kClaimBuf];
+    int32_t arc[kClaimBuf];
+    uint32_t tok[kClaimBuf];
+};
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -200,35 +186,70 @@ __device__ __forceinline__ void wave_lds_sync()
 
 // Appends the wave's n buffered claims to lane L's list: one atomic, then a
 // coalesced copy out of LDS.
-__device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *counter, uint32_t *cbuf,
+__device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
                                              uint32_t n)
 {
     wave_lds_sync();
     uint32_t base = 0;
     if (wlane() == 0) base = atomicAdd(counter, n);
     base = __shfl(base, 0, kWave);
-    uint32_t *dst = w.claims + (size_t)L * w.claims_cap;
-    for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave)
-        if (base + i < w.claims_cap) dst[base + i] = cbuf[i];
+    Claim *dst = w.claims + (size_t)L * w.claims_cap;
+    for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave) {
+        Claim c;
+        c.dest = cb.dest[i];
+        c.arc = cb.arc[i];
+        c.tok = cb.tok[i];
+        c.pad = 0u;
+        if (base + i < w.claims_cap) dst[base + i] = c;
+    }
     wave_lds_sync();
 }
 
+// Buffers the claims of one round of a wavefront (lanes with `first` set),
+// flushing first if the round might not fit.
+__device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
+                                            uint32_t &cb_n, bool first, int32_t dest, int32_t arc,
+                                            uint32_t tok)
+{
+    const unsigned long long fm = __ballot(first);
+    if (!fm) return;
+    if (cb_n + kWave > kClaimBuf) {
+        flush_claims(w, L, counter, cb, cb_n);
+        cb_n = 0;
+    }
+    if (first) {
+        const uint32_t i = cb_n + (uint32_t)__popcll(fm & mask_lt());
+        cb.dest[i] = dest;
+        cb.arc[i] = arc;
+        cb.tok[i] = tok;
+    }
+    cb_n += (uint32_t)__popcll(fm);
+}
+
+// Key of a table entry and the source token of its winner: the claimer's
+// token when the claimer won, else through the arc's source state.
+__device__ __forceinline__ int32_t winner_token(const Work &w, int fp, int L, const Claim &cl,
+                                                int32_t arc)
+{
+    if (arc == cl.arc) return (int32_t)cl.tok;
+    const int32_t src = w.arc_src[arc];
+    return w.pos[fp][(size_t)L * w.num_states + src];
+}
+
 // ---------------------------------------------------------------- k_clear
-// Clears the per-step records and the hash tables of lanes whose claims list
-// overflowed in an earlier decode (the targeted clear cannot see those slots).
+// Clears the per-step records and the recombination tables of lanes whose
+// claims list overflowed in an earlier decode (the targeted clear cannot see
+// those entries).
 __global__ __launch_bounds__(kBlock) void k_clear(Work w)
 {
     const size_t nrec = (size_t)w.max_lanes * (size_t)(w.max_frames + 2) * kStepFields;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nrec; i += stride) w.steps[i] = 0u;
-    const size_t hc = (size_t)w.hash_mask + 1;
+    const size_t ns = (size_t)w.num_states;
     for (int L = 0; L < w.max_lanes; ++L) {
         if (!w.ctl[L].dirty) continue;
-        HashSlot *tbl = w.hash + (size_t)L * hc;
-        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < hc; i += stride) {
-            tbl[i].key = 0u;
-            tbl[i].payload = 0ull;
-        }
+        unsigned long long *tbl = w.best + (size_t)L * ns;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns; i += stride) tbl[i] = 0ull;
     }
 }
 
@@ -326,7 +347,8 @@ constexpr uint32_t kUnit = kWave * kR;
 struct UnitData {
     float e[kR];          // end score (valid where bit r of `live` is set)
     uint32_t arc[kR];
-    int32_t dst[kR];
+    int32_t dst[kR];      // destination (admit pass only)
+    uint32_t tok[kR];     // source token
     uint32_t live;        // bit r: slot r is a candidate whose arc was loaded
 };
 
@@ -365,11 +387,12 @@ __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab,
 // Loads unit u of lane v.L: lane l of the wavefront resolves slots
 // j0 + r*64 + l against register-held windows of 64 token offsets (start token
 // `cur`, moved forward), then issues every arc load of the unit before using
-// any. Tokens whose bound ub + maxlp <= skip are not expanded (exact: no arc of
-// theirs can end above skip).
-template <typename LPT>
+// any: the maximum pass reads {ilabel, weight} records, the admit pass
+// {dest, ilabel, weight}. Tokens whose bound ub + maxlp <= skip are not
+// expanded (exact: no arc of theirs can end above skip).
+template <int MODE, typename LPT>
 __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
-                                          float skip, bool want_dest, UnitData &ud)
+                                          float skip, UnitData &ud)
 {
     const int lane = wlane();
     const uint32_t n = v.n;
@@ -425,11 +448,22 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
         ud.arc[r] = (uint32_t)ab[r] + (j[r] - toff[r]);
+        ud.tok[r] = tok[r];
         const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] + v.lpm > skip;
         if (go) ud.live |= 1u << r;
-        wt[r] = go ? w.weight[ud.arc[r]] : 0.0f;
-        il[r] = (go && row) ? (uint32_t)w.ilabel[ud.arc[r]] : 0u;
-        ud.dst[r] = (want_dest && go && row) ? w.dest[ud.arc[r]] : 0;
+        if (MODE == kModeMax) {
+            ArcLW a = {0u, 0.0f};
+            if (go) a = w.arc_lw[ud.arc[r]];
+            wt[r] = a.weight;
+            il[r] = a.ilabel;
+            ud.dst[r] = 0;
+        } else {
+            ArcDLW a = {0, 0u, 0.0f};
+            if (go) a = w.arc_dlw[ud.arc[r]];
+            wt[r] = a.weight;
+            il[r] = a.ilabel;
+            ud.dst[r] = a.dest;
+        }
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
@@ -449,12 +483,12 @@ __device__ __forceinline__ float unit_max(const UnitData &ud)
 }
 
 // Admits a unit's candidates (end > cut, strict) and recombines them: on a real
-// step through the lane's hash (CAS on the first probe of every candidate at
-// once, then a posted u64 atomicMax of the key), on the final step through one
-// wavefront-reduced atomicMax of the lane's final key. First claimers of a slot
-// go to the wavefront's LDS claims buffer.
+// step with one returning u64 atomicMax per candidate on the lane's
+// direct-mapped table (the candidate that finds the entry empty claims the
+// destination: its claim goes to the wavefront's LDS buffer), on the final step
+// through one wavefront-reduced atomicMax of the lane's final key.
 __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, const UnitData &ud,
-                                           uint32_t *cbuf, uint32_t &cb_n, uint32_t &admitted)
+                                           ClaimBuf *cb, uint32_t &cb_n, uint32_t &admitted)
 {
     LaneCtl &c = w.ctl[L];
     const int lane = wlane();
@@ -465,47 +499,14 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
         admitted += adm[r] ? 1u : 0u;
     }
     if (ph == kPhReal) {
-        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
-        uint32_t hh[kR], old[kR];
-        bool first[kR];
-        int slot[kR];
+        unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
+        unsigned long long old[kR];
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            hh[r] = hash_state((uint32_t)ud.dst[r]) & w.hash_mask;
-            old[r] = adm[r] ? atomicCAS(&tbl[hh[r]].key, 0u, (uint32_t)ud.dst[r] + 1u) : 0u;
-        }
+        for (int r = 0; r < kR; ++r)
+            old[r] = adm[r] ? atomicMax(&tbl[ud.dst[r]], cand_key(ud.e[r], (int32_t)ud.arc[r])) : 1ull;
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            first[r] = false;
-            slot[r] = -1;
-            if (!adm[r]) continue;
-            const uint32_t want = (uint32_t)ud.dst[r] + 1u;
-            if (old[r] == 0u) { first[r] = true; slot[r] = (int)hh[r]; }
-            else if (old[r] == want) slot[r] = (int)hh[r];
-            else {
-                uint32_t h = (hh[r] + 1u) & w.hash_mask;
-                for (int probe = 1; probe < kMaxProbes; ++probe) {
-                    const uint32_t o2 = atomicCAS(&tbl[h].key, 0u, want);
-                    if (o2 == 0u) { first[r] = true; slot[r] = (int)h; break; }
-                    if (o2 == want) { slot[r] = (int)h; break; }
-                    h = (h + 1u) & w.hash_mask;
-                }
-            }
-            if (slot[r] < 0) atomicOr(&c.overflow, kOvfHash);
-            else atomicMax(&tbl[slot[r]].payload, cand_key(ud.e[r], (int32_t)ud.arc[r]));
-        }
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const unsigned long long fm = __ballot(first[r]);
-            if (fm) {
-                if (cb_n + kWave > kClaimBuf) {
-                    flush_claims(w, L, &c.nclaims, cbuf, cb_n);
-                    cb_n = 0;
-                }
-                if (first[r]) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot[r];
-                cb_n += (uint32_t)__popcll(fm);
-            }
-        }
+        for (int r = 0; r < kR; ++r)
+            push_claims(w, L, &c.nclaims, *cb, cb_n, old[r] == 0ull, ud.dst[r], (int32_t)ud.arc[r], ud.tok[r]);
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -539,7 +540,7 @@ __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t
 // the bound skip against the cutoff).
 template <int MODE, typename LPT>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
-                                           uint32_t s, uint32_t s_end, uint32_t *cbuf)
+                                           uint32_t s, uint32_t s_end, ClaimBuf *cbuf)
 {
     const int p = t & 1;
     const int nl = w.max_lanes;
@@ -561,12 +562,12 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
         uint32_t admitted = 0;
         for (; s < seg_end; ++s) {
             UnitData ud;
-            load_unit<LPT>(w, v, s - tab.base[L], cur, MODE == kModeMax ? run : cut, MODE == kModeExpand, ud);
+            load_unit<MODE, LPT>(w, v, s - tab.base[L], cur, MODE == kModeMax ? run : cut, ud);
             if (MODE == kModeMax) run = fmaxf(run, unit_max(ud));
             else admit_unit(w, L, v.ph, cut, ud, cbuf, cb_n, admitted);
         }
         if (MODE == kModeExpand) {
-            if (cb_n) flush_claims(w, L, &c.nclaims, cbuf, cb_n);
+            if (cb_n) flush_claims(w, L, &c.nclaims, *cbuf, cb_n);
             cb_n = 0;
             const uint32_t a = wave_sum(admitted);
             if (lane == 0 && a) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
@@ -578,7 +579,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
 
 template <int MODE, typename LPT>
 __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
-                                           uint32_t *cbuf)
+                                           ClaimBuf *cbuf)
 {
     uint32_t s, s_end;
     wave_share(tab.base[w.max_lanes], &s, &s_end);
@@ -727,9 +728,9 @@ __global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
     __shared__ LaneTab tab;
     slot_prologue<kModeMax>(w, tab, t);
     step_cutoffs(w, t, tab);
-    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
+    __shared__ ClaimBuf cbufs[kBlock / kWave];
     const LpDesc d = *w.lp;
-    walk_slots<kModeExpand, LPT>(w, tab, t, d, cbufs[threadIdx.x / kWave]);
+    walk_slots<kModeExpand, LPT>(w, tab, t, d, &cbufs[threadIdx.x / kWave]);
 }
 
 // -------------------------------------------------------------- k_finalize
@@ -770,8 +771,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             step_rec(w, L, t)[kRecDistinct] = nc;
             if (tab.f0[L] == 0.0f) {
                 // the compaction does not fit: retire the lane before writing any
-                // token; its claimed hash slots stay set, so the table is cleared
-                // before the next decode
+                // token; its claimed table entries stay set, so the table is
+                // cleared before the next decode
                 c.overflow |= nc > w.claims_cap ? kOvfClaims
                             : nc > w.frontier_cap ? kOvfFrontier : kOvfArena;
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
@@ -825,20 +826,20 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         uint32_t deg = 0;
         float end = 0.0f, ub = 0.0f;
         if (valid) {
-            const uint32_t h = w.claims[(size_t)L * w.claims_cap + i];
-            HashSlot *sl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1) + h;
-            const uint32_t key = sl->key;
-            const unsigned long long K = sl->payload;
-            sl->key = 0u;
-            sl->payload = 0ull;
-            dst = (int32_t)key - 1;
+            const Claim cl = w.claims[(size_t)L * w.claims_cap + i];
+            dst = cl.dest;
+            unsigned long long K = 0ull;
+            if ((uint32_t)dst < (uint32_t)w.num_states) {
+                unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)dst;
+                K = *ent;
+                *ent = 0ull;
+            }
             end = ord2f((uint32_t)(K >> 32));
             arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
-            keep = (K != 0ull) && key != 0u && (end > cutoff);
+            keep = (K != 0ull) && (end > cutoff);
             if (keep) {
-                const int32_t src = w.arc_src[arc];
                 const StateInfo si = w.sinfo[dst];
-                const int32_t stok = w.pos[p][(size_t)L * w.num_states + src];
+                const int32_t stok = winner_token(w, p, L, cl, arc);
                 keep = (uint32_t)stok < Q;
                 if (keep) {
                     // without epsilon arcs a token's entry is its compaction's base
@@ -901,7 +902,7 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
     return c.status == kActive && (t < 0 || t < c.T);
 }
 
-__device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, uint32_t *cbuf_wave)
+__device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
@@ -936,13 +937,12 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    uint32_t *cbuf = cbuf_wave;
     for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
         LaneCtl &c = w.ctl[L];
-        HashSlot *tbl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1);
+        unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
         // the 64 sources of this unit and their epsilon ranges
         const uint32_t tok = (i < tab.n[L])
             ? ((k == 1) ? i : w.changed[k & 1][(size_t)L * w.claims_cap + i]) : 0xFFFFFFFFu;
@@ -970,28 +970,21 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             }
             const int32_t a = __shfl(eb, src, kWave) + (int32_t)(x - __shfl(dpre, src, kWave));
             const float ssc = __shfl(sc, src, kWave);
+            const uint32_t stk = __shfl(tok, src, kWave);
             bool first = false;
-            int slot = -1;
+            int32_t dd = 0;
             if (x < dsum) {
-                const float e = ssc + w.weight[a];
+                const ArcDLW ar = w.arc_dlw[a];
+                const float e = ssc + ar.weight;
+                dd = ar.dest;
                 if (e > cutoff) {
                     ++n_adm;
-                    slot = hash_claim(tbl, w.hash_mask, w.dest[a], &first);
-                    if (slot < 0) atomicOr(&c.overflow, kOvfHash);
-                    else atomicMax(&tbl[slot].payload, cand_key(e, a));
+                    first = atomicMax(&tbl[ar.dest], cand_key(e, a)) == 0ull;
                 }
             }
-            const unsigned long long fm = __ballot(first);
-            if (fm) {
-                if (cb_n + kWave > kClaimBuf) {
-                    flush_claims(w, L, &c.nclaims_eps[k & 1], cbuf, cb_n);
-                    cb_n = 0;
-                }
-                if (first) cbuf[cb_n + (uint32_t)__popcll(fm & mask_lt())] = (uint32_t)slot;
-                cb_n += (uint32_t)__popcll(fm);
-            }
+            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, first, dd, a, stk);
         }
-        if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], cbuf, cb_n);
+        if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n);
         const uint32_t sd = wave_sum(n_adm);
         if (lane == 0 && dsum) {
             uint32_t *rec = step_rec(w, L, t);
@@ -1004,8 +997,8 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
 __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
 {
     __shared__ LaneTab tab;
-    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
-    ph_eps_expand(w, t, k, tab, cbufs[threadIdx.x / kWave]);
+    __shared__ ClaimBuf cbufs[kBlock / kWave];
+    ph_eps_expand(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
 }
 
 // Decides, per claimed destination, append / replace / nothing (reads only).
@@ -1051,20 +1044,20 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
         if (i >= tab.n[L]) continue;
         const size_t ci = (size_t)L * w.claims_cap + i;
-        const uint32_t h = w.claims[ci];
-        HashSlot *sl = w.hash + (size_t)L * ((size_t)w.hash_mask + 1) + h;
-        const uint32_t key = sl->key;
-        const unsigned long long K = sl->payload;
-        sl->key = 0u;
-        sl->payload = 0ull;
-        const int32_t dst = (int32_t)key - 1;
+        const Claim cl = w.claims[ci];
+        const int32_t dst = cl.dest;
+        unsigned long long K = 0ull;
+        if ((uint32_t)dst < (uint32_t)w.num_states) {
+            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)dst;
+            K = *ent;
+            *ent = 0ull;
+        }
         const float end = ord2f((uint32_t)(K >> 32));
         const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
         int32_t code = -2;
         int32_t esrc = -1;
-        if (K != 0ull && key != 0u && end > tab.f1[L]) {
-            const int32_t src = w.arc_src[arc];
-            const int32_t stok = w.pos[fp][(size_t)L * w.num_states + src];
+        if (K != 0ull && end > tab.f1[L]) {
+            const int32_t stok = winner_token(w, fp, L, cl, arc);
             esrc = (uint32_t)stok < Q ? w.tok_entry[fp][(size_t)L * Q + stok] : -1;
             const int32_t pd = w.pos[fp][(size_t)L * w.num_states + dst];
             const bool exists = (uint32_t)pd < tab.arcs[L] && w.tok_state[fp][(size_t)L * Q + pd] == dst;
@@ -1266,7 +1259,7 @@ __global__ __launch_bounds__(kWave) void k_backtrack(Work w)
 // frame loop. Phases are separated by a grid barrier instead of kernel
 // boundaries, and the score phase keeps up to kHeld units of candidates per
 // wavefront in registers, so the admit phase after the barrier only issues the
-// hash atomics (the page's section 2 needs two device-wide points per step: the
+// recombination atomics (the page's section 2 needs two device-wide points per step: the
 // exact maximum before the admit test, and the resolved payloads before
 // compaction; the same phases and the same arithmetic as the per-kernel path).
 
@@ -1338,7 +1331,7 @@ __device__ __forceinline__ void score_phase(const Work &w, const LaneTab &tab, i
                 if (cur >= v.n) cur = 0;
                 vl = L;
             }
-            load_unit<LPT>(w, v, s - tab.base[L], cur, -__builtin_inff(), true, held[h].ud);
+            load_unit<kModeExpand, LPT>(w, v, s - tab.base[L], cur, -__builtin_inff(), held[h].ud);
             held[h].L = L;
             held[h].ph = v.ph;
             const float m = unit_max(held[h].ud);
@@ -1356,7 +1349,7 @@ __device__ __forceinline__ void score_phase(const Work &w, const LaneTab &tab, i
 template <typename LPT>
 __device__ __forceinline__ void admit_phase(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                             const Held (&held)[kHeld], int nh, uint32_t s_rest,
-                                            uint32_t s_end, uint32_t *cbuf)
+                                            uint32_t s_end, ClaimBuf *cbuf)
 {
     uint32_t cb_n = 0, admitted = 0;
     int last = -1;
@@ -1365,7 +1358,7 @@ __device__ __forceinline__ void admit_phase(const Work &w, const LaneTab &tab, i
         if (h < nh) {
             const int L = held[h].L;
             if (last >= 0 && L != last) {
-                if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, cbuf, cb_n);
+                if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, *cbuf, cb_n);
                 cb_n = 0;
                 const uint32_t a = wave_sum(admitted);
                 if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
@@ -1376,14 +1369,14 @@ __device__ __forceinline__ void admit_phase(const Work &w, const LaneTab &tab, i
         }
     }
     if (last >= 0) {
-        if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, cbuf, cb_n);
+        if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, *cbuf, cb_n);
         const uint32_t a = wave_sum(admitted);
         if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
     }
     if (s_rest < s_end) walk_range<kModeExpand, LPT>(w, tab, t, d, s_rest, s_end, cbuf);
 }
 
-__device__ __forceinline__ bool closure_phases(const Work &w, int t, LaneTab &tab, uint32_t *cbuf,
+__device__ __forceinline__ bool closure_phases(const Work &w, int t, LaneTab &tab, ClaimBuf *cbuf,
                                                GridSync *gs, uint32_t &gen)
 {
     for (int k = 1; k <= w.eps_iterations; ++k) {
@@ -1401,8 +1394,8 @@ template <typename LPT>
 __global__ __launch_bounds__(kBlock, 3) void k_persistent(Work w, int steps, GridSync *gs)
 {
     __shared__ LaneTab tab;
-    __shared__ uint32_t cbufs[kBlock / kWave][kClaimBuf];
-    uint32_t *cbuf = cbufs[threadIdx.x / kWave];
+    __shared__ ClaimBuf cbufs[kBlock / kWave];
+    ClaimBuf *cbuf = &cbufs[threadIdx.x / kWave];
     uint32_t gen = 0;
     if (threadIdx.x == 0) gen = __hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const LpDesc d = *w.lp;
