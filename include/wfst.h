@@ -42,7 +42,7 @@ extern "C" {
 #define WFST_OVF_SLOTS    1   /* a lane's candidate arcs in one step exceed slot_cap       */
 #define WFST_OVF_HASH     2   /* reserved: recombination is direct-mapped and never overflows */
 #define WFST_OVF_ARENA    4   /* the lane's winners-log region is full                     */
-#define WFST_OVF_CLAIMS   8   /* more distinct destinations in one pass than claims_cap    */
+#define WFST_OVF_CLAIMS   8   /* more admitted candidates in one pass than claims_cap      */
 #define WFST_OVF_FRONTIER 16  /* more surviving tokens than frontier_cap                   */
 #define WFST_OVF_PATH     32  /* best path longer than the device path buffer              */
 
@@ -104,10 +104,11 @@ typedef struct wfst_graph_desc {
  *                  in [0, 16].
  *  use_graphs      1: each decode replays one captured hipGraph of the whole
  *                  frame loop; 0: plain launches (same kernels, same results).
- *  frontier_cap    tokens per lane per step (0: 64 * max_active).
- *  claims_cap      distinct destinations per lane per pass (0: frontier_cap);
- *                  claims_cap * (1 + eps passes) * (largest out-degree of one
- *                  arc class) must stay below 2^32.
+ *  frontier_cap    tokens per lane per step (0: 64 * max_active);
+ *                  frontier_cap * (largest out-degree of one arc class) must
+ *                  stay below 2^32.
+ *  claims_cap      admitted candidates per lane per pass
+ *                  (0: min(slot_cap, max(frontier_cap, 2^20))); in [1, 2^28].
  *  arena_entries   winners-log entries per lane per decode
  *                  (0: 4 * max_active * (max_frames + 2) * (1 + eps passes),
  *                  at least 2^20); max_lanes * arena_entries < 2^31.

@@ -228,7 +228,7 @@ def test_capacity_overflow_is_flagged(cid, cap, bit):
     assert all(int(r.meta[b, 2]) & bit for b in range(2))
     assert all(int(r.meta[b, 0]) == 0 for b in range(2))
     # the same decoder recovers on a decode that fits (a claims overflow leaves
-    # stale hash slots that the next decode clears first)
+    # stale recombination-table entries that the next decode clears first)
     short = np.array([1, 2], dtype=np.int32)
     r2 = dec.decode(x, short)
     o = oracle_lanes(g, lp[:2], short, wl.beam, wl.max_active, eps_iterations=wl.eps_iterations)

@@ -284,14 +284,20 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     const int P = (g->eps_id >= 0) ? c.eps_iterations : 0;
 
     const uint64_t Q = c.frontier_cap ? (uint64_t)c.frontier_cap : std::min<uint64_t>(64ull * (uint64_t)c.max_active, 1ull << 28);
-    const uint64_t CC = c.claims_cap ? (uint64_t)c.claims_cap : Q;
     if (Q < 1 || Q > (1ull << 28)) return fail(WFST_EINVAL, "frontier_cap must lie in [1, 2^28]");
+    const uint64_t slots = c.slot_cap ? (uint64_t)c.slot_cap
+                                      : std::min<uint64_t>(std::max<uint64_t>(512ull * (uint64_t)c.max_active, 1ull << 16), 1ull << 31);
+    const uint64_t strip_cap = (slots + kWave - 1) / kWave;
+    // admitted candidates of one pass are at most its candidate arcs; past a
+    // million per lane the default stops following slot_cap
+    const uint64_t CC = c.claims_cap ? (uint64_t)c.claims_cap
+                                     : std::min<uint64_t>(slots, std::max<uint64_t>(Q, 1ull << 20));
     if (CC < 1 || CC > (1ull << 28)) return fail(WFST_EINVAL, "claims_cap must lie in [1, 2^28]");
     const uint64_t maxdeg = std::max<uint32_t>(g->max_class_deg, 1);
-    // a step counts at most claims_cap tokens per pass (main expand + closure
-    // passes), and their arcs must fit the 32-bit slot space of one lane
-    if (CC * (uint64_t)(1 + P) * maxdeg >= (1ull << 32))
-        return fail(WFST_EINVAL, "claims_cap * (1 + eps passes) * (largest out-degree of one arc class) must stay below 2^32 (32-bit slot offsets)");
+    // a live lane holds at most frontier_cap tokens, and their arcs must fit the
+    // 32-bit slot space of one lane
+    if (Q * maxdeg >= (1ull << 32))
+        return fail(WFST_EINVAL, "frontier_cap * (largest out-degree of one arc class) must stay below 2^32 (32-bit slot offsets)");
     uint64_t arena = c.arena_entries ? (uint64_t)c.arena_entries
                                      : std::max<uint64_t>(1ull << 20, 4ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P));
     if ((uint64_t)c.max_lanes * arena >= (1ull << 31)) {
@@ -299,10 +305,6 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
     }
     const uint64_t path_cap = (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
-    const uint64_t slots = c.slot_cap ? (uint64_t)c.slot_cap
-                                      : std::min<uint64_t>(std::max<uint64_t>(512ull * (uint64_t)c.max_active, 1ull << 16), 1ull << 31);
-    const uint64_t strip_cap = (slots + kWave - 1) / kWave;
-
     HIP_TRY(hipSetDevice(g->device));
     wfst_decoder_s *d = new wfst_decoder_s();
     d->g = g;

@@ -53,14 +53,15 @@ struct ArcDLW {
     float weight;
 };
 
-// Claim of a destination by its first admitted candidate: the destination, the
-// candidate's arc and its source token (position in the frontier being read).
-// When that candidate is also the winner, the source token needs no lookup.
+// An admitted candidate: destination, arc, source token (position in the
+// frontier being read) and end score. Its key (ordered score << 32 | ~arc) is
+// unique per destination, so exactly one candidate of each destination finds
+// its own key in the table once the pass is over: the winner.
 struct alignas(16) Claim {
     int32_t dest;
     int32_t arc;
     uint32_t tok;
-    uint32_t pad;
+    uint32_t score;   // binary32 bits of the end score
 };
 
 // Per-lane control block (one 128-byte line per lane).
@@ -73,19 +74,19 @@ struct alignas(128) LaneCtl {
     float beam[2];             // b_t by step parity (beam[1] = search beam before step 0)
     uint32_t maxkey[2];        // ordered exact maximum M_t by step parity
     float cutoff;              // cutoff of the latest real step (closure passes use it)
-    uint32_t nclaims;          // claims of the main expand of the current step
+    uint32_t nclaims;          // admitted candidates of the main expand of the current step
     uint32_t log_cursor;       // winners-log entries used in this lane's region
     int32_t final_entry;       // winners-log entry of the result (-1 none)
     unsigned long long final_key;  // best final candidate key of the final step
     float final_score;
-    uint32_t nclaims_eps[2];   // claims of closure pass k at [k & 1]
+    uint32_t nclaims_eps[2];   // admitted candidates of closure pass k at [k & 1]
     uint32_t nchanged[2];      // changed-token list sizes of closure pass k at [k & 1]
     uint32_t dirty;            // recombination table may hold stale entries (claims overflow)
     int32_t last_step;         // last step this lane ran
     int32_t phase_final;       // phase code of the lane's last step
-    uint32_t log_pending;      // entries of the last compaction, added to log_cursor by the next kernel
-    uint32_t snap_n;           // frontier size and winners-log cursor as a closure pass's
-    uint32_t snap_log;         //   apply kernel starts (taken by the resolve kernel before it)
+    uint32_t log_pending;      // entries of the last compaction (added by its wavefronts),
+                               //   moved into log_cursor by the next kernel that reads the log
+    uint32_t pad_a, pad_b;
     uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
                                //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
     uint32_t pad[3];

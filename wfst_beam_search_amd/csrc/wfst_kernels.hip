@@ -11,11 +11,13 @@
 //  * pass 1 (k_max) takes the exact per-lane maximum with the per-token upper
 //    bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds in IEEE fp32);
 //  * pass 2 (k_expand) admits end > M - b and recombines per destination in a
-//    direct-mapped per-lane table best[state] with one returning u64 atomicMax
-//    of (ordered score << 32 | ~arc) per candidate, so the greatest score wins
-//    and, among equal scores, the smallest arc id; the candidate that finds the
-//    entry empty appends a claim {dest, arc, source token} to the claims list;
-//  * pass 3 (k_finalize) compacts the claims into the next frontier: one
+//    direct-mapped per-lane table best[state] with one posted u64 atomicMax of
+//    (ordered score << 32 | ~arc) per candidate, so the greatest score wins
+//    and, among equal scores, the smallest arc id; every admitted candidate is
+//    appended to the lane's candidate list {dest, arc, source token, score};
+//  * pass 3 (k_finalize) keeps the candidate of each destination whose key is
+//    the table entry (the winner) and compacts the winners into the next
+//    frontier: one
 //    64-bit atomicAdd per wavefront allocates token positions and arc offsets
 //    together (tokens in the low half, arcs in the high half), which is the
 //    exclusive degree scan of the next step, done as the frontier is built; the
@@ -168,13 +170,15 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
     }
 }
 
-// Per-wavefront LDS buffer of the claims made by the expand passes.
-constexpr uint32_t kClaimBuf = 512;
+// Per-wavefront LDS buffer of the admitted candidates of the expand passes (a
+// unit admits at most kUnit of them).
+constexpr uint32_t kClaimBuf = 256;
 
 struct ClaimBuf {
     int32_t dest[kClaimBuf];
     int32_t arc[kClaimBuf];
     uint32_t tok[kClaimBuf];
+    uint32_t score[kClaimBuf];
 };
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -184,7 +188,7 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Appends the wave's n buffered claims to lane L's list: one atomic, then a
+// Appends the wave's n buffered candidates to lane L's list: one atomic, then a
 // coalesced copy out of LDS.
 __device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
                                              uint32_t n)
@@ -199,41 +203,45 @@ __device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *cou
         c.dest = cb.dest[i];
         c.arc = cb.arc[i];
         c.tok = cb.tok[i];
-        c.pad = 0u;
+        c.score = cb.score[i];
         if (base + i < w.claims_cap) dst[base + i] = c;
     }
     wave_lds_sync();
 }
 
-// Buffers the claims of one round of a wavefront (lanes with `first` set),
+// Buffers the candidates of one round of a wavefront (lanes with `adm` set),
 // flushing first if the round might not fit.
 __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
-                                            uint32_t &cb_n, bool first, int32_t dest, int32_t arc,
-                                            uint32_t tok)
+                                            uint32_t &cb_n, bool adm, int32_t dest, int32_t arc,
+                                            uint32_t tok, float score)
 {
-    const unsigned long long fm = __ballot(first);
+    const unsigned long long fm = __ballot(adm);
     if (!fm) return;
     if (cb_n + kWave > kClaimBuf) {
         flush_claims(w, L, counter, cb, cb_n);
         cb_n = 0;
     }
-    if (first) {
+    if (adm) {
         const uint32_t i = cb_n + (uint32_t)__popcll(fm & mask_lt());
         cb.dest[i] = dest;
         cb.arc[i] = arc;
         cb.tok[i] = tok;
+        cb.score[i] = __float_as_uint(score);
     }
     cb_n += (uint32_t)__popcll(fm);
 }
 
-// Key of a table entry and the source token of its winner: the claimer's
-// token when the claimer won, else through the arc's source state.
-__device__ __forceinline__ int32_t winner_token(const Work &w, int fp, int L, const Claim &cl,
-                                                int32_t arc)
+// Reads candidate i of lane L's list and decides whether it is the winner of
+// its destination: its key is the table entry after the expand pass. The
+// winner clears the entry (a loser reading after that sees 0, never its key).
+__device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, Claim &cl)
 {
-    if (arc == cl.arc) return (int32_t)cl.tok;
-    const int32_t src = w.arc_src[arc];
-    return w.pos[fp][(size_t)L * w.num_states + src];
+    cl = w.claims[(size_t)L * w.claims_cap + i];
+    if ((uint32_t)cl.dest >= (uint32_t)w.num_states) return false;
+    unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
+    const bool win = *ent == cand_key(__uint_as_float(cl.score), cl.arc);
+    if (win) *ent = 0ull;
+    return win;
 }
 
 // ---------------------------------------------------------------- k_clear
@@ -483,10 +491,9 @@ __device__ __forceinline__ float unit_max(const UnitData &ud)
 }
 
 // Admits a unit's candidates (end > cut, strict) and recombines them: on a real
-// step with one returning u64 atomicMax per candidate on the lane's
-// direct-mapped table (the candidate that finds the entry empty claims the
-// destination: its claim goes to the wavefront's LDS buffer), on the final step
-// through one wavefront-reduced atomicMax of the lane's final key.
+// step with one posted u64 atomicMax per candidate on the lane's direct-mapped
+// table, every admitted candidate going to the wavefront's LDS buffer; on the
+// final step through one wavefront-reduced atomicMax of the lane's final key.
 __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, const UnitData &ud,
                                            ClaimBuf *cb, uint32_t &cb_n, uint32_t &admitted)
 {
@@ -500,13 +507,12 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
     }
     if (ph == kPhReal) {
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
-        unsigned long long old[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r)
-            old[r] = adm[r] ? atomicMax(&tbl[ud.dst[r]], cand_key(ud.e[r], (int32_t)ud.arc[r])) : 1ull;
+            if (adm[r]) atomicMax(&tbl[ud.dst[r]], cand_key(ud.e[r], (int32_t)ud.arc[r]));
 #pragma unroll
         for (int r = 0; r < kR; ++r)
-            push_claims(w, L, &c.nclaims, *cb, cb_n, old[r] == 0ull, ud.dst[r], (int32_t)ud.arc[r], ud.tok[r]);
+            push_claims(w, L, &c.nclaims, *cb, cb_n, adm[r], ud.dst[r], (int32_t)ud.arc[r], ud.tok[r], ud.e[r]);
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -745,10 +751,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             const LaneCtl &c = w.ctl[L];
             const int ph = lane_phase(c, t);
             const uint32_t nc = c.nclaims;
-            // every claim becomes a token (the payload is the best admitted
-            // candidate): check the whole compaction fits before writing any
-            const bool fits = nc <= w.claims_cap && nc <= w.frontier_cap &&
-                              (unsigned long long)c.log_cursor + nc <= w.arena;
+            // candidates past claims_cap were never written: the lane cannot be
+            // compacted (token and log capacity are checked per wavefront)
+            const bool fits = nc <= w.claims_cap;
             if (ph == kPhReal && fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = c.log_cursor;          // winners-log base of this compaction
@@ -768,16 +773,14 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const int ph = tab.ph[L];
         if (ph == kPhReal) {
             const uint32_t nc = tab.n[L];
-            step_rec(w, L, t)[kRecDistinct] = nc;
             if (tab.f0[L] == 0.0f) {
-                // the compaction does not fit: retire the lane before writing any
-                // token; its claimed table entries stay set, so the table is
-                // cleared before the next decode
-                c.overflow |= nc > w.claims_cap ? kOvfClaims
-                            : nc > w.frontier_cap ? kOvfFrontier : kOvfArena;
+                // the candidate list overflowed: retire the lane before writing
+                // any token; its table entries stay set, so the table is cleared
+                // before the next decode
+                (void)nc;
+                c.overflow |= kOvfClaims;
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
-                c.log_pending = nc;
                 c.front_base[np] = tab.arcs[L];
             }
             c.nclaims_eps[1] = 0u;
@@ -826,20 +829,14 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         uint32_t deg = 0;
         float end = 0.0f, ub = 0.0f;
         if (valid) {
-            const Claim cl = w.claims[(size_t)L * w.claims_cap + i];
-            dst = cl.dest;
-            unsigned long long K = 0ull;
-            if ((uint32_t)dst < (uint32_t)w.num_states) {
-                unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)dst;
-                K = *ent;
-                *ent = 0ull;
-            }
-            end = ord2f((uint32_t)(K >> 32));
-            arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
-            keep = (K != 0ull) && (end > cutoff);
+            Claim cl;
+            keep = take_winner(w, L, i, cl) && __uint_as_float(cl.score) > cutoff;
             if (keep) {
+                dst = cl.dest;
+                arc = cl.arc;
+                end = __uint_as_float(cl.score);
                 const StateInfo si = w.sinfo[dst];
-                const int32_t stok = winner_token(w, p, L, cl, arc);
+                const int32_t stok = (int32_t)cl.tok;
                 keep = (uint32_t)stok < Q;
                 if (keep) {
                     // without epsilon arcs a token's entry is its compaction's base
@@ -859,12 +856,26 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const uint32_t dpre = wave_excl_sum(keep ? deg : 0u, &dsum);
         const int leader = __ffsll((long long)m) - 1;
         unsigned long long old = 0ull;
-        if (lane == leader)
+        if (lane == leader) {
             old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
+            atomicAdd(step_rec(w, L, t) + kRecDistinct, nkeep);
+            atomicAdd(&c.log_pending, nkeep);   // committed by the next kernel that reads the log
+        }
         old = __shfl(old, leader, kWave);
         const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
+        // exact capacity of this wavefront's tokens and winners-log entries: on
+        // overflow nothing is written and the lane retires (the frontier count
+        // past frontier_cap keeps every later kernel off its tokens)
+        const bool pos_ok = (unsigned long long)p0 + nkeep <= Q;
+        if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena) {
+            if (lane == leader) {
+                atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
+                c.status = kDone;
+                c.phase_final = kPhDead;
+            }
+            continue;
+        }
         if (keep) {
-            // position < nclaims <= frontier_cap and log base + nclaims <= arena (prologue)
             const uint32_t pi = p0 + rank;
             const size_t q = (size_t)L * Q + pi;
             const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
@@ -971,18 +982,20 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             const int32_t a = __shfl(eb, src, kWave) + (int32_t)(x - __shfl(dpre, src, kWave));
             const float ssc = __shfl(sc, src, kWave);
             const uint32_t stk = __shfl(tok, src, kWave);
-            bool first = false;
+            bool adm = false;
             int32_t dd = 0;
+            float e = 0.0f;
             if (x < dsum) {
                 const ArcDLW ar = w.arc_dlw[a];
-                const float e = ssc + ar.weight;
+                e = ssc + ar.weight;
                 dd = ar.dest;
-                if (e > cutoff) {
+                adm = e > cutoff;
+                if (adm) {
                     ++n_adm;
-                    first = atomicMax(&tbl[ar.dest], cand_key(e, a)) == 0ull;
+                    atomicMax(&tbl[ar.dest], cand_key(e, a));
                 }
             }
-            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, first, dd, a, stk);
+            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, stk, e);
         }
         if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n);
         const uint32_t sd = wave_sum(n_adm);
@@ -1024,15 +1037,10 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
-        if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsDistinct] += tab.n[L];
         if (tab.n[L] > w.claims_cap) {
             c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
         }
         c.nchanged[(k + 1) & 1] = 0u;
-        // nothing changes these during resolve; the apply kernel, which advances
-        // them atomically, reads the snapshot in its prologue
-        c.snap_n = (uint32_t)c.cnt[fp];
-        c.snap_log = c.log_cursor;
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
@@ -1042,22 +1050,22 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
     for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
         const int L = (int)find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
-        if (i >= tab.n[L]) continue;
+        const bool valid = i < tab.n[L];
+        Claim cl;
+        const bool win = valid && take_winner(w, L, i, cl);
+        const unsigned long long wm = __ballot(win);
+        if (wm && wlane() == __ffsll((long long)__ballot(valid)) - 1)
+            atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
+        if (!valid) continue;
         const size_t ci = (size_t)L * w.claims_cap + i;
-        const Claim cl = w.claims[ci];
         const int32_t dst = cl.dest;
-        unsigned long long K = 0ull;
-        if ((uint32_t)dst < (uint32_t)w.num_states) {
-            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)dst;
-            K = *ent;
-            *ent = 0ull;
-        }
-        const float end = ord2f((uint32_t)(K >> 32));
-        const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)K);
+        const float end = __uint_as_float(cl.score);
+        const int32_t arc = cl.arc;
+        const unsigned long long K = cand_key(end, arc);
         int32_t code = -2;
         int32_t esrc = -1;
-        if (K != 0ull && end > tab.f1[L]) {
-            const int32_t stok = winner_token(w, fp, L, cl, arc);
+        if (win && end > tab.f1[L]) {
+            const int32_t stok = (int32_t)cl.tok;
             esrc = (uint32_t)stok < Q ? w.tok_entry[fp][(size_t)L * Q + stok] : -1;
             const int32_t pd = w.pos[fp][(size_t)L * w.num_states + dst];
             const bool exists = (uint32_t)pd < tab.arcs[L] && w.tok_state[fp][(size_t)L * Q + pd] == dst;
@@ -1090,12 +1098,10 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
             uint32_t nc = 0;
-            const uint32_t n = c.snap_n;
-            const bool on = closure_lane(c, t) && n <= w.frontier_cap;
+            const bool on = closure_lane(c, t) && (uint32_t)c.cnt[fp] <= w.frontier_cap;
             if (on) nc = c.nclaims_eps[k & 1];
-            // at most nc appends and nc fresh entries: check they fit before writing
-            const bool fits = nc <= w.claims_cap && (unsigned long long)n + nc <= w.frontier_cap &&
-                              (unsigned long long)c.snap_log + nc <= w.arena;
+            // token and log capacity are checked per wavefront as it allocates
+            const bool fits = nc <= w.claims_cap;
             if (fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.T[L] = c.T;
@@ -1109,8 +1115,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         LaneCtl &c = w.ctl[L];
         c.nclaims_eps[(k + 1) & 1] = 0u;
         if (tab.f0[L] != 0.0f) {
-            c.overflow |= tab.n[L] > w.claims_cap ? kOvfClaims
-                        : c.snap_n + tab.n[L] > w.frontier_cap ? kOvfFrontier : kOvfArena;
+            c.overflow |= kOvfClaims;
             c.status = kDone; c.phase_final = kPhDead;
         }
     }
@@ -1159,10 +1164,20 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         old = __shfl(old, leader, kWave);
         lb = __shfl(lb, leader, kWave);
         cb = __shfl(cb, leader, kWave);
+        // exact capacity of this wavefront's appends and winners-log entries: on
+        // overflow nothing is written and the lane retires
+        const bool pos_ok = (unsigned long long)(uint32_t)old + (uint32_t)__popcll(mn) <= Q;
+        if (!pos_ok || (unsigned long long)lb + (uint32_t)__popcll(ma) > w.arena) {
+            if (lane == leader) {
+                atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
+                c.status = kDone;
+                c.phase_final = kPhDead;
+            }
+            continue;
+        }
         if (mn) write_strips(w.strip_tok[fp] + (size_t)L * w.strip_cap, w.strip_cap, (uint32_t)old,
                              (uint32_t)(old >> 32), dpre, dsum, mn);
         if (!any) continue;
-        // positions and entries fit: the prologue checked n + nc and log + nc
         const uint32_t ra = (uint32_t)__popcll(ma & mask_lt());
         const uint32_t le = lb + ra;
         const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
