@@ -38,25 +38,24 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     D distinct destinations, n' survivors = D without epsilon arcs, F lane-frames,
     E epsilon arcs, e*V log-prob row bytes):
       max      12 n + 6 S + e V F       (token score + arc range, ilabel u16 + weight f32, one row per lane-frame)
-      expand   12 n + 6 S + 12 C + 8 D + e V F   (+ dest i32 and u64 payload atomic per admitted, hash key + claim per distinct)
-      finalize 28 D + 20 n'             (claim + payload read-back + targeted clear; next-frontier token 12 B + winners-log entry 8 B)
-      eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, claims, changed tokens)
-      path     20 n + 6 S + 12 C + 28 D + 20 n' + e V F (+ eps terms): the whole step, counted once
-               (also the persistent kernel's bytes: it runs every phase of the frame loop)
+      expand   12 n + 6 S + 28 C + e V F   (+ per admitted: dest i32, u64 table atomic, 16-byte candidate record)
+      finalize 24 C + 28 D              (candidate + table entry read; per winner: table clear 8 B,
+                                         next-frontier token 12 B, winners-log entry 8 B)
+      eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, candidates, changed tokens)
+      path     12 n + 6 S + 52 C + 28 D + e V F (+ eps terms): the whole step, tokens and arcs counted once
     """
     n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
     E, De, Ne = st["eps_arcs"], st["eps_distinct"], st["eps_changed"]
     row = elem_bytes * vocab * F
     per = {
         "max": 12 * n + 6 * S + row,
-        "expand": 12 * n + 6 * S + 12 * C + 8 * D + row,
-        "finalize": 28 * D + 20 * D,
+        "expand": 12 * n + 6 * S + 28 * C + row,
+        "finalize": 24 * C + 28 * D,
         "eps_expand": 16 * E,
         "eps_resolve": 28 * De,
         "eps_apply": 20 * Ne,
     }
-    path = 20 * n + 6 * S + 12 * C + 28 * D + 20 * D + row + 16 * E + 28 * De + 20 * Ne
-    per["persistent"] = path      # the persistent kernel runs the whole frame loop
+    path = 12 * n + 6 * S + 52 * C + 28 * D + row + 16 * E + 28 * De + 20 * Ne
     return per, path
 
 
@@ -122,9 +121,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (1-5); 3 = HLG-scale")
     ap.add_argument("--eager", action="store_true", help="plain launches instead of the captured graph")
-    ap.add_argument("--mode", choices=("graph", "persistent"), default="graph",
-                    help="graph: one kernel per phase, captured as a hipGraph; persistent: the frame "
-                         "loop as one cooperative kernel with grid barriers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
@@ -163,7 +159,7 @@ def main():
     dg = wb.Graph(graph, device=0)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
-                     grid_blocks=args.grid, persistent=args.mode == "persistent")
+                     grid_blocks=args.grid)
     x = torch.from_numpy(lp).to(dev)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -228,8 +224,7 @@ def main():
                                f"{graph.num_arcs} arcs, power-law out-degree), log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
-                   "execution": "persistent cooperative kernel" if args.mode == "persistent"
-                   else ("per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay")},
+                   "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay"},
         "arcs_expanded_per_s": round(arcs_ps, 1),
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),

@@ -115,12 +115,6 @@ typedef struct wfst_graph_desc {
  *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
  *  slot_cap        candidate arcs (slots) per lane per step (0: 512 * max_active,
  *                  at least 2^16); at most 2^31.
- *  persistent      1: the whole frame loop runs as one cooperatively launched
- *                  kernel whose phases are separated by grid barriers (every
- *                  workgroup resident; the grid is capped at the device's
- *                  co-resident size), and the exact-max phase keeps candidates
- *                  in registers for the admit phase; 0: one launch per phase
- *                  (captured as a graph when use_graphs = 1). Same results.
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -137,7 +131,6 @@ typedef struct wfst_decoder_config {
     int32_t grid_blocks;
     int64_t arena_entries;
     int64_t slot_cap;
-    int32_t persistent;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -245,8 +238,7 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_EPS_RESOLVE  7  /* closure pass: append / replace decisions                 */
 #define WFST_K_EPS_APPLY    8  /* closure pass: apply them                                 */
 #define WFST_K_BACKTRACK    9  /* best path to arc ids and words                           */
-#define WFST_K_PERSISTENT  10  /* the whole frame loop in persistent mode                   */
-#define WFST_K_COUNT       11
+#define WFST_K_COUNT       10
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

@@ -19,7 +19,7 @@ GIDX = {name: i for i, name in enumerate(wb.STEP_FIELDS)}
 
 def gpu_decode(graph, lp, lengths, beam, max_active, min_active=0, allow_partial=False,
                eps_iterations=0, use_graphs=True, max_lanes=None, max_frames=None, dgraph=None,
-               with_steps=True, persistent=False, **caps):
+               with_steps=True, **caps):
     import torch
     B, T, V = lp.shape
     own = dgraph is None
@@ -27,7 +27,7 @@ def gpu_decode(graph, lp, lengths, beam, max_active, min_active=0, allow_partial
     dec = wb.Decoder(g, beam, max_active, min_active=min_active, allow_partial=allow_partial,
                      max_lanes=max_lanes or B, max_frames=max_frames or max(T, 1),
                      lp_dtype="f16" if lp.dtype == np.float16 else "f32",
-                     eps_iterations=eps_iterations, use_graphs=use_graphs, persistent=persistent,
+                     eps_iterations=eps_iterations, use_graphs=use_graphs,
                      **caps)
     x = torch.from_numpy(np.ascontiguousarray(lp)).cuda()
     r = dec.decode(x, lengths)

@@ -85,10 +85,6 @@ struct wfst_decoder_s {
     Work w{};
     int grid = 0;
     int passes = 0;                 // closure passes run per step (0 without epsilon arcs)
-    bool persistent = false;        // frame loop as one cooperative launch
-    int pgrid = 0;                  // its grid
-    GridSync *gsync = nullptr;
-    uint32_t *h_abort = nullptr;    // pinned: the barrier's abort flag after a decode
     std::vector<void *> owned;
     size_t bytes = 0;
     LaneCtl *ctl = nullptr;
@@ -115,7 +111,6 @@ struct wfst_decoder_s {
         if (cap_stream) (void)hipStreamDestroy(cap_stream);
         if (h_in) (void)hipHostFree(h_in);
         if (h_res) (void)hipHostFree(h_res);
-        if (h_abort) (void)hipHostFree(h_abort);
         for (void *p : owned) (void)hipFree(p);
         if (g && g->refs.fetch_sub(1) == 1) delete g;
     }
@@ -353,28 +348,14 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&w.wlog, L * arena);
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
-    if (c.persistent) A(&d->gsync, 1);
     if (r != WFST_OK) { delete d; return r; }
-    w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.gsync = d->gsync;
-    if (c.persistent) {
-        int coop = 0, maxg = 0;
-        hipError_t ce = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, g->device);
-        if (ce == hipSuccess) ce = persistent_max_grid(c.lp_dtype, &maxg);
-        if (ce != hipSuccess || !coop || maxg < 1) {
-            delete d;
-            return fail(WFST_EINVAL, "persistent mode needs cooperative launch on this device");
-        }
-        d->persistent = true;
-        d->pgrid = std::min(d->grid, maxg);
-    }
+    w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths;
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
     if (e == hipSuccess) e = hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
     for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
-    if (e == hipSuccess && d->gsync) e = hipMemset(d->gsync, 0, sizeof(GridSync));
-    if (e == hipSuccess && d->gsync) e = hipHostMalloc((void **)&d->h_abort, 4, hipHostMallocDefault);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) { delete d; return hip_fail(e, "decoder workspace"); }
@@ -408,27 +389,10 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
     d->ev_used = 0;
     if ((e = launch(d, kKClear, 0, 0, s)) != hipSuccess) return e;
     if ((e = launch(d, kKInit, 0, 0, s)) != hipSuccess) return e;
-    // the persistent kernel closes the start frontier itself
-    for (int k = 1; k <= d->passes && !d->persistent; ++k) {
+    for (int k = 1; k <= d->passes; ++k) {
         if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
-    }
-    if (d->persistent) {
-        if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
-        if (d->prof_on) {
-            if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
-            if ((e = hipEventRecord(d->ev[d->ev_used], s)) != hipSuccess) return e;
-            d->ev_kind[d->ev_used++] = kKPersistent;
-        }
-        if ((e = launch_persistent(d->w, steps, d->pgrid, d->gsync, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
-        if (d->prof_on) {
-            if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
-            if ((e = hipEventRecord(d->ev[d->ev_used], s)) != hipSuccess) return e;
-            d->ev_kind[d->ev_used++] = -1;
-        }
-        return hipSuccess;
     }
     if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
@@ -509,7 +473,7 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     const int steps = maxlen + 1;
     // timing events cannot be read back from a replayed graph: a profiled decode
     // runs the same kernels as plain launches
-    if (c.use_graphs && !d->prof_on && !d->persistent) {
+    if (c.use_graphs && !d->prof_on) {
         int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
         bucket = std::min(bucket, c.max_frames + 1);
         hipGraphExec_t ex = nullptr;
@@ -525,10 +489,7 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     d->last_profiled = d->prof_on;
     const size_t rs = d->w.res_stride;
     HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
-    if (d->persistent) HIP_TRY(hipMemcpyAsync(d->h_abort, &d->gsync->abort, 4, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
-    if (d->persistent && *d->h_abort)
-        return fail(WFST_EDEVICE, "persistent decode aborted: a grid barrier wait passed its time bound");
 
     d->last_B = B;
     d->last_len.assign(lengths_host, lengths_host + B);

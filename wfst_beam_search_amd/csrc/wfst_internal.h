@@ -92,14 +92,6 @@ struct alignas(128) LaneCtl {
     uint32_t pad[3];
 };
 
-// Grid barrier state of the persistent kernel.
-struct GridSync {
-    uint32_t count;   // arrivals in the current generation
-    uint32_t gen;     // generation (never reset)
-    uint32_t abort;   // raised when a wait passes its time bound
-    uint32_t pad;
-};
-
 // Device-resident description of the caller's log_prob tensor, rewritten before
 // every decode so that a captured graph stays valid across decodes.
 struct LpDesc {
@@ -155,21 +147,16 @@ struct Work {
     int2 *wlog;               // [L][arena] winners log {prev entry, arc}
     int32_t *res;             // [L][res_stride] results
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]
-    GridSync *gsync;          // persistent mode only (else null)
 };
 
 // Kernels of a decode, in launch order within a step (ids match WFST_K_*).
 enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
-    kKEpsApply, kKBacktrack, kKPersistent, kKCount
+    kKEpsApply, kKBacktrack, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.
 hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s);
-// The whole frame loop (steps 0 .. steps-1 and the closures) as one cooperative launch.
-hipError_t launch_persistent(const Work &w, int steps, int grid, GridSync *gs, hipStream_t s);
-// Largest co-resident grid of the persistent kernel on the current device.
-hipError_t persistent_max_grid(int lp_dtype, int *max_blocks);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
 enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };

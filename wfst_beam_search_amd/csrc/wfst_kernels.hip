@@ -297,10 +297,6 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
     c.last_step = -1;
     c.phase_final = kPhNone;
     c.cnt[1] = 0ull;
-    if (L == 0 && w.gsync) {
-        w.gsync->count = 0u;
-        w.gsync->abort = 0u;
-    }
     if (!on) { c.cnt[0] = 0ull; return; }
     const int32_t s = w.start_state;
     const StateInfo si = w.sinfo[s];
@@ -1267,189 +1263,6 @@ __global__ __launch_bounds__(kWave) void k_backtrack(Work w)
         R[6] = c.phase_final;
         R[7] = c.last_step;
     }
-}
-
-// ---------------------------------------------------------- persistent mode
-// One cooperatively launched grid (every workgroup resident) runs the whole
-// frame loop. Phases are separated by a grid barrier instead of kernel
-// boundaries, and the score phase keeps up to kHeld units of candidates per
-// wavefront in registers, so the admit phase after the barrier only issues the
-// recombination atomics (the page's section 2 needs two device-wide points per step: the
-// exact maximum before the admit test, and the resolved payloads before
-// compaction; the same phases and the same arithmetic as the per-kernel path).
-
-constexpr int kHeld = 2;
-constexpr unsigned long long kSyncTimeoutTicks = 200000000ull;   // 2 s of the 100 MHz clock
-
-// Grid barrier by generation. Arrival is an agent-scope atomic with release
-// fences around it; the wait is bounded in wall-clock time: past the bound the
-// waiter raises `abort`, and every workgroup leaves at its next barrier, so the
-// grid always drains.
-__device__ __forceinline__ bool grid_sync(GridSync *gs, uint32_t &gen)
-{
-    __shared__ int ok_s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t g = gen;
-        const uint32_t arrived = atomicAdd(&gs->count, 1u) + 1u;
-        if (arrived == gridDim.x) {
-            atomicExch(&gs->count, 0u);
-            __threadfence();
-            atomicAdd(&gs->gen, 1u);
-        } else {
-            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-                if (__hip_atomic_load(&gs->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncTimeoutTicks) {
-                    atomicExch(&gs->abort, 1u);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        __threadfence();
-        gen = g + 1u;
-        ok_s = __hip_atomic_load(&gs->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
-    }
-    __syncthreads();
-    return ok_s != 0;
-}
-
-struct Held {
-    int L, ph;
-    UnitData ud;
-};
-
-// Score phase: the first kHeld units of this wavefront's share are loaded in
-// full (no bound skip: the admit phase needs every candidate) and kept; the
-// rest only contribute to the maximum (with the bound skip) and are loaded
-// again after the barrier.
-template <typename LPT>
-__device__ __forceinline__ void score_phase(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
-                                            Held (&held)[kHeld], int &nh, uint32_t &s_rest, uint32_t &s_end)
-{
-    const int p = t & 1;
-    uint32_t s;
-    wave_share(tab.base[w.max_lanes], &s, &s_end);
-    nh = 0;
-    int vl = -1;
-    uint32_t cur = 0;
-    LaneView v;
-#pragma unroll
-    for (int h = 0; h < kHeld; ++h) {
-        if (s < s_end) {
-            const int L = find_lane(tab.base, w.max_lanes, s);
-            if (L != vl) {
-                v = lane_view(w, tab, t, d, L);
-                cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
-                if (cur >= v.n) cur = 0;
-                vl = L;
-            }
-            load_unit<kModeExpand, LPT>(w, v, s - tab.base[L], cur, -__builtin_inff(), held[h].ud);
-            held[h].L = L;
-            held[h].ph = v.ph;
-            const float m = unit_max(held[h].ud);
-            if (wlane() == 0 && m > -__builtin_inff()) atomicMax(&w.ctl[L].maxkey[p], f2ord(m));
-            nh = h + 1;
-            ++s;
-        }
-    }
-    s_rest = s;
-    if (s < s_end) walk_range<kModeMax, LPT>(w, tab, t, d, s, s_end, nullptr);
-}
-
-// Admit phase: the kept units admit from registers against the exact cutoff;
-// the others are loaded again (bound skip against the cutoff).
-template <typename LPT>
-__device__ __forceinline__ void admit_phase(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
-                                            const Held (&held)[kHeld], int nh, uint32_t s_rest,
-                                            uint32_t s_end, ClaimBuf *cbuf)
-{
-    uint32_t cb_n = 0, admitted = 0;
-    int last = -1;
-#pragma unroll
-    for (int h = 0; h < kHeld; ++h) {
-        if (h < nh) {
-            const int L = held[h].L;
-            if (last >= 0 && L != last) {
-                if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, *cbuf, cb_n);
-                cb_n = 0;
-                const uint32_t a = wave_sum(admitted);
-                if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
-                admitted = 0;
-            }
-            last = L;
-            admit_unit(w, L, held[h].ph, tab.f1[L], held[h].ud, cbuf, cb_n, admitted);
-        }
-    }
-    if (last >= 0) {
-        if (cb_n) flush_claims(w, last, &w.ctl[last].nclaims, *cbuf, cb_n);
-        const uint32_t a = wave_sum(admitted);
-        if (wlane() == 0 && a) atomicAdd(step_rec(w, last, t) + kRecAdmitted, a);
-    }
-    if (s_rest < s_end) walk_range<kModeExpand, LPT>(w, tab, t, d, s_rest, s_end, cbuf);
-}
-
-__device__ __forceinline__ bool closure_phases(const Work &w, int t, LaneTab &tab, ClaimBuf *cbuf,
-                                               GridSync *gs, uint32_t &gen)
-{
-    for (int k = 1; k <= w.eps_iterations; ++k) {
-        ph_eps_expand(w, t, k, tab, cbuf);
-        if (!grid_sync(gs, gen)) return false;
-        ph_eps_resolve(w, t, k, tab);
-        if (!grid_sync(gs, gen)) return false;
-        ph_eps_apply(w, t, k, tab);
-        if (!grid_sync(gs, gen)) return false;
-    }
-    return true;
-}
-
-template <typename LPT>
-__global__ __launch_bounds__(kBlock, 3) void k_persistent(Work w, int steps, GridSync *gs)
-{
-    __shared__ LaneTab tab;
-    __shared__ ClaimBuf cbufs[kBlock / kWave];
-    ClaimBuf *cbuf = &cbufs[threadIdx.x / kWave];
-    uint32_t gen = 0;
-    if (threadIdx.x == 0) gen = __hip_atomic_load(&gs->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const LpDesc d = *w.lp;
-    if (!closure_phases(w, -1, tab, cbuf, gs, gen)) return;
-    for (int t = 0; t < steps; ++t) {
-        step_open(w, t, tab);
-        Held held[kHeld];
-        int nh;
-        uint32_t s_rest, s_end;
-        score_phase<LPT>(w, tab, t, d, held, nh, s_rest, s_end);
-        if (!grid_sync(gs, gen)) return;
-        step_cutoffs(w, t, tab);
-        admit_phase<LPT>(w, tab, t, d, held, nh, s_rest, s_end, cbuf);
-        if (!grid_sync(gs, gen)) return;
-        ph_finalize(w, t, tab);
-        if (!grid_sync(gs, gen)) return;
-        if (!closure_phases(w, t, tab, cbuf, gs, gen)) return;
-    }
-}
-
-hipError_t launch_persistent(const Work &w, int steps, int grid, GridSync *gs, hipStream_t s)
-{
-    Work wc = w;
-    int st = steps;
-    GridSync *g = gs;
-    void *args[] = {&wc, &st, &g};
-    const void *fn = w.lp_dtype == 1 ? (const void *)k_persistent<__half> : (const void *)k_persistent<float>;
-    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kBlock), args, 0, s);
-}
-
-hipError_t persistent_max_grid(int lp_dtype, int *max_blocks)
-{
-    int dev = 0, ncu = 0, per = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const void *fn = lp_dtype == 1 ? (const void *)k_persistent<__half> : (const void *)k_persistent<float>;
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kBlock, 0);
-    *max_blocks = per * ncu;
-    return e;
 }
 
 // ---------------------------------------------------------------- launchers
