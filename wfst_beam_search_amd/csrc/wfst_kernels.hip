@@ -572,7 +572,8 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
             if (cb_n) flush_claims(w, L, &c.nclaims, *cbuf, cb_n);
             cb_n = 0;
             const uint32_t a = wave_sum(admitted);
-            if (lane == 0 && a) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
+            // real steps: the finalize kernel records the list length instead
+            if (lane == 0 && a && v.ph != kPhReal) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
         } else if (run > posted && lane == 0) {
             atomicMax(&c.maxkey[p], f2ord(run));
         }
@@ -737,6 +738,29 @@ __global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
 
 // -------------------------------------------------------------- k_finalize
 
+// Result of the final step: the winners-log entry of the best final arc (key
+// fk, source token stok of frontier parity p). Written by exactly one thread.
+__device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, int p,
+                                            unsigned long long fk, int32_t stok)
+{
+    const float end = ord2f((uint32_t)(fk >> 32));
+    const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)fk);
+    const int32_t esrc = (uint32_t)stok < w.frontier_cap
+        ? w.tok_entry[p][(size_t)L * w.frontier_cap + stok] : -1;
+    const uint32_t le = c.log_cursor;
+    if (le < w.arena) {
+        const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
+        w.wlog[e] = make_int2(esrc, arc);
+        c.log_cursor = le + 1u;
+        c.final_entry = e;
+        c.final_score = end;
+        c.reached_final = 1;
+    } else {
+        atomicOr(&c.overflow, kOvfArena);
+    }
+}
+
+
 __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 {
     const int p = t & 1, np = p ^ 1;
@@ -758,6 +782,19 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             tab.f0[L] = fits ? 1.0f : 0.0f;
             tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;
             tab.fb[L] = c.front_base[p];
+            if (ph == kPhFinal && !w.has_eps) {
+                // without epsilon arcs no state -> token map is kept: the final
+                // winner's source token is found by scanning the frontier for the
+                // source state of the winning arc (tokens are unique per state)
+                const unsigned long long fk = c.final_key;
+                const uint32_t n = (uint32_t)c.cnt[p];
+                tab.n[L] = 0u;
+                if (fk != 0ull && n <= w.frontier_cap) {
+                    units = (n + kWave - 1) / kWave;
+                    tab.n[L] = n;
+                    tab.arcs[L] = (uint32_t)w.arc_src[(int32_t)(0xFFFFFFFFu - (uint32_t)fk)];
+                }
+            }
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -769,11 +806,11 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const int ph = tab.ph[L];
         if (ph == kPhReal) {
             const uint32_t nc = tab.n[L];
+            step_rec(w, L, t)[kRecAdmitted] = nc;
             if (tab.f0[L] == 0.0f) {
                 // the candidate list overflowed: retire the lane before writing
                 // any token; its table entries stay set, so the table is cleared
                 // before the next decode
-                (void)nc;
                 c.overflow |= kOvfClaims;
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
@@ -783,24 +820,10 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         } else if (ph == kPhFinal) {
             const unsigned long long fk = c.final_key;
             step_rec(w, L, t)[kRecDistinct] = fk ? 1u : 0u;
-            if (fk) {
-                const float end = ord2f((uint32_t)(fk >> 32));
+            if (fk && w.has_eps) {
                 const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)fk);
-                const int32_t src = w.arc_src[arc];
-                const int32_t stok = w.pos[p][(size_t)L * w.num_states + src];
-                const int32_t esrc = (uint32_t)stok < w.frontier_cap
-                    ? w.tok_entry[p][(size_t)L * w.frontier_cap + stok] : -1;
-                const uint32_t le = c.log_cursor;
-                if (le < w.arena) {
-                    const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
-                    w.wlog[e] = make_int2(esrc, arc);
-                    c.log_cursor = le + 1u;
-                    c.final_entry = e;
-                    c.final_score = end;
-                    c.reached_final = 1;
-                } else {
-                    c.overflow |= kOvfArena;
-                }
+                const int32_t stok = w.pos[p][(size_t)L * w.num_states + w.arc_src[arc]];
+                final_entry(w, c, L, p, fk, stok);
             }
             c.status = kDone;
         }
@@ -814,6 +837,13 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
     const uint32_t Q = w.frontier_cap;
     for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
         const int L = find_lane(tab.base, nl, u);
+        if (tab.ph[L] == kPhFinal) {
+            // the frontier scan of the final step (graphs without epsilon arcs)
+            const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+            if (i < tab.n[L] && (uint32_t)w.tok_state[p][(size_t)L * Q + i] == tab.arcs[L])
+                final_entry(w, w.ctl[L], L, p, w.ctl[L].final_key, (int32_t)i);
+            continue;
+        }
         const uint32_t nc = tab.n[L];
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const bool valid = i < nc;
@@ -883,7 +913,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             w.tok_off[np][q] = a0 + dpre;
             w.tok_abeg[np][q] = abeg;
             w.tok_ub[np][q] = ub;
-            w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
+            if (w.has_eps) w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
         }
         write_strips(w.strip_tok[np] + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
