@@ -243,9 +243,9 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its
  * kernels as plain launches (no graph replay, as the page's sections 9 and 12
- * profile) and records a hipEvent on the decode's stream before every launch
- * and after the last one, so the time between consecutive events bounds each
- * launch. Results are identical with timing on or off.
+ * profile), each with a start / end hipEvent pair that its dispatch records on
+ * the decode's stream, so each pair spans that kernel's execution alone.
+ * Results are identical with timing on or off.
  * Errors: WFST_EINVAL, WFST_EDEVICE.
  */
 int wfst_decoder_profile(wfst_decoder_t d, int32_t enable);

@@ -97,7 +97,7 @@ struct wfst_decoder_s {
     int last_B = 0;
     std::vector<int32_t> last_len;
     int last_steps = 0;
-    bool prof_on = false;            // record hipEvents between launches
+    bool prof_on = false;            // time every launch with a start / end event pair
     bool last_profiled = false;
     std::vector<hipEvent_t> ev;
     std::vector<int> ev_kind;
@@ -374,10 +374,10 @@ extern "C" int wfst_decoder_destroy(wfst_decoder_t d)
 static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
 {
     if (d->prof_on) {
-        if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
-        hipError_t e = hipEventRecord(d->ev[d->ev_used], s);
-        if (e != hipSuccess) return e;
-        d->ev_kind[d->ev_used++] = id;
+        if (2 * d->ev_used + 1 >= d->ev.size()) return hipErrorInvalidValue;
+        const size_t i = d->ev_used++;
+        d->ev_kind[i] = id;
+        return launch_kernel(id, d->w, t, k, d->grid, s, d->ev[2 * i], d->ev[2 * i + 1]);
     }
     return launch_kernel(id, d->w, t, k, d->grid, s);
 }
@@ -406,11 +406,6 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
         }
     }
     if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
-    if (d->prof_on) {
-        if (d->ev_used >= d->ev.size()) return hipErrorInvalidValue;
-        if ((e = hipEventRecord(d->ev[d->ev_used], s)) != hipSuccess) return e;
-        d->ev_kind[d->ev_used++] = -1;
-    }
     return hipSuccess;
 }
 
@@ -581,9 +576,9 @@ extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
     HIP_TRY(hipSetDevice(d->g->device));
     if (enable && d->ev.empty()) {
         const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(3 + 3 * d->passes);
-        d->ev.resize(n, nullptr);
+        d->ev.resize(2 * n, nullptr);
         d->ev_kind.assign(n, -1);
-        for (size_t i = 0; i < n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));
+        for (size_t i = 0; i < 2 * n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));
     }
     d->prof_on = enable != 0;
     return WFST_OK;
@@ -596,9 +591,9 @@ extern "C" int wfst_decoder_kernel_times(wfst_decoder_t d, double *out, int32_t 
     if (!d->last_profiled) return fail(WFST_EINVAL, "the last decode was not profiled");
     HIP_TRY(hipSetDevice(d->g->device));
     std::vector<double> v(2 * kKCount, 0.0);
-    for (size_t i = 0; i + 1 < d->ev_used; ++i) {
+    for (size_t i = 0; i < d->ev_used; ++i) {
         float ms = 0.0f;
-        HIP_TRY(hipEventElapsedTime(&ms, d->ev[i], d->ev[i + 1]));
+        HIP_TRY(hipEventElapsedTime(&ms, d->ev[2 * i], d->ev[2 * i + 1]));
         const int id = d->ev_kind[i];
         if (id >= 0 && id < kKCount) { v[2 * id] += ms; v[2 * id + 1] += 1.0; }
     }

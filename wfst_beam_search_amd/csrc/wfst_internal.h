@@ -156,7 +156,9 @@ enum : int {
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.
-hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s);
+// With e0 / e1 given, the dispatch records the kernel's start and end in them.
+hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s,
+                         hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
 enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };

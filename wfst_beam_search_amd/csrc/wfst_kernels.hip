@@ -26,6 +26,7 @@
 //  * epsilon closure passes (expand / resolve / apply) on TLG graphs.
 // All fp32 arithmetic is single operations in the order the page fixes; the
 // file is compiled with -ffp-contract=off.
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -1297,29 +1298,40 @@ __global__ __launch_bounds__(kWave) void k_backtrack(Work w)
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s)
+// Plain launch, or with timing events recorded by the dispatch itself (start and
+// end of the kernel's execution) when e0 is given.
+template <typename... A>
+static void go(void (*kern)(A...), dim3 g, dim3 b, hipStream_t s, hipEvent_t e0, hipEvent_t e1, A... args)
+{
+    if (e0) hipExtLaunchKernelGGL(kern, g, b, 0, s, e0, e1, 0, args...);
+    else hipLaunchKernelGGL(kern, g, b, 0, s, args...);
+}
+
+hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1)
 {
     const bool f16 = w.lp_dtype == 1;
+    const dim3 G(grid), B(kBlock);
     switch (id) {
-    case kKClear: hipLaunchKernelGGL(k_clear, dim3(grid), dim3(kBlock), 0, s, w); break;
-    case kKInit: hipLaunchKernelGGL(k_init, dim3(1), dim3(kWave), 0, s, w); break;
+    case kKClear: go(k_clear, G, B, s, e0, e1, w); break;
+    case kKInit: go(k_init, dim3(1), dim3(kWave), s, e0, e1, w); break;
     case kKLpmax:
-        if (f16) hipLaunchKernelGGL(k_lpmax<__half>, dim3(grid), dim3(kBlock), 0, s, w);
-        else hipLaunchKernelGGL(k_lpmax<float>, dim3(grid), dim3(kBlock), 0, s, w);
+        if (f16) go(k_lpmax<__half>, G, B, s, e0, e1, w);
+        else go(k_lpmax<float>, G, B, s, e0, e1, w);
         break;
     case kKMax:
-        if (f16) hipLaunchKernelGGL(k_max<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
-        else hipLaunchKernelGGL(k_max<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        if (f16) go(k_max<__half>, G, B, s, e0, e1, w, t);
+        else go(k_max<float>, G, B, s, e0, e1, w, t);
         break;
     case kKExpand:
-        if (f16) hipLaunchKernelGGL(k_expand<__half>, dim3(grid), dim3(kBlock), 0, s, w, t);
-        else hipLaunchKernelGGL(k_expand<float>, dim3(grid), dim3(kBlock), 0, s, w, t);
+        if (f16) go(k_expand<__half>, G, B, s, e0, e1, w, t);
+        else go(k_expand<float>, G, B, s, e0, e1, w, t);
         break;
-    case kKFinalize: hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kBlock), 0, s, w, t); break;
-    case kKEpsExpand: hipLaunchKernelGGL(k_eps_expand, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
-    case kKEpsResolve: hipLaunchKernelGGL(k_eps_resolve, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
-    case kKEpsApply: hipLaunchKernelGGL(k_eps_apply, dim3(grid), dim3(kBlock), 0, s, w, t, k); break;
-    case kKBacktrack: hipLaunchKernelGGL(k_backtrack, dim3(w.max_lanes), dim3(kWave), 0, s, w); break;
+    case kKFinalize: go(k_finalize, G, B, s, e0, e1, w, t); break;
+    case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, w, t, k); break;
+    case kKEpsResolve: go(k_eps_resolve, G, B, s, e0, e1, w, t, k); break;
+    case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, w, t, k); break;
+    case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, w); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
