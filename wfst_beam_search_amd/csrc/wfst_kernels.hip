@@ -528,12 +528,25 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
     }
 }
 
+// XCD-aware block order: workgroups are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8), so block b takes virtual position
+// (b % 8) * (grid / 8) + b / 8 and each XCD works on one contiguous eighth of a
+// kernel's unit space. Lanes are laid out in the same order in every kernel's
+// space, so a lane's tokens, strips and candidates are mostly written and read
+// again on the same XCD, where they are still in that XCD's L2.
+__device__ __forceinline__ uint32_t vblock()
+{
+    const uint32_t g = gridDim.x;
+    if (g & 7u) return blockIdx.x;
+    return (blockIdx.x & 7u) * (g >> 3) + (blockIdx.x >> 3);
+}
+
 // This wavefront's contiguous, equal share [s, s_end) of `total` units.
 __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t *s_end)
 {
     const uint32_t wpb = kBlock / kWave;
     const uint32_t nwaves = gridDim.x * wpb;
-    const uint32_t wid = blockIdx.x * wpb + threadIdx.x / kWave;
+    const uint32_t wid = vblock() * wpb + threadIdx.x / kWave;
     *s = (uint32_t)(((unsigned long long)total * wid) / nwaves);
     *s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
 }
@@ -832,11 +845,11 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
-    const uint32_t wpb = kBlock / kWave;
-    const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+    uint32_t u_beg, u_end;
+    wave_share(total, &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         if (tab.ph[L] == kPhFinal) {
             // the frontier scan of the final step (graphs without epsilon arcs)
@@ -971,11 +984,11 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
-    const uint32_t wpb = kBlock / kWave;
-    const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+    uint32_t u_beg, u_end;
+    wave_share(total, &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
@@ -1071,10 +1084,10 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
-    const uint32_t wpb = kBlock / kWave;
-    const uint32_t nwaves = gridDim.x * wpb;
     const uint32_t Q = w.frontier_cap;
-    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+    uint32_t u_beg, u_end;
+    wave_share(total, &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = (int)find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
         const bool valid = i < tab.n[L];
@@ -1148,11 +1161,11 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
-    const uint32_t wpb = kBlock / kWave;
-    const uint32_t nwaves = gridDim.x * wpb;
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    for (uint32_t u = blockIdx.x * wpb + threadIdx.x / kWave; u < total; u += nwaves) {
+    uint32_t u_beg, u_end;
+    wave_share(total, &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = (int)find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const bool valid = i < tab.n[L];
