@@ -65,7 +65,6 @@ struct wfst_graph_s {
     std::vector<void *> owned;
     size_t bytes = 0;
     StateInfo *sinfo = nullptr;
-    ArcLW *arc_lw = nullptr;
     ArcDLW *arc_dlw = nullptr;
     int32_t *olabel = nullptr, *arc_src = nullptr;
 
@@ -210,13 +209,11 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     // interleaved arc records in CSR order (section 4's split, regrouped so that
     // the fields a pass reads for one arc share a cache line)
     std::vector<int32_t> src((size_t)A);
-    std::vector<ArcLW> lw((size_t)A);
     std::vector<ArcDLW> dlw((size_t)A);
     for (int32_t s = 0; s < S; ++s)
         for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) src[(size_t)a] = s;
     for (int32_t a = 0; a < A; ++a) {
         const uint32_t il = g->ilabel[a] == -1 ? (uint32_t)kFinalLabel : (uint32_t)g->ilabel[a];
-        lw[(size_t)a] = ArcLW{il, g->weight[a]};
         dlw[(size_t)a] = ArcDLW{g->dest[a], il, g->weight[a]};
     }
 
@@ -230,7 +227,6 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     h->max_class_deg = md;
     int r = WFST_OK;
     if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->arc_lw, (size_t)A, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->arc_dlw, (size_t)A, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->olabel, (size_t)A, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->arc_src, (size_t)A, &h->owned, &h->bytes))) {
@@ -240,7 +236,6 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMemcpy(h->sinfo, info.data(), sizeof(StateInfo) * (size_t)S, hipMemcpyHostToDevice);
     if (A > 0) {
-        if (e == hipSuccess) e = hipMemcpy(h->arc_lw, lw.data(), sizeof(ArcLW) * (size_t)A, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemcpy(h->arc_dlw, dlw.data(), sizeof(ArcDLW) * (size_t)A, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemcpy(h->olabel, g->olabel, 4 * (size_t)A, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemcpy(h->arc_src, src.data(), 4 * (size_t)A, hipMemcpyHostToDevice);
@@ -318,7 +313,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
 
     Work &w = d->w;
-    w.sinfo = g->sinfo; w.arc_lw = g->arc_lw; w.arc_dlw = g->arc_dlw;
+    w.sinfo = g->sinfo; w.arc_dlw = g->arc_dlw;
     w.olabel = g->olabel; w.arc_src = g->arc_src;
     w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
     w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;

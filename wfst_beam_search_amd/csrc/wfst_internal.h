@@ -39,14 +39,9 @@ struct alignas(32) StateInfo {
     int32_t pad0, pad1;
 };
 
-// Arc records, one contiguous run per state (the CSR order of the graph), so a
-// token's arcs share cache lines: the maximum pass reads {ilabel, weight}, the
-// admit pass and the closure {dest, ilabel, weight}. Final arcs carry
-// kFinalLabel.
-struct alignas(8) ArcLW {
-    uint32_t ilabel;
-    float weight;
-};
+// Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR
+// order of the graph), so the fields a pass reads for a token's arcs share
+// cache lines. Final arcs carry kFinalLabel.
 struct ArcDLW {
     int32_t dest;
     uint32_t ilabel;
@@ -106,7 +101,6 @@ struct LpDesc {
 struct Work {
     // graph (read-only)
     const StateInfo *sinfo;
-    const ArcLW *arc_lw;
     const ArcDLW *arc_dlw;
     const int32_t *olabel;
     const int32_t *arc_src;

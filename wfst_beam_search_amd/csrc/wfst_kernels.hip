@@ -392,8 +392,7 @@ __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab,
 // Loads unit u of lane v.L: lane l of the wavefront resolves slots
 // j0 + r*64 + l against register-held windows of 64 token offsets (start token
 // `cur`, moved forward), then issues every arc load of the unit before using
-// any: the maximum pass reads {ilabel, weight} records, the admit pass
-// {dest, ilabel, weight}. Tokens whose bound ub + maxlp <= skip are not
+// any. Tokens whose bound ub + maxlp <= skip are not
 // expanded (exact: no arc of theirs can end above skip).
 template <int MODE, typename LPT>
 __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
@@ -456,19 +455,13 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
         ud.tok[r] = tok[r];
         const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] + v.lpm > skip;
         if (go) ud.live |= 1u << r;
-        if (MODE == kModeMax) {
-            ArcLW a = {0u, 0.0f};
-            if (go) a = w.arc_lw[ud.arc[r]];
-            wt[r] = a.weight;
-            il[r] = a.ilabel;
-            ud.dst[r] = 0;
-        } else {
-            ArcDLW a = {0, 0u, 0.0f};
-            if (go) a = w.arc_dlw[ud.arc[r]];
-            wt[r] = a.weight;
-            il[r] = a.ilabel;
-            ud.dst[r] = a.dest;
-        }
+        // both passes read the same records: the admit pass then finds the
+        // lines the maximum pass loaded still in its XCD's L2 (same split)
+        ArcDLW a = {0, 0u, 0.0f};
+        if (go) a = w.arc_dlw[ud.arc[r]];
+        wt[r] = a.weight;
+        il[r] = a.ilabel;
+        ud.dst[r] = a.dest;
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
