@@ -37,10 +37,13 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     Per-unit figures (n tokens expanded, S candidate arcs, C admitted candidates,
     D distinct destinations, n' survivors = D without epsilon arcs, F lane-frames,
     E epsilon arcs, e*V log-prob row bytes):
-      max      12 n + 6 S + e V F       (token score + arc range, ilabel u16 + weight f32, one row per lane-frame)
-      expand   12 n + 6 S + 28 C + e V F   (+ per admitted: dest i32, u64 table atomic, 16-byte candidate record)
+      max      12 n + 6 S + 28 C + e V F   (the one slot pass: token score + arc range, ilabel u16 +
+                                         weight f32, one row per lane-frame; per admitted candidate
+                                         dest i32, u64 table atomic, 16-byte candidate record)
       finalize 24 C + 28 D              (candidate + table entry read; per winner: table clear 8 B,
                                          next-frontier token 12 B, winners-log entry 8 B)
+    Only the admitted candidates C count, not the larger list the slot pass writes
+    while the maximum is still being found.
       eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, candidates, changed tokens)
       path     12 n + 6 S + 52 C + 28 D + e V F (+ eps terms): the whole step, tokens and arcs counted once
     """
@@ -48,8 +51,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     E, De, Ne = st["eps_arcs"], st["eps_distinct"], st["eps_changed"]
     row = elem_bytes * vocab * F
     per = {
-        "max": 12 * n + 6 * S + row,
-        "expand": 12 * n + 6 * S + 28 * C + row,
+        "max": 12 * n + 6 * S + 28 * C + row,
         "finalize": 24 * C + 28 * D,
         "eps_expand": 16 * E,
         "eps_resolve": 28 * De,

@@ -205,21 +205,23 @@ int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, in
 int wfst_decoder_destroy(wfst_decoder_t d);
 
 /*
- * Counters of the last decode, summed over its lanes (n up to 13 values):
+ * Counters of the last decode, summed over its lanes (n up to 14 values):
  *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
  *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
  *  frontier sizes), [4] epsilon arcs relaxed, [5] epsilon candidates admitted,
  *  [6] epsilon destinations claimed, [7] tokens appended or replaced by the
  *  closure, [8] winners-log entries written, [9] steps run (frame loop length),
  *  [10] largest frontier, [11] device bytes reserved by the decoder,
- *  [12] real (frame) steps run, summed over lanes.
+ *  [12] real (frame) steps run, summed over lanes, [13] candidates listed by
+ *  the slot passes (a superset of [1]: every candidate above the running
+ *  maximum minus the beam while the exact maximum was still being found).
  */
 int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 
 /*
  * Per-step records of lane `lane` in the last decode, 16 int64 each:
  *  {n, beam bits, max bits, arcs, admitted, distinct, eps arcs, eps admitted,
- *   eps distinct, eps new, eps replaced, eps passes, phase, 0, 0, 0}
+ *   eps distinct, eps new, eps replaced, eps passes, phase, listed, 0, 0}
  * record 0 describes the start frontier's closure (only the eps fields), record
  * t + 1 step t. phase: 0 real, 1 final, 2 redirect, 3 dead, -1 not run.
  * Writes min(steps_cap, lengths[lane] + 2) records; returns how many it wrote

@@ -30,10 +30,10 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
            "eps_apply", "backtrack")
 STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
-               "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "_13", "_14", "_15")
+               "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "listed", "_14", "_15")
 STAT_FIELDS = ("arcs", "admitted", "distinct", "tokens", "eps_arcs", "eps_admitted",
                "eps_distinct", "eps_changed", "log_entries", "steps", "max_frontier", "bytes_reserved",
-               "lane_frames")
+               "lane_frames", "listed")
 
 
 class WfstError(RuntimeError):

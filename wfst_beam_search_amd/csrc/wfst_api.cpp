@@ -152,7 +152,10 @@ static int validate_graph(const wfst_graph_desc *g, std::vector<StateInfo> *info
         si.emit_b = a;
         float emax = -INFINITY, fmax = -INFINITY;
         while (a < e && g->ilabel[a] >= 0 && g->ilabel[a] < V && g->ilabel[a] != eps) {
-            emax = std::max(emax, g->weight[a]);
+            if (g->weight[a] > emax) {
+                emax = g->weight[a];
+                si.emit_il = (uint32_t)g->ilabel[a];
+            }
             ++a;
         }
         si.fin_b = a;
@@ -392,7 +395,6 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
     if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKExpand, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
@@ -517,7 +519,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
 {
     if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
     std::lock_guard<std::mutex> lock(d->mu);
-    int64_t v[13] = {0};
+    int64_t v[14] = {0};
     if (d->last_B > 0) {
         std::vector<uint32_t> rec;
         int rc = fetch_records(d, &rec);
@@ -531,6 +533,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
                 v[7] += (int64_t)x[kRecEpsNew] + x[kRecEpsReplaced];
                 v[10] = std::max<int64_t>(v[10], x[kRecN]);
                 if (r >= 1 && x[kRecPhase] == (uint32_t)kPhReal && x[kRecN] > 0) v[12] += 1;
+                v[13] += x[kRecListed];
             }
         }
         std::vector<LaneCtl> ctl((size_t)d->cfg.max_lanes);
@@ -539,7 +542,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
     }
     v[9] = d->last_steps;
     v[11] = (int64_t)(d->bytes + d->g->bytes);
-    for (int32_t i = 0; i < n && i < 13; ++i) out[i] = v[i];
+    for (int32_t i = 0; i < n && i < 14; ++i) out[i] = v[i];
     return WFST_OK;
 }
 

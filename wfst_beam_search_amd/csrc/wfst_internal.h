@@ -27,7 +27,8 @@ enum : uint32_t {
 // Per-step record fields (u32).
 enum : int {
     kRecN = 0, kRecBeam, kRecMax, kRecArcs, kRecAdmitted, kRecDistinct, kRecEpsArcs,
-    kRecEpsAdmitted, kRecEpsDistinct, kRecEpsNew, kRecEpsReplaced, kRecEpsPasses, kRecPhase
+    kRecEpsAdmitted, kRecEpsDistinct, kRecEpsNew, kRecEpsReplaced, kRecEpsPasses, kRecPhase,
+    kRecListed    // candidates the slot pass listed (its superset of the admitted ones)
 };
 
 // Per-state arc ranges and upper-bound weights, one 32-byte line per state:
@@ -36,7 +37,8 @@ struct alignas(32) StateInfo {
     int32_t eps_b, emit_b, fin_b, end;
     float emit_maxw;   // largest weight over the emitting arcs (-inf if none)
     float fin_maxw;    // largest weight over the final arcs (-inf if none)
-    int32_t pad0, pad1;
+    uint32_t emit_il;  // ilabel of the first emitting arc of weight emit_maxw (any if none)
+    int32_t pad1;
 };
 
 // Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR
@@ -69,7 +71,7 @@ struct alignas(128) LaneCtl {
     float beam[2];             // b_t by step parity (beam[1] = search beam before step 0)
     uint32_t maxkey[2];        // ordered exact maximum M_t by step parity
     float cutoff;              // cutoff of the latest real step (closure passes use it)
-    uint32_t nclaims;          // admitted candidates of the main expand of the current step
+    uint32_t nclaims[2];       // candidate-list length of the slot pass by step parity
     uint32_t log_cursor;       // winners-log entries used in this lane's region
     int32_t final_entry;       // winners-log entry of the result (-1 none)
     unsigned long long final_key;  // best final candidate key of the final step
@@ -84,7 +86,8 @@ struct alignas(128) LaneCtl {
     uint32_t pad_a, pad_b;
     uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
                                //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
-    uint32_t pad[3];
+    uint32_t lbkey[2];         // ordered lower bound of M_t by step parity: the best candidate
+                               //   through each token's largest-weight arc (posted by finalize)
 };
 
 // Device-resident description of the caller's log_prob tensor, rewritten before

@@ -281,8 +281,11 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
     c.beam[1] = w.beam;
     c.maxkey[0] = kOrdNegInf;
     c.maxkey[1] = kOrdNegInf;
+    c.lbkey[0] = kOrdNegInf;
+    c.lbkey[1] = kOrdNegInf;
     c.cutoff = 0.0f - w.beam;
-    c.nclaims = 0u;
+    c.nclaims[0] = 0u;
+    c.nclaims[1] = 0u;
     c.log_cursor = 0u;
     c.final_entry = -1;
     c.final_key = 0ull;
@@ -339,8 +342,6 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(Work w)
 
 // ------------------------------------------------- slot walk (max / expand)
 
-enum { kModeMax = 0, kModeExpand = 1 };
-
 // A wavefront walks its run of the flattened slot space in units of kUnit slots:
 // lane l owns slots j0 + r*64 + l for r < kR, so one window of token offsets and
 // one round of independent arc loads serve kR strips (memory-level parallelism
@@ -394,7 +395,7 @@ __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab,
 // `cur`, moved forward), then issues every arc load of the unit before using
 // any. Tokens whose bound ub + maxlp <= skip are not
 // expanded (exact: no arc of theirs can end above skip).
-template <int MODE, typename LPT>
+template <typename LPT>
 __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
                                           float skip, UnitData &ud)
 {
@@ -480,29 +481,25 @@ __device__ __forceinline__ float unit_max(const UnitData &ud)
     return wave_max(m);
 }
 
-// Admits a unit's candidates (end > cut, strict) and recombines them: on a real
-// step with one posted u64 atomicMax per candidate on the lane's direct-mapped
-// table, every admitted candidate going to the wavefront's LDS buffer; on the
-// final step through one wavefront-reduced atomicMax of the lane's final key.
+// Admits a unit's candidates into the step's superset (end > cut, strict, with
+// cut = running max - b <= M - b, so every candidate the exact cutoff will admit
+// is in) and recombines them: on a real step with one posted u64 atomicMax per
+// candidate on the lane's direct-mapped table, on the final step with one
+// wavefront-reduced atomicMax of the lane's final key. Every candidate of the
+// superset goes to the wavefront's LDS buffer, then to the lane's list.
 __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, const UnitData &ud,
-                                           ClaimBuf *cb, uint32_t &cb_n, uint32_t &admitted)
+                                           uint32_t *counter, ClaimBuf *cb, uint32_t &cb_n)
 {
     LaneCtl &c = w.ctl[L];
     const int lane = wlane();
     bool adm[kR];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        adm[r] = ((ud.live >> r) & 1u) && ud.e[r] > cut;
-        admitted += adm[r] ? 1u : 0u;
-    }
+    for (int r = 0; r < kR; ++r) adm[r] = ((ud.live >> r) & 1u) && ud.e[r] > cut;
     if (ph == kPhReal) {
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
 #pragma unroll
         for (int r = 0; r < kR; ++r)
             if (adm[r]) atomicMax(&tbl[ud.dst[r]], cand_key(ud.e[r], (int32_t)ud.arc[r]));
-#pragma unroll
-        for (int r = 0; r < kR; ++r)
-            push_claims(w, L, &c.nclaims, *cb, cb_n, adm[r], ud.dst[r], (int32_t)ud.arc[r], ud.tok[r], ud.e[r]);
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -519,6 +516,9 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
         }
         if (lane == 0 && fkey) atomicMax(&c.final_key, fkey);
     }
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+        push_claims(w, L, counter, *cb, cb_n, adm[r], ud.dst[r], (int32_t)ud.arc[r], ud.tok[r], ud.e[r]);
 }
 
 // XCD-aware block order: workgroups are dealt to the 8 XCDs round-robin
@@ -544,16 +544,16 @@ __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t
     *s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
 }
 
-// Units [s, s_end) of the flattened slot space: exact max (MODE max, with the
-// bound skip against the running max) or admit + recombine (MODE expand, with
-// the bound skip against the cutoff).
-template <int MODE, typename LPT>
+// Units [s, s_end) of the flattened slot space, in one pass: the exact maximum
+// (running max seeded with the lower bound the compaction posted, tokens whose
+// bound ub + maxlp <= running max - b skipped: exact for both results) and the
+// superset admission against running max - b.
+template <typename LPT>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            uint32_t s, uint32_t s_end, ClaimBuf *cbuf)
 {
     const int p = t & 1;
     const int nl = w.max_lanes;
-    const int lane = wlane();
     uint32_t cb_n = 0;
     while (s < s_end) {
         const int L = find_lane(tab.base, nl, s);
@@ -562,42 +562,46 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
         LaneCtl &c = w.ctl[L];
         uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
         if (cur >= v.n) cur = 0;
-        float run = -__builtin_inff(), posted = -__builtin_inff();
-        if (MODE == kModeMax) {
-            posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            run = posted;
-        }
-        const float cut = tab.f1[L];
-        uint32_t admitted = 0;
+        const float posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float run = fmaxf(posted, ord2f(tab.fb[L]));
+        const float b = tab.f1[L];
         for (; s < seg_end; ++s) {
             UnitData ud;
-            load_unit<MODE, LPT>(w, v, s - tab.base[L], cur, MODE == kModeMax ? run : cut, ud);
-            if (MODE == kModeMax) run = fmaxf(run, unit_max(ud));
-            else admit_unit(w, L, v.ph, cut, ud, cbuf, cb_n, admitted);
+            load_unit<LPT>(w, v, s - tab.base[L], cur, run - b, ud);
+            run = fmaxf(run, unit_max(ud));
+            admit_unit(w, L, v.ph, run - b, ud, &c.nclaims[p], cbuf, cb_n);
         }
-        if (MODE == kModeExpand) {
-            if (cb_n) flush_claims(w, L, &c.nclaims, *cbuf, cb_n);
-            cb_n = 0;
-            const uint32_t a = wave_sum(admitted);
-            // real steps: the finalize kernel records the list length instead
-            if (lane == 0 && a && v.ph != kPhReal) atomicAdd(step_rec(w, L, t) + kRecAdmitted, a);
-        } else if (run > posted && lane == 0) {
-            atomicMax(&c.maxkey[p], f2ord(run));
-        }
+        if (cb_n) flush_claims(w, L, &c.nclaims[p], *cbuf, cb_n);
+        cb_n = 0;
+        if (run > posted && wlane() == 0) atomicMax(&c.maxkey[p], f2ord(run));
     }
 }
 
-template <int MODE, typename LPT>
+template <typename LPT>
 __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            ClaimBuf *cbuf)
 {
     uint32_t s, s_end;
     wave_share(tab.base[w.max_lanes], &s, &s_end);
-    walk_range<MODE, LPT>(w, tab, t, d, s, s_end, cbuf);
+    walk_range<LPT>(w, tab, t, d, s, s_end, cbuf);
 }
 
-// Per-lane table for the two slot passes of step t.
-template <int MODE>
+// Dynamic beam b_t of a lane (page section 3), every operation one fp32
+// rounding; n = frontier size entering the step. Every workgroup of the slot
+// pass computes it (the same value workgroup 0 stores).
+__device__ __forceinline__ float step_beam(const Work &w, const LaneCtl &c, int t, int ph, uint32_t n)
+{
+    if (ph == kPhFinal) return 1e10f;
+    int mina = w.min_active;
+    if (c.T - t <= 5 && w.max_active / 2 > mina) mina = w.max_active / 2;
+    const float bp = c.beam[(t & 1) ^ 1];
+    if ((long long)n > (long long)w.max_active) return __fmul_rn(fminf(bp, w.beam), 0.8f);
+    if ((long long)n < (long long)mina) return __fmul_rn(fmaxf(bp, w.beam), 1.25f);
+    return __fadd_rn(__fmul_rn(0.8f, bp), __fmul_rn(0.2f, w.beam));
+}
+
+// Per-lane table of the slot pass of step t: units, row maximum, beam, and the
+// compaction's lower bound of the step's maximum.
 __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t)
 {
     if (threadIdx.x >= kWave) return;
@@ -610,16 +614,21 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         const unsigned long long cn = c.cnt[p];
         const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
         if (ph != kPhNone && (n > w.frontier_cap || arcs > w.strip_cap * (uint32_t)kWave)) ph = kPhNone;
-        float lpm = 0.0f, f1 = 0.0f;
+        float lpm = 0.0f, b = 0.0f;
+        uint32_t lb = kOrdNegInf;
         if (ph == kPhReal) lpm = w.lpmax[(size_t)L * w.max_frames + t];
-        if (MODE == kModeExpand && ph != kPhNone) f1 = ord2f(c.maxkey[p]) - c.beam[p];
-        if (ph != kPhNone && n > 0u && arcs > 0u) units = (arcs + kUnit - 1) / kUnit;
+        if (ph != kPhNone && n > 0u && arcs > 0u) {
+            units = (arcs + kUnit - 1) / kUnit;
+            b = step_beam(w, c, t, ph, n);
+            if (ph == kPhReal) lb = c.lbkey[p];
+        }
         tab.n[L] = n;
         tab.arcs[L] = arcs;
         tab.ph[L] = ph;
         tab.T[L] = c.T;
         tab.f0[L] = lpm;
-        tab.f1[L] = f1;
+        tab.f1[L] = b;
+        tab.fb[L] = lb;
     }
     tab_publish(tab, w.max_lanes, units);
 }
@@ -643,29 +652,15 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
-    // dynamic beam (page section 3), every operation one fp32 rounding
-    float b;
-    if (ph == kPhFinal) {
-        b = 1e10f;
-    } else {
-        int mina = w.min_active;
-        if (c.T - t <= 5 && w.max_active / 2 > mina) mina = w.max_active / 2;
-        const float bp = c.beam[p ^ 1];
-        if ((long long)n > (long long)w.max_active) {
-            b = __fmul_rn(fminf(bp, w.beam), 0.8f);
-        } else if ((long long)n < (long long)mina) {
-            b = __fmul_rn(fmaxf(bp, w.beam), 1.25f);
-        } else {
-            b = __fadd_rn(__fmul_rn(0.8f, bp), __fmul_rn(0.2f, w.beam));
-        }
-    }
+    const float b = step_beam(w, c, t, ph, n);
     c.beam[p] = b;
     rec[kRecBeam] = __float_as_uint(b);
     rec[kRecPhase] = ph;
     c.phase_final = ph;
-    c.nclaims = 0u;
+    c.nclaims[p ^ 1] = 0u;   // this step's list counter was cleared one step ago
     c.cnt[p ^ 1] = 0ull;
     c.maxkey[p ^ 1] = kOrdNegInf;
+    c.lbkey[p ^ 1] = kOrdNegInf;
     if (arcs == 0u) {
         if (ph == kPhReal) {
             c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead;
@@ -693,57 +688,34 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
 }
 
 // Start of a step: the lane table of the step's slot space, then workgroup 0
-// runs the per-lane bookkeeping (beam update, retirements, resets).
+// runs the per-lane bookkeeping (beam update, retirements, resets of the other
+// parity's counters: the slot pass of this step is running beside it).
 __device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
 {
-    slot_prologue<kModeMax>(w, tab, t);
+    slot_prologue(w, tab, t);
     __syncthreads();
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
 }
 
-// After the exact maxima are known: every workgroup refreshes the cutoffs in its
-// table (the slot space is unchanged); workgroup 0 records them.
-__device__ __forceinline__ void step_cutoffs(const Work &w, int t, LaneTab &tab)
-{
-    __syncthreads();
-    if (threadIdx.x < (unsigned)w.max_lanes) {
-        const int L = (int)threadIdx.x;
-        const int p = t & 1;
-        // lanes without candidates (dead, redirected, retired) keep no maximum
-        if (tab.ph[L] != kPhNone && tab.n[L] > 0u && tab.arcs[L] > 0u) {
-            LaneCtl &c = w.ctl[L];
-            const float cut = ord2f(c.maxkey[p]) - c.beam[p];
-            tab.f1[L] = cut;
-            if (blockIdx.x == 0) {
-                step_rec(w, L, t)[kRecMax] = __float_as_uint(ord2f(c.maxkey[p]));
-                if (tab.ph[L] == kPhReal) c.cutoff = cut;
-            }
-        }
-    }
-    __syncthreads();
-}
-
+// The slot pass of step t: exact maximum and superset admission in one walk.
 template <typename LPT>
 __global__ __launch_bounds__(kBlock) void k_max(Work w, int t)
 {
     __shared__ LaneTab tab;
+    __shared__ ClaimBuf cbufs[kBlock / kWave];
     step_open(w, t, tab);
     const LpDesc d = *w.lp;
-    walk_slots<kModeMax, LPT>(w, tab, t, d, nullptr);
-}
-
-template <typename LPT>
-__global__ __launch_bounds__(kBlock) void k_expand(Work w, int t)
-{
-    __shared__ LaneTab tab;
-    slot_prologue<kModeMax>(w, tab, t);
-    step_cutoffs(w, t, tab);
-    __shared__ ClaimBuf cbufs[kBlock / kWave];
-    const LpDesc d = *w.lp;
-    walk_slots<kModeExpand, LPT>(w, tab, t, d, &cbufs[threadIdx.x / kWave]);
+    walk_slots<LPT>(w, tab, t, d, &cbufs[threadIdx.x / kWave]);
 }
 
 // -------------------------------------------------------------- k_finalize
+
+// Posts a wavefront's lower bound of lane L's next-step maximum (L < 0: none).
+__device__ __forceinline__ void post_bound(const Work &w, int L, int np, float v)
+{
+    const float m = wave_max(v);
+    if (L >= 0 && wlane() == 0 && m > -__builtin_inff()) atomicMax(&w.ctl[L].lbkey[np], f2ord(m));
+}
 
 // Result of the final step: the winners-log entry of the best final arc (key
 // fk, source token stok of frontier parity p). Written by exactly one thread.
@@ -770,6 +742,7 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
 
 __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 {
+    const LpDesc lpd = *w.lp;
     const int p = t & 1, np = p ^ 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -777,31 +750,18 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
             const int ph = lane_phase(c, t);
-            const uint32_t nc = c.nclaims;
+            const uint32_t nc = c.nclaims[p];
             // candidates past claims_cap were never written: the lane cannot be
             // compacted (token and log capacity are checked per wavefront)
             const bool fits = nc <= w.claims_cap;
-            if (ph == kPhReal && fits) units = (nc + kWave - 1) / kWave;
+            if ((ph == kPhReal || ph == kPhFinal) && fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = c.log_cursor;          // winners-log base of this compaction
             tab.ph[L] = ph;
             tab.T[L] = c.T;
             tab.f0[L] = fits ? 1.0f : 0.0f;
-            tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;
+            tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;   // the exact cutoff
             tab.fb[L] = c.front_base[p];
-            if (ph == kPhFinal && !w.has_eps) {
-                // without epsilon arcs no state -> token map is kept: the final
-                // winner's source token is found by scanning the frontier for the
-                // source state of the winning arc (tokens are unique per state)
-                const unsigned long long fk = c.final_key;
-                const uint32_t n = (uint32_t)c.cnt[p];
-                tab.n[L] = 0u;
-                if (fk != 0ull && n <= w.frontier_cap) {
-                    units = (n + kWave - 1) / kWave;
-                    tab.n[L] = n;
-                    tab.arcs[L] = (uint32_t)w.arc_src[(int32_t)(0xFFFFFFFFu - (uint32_t)fk)];
-                }
-            }
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -811,9 +771,14 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
         const int ph = tab.ph[L];
+        const unsigned long long cn = c.cnt[p];
+        if ((ph == kPhReal || ph == kPhFinal) && (uint32_t)cn > 0u && (uint32_t)(cn >> 32) > 0u) {
+            // lanes with candidates: the exact maximum and the cutoff of the step
+            step_rec(w, L, t)[kRecMax] = __float_as_uint(ord2f(c.maxkey[p]));
+            step_rec(w, L, t)[kRecListed] = tab.n[L];
+            if (ph == kPhReal) c.cutoff = tab.f1[L];
+        }
         if (ph == kPhReal) {
-            const uint32_t nc = tab.n[L];
-            step_rec(w, L, t)[kRecAdmitted] = nc;
             if (tab.f0[L] == 0.0f) {
                 // the candidate list overflowed: retire the lane before writing
                 // any token; its table entries stay set, so the table is cleared
@@ -825,13 +790,11 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             }
             c.nclaims_eps[1] = 0u;
         } else if (ph == kPhFinal) {
+            // the final key is the best of the superset: a result iff admitted
             const unsigned long long fk = c.final_key;
-            step_rec(w, L, t)[kRecDistinct] = fk ? 1u : 0u;
-            if (fk && w.has_eps) {
-                const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)fk);
-                const int32_t stok = w.pos[p][(size_t)L * w.num_states + w.arc_src[arc]];
-                final_entry(w, c, L, p, fk, stok);
-            }
+            const bool got = fk != 0ull && ord2f((uint32_t)(fk >> 32)) > tab.f1[L] && tab.f0[L] != 0.0f;
+            step_rec(w, L, t)[kRecDistinct] = got ? 1u : 0u;
+            if (tab.f0[L] == 0.0f) c.overflow |= kOvfClaims;
             c.status = kDone;
         }
     }
@@ -842,15 +805,10 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
     const uint32_t Q = w.frontier_cap;
     uint32_t u_beg, u_end;
     wave_share(total, &u_beg, &u_end);
+    int lb_lane = -1;
+    float lb_acc = -__builtin_inff();
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
-        if (tab.ph[L] == kPhFinal) {
-            // the frontier scan of the final step (graphs without epsilon arcs)
-            const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
-            if (i < tab.n[L] && (uint32_t)w.tok_state[p][(size_t)L * Q + i] == tab.arcs[L])
-                final_entry(w, w.ctl[L], L, p, w.ctl[L].final_key, (int32_t)i);
-            continue;
-        }
         const uint32_t nc = tab.n[L];
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const bool valid = i < nc;
@@ -860,10 +818,31 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         bool keep = false;
         int32_t dst = 0, arc = 0, esrc = -1, abeg = 0;
         uint32_t deg = 0;
-        float end = 0.0f, ub = 0.0f;
+        float end = 0.0f, ub = 0.0f, lbv = -__builtin_inff();
+        // the list is a superset: a candidate is admitted iff end > the exact
+        // cutoff; the one whose key is its destination's entry owns the entry
+        // (clears it) and becomes the token if admitted
+        Claim cl;
+        bool adm = false;
         if (valid) {
-            Claim cl;
-            keep = take_winner(w, L, i, cl) && __uint_as_float(cl.score) > cutoff;
+            cl = w.claims[(size_t)L * w.claims_cap + i];
+            adm = __uint_as_float(cl.score) > cutoff;
+        }
+        const unsigned long long am = __ballot(adm);
+        if (lane == 0 && am) atomicAdd(step_rec(w, L, t) + kRecAdmitted, (uint32_t)__popcll(am));
+        if (tab.ph[L] == kPhFinal) {
+            if (adm && cand_key(__uint_as_float(cl.score), cl.arc) == c.final_key)
+                final_entry(w, c, L, p, c.final_key, (int32_t)cl.tok);
+            continue;
+        }
+        if (valid && (uint32_t)cl.dest < (uint32_t)w.num_states) {
+            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
+            if (*ent == cand_key(__uint_as_float(cl.score), cl.arc)) {
+                *ent = 0ull;
+                keep = adm;
+            }
+        }
+        {
             if (keep) {
                 dst = cl.dest;
                 arc = cl.arc;
@@ -878,9 +857,27 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                     esrc = w.has_eps ? w.tok_entry[p][(size_t)L * Q + stok]
                          : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
                     class_of(si, next_final, end, &abeg, &deg, &ub);
+                    if (!next_final && deg > 0u) {
+                        // a candidate of the next step: through the state's
+                        // largest-weight arc, (score + weight) + lp as the
+                        // maximum pass adds it
+                        const long long off = (long long)L * lpd.stride_b + (long long)(t + 1) * lpd.stride_t +
+                                              (long long)si.emit_il;
+                        const float lpv = (w.lp_dtype == 1) ? __half2float(((const __half *)lpd.base)[off])
+                                                            : ((const float *)lpd.base)[off];
+                        lbv = (end + si.emit_maxw) + lpv;
+                    }
                 }
             }
         }
+        // lower bound of the next step's maximum (posted per lane after the
+        // loop, so its log-prob load overlaps the allocation below)
+        if (L != lb_lane) {
+            post_bound(w, lb_lane, np, lb_acc);
+            lb_lane = L;
+            lb_acc = -__builtin_inff();
+        }
+        lb_acc = fmaxf(lb_acc, lbv);
         const unsigned long long m = __ballot(keep);
         if (m == 0ull) continue;
         const uint32_t nkeep = (uint32_t)__popcll(m);
@@ -924,6 +921,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         }
         write_strips(w.strip_tok[np] + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
+    post_bound(w, lb_lane, np, lb_acc);
 }
 
 __global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
@@ -1328,10 +1326,6 @@ hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStrea
     case kKMax:
         if (f16) go(k_max<__half>, G, B, s, e0, e1, w, t);
         else go(k_max<float>, G, B, s, e0, e1, w, t);
-        break;
-    case kKExpand:
-        if (f16) go(k_expand<__half>, G, B, s, e0, e1, w, t);
-        else go(k_expand<float>, G, B, s, e0, e1, w, t);
         break;
     case kKFinalize: go(k_finalize, G, B, s, e0, e1, w, t); break;
     case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, w, t, k); break;
