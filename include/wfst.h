@@ -115,6 +115,13 @@ typedef struct wfst_graph_desc {
  *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
  *  slot_cap        candidate arcs (slots) per lane per step (0: 512 * max_active,
  *                  at least 2^16); at most 2^31.
+ *  plain_keys      0: on graphs with at most 2^25 arcs the recombination table's
+ *                  keys carry the round's epoch in the bits the arc ids leave
+ *                  free, so entries are never cleared one by one (the table is
+ *                  wiped at the start of a decode and whenever the epoch
+ *                  counter wraps: every 2^(32 - ceil(log2 num_arcs)) - 1
+ *                  rounds, at least 127); 1: plain keys, each entry cleared by
+ *                  its owner (always the case on larger graphs). Same results.
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -131,6 +138,7 @@ typedef struct wfst_decoder_config {
     int32_t grid_blocks;
     int64_t arena_entries;
     int64_t slot_cap;
+    int32_t plain_keys;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays

@@ -39,7 +39,8 @@ def _golden_cases():
     return out
 
 
-MODES = {"graph": dict(use_graphs=True), "eager": dict(use_graphs=False)}
+MODES = {"graph": dict(use_graphs=True), "eager": dict(use_graphs=False),
+         "plain": dict(use_graphs=True, plain_keys=True)}
 
 
 @pytest.mark.parametrize("name,g,lp,case,eps,ap", _golden_cases(), ids=lambda x: x if isinstance(x, str) else "")
@@ -89,7 +90,7 @@ def test_random_small_graphs(eps):
     for seed in range(150):
         g, lp, L, beam, ma, mi, ap, P = _random_case(seed + (1000 if eps else 0), eps)
         _say("random", eps, seed, lp.shape, beam, ma, mi, ap, P)
-        mode = ("graph", "eager")[seed % 2]
+        mode = ("graph", "eager", "plain")[seed % 3]
         r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, **MODES[mode])
         o = oracle_lanes(g, lp, L, beam, ma, mi, ap, P)
         compare_batch(r, steps, o)
@@ -129,7 +130,7 @@ def test_workload_parity(cid, workload_graphs):
     dg = wb.Graph(g)
     runs = {}
     try:
-        for mode in ("graph", "eager"):
+        for mode in ("graph", "eager") + (("plain",) if cid in (2, 4) else ()):
             runs[mode] = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
                                     dgraph=dg, **MODES[mode])
             _say("  gpu", mode, "done; stats", runs[mode][2])

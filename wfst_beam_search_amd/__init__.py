@@ -59,7 +59,8 @@ class _Config(ctypes.Structure):
                 ("lp_dtype", ctypes.c_int32), ("eps_iterations", ctypes.c_int32),
                 ("use_graphs", ctypes.c_int32), ("frontier_cap", ctypes.c_int32),
                 ("claims_cap", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
-                ("arena_entries", ctypes.c_int64), ("slot_cap", ctypes.c_int64)]
+                ("arena_entries", ctypes.c_int64), ("slot_cap", ctypes.c_int64),
+                ("plain_keys", ctypes.c_int32)]
 
 
 _lib = None
@@ -172,12 +173,13 @@ class Decoder:
                  allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
                  lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
-                 grid_blocks: int = 0, slot_cap: int = 0):
+                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False):
         lib = load_library()
         cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                       int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                       int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
-                      int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap))
+                      int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
+                      int(bool(plain_keys)))
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h

@@ -18,6 +18,9 @@ FLAGS = [
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # the kernels' few argument dwords (a Work pointer, step, pass) arrive in
+    # SGPRs with the dispatch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

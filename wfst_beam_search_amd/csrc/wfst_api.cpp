@@ -87,6 +87,7 @@ struct wfst_decoder_s {
     std::vector<void *> owned;
     size_t bytes = 0;
     LaneCtl *ctl = nullptr;
+    Work *d_work = nullptr;         // device copy of w: the kernels' one pointer argument
     LpDesc *d_desc = nullptr;
     int32_t *d_lengths = nullptr;
     void *h_in = nullptr;           // pinned: LpDesc + lengths
@@ -274,6 +275,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.frontier_cap < 0 || c.claims_cap < 0 || c.arena_entries < 0 || c.grid_blocks < 0 ||
         c.slot_cap < 0 || c.slot_cap > (1ll << 31))
         return fail(WFST_EINVAL, "capacities must be >= 0");
+    if (c.plain_keys != 0 && c.plain_keys != 1) return fail(WFST_EINVAL, "plain_keys must be 0 or 1");
     const int P = (g->eps_id >= 0) ? c.eps_iterations : 0;
 
     const uint64_t Q = c.frontier_cap ? (uint64_t)c.frontier_cap : std::min<uint64_t>(64ull * (uint64_t)c.max_active, 1ull << 28);
@@ -320,6 +322,14 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.olabel = g->olabel; w.arc_src = g->arc_src;
     w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
     w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
+    {
+        uint32_t ab = 1;
+        while (ab < 31 && (1ll << ab) < (long long)g->num_arcs) ++ab;
+        w.arc_bits = ab;
+        w.epochs = (ab <= kMaxEpochArcBits && !c.plain_keys) ? 1 : 0;
+        // more than 2^16 rounds between clears would gain nothing measurable
+        w.epoch_period = (uint32_t)std::min<uint64_t>((1ull << (32 - ab)) - 1, 65535);
+    }
     w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
     w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
     w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
@@ -331,6 +341,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     int r = WFST_OK;
     auto A = [&](auto **p, size_t n) { if (r == WFST_OK) r = dalloc(p, n, &d->owned, &d->bytes); };
     A(&d->ctl, L);
+    A(&d->d_work, 1);
     A(&d->d_desc, 1);
     A(&d->d_lengths, L);
     A(&w.lpmax, L * (size_t)c.max_frames);
@@ -350,6 +361,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths;
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
+    if (e == hipSuccess) e = hipMemcpy(d->d_work, &w, sizeof(Work), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
     for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
@@ -375,9 +387,19 @@ static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
         if (2 * d->ev_used + 1 >= d->ev.size()) return hipErrorInvalidValue;
         const size_t i = d->ev_used++;
         d->ev_kind[i] = id;
-        return launch_kernel(id, d->w, t, k, d->grid, s, d->ev[2 * i], d->ev[2 * i + 1]);
+        return launch_kernel(id, d->w, d->d_work, t, k, d->grid, s, d->ev[2 * i], d->ev[2 * i + 1]);
     }
-    return launch_kernel(id, d->w, t, k, d->grid, s);
+    return launch_kernel(id, d->w, d->d_work, t, k, d->grid, s);
+}
+
+// With epoch-tagged table keys the epoch of round (t, k) restarts at 1 every
+// epoch_period rounds: the whole table is cleared before such a round.
+static hipError_t wrap_clear(wfst_decoder_s *d, int t, int k, hipStream_t s)
+{
+    if (!d->w.epochs) return hipSuccess;
+    const long long q = (long long)(t + 1) * (1 + d->passes) + k;
+    if (q <= 0 || q % d->w.epoch_period != 0) return hipSuccess;
+    return launch(d, kKClear, t, 1, s);
 }
 
 // Queue one whole decode of `steps` frame-loop steps on stream s.
@@ -388,15 +410,18 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
     if ((e = launch(d, kKClear, 0, 0, s)) != hipSuccess) return e;
     if ((e = launch(d, kKInit, 0, 0, s)) != hipSuccess) return e;
     for (int k = 1; k <= d->passes; ++k) {
+        if ((e = wrap_clear(d, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
     }
     if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
+        if ((e = wrap_clear(d, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
         for (int k = 1; k <= d->passes; ++k) {
+            if ((e = wrap_clear(d, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
@@ -573,7 +598,8 @@ extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
     std::lock_guard<std::mutex> lock(d->mu);
     HIP_TRY(hipSetDevice(d->g->device));
     if (enable && d->ev.empty()) {
-        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(3 + 3 * d->passes);
+        const size_t rounds = (size_t)(d->cfg.max_frames + 2) * (size_t)(1 + d->passes);
+        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(3 + 3 * d->passes) + rounds / d->w.epoch_period;
         d->ev.resize(2 * n, nullptr);
         d->ev_kind.assign(n, -1);
         for (size_t i = 0; i < 2 * n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));

@@ -11,6 +11,7 @@ constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kBlock = 256;         // threads per workgroup of the frame-loop kernels
 constexpr int kMaxLanes = 64;       // one wavefront scans the per-lane table
 constexpr int kStepFields = 16;     // u32 fields of one per-step record
+constexpr uint32_t kMaxEpochArcBits = 25;  // epoch-tagged table keys need arc ids below 2^25
 constexpr uint16_t kFinalLabel = 0xFFFF;
 
 // Lane status.
@@ -109,6 +110,9 @@ struct Work {
     const int32_t *arc_src;
     int32_t num_states, num_arcs, start_state, vocab, super_final;
     int32_t has_eps;
+    int32_t epochs;           // table keys carry the round's epoch: entries are never cleared singly
+    uint32_t arc_bits;        // arc id bits of an epoch-tagged key (the epoch takes 32 - arc_bits)
+    uint32_t epoch_period;    // rounds between full clears of the table
     // search settings
     float beam;
     int32_t min_active, max_active, allow_partial, eps_iterations;
@@ -154,7 +158,9 @@ enum : int {
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.
 // With e0 / e1 given, the dispatch records the kernel's start and end in them.
-hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s,
+// Kernels receive `dw`, the device copy of `w` (a kernel argument of one pointer:
+// dispatch cost grows with argument size); `w` gives host-side launch shapes.
+hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, int grid, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).

@@ -55,6 +55,29 @@ __device__ __forceinline__ unsigned long long cand_key(float score, int32_t arc)
     return ((unsigned long long)f2ord(score) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)arc);
 }
 
+// Epoch of recombination round (t, k): step t's slot pass is k = 0, closure
+// pass k after it is k (t = -1: the start closure). 1..epoch_period; 0 marks an
+// empty entry. Kernels compute it once (the modulus is not a constant).
+__device__ __forceinline__ uint32_t round_epoch(const Work &w, int t, int k)
+{
+    const uint32_t q = (uint32_t)((t + 1) * (1 + w.eps_iterations) + k);
+    return 1u + q % w.epoch_period;
+}
+
+// Key of a candidate in the recombination table. With epochs (arc ids below
+// 2^a, a = arc_bits <= 25): epoch << (32 + a) | ordered score << a |
+// (2^a - 1 - arc), so every key of an earlier round is smaller than every key
+// of the current one: no entry needs clearing (the host wipes the table before
+// the epoch counter wraps); within a round the order is cand_key's: greater
+// score, then smaller arc id.
+__device__ __forceinline__ unsigned long long table_key(const Work &w, float score, int32_t arc, uint32_t ep)
+{
+    if (!w.epochs) return cand_key(score, arc);
+    const uint32_t a = w.arc_bits;
+    return ((unsigned long long)ep << (32 + a)) | ((unsigned long long)f2ord(score) << a) |
+           (unsigned long long)(((1u << a) - 1u) - (uint32_t)arc);
+}
+
 __device__ __forceinline__ int wlane() { return (int)(threadIdx.x & (kWave - 1)); }
 
 __device__ __forceinline__ unsigned long long mask_lt() { return (1ull << wlane()) - 1ull; }
@@ -233,40 +256,62 @@ __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *coun
 }
 
 // Reads candidate i of lane L's list and decides whether it is the winner of
-// its destination: its key is the table entry after the expand pass. The
-// winner clears the entry (a loser reading after that sees 0, never its key).
-__device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, Claim &cl)
+// its destination in round epoch ep: its key is the table entry after the
+// expand pass. Without epochs the winner clears the entry (a loser reading
+// after that sees 0, never its key).
+__device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, uint32_t ep, Claim &cl)
 {
     cl = w.claims[(size_t)L * w.claims_cap + i];
     if ((uint32_t)cl.dest >= (uint32_t)w.num_states) return false;
     unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
-    const bool win = *ent == cand_key(__uint_as_float(cl.score), cl.arc);
-    if (win) *ent = 0ull;
+    const bool win = *ent == table_key(w, __uint_as_float(cl.score), cl.arc, ep);
+    if (win && !w.epochs) *ent = 0ull;
     return win;
 }
 
 // ---------------------------------------------------------------- k_clear
-// Clears the per-step records and the recombination tables of lanes whose
-// claims list overflowed in an earlier decode (the targeted clear cannot see
-// those entries).
-__global__ __launch_bounds__(kBlock) void k_clear(Work w)
+// k = 0 (start of a decode): clears the per-step records and the recombination
+// tables — all of them with epoch-tagged keys, else those of lanes whose
+// candidate list overflowed in an earlier decode (the targeted clears cannot
+// see those entries). k = 1: clears every table (before the epoch counter
+// wraps).
+__global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, int k)
 {
-    const size_t nrec = (size_t)w.max_lanes * (size_t)(w.max_frames + 2) * kStepFields;
+    const Work &w = *wp;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nrec; i += stride) w.steps[i] = 0u;
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k == 0) {
+        const size_t nrec = (size_t)w.max_lanes * (size_t)(w.max_frames + 2) * kStepFields;
+        for (size_t i = tid; i < nrec; i += stride) w.steps[i] = 0u;
+    }
     const size_t ns = (size_t)w.num_states;
+    if (w.epochs) {
+        // non-temporal 16-byte stores over the whole [L][num_states] table
+        // (hipMalloc'd: 256-byte aligned), an odd last entry singly: the
+        // zeros bypass the caches instead of leaving them full of dirty lines
+        // that later kernels would have to write back
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        const size_t n = (size_t)w.max_lanes * ns;
+        v4u *t4 = (v4u *)w.best;
+        const v4u z = {0u, 0u, 0u, 0u};
+        for (size_t i = tid; i < n / 2; i += stride) __builtin_nontemporal_store(z, &t4[i]);
+        if (tid == 0 && (n & 1)) w.best[n - 1] = 0ull;
+        return;
+    }
+    if (k != 0) return;
     for (int L = 0; L < w.max_lanes; ++L) {
         if (!w.ctl[L].dirty) continue;
         unsigned long long *tbl = w.best + (size_t)L * ns;
-        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns; i += stride) tbl[i] = 0ull;
+        for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
     }
 }
 
 // ----------------------------------------------------------------- k_init
 // Lane control blocks and the start token (page section 2: InitKernel resets all
 // state, so a decode is idempotent).
-__global__ __launch_bounds__(kWave) void k_init(Work w)
+__global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
 {
+    const Work &w = *wp;
     const int L = (int)threadIdx.x;
     if (L >= w.max_lanes) return;
     const LpDesc d = *w.lp;
@@ -323,8 +368,9 @@ __global__ __launch_bounds__(kWave) void k_init(Work w)
 // ---------------------------------------------------------------- k_lpmax
 // Max log-prob of every (lane, frame) row, for the upper-bound skip.
 template <typename LPT>
-__global__ __launch_bounds__(kBlock) void k_lpmax(Work w)
+__global__ __launch_bounds__(kBlock) void k_lpmax(const Work *__restrict__ wp)
 {
+    const Work &w = *wp;
     const LpDesc d = *w.lp;
     const int wpb = kBlock / kWave;
     const long long rows = (long long)d.B * w.max_frames;
@@ -487,8 +533,8 @@ __device__ __forceinline__ float unit_max(const UnitData &ud)
 // candidate on the lane's direct-mapped table, on the final step with one
 // wavefront-reduced atomicMax of the lane's final key. Every candidate of the
 // superset goes to the wavefront's LDS buffer, then to the lane's list.
-__device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, const UnitData &ud,
-                                           uint32_t *counter, ClaimBuf *cb, uint32_t &cb_n)
+__device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, uint32_t ep,
+                                           const UnitData &ud, uint32_t *counter, ClaimBuf *cb, uint32_t &cb_n)
 {
     LaneCtl &c = w.ctl[L];
     const int lane = wlane();
@@ -499,7 +545,7 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
 #pragma unroll
         for (int r = 0; r < kR; ++r)
-            if (adm[r]) atomicMax(&tbl[ud.dst[r]], cand_key(ud.e[r], (int32_t)ud.arc[r]));
+            if (adm[r]) atomicMax(&tbl[ud.dst[r]], table_key(w, ud.e[r], (int32_t)ud.arc[r], ep));
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -554,6 +600,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
 {
     const int p = t & 1;
     const int nl = w.max_lanes;
+    const uint32_t ep = round_epoch(w, t, 0);
     uint32_t cb_n = 0;
     while (s < s_end) {
         const int L = find_lane(tab.base, nl, s);
@@ -569,7 +616,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
             UnitData ud;
             load_unit<LPT>(w, v, s - tab.base[L], cur, run - b, ud);
             run = fmaxf(run, unit_max(ud));
-            admit_unit(w, L, v.ph, run - b, ud, &c.nclaims[p], cbuf, cb_n);
+            admit_unit(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
         }
         if (cb_n) flush_claims(w, L, &c.nclaims[p], *cbuf, cb_n);
         cb_n = 0;
@@ -699,8 +746,9 @@ __device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
 
 // The slot pass of step t: exact maximum and superset admission in one walk.
 template <typename LPT>
-__global__ __launch_bounds__(kBlock) void k_max(Work w, int t)
+__global__ __launch_bounds__(kBlock) void k_max(const Work *__restrict__ wp, int t)
 {
+    const Work &w = *wp;
     __shared__ LaneTab tab;
     __shared__ ClaimBuf cbufs[kBlock / kWave];
     step_open(w, t, tab);
@@ -742,6 +790,7 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
 
 __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 {
+    const uint32_t ep = round_epoch(w, t, 0);
     const LpDesc lpd = *w.lp;
     const int p = t & 1, np = p ^ 1;
     if (threadIdx.x < kWave) {
@@ -835,10 +884,12 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                 final_entry(w, c, L, p, c.final_key, (int32_t)cl.tok);
             continue;
         }
-        if (valid && (uint32_t)cl.dest < (uint32_t)w.num_states) {
+        // with epochs only admitted candidates need the table (stale entries of
+        // earlier rounds always lose); without, every owner clears its entry
+        if (valid && (adm || !w.epochs) && (uint32_t)cl.dest < (uint32_t)w.num_states) {
             unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
-            if (*ent == cand_key(__uint_as_float(cl.score), cl.arc)) {
-                *ent = 0ull;
+            if (*ent == table_key(w, __uint_as_float(cl.score), cl.arc, ep)) {
+                if (!w.epochs) *ent = 0ull;
                 keep = adm;
             }
         }
@@ -924,8 +975,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
     post_bound(w, lb_lane, np, lb_acc);
 }
 
-__global__ __launch_bounds__(kBlock) void k_finalize(Work w, int t)
+__global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp, int t)
 {
+    const Work &w = *wp;
     __shared__ LaneTab tab;
     ph_finalize(w, t, tab);
 }
@@ -946,6 +998,7 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
 
 __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
+    const uint32_t ep = round_epoch(w, t, k);
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -1023,7 +1076,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 adm = e > cutoff;
                 if (adm) {
                     ++n_adm;
-                    atomicMax(&tbl[ar.dest], cand_key(e, a));
+                    atomicMax(&tbl[ar.dest], table_key(w, e, a, ep));
                 }
             }
             push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, stk, e);
@@ -1038,8 +1091,9 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
+__global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ wp, int t, int k)
 {
+    const Work &w = *wp;
     __shared__ LaneTab tab;
     __shared__ ClaimBuf cbufs[kBlock / kWave];
     ph_eps_expand(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
@@ -1048,6 +1102,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(Work w, int t, int k)
 // Decides, per claimed destination, append / replace / nothing (reads only).
 __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, LaneTab &tab)
 {
+    const uint32_t ep = round_epoch(w, t, k);
     const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
@@ -1083,7 +1138,7 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
         const bool valid = i < tab.n[L];
         Claim cl;
-        const bool win = valid && take_winner(w, L, i, cl);
+        const bool win = valid && take_winner(w, L, i, ep, cl);
         const unsigned long long wm = __ballot(win);
         if (wm && wlane() == __ffsll((long long)__ballot(valid)) - 1)
             atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
@@ -1112,8 +1167,9 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_eps_resolve(Work w, int t, int k)
+__global__ __launch_bounds__(kBlock) void k_eps_resolve(const Work *__restrict__ wp, int t, int k)
 {
+    const Work &w = *wp;
     __shared__ LaneTab tab;
     ph_eps_resolve(w, t, k, tab);
 }
@@ -1234,8 +1290,9 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
+__global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ wp, int t, int k)
 {
+    const Work &w = *wp;
     __shared__ LaneTab tab;
     ph_eps_apply(w, t, k, tab);
 }
@@ -1244,8 +1301,9 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(Work w, int t, int k)
 // One wavefront per lane: lane 0 walks the winners chain from the result entry
 // (newest arc first), then the wavefront reverses it in place and gathers the
 // word ids (page section 7).
-__global__ __launch_bounds__(kWave) void k_backtrack(Work w)
+__global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp)
 {
+    const Work &w = *wp;
     const int L = (int)blockIdx.x;
     const LpDesc d = *w.lp;
     if (L >= d.B) return;
@@ -1311,27 +1369,27 @@ static void go(void (*kern)(A...), dim3 g, dim3 b, hipStream_t s, hipEvent_t e0,
     else hipLaunchKernelGGL(kern, g, b, 0, s, args...);
 }
 
-hipError_t launch_kernel(int id, const Work &w, int t, int k, int grid, hipStream_t s, hipEvent_t e0,
-                         hipEvent_t e1)
+hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, int grid, hipStream_t s,
+                         hipEvent_t e0, hipEvent_t e1)
 {
     const bool f16 = w.lp_dtype == 1;
     const dim3 G(grid), B(kBlock);
     switch (id) {
-    case kKClear: go(k_clear, G, B, s, e0, e1, w); break;
-    case kKInit: go(k_init, dim3(1), dim3(kWave), s, e0, e1, w); break;
+    case kKClear: go(k_clear, G, B, s, e0, e1, dw, k); break;
+    case kKInit: go(k_init, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKLpmax:
-        if (f16) go(k_lpmax<__half>, G, B, s, e0, e1, w);
-        else go(k_lpmax<float>, G, B, s, e0, e1, w);
+        if (f16) go(k_lpmax<__half>, G, B, s, e0, e1, dw);
+        else go(k_lpmax<float>, G, B, s, e0, e1, dw);
         break;
     case kKMax:
-        if (f16) go(k_max<__half>, G, B, s, e0, e1, w, t);
-        else go(k_max<float>, G, B, s, e0, e1, w, t);
+        if (f16) go(k_max<__half>, G, B, s, e0, e1, dw, t);
+        else go(k_max<float>, G, B, s, e0, e1, dw, t);
         break;
-    case kKFinalize: go(k_finalize, G, B, s, e0, e1, w, t); break;
-    case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, w, t, k); break;
-    case kKEpsResolve: go(k_eps_resolve, G, B, s, e0, e1, w, t, k); break;
-    case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, w, t, k); break;
-    case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, w); break;
+    case kKFinalize: go(k_finalize, G, B, s, e0, e1, dw, t); break;
+    case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, dw, t, k); break;
+    case kKEpsResolve: go(k_eps_resolve, G, B, s, e0, e1, dw, t, k); break;
+    case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, dw, t, k); break;
+    case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
