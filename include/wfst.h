@@ -241,9 +241,9 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_CLEAR        0  /* per-decode clear of records and stale recombination tables */
 #define WFST_K_INIT         1  /* lane control blocks and start tokens                     */
 #define WFST_K_LPMAX        2  /* max log-prob per (lane, frame) row for the bound skip    */
-#define WFST_K_MAX          3  /* exact per-lane maximum of the step                       */
-#define WFST_K_EXPAND       4  /* admit + recombination                                    */
-#define WFST_K_FINALIZE     5  /* compaction into the next frontier, winners log           */
+#define WFST_K_MAX          3  /* slot pass: exact maximum, superset admit + recombination  */
+#define WFST_K_EXPAND       4  /* not launched (its work is part of WFST_K_MAX)            */
+#define WFST_K_FINALIZE     5  /* exact admit, compaction, winners log, next lower bound   */
 #define WFST_K_EPS_EXPAND   6  /* closure pass: relax epsilon arcs                         */
 #define WFST_K_EPS_RESOLVE  7  /* closure pass: append / replace decisions                 */
 #define WFST_K_EPS_APPLY    8  /* closure pass: apply them                                 */

@@ -8,21 +8,21 @@
 //    with a forward token cursor resolved by a 6-shuffle search over a
 //    register-held window of 64 token offsets (section 5.2/5.3 problem, wave64
 //    solution);
-//  * pass 1 (k_max) takes the exact per-lane maximum with the per-token upper
-//    bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds in IEEE fp32);
-//  * pass 2 (k_expand) admits end > M - b and recombines per destination in a
-//    direct-mapped per-lane table best[state] with one posted u64 atomicMax of
-//    (ordered score << 32 | ~arc) per candidate, so the greatest score wins
-//    and, among equal scores, the smallest arc id; every admitted candidate is
-//    appended to the lane's candidate list {dest, arc, source token, score};
-//  * pass 3 (k_finalize) keeps the candidate of each destination whose key is
-//    the table entry (the winner) and compacts the winners into the next
-//    frontier: one
-//    64-bit atomicAdd per wavefront allocates token positions and arc offsets
+//  * the slot pass (k_max) takes the exact per-lane maximum M with the
+//    per-token upper-bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds
+//    in IEEE fp32), its running maximum seeded with a lower bound the previous
+//    compaction posted; in the same walk it lists every candidate with
+//    end > running max - b, a superset of the admitted ones (end > M - b), and
+//    recombines them per destination in a direct-mapped per-lane table
+//    best[state] with one posted u64 atomicMax of (ordered score | ~arc), so
+//    the greatest score wins and, among equal scores, the smallest arc id;
+//  * the compaction (k_finalize), with M known, admits from the list, keeps
+//    the candidate of each destination whose key is the table entry (the
+//    winner) and compacts the winners into the next frontier: one 64-bit
+//    atomicAdd per wavefront allocates token positions and arc offsets
 //    together (tokens in the low half, arcs in the high half), which is the
-//    exclusive degree scan of the next step, done as the frontier is built; the
-//    winners-log entry {source entry, arc} is written and the table entry
-//    cleared;
+//    exclusive degree scan of the next step, done as the frontier is built;
+//    the winners-log entry {source entry, arc} is written;
 //  * epsilon closure passes (expand / resolve / apply) on TLG graphs.
 // All fp32 arithmetic is single operations in the order the page fixes; the
 // file is compiled with -ffp-contract=off.
@@ -194,8 +194,8 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
     }
 }
 
-// Per-wavefront LDS buffer of the admitted candidates of the expand passes (a
-// unit admits at most kUnit of them).
+// Per-wavefront LDS buffer of the listed candidates of the slot pass and the
+// closure's expand passes (a unit lists at most kUnit of them).
 constexpr uint32_t kClaimBuf = 256;
 
 struct ClaimBuf {
@@ -257,8 +257,8 @@ __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *coun
 
 // Reads candidate i of lane L's list and decides whether it is the winner of
 // its destination in round epoch ep: its key is the table entry after the
-// expand pass. Without epochs the winner clears the entry (a loser reading
-// after that sees 0, never its key).
+// closure's expand pass. Without epochs the winner clears the entry (a loser
+// reading after that sees 0, never its key).
 __device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, uint32_t ep, Claim &cl)
 {
     cl = w.claims[(size_t)L * w.claims_cap + i];
@@ -399,7 +399,7 @@ constexpr uint32_t kUnit = kWave * kR;
 struct UnitData {
     float e[kR];          // end score (valid where bit r of `live` is set)
     uint32_t arc[kR];
-    int32_t dst[kR];      // destination (admit pass only)
+    int32_t dst[kR];      // destination
     uint32_t tok[kR];     // source token
     uint32_t live;        // bit r: slot r is a candidate whose arc was loaded
 };
@@ -502,8 +502,7 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
         ud.tok[r] = tok[r];
         const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] + v.lpm > skip;
         if (go) ud.live |= 1u << r;
-        // both passes read the same records: the admit pass then finds the
-        // lines the maximum pass loaded still in its XCD's L2 (same split)
+        // {dest, ilabel, weight} in one 12-byte record
         ArcDLW a = {0, 0u, 0.0f};
         if (go) a = w.arc_dlw[ud.arc[r]];
         wt[r] = a.weight;
