@@ -151,14 +151,19 @@ static int validate_graph(const wfst_graph_desc *g, std::vector<StateInfo> *info
         if (eps >= 0)
             while (a < e && g->ilabel[a] == eps) ++a;
         si.emit_b = a;
-        float emax = -INFINITY, fmax = -INFINITY;
+        float emax = -INFINITY, fmax = -INFINITY, e2 = -INFINITY;
+        uint32_t il1 = 0, il2 = 0xFFFFu;
+        int32_t a1 = -1;
         while (a < e && g->ilabel[a] >= 0 && g->ilabel[a] < V && g->ilabel[a] != eps) {
-            if (g->weight[a] > emax) {
-                emax = g->weight[a];
-                si.emit_il = (uint32_t)g->ilabel[a];
-            }
+            if (a1 < 0 || g->weight[a] > emax) { emax = g->weight[a]; il1 = (uint32_t)g->ilabel[a]; a1 = a; }
             ++a;
         }
+        // the two largest-weight emitting arcs (their labels and weights feed the
+        // lower bound of the next step's maximum)
+        for (int32_t b = si.emit_b; b < a; ++b)
+            if (b != a1 && (il2 == 0xFFFFu || g->weight[b] > e2)) { e2 = g->weight[b]; il2 = (uint32_t)g->ilabel[b]; }
+        si.emit_il = (il1 & 0xFFFFu) | (il2 << 16);
+        si.emit_w2 = e2;
         si.fin_b = a;
         while (a < e && g->ilabel[a] == -1) {
             fmax = std::max(fmax, g->weight[a]);

@@ -38,8 +38,9 @@ struct alignas(32) StateInfo {
     int32_t eps_b, emit_b, fin_b, end;
     float emit_maxw;   // largest weight over the emitting arcs (-inf if none)
     float fin_maxw;    // largest weight over the final arcs (-inf if none)
-    uint32_t emit_il;  // ilabel of the first emitting arc of weight emit_maxw (any if none)
-    int32_t pad1;
+    uint32_t emit_il;  // ilabels of two emitting arcs: bits 0-15 the first of weight emit_maxw,
+                       //   bits 16-31 another of the next largest weight (0xFFFF: none)
+    float emit_w2;     // weight of that second arc (-inf if none)
 };
 
 // Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR

@@ -908,14 +908,24 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                          : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
                     class_of(si, next_final, end, &abeg, &deg, &ub);
                     if (!next_final && deg > 0u) {
-                        // a candidate of the next step: through the state's
-                        // largest-weight arc, (score + weight) + lp as the
-                        // maximum pass adds it
-                        const long long off = (long long)L * lpd.stride_b + (long long)(t + 1) * lpd.stride_t +
-                                              (long long)si.emit_il;
-                        const float lpv = (w.lp_dtype == 1) ? __half2float(((const __half *)lpd.base)[off])
-                                                            : ((const float *)lpd.base)[off];
-                        lbv = (end + si.emit_maxw) + lpv;
+                        // candidates of the next step: through the state's two
+                        // largest-weight arcs, (score + weight) + lp as the
+                        // maximum pass adds them
+                        const long long row = (long long)L * lpd.stride_b + (long long)(t + 1) * lpd.stride_t;
+                        const uint32_t il1 = si.emit_il & 0xFFFFu, il2 = si.emit_il >> 16;
+                        const bool two = il2 != 0xFFFFu;
+                        float lp1, lp2 = 0.0f;
+                        if (w.lp_dtype == 1) {
+                            const __half *r = (const __half *)lpd.base + row;
+                            lp1 = __half2float(r[il1]);
+                            if (two) lp2 = __half2float(r[il2]);
+                        } else {
+                            const float *r = (const float *)lpd.base + row;
+                            lp1 = r[il1];
+                            if (two) lp2 = r[il2];
+                        }
+                        lbv = (end + si.emit_maxw) + lp1;
+                        if (two) lbv = fmaxf(lbv, (end + si.emit_w2) + lp2);
                     }
                 }
             }
