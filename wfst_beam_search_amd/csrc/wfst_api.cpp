@@ -151,19 +151,22 @@ static int validate_graph(const wfst_graph_desc *g, std::vector<StateInfo> *info
         if (eps >= 0)
             while (a < e && g->ilabel[a] == eps) ++a;
         si.emit_b = a;
-        float emax = -INFINITY, fmax = -INFINITY, e2 = -INFINITY;
-        uint32_t il1 = 0, il2 = 0xFFFFu;
-        int32_t a1 = -1;
+        float fmax = -INFINITY;
+        for (int k = 0; k < kTopArcs; ++k) { si.top_w[k] = -INFINITY; si.top_il[k] = 0; }
         while (a < e && g->ilabel[a] >= 0 && g->ilabel[a] < V && g->ilabel[a] != eps) {
-            if (a1 < 0 || g->weight[a] > emax) { emax = g->weight[a]; il1 = (uint32_t)g->ilabel[a]; a1 = a; }
+            // keep the kTopArcs largest-weight emitting arcs, by weight descending
+            // (their candidates give the lower bound of the next step's maximum)
+            const float wa = g->weight[a];
+            const int filled = std::min(a - si.emit_b, kTopArcs);
+            int k = filled;
+            while (k > 0 && si.top_w[k - 1] < wa) --k;
+            if (k < kTopArcs) {
+                for (int j = kTopArcs - 1; j > k; --j) { si.top_w[j] = si.top_w[j - 1]; si.top_il[j] = si.top_il[j - 1]; }
+                si.top_w[k] = wa;
+                si.top_il[k] = (uint16_t)g->ilabel[a];
+            }
             ++a;
         }
-        // the two largest-weight emitting arcs (their labels and weights feed the
-        // lower bound of the next step's maximum)
-        for (int32_t b = si.emit_b; b < a; ++b)
-            if (b != a1 && (il2 == 0xFFFFu || g->weight[b] > e2)) { e2 = g->weight[b]; il2 = (uint32_t)g->ilabel[b]; }
-        si.emit_il = (il1 & 0xFFFFu) | (il2 << 16);
-        si.emit_w2 = e2;
         si.fin_b = a;
         while (a < e && g->ilabel[a] == -1) {
             fmax = std::max(fmax, g->weight[a]);
@@ -178,7 +181,6 @@ static int validate_graph(const wfst_graph_desc *g, std::vector<StateInfo> *info
             return fail(WFST_ECORRUPT, "corrupt graph: arc " + std::to_string(a) + " has ilabel " + std::to_string(il) +
                                            " outside {-1, epsilon_id} and [0, vocab_size)");
         }
-        si.emit_maxw = emax;
         si.fin_maxw = fmax;
         md = std::max(md, (uint32_t)(si.fin_b - si.emit_b));
         md = std::max(md, (uint32_t)(si.end - si.fin_b));

@@ -32,16 +32,22 @@ enum : int {
     kRecListed    // candidates the slot pass listed (its superset of the admitted ones)
 };
 
-// Per-state arc ranges and upper-bound weights, one 32-byte line per state:
-// arcs [eps_b, emit_b) are epsilon, [emit_b, fin_b) emitting, [fin_b, end) final.
-struct alignas(32) StateInfo {
+// Emitting arcs per state whose (label, weight) the state's record keeps for
+// the lower bound of the next step's maximum (the most that fit its 64 bytes).
+constexpr int kTopArcs = 7;
+
+// Per-state arc ranges and weights, one 64-byte record per state: arcs
+// [eps_b, emit_b) are epsilon, [emit_b, fin_b) emitting, [fin_b, end) final.
+// top_w / top_il are the kTopArcs largest-weight emitting arcs, by weight
+// descending (top_w[0] is the largest emitting weight, -inf if none); unused
+// entries have weight -inf and label 0.
+struct alignas(64) StateInfo {
     int32_t eps_b, emit_b, fin_b, end;
-    float emit_maxw;   // largest weight over the emitting arcs (-inf if none)
-    float fin_maxw;    // largest weight over the final arcs (-inf if none)
-    uint32_t emit_il;  // ilabels of two emitting arcs: bits 0-15 the first of weight emit_maxw,
-                       //   bits 16-31 another of the next largest weight (0xFFFF: none)
-    float emit_w2;     // weight of that second arc (-inf if none)
+    float fin_maxw;              // largest weight over the final arcs (-inf if none)
+    float top_w[kTopArcs];
+    uint16_t top_il[kTopArcs];
 };
+static_assert(sizeof(StateInfo) == 64, "one state record is one 64-byte line");
 
 // Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR
 // order of the graph), so the fields a pass reads for a token's arcs share

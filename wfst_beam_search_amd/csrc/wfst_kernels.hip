@@ -163,7 +163,7 @@ __device__ __forceinline__ void class_of(const StateInfo &si, bool final_step, f
     if (final_step) {
         *abeg = si.fin_b; *deg = (uint32_t)(si.end - si.fin_b); *ub = score + si.fin_maxw;
     } else {
-        *abeg = si.emit_b; *deg = (uint32_t)(si.fin_b - si.emit_b); *ub = score + si.emit_maxw;
+        *abeg = si.emit_b; *deg = (uint32_t)(si.fin_b - si.emit_b); *ub = score + si.top_w[0];
     }
 }
 
@@ -908,24 +908,22 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                          : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
                     class_of(si, next_final, end, &abeg, &deg, &ub);
                     if (!next_final && deg > 0u) {
-                        // candidates of the next step: through the state's two
+                        // candidates of the next step through the state's
                         // largest-weight arcs, (score + weight) + lp as the
-                        // maximum pass adds them
+                        // maximum pass adds them (unused entries weigh -inf)
                         const long long row = (long long)L * lpd.stride_b + (long long)(t + 1) * lpd.stride_t;
-                        const uint32_t il1 = si.emit_il & 0xFFFFu, il2 = si.emit_il >> 16;
-                        const bool two = il2 != 0xFFFFu;
-                        float lp1, lp2 = 0.0f;
+                        float lpk[kTopArcs];
                         if (w.lp_dtype == 1) {
                             const __half *r = (const __half *)lpd.base + row;
-                            lp1 = __half2float(r[il1]);
-                            if (two) lp2 = __half2float(r[il2]);
+#pragma unroll
+                            for (int k = 0; k < kTopArcs; ++k) lpk[k] = __half2float(r[si.top_il[k]]);
                         } else {
                             const float *r = (const float *)lpd.base + row;
-                            lp1 = r[il1];
-                            if (two) lp2 = r[il2];
+#pragma unroll
+                            for (int k = 0; k < kTopArcs; ++k) lpk[k] = r[si.top_il[k]];
                         }
-                        lbv = (end + si.emit_maxw) + lp1;
-                        if (two) lbv = fmaxf(lbv, (end + si.emit_w2) + lp2);
+#pragma unroll
+                        for (int k = 0; k < kTopArcs; ++k) lbv = fmaxf(lbv, (end + si.top_w[k]) + lpk[k]);
                     }
                 }
             }
