@@ -69,33 +69,37 @@ struct alignas(16) Claim {
     uint32_t score;   // binary32 bits of the end score
 };
 
-// Per-lane control block (one 128-byte line per lane).
+// Per-lane control block. Device-scope atomics on one 128-byte line serialize
+// even on different words, so every counter that many wavefronts of one kernel
+// update atomically has a line of its own; the first line holds the fields the
+// kernels only read, or that one thread writes.
 struct alignas(128) LaneCtl {
     int32_t T;                 // frames of this lane
     int32_t status;            // kActive / kDone
     uint32_t overflow;         // kOvf* bits
     int32_t reached_final;
-    unsigned long long cnt[2]; // frontier counter by parity: tokens | (arcs of the step's class) << 32
     float beam[2];             // b_t by step parity (beam[1] = search beam before step 0)
-    uint32_t maxkey[2];        // ordered exact maximum M_t by step parity
     float cutoff;              // cutoff of the latest real step (closure passes use it)
-    uint32_t nclaims[2];       // candidate-list length of the slot pass by step parity
-    uint32_t log_cursor;       // winners-log entries used in this lane's region
     int32_t final_entry;       // winners-log entry of the result (-1 none)
     unsigned long long final_key;  // best final candidate key of the final step
     float final_score;
-    uint32_t nclaims_eps[2];   // admitted candidates of closure pass k at [k & 1]
-    uint32_t nchanged[2];      // changed-token list sizes of closure pass k at [k & 1]
     uint32_t dirty;            // recombination table may hold stale entries (claims overflow)
     int32_t last_step;         // last step this lane ran
     int32_t phase_final;       // phase code of the lane's last step
-    uint32_t log_pending;      // entries of the last compaction (added by its wavefronts),
-                               //   moved into log_cursor by the next kernel that reads the log
-    uint32_t pad_a, pad_b;
+    uint32_t log_open;         // 1: the last compaction's entries (its token count) are not yet
+                               //   in log_cursor; the next kernel that reads the log adds them
     uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
                                //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
-    uint32_t lbkey[2];         // ordered lower bound of M_t by step parity: the best candidate
-                               //   through each token's largest-weight arc (posted by finalize)
+    alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
+                                             //   step's class) << 32
+    alignas(128) uint32_t nclaims[2];        // candidate-list length of the slot pass by step parity
+    alignas(128) uint32_t maxkey[2];         // ordered exact maximum M_t by step parity (slot pass)
+    uint32_t lbkey[2];                       // ordered lower bound of M_t by step parity: the best
+                                             //   candidate through each token's largest-weight arcs
+                                             //   (posted by the compaction of the step before)
+    alignas(128) uint32_t log_cursor;        // winners-log entries used in this lane's region
+    alignas(128) uint32_t nclaims_eps[2];    // admitted candidates of closure pass k at [k & 1]
+    alignas(128) uint32_t nchanged[2];       // changed-token list sizes of closure pass k at [k & 1]
 };
 
 // Device-resident description of the caller's log_prob tensor, rewritten before

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
     c.nchanged[0] = 0u;
     c.nchanged[1] = 0u;
     c.dirty = 0u;
-    c.log_pending = 0u;
+    c.log_open = 0u;
     c.front_base[0] = 0xFFFFFFFFu;
     c.front_base[1] = 0xFFFFFFFFu;
     c.last_step = -1;
@@ -608,8 +608,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
         LaneCtl &c = w.ctl[L];
         uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
         if (cur >= v.n) cur = 0;
-        const float posted = ord2f(__hip_atomic_load(&c.maxkey[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        float run = fmaxf(posted, ord2f(tab.fb[L]));
+        float run = ord2f(tab.fb[L]);
         const float b = tab.f1[L];
         for (; s < seg_end; ++s) {
             UnitData ud;
@@ -619,7 +618,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
         }
         if (cb_n) flush_claims(w, L, &c.nclaims[p], *cbuf, cb_n);
         cb_n = 0;
-        if (run > posted && wlane() == 0) atomicMax(&c.maxkey[p], f2ord(run));
+        if (run > -__builtin_inff() && wlane() == 0) atomicMax(&c.maxkey[p], f2ord(run));
     }
 }
 
@@ -684,14 +683,19 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
 __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
 {
     LaneCtl &c = w.ctl[L];
-    const int ph = lane_phase(c, t);
-    if (ph == kPhNone) return;
     const int p = t & 1;
     const unsigned long long cn = c.cnt[p];
     const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
+    if (c.log_open) {
+        // the compaction of step t - 1 (no closure ran after it): its token
+        // count is its number of winners and of winners-log entries
+        c.log_cursor += n;
+        step_rec(w, L, t - 1)[kRecDistinct] = n;
+        c.log_open = 0u;
+    }
+    const int ph = lane_phase(c, t);
+    if (ph == kPhNone) return;
     uint32_t *rec = step_rec(w, L, t);
-    c.log_cursor += c.log_pending;   // entries of the previous compaction
-    c.log_pending = 0u;
     c.last_step = t;
     rec[kRecN] = n;
     rec[kRecArcs] = arcs;
@@ -835,6 +839,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
                 c.front_base[np] = tab.arcs[L];
+                c.log_open = 1u;   // entries added to log_cursor by the next kernel
             }
             c.nclaims_eps[1] = 0u;
         } else if (ph == kPhFinal) {
@@ -946,8 +951,6 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         unsigned long long old = 0ull;
         if (lane == leader) {
             old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
-            atomicAdd(step_rec(w, L, t) + kRecDistinct, nkeep);
-            atomicAdd(&c.log_pending, nkeep);   // committed by the next kernel that reads the log
         }
         old = __shfl(old, leader, kWave);
         const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
@@ -1027,9 +1030,13 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
-        if (k == 1) {   // entries of the compaction before this closure
-            c.log_cursor += c.log_pending;
-            c.log_pending = 0u;
+        if (k == 1 && c.log_open) {
+            // the compaction before this closure: its token count (no closure
+            // token added yet) is its number of winners and of log entries
+            const uint32_t nd = (uint32_t)c.cnt[fp];
+            c.log_cursor += nd;
+            step_rec(w, L, t)[kRecDistinct] = nd;
+            c.log_open = 0u;
         }
         if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
     }
