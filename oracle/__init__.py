@@ -43,7 +43,8 @@ class _Graph(ctypes.Structure):
 class _Config(ctypes.Structure):
     _fields_ = [("beam", ctypes.c_float), ("min_active", ctypes.c_int32),
                 ("max_active", ctypes.c_int32), ("allow_partial", ctypes.c_int32),
-                ("eps_iterations", ctypes.c_int32)]
+                ("eps_iterations", ctypes.c_int32), ("online", ctypes.c_int32),
+                ("partial", ctypes.c_int32)]
 
 
 class _Result(ctypes.Structure):
@@ -101,8 +102,13 @@ class OracleGraph:
 
 
 def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active: int,
-                min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0):
+                min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0,
+                online: bool = False, partial: bool = False):
     """Decode one utterance. ``lp_lane`` is [T, V] (float32, or float16 widened exactly).
+
+    ``online``: streaming semantics (no "last ~5 frames" raise of min_active).
+    ``partial``: stop after the ``length`` real steps; the result is the path of the
+    best current token (no final step).
 
     Returns a dict: score (float32), reached_final, dead, arcs, words (int32 arrays),
     steps (int64 [n_steps, 16], fields ``FIELDS``), start_closure, log_entries.
@@ -116,7 +122,7 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
     if length < 0 or length > lp.shape[0]:
         raise ValueError("length outside [0, T]")
     cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
-                  int(eps_iterations))
+                  int(eps_iterations), int(bool(online)), int(bool(partial)))
     arcs_cap = (length + 2) * (1 + max(0, int(eps_iterations))) + 8
     steps_cap = length + 2
     arcs = np.zeros(arcs_cap, dtype=np.int32)
@@ -139,14 +145,14 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
 
 def decode_batch(graph, lp: np.ndarray, lengths, beam: float, max_active: int,
                  min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0,
-                 lanes=None, threads: int = 1):
+                 lanes=None, threads: int = 1, online: bool = False, partial: bool = False):
     """Decode lanes of a batch independently (each lane on one thread of a pool)."""
     og = graph if isinstance(graph, OracleGraph) else OracleGraph(graph)
     lanes = list(range(lp.shape[0])) if lanes is None else list(lanes)
 
     def one(b):
         return decode_lane(og, lp[b], int(lengths[b]), beam, max_active, min_active,
-                           allow_partial, eps_iterations)
+                           allow_partial, eps_iterations, online, partial)
 
     if threads <= 1:
         return [one(b) for b in lanes]

@@ -42,6 +42,8 @@ typedef struct {
     int32_t max_active;
     int32_t allow_partial;
     int32_t eps_iterations;
+    int32_t online;    /* 1: streaming (online) semantics, see wo_decode */
+    int32_t partial;   /* 1: no final step; the result is the best current token */
 } wo_config;
 
 /* Per-step record written for every step the lane runs (t = 0 .. T). */
@@ -297,6 +299,18 @@ out:
  * final step with no candidate redirects when allow_partial is set: each token
  * is offered with a virtual arc of weight 0 and id num_arcs + state, and the
  * best key wins (reached_final = 0, the virtual arc is not on the path).
+ *
+ * Streaming (section 3, last paragraph, and section 8 "Streaming Lifecycle"):
+ * with cfg->online the utterance length is unknown while frames arrive (T is
+ * unbounded until the caller ends the stream), so the "last ~5 frames" raise of
+ * min_active never applies; ending the stream at T runs the same final step.
+ * Chunk boundaries are invisible to the search, so online decoding of T frames
+ * in any chunking is this one call. With cfg->partial the search stops after
+ * the T real steps (and their closures) without a final step, and the result is
+ * the partial hypothesis of section 8: the path of the best token of the current
+ * frontier. Reading: best = greatest key(score, arc that gave the token its
+ * current score), the same order as recombination (higher score, then smaller
+ * arc id; the start token's arc -1 ranks lowest); reached_final = 0.
  */
 int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t T,
               int64_t lp_stride, int32_t *arcs, int32_t arcs_cap, int32_t *words,
@@ -329,6 +343,24 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     for (int32_t t = 0; t <= T; t++) {
         int is_final = (t == T);
         int64_t n = cur.n;
+        if (is_final && cfg->partial) {
+            /* partial hypothesis: the best token of the current frontier */
+            int64_t bi = -1;
+            uint64_t bk = 0;
+            for (int64_t i = 0; i < n; i++) {
+                uint64_t k = wo_key(cur.score[i], cur.last[i]);
+                if (bi < 0 || k > bk) { bk = k; bi = i; }
+            }
+            if (bi >= 0) {
+                res->score = cur.score[bi];
+                res->reached_final = 0;
+                final_entry = cur.entry[bi];
+                have_path = 1;
+            } else {
+                res->dead = 1;
+            }
+            break;
+        }
         int64_t rec[WO_FIELDS];
         float b, M = -INFINITY, cutoff;
         int64_t S = 0, C = 0;
@@ -346,7 +378,7 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
             b = 1e10f;
         } else {
             int32_t mina = cfg->min_active;
-            if (T - t <= 5 && cfg->max_active / 2 > mina) mina = cfg->max_active / 2;
+            if (!cfg->online && T - t <= 5 && cfg->max_active / 2 > mina) mina = cfg->max_active / 2;
             if (n > cfg->max_active) {
                 b = (b_prev < cfg->beam ? b_prev : cfg->beam) * 0.8f;
             } else if (n < mina) {

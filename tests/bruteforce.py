@@ -9,6 +9,8 @@ their weight).
 
 * ``viterbi_exact``: a full trellis dynamic program that updates every state at
   every frame (infinite beam), with the epsilon closure computed to a fixpoint.
+* ``viterbi_partial``: the same trellis stopped after T frames, best state
+  without a final arc (the partial hypothesis of a stream).
 * ``enumerate_paths``: lists every path (at most ``max_eps`` epsilon arcs
   between frames) and takes the maximum.
 """
@@ -33,13 +35,9 @@ def _classes(g):
     return final, eps, emit
 
 
-def viterbi_exact(g, lp, T):
-    """Best score and one best path over the full graph x frames trellis.
-
-    Returns (score, arcs, tied) where ``tied`` says whether any maximum on the
-    returned path was reached by more than one candidate (then the path is not
-    unique and only the score is meaningful).
-    """
+def _trellis(g, lp, T):
+    """Scores, one best path and tie flags of every state after T frames of the
+    full trellis (epsilon closure to a fixpoint after the start and every frame)."""
     src = _arc_src(g)
     final, eps, emit = _classes(g)
     S = g.num_states
@@ -78,6 +76,19 @@ def viterbi_exact(g, lp, T):
                 ntie[d] = True
         score, path, tie = ns, npth, ntie
         closure()
+    return score, path, tie
+
+
+def viterbi_exact(g, lp, T):
+    """Best score and one best path over the full graph x frames trellis.
+
+    Returns (score, arcs, tied) where ``tied`` says whether any maximum on the
+    returned path was reached by more than one candidate (then the path is not
+    unique and only the score is meaningful).
+    """
+    src = _arc_src(g)
+    final, _, _ = _classes(g)
+    score, path, tie = _trellis(g, lp, T)
     best, bpath, btie = None, None, False
     for a in np.nonzero(final)[0]:
         s = int(src[a])
@@ -87,6 +98,25 @@ def viterbi_exact(g, lp, T):
         if bpath is None or c > best:
             best, bpath, btie = c, path[s] + [int(a)], tie[s]
         elif c == best:
+            btie = True
+    if bpath is None:
+        return NEG, [], False
+    return best, bpath, btie
+
+
+def viterbi_partial(g, lp, T):
+    """Best state of the trellis after T frames (no final arc): its score and path.
+
+    Returns (score, arcs, tied); ``tied`` is set when another state reaches the
+    same score or the path itself was tied."""
+    score, path, tie = _trellis(g, lp, T)
+    best, bpath, btie = None, None, False
+    for s in range(g.num_states):
+        if path[s] is None:
+            continue
+        if bpath is None or score[s] > best:
+            best, bpath, btie = score[s], path[s], tie[s]
+        elif score[s] == best:
             btie = True
     if bpath is None:
         return NEG, [], False

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from bruteforce import enumerate_paths, viterbi_exact
+from bruteforce import enumerate_paths, viterbi_exact, viterbi_partial
 from cases import check_path, f32_value, graph_from_states, load_golden
 
 F32 = np.float32
@@ -24,8 +24,10 @@ def _bits(x):
     return int(np.array(F32(x)).view(np.uint32))
 
 
-def _decode(g, lp, T, beam, max_active, min_active=0, allow_partial=False, eps=0):
-    return oracle.decode_lane(g, lp, T, beam, max_active, min_active, allow_partial, eps)
+def _decode(g, lp, T, beam, max_active, min_active=0, allow_partial=False, eps=0,
+            online=False, partial=False):
+    return oracle.decode_lane(g, lp, T, beam, max_active, min_active, allow_partial, eps,
+                              online=online, partial=partial)
 
 
 def _const_lp(frames, vocab, value):
@@ -230,12 +232,12 @@ def test_forced_alignment_closed_form():
 
 # ------------------------------------------------------ dynamic beam consistency
 
-def _recompute_beams(steps, length, beam, max_active, min_active):
+def _recompute_beams(steps, length, beam, max_active, min_active, online=False):
     out, bp = [], F32(beam)
     for t, n in enumerate(steps[:, IDX["n"]]):
         if t == length:
             out.append(F32(1e10)); continue
-        mina = max(min_active, max_active // 2) if length - t <= 5 else min_active
+        mina = max(min_active, max_active // 2) if (length - t <= 5 and not online) else min_active
         if n > max_active:
             b = F32(min(bp, F32(beam)) * F32(0.8))
         elif n < mina:
@@ -280,3 +282,103 @@ def test_workload_paths_are_consistent(cid, lanes):
         if not wl.epsilon:
             assert np.array_equal(st[:-1, IDX["n_next"]], st[1:, IDX["n"]])
             assert np.array_equal(st[:, IDX["n_next"]], st[:, IDX["distinct"]])
+
+
+# ------------------------------------------- streaming: online beam, partial results
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_partial_at_infinite_beam_equals_trellis_best(eps):
+    """Page section 8: a partial hypothesis is the path of the best current token.
+    At infinite beam the frontier is the whole trellis column, so it is the best
+    state of the exact trellis after T frames."""
+    compared = 0
+    for seed in range(500, 620):
+        g, lp, T = _tiny(seed, eps)
+        P = 2 if eps else 0
+        r = _decode(g, lp, T, INF_BEAM, 1 << 20, eps=P, online=True, partial=True)
+        best, path, tied = viterbi_partial(g, lp, T)
+        assert r["reached_final"] == 0
+        assert r["score"] == best, (seed, r["score"], best)
+        if not tied:
+            assert list(r["arcs"]) == path, seed
+            compared += 1
+    assert compared > 60
+
+
+def _no_final_spec(seed):
+    """A random graph whose states have no final arc (the super-final state is
+    unreachable), so an offline decode with allow_partial always redirects."""
+    rng = np.random.default_rng(seed)
+    n, vocab = int(rng.integers(2, 8)), int(rng.integers(2, 5))
+    states = []
+    for _ in range(n):
+        arcs = [[int(rng.integers(0, n)), int(rng.integers(0, vocab)), int(rng.integers(0, 3)),
+                 float(rng.normal())] for _ in range(int(rng.integers(1, 4)))]
+        arcs.sort(key=lambda a: a[1])
+        states.append(arcs)
+    states.append([])
+    return {"start": 0, "vocab": vocab, "epsilon_id": -1, "states": states}, vocab
+
+
+def test_partial_equals_redirect_without_final_arcs():
+    """Section 3: with no final arc and allow_partial the final step hands the
+    result to the best token (key over score + 0); the partial hypothesis takes
+    the best token too. With distinct scores both name the same token, and with
+    min_active >= max_active / 2 the offline "last frames" clause changes nothing."""
+    checked = 0
+    for seed in range(700, 780):
+        spec, vocab = _no_final_spec(seed)
+        g = graph_from_states(spec)
+        T = int(np.random.default_rng(seed).integers(1, 8))
+        lp = synth.random_logprobs(seed, 1, T, vocab)[0]
+        off = _decode(g, lp, T, 3.0, 6, min_active=3, allow_partial=True)
+        on = _decode(g, lp, T, 3.0, 6, min_active=3, online=True, partial=True)
+        if off["dead"]:
+            assert on["dead"] == 1
+            continue
+        assert off["steps"][-1, IDX["phase"]] == oracle.PHASE_REDIRECT
+        assert on["score"] == off["score"] and list(on["arcs"]) == list(off["arcs"]), seed
+        assert list(on["words"]) == list(off["words"])
+        checked += 1
+    assert checked > 50
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_online_beams_skip_the_final_window(cid):
+    """Section 3: a stream's length is unknown until it ends, so the raise of
+    min_active over the last frames never happens; every other beam rule holds."""
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    differs = 0
+    for b in range(min(wl.batch, 3)):
+        r = _decode(g, lp[b], int(L[b]), wl.beam, wl.max_active, online=True)
+        st = r["steps"]
+        got = np.array(st[:, IDX["beam"]], dtype=np.uint32).view(np.float32)
+        assert np.array_equal(got, _recompute_beams(st, int(L[b]), wl.beam, wl.max_active, 0, online=True))
+        off = _decode(g, lp[b], int(L[b]), wl.beam, wl.max_active)
+        differs += int(not np.array_equal(off["steps"], st))
+    assert differs > 0   # the clause matters on these lanes, so the test can fail
+
+
+def test_online_equals_offline_when_the_final_window_is_inert():
+    for seed in range(800, 860):
+        g, lp, T = _tiny(seed, seed % 2 == 1)
+        P = 2 if seed % 2 else 0
+        kw = dict(eps=P, min_active=2)
+        a = _decode(g, lp, T, 1.5, 4, **kw)
+        b = _decode(g, lp, T, 1.5, 4, online=True, **kw)
+        assert a["score"] == b["score"] or (np.isneginf(a["score"]) and np.isneginf(b["score"]))
+        assert list(a["arcs"]) == list(b["arcs"]) and np.array_equal(a["steps"], b["steps"])
+
+
+def test_partial_prefix_of_final_steps():
+    """A partial result after t frames is the search state after those frames:
+    its records are the first t records of the whole (online) decode."""
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    T = int(L[0])
+    full = _decode(g, lp[0], T, wl.beam, wl.max_active, online=True)
+    for t in (0, 1, 17, T // 2, T):
+        part = _decode(g, lp[0], t, wl.beam, wl.max_active, online=True, partial=True)
+        assert np.array_equal(part["steps"], full["steps"][:t])
+        check_path(g, lp[0].astype(np.float32), t, part["arcs"], part["words"], part["score"], 0)
