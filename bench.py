@@ -116,6 +116,110 @@ def cpu_baseline(graph, lp, lengths, wl, seconds):
                       f"single-threaded C oracle pinned to one core; host nproc {os.cpu_count()}, {model})"}
 
 
+def stream_bench(args, wl, graph, lp, lengths, dev):
+    """Streams the workload's utterances (one stream per lane, all lanes advanced
+    together chunk by chunk, then finalized): a step is the whole batch streamed.
+    The chunks are packed on the device before the timed region."""
+    import numpy as np
+    import torch
+
+    import wfst_beam_search_amd as wb
+
+    B, T, V = lp.shape
+    N = args.stream_chunk
+    P = wl.eps_iterations if graph.epsilon_id >= 0 else 0
+    arena = min(max(1 << 20, 4 * wl.max_active * (T + 2) * (1 + P)), ((1 << 31) - 1) // B)
+    dg = wb.Graph(graph, device=0)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=N, lp_dtype=wl.dtype,
+                     eps_iterations=wl.eps_iterations, use_graphs=not args.eager, grid_blocks=args.grid,
+                     path_cap=(T + 2) * (1 + P), arena_entries=arena)
+    x = torch.from_numpy(lp).to(dev)
+    chunks = []
+    for s in range(0, T, N):
+        lens = np.clip(np.asarray(lengths) - s, 0, N).astype(np.int32)
+        if lens.max() == 0:
+            break
+        live = [b for b in range(B) if lens[b] > 0]
+        xc = x[live, s:s + N].contiguous()
+        if xc.shape[1] < N:
+            xc = torch.cat([xc, torch.zeros((len(live), N - xc.shape[1], V), dtype=xc.dtype, device=dev)], 1)
+        chunks.append((live, xc, lens[live]))
+    torch.cuda.synchronize()
+
+    phase = [0.0, 0.0, 0.0]   # seconds in create, advance, finalize + release calls
+
+    def one():
+        ta = time.perf_counter()
+        ch = [dec.create_stream() for _ in range(B)]
+        tb = time.perf_counter()
+        for live, xc, lens in chunks:
+            dec.advance_chunk([ch[b] for b in live], xc, lens, want_partial=args.stream_partial)
+        tc = time.perf_counter()
+        res = [dec.finalize_stream(c) for c in ch]
+        for c in ch:
+            dec.release_stream(c)
+        td = time.perf_counter()
+        phase[0] += tb - ta
+        phase[1] += tc - tb
+        phase[2] += td - tc
+        return res
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    phase[:] = [0.0, 0.0, 0.0]
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = one()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    frames = int(np.asarray(lengths).sum())
+    ok = all(int(r.meta[0, 0]) == 1 and int(r.meta[0, 2]) == 0 for r in res)
+    ktimes = {}
+    if not args.no_profile_pass:
+        dec.profile(True)
+        acc = {}
+        ch = [dec.create_stream() for _ in range(B)]
+        for live, xc, lens in chunks:
+            dec.advance_chunk([ch[b] for b in live], xc, lens, want_partial=args.stream_partial)
+            for k, (ms, cnt) in dec.kernel_times().items():
+                a = acc.setdefault(k, [0.0, 0])
+                a[0] += ms
+                a[1] += cnt
+        for c in ch:
+            dec.finalize_stream(c)
+            dec.release_stream(c)
+        dec.profile(False)
+        ktimes = {k: {"total_ms_per_decode": v[0], "launches_per_decode": v[1],
+                      "avg_launch_us": (v[0] / v[1] * 1e3) if v[1] else 0.0} for k, v in acc.items() if v[1]}
+    line = {
+        "metric": "streamed frames/sec at 1 GPU (every lane a stream, advanced chunk by chunk)",
+        "value": round(frames * args.steps / dt, 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name} streamed in chunks of {N} frames"
+                               f"{' with partial hypotheses after each chunk' if args.stream_partial else ''}: "
+                               f"{graph.num_states - 1} states, {graph.num_arcs} arcs, log_prob {wl.dtype} "
+                               f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
+                   "batch": B, "frames": T, "vocab": V, "chunk": N, "chunk_calls_per_step": len(chunks),
+                   "beam": wl.beam, "max_active": wl.max_active,
+                   "execution": "per-phase kernels, " + ("eager" if args.eager else "hipGraph replay per chunk")},
+        "ms_per_chunk_call": round(phase[1] / args.steps / max(len(chunks), 1) * 1e3, 4),
+        "ms_per_step_by_call": {"create": round(phase[0] / args.steps * 1e3, 3),
+                                "advance": round(phase[1] / args.steps * 1e3, 3),
+                                "finalize_release": round(phase[2] / args.steps * 1e3, 3)},
+        "parity_meta_ok": ok,
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump({"line": line, "kernels": ktimes, "kernel_source": kernel_source_hash()}, f, indent=1)
+    dec.close()
+    dg.release()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +232,11 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
+    ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
+                    help="stream every lane in chunks of N frames (create / advance / finalize / "
+                         "release per timed step) instead of one batch decode")
+    ap.add_argument("--stream-partial", action="store_true",
+                    help="with --stream-chunk: ask for every lane's partial hypothesis after each chunk")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -158,6 +267,9 @@ def main():
     graph, lp, lengths = synth.workload_inputs(args.workload)
     B, T, V = lp.shape
     dev = torch.device("cuda:0")
+    if args.stream_chunk > 0:
+        stream_bench(args, wl, graph, lp, lengths, dev)
+        return
     dg = wb.Graph(graph, device=0)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,

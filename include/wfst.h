@@ -122,6 +122,11 @@ typedef struct wfst_graph_desc {
  *                  counter wraps: every 2^(32 - ceil(log2 num_arcs)) - 1
  *                  rounds, at least 127); 1: plain keys, each entry cleared by
  *                  its owner (always the case on larger graphs). Same results.
+ *  path_cap        arcs of a result path kept per lane (0: (max_frames + 2) *
+ *                  (1 + eps passes)); in [0, 2^26]. A longer path keeps its
+ *                  newest path_cap arcs (its words are those arcs' words) and
+ *                  sets WFST_OVF_PATH. A stream's path spans all its frames
+ *                  (section 8): size this for the longest stream.
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -139,6 +144,7 @@ typedef struct wfst_decoder_config {
     int64_t arena_entries;
     int64_t slot_cap;
     int32_t plain_keys;
+    int32_t path_cap;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -201,7 +207,8 @@ int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *c, wfst_decod
  * the last step without allow_partial) reports ok = 1, reached_final = 0,
  * score -inf and no arcs. The call is idempotent and serial per decoder (an
  * internal mutex); other decoders may run concurrently.
- * Errors: WFST_EINVAL (ranges above, null pointers, V mismatch), WFST_EDEVICE.
+ * Errors: WFST_EINVAL (ranges above, null pointers, V mismatch, or the decoder
+ * holds open streams), WFST_EDEVICE.
  */
 int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
                 const int32_t *lengths_host, void *stream,
@@ -213,7 +220,66 @@ int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, in
 int wfst_decoder_destroy(wfst_decoder_t d);
 
 /*
- * Counters of the last decode, summed over its lanes (n up to 14 values):
+ * Streams (page section 8 "Streaming Lifecycle", section 3 on the online beam):
+ * a stream decodes one utterance whose frames arrive in chunks. It holds one
+ * lane of the decoder from wfst_create_stream to wfst_release_stream; its search
+ * state stays on the device between calls. Until wfst_finalize_stream the
+ * utterance length counts as unbounded, so the raise of min_active over an
+ * utterance's last frames never applies (k2's online semantics); any chunking
+ * of the same frames gives the same search. A stream's whole path stays in its
+ * lane's winners-log region (arena_entries entries): a longer stream overflows
+ * it (WFST_OVF_ARENA). max_frames bounds one chunk, not the stream. While any
+ * stream is open, wfst_decode is refused. All calls are serial per decoder.
+ */
+
+/*
+ * Open a stream: *channel = the lane it holds, or -1 when every lane holds one
+ * (not an error). Runs the start frontier's epsilon closure for that lane only.
+ * Errors: WFST_EINVAL (null), WFST_EDEVICE.
+ */
+int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel);
+
+/*
+ * Advance C open streams by one chunk each.
+ *  channels      [C] host: distinct open channels, 1 <= C <= max_lanes.
+ *  log_prob      device pointer to a packed [C, T, V] tensor of lp_dtype: row j
+ *                holds channels[j]'s next frames; owned by the caller and left
+ *                untouched; must stay valid until the call returns.
+ *  T, V          0 <= T <= max_frames, V = graph vocab_size.
+ *  lengths_host  [C] host: frames of each channel's chunk, in [0, T].
+ *  stream        the caller's HIP stream; the call returns after synchronising it.
+ *  want_partial  non-zero: write each channel's partial hypothesis (the path of
+ *                its best current token: greatest (score, then smallest arc id
+ *                of the arc that gave the token its score)) to the outputs,
+ *                laid out as wfst_decode's for B = C, row j for channels[j], with
+ *                reached_final = 0 (score -inf and no arcs once the stream's
+ *                search has died). Otherwise the outputs are not touched and may
+ *                be null.
+ * Errors: WFST_EINVAL (ranges above, a channel not open or repeated, null
+ * pointers), WFST_EDEVICE.
+ */
+int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int32_t C, const void *log_prob,
+                       int32_t T, int32_t V, const int32_t *lengths_host, void *stream,
+                       int32_t want_partial, int32_t *out_words, int32_t words_cap,
+                       int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap,
+                       int32_t *out_arc_lens, float *out_scores, int32_t *out_meta);
+
+/*
+ * End a stream: its utterance length becomes the frames it has received, the
+ * final step runs (final arcs, beam 1e10, redirect with allow_partial) and the
+ * result is written as wfst_decode's for one lane. The channel stays held (a
+ * second call returns the same result) until released.
+ * Errors: WFST_EINVAL (channel not open, null pointers), WFST_EDEVICE.
+ */
+int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_t *out_words,
+                         int32_t words_cap, int32_t *out_word_len, int32_t *out_arcs, int32_t arcs_cap,
+                         int32_t *out_arc_len, float *out_score, int32_t *out_meta);
+
+/* Give a stream's lane back (no device work). Errors: WFST_EINVAL (not open). */
+int wfst_release_stream(wfst_decoder_t d, int32_t channel);
+
+/*
+ * Counters of the last decode or stream call, summed over its lanes (n up to 14 values):
  *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
  *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
  *  frontier sizes), [4] epsilon arcs relaxed, [5] epsilon candidates admitted,
@@ -227,7 +293,8 @@ int wfst_decoder_destroy(wfst_decoder_t d);
 int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 
 /*
- * Per-step records of lane `lane` in the last decode, 16 int64 each:
+ * Per-step records of lane `lane` in the last decode or stream call (steps
+ * numbered from the call's first), 16 int64 each:
  *  {n, beam bits, max bits, arcs, admitted, distinct, eps arcs, eps admitted,
  *   eps distinct, eps new, eps replaced, eps passes, phase, listed, 0, 0}
  * record 0 describes the start frontier's closure (only the eps fields), record
@@ -247,8 +314,11 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_EPS_EXPAND   6  /* closure pass: relax epsilon arcs                         */
 #define WFST_K_EPS_RESOLVE  7  /* closure pass: append / replace decisions                 */
 #define WFST_K_EPS_APPLY    8  /* closure pass: apply them                                 */
-#define WFST_K_BACKTRACK    9  /* best path to arc ids and words                           */
-#define WFST_K_COUNT       10
+#define WFST_K_BACKTRACK    9  /* best path (or a stream's best current token) to arcs, words */
+#define WFST_K_STREAM_BEGIN 10 /* stream call: applies the per-lane plan                   */
+#define WFST_K_STREAM_END  11  /* stream call: commits the chunk's last compaction        */
+#define WFST_K_RECLASS     12  /* stream end: final-step class of the stream's tokens      */
+#define WFST_K_COUNT       13
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

@@ -26,9 +26,10 @@ LP_F32, LP_F16 = 0, 1
 EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release",
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
                     "wfst_decoder_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
-                    "wfst_decoder_kernel_times")
+                    "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
+                    "wfst_finalize_stream", "wfst_release_stream")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
-           "eps_apply", "backtrack")
+           "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass")
 STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
                "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "listed", "_14", "_15")
 STAT_FIELDS = ("arcs", "admitted", "distinct", "tokens", "eps_arcs", "eps_admitted",
@@ -60,7 +61,7 @@ class _Config(ctypes.Structure):
                 ("use_graphs", ctypes.c_int32), ("frontier_cap", ctypes.c_int32),
                 ("claims_cap", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
                 ("arena_entries", ctypes.c_int64), ("slot_cap", ctypes.c_int64),
-                ("plain_keys", ctypes.c_int32)]
+                ("plain_keys", ctypes.c_int32), ("path_cap", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,6 +101,11 @@ def load_library():
         lib.wfst_decoder_step_stats.argtypes = [vp, i32, vp, i32]
         lib.wfst_decoder_profile.argtypes = [vp, i32]
         lib.wfst_decoder_kernel_times.argtypes = [vp, vp, i32]
+        lib.wfst_create_stream.argtypes = [vp, vp, vp]
+        lib.wfst_advance_chunk.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, i32, vp, vp, i32,
+                                           vp, vp, vp]
+        lib.wfst_finalize_stream.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+        lib.wfst_release_stream.argtypes = [vp, i32]
         for name in EXPORTED_SYMBOLS:
             if name != "wfst_last_error":
                 getattr(lib, name).restype = ctypes.c_int
@@ -173,13 +179,13 @@ class Decoder:
                  allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
                  lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
-                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False):
+                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False, path_cap: int = 0):
         lib = load_library()
         cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                       int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                       int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
                       int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
-                      int(bool(plain_keys)))
+                      int(bool(plain_keys)), int(path_cap))
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h
@@ -189,10 +195,7 @@ class Decoder:
         self.lp_dtype = lp_dtype
         self.eps_iterations = int(eps_iterations)
 
-    def decode(self, log_prob, lengths, stream=None, words_cap: int | None = None,
-               arcs_cap: int | None = None) -> DecodeResult:
-        """Decode ``log_prob`` ([B, T, V] torch tensor on the decoder's device, packed,
-        in the decoder's dtype) with per-lane ``lengths``; returns host results."""
+    def _check_lp(self, log_prob):
         import torch
         if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda:
             raise TypeError("log_prob must be a torch tensor on the GPU")
@@ -201,27 +204,92 @@ class Decoder:
         want = torch.float16 if self.lp_dtype == "f16" else torch.float32
         if log_prob.dtype != want:
             raise TypeError(f"log_prob must be {want}")
+        if log_prob.dim() != 3:
+            raise ValueError("log_prob must be [B, T, V]")
+
+    @staticmethod
+    def _stream(stream, device):
+        import torch
+        return torch.cuda.current_stream(device).cuda_stream if stream is None else stream
+
+    @staticmethod
+    def _outputs(n, wcap, acap):
+        return (np.zeros((n, max(wcap, 1)), dtype=np.int32), np.zeros(n, dtype=np.int32),
+                np.zeros((n, max(acap, 1)), dtype=np.int32), np.zeros(n, dtype=np.int32),
+                np.zeros(n, dtype=np.float32), np.zeros((n, 3), dtype=np.int32))
+
+    @staticmethod
+    def _result(out, wcap, acap):
+        out_words, wl, out_arcs, al, sc, meta = out
+        n = sc.shape[0]
+        words = [out_words[b, :min(int(wl[b]), wcap)].copy() for b in range(n)]
+        arcs = [out_arcs[b, :min(int(al[b]), acap)].copy() for b in range(n)]
+        return DecodeResult(words, arcs, sc, meta, wl, al)
+
+    def decode(self, log_prob, lengths, stream=None, words_cap: int | None = None,
+               arcs_cap: int | None = None) -> DecodeResult:
+        """Decode ``log_prob`` ([B, T, V] torch tensor on the decoder's device, packed,
+        in the decoder's dtype) with per-lane ``lengths``; returns host results."""
+        self._check_lp(log_prob)
         B, T, V = (int(x) for x in log_prob.shape)
         lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
         if lens.shape[0] != B:
             raise ValueError("lengths must have B entries")
-        if stream is None:
-            stream = torch.cuda.current_stream(log_prob.device).cuda_stream
+        stream = self._stream(stream, log_prob.device)
         wcap = int(words_cap) if words_cap is not None else T + 2
         acap = int(arcs_cap) if arcs_cap is not None else (T + 2) * (1 + max(0, self.eps_iterations))
-        out_words = np.zeros((B, max(wcap, 1)), dtype=np.int32)
-        out_arcs = np.zeros((B, max(acap, 1)), dtype=np.int32)
-        wl = np.zeros(B, dtype=np.int32)
-        al = np.zeros(B, dtype=np.int32)
-        sc = np.zeros(B, dtype=np.float32)
-        meta = np.zeros((B, 3), dtype=np.int32)
+        out = self._outputs(B, wcap, acap)
+        out_words, wl, out_arcs, al, sc, meta = out
         _check(_lib.wfst_decode(self.handle, ctypes.c_void_p(log_prob.data_ptr()), B, T, V,
                                 _ptr(lens), ctypes.c_void_p(int(stream)),
                                 _ptr(out_words), wcap, _ptr(wl), _ptr(out_arcs), acap, _ptr(al),
                                 _ptr(sc), _ptr(meta)))
-        words = [out_words[b, :min(int(wl[b]), wcap)].copy() for b in range(B)]
-        arcs = [out_arcs[b, :min(int(al[b]), acap)].copy() for b in range(B)]
-        return DecodeResult(words, arcs, sc, meta, wl, al)
+        return self._result(out, wcap, acap)
+
+    # ---- streams (page section 8): one lane per stream, search state kept on the device
+
+    def create_stream(self, stream=None) -> int:
+        """Open a stream; returns its channel, or -1 when every lane holds one."""
+        import torch
+        ch = ctypes.c_int32(-1)
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        _check(_lib.wfst_create_stream(self.handle, ctypes.c_void_p(int(s)), ctypes.byref(ch)))
+        return int(ch.value)
+
+    def advance_chunk(self, channels, log_prob, lengths, want_partial: bool = False, stream=None,
+                      words_cap: int = 4096, arcs_cap: int = 4096):
+        """Advance each channel by its chunk (row j of ``log_prob`` [C, T, V] for
+        channels[j], ``lengths[j]`` frames). Returns the partial hypotheses as a
+        DecodeResult (row j for channels[j]) when ``want_partial``, else None."""
+        self._check_lp(log_prob)
+        C, T, V = (int(x) for x in log_prob.shape)
+        chans = np.ascontiguousarray(np.asarray(channels, dtype=np.int32).reshape(-1))
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
+        if chans.shape[0] != C or lens.shape[0] != C:
+            raise ValueError("channels and lengths must have C entries")
+        stream = self._stream(stream, log_prob.device)
+        out = self._outputs(C, words_cap, arcs_cap)
+        out_words, wl, out_arcs, al, sc, meta = out
+        _check(_lib.wfst_advance_chunk(self.handle, _ptr(chans), C, ctypes.c_void_p(log_prob.data_ptr()),
+                                       T, V, _ptr(lens), ctypes.c_void_p(int(stream)), int(bool(want_partial)),
+                                       _ptr(out_words), words_cap, _ptr(wl), _ptr(out_arcs), arcs_cap,
+                                       _ptr(al), _ptr(sc), _ptr(meta)))
+        return self._result(out, words_cap, arcs_cap) if want_partial else None
+
+    def finalize_stream(self, channel: int, stream=None, words_cap: int = 1 << 16,
+                        arcs_cap: int = 1 << 16) -> DecodeResult:
+        """End a stream: final step and best path (a one-row DecodeResult)."""
+        import torch
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        out = self._outputs(1, words_cap, arcs_cap)
+        out_words, wl, out_arcs, al, sc, meta = out
+        _check(_lib.wfst_finalize_stream(self.handle, int(channel), ctypes.c_void_p(int(s)), _ptr(out_words),
+                                         words_cap, _ptr(wl), _ptr(out_arcs), arcs_cap, _ptr(al), _ptr(sc),
+                                         _ptr(meta)))
+        return self._result(out, words_cap, arcs_cap)
+
+    def release_stream(self, channel: int):
+        _check(_lib.wfst_release_stream(self.handle, int(channel)))
 
     def stats(self) -> dict:
         out = np.zeros(len(STAT_FIELDS), dtype=np.int64)

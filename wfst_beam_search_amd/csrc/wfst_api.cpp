@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -94,8 +95,16 @@ struct wfst_decoder_s {
     int32_t *h_res = nullptr;       // pinned: results
     hipStream_t cap_stream = nullptr;
     std::map<int, hipGraphExec_t> graphs;
-    int last_B = 0;
-    std::vector<int32_t> last_len;
+    std::map<int, hipGraphExec_t> stream_graphs;   // stream sequences by (kind, steps)
+    std::vector<int32_t> last_len;   // per lane: frames of the last call (-1: not in it)
+    // streams (page section 8): a stream holds one lane for its lifetime
+    std::vector<uint8_t> chan_open;
+    int open_streams = 0;
+    int32_t *d_plan = nullptr;       // [L][kPlanFields] device copy of the plan
+    int32_t *h_plan = nullptr;       // pinned: plan, then the sequence's round base
+    uint64_t round_next = 0;         // first recombination round of the next stream sequence
+                                     //   (counted since the last clear of the whole table)
+    uint32_t dev_round_base = 0;     // round base the device-side Work holds
     int last_steps = 0;
     bool prof_on = false;            // time every launch with a start / end event pair
     bool last_profiled = false;
@@ -107,10 +116,12 @@ struct wfst_decoder_s {
     {
         (void)hipSetDevice(g ? g->device : 0);
         for (auto &kv : graphs) (void)hipGraphExecDestroy(kv.second);
+        for (auto &kv : stream_graphs) (void)hipGraphExecDestroy(kv.second);
         for (hipEvent_t e : ev) (void)hipEventDestroy(e);
         if (cap_stream) (void)hipStreamDestroy(cap_stream);
         if (h_in) (void)hipHostFree(h_in);
         if (h_res) (void)hipHostFree(h_res);
+        if (h_plan) (void)hipHostFree(h_plan);
         for (void *p : owned) (void)hipFree(p);
         if (g && g->refs.fetch_sub(1) == 1) delete g;
     }
@@ -306,7 +317,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         if (c.arena_entries) return fail(WFST_EINVAL, "max_lanes * arena_entries must stay below 2^31");
         arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
     }
-    const uint64_t path_cap = (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
+    if (c.path_cap < 0 || c.path_cap > (1 << 26)) return fail(WFST_EINVAL, "path_cap must lie in [0, 2^26]");
+    const uint64_t path_cap = c.path_cap ? (uint64_t)c.path_cap : (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
     HIP_TRY(hipSetDevice(g->device));
     wfst_decoder_s *d = new wfst_decoder_s();
     d->g = g;
@@ -364,8 +376,12 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&w.wlog, L * arena);
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
+    A(&d->d_plan, L * kPlanFields);
     if (r != WFST_OK) { delete d; return r; }
-    w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths;
+    w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
+    w.round_base = 0;
+    d->chan_open.assign(L, 0);
+    d->last_len.assign(L, -1);
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
     if (e == hipSuccess) e = hipMemcpy(d->d_work, &w, sizeof(Work), hipMemcpyHostToDevice);
@@ -373,6 +389,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_plan, 4 * (L * kPlanFields + 1), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipMemset(d->d_plan, 0, 4 * L * kPlanFields);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) { delete d; return hip_fail(e, "decoder workspace"); }
@@ -458,6 +476,40 @@ static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)
     return WFST_OK;
 }
 
+// Round base held by the device-side Work (a decode runs with 0).
+static int set_round_base(wfst_decoder_s *d, uint32_t v, hipStream_t s)
+{
+    if (d->dev_round_base == v) return WFST_OK;
+    uint32_t *h = (uint32_t *)(d->h_plan + (size_t)d->cfg.max_lanes * kPlanFields);
+    *h = v;
+    HIP_TRY(hipMemcpyAsync((char *)d->d_work + offsetof(Work, round_base), h, 4, hipMemcpyHostToDevice, s));
+    d->dev_round_base = v;
+    return WFST_OK;
+}
+
+// Copies result block `lane` (already in h_res) to output row j.
+static void copy_result(const wfst_decoder_s *d, int lane, int j, int32_t *out_words, int32_t words_cap,
+                        int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
+                        float *out_scores, int32_t *out_meta)
+{
+    const int32_t *R = d->h_res + (size_t)d->w.res_stride * (size_t)lane;
+    const int32_t *arcs = R + kResHeader;
+    const int32_t *words = arcs + d->w.path_cap;
+    const int32_t alen = R[kResArcLen], wlen = R[kResWordLen];
+    const int32_t astored = std::min<int32_t>(alen, (int32_t)d->w.path_cap);
+    out_meta[3 * j + 0] = R[kResOk];
+    out_meta[3 * j + 1] = R[kResReached];
+    out_meta[3 * j + 2] = R[kResOverflow];
+    uint32_t sb = (uint32_t)R[kResScore];
+    float sc;
+    std::memcpy(&sc, &sb, 4);
+    out_scores[j] = sc;
+    out_arc_lens[j] = alen;
+    out_word_lens[j] = wlen;
+    if (arcs_cap > 0) std::memcpy(out_arcs + (size_t)j * arcs_cap, arcs, 4 * (size_t)std::min(astored, arcs_cap));
+    if (words_cap > 0) std::memcpy(out_words + (size_t)j * words_cap, words, 4 * (size_t)std::min(wlen, words_cap));
+}
+
 extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
                            const int32_t *lengths_host, void *stream, int32_t *out_words, int32_t words_cap,
                            int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
@@ -480,9 +532,12 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     if (maxlen > 0 && !log_prob) return fail(WFST_EINVAL, "log_prob is null");
 
     std::lock_guard<std::mutex> lock(d->mu);
+    if (d->open_streams > 0) return fail(WFST_EINVAL, "the decoder has open streams (release them first)");
     HIP_TRY(hipSetDevice(d->g->device));
     hipStream_t s = (hipStream_t)stream;
     const size_t L = (size_t)c.max_lanes;
+    int rc0 = set_round_base(d, 0, s);
+    if (rc0 != WFST_OK) return rc0;
     LpDesc *hd = (LpDesc *)d->h_in;
     hd->base = log_prob;
     hd->stride_t = V;
@@ -510,31 +565,246 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
         d->last_steps = steps;
     }
+    // later stream sequences number their rounds on from this decode's (its
+    // entries are still in the table)
+    d->round_next = (uint64_t)(d->last_steps + 1) * (uint64_t)(1 + d->passes);
     d->last_profiled = d->prof_on;
     const size_t rs = d->w.res_stride;
     HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
 
-    d->last_B = B;
-    d->last_len.assign(lengths_host, lengths_host + B);
-    for (int32_t b = 0; b < B; ++b) {
-        const int32_t *R = d->h_res + rs * (size_t)b;
-        const int32_t *arcs = R + kResHeader;
-        const int32_t *words = arcs + d->w.path_cap;
-        const int32_t alen = R[kResArcLen], wlen = R[kResWordLen];
-        const int32_t astored = std::min<int32_t>(alen, (int32_t)d->w.path_cap);
-        out_meta[3 * b + 0] = R[kResOk];
-        out_meta[3 * b + 1] = R[kResReached];
-        out_meta[3 * b + 2] = R[kResOverflow];
-        uint32_t sb = (uint32_t)R[kResScore];
-        float sc;
-        std::memcpy(&sc, &sb, 4);
-        out_scores[b] = sc;
-        out_arc_lens[b] = alen;
-        out_word_lens[b] = wlen;
-        if (arcs_cap > 0) std::memcpy(out_arcs + (size_t)b * arcs_cap, arcs, 4 * (size_t)std::min(astored, arcs_cap));
-        if (words_cap > 0) std::memcpy(out_words + (size_t)b * words_cap, words, 4 * (size_t)std::min(wlen, words_cap));
+    d->last_len.assign(L, -1);
+    for (int32_t b = 0; b < B; ++b) d->last_len[(size_t)b] = lengths_host[b];
+    for (int32_t b = 0; b < B; ++b)
+        copy_result(d, b, b, out_words, words_cap, out_word_lens, out_arcs, arcs_cap, out_arc_lens, out_scores, out_meta);
+    return WFST_OK;
+}
+
+// ----------------------------------------------------------------- streams
+
+enum { kSeqOpen = 0, kSeqAdvance, kSeqFinish };
+
+// Queues one stream sequence (plan already in d_plan): records cleared, plan
+// applied, then the start closure (open), the final class (finish) or the row
+// maxima (advance), `steps` steps, the commit and the wanted results. Its
+// recombination rounds continue the count of earlier sequences, with the table
+// cleared before the epoch wraps.
+static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStream_t s)
+{
+    hipError_t e;
+    d->ev_used = 0;
+    const uint64_t base = d->round_next;
+    auto wrap = [&](int t, int k) -> hipError_t {
+        if (!d->w.epochs) return hipSuccess;   // (a captured sequence has no wrap: see stream_wraps)
+        const uint64_t q = base + (uint64_t)((long long)(t + 1) * (1 + d->passes) + k);
+        if (q % d->w.epoch_period != 0) return hipSuccess;
+        return launch(d, kKClear, t, 1, s);
+    };
+    if ((e = launch(d, kKClear, 0, 2, s)) != hipSuccess) return e;
+    if ((e = launch(d, kKStreamBegin, 0, 0, s)) != hipSuccess) return e;
+    if (kind == kSeqOpen) {
+        for (int k = 1; k <= d->passes; ++k) {
+            if ((e = wrap(-1, k)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
+        }
     }
+    if (kind == kSeqFinish && (e = launch(d, kKReclass, 0, 0, s)) != hipSuccess) return e;
+    if (kind == kSeqAdvance && steps > 0 && (e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
+    for (int t = 0; t < steps; ++t) {
+        if ((e = wrap(t, 0)) != hipSuccess) return e;
+        if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
+        if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
+        if (kind != kSeqAdvance) continue;
+        for (int k = 1; k <= d->passes; ++k) {
+            if ((e = wrap(t, k)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
+            if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
+        }
+    }
+    if ((e = launch(d, kKStreamEnd, 0, 0, s)) != hipSuccess) return e;
+    if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
+// Recombination rounds a stream sequence uses.
+static uint64_t stream_rounds(const wfst_decoder_s *d, int kind, int steps)
+{
+    return (uint64_t)((kind == kSeqOpen ? 0 : steps) + 1) * (uint64_t)(1 + d->passes);
+}
+
+// Whether the sequence's rounds pass an epoch wrap (then it clears the table
+// before that round, and runs as plain launches).
+static bool stream_wraps(const wfst_decoder_s *d, int kind, int steps)
+{
+    if (!d->w.epochs) return false;
+    const uint64_t P = d->w.epoch_period, b = d->round_next;
+    return (b + stream_rounds(d, kind, steps) - 1) / P != b / P;
+}
+
+// Runs a stream sequence with the plan in h_plan and waits for it; copies the
+// result blocks of `lanes` (the lanes whose result is wanted) to h_res. With
+// use_graphs the sequence replays a graph captured once per (kind, steps).
+static int run_stream(wfst_decoder_s *d, int kind, int steps, hipStream_t s, const std::vector<int> &lanes)
+{
+    const size_t L = (size_t)d->cfg.max_lanes;
+    const uint32_t rb = d->w.epochs ? (uint32_t)(d->round_next % d->w.epoch_period) : 0u;
+    int rc = set_round_base(d, rb, s);
+    if (rc != WFST_OK) return rc;
+    HIP_TRY(hipMemcpyAsync(d->d_plan, d->h_plan, 4 * L * kPlanFields, hipMemcpyHostToDevice, s));
+    if (d->cfg.use_graphs && !d->prof_on && !stream_wraps(d, kind, steps)) {
+        const int key = steps * 4 + kind;
+        auto it = d->stream_graphs.find(key);
+        hipGraphExec_t ex = nullptr;
+        if (it != d->stream_graphs.end()) {
+            ex = it->second;
+        } else {
+            hipGraph_t graph = nullptr;
+            HIP_TRY(hipStreamBeginCapture(d->cap_stream, hipStreamCaptureModeThreadLocal));
+            hipError_t e = enqueue_stream(d, kind, steps, d->cap_stream);
+            hipError_t e2 = hipStreamEndCapture(d->cap_stream, &graph);
+            if (e != hipSuccess) { if (graph) (void)hipGraphDestroy(graph); return hip_fail(e, "kernel launch during capture"); }
+            if (e2 != hipSuccess) return hip_fail(e2, "hipStreamEndCapture");
+            e = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(graph);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+            d->stream_graphs[key] = ex;
+        }
+        HIP_TRY(hipGraphLaunch(ex, s));
+    } else {
+        hipError_t e = enqueue_stream(d, kind, steps, s);
+        if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    }
+    if (!lanes.empty()) {
+        // one copy over the span of wanted lanes
+        const size_t rs = d->w.res_stride;
+        const int lo = *std::min_element(lanes.begin(), lanes.end());
+        const int hi = *std::max_element(lanes.begin(), lanes.end());
+        HIP_TRY(hipMemcpyAsync(d->h_res + rs * (size_t)lo, d->w.res + rs * (size_t)lo, 4 * rs * (size_t)(hi - lo + 1),
+                               hipMemcpyDeviceToHost, s));
+    }
+    HIP_TRY(hipStreamSynchronize(s));
+    d->round_next += stream_rounds(d, kind, steps);
+    d->last_profiled = d->prof_on;
+    d->last_steps = steps;
+    return WFST_OK;
+}
+
+static void plan_clear(wfst_decoder_s *d)
+{
+    std::memset(d->h_plan, 0, 4 * (size_t)d->cfg.max_lanes * kPlanFields);   // kCmdPark
+}
+
+extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel)
+{
+    if (!d || !channel) return fail(WFST_EINVAL, "decoder or channel is null");
+    *channel = -1;
+    std::lock_guard<std::mutex> lock(d->mu);
+    int lane = -1;
+    for (int L = 0; L < d->cfg.max_lanes; ++L)
+        if (!d->chan_open[(size_t)L]) { lane = L; break; }
+    if (lane < 0) return WFST_OK;   // every lane holds a stream
+    HIP_TRY(hipSetDevice(d->g->device));
+    plan_clear(d);
+    d->h_plan[lane * kPlanFields + kPlanCmd] = kCmdOpen;
+    int rc = run_stream(d, kSeqOpen, 0, (hipStream_t)stream, {});
+    if (rc != WFST_OK) return rc;
+    d->last_len.assign((size_t)d->cfg.max_lanes, -1);
+    d->last_len[(size_t)lane] = 0;
+    d->chan_open[(size_t)lane] = 1;
+    d->open_streams += 1;
+    *channel = lane;
+    return WFST_OK;
+}
+
+extern "C" int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int32_t C, const void *log_prob,
+                                  int32_t T, int32_t V, const int32_t *lengths_host, void *stream,
+                                  int32_t want_partial, int32_t *out_words, int32_t words_cap,
+                                  int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap,
+                                  int32_t *out_arc_lens, float *out_scores, int32_t *out_meta)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    const wfst_decoder_config &c = d->cfg;
+    if (C < 1 || C > c.max_lanes || !channels || !lengths_host) return fail(WFST_EINVAL, "C must lie in [1, max_lanes] with channels and lengths given");
+    if (T < 0 || T > c.max_frames) return fail(WFST_EINVAL, "T (chunk frames) must lie in [0, max_frames]");
+    if (V != d->g->vocab) return fail(WFST_EINVAL, "V differs from the graph's vocab_size");
+    if (want_partial && (!out_word_lens || !out_arc_lens || !out_scores || !out_meta ||
+                         words_cap < 0 || arcs_cap < 0 || (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs)))
+        return fail(WFST_EINVAL, "want_partial needs the output buffers");
+    std::lock_guard<std::mutex> lock(d->mu);
+    std::vector<uint8_t> seen((size_t)c.max_lanes, 0);
+    int32_t steps = 0;
+    for (int32_t j = 0; j < C; ++j) {
+        const int32_t ch = channels[j];
+        if (ch < 0 || ch >= c.max_lanes || !d->chan_open[(size_t)ch]) return fail(WFST_EINVAL, "a channel is not an open stream");
+        if (seen[(size_t)ch]) return fail(WFST_EINVAL, "a channel appears twice");
+        seen[(size_t)ch] = 1;
+        if (lengths_host[j] < 0 || lengths_host[j] > T) return fail(WFST_EINVAL, "lengths must lie in [0, T]");
+        steps = std::max(steps, lengths_host[j]);
+    }
+    if (steps > 0 && !log_prob) return fail(WFST_EINVAL, "log_prob is null");
+    HIP_TRY(hipSetDevice(d->g->device));
+    hipStream_t s = (hipStream_t)stream;
+    LpDesc *hd = (LpDesc *)d->h_in;
+    hd->base = log_prob;
+    hd->stride_t = V;
+    hd->stride_b = (long long)T * V;
+    hd->B = C;
+    hd->dtype = c.lp_dtype;
+    HIP_TRY(hipMemcpyAsync(d->d_desc, hd, sizeof(LpDesc), hipMemcpyHostToDevice, s));
+    plan_clear(d);
+    std::vector<int> lanes;
+    for (int32_t j = 0; j < C; ++j) {
+        int32_t *pl = d->h_plan + channels[j] * kPlanFields;
+        pl[kPlanCmd] = kCmdAdvance;
+        pl[kPlanLen] = lengths_host[j];
+        pl[kPlanRow] = j;
+        pl[kPlanWant] = want_partial ? 1 : 0;
+        if (want_partial) lanes.push_back(channels[j]);
+    }
+    int rc = run_stream(d, kSeqAdvance, steps, s, lanes);
+    if (rc != WFST_OK) return rc;
+    d->last_len.assign((size_t)c.max_lanes, -1);
+    for (int32_t j = 0; j < C; ++j) d->last_len[(size_t)channels[j]] = lengths_host[j];
+    if (want_partial)
+        for (int32_t j = 0; j < C; ++j)
+            copy_result(d, channels[j], j, out_words, words_cap, out_word_lens, out_arcs, arcs_cap, out_arc_lens,
+                        out_scores, out_meta);
+    return WFST_OK;
+}
+
+extern "C" int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_t *out_words,
+                                    int32_t words_cap, int32_t *out_word_len, int32_t *out_arcs, int32_t arcs_cap,
+                                    int32_t *out_arc_len, float *out_score, int32_t *out_meta)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    if (!out_word_len || !out_arc_len || !out_score || !out_meta || words_cap < 0 || arcs_cap < 0 ||
+        (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs))
+        return fail(WFST_EINVAL, "an output pointer is null");
+    std::lock_guard<std::mutex> lock(d->mu);
+    if (channel < 0 || channel >= d->cfg.max_lanes || !d->chan_open[(size_t)channel])
+        return fail(WFST_EINVAL, "channel is not an open stream");
+    HIP_TRY(hipSetDevice(d->g->device));
+    plan_clear(d);
+    d->h_plan[channel * kPlanFields + kPlanCmd] = kCmdFinish;
+    int rc = run_stream(d, kSeqFinish, 1, (hipStream_t)stream, {channel});
+    if (rc != WFST_OK) return rc;
+    d->last_len.assign((size_t)d->cfg.max_lanes, -1);
+    d->last_len[(size_t)channel] = 0;
+    copy_result(d, channel, 0, out_words, words_cap, out_word_len, out_arcs, arcs_cap, out_arc_len, out_score, out_meta);
+    return WFST_OK;
+}
+
+extern "C" int wfst_release_stream(wfst_decoder_t d, int32_t channel)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    std::lock_guard<std::mutex> lock(d->mu);
+    if (channel < 0 || channel >= d->cfg.max_lanes || !d->chan_open[(size_t)channel])
+        return fail(WFST_EINVAL, "channel is not an open stream");
+    d->chan_open[(size_t)channel] = 0;
+    d->open_streams -= 1;
     return WFST_OK;
 }
 
@@ -552,12 +822,15 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
     if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
     std::lock_guard<std::mutex> lock(d->mu);
     int64_t v[14] = {0};
-    if (d->last_B > 0) {
+    bool any = false;
+    for (int32_t x : d->last_len) any |= x >= 0;
+    if (any) {
         std::vector<uint32_t> rec;
         int rc = fetch_records(d, &rec);
         if (rc != WFST_OK) return rc;
         const size_t per = (size_t)(d->cfg.max_frames + 2);
-        for (int b = 0; b < d->last_B; ++b) {
+        for (int b = 0; b < d->cfg.max_lanes; ++b) {
+            if (d->last_len[(size_t)b] < 0) continue;
             for (size_t r = 0; r < per; ++r) {
                 const uint32_t *x = rec.data() + ((size_t)b * per + r) * kStepFields;
                 v[0] += x[kRecArcs]; v[1] += x[kRecAdmitted]; v[2] += x[kRecDistinct]; v[3] += x[kRecN];
@@ -570,7 +843,8 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
         }
         std::vector<LaneCtl> ctl((size_t)d->cfg.max_lanes);
         HIP_TRY(hipMemcpy(ctl.data(), d->ctl, sizeof(LaneCtl) * ctl.size(), hipMemcpyDeviceToHost));
-        for (int b = 0; b < d->last_B; ++b) v[8] += ctl[(size_t)b].log_cursor;
+        for (int b = 0; b < d->cfg.max_lanes; ++b)
+            if (d->last_len[(size_t)b] >= 0) v[8] += ctl[(size_t)b].log_cursor;
     }
     v[9] = d->last_steps;
     v[11] = (int64_t)(d->bytes + d->g->bytes);
@@ -582,12 +856,14 @@ extern "C" int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *
 {
     if (!d || !out || steps_cap < 0) return fail(WFST_EINVAL, "bad arguments");
     std::lock_guard<std::mutex> lock(d->mu);
-    if (lane < 0 || lane >= d->last_B) return fail(WFST_EINVAL, "lane outside the last decode's batch");
+    if (lane < 0 || lane >= d->cfg.max_lanes || d->last_len[(size_t)lane] < 0)
+        return fail(WFST_EINVAL, "lane not in the last decode or stream call");
     std::vector<uint32_t> rec;
     int rc = fetch_records(d, &rec);
     if (rc != WFST_OK) return rc;
-    const int32_t *R = d->h_res + (size_t)d->w.res_stride * (size_t)lane;
-    const int32_t last = R[7];
+    // the lane's last step of the call (its result header on the device)
+    int32_t last = -1;
+    HIP_TRY(hipMemcpy(&last, d->w.res + (size_t)d->w.res_stride * (size_t)lane + 7, 4, hipMemcpyDeviceToHost));
     const size_t per = (size_t)(d->cfg.max_frames + 2);
     const int32_t nrec = std::min<int32_t>(steps_cap, d->last_len[(size_t)lane] + 2);
     for (int32_t r = 0; r < nrec; ++r) {

@@ -79,17 +79,26 @@ struct alignas(128) LaneCtl {
     uint32_t overflow;         // kOvf* bits
     int32_t reached_final;
     float beam[2];             // b_t by step parity (beam[1] = search beam before step 0)
+    uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
+                               //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
+    unsigned long long final_key;  // best final candidate key of the final step
     float cutoff;              // cutoff of the latest real step (closure passes use it)
     int32_t final_entry;       // winners-log entry of the result (-1 none)
-    unsigned long long final_key;  // best final candidate key of the final step
     float final_score;
     uint32_t dirty;            // recombination table may hold stale entries (claims overflow)
     int32_t last_step;         // last step this lane ran
     int32_t phase_final;       // phase code of the lane's last step
     uint32_t log_open;         // 1: the last compaction's entries (its token count) are not yet
                                //   in log_cursor; the next kernel that reads the log adds them
-    uint32_t front_base[2];    // winners-log base of the compaction that built the frontier of each
-                               //   parity (0xFFFFFFFF: the start frontier, whose token has entry -1)
+    // Steps of one launch sequence (a decode, a stream's chunk or its end) are
+    // numbered t = 0, 1, ... in every lane; a lane's own step is base + t, and the
+    // frontier feeding it has parity (base + t) & 1.
+    int32_t base;              // the lane's steps before this sequence (0 for a decode)
+    int32_t win;               // the lane runs steps t < win of this sequence (-1: parked)
+    int32_t lp_row;            // batch row of the lane's frames in this sequence's log_prob (-1 none)
+    int32_t frames;            // a stream's frames so far
+    int32_t want;              // result wanted after the sequence: 0 none, 1 the lane's result,
+                               //   2 the partial hypothesis (best current token)
     alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
                                              //   step's class) << 32
     alignas(128) uint32_t nclaims[2];        // candidate-list length of the slot pass by step parity
@@ -124,6 +133,7 @@ struct Work {
     int32_t epochs;           // table keys carry the round's epoch: entries are never cleared singly
     uint32_t arc_bits;        // arc id bits of an epoch-tagged key (the epoch takes 32 - arc_bits)
     uint32_t epoch_period;    // rounds between full clears of the table
+    uint32_t round_base;      // rounds of earlier sequences since the table was last cleared
     // search settings
     float beam;
     int32_t min_active, max_active, allow_partial, eps_iterations;
@@ -159,12 +169,17 @@ struct Work {
     int2 *wlog;               // [L][arena] winners log {prev entry, arc}
     int32_t *res;             // [L][res_stride] results
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]
+    const int32_t *plan;      // [L][kPlanFields] stream commands of the next sequence
 };
+
+// Per-lane stream command of a launch sequence (written by the host).
+enum : int32_t { kPlanCmd = 0, kPlanLen, kPlanRow, kPlanWant, kPlanFields = 4 };
+enum : int32_t { kCmdPark = 0, kCmdOpen = 1, kCmdAdvance = 2, kCmdFinish = 3 };
 
 // Kernels of a decode, in launch order within a step (ids match WFST_K_*).
 enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
-    kKEpsApply, kKBacktrack, kKCount
+    kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -56,11 +56,12 @@ __device__ __forceinline__ unsigned long long cand_key(float score, int32_t arc)
 }
 
 // Epoch of recombination round (t, k): step t's slot pass is k = 0, closure
-// pass k after it is k (t = -1: the start closure). 1..epoch_period; 0 marks an
-// empty entry. Kernels compute it once (the modulus is not a constant).
+// pass k after it is k (t = -1: the start closure), counted on from the rounds
+// of earlier sequences since the last clear. 1..epoch_period; 0 marks an empty
+// entry. Kernels compute it once (the modulus is not a constant).
 __device__ __forceinline__ uint32_t round_epoch(const Work &w, int t, int k)
 {
-    const uint32_t q = (uint32_t)((t + 1) * (1 + w.eps_iterations) + k);
+    const uint32_t q = w.round_base + (uint32_t)((t + 1) * (1 + w.eps_iterations) + k);
     return 1u + q % w.epoch_period;
 }
 
@@ -116,13 +117,54 @@ __device__ __forceinline__ uint32_t *step_rec(const Work &w, int L, int t)
     return w.steps + ((size_t)L * (size_t)(w.max_frames + 2) + (size_t)(t + 1)) * kStepFields;
 }
 
-// Phase of lane c at step t: real for t < T, final at t == T.
+// Phase of lane c at step t of the sequence: real for t < T, final at t == T,
+// none outside the lane's window of this sequence.
 __device__ __forceinline__ int lane_phase(const LaneCtl &c, int t)
 {
-    if (c.status != kActive) return kPhNone;
+    if (c.status != kActive || t >= c.win) return kPhNone;
     if (t < c.T) return kPhReal;
     if (t == c.T) return kPhFinal;
     return kPhNone;
+}
+
+// Parity of the frontier that feeds lane c's step t of the sequence.
+__device__ __forceinline__ int lane_par(const LaneCtl &c, int t) { return (c.base + t) & 1; }
+
+// Buffer of parity p (wavefront-uniform) out of a pair: a select between the two
+// pointers, which a kernel loads once, instead of an indexed load per use.
+template <typename T>
+__device__ __forceinline__ T *pick(T *const (&a)[2], int p) { return p ? a[1] : a[0]; }
+
+// Both parities of a per-lane pair in one load, then the one of parity p: no
+// load of a kernel's prologue waits for the lane's parity.
+__device__ __forceinline__ unsigned long long pair_at(const unsigned long long (&a)[2], int p)
+{
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(a);
+    return p ? v.y : v.x;
+}
+__device__ __forceinline__ uint32_t pair_at(const uint32_t (&a)[2], int p)
+{
+    const uint2 v = *reinterpret_cast<const uint2 *>(a);
+    return p ? v.y : v.x;
+}
+__device__ __forceinline__ float pair_at(const float (&a)[2], int p)
+{
+    const float2 v = *reinterpret_cast<const float2 *>(a);
+    return p ? v.y : v.x;
+}
+
+// A lane's parity from the LDS table, as a wavefront-uniform value.
+__device__ __forceinline__ int upar(const int32_t *par, int L) { return __builtin_amdgcn_readfirstlane(par[L]); }
+
+// Commits the compaction of step t that no closure followed: its token count n
+// is its number of winners and of winners-log entries. Run by one thread of the
+// next kernel that reads the log.
+__device__ __forceinline__ void commit_log(const Work &w, LaneCtl &c, int L, int t, uint32_t n)
+{
+    if (!c.log_open) return;
+    c.log_cursor += n;
+    step_rec(w, L, t)[kRecDistinct] = n;
+    c.log_open = 0u;
 }
 
 // Per-workgroup view of the lanes, built by wavefront 0 of every workgroup.
@@ -135,6 +177,10 @@ struct LaneTab {
     float f0[kMaxLanes];           // max log-prob of the lane's row (0 on the final step)
     float f1[kMaxLanes];           // cutoff, or the running max
     uint32_t fb[kMaxLanes];        // winners-log base of the sources' compaction
+    int32_t par[kMaxLanes];        // parity of the frontier the kernel reads (k_max, k_finalize)
+                                   //   or closes (closure passes)
+    int32_t row[kMaxLanes];        // batch row of the lane's log-probs (k_max, k_finalize)
+    int32_t win[kMaxLanes];        // the lane's window of the sequence (k_finalize)
 };
 
 __device__ __forceinline__ void tab_publish(LaneTab &tab, int nl, uint32_t units)
@@ -274,12 +320,28 @@ __device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, ui
 // tables — all of them with epoch-tagged keys, else those of lanes whose
 // candidate list overflowed in an earlier decode (the targeted clears cannot
 // see those entries). k = 1: clears every table (before the epoch counter
-// wraps).
+// wraps). k = 2 (start of a stream sequence): the records of the lanes the
+// plan names, and without epochs the table of a lane being opened after an
+// overflow.
 __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, int k)
 {
     const Work &w = *wp;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k == 2) {
+        const size_t per = (size_t)(w.max_frames + 2) * kStepFields;
+        const size_t ns = (size_t)w.num_states;
+        for (int L = 0; L < w.max_lanes; ++L) {
+            const int cmd = w.plan[L * kPlanFields + kPlanCmd];
+            if (cmd == kCmdPark) continue;
+            for (size_t i = tid; i < per; i += stride) w.steps[(size_t)L * per + i] = 0u;
+            if (cmd == kCmdOpen && !w.epochs && w.ctl[L].dirty) {
+                unsigned long long *tbl = w.best + (size_t)L * ns;
+                for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
+            }
+        }
+        return;
+    }
     if (k == 0) {
         const size_t nrec = (size_t)w.max_lanes * (size_t)(w.max_frames + 2) * kStepFields;
         for (size_t i = tid; i < nrec; i += stride) w.steps[i] = 0u;
@@ -309,17 +371,13 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
 // ----------------------------------------------------------------- k_init
 // Lane control blocks and the start token (page section 2: InitKernel resets all
 // state, so a decode is idempotent).
-__global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
+// Fresh search state of lane L with T frames (T = INT32_MAX: a stream, whose end
+// is not known yet): control block and start token at parity 0.
+__device__ void init_lane(const Work &w, int L, int T)
 {
-    const Work &w = *wp;
-    const int L = (int)threadIdx.x;
-    if (L >= w.max_lanes) return;
-    const LpDesc d = *w.lp;
     LaneCtl &c = w.ctl[L];
-    const bool on = L < d.B;
-    const int T = on ? w.lengths[L] : 0;
     c.T = T;
-    c.status = on ? kActive : kDone;
+    c.status = kActive;
     c.overflow = 0u;
     c.reached_final = 0;
     c.beam[0] = w.beam;
@@ -339,14 +397,14 @@ __global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
     c.nclaims_eps[1] = 0u;
     c.nchanged[0] = 0u;
     c.nchanged[1] = 0u;
-    c.dirty = 0u;
     c.log_open = 0u;
     c.front_base[0] = 0xFFFFFFFFu;
     c.front_base[1] = 0xFFFFFFFFu;
     c.last_step = -1;
     c.phase_final = kPhNone;
+    c.base = 0;
+    c.frames = 0;
     c.cnt[1] = 0ull;
-    if (!on) { c.cnt[0] = 0ull; return; }
     const int32_t s = w.start_state;
     const StateInfo si = w.sinfo[s];
     int32_t abeg; uint32_t deg; float ub;
@@ -365,6 +423,36 @@ __global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
     c.cnt[0] = 1ull | ((unsigned long long)deg << 32);
 }
 
+// Start of a decode: lanes of the batch (their lengths) from their start state,
+// the others idle.
+__global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    const LpDesc d = *w.lp;
+    LaneCtl &c = w.ctl[L];
+    const bool on = L < d.B;
+    c.dirty = 0u;        // the clear at the start of the decode has run
+    c.win = 0x7FFFFFFF;
+    c.lp_row = on ? L : -1;
+    c.want = on ? 1 : 0;
+    if (on) {
+        init_lane(w, L, w.lengths[L]);
+    } else {
+        c.T = 0;
+        c.status = kDone;
+        c.overflow = 0u;
+        c.final_entry = -1;
+        c.log_open = 0u;
+        c.base = 0;
+        c.cnt[0] = 0ull;
+        c.cnt[1] = 0ull;
+        c.last_step = -1;
+        c.phase_final = kPhNone;
+    }
+}
+
 // ---------------------------------------------------------------- k_lpmax
 // Max log-prob of every (lane, frame) row, for the upper-bound skip.
 template <typename LPT>
@@ -373,12 +461,14 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(const Work *__restrict__ wp)
     const Work &w = *wp;
     const LpDesc d = *w.lp;
     const int wpb = kBlock / kWave;
-    const long long rows = (long long)d.B * w.max_frames;
+    const long long rows = (long long)w.max_lanes * w.max_frames;
     for (long long r = (long long)blockIdx.x * wpb + threadIdx.x / kWave; r < rows;
          r += (long long)gridDim.x * wpb) {
         const int L = (int)(r / w.max_frames), t = (int)(r % w.max_frames);
-        if (t >= w.lengths[L]) continue;
-        const LPT *row = (const LPT *)d.base + (long long)L * d.stride_b + (long long)t * d.stride_t;
+        const LaneCtl &c = w.ctl[L];
+        // the real steps of the sequence that read a row of this input
+        if (c.status != kActive || c.lp_row < 0 || t >= c.T || t >= c.win) continue;
+        const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)t * d.stride_t;
         float m = -__builtin_inff();
         for (int v = wlane(); v < w.vocab; v += kWave) m = fmaxf(m, lp_at(row, (uint32_t)v));
         m = wave_max(m);
@@ -419,17 +509,17 @@ struct LaneView {
 __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab, int t, const LpDesc &d, int L)
 {
     LaneView v;
-    const int p = t & 1;
+    const int p = upar(tab.par, L);
     const size_t qo = (size_t)L * w.frontier_cap;
     v.L = L;
     v.ph = tab.ph[L];
     v.n = tab.n[L];
     v.arcs = tab.arcs[L];
-    v.off = w.tok_off[p] + qo;
-    v.abeg = w.tok_abeg[p] + qo;
-    v.score = w.tok_score[p] + qo;
-    v.ubv = w.tok_ub[p] + qo;
-    const long long eoff = (long long)L * d.stride_b + (long long)t * d.stride_t;
+    v.off = pick(w.tok_off, p) + qo;
+    v.abeg = pick(w.tok_abeg, p) + qo;
+    v.score = pick(w.tok_score, p) + qo;
+    v.ubv = pick(w.tok_ub, p) + qo;
+    const long long eoff = (long long)tab.row[L] * d.stride_b + (long long)t * d.stride_t;
     v.row = (v.ph == kPhReal)
         ? (const void *)((const char *)d.base + eoff * (w.lp_dtype == 1 ? 2 : 4)) : nullptr;
     v.lpm = tab.f0[L];
@@ -597,16 +687,16 @@ template <typename LPT>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            uint32_t s, uint32_t s_end, ClaimBuf *cbuf)
 {
-    const int p = t & 1;
     const int nl = w.max_lanes;
     const uint32_t ep = round_epoch(w, t, 0);
     uint32_t cb_n = 0;
     while (s < s_end) {
         const int L = find_lane(tab.base, nl, s);
+        const int p = upar(tab.par, L);
         const uint32_t seg_end = min(s_end, tab.base[L + 1]);
         const LaneView v = lane_view(w, tab, t, d, L);
         LaneCtl &c = w.ctl[L];
-        uint32_t cur = w.strip_tok[p][(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
+        uint32_t cur = pick(w.strip_tok, p)[(size_t)L * w.strip_cap + (s - tab.base[L]) * kR];
         if (cur >= v.n) cur = 0;
         float run = ord2f(tab.fb[L]);
         const float b = tab.f1[L];
@@ -634,12 +724,13 @@ __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, in
 // Dynamic beam b_t of a lane (page section 3), every operation one fp32
 // rounding; n = frontier size entering the step. Every workgroup of the slot
 // pass computes it (the same value workgroup 0 stores).
-__device__ __forceinline__ float step_beam(const Work &w, const LaneCtl &c, int t, int ph, uint32_t n)
+// T = the lane's frames, bp = the beam of its previous step.
+__device__ __forceinline__ float step_beam(const Work &w, int T, float bp, int t, int ph, uint32_t n)
 {
     if (ph == kPhFinal) return 1e10f;
     int mina = w.min_active;
-    if (c.T - t <= 5 && w.max_active / 2 > mina) mina = w.max_active / 2;
-    const float bp = c.beam[(t & 1) ^ 1];
+    // a stream's T stays unbounded until it ends, so there this never applies
+    if ((long long)T - t <= 5 && w.max_active / 2 > mina) mina = w.max_active / 2;
     if ((long long)n > (long long)w.max_active) return __fmul_rn(fminf(bp, w.beam), 0.8f);
     if ((long long)n < (long long)mina) return __fmul_rn(fmaxf(bp, w.beam), 1.25f);
     return __fadd_rn(__fmul_rn(0.8f, bp), __fmul_rn(0.2f, w.beam));
@@ -651,21 +742,25 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
 {
     if (threadIdx.x >= kWave) return;
     const int L = (int)threadIdx.x;
-    const int p = t & 1;
     uint32_t units = 0;
     if (L < w.max_lanes) {
         const LaneCtl &c = w.ctl[L];
+        // every load first (none waits for another), then the decisions
+        const int p = lane_par(c, t);
         int ph = lane_phase(c, t);
-        const unsigned long long cn = c.cnt[p];
+        const unsigned long long cn = pair_at(c.cnt, p);
+        const uint32_t lbk = pair_at(c.lbkey, p);
+        const float bprev = pair_at(c.beam, p ^ 1);
+        const float lpmt = t < w.max_frames ? w.lpmax[(size_t)L * w.max_frames + t] : 0.0f;
         const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
         if (ph != kPhNone && (n > w.frontier_cap || arcs > w.strip_cap * (uint32_t)kWave)) ph = kPhNone;
         float lpm = 0.0f, b = 0.0f;
         uint32_t lb = kOrdNegInf;
-        if (ph == kPhReal) lpm = w.lpmax[(size_t)L * w.max_frames + t];
+        if (ph == kPhReal) lpm = lpmt;
         if (ph != kPhNone && n > 0u && arcs > 0u) {
             units = (arcs + kUnit - 1) / kUnit;
-            b = step_beam(w, c, t, ph, n);
-            if (ph == kPhReal) lb = c.lbkey[p];
+            b = step_beam(w, c.T, bprev, t, ph, n);
+            if (ph == kPhReal) lb = lbk;
         }
         tab.n[L] = n;
         tab.arcs[L] = arcs;
@@ -674,6 +769,8 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         tab.f0[L] = lpm;
         tab.f1[L] = b;
         tab.fb[L] = lb;
+        tab.par[L] = p;
+        tab.row[L] = c.lp_row;
     }
     tab_publish(tab, w.max_lanes, units);
 }
@@ -683,16 +780,10 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
 __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
 {
     LaneCtl &c = w.ctl[L];
-    const int p = t & 1;
-    const unsigned long long cn = c.cnt[p];
+    const int p = lane_par(c, t);
+    const unsigned long long cn = pair_at(c.cnt, p);
     const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
-    if (c.log_open) {
-        // the compaction of step t - 1 (no closure ran after it): its token
-        // count is its number of winners and of winners-log entries
-        c.log_cursor += n;
-        step_rec(w, L, t - 1)[kRecDistinct] = n;
-        c.log_open = 0u;
-    }
+    commit_log(w, c, L, t - 1, n);
     const int ph = lane_phase(c, t);
     if (ph == kPhNone) return;
     uint32_t *rec = step_rec(w, L, t);
@@ -702,7 +793,7 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
-    const float b = step_beam(w, c, t, ph, n);
+    const float b = step_beam(w, c.T, c.beam[p ^ 1], t, ph, n);
     c.beam[p] = b;
     rec[kRecBeam] = __float_as_uint(b);
     rec[kRecPhase] = ph;
@@ -776,7 +867,7 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
     const float end = ord2f((uint32_t)(fk >> 32));
     const int32_t arc = (int32_t)(0xFFFFFFFFu - (uint32_t)fk);
     const int32_t esrc = (uint32_t)stok < w.frontier_cap
-        ? w.tok_entry[p][(size_t)L * w.frontier_cap + stok] : -1;
+        ? pick(w.tok_entry, p)[(size_t)L * w.frontier_cap + stok] : -1;
     const uint32_t le = c.log_cursor;
     if (le < w.arena) {
         const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
@@ -795,14 +886,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
 {
     const uint32_t ep = round_epoch(w, t, 0);
     const LpDesc lpd = *w.lp;
-    const int p = t & 1, np = p ^ 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
             const int ph = lane_phase(c, t);
-            const uint32_t nc = c.nclaims[p];
+            const int p = lane_par(c, t);
+            const uint32_t nc = pair_at(c.nclaims, p);
+            const uint32_t mk = pair_at(c.maxkey, p);
+            const float bt = pair_at(c.beam, p);
+            const uint32_t fbase = pair_at(c.front_base, p);
             // candidates past claims_cap were never written: the lane cannot be
             // compacted (token and log capacity are checked per wavefront)
             const bool fits = nc <= w.claims_cap;
@@ -812,8 +906,11 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             tab.ph[L] = ph;
             tab.T[L] = c.T;
             tab.f0[L] = fits ? 1.0f : 0.0f;
-            tab.f1[L] = (ph != kPhNone) ? ord2f(c.maxkey[p]) - c.beam[p] : 0.0f;   // the exact cutoff
-            tab.fb[L] = c.front_base[p];
+            tab.f1[L] = (ph != kPhNone) ? ord2f(mk) - bt : 0.0f;   // the exact cutoff
+            tab.fb[L] = fbase;
+            tab.par[L] = p;
+            tab.row[L] = c.lp_row;
+            tab.win[L] = c.win;
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -823,6 +920,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
         const int ph = tab.ph[L];
+        const int p = tab.par[L], np = p ^ 1;
         const unsigned long long cn = c.cnt[p];
         if ((ph == kPhReal || ph == kPhFinal) && (uint32_t)cn > 0u && (uint32_t)(cn >> 32) > 0u) {
             // lanes with candidates: the exact maximum and the cutoff of the step
@@ -858,10 +956,11 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
     const uint32_t Q = w.frontier_cap;
     uint32_t u_beg, u_end;
     wave_share(total, &u_beg, &u_end);
-    int lb_lane = -1;
+    int lb_lane = -1, lb_np = 0;
     float lb_acc = -__builtin_inff();
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
+        const int p = upar(tab.par, L), np = p ^ 1;
         const uint32_t nc = tab.n[L];
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const bool valid = i < nc;
@@ -909,14 +1008,15 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                     // without epsilon arcs a token's entry is its compaction's base
                     // plus its position; the closure may give a token a fresh entry
                     const uint32_t fb = tab.fb[L];
-                    esrc = w.has_eps ? w.tok_entry[p][(size_t)L * Q + stok]
+                    esrc = w.has_eps ? pick(w.tok_entry, p)[(size_t)L * Q + stok]
                          : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
                     class_of(si, next_final, end, &abeg, &deg, &ub);
-                    if (!next_final && deg > 0u) {
+                    // (no bound past the sequence's window: its row is not in this input)
+                    if (!next_final && deg > 0u && t + 1 < tab.win[L]) {
                         // candidates of the next step through the state's
                         // largest-weight arcs, (score + weight) + lp as the
                         // maximum pass adds them (unused entries weigh -inf)
-                        const long long row = (long long)L * lpd.stride_b + (long long)(t + 1) * lpd.stride_t;
+                        const long long row = (long long)tab.row[L] * lpd.stride_b + (long long)(t + 1) * lpd.stride_t;
                         float lpk[kTopArcs];
                         if (w.lp_dtype == 1) {
                             const __half *r = (const __half *)lpd.base + row;
@@ -936,8 +1036,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         // lower bound of the next step's maximum (posted per lane after the
         // loop, so its log-prob load overlaps the allocation below)
         if (L != lb_lane) {
-            post_bound(w, lb_lane, np, lb_acc);
+            post_bound(w, lb_lane, lb_np, lb_acc);
             lb_lane = L;
+            lb_np = np;
             lb_acc = -__builtin_inff();
         }
         lb_acc = fmaxf(lb_acc, lbv);
@@ -971,18 +1072,18 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             const size_t q = (size_t)L * Q + pi;
             const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
             w.wlog[e] = make_int2(esrc, arc);
-            w.tok_state[np][q] = dst;
-            w.tok_score[np][q] = end;
-            w.tok_entry[np][q] = e;
-            w.tok_last[np][q] = arc;
-            w.tok_off[np][q] = a0 + dpre;
-            w.tok_abeg[np][q] = abeg;
-            w.tok_ub[np][q] = ub;
-            if (w.has_eps) w.pos[np][(size_t)L * w.num_states + dst] = (int32_t)pi;
+            pick(w.tok_state, np)[q] = dst;
+            pick(w.tok_score, np)[q] = end;
+            pick(w.tok_entry, np)[q] = e;
+            pick(w.tok_last, np)[q] = arc;
+            pick(w.tok_off, np)[q] = a0 + dpre;
+            pick(w.tok_abeg, np)[q] = abeg;
+            pick(w.tok_ub, np)[q] = ub;
+            if (w.has_eps) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
         }
-        write_strips(w.strip_tok[np] + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
+        write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
-    post_bound(w, lb_lane, np, lb_acc);
+    post_bound(w, lb_lane, lb_np, lb_acc);
 }
 
 __global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp, int t)
@@ -994,7 +1095,7 @@ __global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp
 
 // ---------------------------------------------------------- epsilon closure
 // Pass k of the closure that follows step t (t = -1: the start frontier). The
-// frontier being closed has parity fp = (t + 1) & 1 and feeds step t + 1.
+// frontier being closed feeds step t + 1 (parity lane_par(c, t + 1)).
 
 // A lane whose winners log or frontier overflowed holds tokens that were
 // counted but never written; it is skipped until the next step retires it.
@@ -1003,23 +1104,22 @@ __global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp
 // so an active lane never holds a counted but unwritten token.
 __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
 {
-    return c.status == kActive && (t < 0 || t < c.T);
+    return c.status == kActive && t < c.win && (t < 0 || t < c.T);
 }
 
 __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
     const uint32_t ep = round_epoch(w, t, k);
-    const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
+            const int fp = lane_par(c, t + 1);
+            tab.par[L] = fp;
             uint32_t ns = 0;
-            if (closure_lane(c, t)) {
-                const uint32_t n = (uint32_t)c.cnt[fp];
-                if (n <= w.frontier_cap) ns = (k == 1) ? n : c.nchanged[k & 1];
-            }
+            const uint32_t n = (uint32_t)pair_at(c.cnt, fp), nch = c.nchanged[k & 1];
+            if (closure_lane(c, t) && n <= w.frontier_cap) ns = (k == 1) ? n : nch;
             units = (ns + kWave - 1) / kWave;
             tab.n[L] = ns;
             tab.f1[L] = c.cutoff;
@@ -1030,14 +1130,8 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
-        if (k == 1 && c.log_open) {
-            // the compaction before this closure: its token count (no closure
-            // token added yet) is its number of winners and of log entries
-            const uint32_t nd = (uint32_t)c.cnt[fp];
-            c.log_cursor += nd;
-            step_rec(w, L, t)[kRecDistinct] = nd;
-            c.log_open = 0u;
-        }
+        // the compaction before this closure (no closure token added yet)
+        if (k == 1) commit_log(w, c, L, t, (uint32_t)c.cnt[tab.par[L]]);
         if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
     }
     const int nl = w.max_lanes;
@@ -1048,6 +1142,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     wave_share(total, &u_beg, &u_end);
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
+        const int fp = upar(tab.par, L);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
         LaneCtl &c = w.ctl[L];
@@ -1060,8 +1155,8 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         float sc = 0.0f;
         if (tok < Q) {
             const size_t q = (size_t)L * Q + tok;
-            const StateInfo si = w.sinfo[w.tok_state[fp][q]];
-            sc = w.tok_score[fp][q];
+            const StateInfo si = w.sinfo[pick(w.tok_state, fp)[q]];
+            sc = pick(w.tok_score, fp)[q];
             eb = si.eps_b;
             ed = (uint32_t)(si.emit_b - si.eps_b);
         }
@@ -1117,15 +1212,16 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ 
 __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, LaneTab &tab)
 {
     const uint32_t ep = round_epoch(w, t, k);
-    const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
+            const int fp = lane_par(c, t + 1);
+            tab.par[L] = fp;
             uint32_t nc = 0;
-            const uint32_t n = (uint32_t)c.cnt[fp];
-            if (closure_lane(c, t) && n <= w.frontier_cap) nc = c.nclaims_eps[k & 1];
+            const uint32_t n = (uint32_t)pair_at(c.cnt, fp), nce = c.nclaims_eps[k & 1];
+            if (closure_lane(c, t) && n <= w.frontier_cap) nc = nce;
             if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = n;
@@ -1149,6 +1245,7 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
     wave_share(total, &u_beg, &u_end);
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = (int)find_lane(tab.base, nl, u);
+        const int fp = upar(tab.par, L);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
         const bool valid = i < tab.n[L];
         Claim cl;
@@ -1166,14 +1263,14 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
         int32_t esrc = -1;
         if (win && end > tab.f1[L]) {
             const int32_t stok = (int32_t)cl.tok;
-            esrc = (uint32_t)stok < Q ? w.tok_entry[fp][(size_t)L * Q + stok] : -1;
-            const int32_t pd = w.pos[fp][(size_t)L * w.num_states + dst];
-            const bool exists = (uint32_t)pd < tab.arcs[L] && w.tok_state[fp][(size_t)L * Q + pd] == dst;
+            esrc = (uint32_t)stok < Q ? pick(w.tok_entry, fp)[(size_t)L * Q + stok] : -1;
+            const int32_t pd = pick(w.pos, fp)[(size_t)L * w.num_states + dst];
+            const bool exists = (uint32_t)pd < tab.arcs[L] && pick(w.tok_state, fp)[(size_t)L * Q + pd] == dst;
             if (!exists) {
                 code = -1;
             } else {
                 const size_t q = (size_t)L * Q + pd;
-                if (K > cand_key(w.tok_score[fp][q], w.tok_last[fp][q])) code = pd;
+                if (K > cand_key(pick(w.tok_score, fp)[q], pick(w.tok_last, fp)[q])) code = pd;
             }
         }
         w.dec[ci] = make_int4(code, (int)__float_as_uint(end), arc, esrc);
@@ -1192,15 +1289,17 @@ __global__ __launch_bounds__(kBlock) void k_eps_resolve(const Work *__restrict__
 // next-step class and arc offsets), replaced tokens, the next pass's sources.
 __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
 {
-    const int fp = (t + 1) & 1;
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
+            const int fp = lane_par(c, t + 1);
+            tab.par[L] = fp;
             uint32_t nc = 0;
-            const bool on = closure_lane(c, t) && (uint32_t)c.cnt[fp] <= w.frontier_cap;
-            if (on) nc = c.nclaims_eps[k & 1];
+            const uint32_t nce = c.nclaims_eps[k & 1];
+            const bool on = closure_lane(c, t) && (uint32_t)pair_at(c.cnt, fp) <= w.frontier_cap;
+            if (on) nc = nce;
             // token and log capacity are checked per wavefront as it allocates
             const bool fits = nc <= w.claims_cap;
             if (fits) units = (nc + kWave - 1) / kWave;
@@ -1228,6 +1327,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
     wave_share(total, &u_beg, &u_end);
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = (int)find_lane(tab.base, nl, u);
+        const int fp = upar(tab.par, L);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const bool valid = i < tab.n[L];
         const bool next_final = (t + 1 == tab.T[L]);
@@ -1276,7 +1376,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             }
             continue;
         }
-        if (mn) write_strips(w.strip_tok[fp] + (size_t)L * w.strip_cap, w.strip_cap, (uint32_t)old,
+        if (mn) write_strips(pick(w.strip_tok, fp) + (size_t)L * w.strip_cap, w.strip_cap, (uint32_t)old,
                              (uint32_t)(old >> 32), dpre, dsum, mn);
         if (!any) continue;
         const uint32_t ra = (uint32_t)__popcll(ma & mask_lt());
@@ -1287,18 +1387,18 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         if (isnew) {
             pi = (uint32_t)old + (uint32_t)__popcll(mn & mask_lt());
             const size_t q = (size_t)L * Q + pi;
-            w.tok_state[fp][q] = dst;
-            w.tok_off[fp][q] = (uint32_t)(old >> 32) + dpre;
-            w.tok_abeg[fp][q] = abeg;
-            w.pos[fp][(size_t)L * w.num_states + dst] = (int32_t)pi;
+            pick(w.tok_state, fp)[q] = dst;
+            pick(w.tok_off, fp)[q] = (uint32_t)(old >> 32) + dpre;
+            pick(w.tok_abeg, fp)[q] = abeg;
+            pick(w.pos, fp)[(size_t)L * w.num_states + dst] = (int32_t)pi;
         } else {
             pi = (uint32_t)dd.x;
         }
         const size_t q = (size_t)L * Q + pi;
-        w.tok_score[fp][q] = end;
-        w.tok_entry[fp][q] = e;
-        w.tok_last[fp][q] = dd.z;
-        w.tok_ub[fp][q] = ub;
+        pick(w.tok_score, fp)[q] = end;
+        pick(w.tok_entry, fp)[q] = e;
+        pick(w.tok_last, fp)[q] = dd.z;
+        pick(w.tok_ub, fp)[q] = ub;
         const uint32_t ci = cb + ra;
         if (ci < w.claims_cap) w.changed[(k + 1) & 1][(size_t)L * w.claims_cap + ci] = pi;
     }
@@ -1311,27 +1411,178 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
     ph_eps_apply(w, t, k, tab);
 }
 
+// ---------------------------------------------------------- stream sequences
+// A stream (page section 8) holds one lane for its lifetime; every call is a
+// short sequence of the same step kernels, framed by these three. The host
+// writes one plan record per lane first (kPlan*).
+
+// Applies the plan: parks the lanes it does not name (their state is kept),
+// opens a lane (fresh start token; the start closure that follows runs for it
+// alone, at t = -1 < win = 0), opens the window of an advancing lane on its next
+// `len` frames (row `row` of this call's log_prob; T stays unbounded), or arms a
+// lane's end (T = 0: step 0 of the sequence is its final step).
+__global__ __launch_bounds__(kWave) void k_stream_begin(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    const int32_t *pl = w.plan + L * kPlanFields;
+    LaneCtl &c = w.ctl[L];
+    c.want = 0;
+    if (pl[kPlanCmd] != kCmdPark) c.last_step = -1;   // steps of this sequence not run yet
+    switch (pl[kPlanCmd]) {
+    case kCmdOpen:
+        init_lane(w, L, 0x7FFFFFFF);
+        c.dirty = 0u;     // k_clear ran first for this lane
+        c.win = 0;
+        c.lp_row = -1;
+        break;
+    case kCmdAdvance:
+        c.base = c.frames;
+        c.win = pl[kPlanLen];
+        c.lp_row = pl[kPlanRow];
+        c.want = pl[kPlanWant] ? 2 : 0;
+        break;
+    case kCmdFinish:
+        c.base = c.frames;
+        c.T = 0;
+        c.win = 1;
+        c.lp_row = -1;
+        c.want = 1;
+        break;
+    default:
+        c.win = -1;
+        break;
+    }
+}
+
+// End of a sequence: commits the last compaction of an advancing lane and moves
+// its frame count past the window.
+__global__ __launch_bounds__(kWave) void k_stream_end(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    const int cmd = w.plan[L * kPlanFields + kPlanCmd];
+    if (cmd != kCmdAdvance) return;
+    LaneCtl &c = w.ctl[L];
+    const int n = c.win;
+    commit_log(w, c, L, n - 1, (uint32_t)c.cnt[lane_par(c, n)]);
+    c.frames = c.base + n;
+    // the steps this sequence ran, for the caller's records
+    int32_t *R = w.res + (size_t)L * w.res_stride;
+    R[6] = c.phase_final;
+    R[7] = c.last_step;
+}
+
+// Before a stream's final step: its tokens hold the class of an emitting step
+// (T was unbounded when they were made); one workgroup per ending lane gives
+// them the final class in place — first arc, degree and bound of the final arcs,
+// slot offsets by a workgroup scan in token order, strip map, slot count.
+__global__ __launch_bounds__(kBlock) void k_reclass(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.x;
+    if (L >= w.max_lanes || w.plan[L * kPlanFields + kPlanCmd] != kCmdFinish) return;
+    LaneCtl &c = w.ctl[L];
+    if (c.status != kActive) return;
+    const int par = lane_par(c, 0);
+    const uint32_t n = (uint32_t)c.cnt[par];
+    const uint32_t Q = w.frontier_cap;
+    if (n > Q) return;   // an overflowed lane: its step retires it
+    __shared__ uint32_t wtot[kBlock / kWave];
+    const int wid = (int)(threadIdx.x / kWave);
+    uint32_t *strips = w.strip_tok[par] + (size_t)L * w.strip_cap;
+    unsigned long long run = 0;
+    for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
+        const uint32_t i = i0 + threadIdx.x;
+        int32_t abeg = 0;
+        uint32_t deg = 0;
+        float ub = 0.0f;
+        const size_t q = (size_t)L * Q + i;
+        if (i < n) class_of(w.sinfo[w.tok_state[par][q]], true, w.tok_score[par][q], &abeg, &deg, &ub);
+        uint32_t tot;
+        const uint32_t dpre = wave_excl_sum(deg, &tot);
+        if (wlane() == 0) wtot[wid] = tot;
+        __syncthreads();
+        unsigned long long before = 0, all = 0;
+        for (int x = 0; x < kBlock / kWave; ++x) {
+            if (x < wid) before += wtot[x];
+            all += wtot[x];
+        }
+        const unsigned long long off = run + before + dpre;
+        if (i < n) {
+            w.tok_off[par][q] = (uint32_t)off;
+            w.tok_abeg[par][q] = abeg;
+            w.tok_ub[par][q] = ub;
+            // strips whose first slot this token holds
+            for (unsigned long long sb = (off + kWave - 1) / kWave; sb * kWave < off + deg && sb < w.strip_cap; ++sb)
+                strips[sb] = i;
+        }
+        run += all;
+        __syncthreads();
+    }
+    // more slots than the lane's slot space: its final step retires it
+    if (threadIdx.x == 0) c.cnt[par] = (unsigned long long)n | ((unsigned long long)min(run, 0xFFFFFFFFull) << 32);
+}
+
 // -------------------------------------------------------------- k_backtrack
-// One wavefront per lane: lane 0 walks the winners chain from the result entry
-// (newest arc first), then the wavefront reverses it in place and gathers the
-// word ids (page section 7).
+// One wavefront per lane that wants a result: its result entry (want 1), or the
+// best token of its current frontier (want 2: a stream's partial hypothesis,
+// the greatest key(score, arc that gave the token its score)). Lane 0 walks the
+// winners chain from there (newest arc first), then the wavefront reverses it in
+// place and gathers the word ids (page sections 7 and 8).
 __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
     const int L = (int)blockIdx.x;
-    const LpDesc d = *w.lp;
-    if (L >= d.B) return;
+    if (L >= w.max_lanes) return;
     const LaneCtl &c = w.ctl[L];
+    const int want = c.want;
+    if (want == 0) return;
     int32_t *R = w.res + (size_t)L * w.res_stride;
     int32_t *arcs = R + kResHeader;
     int32_t *words = arcs + w.path_cap;
     const int lane = wlane();
     uint32_t len = 0;
     uint32_t ovf = c.overflow;
-    const bool has_path = c.final_entry >= 0;
+    int32_t start = c.final_entry;
+    float score = c.final_score;
+    int32_t reached = c.reached_final;
+    bool has_path = start >= 0;
+    if (want == 2) {
+        start = -1;
+        score = -__builtin_inff();
+        reached = 0;
+        const int par = lane_par(c, c.win);
+        const uint32_t n = (uint32_t)c.cnt[par];
+        unsigned long long bk = 0ull;
+        int32_t be = -1;
+        float bs = 0.0f;
+        if (c.status == kActive && n <= w.frontier_cap) {
+            const size_t qo = (size_t)L * w.frontier_cap;
+            for (uint32_t i = (uint32_t)lane; i < n; i += kWave) {
+                const unsigned long long k = cand_key(w.tok_score[par][qo + i], w.tok_last[par][qo + i]);
+                if (k > bk) { bk = k; be = w.tok_entry[par][qo + i]; bs = w.tok_score[par][qo + i]; }
+            }
+        }
+        unsigned long long m = bk;
+#pragma unroll
+        for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
+            const unsigned long long o = __shfl_xor(m, dd, kWave);
+            m = o > m ? o : m;
+        }
+        const unsigned long long who = __ballot(bk == m && m != 0ull);
+        has_path = who != 0ull;
+        if (has_path) {
+            const int src = __ffsll((long long)who) - 1;
+            start = __shfl(be, src, kWave);
+            score = __shfl(bs, src, kWave);
+        }
+    }
     if (lane == 0 && has_path) {
         const long long limit = (long long)w.max_lanes * w.arena;
-        int32_t e = c.final_entry;
+        int32_t e = start;   // -1: the start token (empty path)
         while (e >= 0 && e < limit) {
             const int2 r = w.wlog[e];
             if (len < w.path_cap) arcs[len] = r.y;
@@ -1362,11 +1613,11 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
     }
     if (lane == 0) {
         R[kResOk] = ovf == 0u ? 1 : 0;
-        R[kResReached] = c.reached_final;
+        R[kResReached] = reached;
         R[kResOverflow] = (int32_t)ovf;
         R[kResArcLen] = (int32_t)len;
         R[kResWordLen] = (int32_t)nw;
-        R[kResScore] = (int32_t)__float_as_uint(has_path ? c.final_score : -__builtin_inff());
+        R[kResScore] = (int32_t)__float_as_uint(has_path ? score : -__builtin_inff());
         R[6] = c.phase_final;
         R[7] = c.last_step;
     }
@@ -1404,6 +1655,9 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKEpsResolve: go(k_eps_resolve, G, B, s, e0, e1, dw, t, k); break;
     case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, dw, t, k); break;
     case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
+    case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
+    case kKStreamEnd: go(k_stream_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
+    case kKReclass: go(k_reclass, dim3(w.max_lanes), dim3(kBlock), s, e0, e1, dw); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
