@@ -47,6 +47,14 @@ class _Config(ctypes.Structure):
                 ("partial", ctypes.c_int32)]
 
 
+class _Lattice(ctypes.Structure):
+    _fields_ = [("output_beam", ctypes.c_float), ("cap", ctypes.c_int64), ("n", ctypes.c_int64),
+                ("rec", ctypes.c_void_p), ("vals", ctypes.c_void_p)]
+
+
+LAT_FIELDS = ("frame", "src", "dst", "ilabel", "arc", "score_bits", "keep", "flags")
+
+
 class _Result(ctypes.Structure):
     _fields_ = [("score", ctypes.c_float), ("reached_final", ctypes.c_int32),
                 ("dead", ctypes.c_int32), ("n_arcs", ctypes.c_int32),
@@ -80,7 +88,7 @@ def _load():
                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
-                                      ctypes.POINTER(_Result)]
+                                      ctypes.POINTER(_Result), ctypes.c_void_p]
             _lib = lib
     return _lib
 
@@ -103,12 +111,15 @@ class OracleGraph:
 
 def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active: int,
                 min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0,
-                online: bool = False, partial: bool = False):
+                online: bool = False, partial: bool = False, output_beam=None):
     """Decode one utterance. ``lp_lane`` is [T, V] (float32, or float16 widened exactly).
 
     ``online``: streaming semantics (no "last ~5 frames" raise of min_active).
     ``partial``: stop after the ``length`` real steps; the result is the path of the
     best current token (no final step).
+    ``output_beam``: also build the lattice (epsilon-free search) and prune it;
+    adds ``lattice`` (int32 [n, 8], fields ``LAT_FIELDS``, every admitted arc with
+    its keep bit) and ``lattice_vals`` (float32 [n, 3]: fwd(src), arc score, bwd(dst)).
 
     Returns a dict: score (float32), reached_final, dead, arcs, words (int32 arrays),
     steps (int64 [n_steps, 16], fields ``FIELDS``), start_closure, log_entries.
@@ -129,14 +140,28 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
     words = np.zeros(arcs_cap, dtype=np.int32)
     steps = np.zeros((steps_cap, NFIELDS), dtype=np.int64)
     res = _Result()
-    rc = lib.wo_decode(ctypes.byref(og.c), ctypes.byref(cfg), lp.ctypes.data if lp.size else None,
-                       length, int(lp.shape[1]), arcs.ctypes.data, arcs_cap, words.ctypes.data,
-                       arcs_cap, steps.ctypes.data, steps_cap, ctypes.byref(res))
-    if rc != 0:
-        raise RuntimeError(f"oracle failed (rc={rc})")
+    lat = None
+    cap = 0
+    while True:
+        if output_beam is not None:
+            rec = np.zeros((max(cap, 1), 8), dtype=np.int32)
+            vals = np.zeros((max(cap, 1), 3), dtype=np.float32)
+            lat = _Lattice(float(output_beam), cap, 0, rec.ctypes.data, vals.ctypes.data)
+        rc = lib.wo_decode(ctypes.byref(og.c), ctypes.byref(cfg), lp.ctypes.data if lp.size else None,
+                           length, int(lp.shape[1]), arcs.ctypes.data, arcs_cap, words.ctypes.data,
+                           arcs_cap, steps.ctypes.data, steps_cap, ctypes.byref(res),
+                           ctypes.byref(lat) if lat is not None else None)
+        if rc != 0:
+            raise RuntimeError(f"oracle failed (rc={rc})")
+        if lat is None or lat.n <= cap:
+            break
+        cap = int(lat.n)   # rerun with room for every lattice arc
     if res.n_arcs > arcs_cap or res.n_steps > steps_cap:
         raise RuntimeError("oracle output larger than its buffers")
-    return dict(score=np.float32(res.score), reached_final=int(res.reached_final),
+    extra = {}
+    if lat is not None:
+        extra = dict(lattice=rec[:lat.n].copy(), lattice_vals=vals[:lat.n].copy())
+    return dict(**extra, score=np.float32(res.score), reached_final=int(res.reached_final),
                 dead=int(res.dead), arcs=arcs[:res.n_arcs].copy(),
                 words=words[:res.n_words].copy(), steps=steps[:res.n_steps].copy(),
                 start_closure=np.array(res.start_closure[:], dtype=np.int64),

@@ -77,6 +77,22 @@ typedef struct {
     int64_t start_closure[8]; /* eps arcs, admitted, distinct, new, replaced, passes, n after */
 } wo_result;
 
+/* Lattice output (page section 1 "Lattice mode", section 3 on output_beam,
+ * section 7 "Lattice"): every admitted candidate of every step is a lattice arc
+ * from its source token (frame t) to its destination's token (frame t + 1, or
+ * the super-final state on the final step). Each record is
+ * {frame, src state, dst state, ilabel (-1 final), arc id, score bits, keep, flags}
+ * with the arc's own score s (weight + log-prob, one binary32 addition; a final
+ * arc's weight; 0 for the redirect's virtual arc, flags 2; final arcs flags 1),
+ * and vals {fwd(src), s, bwd(dst)}. keep is the output_beam prune. */
+typedef struct {
+    float output_beam;   /* finite, >= 0 */
+    int64_t cap;         /* records rec / vals hold */
+    int64_t n;           /* lattice arcs (true count, may exceed cap) */
+    int32_t *rec;        /* [cap][8] */
+    float *vals;         /* [cap][3] */
+} wo_lattice;
+
 /* ---- ordering key: greater = better (higher score, then smaller arc id) ---- */
 
 /* Monotone map from binary32 to u32: a < b (as floats) iff map(a) < map(b).
@@ -144,6 +160,20 @@ static int64_t wo_log_push(wo_log *l, int32_t prev, int32_t arc)
     }
     l->prev[l->n] = prev; l->arc[l->n] = arc;
     return l->n++;
+}
+
+typedef struct { float *v; int64_t n, cap; } wo_fvec;
+
+static int wo_fvec_push(wo_fvec *v, float x)
+{
+    if (v->n == v->cap) {
+        int64_t nc = v->cap ? 2 * v->cap : 1024;
+        float *a = realloc(v->v, nc * 4);
+        if (!a) return -1;
+        v->v = a; v->cap = nc;
+    }
+    v->v[v->n++] = x;
+    return 0;
 }
 
 static int wo_ivec_push(wo_ivec *v, int32_t x)
@@ -314,11 +344,18 @@ out:
  */
 int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t T,
               int64_t lp_stride, int32_t *arcs, int32_t arcs_cap, int32_t *words,
-              int32_t words_cap, int64_t *steps, int32_t steps_cap, wo_result *res)
+              int32_t words_cap, int64_t *steps, int32_t steps_cap, wo_result *res,
+              wo_lattice *lat)
 {
     wo_front cur = {0}, nxt = {0};
     wo_log lg = {0};
     wo_scratch sc = {0};
+    /* lattice: tokens of every frame (state, score), arcs of every step
+     * (source token index in its frame, arc id, arc score), offsets by step */
+    wo_ivec lt_state = {0}, la_src = {0}, la_arc = {0};
+    wo_fvec lt_score = {0}, la_s = {0};
+    int64_t *lt_off = NULL, *la_off = NULL;
+    int32_t lat_steps = 0;
     int rc = -1;
     int32_t final_entry = -1;
     int have_path = 0;
@@ -327,6 +364,15 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     memset(res, 0, sizeof(*res));
     res->score = -INFINITY;
     if (!g || !cfg || T < 0 || (T > 0 && !lp)) return -2;
+    /* lattice mode: epsilon-free search only (no closure), not with partial results */
+    if (lat && ((g->epsilon_id >= 0 && cfg->eps_iterations > 0) || cfg->partial ||
+                !(lat->output_beam >= 0.0f) || isinf(lat->output_beam))) return -2;
+    if (lat) {
+        lat->n = 0;
+        lt_off = malloc(((size_t)T + 3) * 8);
+        la_off = malloc(((size_t)T + 3) * 8);
+        if (!lt_off || !la_off) goto out;
+    }
     sc.tok_of_state = malloc((size_t)g->num_states * 4);
     sc.best_key = calloc((size_t)g->num_states, 8);
     sc.best_src = malloc((size_t)g->num_states * 4);
@@ -367,6 +413,13 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
         memset(rec, 0, sizeof(rec));
         rec[WO_N] = n;
         rec[WO_PHASE] = is_final ? 1 : 0;
+        if (lat) {
+            lt_off[t] = lt_state.n;
+            la_off[t] = la_src.n;
+            lat_steps = t + 1;
+            for (int64_t i = 0; i < n; i++)
+                if (wo_ivec_push(&lt_state, cur.state[i]) || wo_fvec_push(&lt_score, cur.score[i])) goto out;
+        }
         if (n == 0) {
             res->dead = 1;
             rec[WO_PHASE] = 3;
@@ -420,6 +473,9 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
                 final_entry = cur.entry[bi];
                 have_path = 1;
                 rec[WO_PHASE] = 2;
+                if (lat && (wo_ivec_push(&la_src, (int32_t)bi) ||
+                            wo_ivec_push(&la_arc, (int32_t)((uint32_t)g->num_arcs + (uint32_t)cur.state[bi])) ||
+                            wo_fvec_push(&la_s, 0.0f))) goto out;
             } else if (!is_final) {
                 res->dead = 1;
                 rec[WO_PHASE] = 3;
@@ -443,6 +499,12 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
                 if (end > cutoff) {
                     C++;
                     if (wo_offer(&sc, g->dest[a], end, a, cur.entry[i])) goto out;
+                    if (lat) {
+                        /* the arc's own score: weight + log-prob (final: weight) */
+                        float sa = is_final ? g->weight[a] : g->weight[a] + row[g->ilabel[a]];
+                        if (wo_ivec_push(&la_src, (int32_t)i) || wo_ivec_push(&la_arc, a) ||
+                            wo_fvec_push(&la_s, sa)) goto out;
+                    }
                 }
             }
         }
@@ -489,6 +551,67 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
         res->n_steps++;
     }
 
+    /*
+     * Lattice backward pass and output_beam prune (section 3: forward[src] + arc +
+     * backward[dst] >= best - output_beam; section 1 "Lattice mode"). Readings:
+     * bwd(super-final) = 0; bwd(token) = max over the token's lattice arcs of
+     * s + bwd(dst), steps from the last back to the first (one binary32 addition
+     * each; -inf without arcs); fwd(token) = its search score; an arc is kept iff
+     * (fwd(src) + s) + bwd(dst) >= best - output_beam, in that order, with best
+     * the lane's result score. Only lanes with a result have a lattice.
+     */
+    if (lat && have_path && lat_steps > 0) {
+        float *bnext = NULL, *bcur = NULL;
+        const float thresh = res->score - lat->output_beam;
+        lt_off[lat_steps] = lt_state.n;
+        la_off[lat_steps] = la_src.n;
+        for (int32_t t = lat_steps - 1; t >= 0; t--) {
+            const int64_t t0 = lt_off[t], nt = lt_off[t + 1] - t0;
+            const int last = (t == lat_steps - 1);
+            float *b = malloc((size_t)(nt > 0 ? nt : 1) * 4);
+            if (!b) { free(bnext); goto out; }
+            for (int64_t i = 0; i < nt; i++) b[i] = -INFINITY;
+            /* state -> token index of frame t + 1 (the destinations) */
+            if (!last)
+                for (int64_t j = lt_off[t + 1]; j < lt_off[t + 2]; j++)
+                    sc.tok_of_state[lt_state.v[j]] = (int32_t)(j - lt_off[t + 1]);
+            for (int64_t k = la_off[t]; k < la_off[t + 1]; k++) {
+                const int32_t i = la_src.v[k], a = la_arc.v[k];
+                const int redirect = a >= g->num_arcs;
+                const float sa = la_s.v[k];
+                float bd = 0.0f;
+                if (!last) bd = bnext[sc.tok_of_state[g->dest[a]]];
+                const float v = sa + bd;
+                if (v > b[i]) b[i] = v;
+                const float fwd = lt_score.v[t0 + i];
+                const float thr = (fwd + sa) + bd;
+                if (lat->n < lat->cap) {
+                    int32_t *r = lat->rec + lat->n * 8;
+                    uint32_t u;
+                    memcpy(&u, &sa, 4);
+                    r[0] = t;
+                    r[1] = lt_state.v[t0 + i];
+                    r[2] = redirect ? g->num_states - 1 : g->dest[a];
+                    r[3] = (redirect || last) ? -1 : g->ilabel[a];
+                    r[4] = a;
+                    r[5] = (int32_t)u;
+                    r[6] = thr >= thresh ? 1 : 0;
+                    r[7] = redirect ? 2 : (last ? 1 : 0);
+                    lat->vals[lat->n * 3 + 0] = fwd;
+                    lat->vals[lat->n * 3 + 1] = sa;
+                    lat->vals[lat->n * 3 + 2] = bd;
+                }
+                lat->n++;
+            }
+            if (!last)
+                for (int64_t j = lt_off[t + 1]; j < lt_off[t + 2]; j++) sc.tok_of_state[lt_state.v[j]] = -1;
+            free(bnext);
+            bnext = b;
+            (void)bcur;
+        }
+        free(bnext);
+    }
+
     /* backtrack: entry -> prev to -1, collected newest first, written oldest first */
     if (have_path) {
         int32_t len = 0, nw = 0;
@@ -525,6 +648,8 @@ out:
     free(nxt.state); free(nxt.entry); free(nxt.last); free(nxt.score);
     free(lg.prev); free(lg.arc);
     free(sc.tok_of_state); free(sc.best_key); free(sc.best_src); free(sc.touched.v);
+    free(lt_state.v); free(la_src.v); free(la_arc.v); free(lt_score.v); free(la_s.v);
+    free(lt_off); free(la_off);
     return rc;
 }
 

@@ -11,6 +11,8 @@ their weight).
   every frame (infinite beam), with the epsilon closure computed to a fixpoint.
 * ``viterbi_partial``: the same trellis stopped after T frames, best state
   without a final arc (the partial hypothesis of a stream).
+* ``complete_paths``: every complete path of an epsilon-free graph with its
+  score (the lattice pins compare kept arcs with them).
 * ``enumerate_paths``: lists every path (at most ``max_eps`` epsilon arcs
   between frames) and takes the maximum.
 """
@@ -146,3 +148,21 @@ def enumerate_paths(g, lp, T, max_eps):
 
     rec(g.start, 0, F32(0.0), [], max_eps)
     return best[0], (best[1] or []), best[2]
+
+
+def complete_paths(g, lp, T):
+    """Every path x^T f of an epsilon-free graph from the start state: a list of
+    (score, arcs) with the fp32 left-to-right score of section 5.3."""
+    final, _, emit = _classes(g)
+    rs = g.row_splits
+    out = []
+
+    def rec(s, t, sc, arcs):
+        for a in range(rs[s], rs[s + 1]):
+            if emit[a] and t < T:
+                rec(int(g.dest[a]), t + 1, F32(F32(sc + g.weight[a]) + F32(lp[t, g.ilabel[a]])), arcs + [a])
+            elif final[a] and t == T:
+                out.append((F32(sc + g.weight[a]), arcs + [a]))
+
+    rec(g.start, 0, F32(0.0), [])
+    return out

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from bruteforce import enumerate_paths, viterbi_exact, viterbi_partial
+from bruteforce import complete_paths, enumerate_paths, viterbi_exact, viterbi_partial
 from cases import check_path, f32_value, graph_from_states, load_golden
 
 F32 = np.float32
@@ -382,3 +382,116 @@ def test_partial_prefix_of_final_steps():
         part = _decode(g, lp[0], t, wl.beam, wl.max_active, online=True, partial=True)
         assert np.array_equal(part["steps"], full["steps"][:t])
         check_path(g, lp[0].astype(np.float32), t, part["arcs"], part["words"], part["score"], 0)
+
+
+# ------------------------------------------------ lattice: backward pass and prune
+
+LF = {name: i for i, name in enumerate(oracle.LAT_FIELDS)}
+
+
+def _lat(g, lp, T, beam, max_active, output_beam, **kw):
+    return oracle.decode_lane(g, lp, T, beam, max_active, output_beam=output_beam, **kw)
+
+
+def _continuations(lat, sf):
+    """Best right-folded continuation score of every lattice node (frame, state),
+    by listing every continuation path to the super-final state explicitly."""
+    out_arcs = {}
+    for k, r in enumerate(lat["lattice"]):
+        out_arcs.setdefault((int(r[LF["frame"]]), int(r[LF["src"]])), []).append(k)
+    vals = lat["lattice_vals"]
+
+    def paths(node):
+        res = []
+        for k in out_arcs.get(node, []):
+            r = lat["lattice"][k]
+            s = F32(vals[k, 1])
+            if int(r[LF["dst"]]) == sf:
+                res.append([s])
+            else:
+                for p in paths((int(r[LF["frame"]]) + 1, int(r[LF["dst"]]))):
+                    res.append([s] + p)
+        return res
+
+    def fold(p):
+        acc = F32(0.0)
+        for s in reversed(p):
+            acc = F32(s + acc)
+        return acc
+
+    best = {}
+    for node in out_arcs:
+        ps = paths(node)
+        best[node] = max((fold(p) for p in ps), default=F32(-np.inf))
+    return best
+
+
+def test_lattice_backward_scores_are_best_continuations():
+    """Section 3 / 7 "Lattice": bwd(dst) of every arc is the best score of a
+    continuation from its destination to the super-final state, each path's score
+    folded from its last arc back (its own recursion, written out as lists)."""
+    checked = 0
+    for seed in range(900, 960):
+        g, lp, T = _tiny(seed, False)
+        r = _lat(g, lp, T, 4.0, 50, 3.0)
+        if r["reached_final"] != 1:
+            continue
+        sf = g.num_states - 1
+        best = _continuations(r, sf)
+        for k, rr in enumerate(r["lattice"]):
+            dst = int(rr[LF["dst"]])
+            want = F32(0.0) if dst == sf else best.get((int(rr[LF["frame"]]) + 1, dst), F32(-np.inf))
+            assert r["lattice_vals"][k, 2] == want, (seed, k)
+            checked += 1
+    assert checked > 300
+
+
+def test_lattice_keep_rule_and_best_path():
+    """Section 3: output_beam acts only in the backward prune,
+    forward[src] + arc + backward[dst] >= best - output_beam; the best path itself
+    always survives a positive output_beam."""
+    for cid, lanes in ((1, [0]), (2, [0, 3])):
+        g, lp, L = synth.workload_inputs(cid)
+        wl = synth.WORKLOADS[cid]
+        for b in lanes:
+            for ob in (0.5, 4.0):
+                r = _lat(g, lp[b].astype(np.float32), int(L[b]), wl.beam, wl.max_active, ob)
+                v = r["lattice_vals"]
+                thr = (v[:, 0] + v[:, 1]).astype(np.float32) + v[:, 2]
+                keep = (thr.astype(np.float32) >= np.float32(r["score"] - np.float32(ob))).astype(np.int32)
+                assert np.array_equal(keep, r["lattice"][:, LF["keep"]])
+                kept = {(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in r["lattice"] if x[LF["keep"]]}
+                assert all((t, int(a)) in kept for t, a in enumerate(r["arcs"]))
+                st = r["steps"]
+                per_frame = np.bincount(r["lattice"][:, LF["frame"]], minlength=st.shape[0])
+                assert np.array_equal(per_frame, st[:, IDX["admitted"]])   # every admitted arc is an arc
+
+
+def test_lattice_at_infinite_beam_is_every_complete_path():
+    """At infinite search beam every candidate is admitted; with a wide output beam
+    the kept (frame, arc) pairs are exactly the arc occurrences of complete paths,
+    and with a narrow one those on a path within output_beam of the best (pairs
+    within 1e-4 of the threshold are not judged)."""
+    judged = 0
+    for seed in range(1000, 1060):
+        g, lp, T = _tiny(seed, False)
+        paths = complete_paths(g, lp, T)
+        if not paths:
+            continue
+        best = max(p[0] for p in paths)
+        for ob in (1e6, 1.0):
+            r = _lat(g, lp, T, INF_BEAM, 1 << 20, ob)
+            assert r["score"] == best
+            kept = {(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in r["lattice"] if x[LF["keep"]]}
+            through = {}
+            for sc, arcs in paths:
+                for t, a in enumerate(arcs):
+                    through[(t, a)] = max(through.get((t, a), F32(-np.inf)), sc)
+            for key, sc in through.items():
+                margin = float(sc) - (float(best) - ob)
+                if abs(margin) < 1e-4:
+                    continue
+                assert (key in kept) == (margin > 0), (seed, ob, key)
+                judged += 1
+            assert kept <= set(through), seed
+    assert judged > 500
