@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
+    ap.add_argument("--lattice", type=float, default=None, metavar="OUTPUT_BEAM",
+                    help="lattice mode: keep every admitted arc and prune with this output beam")
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
@@ -271,9 +273,10 @@ def main():
         stream_bench(args, wl, graph, lp, lengths, dev)
         return
     dg = wb.Graph(graph, device=0)
+    lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
-                     grid_blocks=args.grid)
+                     grid_blocks=args.grid, **lat)
     x = torch.from_numpy(lp).to(dev)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -338,7 +341,8 @@ def main():
                                f"{graph.num_arcs} arcs, power-law out-degree), log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
-                   "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay"},
+                   "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay",
+                   **({} if args.lattice is None else {"lattice_output_beam": args.lattice})},
         "arcs_expanded_per_s": round(arcs_ps, 1),
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
@@ -346,6 +350,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.lattice is not None:
+        line["lattice_kept_arcs"] = int(sum(dec.lattice(b).shape[0] for b in range(B)))
+        line["lattice_arcs"] = int(st["admitted"])
     print(json.dumps(line), flush=True)
     if args.report:
         with open(args.report, "w") as f:

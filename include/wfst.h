@@ -127,6 +127,23 @@ typedef struct wfst_graph_desc {
  *                  newest path_cap arcs (its words are those arcs' words) and
  *                  sets WFST_OVF_PATH. A stream's path spans all its frames
  *                  (section 8): size this for the longest stream.
+ *  lattice         1: lattice mode (section 1 "Lattice mode", section 7
+ *                  "Lattice"): every admitted candidate of every step is kept
+ *                  as a lattice arc, and after the decode a backward pass
+ *                  prunes them with output_beam (section 3); read the result
+ *                  with wfst_lattice_records. Needs an epsilon-free search
+ *                  (no epsilon arcs, or eps_iterations 0); no streams.
+ *  output_beam     the lattice prune's beam (finite, >= 0): an arc survives iff
+ *                  (fwd(src) + s) + bwd(dst) >= best - output_beam, with s the
+ *                  arc's own score (weight + log-prob; a final arc's weight; 0 for
+ *                  the redirect's virtual arc), fwd the search score of its source
+ *                  token, bwd(token) the best continuation to the super-final
+ *                  state (s + bwd(dst) maximised over its arcs, last step first),
+ *                  best the lane's result score; binary32, in that order.
+ *  lattice_cap     lattice arcs (and kept records) per lane per decode
+ *                  (0: 2 * max_active * (max_frames + 2), at least 2^20); in
+ *                  [0, 2^28]. More
+ *                  sets WFST_OVF_ARENA (the 1-best result is still exact).
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -145,6 +162,9 @@ typedef struct wfst_decoder_config {
     int64_t slot_cap;
     int32_t plain_keys;
     int32_t path_cap;
+    int32_t lattice;
+    float output_beam;
+    int64_t lattice_cap;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -279,6 +299,21 @@ int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_
 int wfst_release_stream(wfst_decoder_t d, int32_t channel);
 
 /*
+ * The pruned lattice of lane `lane` in the last decode (lattice mode; section 7
+ * "Lattice": flat records). *n = the number of kept arcs; the first min(*n, cap)
+ * records are written to out, 8 int32 each, in no particular order:
+ *   {frame t, source state, destination state (the super-final state for final
+ *    and redirect arcs), ilabel (-1 final), arc id (num_arcs + state for the
+ *    redirect's virtual arc), arc score bits (binary32 s), lane, flags (1 final
+ *    arc, 2 redirect)}
+ * A source is the token of its state at frame t, an emitting arc's destination
+ * the token of its state at frame t + 1. A lane with no result has no arcs.
+ * Errors: WFST_EINVAL (not lattice mode, lane outside the last decode, null),
+ * WFST_EDEVICE.
+ */
+int wfst_lattice_records(wfst_decoder_t d, int32_t lane, int32_t *out, int64_t cap, int64_t *n);
+
+/*
  * Counters of the last decode or stream call, summed over its lanes (n up to 14 values):
  *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
  *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
@@ -318,7 +353,10 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_STREAM_BEGIN 10 /* stream call: applies the per-lane plan                   */
 #define WFST_K_STREAM_END  11  /* stream call: commits the chunk's last compaction        */
 #define WFST_K_RECLASS     12  /* stream end: final-step class of the stream's tokens      */
-#define WFST_K_COUNT       13
+#define WFST_K_LAT_RESOLVE 13  /* lattice: destination positions of a step's arcs         */
+#define WFST_K_LAT_INIT    14  /* lattice: backward scores to -inf                        */
+#define WFST_K_LAT_BACK    15  /* lattice: backward pass and prune of one step's arcs     */
+#define WFST_K_COUNT       16
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

@@ -1,0 +1,118 @@
+"""GPU parity of lattice mode (page section 1 "Lattice mode", section 3 on
+output_beam, section 7 "Lattice"): the kept lattice arcs of every lane, as flat
+records, equal the oracle's kept arcs bit for bit (frame, states, labels, arc
+ids, arc-score bits, flags); the 1-best results stay those of a plain decode."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import wfst_beam_search_amd as wb
+from gpu_util import compare_batch, oracle_lanes
+
+pytestmark = pytest.mark.gpu
+
+OF = {name: i for i, name in enumerate(oracle.LAT_FIELDS)}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob, lane):
+    r = oracle.decode_lane(g, lp_lane.astype(np.float32), T, beam, max_active, min_active, allow_partial,
+                           output_beam=ob)
+    lat = r["lattice"]
+    k = lat[lat[:, OF["keep"]] == 1]
+    out = np.stack([k[:, OF["frame"]], k[:, OF["src"]], k[:, OF["dst"]], k[:, OF["ilabel"]], k[:, OF["arc"]],
+                    k[:, OF["score_bits"]], np.full(k.shape[0], lane, np.int32), k[:, OF["flags"]]], 1) \
+        if k.shape[0] else np.zeros((0, 8), np.int32)
+    out = out.astype(np.int32)
+    return out[np.lexsort((out[:, 4], out[:, 1], out[:, 0]))] if out.shape[0] else out, r
+
+
+def lattice_case(g, lp, L, beam, ma, mi, ap, ob, dgraph=None, **caps):
+    import torch
+    B, T, V = lp.shape
+    own = dgraph is None
+    dg = wb.Graph(g) if own else dgraph
+    dec = wb.Decoder(dg, beam, ma, min_active=mi, allow_partial=ap, max_lanes=B, max_frames=max(T, 1),
+                     lp_dtype="f16" if lp.dtype == np.float16 else "f32", lattice=True, output_beam=ob, **caps)
+    r = dec.decode(torch.from_numpy(np.ascontiguousarray(lp)).cuda(), L)
+    lats = [dec.lattice(b) for b in range(B)]
+    dec.close()
+    if own:
+        dg.release()
+    o = oracle_lanes(g, lp, L, beam, ma, mi, ap)
+    compare_batch(r, None, o, check_steps=False)
+    for b in range(B):
+        want, _ = _oracle_kept(g, lp[b], int(L[b]), beam, ma, mi, ap, ob, b)
+        got = lats[b]
+        assert got.shape == want.shape, f"lane {b}: {got.shape[0]} kept arcs vs {want.shape[0]}"
+        assert np.array_equal(got, want), f"lane {b}: lattice records differ"
+    return r, lats
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(70_000 + seed)
+    n = int(rng.integers(3, 40))
+    vocab = int(rng.integers(2, 10))
+    g = synth.random_graph(seed + 11, n=n, deg=(1, int(rng.integers(2, 8))), vocab=vocab,
+                           self_loop=float(rng.choice([0.0, 0.3])))
+    B = int(rng.integers(1, 5))
+    T = int(rng.integers(0, 20))
+    lp = synth.random_logprobs(seed + 5, B, max(T, 1), vocab, sigma=float(rng.uniform(0.5, 3.0)))
+    if T == 0:
+        lp = lp[:, :0, :]
+    L = rng.integers(0, T + 1, size=B).astype(np.int32)
+    beam = float(rng.choice([1.0, 3.0, 8.0, 1e10]))
+    ma = int(rng.choice([2, 5, 50, 1000]))
+    mi = int(rng.choice([0, 0, 3]))
+    ap = bool(rng.integers(0, 2))
+    ob = float(rng.choice([0.0, 0.5, 2.0, 10.0]))
+    return g, lp, L, beam, ma, mi, ap, ob
+
+
+def test_lattice_random_small_graphs():
+    kept = 0
+    for seed in range(60):
+        g, lp, L, beam, ma, mi, ap, ob = _random_case(seed)
+        _say("lattice random", seed, lp.shape, beam, ma, mi, ap, ob)
+        _, lats = lattice_case(g, lp, L, beam, ma, mi, ap, ob)
+        kept += sum(x.shape[0] for x in lats)
+    assert kept > 500
+
+
+@pytest.mark.parametrize("ob", [0.5, 4.0])
+def test_lattice_workload(ob):
+    cid = 2
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    lanes = [0, 5]
+    lp2 = np.ascontiguousarray(lp[lanes, :120])
+    L2 = np.minimum(L[lanes], 120).astype(np.int32)
+    _say("lattice workload", ob, lp2.shape)
+    _, lats = lattice_case(g, lp2, L2, wl.beam, wl.max_active, 0, False, ob)
+    assert all(x.shape[0] > L2[b] for b, x in enumerate(lats))
+
+
+def test_lattice_capacity_and_rejections():
+    import torch
+    g, lp, L, beam, ma, mi, ap, _ = _random_case(3)
+    lp = synth.random_logprobs(9, 1, 12, g.vocab)
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, 8.0, 1000, max_lanes=1, max_frames=12, lattice=True, output_beam=5.0, lattice_cap=4)
+    r = dec.decode(torch.from_numpy(lp).cuda(), [12])
+    assert int(r.meta[0, 2]) & 4 and int(r.meta[0, 0]) == 0      # arena bit: lattice full
+    with pytest.raises(wb.WfstError):
+        dec.create_stream()                                          # no streams in lattice mode
+    dec.close()
+    with pytest.raises(wb.WfstError):
+        wb.Decoder(dg, 8.0, 100, lattice=True, output_beam=float("inf"))
+    eg = synth.random_graph(4, n=6, deg=(1, 3), vocab=4, epsilon=True, eps_levels=3)
+    deg_ = wb.Graph(eg)
+    with pytest.raises(wb.WfstError):
+        wb.Decoder(deg_, 8.0, 100, eps_iterations=2, lattice=True, output_beam=1.0)
+    deg_.release()
+    dg.release()

@@ -27,9 +27,11 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
                     "wfst_decoder_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
-                    "wfst_finalize_stream", "wfst_release_stream")
+                    "wfst_finalize_stream", "wfst_release_stream", "wfst_lattice_records")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
-           "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass")
+           "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
+           "lat_back")
+LATTICE_FIELDS = ("frame", "src", "dst", "ilabel", "arc", "score_bits", "lane", "flags")
 STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
                "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "listed", "_14", "_15")
 STAT_FIELDS = ("arcs", "admitted", "distinct", "tokens", "eps_arcs", "eps_admitted",
@@ -61,7 +63,9 @@ class _Config(ctypes.Structure):
                 ("use_graphs", ctypes.c_int32), ("frontier_cap", ctypes.c_int32),
                 ("claims_cap", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
                 ("arena_entries", ctypes.c_int64), ("slot_cap", ctypes.c_int64),
-                ("plain_keys", ctypes.c_int32), ("path_cap", ctypes.c_int32)]
+                ("plain_keys", ctypes.c_int32), ("path_cap", ctypes.c_int32),
+                ("lattice", ctypes.c_int32), ("output_beam", ctypes.c_float),
+                ("lattice_cap", ctypes.c_int64)]
 
 
 _lib = None
@@ -106,6 +110,7 @@ def load_library():
                                            vp, vp, vp]
         lib.wfst_finalize_stream.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_release_stream.argtypes = [vp, i32]
+        lib.wfst_lattice_records.argtypes = [vp, i32, vp, ctypes.c_int64, vp]
         for name in EXPORTED_SYMBOLS:
             if name != "wfst_last_error":
                 getattr(lib, name).restype = ctypes.c_int
@@ -179,13 +184,15 @@ class Decoder:
                  allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
                  lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
-                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False, path_cap: int = 0):
+                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False, path_cap: int = 0,
+                 lattice: bool = False, output_beam: float = 0.0, lattice_cap: int = 0):
         lib = load_library()
         cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                       int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                       int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
                       int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
-                      int(bool(plain_keys)), int(path_cap))
+                      int(bool(plain_keys)), int(path_cap), int(bool(lattice)), float(output_beam),
+                      int(lattice_cap))
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h
@@ -290,6 +297,16 @@ class Decoder:
 
     def release_stream(self, channel: int):
         _check(_lib.wfst_release_stream(self.handle, int(channel)))
+
+    def lattice(self, lane: int) -> np.ndarray:
+        """Kept lattice arcs of ``lane`` in the last decode (lattice mode): int32
+        [n, 8], fields ``LATTICE_FIELDS``, sorted by (frame, src, arc)."""
+        n = ctypes.c_int64(0)
+        _check(_lib.wfst_lattice_records(self.handle, int(lane), None, 0, ctypes.byref(n)))
+        out = np.zeros((max(int(n.value), 1), 8), dtype=np.int32)
+        _check(_lib.wfst_lattice_records(self.handle, int(lane), _ptr(out), out.shape[0], ctypes.byref(n)))
+        out = out[:int(n.value)]
+        return out[np.lexsort((out[:, 4], out[:, 1], out[:, 0]))] if out.shape[0] else out
 
     def stats(self) -> dict:
         out = np.zeros(len(STAT_FIELDS), dtype=np.int64)

@@ -318,6 +318,13 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
     }
     if (c.path_cap < 0 || c.path_cap > (1 << 26)) return fail(WFST_EINVAL, "path_cap must lie in [0, 2^26]");
+    if (c.lattice != 0 && c.lattice != 1) return fail(WFST_EINVAL, "lattice must be 0 or 1");
+    if (c.lattice && P > 0) return fail(WFST_EINVAL, "lattice mode needs an epsilon-free search (eps_iterations 0 or no epsilon arcs)");
+    if (c.lattice && (!(c.output_beam >= 0.0f) || std::isinf(c.output_beam))) return fail(WFST_EINVAL, "output_beam must be finite and >= 0");
+    if (c.lattice_cap < 0 || c.lattice_cap > (1ll << 28)) return fail(WFST_EINVAL, "lattice_cap must lie in [0, 2^28]");
+    const uint64_t lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
+        : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
+                             1ull << 28);
     const uint64_t path_cap = c.path_cap ? (uint64_t)c.path_cap : (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
     HIP_TRY(hipSetDevice(g->device));
     wfst_decoder_s *d = new wfst_decoder_s();
@@ -355,6 +362,9 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC;
     w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap; w.strip_cap = (uint32_t)strip_cap;
     w.res_stride = (uint32_t)(kResHeader + 2 * path_cap);
+    w.lattice = c.lattice;
+    w.output_beam = c.lattice ? c.output_beam : 0.0f;
+    w.lat_cap = (uint32_t)lat_cap;
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
     int r = WFST_OK;
@@ -377,6 +387,15 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
     A(&d->d_plan, L * kPlanFields);
+    if (c.lattice) {
+        const size_t F = (size_t)c.max_frames + 3;
+        A(&w.lat_arc, L * lat_cap);
+        A(&w.lat_aoff, L * F);
+        A(&w.lat_fbase, L * F);
+        A(&w.lat_score, L * (size_t)arena);
+        A(&w.lat_bwd, L * ((size_t)arena + 1));
+        A(&w.lat_out, L * lat_cap * kLatFields);
+    }
     if (r != WFST_OK) { delete d; return r; }
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
     w.round_base = 0;
@@ -445,12 +464,18 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
         if ((e = wrap_clear(d, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
+        if (d->w.lattice && (e = launch(d, kKLatResolve, t, 0, s)) != hipSuccess) return e;
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = wrap_clear(d, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
         }
+    }
+    if (d->w.lattice) {
+        if ((e = launch(d, kKLatInit, 0, 0, s)) != hipSuccess) return e;
+        for (int t = steps - 1; t >= 0; --t)
+            if ((e = launch(d, kKLatBack, t, 0, s)) != hipSuccess) return e;
     }
     if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
     return hipSuccess;
@@ -701,6 +726,7 @@ extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *chann
 {
     if (!d || !channel) return fail(WFST_EINVAL, "decoder or channel is null");
     *channel = -1;
+    if (d->w.lattice) return fail(WFST_EINVAL, "a lattice-mode decoder does not stream");
     std::lock_guard<std::mutex> lock(d->mu);
     int lane = -1;
     for (int L = 0; L < d->cfg.max_lanes; ++L)
@@ -882,7 +908,7 @@ extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
     HIP_TRY(hipSetDevice(d->g->device));
     if (enable && d->ev.empty()) {
         const size_t rounds = (size_t)(d->cfg.max_frames + 2) * (size_t)(1 + d->passes);
-        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(3 + 3 * d->passes) + rounds / d->w.epoch_period;
+        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(5 + 3 * d->passes) + rounds / d->w.epoch_period;
         d->ev.resize(2 * n, nullptr);
         d->ev_kind.assign(n, -1);
         for (size_t i = 0; i < 2 * n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));
@@ -905,5 +931,24 @@ extern "C" int wfst_decoder_kernel_times(wfst_decoder_t d, double *out, int32_t 
         if (id >= 0 && id < kKCount) { v[2 * id] += ms; v[2 * id + 1] += 1.0; }
     }
     for (int32_t i = 0; i < n && i < 2 * kKCount; ++i) out[i] = v[(size_t)i];
+    return WFST_OK;
+}
+
+extern "C" int wfst_lattice_records(wfst_decoder_t d, int32_t lane, int32_t *out, int64_t cap, int64_t *n)
+{
+    if (!d || !n || cap < 0 || (cap > 0 && !out)) return fail(WFST_EINVAL, "bad arguments");
+    std::lock_guard<std::mutex> lock(d->mu);
+    *n = 0;
+    if (!d->w.lattice) return fail(WFST_EINVAL, "the decoder is not in lattice mode");
+    if (lane < 0 || lane >= d->cfg.max_lanes || d->last_len[(size_t)lane] < 0)
+        return fail(WFST_EINVAL, "lane not in the last decode");
+    HIP_TRY(hipSetDevice(d->g->device));
+    uint32_t kept = 0;
+    HIP_TRY(hipMemcpy(&kept, (const char *)(d->ctl + lane) + offsetof(LaneCtl, lat_out_n), 4, hipMemcpyDeviceToHost));
+    *n = kept;
+    const int64_t m = std::min<int64_t>(std::min<int64_t>(kept, cap), (int64_t)d->w.lat_cap);
+    if (m > 0)
+        HIP_TRY(hipMemcpy(out, d->w.lat_out + (size_t)lane * d->w.lat_cap * kLatFields,
+                          4 * (size_t)m * kLatFields, hipMemcpyDeviceToHost));
     return WFST_OK;
 }

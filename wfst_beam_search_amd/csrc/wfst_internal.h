@@ -109,6 +109,8 @@ struct alignas(128) LaneCtl {
     alignas(128) uint32_t log_cursor;        // winners-log entries used in this lane's region
     alignas(128) uint32_t nclaims_eps[2];    // admitted candidates of closure pass k at [k & 1]
     alignas(128) uint32_t nchanged[2];       // changed-token list sizes of closure pass k at [k & 1]
+    alignas(128) uint32_t lat_cursor;        // lattice arcs persisted (lattice mode)
+    alignas(128) uint32_t lat_out_n;         // lattice records kept by the prune (lattice mode)
 };
 
 // Device-resident description of the caller's log_prob tensor, rewritten before
@@ -170,7 +172,21 @@ struct Work {
     int32_t *res;             // [L][res_stride] results
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]
     const int32_t *plan;      // [L][kPlanFields] stream commands of the next sequence
+    // lattice mode (epsilon-free search): every admitted candidate of every step
+    int32_t lattice;          // 1: persist and prune the lattice
+    float output_beam;        // the prune's beam
+    uint32_t lat_cap;         // lattice arcs (and kept records) per lane
+    int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position, 0}
+    uint32_t *lat_aoff;       // [L][max_frames + 3] first lattice arc of each step
+    uint32_t *lat_fbase;      // [L][max_frames + 3] winners-log base of each frame's tokens
+    float *lat_score;         // [L][arena] score of each winners-log entry's token
+    uint32_t *lat_bwd;        // [L][arena + 1] ordered backward score by entry (+ the start token)
+    int32_t *lat_out;         // [L][lat_cap][kLatFields] kept records
 };
+
+// Fields of a kept lattice record (int32 each).
+enum : int32_t { kLatFrame = 0, kLatSrc, kLatDst, kLatIlabel, kLatArc, kLatScore, kLatLane, kLatFlags,
+                 kLatFields = 8 };
 
 // Per-lane stream command of a launch sequence (written by the host).
 enum : int32_t { kPlanCmd = 0, kPlanLen, kPlanRow, kPlanWant, kPlanFields = 4 };
@@ -179,7 +195,8 @@ enum : int32_t { kCmdPark = 0, kCmdOpen = 1, kCmdAdvance = 2, kCmdFinish = 3 };
 // Kernels of a decode, in launch order within a step (ids match WFST_K_*).
 enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
-    kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKCount
+    kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
+    kKLatBack, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -404,6 +404,8 @@ __device__ void init_lane(const Work &w, int L, int T)
     c.phase_final = kPhNone;
     c.base = 0;
     c.frames = 0;
+    c.lat_cursor = 0u;
+    c.lat_out_n = 0u;
     c.cnt[1] = 0ull;
     const int32_t s = w.start_state;
     const StateInfo si = w.sinfo[s];
@@ -450,6 +452,8 @@ __global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
         c.cnt[1] = 0ull;
         c.last_step = -1;
         c.phase_final = kPhNone;
+        c.lat_cursor = 0u;
+        c.lat_out_n = 0u;
     }
 }
 
@@ -788,6 +792,7 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     if (ph == kPhNone) return;
     uint32_t *rec = step_rec(w, L, t);
     c.last_step = t;
+    if (w.lattice) w.lat_aoff[(size_t)L * (w.max_frames + 3) + t] = c.lat_cursor;
     rec[kRecN] = n;
     rec[kRecArcs] = arcs;
     if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
@@ -821,6 +826,18 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
                 c.final_score = w.tok_score[p][qo + bi] + 0.0f;
                 c.reached_final = 0;
                 rec[kRecPhase] = kPhRedirect;
+                if (w.lattice) {
+                    // the redirect's virtual arc is the lattice's one final arc
+                    const uint32_t li = c.lat_cursor;
+                    if (li < w.lat_cap) {
+                        w.lat_arc[(size_t)L * w.lat_cap + li] =
+                            make_int4((int)bi, (int)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + bi]),
+                                      w.super_final, 0);
+                        c.lat_cursor = li + 1u;
+                    } else {
+                        c.overflow |= kOvfArena;
+                    }
+                }
                 c.phase_final = kPhRedirect;
             }
             c.status = kDone;
@@ -937,6 +954,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
                 c.front_base[np] = tab.arcs[L];
+                if (w.lattice) w.lat_fbase[(size_t)L * (w.max_frames + 3) + t + 1] = tab.arcs[L];
                 c.log_open = 1u;   // entries added to log_cursor by the next kernel
             }
             c.nclaims_eps[1] = 0u;
@@ -982,6 +1000,19 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         }
         const unsigned long long am = __ballot(adm);
         if (lane == 0 && am) atomicAdd(step_rec(w, L, t) + kRecAdmitted, (uint32_t)__popcll(am));
+        if (w.lattice && am) {
+            // lattice mode: every admitted candidate is a lattice arc (source
+            // position, arc, destination state: resolved to its position later)
+            uint32_t lb0 = 0u;
+            if (lane == 0) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
+            lb0 = __shfl(lb0, 0, kWave);
+            if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
+                if (lane == 0) atomicOr(&c.overflow, kOvfArena);
+            } else if (adm) {
+                w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
+                    make_int4((int)cl.tok, cl.arc, cl.dest, 0);
+            }
+        }
         if (tab.ph[L] == kPhFinal) {
             if (adm && cand_key(__uint_as_float(cl.score), cl.arc) == c.final_key)
                 final_entry(w, c, L, p, c.final_key, (int32_t)cl.tok);
@@ -1079,7 +1110,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             pick(w.tok_off, np)[q] = a0 + dpre;
             pick(w.tok_abeg, np)[q] = abeg;
             pick(w.tok_ub, np)[q] = ub;
-            if (w.has_eps) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
+            if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
+            if (w.lattice) w.lat_score[(size_t)L * w.arena + tab.arcs[L] + pi] = end;
         }
         write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
@@ -1411,6 +1443,166 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
     ph_eps_apply(w, t, k, tab);
 }
 
+// ------------------------------------------------------------------ lattice
+// Lattice mode (page section 1 "Lattice mode", section 3 on output_beam,
+// section 7 "Lattice"; epsilon-free search): finalize persists every admitted
+// candidate as a lattice arc {source position at frame t, arc, destination
+// state}, every winner's score by winners-log entry, and each frame's log base.
+// After the decode a backward pass over the steps (last to first) computes
+// bwd(token) = max over its arcs of s + bwd(destination) and keeps the arcs with
+// (fwd(source) + s) + bwd(destination) >= best - output_beam, where s is the
+// arc's own score (weight + log-prob; a final arc's weight; 0 for a redirect).
+
+// After finalize of step t: the destination state of each of the step's arcs
+// becomes its token's position at frame t + 1 (the position map of that frame).
+__global__ __launch_bounds__(kBlock) void k_lat_resolve(const Work *__restrict__ wp, int t)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    const size_t F = (size_t)w.max_frames + 3;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            // a real step the lane ran and survived
+            const bool on = c.status == kActive && c.last_step == t && t < c.T;
+            const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
+            const uint32_t a1 = min(c.lat_cursor, w.lat_cap);
+            const uint32_t n = (on && a1 > a0) ? a1 - a0 : 0u;
+            units = (n + kWave - 1) / kWave;
+            tab.n[L] = n;
+            tab.fb[L] = a0;
+            tab.par[L] = lane_par(c, t + 1);
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const int p = upar(tab.par, L);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (i >= tab.n[L]) continue;
+        int4 *r = w.lat_arc + (size_t)L * w.lat_cap + tab.fb[L] + i;
+        const int32_t d = r->z;
+        if ((uint32_t)d < (uint32_t)w.num_states) r->z = pick(w.pos, p)[(size_t)L * w.num_states + d];
+    }
+}
+
+// Before the backward pass: every backward score of a lane with a result is
+// -inf (its winners-log entries and the start token's slot).
+__global__ __launch_bounds__(kBlock) void k_lat_init(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int L = 0; L < w.max_lanes; ++L) {
+        const LaneCtl &c = w.ctl[L];
+        if (c.final_entry < 0) continue;
+        const size_t n = min(c.log_cursor, w.arena);
+        uint32_t *b = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
+        for (size_t i = tid; i < n; i += stride) b[i] = kOrdNegInf;
+        if (tid == 0) b[w.arena] = kOrdNegInf;
+    }
+}
+
+// Backward pass over the arcs of step t (launched for t = last .. 0).
+template <typename LPT>
+__global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp, int t)
+{
+    const Work &w = *wp;
+    const LpDesc d = *w.lp;
+    __shared__ LaneTab tab;
+    const size_t F = (size_t)w.max_frames + 3;
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            const bool on = c.final_entry >= 0 && t <= c.last_step;
+            const bool fin = t == c.last_step;   // the lane's final step (or its redirect)
+            const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
+            const uint32_t a1 = fin ? min(c.lat_cursor, w.lat_cap) : w.lat_aoff[(size_t)L * F + t + 1];
+            const uint32_t n = (on && a1 > a0) ? a1 - a0 : 0u;
+            units = (n + kWave - 1) / kWave;
+            tab.n[L] = n;
+            tab.fb[L] = a0;
+            tab.ph[L] = fin ? 1 : 0;
+            tab.f1[L] = c.final_score - w.output_beam;
+            tab.row[L] = c.lp_row;
+            tab.arcs[L] = t > 0 ? w.lat_fbase[(size_t)L * F + t] : 0u;                 // frame t's log base
+            tab.win[L] = (int32_t)(fin ? 0u : w.lat_fbase[(size_t)L * F + t + 1]);    // frame t + 1's
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+    const int nl = w.max_lanes;
+    const int lane = wlane();
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const bool valid = i < tab.n[L];
+        const bool fin = tab.ph[L] != 0;
+        uint32_t *bwd = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
+        bool keep = false;
+        int32_t rec[kLatFields];
+        if (valid) {
+            const int4 r = w.lat_arc[(size_t)L * w.lat_cap + tab.fb[L] + i];
+            const int32_t arc = r.y;
+            const bool redirect = (uint32_t)arc >= (uint32_t)w.num_arcs;
+            ArcDLW ad = {0, 0u, 0.0f};
+            if (!redirect) ad = w.arc_dlw[arc];
+            float sa;
+            if (fin) {
+                sa = redirect ? 0.0f : ad.weight;
+            } else {
+                const LPT *row = (const LPT *)d.base + (long long)tab.row[L] * d.stride_b + (long long)t * d.stride_t;
+                sa = ad.weight + lp_at(row, ad.ilabel);
+            }
+            const uint32_t srcpos = (uint32_t)r.x;
+            const size_t se = t > 0 ? (size_t)tab.arcs[L] + srcpos : (size_t)w.arena;   // source slot
+            const float bd = fin ? 0.0f : ord2f(bwd[(uint32_t)tab.win[L] + (uint32_t)r.z]);
+            const float v = sa + bd;
+            if (v > -__builtin_inff()) atomicMax(&bwd[se], f2ord(v));
+            const float fwd = t > 0 ? w.lat_score[(size_t)L * w.arena + se] : 0.0f;
+            const float thr = (fwd + sa) + bd;
+            keep = thr >= tab.f1[L];
+            if (keep) {
+                int32_t src_state = w.start_state;
+                if (t > 0) src_state = w.arc_dlw[w.wlog[(size_t)L * w.arena + se].y].dest;
+                rec[kLatFrame] = t;
+                rec[kLatSrc] = src_state;
+                rec[kLatDst] = (redirect || fin) ? w.super_final : ad.dest;
+                rec[kLatIlabel] = fin ? -1 : (int32_t)ad.ilabel;
+                rec[kLatArc] = arc;
+                rec[kLatScore] = (int32_t)__float_as_uint(sa);
+                rec[kLatLane] = L;
+                rec[kLatFlags] = redirect ? 2 : (fin ? 1 : 0);
+            }
+        }
+        const unsigned long long m = __ballot(keep);
+        if (m == 0ull) continue;
+        LaneCtl &c = w.ctl[L];
+        const int leader = __ffsll((long long)m) - 1;
+        uint32_t ob = 0u;
+        if (lane == leader) ob = atomicAdd(&c.lat_out_n, (uint32_t)__popcll(m));
+        ob = __shfl(ob, leader, kWave);
+        if (keep) {
+            const uint32_t oi = ob + (uint32_t)__popcll(m & mask_lt());
+            if (oi < w.lat_cap) {
+                int32_t *o = w.lat_out + ((size_t)L * w.lat_cap + oi) * kLatFields;
+#pragma unroll
+                for (int f = 0; f < kLatFields; ++f) o[f] = rec[f];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------- stream sequences
 // A stream (page section 8) holds one lane for its lifetime; every call is a
 // short sequence of the same step kernels, framed by these three. The host
@@ -1658,6 +1850,12 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamEnd: go(k_stream_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKReclass: go(k_reclass, dim3(w.max_lanes), dim3(kBlock), s, e0, e1, dw); break;
+    case kKLatResolve: go(k_lat_resolve, G, B, s, e0, e1, dw, t); break;
+    case kKLatInit: go(k_lat_init, G, B, s, e0, e1, dw); break;
+    case kKLatBack:
+        if (f16) go(k_lat_back<__half>, G, B, s, e0, e1, dw, t);
+        else go(k_lat_back<float>, G, B, s, e0, e1, dw, t);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
