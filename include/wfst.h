@@ -299,6 +299,22 @@ int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_
 int wfst_release_stream(wfst_decoder_t d, int32_t channel);
 
 /*
+ * Blank-skip frame pre-slicing before a decode (page section 3: it stays outside
+ * the decoder, WeNet-style, threshold 0.98 by default): frame t < lengths[b] of
+ * lane b is dropped iff its blank probability exceeds `threshold`, tested in
+ * binary32 as log_prob[b, t, blank_id] > (float) log(threshold); the kept rows
+ * keep their order. out_log_prob (device, [B, T, V] packed in lp_dtype, not
+ * aliasing log_prob) receives each lane's kept rows first and zeros after them;
+ * out_lengths_host [B] the kept counts. Runs on the decoder's device and stream
+ * argument like wfst_decode (its scratch is the decoder's); returns after
+ * synchronising the stream. Ranges as wfst_decode's, blank_id in [0, V),
+ * threshold > 0 finite. Errors: WFST_EINVAL, WFST_EDEVICE.
+ */
+int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
+                    const int32_t *lengths_host, int32_t blank_id, float threshold, void *out_log_prob,
+                    int32_t *out_lengths_host, void *stream);
+
+/*
  * The pruned lattice of lane `lane` in the last decode (lattice mode; section 7
  * "Lattice": flat records). *n = the number of kept arcs; the first min(*n, cap)
  * records are written to out, 8 int32 each, in no particular order:

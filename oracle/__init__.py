@@ -183,3 +183,25 @@ def decode_batch(graph, lp: np.ndarray, lengths, beam: float, max_active: int,
         return [one(b) for b in lanes]
     with ThreadPoolExecutor(max_workers=threads) as ex:
         return list(ex.map(one, lanes))
+
+
+def blank_skip(lp: np.ndarray, lengths, blank_id: int, threshold: float):
+    """Blank-skip frame pre-slicing (page section 3, "Blank-skip stays outside the
+    decoder": WeNet-style, threshold 0.98 by default). Reading: frame t < length of
+    a lane is dropped iff its blank probability exceeds the threshold, tested in
+    binary32 as lp[t, blank] > (float32) log(threshold), where the threshold is a
+    binary32 value (as the C call takes it) and its log is taken in binary64 and
+    rounded once; the kept rows keep their order. Returns (log_prob [B, T, V] with
+    the kept rows first in each lane and zeros after them, lengths int32 [B])."""
+    lp = np.asarray(lp)
+    B, T, V = lp.shape
+    lthr = np.float32(np.log(np.float64(np.float32(threshold))))
+    out = np.zeros_like(lp)
+    outl = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = int(lengths[b])
+        keep = [t for t in range(n) if not (np.float32(lp[b, t, blank_id]) > lthr)]
+        outl[b] = len(keep)
+        if keep:
+            out[b, :len(keep)] = lp[b, keep]
+    return out, outl

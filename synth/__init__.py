@@ -246,3 +246,23 @@ def random_logprobs(seed: int, batch: int, frames: int, vocab: int, sigma: float
     """Small random log_prob[B, T, V] of the workloads' family, for tests."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return _draw_logprobs(rng, batch, frames, vocab, sigma, boost, dtype)
+
+
+def drop_finals(g: Graph, seed: int, keep: float) -> Graph:
+    """``g`` with the final arc of each real state kept with probability ``keep``
+    (seed ``seed``; the start state's too): graphs with sparse finals, where a
+    lane may end without a final arc."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = g.num_states - 1
+    rs = np.asarray(g.row_splits, dtype=np.int64)
+    drop_state = rng.random(n) >= keep
+    src = np.repeat(np.arange(g.num_states), np.diff(rs))
+    drop = (np.asarray(g.ilabel) == -1) & np.concatenate([drop_state, [False]])[src]
+    keep_arc = ~drop
+    counts = np.bincount(src[keep_arc], minlength=g.num_states)
+    row_splits = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return Graph(num_states=g.num_states, start=g.start, vocab=g.vocab, epsilon_id=g.epsilon_id,
+                 row_splits=row_splits, dest=np.asarray(g.dest)[keep_arc].astype(np.int32),
+                 ilabel=np.asarray(g.ilabel)[keep_arc].astype(np.int32),
+                 olabel=np.asarray(g.olabel)[keep_arc].astype(np.int32),
+                 weight=np.asarray(g.weight)[keep_arc].astype(np.float32))

@@ -495,3 +495,35 @@ def test_lattice_at_infinite_beam_is_every_complete_path():
                 judged += 1
             assert kept <= set(through), seed
     assert judged > 500
+
+
+# ------------------------------------------------------------ blank-skip slicing
+
+def _blank_lp(case, V=3):
+    n = len(case["blank_logprob"])
+    lp = np.full((1, max(n, 1), V), -5.0, dtype=np.float32)
+    for t, x in enumerate(case["blank_logprob"]):
+        lp[0, t, 0] = np.float32(x)
+        lp[0, t, 1] = np.float32(-1.0 - t)      # marks the row
+    return lp
+
+
+@pytest.mark.parametrize("case", load_golden("blank_skip.json")["cases"], ids=lambda c: c["name"])
+def test_golden_blank_skip(case):
+    fx = load_golden("blank_skip.json")
+    assert hex(int(np.array(np.float32(np.log(np.float64(np.float32(fx["threshold"]))))).view(np.uint32))) == fx["lthr_float32_bits"]
+    lp = _blank_lp(case)
+    out, n = oracle.blank_skip(lp, [case["length"]], fx["blank_id"], fx["threshold"])
+    assert int(n[0]) == len(case["expect_kept"])
+    assert np.array_equal(out[0, :n[0]], lp[0, case["expect_kept"]])
+    assert not out[0, n[0]:].any()
+
+
+def test_blank_skip_threshold_one_keeps_everything():
+    """Log-probs are <= 0, so no blank probability exceeds a threshold of 1."""
+    lp = synth.random_logprobs(31, 3, 40, 7, boost=8.0)
+    L = np.array([40, 13, 0], np.int32)
+    out, n = oracle.blank_skip(lp, L, 0, 1.0)
+    assert np.array_equal(n, L)
+    for b in range(3):
+        assert np.array_equal(out[b, :L[b]], lp[b, :L[b]])

@@ -27,7 +27,8 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
                     "wfst_decoder_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
-                    "wfst_finalize_stream", "wfst_release_stream", "wfst_lattice_records")
+                    "wfst_finalize_stream", "wfst_release_stream", "wfst_lattice_records",
+                    "wfst_blank_skip")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
            "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
            "lat_back")
@@ -111,6 +112,7 @@ def load_library():
         lib.wfst_finalize_stream.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_release_stream.argtypes = [vp, i32]
         lib.wfst_lattice_records.argtypes = [vp, i32, vp, ctypes.c_int64, vp]
+        lib.wfst_blank_skip.argtypes = [vp, vp, i32, i32, i32, vp, i32, ctypes.c_float, vp, vp, vp]
         for name in EXPORTED_SYMBOLS:
             if name != "wfst_last_error":
                 getattr(lib, name).restype = ctypes.c_int
@@ -297,6 +299,23 @@ class Decoder:
 
     def release_stream(self, channel: int):
         _check(_lib.wfst_release_stream(self.handle, int(channel)))
+
+    def blank_skip(self, log_prob, lengths, blank_id: int = 0, threshold: float = 0.98, stream=None):
+        """Blank-skip pre-slicing on the device: returns (sliced log_prob, same
+        shape, kept rows first; kept lengths int32 [B])."""
+        import torch
+        self._check_lp(log_prob)
+        B, T, V = (int(x) for x in log_prob.shape)
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
+        if lens.shape[0] != B:
+            raise ValueError("lengths must have B entries")
+        out = torch.empty_like(log_prob)
+        outl = np.zeros(B, dtype=np.int32)
+        stream = self._stream(stream, log_prob.device)
+        _check(_lib.wfst_blank_skip(self.handle, ctypes.c_void_p(log_prob.data_ptr()), B, T, V, _ptr(lens),
+                                    int(blank_id), float(threshold), ctypes.c_void_p(out.data_ptr()), _ptr(outl),
+                                    ctypes.c_void_p(int(stream))))
+        return out, outl
 
     def lattice(self, lane: int) -> np.ndarray:
         """Kept lattice arcs of ``lane`` in the last decode (lattice mode): int32

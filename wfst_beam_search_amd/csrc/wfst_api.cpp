@@ -387,6 +387,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
     A(&d->d_plan, L * kPlanFields);
+    A(&w.bs_src, L * (size_t)c.max_frames);
+    A(&w.bs_len, L);
     if (c.lattice) {
         const size_t F = (size_t)c.max_frames + 3;
         A(&w.lat_arc, L * lat_cap);
@@ -950,5 +952,47 @@ extern "C" int wfst_lattice_records(wfst_decoder_t d, int32_t lane, int32_t *out
     if (m > 0)
         HIP_TRY(hipMemcpy(out, d->w.lat_out + (size_t)lane * d->w.lat_cap * kLatFields,
                           4 * (size_t)m * kLatFields, hipMemcpyDeviceToHost));
+    return WFST_OK;
+}
+
+extern "C" int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
+                               const int32_t *lengths_host, int32_t blank_id, float threshold, void *out_log_prob,
+                               int32_t *out_lengths_host, void *stream)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    const wfst_decoder_config &c = d->cfg;
+    if (B < 1 || B > c.max_lanes) return fail(WFST_EINVAL, "B must lie in [1, max_lanes]");
+    if (T < 0 || T > c.max_frames) return fail(WFST_EINVAL, "T must lie in [0, max_frames]");
+    if (V != d->g->vocab) return fail(WFST_EINVAL, "V differs from the graph's vocab_size");
+    if (blank_id < 0 || blank_id >= V) return fail(WFST_EINVAL, "blank_id must lie in [0, V)");
+    if (!(threshold > 0.0f) || std::isinf(threshold)) return fail(WFST_EINVAL, "threshold must be positive and finite");
+    if (!lengths_host || !out_lengths_host || (T > 0 && (!log_prob || !out_log_prob)))
+        return fail(WFST_EINVAL, "a pointer is null");
+    if (T > 0 && out_log_prob == log_prob) return fail(WFST_EINVAL, "out_log_prob must not alias log_prob");
+    for (int32_t b = 0; b < B; ++b)
+        if (lengths_host[b] < 0 || lengths_host[b] > T) return fail(WFST_EINVAL, "lengths must lie in [0, T]");
+    std::lock_guard<std::mutex> lock(d->mu);
+    HIP_TRY(hipSetDevice(d->g->device));
+    hipStream_t s = (hipStream_t)stream;
+    const size_t L = (size_t)c.max_lanes;
+    LpDesc *hd = (LpDesc *)d->h_in;
+    hd->base = log_prob;
+    hd->stride_t = V;
+    hd->stride_b = (long long)T * V;
+    hd->B = B;
+    hd->dtype = c.lp_dtype;
+    int32_t *hl = (int32_t *)((char *)d->h_in + sizeof(LpDesc));
+    for (size_t b = 0; b < L; ++b) hl[b] = (int32_t)b < B ? lengths_host[b] : 0;
+    HIP_TRY(hipMemcpyAsync(d->d_desc, hd, sizeof(LpDesc), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(d->d_lengths, hl, 4 * L, hipMemcpyHostToDevice, s));
+    if (T > 0) {
+        // the threshold as a log-probability, rounded once to binary32
+        const float lthr = (float)std::log((double)threshold);
+        HIP_TRY(launch_blank_skip(d->w, d->d_work, out_log_prob, lthr, blank_id, B, T, d->grid, s));
+        HIP_TRY(hipMemcpyAsync(out_lengths_host, d->w.bs_len, 4 * (size_t)B, hipMemcpyDeviceToHost, s));
+    } else {
+        for (int32_t b = 0; b < B; ++b) out_lengths_host[b] = 0;
+    }
+    HIP_TRY(hipStreamSynchronize(s));
     return WFST_OK;
 }

@@ -182,6 +182,9 @@ struct Work {
     float *lat_score;         // [L][arena] score of each winners-log entry's token
     uint32_t *lat_bwd;        // [L][arena + 1] ordered backward score by entry (+ the start token)
     int32_t *lat_out;         // [L][lat_cap][kLatFields] kept records
+    // blank-skip pre-slicing
+    int32_t *bs_src;          // [L][max_frames] source frame of each kept row
+    int32_t *bs_len;          // [L] kept rows
 };
 
 // Fields of a kept lattice record (int32 each).
@@ -205,6 +208,12 @@ enum : int {
 // dispatch cost grows with argument size); `w` gives host-side launch shapes.
 hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, int grid, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+
+// Blank-skip pre-slicing of the log_prob the device descriptor names (B lanes,
+// T frames, lengths in Work::lengths) into `out` (same shape): rows whose blank
+// log-prob exceeds lthr are dropped, the kept rows packed first, zeros after.
+hipError_t launch_blank_skip(const Work &w, const Work *dw, void *out, float lthr, int blank, int B, int T,
+                             int grid, hipStream_t s);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
 enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };

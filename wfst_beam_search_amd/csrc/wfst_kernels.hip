@@ -127,6 +127,14 @@ __device__ __forceinline__ int lane_phase(const LaneCtl &c, int t)
     return kPhNone;
 }
 
+// Whether lane c has a result: a final-step winner, or the redirect's best token
+// (whose entry is -1 when it is the start token: an empty path). A result's
+// score is never -inf (it was admitted, or is a token's score).
+__device__ __forceinline__ bool lane_has_result(const LaneCtl &c)
+{
+    return c.final_entry >= 0 || c.final_score > -__builtin_inff();
+}
+
 // Parity of the frontier that feeds lane c's step t of the sequence.
 __device__ __forceinline__ int lane_par(const LaneCtl &c, int t) { return (c.base + t) & 1; }
 
@@ -446,6 +454,7 @@ __global__ __launch_bounds__(kWave) void k_init(const Work *__restrict__ wp)
         c.status = kDone;
         c.overflow = 0u;
         c.final_entry = -1;
+        c.final_score = -__builtin_inff();
         c.log_open = 0u;
         c.base = 0;
         c.cnt[0] = 0ull;
@@ -1501,7 +1510,7 @@ __global__ __launch_bounds__(kBlock) void k_lat_init(const Work *__restrict__ wp
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int L = 0; L < w.max_lanes; ++L) {
         const LaneCtl &c = w.ctl[L];
-        if (c.final_entry < 0) continue;
+        if (!lane_has_result(c)) continue;
         const size_t n = min(c.log_cursor, w.arena);
         uint32_t *b = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
         for (size_t i = tid; i < n; i += stride) b[i] = kOrdNegInf;
@@ -1522,7 +1531,7 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
-            const bool on = c.final_entry >= 0 && t <= c.last_step;
+            const bool on = lane_has_result(c) && t <= c.last_step;
             const bool fin = t == c.last_step;   // the lane's final step (or its redirect)
             const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
             const uint32_t a1 = fin ? min(c.lat_cursor, w.lat_cap) : w.lat_aoff[(size_t)L * F + t + 1];
@@ -1671,7 +1680,9 @@ __global__ __launch_bounds__(kWave) void k_stream_end(const Work *__restrict__ w
 // (T was unbounded when they were made); one workgroup per ending lane gives
 // them the final class in place — first arc, degree and bound of the final arcs,
 // slot offsets by a workgroup scan in token order, strip map, slot count.
-__global__ __launch_bounds__(kBlock) void k_reclass(const Work *__restrict__ wp)
+constexpr int kReclassBlock = 1024;
+
+__global__ __launch_bounds__(kReclassBlock) void k_reclass(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
     const int L = (int)blockIdx.x;
@@ -1682,11 +1693,11 @@ __global__ __launch_bounds__(kBlock) void k_reclass(const Work *__restrict__ wp)
     const uint32_t n = (uint32_t)c.cnt[par];
     const uint32_t Q = w.frontier_cap;
     if (n > Q) return;   // an overflowed lane: its step retires it
-    __shared__ uint32_t wtot[kBlock / kWave];
+    __shared__ uint32_t wtot[kReclassBlock / kWave];
     const int wid = (int)(threadIdx.x / kWave);
     uint32_t *strips = w.strip_tok[par] + (size_t)L * w.strip_cap;
     unsigned long long run = 0;
-    for (uint32_t i0 = 0; i0 < n; i0 += kBlock) {
+    for (uint32_t i0 = 0; i0 < n; i0 += kReclassBlock) {
         const uint32_t i = i0 + threadIdx.x;
         int32_t abeg = 0;
         uint32_t deg = 0;
@@ -1698,7 +1709,7 @@ __global__ __launch_bounds__(kBlock) void k_reclass(const Work *__restrict__ wp)
         if (wlane() == 0) wtot[wid] = tot;
         __syncthreads();
         unsigned long long before = 0, all = 0;
-        for (int x = 0; x < kBlock / kWave; ++x) {
+        for (int x = 0; x < kReclassBlock / kWave; ++x) {
             if (x < wid) before += wtot[x];
             all += wtot[x];
         }
@@ -1741,7 +1752,7 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
     int32_t start = c.final_entry;
     float score = c.final_score;
     int32_t reached = c.reached_final;
-    bool has_path = start >= 0;
+    bool has_path = lane_has_result(c);
     if (want == 2) {
         start = -1;
         score = -__builtin_inff();
@@ -1815,6 +1826,83 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
     }
 }
 
+// -------------------------------------------------------- blank-skip slicing
+// Frame pre-slicing before a decode (page section 3: blank-skip stays outside
+// the decoder, WeNet-style): a frame t < length is dropped iff its blank
+// log-prob exceeds lthr = log(threshold); the kept frames keep their order.
+
+// One workgroup per lane: keep flags, a workgroup scan in frame order, the
+// source frame of every kept row and the kept count.
+constexpr int kSkipBlock = 1024;
+
+template <typename LPT>
+__global__ __launch_bounds__(kSkipBlock) void k_blank_scan(const Work *__restrict__ wp, float lthr, int blank, int T)
+{
+    const Work &w = *wp;
+    const LpDesc d = *w.lp;
+    const int b = (int)blockIdx.x;
+    if (b >= d.B) return;
+    const int len = w.lengths[b];
+    __shared__ uint32_t wtot[kSkipBlock / kWave];
+    const int wid = (int)(threadIdx.x / kWave);
+    int32_t *src = w.bs_src + (size_t)b * w.max_frames;
+    uint32_t run = 0;
+    for (int t0 = 0; t0 < T; t0 += kSkipBlock) {
+        const int t = t0 + (int)threadIdx.x;
+        bool keep = false;
+        if (t < len) {
+            const LPT *row = (const LPT *)d.base + (long long)b * d.stride_b + (long long)t * d.stride_t;
+            keep = !(lp_at(row, (uint32_t)blank) > lthr);
+        }
+        const unsigned long long m = __ballot(keep);
+        if (wlane() == 0) wtot[wid] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (int x = 0; x < kSkipBlock / kWave; ++x) {
+            if (x < wid) before += wtot[x];
+            all += wtot[x];
+        }
+        if (keep) src[run + before + (uint32_t)__popcll(m & mask_lt())] = t;
+        run += all;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) w.bs_len[b] = (int32_t)run;
+}
+
+// One wavefront per output row: the kept row's copy, or zeros past the count.
+template <typename LPT>
+__global__ __launch_bounds__(kBlock) void k_blank_copy(const Work *__restrict__ wp, LPT *__restrict__ out, int T)
+{
+    const Work &w = *wp;
+    const LpDesc d = *w.lp;
+    const int wpb = kBlock / kWave;
+    const long long rows = (long long)d.B * T;
+    for (long long r = (long long)blockIdx.x * wpb + threadIdx.x / kWave; r < rows; r += (long long)gridDim.x * wpb) {
+        const int b = (int)(r / T), i = (int)(r % T);
+        LPT *o = out + (long long)b * d.stride_b + (long long)i * d.stride_t;
+        if (i < w.bs_len[b]) {
+            const LPT *row = (const LPT *)d.base + (long long)b * d.stride_b +
+                             (long long)w.bs_src[(size_t)b * w.max_frames + i] * d.stride_t;
+            for (int v = wlane(); v < w.vocab; v += kWave) o[v] = row[v];
+        } else {
+            for (int v = wlane(); v < w.vocab; v += kWave) o[v] = (LPT)0.0f;
+        }
+    }
+}
+
+hipError_t launch_blank_skip(const Work &w, const Work *dw, void *out, float lthr, int blank, int B, int T,
+                             int grid, hipStream_t s)
+{
+    if (w.lp_dtype == 1) {
+        hipLaunchKernelGGL(k_blank_scan<__half>, dim3(B), dim3(kSkipBlock), 0, s, dw, lthr, blank, T);
+        hipLaunchKernelGGL(k_blank_copy<__half>, dim3(grid), dim3(kBlock), 0, s, dw, (__half *)out, T);
+    } else {
+        hipLaunchKernelGGL(k_blank_scan<float>, dim3(B), dim3(kSkipBlock), 0, s, dw, lthr, blank, T);
+        hipLaunchKernelGGL(k_blank_copy<float>, dim3(grid), dim3(kBlock), 0, s, dw, (float *)out, T);
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 // Plain launch, or with timing events recorded by the dispatch itself (start and
@@ -1849,7 +1937,7 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamEnd: go(k_stream_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
-    case kKReclass: go(k_reclass, dim3(w.max_lanes), dim3(kBlock), s, e0, e1, dw); break;
+    case kKReclass: go(k_reclass, dim3(w.max_lanes), dim3(kReclassBlock), s, e0, e1, dw); break;
     case kKLatResolve: go(k_lat_resolve, G, B, s, e0, e1, dw, t); break;
     case kKLatInit: go(k_lat_init, G, B, s, e0, e1, dw); break;
     case kKLatBack:
