@@ -130,9 +130,11 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
     P = wl.eps_iterations if graph.epsilon_id >= 0 else 0
     arena = min(max(1 << 20, 4 * wl.max_active * (T + 2) * (1 + P)), ((1 << 31) - 1) // B)
     dg = wb.Graph(graph, device=0)
+    if args.arena:
+        arena = args.arena
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=N, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager, grid_blocks=args.grid,
-                     path_cap=(T + 2) * (1 + P), arena_entries=arena)
+                     path_cap=(T + 2) * (1 + P), arena_entries=arena, gc_interval=args.gc_interval)
     x = torch.from_numpy(lp).to(dev)
     chunks = []
     for s in range(0, T, N):
@@ -234,6 +236,10 @@ def main():
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
     ap.add_argument("--lattice", type=float, default=None, metavar="OUTPUT_BEAM",
                     help="lattice mode: keep every admitted arc and prune with this output beam")
+    ap.add_argument("--gc-interval", type=int, default=0, metavar="N",
+                    help="compact the winners log every N steps (and per stream chunk)")
+    ap.add_argument("--arena", type=int, default=0, metavar="ENTRIES",
+                    help="winners-log entries per lane (0: the decoder's default)")
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
@@ -274,6 +280,7 @@ def main():
         return
     dg = wb.Graph(graph, device=0)
     lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice)
+    lat.update(gc_interval=args.gc_interval, arena_entries=args.arena)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
                      grid_blocks=args.grid, **lat)
@@ -342,7 +349,9 @@ def main():
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
                    "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay",
-                   **({} if args.lattice is None else {"lattice_output_beam": args.lattice})},
+                   **({} if args.lattice is None else {"lattice_output_beam": args.lattice}),
+                   **({} if not args.gc_interval else {"gc_interval": args.gc_interval}),
+                   **({} if not args.arena else {"arena_entries": args.arena})},
         "arcs_expanded_per_s": round(arcs_ps, 1),
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
@@ -350,6 +359,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    line["log_entries_at_end"] = int(st["log_entries"])
     if args.lattice is not None:
         line["lattice_kept_arcs"] = int(sum(dec.lattice(b).shape[0] for b in range(B)))
         line["lattice_arcs"] = int(st["admitted"])

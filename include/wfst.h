@@ -142,8 +142,17 @@ typedef struct wfst_graph_desc {
  *                  best the lane's result score; binary32, in that order.
  *  lattice_cap     lattice arcs (and kept records) per lane per decode
  *                  (0: 2 * max_active * (max_frames + 2), at least 2^20); in
- *                  [0, 2^28]. More
- *                  sets WFST_OVF_ARENA (the 1-best result is still exact).
+ *                  [0, 2^28]. More sets WFST_OVF_ARENA (the 1-best result is
+ *                  still exact).
+ *  gc_interval     0: the winners log keeps every entry of a decode (arena_entries
+ *                  per lane must hold them all). n > 0: after every n steps, and
+ *                  at the end of each stream chunk, a compaction round keeps only
+ *                  the entries a live token still reaches (page section 8.1):
+ *                  the log then holds the path all tokens share (about one entry
+ *                  per frame) plus the recent tree, so a small arena_entries
+ *                  serves long utterances and streams. Results are identical.
+ *                  Not with lattice mode. With n > 0 arena_entries defaults to
+ *                  max(2^20, 8 * max_active * (n + 2) * (1 + eps passes)).
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -165,6 +174,7 @@ typedef struct wfst_decoder_config {
     int32_t lattice;
     float output_beam;
     int64_t lattice_cap;
+    int32_t gc_interval;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -372,7 +382,15 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_LAT_RESOLVE 13  /* lattice: destination positions of a step's arcs         */
 #define WFST_K_LAT_INIT    14  /* lattice: backward scores to -inf                        */
 #define WFST_K_LAT_BACK    15  /* lattice: backward pass and prune of one step's arcs     */
-#define WFST_K_COUNT       16
+#define WFST_K_GC_BEGIN    16  /* log compaction round: set-up and commit                 */
+#define WFST_K_GC_MARK     17  /* log compaction: live entries from the frontier          */
+#define WFST_K_GC_SCAN     18  /* log compaction: positions of live entries               */
+#define WFST_K_GC_COMPACT  19  /* log compaction: renumbered entries into the buffer      */
+#define WFST_K_GC_COMMIT   20  /* log compaction: buffer back into the log                */
+#define WFST_K_GC_ROOTS    21  /* log compaction: the frontier's entries renumbered       */
+#define WFST_K_GC_CLEAR    22  /* log compaction: live map and counts cleared             */
+#define WFST_K_GC_END      23  /* log compaction: log end and the sealed prefix           */
+#define WFST_K_COUNT       24
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

@@ -1,0 +1,125 @@
+"""GPU tests of winners-log compaction (page section 8.1: a GC round keeps the
+entries live tokens still reach; memory bounded, results identical): decodes and
+streams with compaction rounds equal the oracle (arc ids and words bit-exact,
+scores and every per-step record), and a winners-log region too small for an
+uncompacted decode or stream suffices once rounds run."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import wfst_beam_search_amd as wb
+from gpu_util import compare_batch, gpu_decode, oracle_lanes
+from test_gpu_stream import check_stream, stream_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _case(seed, eps):
+    rng = np.random.default_rng(120_000 + seed)
+    n = int(rng.integers(3, 50))
+    vocab = int(rng.integers(2, 10))
+    g = synth.random_graph(seed + 500, n=n, deg=(1, int(rng.integers(2, 8))), vocab=vocab, epsilon=eps,
+                           eps_levels=int(rng.integers(2, 5)), self_loop=float(rng.choice([0.0, 0.3])))
+    B = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 40))
+    lp = synth.random_logprobs(seed + 9, B, T, vocab, sigma=float(rng.uniform(0.5, 3.0)))
+    L = rng.integers(0, T + 1, size=B).astype(np.int32)
+    beam = float(rng.choice([1.0, 4.0, 10.0, 1e10]))
+    ma = int(rng.choice([2, 5, 30, 1000]))
+    ap = bool(rng.integers(0, 2))
+    P = int(rng.integers(1, 4)) if eps else 0
+    gi = int(rng.choice([1, 2, 3, 7]))
+    return g, lp, L, beam, ma, ap, P, gi
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_gc_random_graphs(eps):
+    for seed in range(50):
+        g, lp, L, beam, ma, ap, P, gi = _case(seed + (300 if eps else 0), eps)
+        _say("gc random", eps, seed, lp.shape, beam, ma, ap, P, "interval", gi)
+        r, steps, _ = gpu_decode(g, lp, L, beam, ma, 0, ap, P, gc_interval=gi,
+                                 use_graphs=bool(seed % 2))
+        o = oracle_lanes(g, lp, L, beam, ma, 0, ap, P)
+        compare_batch(r, steps, o)
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_gc_workload_bounds_the_log(cid):
+    """mid-hlg-50k and the TLG: the same results with rounds every 8 steps, and
+    the compacted log holds a small fraction of the uncompacted one."""
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    lanes = [0, 1] if cid == 4 else [0, 3, 6]
+    lp2 = np.ascontiguousarray(lp[lanes])
+    L2 = L[lanes]
+    dg = wb.Graph(g)
+    try:
+        r0, _, s0 = gpu_decode(g, lp2, L2, wl.beam, wl.max_active, 0, False, wl.eps_iterations, dgraph=dg)
+        r1, steps, s1 = gpu_decode(g, lp2, L2, wl.beam, wl.max_active, 0, False, wl.eps_iterations, dgraph=dg,
+                                   gc_interval=8)
+    finally:
+        dg.release()
+    _say("log entries", s0["log_entries"], "->", s1["log_entries"])
+    o = oracle_lanes(g, lp2, L2, wl.beam, wl.max_active, 0, False, wl.eps_iterations)
+    compare_batch(r1, steps, o)
+    for b in range(len(lanes)):
+        assert np.array_equal(r0.arcs[b], r1.arcs[b])
+    assert s1["log_entries"] * 5 < s0["log_entries"]
+
+
+def test_gc_small_arena_decode():
+    """A region that an uncompacted decode overflows (arena bit) holds a
+    compacted one, with the oracle's result."""
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    lp1 = np.ascontiguousarray(lp[:2])
+    L1 = L[:2]
+    dg = wb.Graph(g)
+    try:
+        arena = 60_000
+        r0, _, _ = gpu_decode(g, lp1, L1, wl.beam, wl.max_active, 0, False, 0, dgraph=dg, with_steps=False,
+                              arena_entries=arena)
+        assert all(int(m[2]) & 4 for m in r0.meta)
+        r1, steps, _ = gpu_decode(g, lp1, L1, wl.beam, wl.max_active, 0, False, 0, dgraph=dg,
+                                  arena_entries=arena, gc_interval=4)
+    finally:
+        dg.release()
+    compare_batch(r1, steps, oracle_lanes(g, lp1, L1, wl.beam, wl.max_active))
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_gc_streams(eps):
+    for seed in range(15):
+        g, lp, L, beam, ma, ap, P, gi = _case(seed + (700 if eps else 0), eps)
+        chunk = int(np.random.default_rng(seed).choice([1, 3, 8, 16]))
+        _say("gc stream", eps, seed, lp.shape, chunk, "interval", gi)
+        check_stream(g, lp, L, chunk, beam, ma, 0, ap, P, gc_interval=gi, use_graphs=bool(seed % 2))
+
+
+def test_gc_long_stream_in_a_small_region():
+    """A 600-frame stream through a winners-log region of 60k entries: without
+    rounds it overflows; with them it ends with the oracle's online result."""
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    T = 600
+    lp1 = np.ascontiguousarray(np.concatenate([lp[0, :200], lp[1, :200], lp[2, :200]])[None])
+    L1 = np.array([T], np.int32)
+    dg = wb.Graph(g)
+    try:
+        _, _, _, fin0 = stream_run(g, lp1, L1, 32, wl.beam, wl.max_active, dgraph=dg, partial_every=1000,
+                                   arena_entries=60_000)
+        assert int(fin0[0][3][2]) & 4
+        _, _, _, fin = stream_run(g, lp1, L1, 32, wl.beam, wl.max_active, dgraph=dg, partial_every=1000,
+                                  arena_entries=60_000, gc_interval=4)
+    finally:
+        dg.release()
+    o = oracle.decode_lane(g, lp1[0], T, wl.beam, wl.max_active, online=True)
+    words, arcs, score, meta, _ = fin[0]
+    assert int(meta[2]) == 0 and list(arcs) == list(o["arcs"]) and list(words) == list(o["words"])
+    assert np.float32(score) == np.float32(o["score"])

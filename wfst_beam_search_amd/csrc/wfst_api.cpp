@@ -312,7 +312,9 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (Q * maxdeg >= (1ull << 32))
         return fail(WFST_EINVAL, "frontier_cap * (largest out-degree of one arc class) must stay below 2^32 (32-bit slot offsets)");
     uint64_t arena = c.arena_entries ? (uint64_t)c.arena_entries
-                                     : std::max<uint64_t>(1ull << 20, 4ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P));
+                   : c.gc_interval > 0
+                       ? std::max<uint64_t>(1ull << 20, 8ull * (uint64_t)c.max_active * (uint64_t)(c.gc_interval + 2) * (uint64_t)(1 + P))
+                       : std::max<uint64_t>(1ull << 20, 4ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P));
     if ((uint64_t)c.max_lanes * arena >= (1ull << 31)) {
         if (c.arena_entries) return fail(WFST_EINVAL, "max_lanes * arena_entries must stay below 2^31");
         arena = ((1ull << 31) - 1) / (uint64_t)c.max_lanes;
@@ -322,6 +324,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.lattice && P > 0) return fail(WFST_EINVAL, "lattice mode needs an epsilon-free search (eps_iterations 0 or no epsilon arcs)");
     if (c.lattice && (!(c.output_beam >= 0.0f) || std::isinf(c.output_beam))) return fail(WFST_EINVAL, "output_beam must be finite and >= 0");
     if (c.lattice_cap < 0 || c.lattice_cap > (1ll << 28)) return fail(WFST_EINVAL, "lattice_cap must lie in [0, 2^28]");
+    if (c.gc_interval < 0) return fail(WFST_EINVAL, "gc_interval must be >= 0");
+    if (c.gc_interval > 0 && c.lattice) return fail(WFST_EINVAL, "log compaction (gc_interval) does not run in lattice mode");
     const uint64_t lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
         : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
                              1ull << 28);
@@ -365,6 +369,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.lattice = c.lattice;
     w.output_beam = c.lattice ? c.output_beam : 0.0f;
     w.lat_cap = (uint32_t)lat_cap;
+    w.gc_interval = c.gc_interval;
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
     int r = WFST_OK;
@@ -389,6 +394,13 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&d->d_plan, L * kPlanFields);
     A(&w.bs_src, L * (size_t)c.max_frames);
     A(&w.bs_len, L);
+    if (c.gc_interval > 0) {
+        const size_t words = (size_t)arena / 32 + 1;
+        A(&w.gc_mark, L * words);
+        A(&w.gc_wpre, L * words);
+        A(&w.gc_child, L * (size_t)arena);
+        A(&w.gc_buf, L * (size_t)arena);
+    }
     if (c.lattice) {
         const size_t F = (size_t)c.max_frames + 3;
         A(&w.lat_arc, L * lat_cap);
@@ -412,6 +424,11 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_plan, 4 * (L * kPlanFields + 1), hipHostMallocDefault);
     if (e == hipSuccess) e = hipMemset(d->d_plan, 0, 4 * L * kPlanFields);
+    if (e == hipSuccess && c.gc_interval > 0) {
+        const size_t words = (size_t)arena / 32 + 1;
+        e = hipMemset(w.gc_mark, 0, 4 * L * words);
+        if (e == hipSuccess) e = hipMemset(w.gc_child, 0, 4 * L * (size_t)arena);
+    }
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) { delete d; return hip_fail(e, "decoder workspace"); }
@@ -448,6 +465,17 @@ static hipError_t wrap_clear(wfst_decoder_s *d, int t, int k, hipStream_t s)
     return launch(d, kKClear, t, 1, s);
 }
 
+// One winners-log compaction round (lanes that ran a real step).
+static hipError_t gc_round(wfst_decoder_s *d, hipStream_t s)
+{
+    static const int ids[] = {kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd};
+    for (int id : ids) {
+        hipError_t e = launch(d, id, 0, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Queue one whole decode of `steps` frame-loop steps on stream s.
 static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
 {
@@ -473,6 +501,8 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
             if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
         }
+        if (d->w.gc_interval > 0 && (t + 1) % d->w.gc_interval == 0 && t + 1 < steps &&
+            (e = gc_round(d, s)) != hipSuccess) return e;
     }
     if (d->w.lattice) {
         if ((e = launch(d, kKLatInit, 0, 0, s)) != hipSuccess) return e;
@@ -650,6 +680,9 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
             if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
         }
+        // every gc_interval steps and at the end of the chunk
+        if (d->w.gc_interval > 0 && ((t + 1) % d->w.gc_interval == 0 || t + 1 == steps) &&
+            (e = gc_round(d, s)) != hipSuccess) return e;
     }
     if ((e = launch(d, kKStreamEnd, 0, 0, s)) != hipSuccess) return e;
     if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
@@ -910,7 +943,7 @@ extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
     HIP_TRY(hipSetDevice(d->g->device));
     if (enable && d->ev.empty()) {
         const size_t rounds = (size_t)(d->cfg.max_frames + 2) * (size_t)(1 + d->passes);
-        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(5 + 3 * d->passes) + rounds / d->w.epoch_period;
+        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(5 + 3 * d->passes + 8) + rounds / d->w.epoch_period;
         d->ev.resize(2 * n, nullptr);
         d->ev_kind.assign(n, -1);
         for (size_t i = 0; i < 2 * n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));

@@ -99,6 +99,13 @@ struct alignas(128) LaneCtl {
     int32_t frames;            // a stream's frames so far
     int32_t want;              // result wanted after the sequence: 0 none, 1 the lane's result,
                                //   2 the partial hypothesis (best current token)
+    // winners-log compaction: entries [0, sealed) of the lane's region are the
+    // path every live token shares (never moved again); a round compacts the
+    // live entries of [sealed, log_cursor)
+    uint32_t sealed;
+    uint32_t gc_on;            // this round compacts the lane
+    uint32_t gc_live;          // live entries of the window (after the scan)
+    uint32_t gc_root0;         // local entry of the frontier's first token (epsilon-free lanes)
     alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
                                              //   step's class) << 32
     alignas(128) uint32_t nclaims[2];        // candidate-list length of the slot pass by step parity
@@ -111,6 +118,8 @@ struct alignas(128) LaneCtl {
     alignas(128) uint32_t nchanged[2];       // changed-token list sizes of closure pass k at [k & 1]
     alignas(128) uint32_t lat_cursor;        // lattice arcs persisted (lattice mode)
     alignas(128) uint32_t lat_out_n;         // lattice records kept by the prune (lattice mode)
+    alignas(128) uint32_t gc_base_children;  // live window entries whose predecessor is sealed
+    uint32_t gc_k;                           // first window position that ends the shared path
 };
 
 // Device-resident description of the caller's log_prob tensor, rewritten before
@@ -185,6 +194,12 @@ struct Work {
     // blank-skip pre-slicing
     int32_t *bs_src;          // [L][max_frames] source frame of each kept row
     int32_t *bs_len;          // [L] kept rows
+    // winners-log compaction (gc_interval > 0), per lane over its arena region
+    int32_t gc_interval;      // steps between compaction rounds (0: none)
+    uint32_t *gc_mark;        // [L][arena / 32 + 1] live bits
+    uint32_t *gc_wpre;        // [L][arena / 32 + 1] live entries before each 32-entry word
+    uint32_t *gc_child;       // [L][arena] live children by compacted position
+    int2 *gc_buf;             // [L][arena] compacted entries
 };
 
 // Fields of a kept lattice record (int32 each).
@@ -199,7 +214,8 @@ enum : int32_t { kCmdPark = 0, kCmdOpen = 1, kCmdAdvance = 2, kCmdFinish = 3 };
 enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
-    kKLatBack, kKCount
+    kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
+    kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -414,6 +414,8 @@ __device__ void init_lane(const Work &w, int L, int T)
     c.frames = 0;
     c.lat_cursor = 0u;
     c.lat_out_n = 0u;
+    c.sealed = 0u;
+    c.gc_on = 0u;
     c.cnt[1] = 0ull;
     const int32_t s = w.start_state;
     const StateInfo si = w.sinfo[s];
@@ -1826,6 +1828,285 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
     }
 }
 
+// ------------------------------------------------------ winners-log compaction
+// A compaction round (page section 8.1 and the page's winners-log GC: memory
+// bounded, results bit-identical) keeps only the winners-log entries a live
+// token still reaches, renumbered in log order, and extends the lane's sealed
+// prefix: the path every live token shares, which later rounds neither walk nor
+// move. Entries hold global ids (lane * arena + local) or -1. A round's window
+// is [sealed, log_cursor) in local ids; bit j of the live map is local entry
+// sealed + j; a live entry's compacted position is the count of live bits before
+// it. Kernels, in order: begin, mark, scan, compact, commit, roots, clear, end.
+
+// Whether lane c's round runs: it ran a real step in this sequence, is active,
+// and is not in lattice mode (lattice arrays index entries).
+__device__ __forceinline__ bool gc_due(const Work &w, const LaneCtl &c)
+{
+    return !w.lattice && c.status == kActive && c.last_step >= 0 && c.last_step < c.T;
+}
+
+// Round set-up, one thread per lane: the compaction of the lane's last step is
+// committed (its entries are the roots' own), counters reset.
+__global__ __launch_bounds__(kWave) void k_gc_begin(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    const bool on = gc_due(w, c);
+    c.gc_on = on ? 1u : 0u;
+    if (!on) return;
+    const int p = lane_par(c, c.last_step + 1);
+    commit_log(w, c, L, c.last_step, (uint32_t)pair_at(c.cnt, p));
+    c.gc_base_children = 0u;
+    c.gc_k = 0xFFFFFFFFu;
+    c.gc_live = 0u;
+}
+
+// Per-lane table of a round: units of `what` (0: the frontier's tokens, 1: the
+// window's entries, 2: the live entries, 3: the window's 32-entry words), the
+// frontier parity, the window [sealed, cursor).
+__device__ __forceinline__ void gc_prologue(const Work &w, LaneTab &tab, int what)
+{
+    if (threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t units = 0;
+        if (L < w.max_lanes) {
+            const LaneCtl &c = w.ctl[L];
+            const int p = lane_par(c, c.last_step + 1);
+            const uint32_t n = (uint32_t)pair_at(c.cnt, p);
+            const uint32_t win = c.log_cursor > c.sealed ? c.log_cursor - c.sealed : 0u;
+            uint32_t items = 0;
+            if (c.gc_on && n <= w.frontier_cap && c.log_cursor <= w.arena)
+                items = what == 0 ? n : what == 1 ? win : what == 2 ? c.gc_live : (win + 31u) / 32u;
+            units = (items + kWave - 1) / kWave;
+            tab.n[L] = items;
+            tab.arcs[L] = c.sealed;
+            tab.par[L] = p;
+            tab.fb[L] = c.log_cursor;
+        }
+        tab_publish(tab, w.max_lanes, units);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ size_t gc_words(const Work &w) { return (size_t)w.arena / 32 + 1; }
+
+// Compacted position of live window entry j.
+__device__ __forceinline__ uint32_t gc_pos(const uint32_t *mark, const uint32_t *wpre, uint32_t j)
+{
+    return wpre[j >> 5] + (uint32_t)__popc(mark[j >> 5] & ((1u << (j & 31u)) - 1u));
+}
+
+// Marking: every frontier token walks its chain back through the window, setting
+// live bits, and stops at the first entry already marked (or sealed, or -1).
+__global__ __launch_bounds__(kBlock) void k_gc_mark(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    gc_prologue(w, tab, 0);
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const int p = upar(tab.par, L);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (i >= tab.n[L]) continue;
+        const uint32_t sealed = tab.arcs[L], cursor = tab.fb[L];
+        uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
+        const long long lbase = (long long)L * w.arena;
+        const int32_t ge = pick(w.tok_entry, p)[(size_t)L * w.frontier_cap + i];
+        long long e = ge < 0 ? -1 : (long long)ge - lbase;   // the start token has no entry
+        while (e >= (long long)sealed && e < (long long)cursor) {
+            const uint32_t j = (uint32_t)(e - sealed), bit = 1u << (j & 31u);
+            if (atomicOr(&mark[j >> 5], bit) & bit) break;
+            const int32_t prev = w.wlog[lbase + e].x;
+            e = prev < 0 ? -1 : (long long)prev - lbase;
+        }
+    }
+}
+
+// Prefix counts of live entries by 32-entry word, one workgroup per lane.
+constexpr int kGcScanBlock = 1024;
+
+__global__ __launch_bounds__(kGcScanBlock) void k_gc_scan(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    const int p = lane_par(c, c.last_step + 1);
+    if (!c.gc_on || c.log_cursor > w.arena || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
+    const uint32_t win = c.log_cursor > c.sealed ? c.log_cursor - c.sealed : 0u;
+    const uint32_t nw = (win + 31u) / 32u;
+    const uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
+    uint32_t *wpre = w.gc_wpre + (size_t)L * gc_words(w);
+    __shared__ uint32_t wtot[kGcScanBlock / kWave];
+    const int wid = (int)(threadIdx.x / kWave);
+    uint32_t run = 0;
+    for (uint32_t x0 = 0; x0 < nw; x0 += kGcScanBlock) {
+        const uint32_t x = x0 + threadIdx.x;
+        const uint32_t cnt = x < nw ? (uint32_t)__popc(mark[x]) : 0u;
+        uint32_t tot;
+        const uint32_t pre = wave_excl_sum(cnt, &tot);
+        if (wlane() == 0) wtot[wid] = tot;
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (int k = 0; k < kGcScanBlock / kWave; ++k) {
+            if (k < wid) before += wtot[k];
+            all += wtot[k];
+        }
+        if (x < nw) wpre[x] = run + before + pre;
+        run += all;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) c.gc_live = run;
+}
+
+// Compaction into the lane's buffer: each live window entry at its position,
+// its predecessor renumbered; live-children counts by position (children of the
+// sealed prefix's last entry, or of the start token, counted apart).
+__global__ __launch_bounds__(kBlock) void k_gc_compact(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    gc_prologue(w, tab, 1);
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t j = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (j >= tab.n[L]) continue;
+        const uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
+        if (!((mark[j >> 5] >> (j & 31u)) & 1u)) continue;
+        const uint32_t *wpre = w.gc_wpre + (size_t)L * gc_words(w);
+        const uint32_t sealed = tab.arcs[L];
+        const long long lbase = (long long)L * w.arena;
+        const int2 r = w.wlog[lbase + sealed + j];
+        int32_t np = r.x;
+        const long long pe = r.x < 0 ? -1 : (long long)r.x - lbase;
+        if (pe >= (long long)sealed) {
+            const uint32_t pp = gc_pos(mark, wpre, (uint32_t)(pe - sealed));
+            np = (int32_t)(lbase + sealed + pp);
+            atomicAdd(&w.gc_child[(size_t)L * w.arena + pp], 1u);
+        } else {
+            atomicAdd(&w.ctl[L].gc_base_children, 1u);
+        }
+        w.gc_buf[(size_t)L * w.arena + gc_pos(mark, wpre, j)] = make_int2(np, r.y);
+    }
+}
+
+// The buffer back into the log; a position without exactly one live child ends
+// the shared path (one atomic per 64 positions: the first such one).
+__global__ __launch_bounds__(kBlock) void k_gc_commit(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    gc_prologue(w, tab, 2);
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        const bool valid = i < tab.n[L];
+        bool ends = false;
+        if (valid) {
+            const size_t q = (size_t)L * w.arena + i;
+            w.wlog[(long long)L * w.arena + tab.arcs[L] + i] = w.gc_buf[q];
+            ends = w.gc_child[q] != 1u;
+        }
+        const unsigned long long m = __ballot(ends);
+        if (m && wlane() == __ffsll((long long)m) - 1) atomicMin(&w.ctl[L].gc_k, i);
+    }
+}
+
+// The frontier's entries renumbered (an epsilon-free frontier's base too). Every
+// frontier token's entry lies at or after its compaction's base, so the base's
+// position bounds the shared path.
+__global__ __launch_bounds__(kBlock) void k_gc_roots(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    gc_prologue(w, tab, 0);
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const int p = upar(tab.par, L);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (i >= tab.n[L]) continue;
+        const uint32_t sealed = tab.arcs[L], cursor = tab.fb[L];
+        const uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
+        const uint32_t *wpre = w.gc_wpre + (size_t)L * gc_words(w);
+        const long long lbase = (long long)L * w.arena;
+        LaneCtl &c = w.ctl[L];
+        int32_t *te = pick(w.tok_entry, p) + (size_t)L * w.frontier_cap + i;
+        const int32_t ge = *te;
+        if (ge >= 0) {
+            const long long e = (long long)ge - lbase;
+            if (e >= (long long)sealed && e < (long long)cursor)
+                *te = (int32_t)(lbase + sealed + gc_pos(mark, wpre, (uint32_t)(e - sealed)));
+        }
+        if (i == 0) {
+            const uint32_t fb = c.front_base[p];
+            if (fb != 0xFFFFFFFFu && fb >= sealed && fb < cursor) {
+                // live entries before the base (the base itself may be dead on an
+                // epsilon lane whose first token was replaced)
+                const uint32_t pos = gc_pos(mark, wpre, fb - sealed);
+                atomicMin(&c.gc_k, pos);
+                // the epsilon-free frontier's entries are its base plus the token's
+                // position: the base moves with token 0's entry
+                if (!w.has_eps) c.front_base[p] = sealed + pos;
+            }
+        }
+    }
+}
+
+// Clears the round's live map and child counts.
+__global__ __launch_bounds__(kBlock) void k_gc_clear(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    gc_prologue(w, tab, 3);
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t x = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        if (x >= tab.n[L]) continue;
+        w.gc_mark[(size_t)L * gc_words(w) + x] = 0u;
+        // the child counts of positions 32x .. 32x + 31
+        for (uint32_t k = 0; k < 32u; ++k) {
+            const size_t q = (size_t)x * 32u + k;
+            if (q < (size_t)w.arena) w.gc_child[(size_t)L * w.arena + q] = 0u;
+        }
+    }
+}
+
+// End of a round, one thread per lane: the log ends after the live entries, and
+// the sealed prefix grows by the shared path (positions 0 .. k of the window,
+// when exactly one live entry hangs off the old prefix).
+__global__ __launch_bounds__(kWave) void k_gc_end(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)threadIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    const int p = lane_par(c, c.last_step + 1);
+    if (!c.gc_on || c.log_cursor > w.arena || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
+    const uint32_t live = c.gc_live;
+    uint32_t grow = 0;
+    if (c.gc_base_children == 1u && live > 0u) grow = min(c.gc_k, live - 1u) + 1u;
+    c.log_cursor = c.sealed + live;
+    c.sealed += grow;
+    c.gc_on = 0u;
+}
+
 // -------------------------------------------------------- blank-skip slicing
 // Frame pre-slicing before a decode (page section 3: blank-skip stays outside
 // the decoder, WeNet-style): a frame t < length is dropped iff its blank
@@ -1944,6 +2225,14 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         if (f16) go(k_lat_back<__half>, G, B, s, e0, e1, dw, t);
         else go(k_lat_back<float>, G, B, s, e0, e1, dw, t);
         break;
+    case kKGcBegin: go(k_gc_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
+    case kKGcMark: go(k_gc_mark, G, B, s, e0, e1, dw); break;
+    case kKGcScan: go(k_gc_scan, dim3(w.max_lanes), dim3(kGcScanBlock), s, e0, e1, dw); break;
+    case kKGcCompact: go(k_gc_compact, G, B, s, e0, e1, dw); break;
+    case kKGcCommit: go(k_gc_commit, G, B, s, e0, e1, dw); break;
+    case kKGcRoots: go(k_gc_roots, G, B, s, e0, e1, dw); break;
+    case kKGcClear: go(k_gc_clear, G, B, s, e0, e1, dw); break;
+    case kKGcEnd: go(k_gc_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
