@@ -240,6 +240,9 @@ def main():
                     help="compact the winners log every N steps (and per stream chunk)")
     ap.add_argument("--arena", type=int, default=0, metavar="ENTRIES",
                     help="winners-log entries per lane (0: the decoder's default)")
+    ap.add_argument("--arena-commit", type=int, default=0, metavar="ENTRIES",
+                    help="winners-log entries per lane committed at creation (0: the decoder's "
+                         "lazy default, -1: the whole region)")
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
@@ -280,7 +283,7 @@ def main():
         return
     dg = wb.Graph(graph, device=0)
     lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice)
-    lat.update(gc_interval=args.gc_interval, arena_entries=args.arena)
+    lat.update(gc_interval=args.gc_interval, arena_entries=args.arena, arena_commit=args.arena_commit)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
                      grid_blocks=args.grid, **lat)
@@ -360,6 +363,8 @@ def main():
         "cpu_baseline": cpu,
     }
     line["log_entries_at_end"] = int(st["log_entries"])
+    line["log_bytes_committed"] = int(st["log_committed_bytes"])
+    line["log_bytes_reserved"] = int(st["log_reserved_bytes"])
     if args.lattice is not None:
         line["lattice_kept_arcs"] = int(sum(dec.lattice(b).shape[0] for b in range(B)))
         line["lattice_arcs"] = int(st["admitted"])

@@ -153,6 +153,19 @@ typedef struct wfst_graph_desc {
  *                  serves long utterances and streams. Results are identical.
  *                  Not with lattice mode. With n > 0 arena_entries defaults to
  *                  max(2^20, 8 * max_active * (n + 2) * (1 + eps passes)).
+ *  arena_commit    how much of the winners-log regions is backed by memory
+ *                  (page section 6.2, lazily committed regions): the whole
+ *                  max_lanes * arena_entries range is reserved as address space
+ *                  at creation, and 4 MiB chunks are mapped behind it as lanes
+ *                  need them. 0: commit min(arena_entries, 2^19) entries per lane
+ *                  first; n > 0: min(arena_entries, n) first; -1: one plain
+ *                  allocation of the whole range (as on a device without virtual
+ *                  memory management, where the others do the same). A decode in
+ *                  which a lane outgrows the committed part commits more (at
+ *                  least double, aimed at the longest lane's end) and runs again
+ *                  on the same inputs, so results are those of a fully committed
+ *                  region; wfst_decoder_stats reports the re-runs. Creating a
+ *                  stream commits the whole range (a stream cannot run again).
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -175,6 +188,7 @@ typedef struct wfst_decoder_config {
     float output_beam;
     int64_t lattice_cap;
     int32_t gc_interval;
+    int64_t arena_commit;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -340,16 +354,19 @@ int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T
 int wfst_lattice_records(wfst_decoder_t d, int32_t lane, int32_t *out, int64_t cap, int64_t *n);
 
 /*
- * Counters of the last decode or stream call, summed over its lanes (n up to 14 values):
+ * Counters of the last decode or stream call, summed over its lanes (n up to 17 values):
  *  [0] candidate arcs expanded on real and final steps, [1] admitted candidates,
  *  [2] distinct admitted destinations, [3] frontier tokens expanded (sum of
  *  frontier sizes), [4] epsilon arcs relaxed, [5] epsilon candidates admitted,
  *  [6] epsilon destinations claimed, [7] tokens appended or replaced by the
  *  closure, [8] winners-log entries written, [9] steps run (frame loop length),
- *  [10] largest frontier, [11] device bytes reserved by the decoder,
+ *  [10] largest frontier, [11] device bytes held by the decoder and its graph
+ *  (the winners log as committed),
  *  [12] real (frame) steps run, summed over lanes, [13] candidates listed by
  *  the slot passes (a superset of [1]: every candidate above the running
- *  maximum minus the beam while the exact maximum was still being found).
+ *  maximum minus the beam while the exact maximum was still being found),
+ *  [14] winners-log address space reserved (bytes), [15] winners-log bytes
+ *  committed, [16] runs of the last decode repeated after a commit (0: none).
  */
 int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 

@@ -37,6 +37,25 @@ def test_header_and_library_agree(lib):
         assert hasattr(lib, name), name
 
 
+_CTYPES = {"float": ctypes.c_float, "int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64}
+
+
+@pytest.mark.parametrize("name,cls", [("wfst_decoder_config", wb._Config), ("wfst_graph_desc", wb._GraphDesc)])
+def test_binding_structs_match_header(name, cls):
+    """The binding's ctypes structs list the header's fields in the same order
+    with the same types, so the C library reads what Python writes."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "wfst.h")).read(), flags=re.S)
+    body = re.search(r"typedef struct " + name + r"\s*\{(.*?)\}\s*" + name + ";", src, flags=re.S).group(1)
+    fields = re.findall(r"([A-Za-z_][A-Za-z0-9_ ]*?[\s*]+)([a-z_]+)\s*;", body)
+    assert [f for _, f in fields] == [f for f, _ in cls._fields_]
+    for (ctype, fname), (pname, ptype) in zip(fields, cls._fields_):
+        ctype = ctype.strip()
+        if "*" in ctype:
+            assert ptype is ctypes.c_void_p, fname
+        else:
+            assert _CTYPES[ctype] is ptype, fname
+
+
 def _good_spec():
     return {"start": 0, "vocab": 3, "epsilon_id": -1,
             "states": [[[1, 1, 5, -0.5], [0, 2, 0, -1.0], [2, -1, 0, 0.0]],

@@ -1,8 +1,11 @@
-"""GPU tests of winners-log compaction (page section 8.1: a GC round keeps the
-entries live tokens still reach; memory bounded, results identical): decodes and
-streams with compaction rounds equal the oracle (arc ids and words bit-exact,
-scores and every per-step record), and a winners-log region too small for an
-uncompacted decode or stream suffices once rounds run."""
+"""GPU tests of the winners log's memory: compaction (page section 8.1: a GC
+round keeps the entries live tokens still reach; memory bounded, results
+identical) and lazily committed regions (section 6.2: address space reserved
+once, memory mapped as the logs grow, a decode that outgrows it run again).
+Decodes and streams with compaction rounds equal the oracle (arc ids and words
+bit-exact, scores and every per-step record), a winners-log region too small for
+an uncompacted decode or stream suffices once rounds run, and a decoder whose
+regions start nearly empty returns the fully committed decoder's results."""
 
 import numpy as np
 import pytest
@@ -123,3 +126,47 @@ def test_gc_long_stream_in_a_small_region():
     words, arcs, score, meta, _ = fin[0]
     assert int(meta[2]) == 0 and list(arcs) == list(o["arcs"]) and list(words) == list(o["words"])
     assert np.float32(score) == np.float32(o["score"])
+
+
+def test_lazy_region_commits_on_demand():
+    """A first commitment of 4096 entries per lane: the first decode outgrows it,
+    commits more and runs again; its result is the oracle's and the fully
+    committed decoder's, and the next decode runs once."""
+    import torch
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    lanes = [0, 3, 6]
+    lp2 = np.ascontiguousarray(lp[lanes])
+    L2 = L[lanes]
+    dg = wb.Graph(g)
+    try:
+        dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=3, max_frames=lp2.shape[1], arena_commit=4096)
+        x = torch.from_numpy(lp2).cuda()
+        r1 = dec.decode(x, L2)
+        s1 = dec.stats()
+        r2 = dec.decode(x, L2)
+        s2 = dec.stats()
+        steps = [dec.step_stats(b) for b in range(3)]
+        dec.close()
+        rf, _, sf = gpu_decode(g, lp2, L2, wl.beam, wl.max_active, dgraph=dg, with_steps=False, arena_commit=-1)
+    finally:
+        dg.release()
+    _say("lazy", s1["regrows"], s1["log_committed_bytes"], "of", s1["log_reserved_bytes"], "entries", s1["log_entries"])
+    assert s1["regrows"] >= 1 and s2["regrows"] == 0
+    assert s1["log_entries"] * 8 <= s1["log_committed_bytes"] < s1["log_reserved_bytes"]
+    assert sf["log_committed_bytes"] >= sf["log_reserved_bytes"] and sf["regrows"] == 0
+    compare_batch(r2, steps, oracle_lanes(g, lp2, L2, wl.beam, wl.max_active))
+    for b in range(3):
+        for r in (r1, rf):
+            assert np.array_equal(r.arcs[b], r2.arcs[b]) and np.array_equal(r.words[b], r2.words[b])
+            assert np.float32(r.scores[b]) == np.float32(r2.scores[b]) and np.array_equal(r.meta[b], r2.meta[b])
+
+
+@pytest.mark.parametrize("gi", [0, 3])
+def test_lazy_region_streams(gi):
+    """Streams on a decoder whose regions start with 2048 committed entries per
+    lane: opening a stream commits the whole region, results are the oracle's."""
+    for seed in range(4):
+        g, lp, L, beam, ma, ap, P, _ = _case(seed + 900, bool(seed % 2))
+        _say("lazy stream", seed, lp.shape, "interval", gi)
+        check_stream(g, lp, L, 5, beam, ma, 0, ap, P, gc_interval=gi, arena_commit=2048)

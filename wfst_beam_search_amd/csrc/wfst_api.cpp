@@ -56,6 +56,115 @@ int dalloc(T **p, size_t count, std::vector<void *> *owned, size_t *bytes)
 }
 
 
+// The winners log as a lazily committed region (page section 6.2): the whole
+// max_lanes x arena range is reserved as device address space once, so every
+// pointer a kernel or a captured graph holds stays valid, and physical chunks
+// are mapped behind it only where the lanes' logs reach. Lane L's region is
+// [L * arena, L * arena + lim) in entries; the chunks covering those ranges for
+// the current lim are mapped (a chunk may straddle two lanes' ranges).
+struct LogRegion {
+    bool vmm = false;                 // false: one plain allocation, all committed
+    int device = 0;
+    char *va = nullptr;
+    size_t va_bytes = 0;
+    size_t chunk = 0;                 // mapping unit, bytes
+    std::vector<hipMemGenericAllocationHandle_t> h;   // by chunk, null = unmapped
+    size_t mapped = 0;                // chunks mapped
+    uint32_t lanes = 0, arena = 0, lim = 0;
+
+    // Reserves the range (falls back to a plain allocation when the device has
+    // no virtual memory management) and commits lim0 entries per lane.
+    hipError_t init(int dev, uint32_t L, uint32_t arena_entries, uint32_t lim0, bool lazy)
+    {
+        device = dev; lanes = L; arena = arena_entries;
+        const size_t need = (size_t)L * arena * sizeof(int2);
+        int vmm_ok = 0;
+        if (lazy && hipDeviceGetAttribute(&vmm_ok, hipDeviceAttributeVirtualMemoryManagementSupported, dev) != hipSuccess)
+            vmm_ok = 0;
+        size_t gran = 0;
+        hipMemAllocationProp prop = props();
+        if (vmm_ok && (hipMemGetAllocationGranularity(&gran, &prop, hipMemAllocationGranularityMinimum) != hipSuccess ||
+                       gran == 0))
+            vmm_ok = 0;
+        if (vmm_ok) {
+            // 4 MiB units: few mappings for a large log, little waste for a small one
+            chunk = ((std::max<size_t>(4u << 20, gran) + gran - 1) / gran) * gran;
+            va_bytes = (need + chunk - 1) / chunk * chunk;
+            void *p = nullptr;
+            if (hipMemAddressReserve(&p, va_bytes, chunk, nullptr, 0) == hipSuccess) {
+                vmm = true;
+                va = (char *)p;
+                h.assign(va_bytes / chunk, hipMemGenericAllocationHandle_t{});
+                return commit(lim0);
+            }
+        }
+        vmm = false;
+        va_bytes = need;
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, std::max<size_t>(need, 1));
+        if (e != hipSuccess) return e;
+        va = (char *)p;
+        lim = arena;
+        return hipSuccess;
+    }
+
+    static hipMemAllocationProp props_for(int dev)
+    {
+        hipMemAllocationProp p{};
+        p.type = hipMemAllocationTypePinned;
+        p.location.type = hipMemLocationTypeDevice;
+        p.location.id = dev;
+        return p;
+    }
+    hipMemAllocationProp props() const { return props_for(device); }
+
+    // Maps the chunks covering every lane's first n entries (lim never shrinks).
+    hipError_t commit(uint32_t n)
+    {
+        n = std::min(n, arena);
+        if (!vmm || n <= lim) return hipSuccess;
+        const hipMemAllocationProp prop = props();
+        hipMemAccessDesc acc{};
+        acc.location = prop.location;
+        acc.flags = hipMemAccessFlagsProtReadWrite;
+        for (uint32_t L = 0; L < lanes; ++L) {
+            const size_t b0 = ((size_t)L * arena + lim) * sizeof(int2);
+            const size_t b1 = ((size_t)L * arena + n) * sizeof(int2);
+            for (size_t k = b0 / chunk; k < (b1 + chunk - 1) / chunk; ++k) {
+                if (h[k]) continue;
+                hipMemGenericAllocationHandle_t x{};
+                hipError_t e = hipMemCreate(&x, chunk, &prop, 0);
+                if (e != hipSuccess) return e;
+                e = hipMemMap(va + k * chunk, chunk, 0, x, 0);
+                if (e != hipSuccess) { (void)hipMemRelease(x); return e; }
+                h[k] = x;
+                ++mapped;
+                e = hipMemSetAccess(va + k * chunk, chunk, &acc, 1);
+                if (e != hipSuccess) return e;
+            }
+        }
+        lim = n;
+        return hipSuccess;
+    }
+
+    size_t committed_bytes() const { return vmm ? mapped * chunk : va_bytes; }
+
+    void release()
+    {
+        if (!va) return;
+        if (vmm) {
+            for (size_t k = 0; k < h.size(); ++k)
+                if (h[k]) { (void)hipMemUnmap(va + k * chunk, chunk); (void)hipMemRelease(h[k]); }
+            (void)hipMemAddressFree(va, va_bytes);
+        } else {
+            (void)hipFree(va);
+        }
+        va = nullptr;
+        h.clear();
+        mapped = 0;
+    }
+};
+
 }  // namespace
 
 struct wfst_graph_s {
@@ -111,6 +220,8 @@ struct wfst_decoder_s {
     std::vector<hipEvent_t> ev;
     std::vector<int> ev_kind;
     size_t ev_used = 0;
+    LogRegion log;                   // the winners log (w.wlog)
+    int last_regrows = 0;            // re-decodes of the last decode after the log grew
 
     ~wfst_decoder_s()
     {
@@ -123,6 +234,7 @@ struct wfst_decoder_s {
         if (h_res) (void)hipHostFree(h_res);
         if (h_plan) (void)hipHostFree(h_plan);
         for (void *p : owned) (void)hipFree(p);
+        log.release();
         if (g && g->refs.fetch_sub(1) == 1) delete g;
     }
 };
@@ -325,6 +437,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.lattice && (!(c.output_beam >= 0.0f) || std::isinf(c.output_beam))) return fail(WFST_EINVAL, "output_beam must be finite and >= 0");
     if (c.lattice_cap < 0 || c.lattice_cap > (1ll << 28)) return fail(WFST_EINVAL, "lattice_cap must lie in [0, 2^28]");
     if (c.gc_interval < 0) return fail(WFST_EINVAL, "gc_interval must be >= 0");
+    if (c.arena_commit < -1) return fail(WFST_EINVAL, "arena_commit must be >= -1");
     if (c.gc_interval > 0 && c.lattice) return fail(WFST_EINVAL, "log compaction (gc_interval) does not run in lattice mode");
     const uint64_t lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
         : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
@@ -388,7 +501,6 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     A(&w.best, L * S);
     A(&w.claims, L * CC);
     if (P > 0) { A(&w.dec, L * CC); A(&w.dec_dest, L * CC); }
-    A(&w.wlog, L * arena);
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
     A(&d->d_plan, L * kPlanFields);
@@ -411,6 +523,15 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         A(&w.lat_out, L * lat_cap * kLatFields);
     }
     if (r != WFST_OK) { delete d; return r; }
+    {
+        const uint64_t lim0 = c.arena_commit < 0 ? arena
+                            : c.arena_commit > 0 ? std::min<uint64_t>((uint64_t)c.arena_commit, arena)
+                                                 : std::min<uint64_t>(arena, 1ull << 19);
+        hipError_t e = d->log.init(g->device, (uint32_t)L, (uint32_t)arena, (uint32_t)lim0, c.arena_commit >= 0);
+        if (e != hipSuccess) { delete d; return hip_fail(e, "winners-log region"); }
+        w.wlog = (int2 *)d->log.va;
+        w.arena_lim = d->log.lim;
+    }
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
     w.round_base = 0;
     d->chan_open.assign(L, 0);
@@ -544,6 +665,19 @@ static int set_round_base(wfst_decoder_s *d, uint32_t v, hipStream_t s)
     return WFST_OK;
 }
 
+// Commits n winners-log entries per lane and publishes the bound to the
+// kernels (their Work copy). The caller has no kernel of this decoder in flight
+// that the new bound could matter to.
+static int grow_log(wfst_decoder_s *d, uint32_t n)
+{
+    if (n <= d->log.lim) return WFST_OK;
+    hipError_t e = d->log.commit(n);
+    if (e != hipSuccess) return hip_fail(e, "winners-log commit");
+    d->w.arena_lim = d->log.lim;
+    HIP_TRY(hipMemcpy((char *)d->d_work + offsetof(Work, arena_lim), &d->w.arena_lim, 4, hipMemcpyHostToDevice));
+    return WFST_OK;
+}
+
 // Copies result block `lane` (already in h_res) to output row j.
 static void copy_result(const wfst_decoder_s *d, int lane, int j, int32_t *out_words, int32_t words_cap,
                         int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
@@ -607,28 +741,52 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     HIP_TRY(hipMemcpyAsync(d->d_lengths, hl, 4 * L, hipMemcpyHostToDevice, s));
 
     const int steps = maxlen + 1;
-    // timing events cannot be read back from a replayed graph: a profiled decode
-    // runs the same kernels as plain launches
-    if (c.use_graphs && !d->prof_on) {
-        int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
-        bucket = std::min(bucket, c.max_frames + 1);
-        hipGraphExec_t ex = nullptr;
-        int rc = graph_for(d, bucket, &ex);
-        if (rc != WFST_OK) return rc;
-        HIP_TRY(hipGraphLaunch(ex, s));
-        d->last_steps = bucket;
-    } else {
-        hipError_t e = enqueue_decode(d, steps, s);
-        if (e != hipSuccess) return hip_fail(e, "kernel launch");
-        d->last_steps = steps;
-    }
-    // later stream sequences number their rounds on from this decode's (its
-    // entries are still in the table)
-    d->round_next = (uint64_t)(d->last_steps + 1) * (uint64_t)(1 + d->passes);
-    d->last_profiled = d->prof_on;
     const size_t rs = d->w.res_stride;
-    HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
+    d->last_regrows = 0;
+    for (;;) {
+        // timing events cannot be read back from a replayed graph: a profiled
+        // decode runs the same kernels as plain launches
+        if (c.use_graphs && !d->prof_on) {
+            int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
+            bucket = std::min(bucket, c.max_frames + 1);
+            hipGraphExec_t ex = nullptr;
+            int rc = graph_for(d, bucket, &ex);
+            if (rc != WFST_OK) return rc;
+            HIP_TRY(hipGraphLaunch(ex, s));
+            d->last_steps = bucket;
+        } else {
+            hipError_t e = enqueue_decode(d, steps, s);
+            if (e != hipSuccess) return hip_fail(e, "kernel launch");
+            d->last_steps = steps;
+        }
+        // later stream sequences number their rounds on from this decode's (its
+        // entries are still in the table)
+        d->round_next = (uint64_t)(d->last_steps + 1) * (uint64_t)(1 + d->passes);
+        d->last_profiled = d->prof_on;
+        HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        // a lane whose log outgrew the committed part of its region: commit more
+        // (page section 6.2: grow and decode again; a decode starts from nothing,
+        // so the result is the one a fully committed region gives)
+        if (d->log.lim >= d->w.arena) break;
+        bool grow = false;
+        for (int32_t b = 0; b < B; ++b)
+            grow |= (d->h_res[rs * (size_t)b + kResOverflow] & kOvfArena) != 0;
+        if (!grow) break;
+        // the log grows about linearly with the frames: aim at the longest lane's
+        // end from the step where the first one stopped, at least doubling
+        std::vector<LaneCtl> ctl((size_t)c.max_lanes);
+        HIP_TRY(hipMemcpy(ctl.data(), d->ctl, sizeof(LaneCtl) * ctl.size(), hipMemcpyDeviceToHost));
+        uint64_t want = 2ull * d->log.lim;
+        for (int32_t b = 0; b < B; ++b) {
+            if (!(d->h_res[rs * (size_t)b + kResOverflow] & kOvfArena)) continue;
+            const uint64_t done = (uint64_t)std::max(ctl[(size_t)b].last_step, 0) + 1;
+            want = std::max<uint64_t>(want, (uint64_t)d->log.lim * ((uint64_t)lengths_host[b] + 2) * 5 / (4 * done));
+        }
+        int rc = grow_log(d, (uint32_t)std::min<uint64_t>(want, d->w.arena));
+        if (rc != WFST_OK) return rc;
+        d->last_regrows += 1;
+    }
 
     d->last_len.assign(L, -1);
     for (int32_t b = 0; b < B; ++b) d->last_len[(size_t)b] = lengths_host[b];
@@ -768,6 +926,13 @@ extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *chann
         if (!d->chan_open[(size_t)L]) { lane = L; break; }
     if (lane < 0) return WFST_OK;   // every lane holds a stream
     HIP_TRY(hipSetDevice(d->g->device));
+    // a stream cannot be decoded again: its lane's whole region is committed
+    // (streams wait for the device before a commit, see grow_log)
+    if (d->log.lim < d->w.arena) {
+        HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+        int rc0 = grow_log(d, d->w.arena);
+        if (rc0 != WFST_OK) return rc0;
+    }
     plan_clear(d);
     d->h_plan[lane * kPlanFields + kPlanCmd] = kCmdOpen;
     int rc = run_stream(d, kSeqOpen, 0, (hipStream_t)stream, {});
@@ -882,7 +1047,7 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
 {
     if (!d || !out || n < 0) return fail(WFST_EINVAL, "bad arguments");
     std::lock_guard<std::mutex> lock(d->mu);
-    int64_t v[14] = {0};
+    int64_t v[17] = {0};
     bool any = false;
     for (int32_t x : d->last_len) any |= x >= 0;
     if (any) {
@@ -908,8 +1073,11 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
             if (d->last_len[(size_t)b] >= 0) v[8] += ctl[(size_t)b].log_cursor;
     }
     v[9] = d->last_steps;
-    v[11] = (int64_t)(d->bytes + d->g->bytes);
-    for (int32_t i = 0; i < n && i < 14; ++i) out[i] = v[i];
+    v[11] = (int64_t)(d->bytes + d->log.committed_bytes() + d->g->bytes);
+    v[14] = (int64_t)d->log.va_bytes;
+    v[15] = (int64_t)d->log.committed_bytes();
+    v[16] = d->last_regrows;
+    for (int32_t i = 0; i < n && i < 17; ++i) out[i] = v[i];
     return WFST_OK;
 }
 

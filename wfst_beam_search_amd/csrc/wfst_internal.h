@@ -154,7 +154,8 @@ struct Work {
     int32_t max_frames;
     uint32_t frontier_cap;    // Q
     uint32_t claims_cap;      // CC
-    uint32_t arena;           // winners-log entries per lane
+    uint32_t arena;           // winners-log entries per lane (region stride, global id = L * arena + local)
+    uint32_t arena_lim;       // winners-log entries per lane backed by memory (<= arena): the append bound
     uint32_t path_cap;        // device path buffer per lane
     uint32_t strip_cap;       // 64-slot strips per lane and step (slot space = 64 * strip_cap)
     uint32_t res_stride;      // int32 per lane in the result buffer

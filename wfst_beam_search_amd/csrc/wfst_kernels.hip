@@ -897,7 +897,7 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
     const int32_t esrc = (uint32_t)stok < w.frontier_cap
         ? pick(w.tok_entry, p)[(size_t)L * w.frontier_cap + stok] : -1;
     const uint32_t le = c.log_cursor;
-    if (le < w.arena) {
+    if (le < w.arena_lim) {
         const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
         w.wlog[e] = make_int2(esrc, arc);
         c.log_cursor = le + 1u;
@@ -1101,7 +1101,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         // overflow nothing is written and the lane retires (the frontier count
         // past frontier_cap keeps every later kernel off its tokens)
         const bool pos_ok = (unsigned long long)p0 + nkeep <= Q;
-        if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena) {
+        if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena_lim) {
             if (lane == leader) {
                 atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
                 c.status = kDone;
@@ -1411,7 +1411,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         // exact capacity of this wavefront's appends and winners-log entries: on
         // overflow nothing is written and the lane retires
         const bool pos_ok = (unsigned long long)(uint32_t)old + (uint32_t)__popcll(mn) <= Q;
-        if (!pos_ok || (unsigned long long)lb + (uint32_t)__popcll(ma) > w.arena) {
+        if (!pos_ok || (unsigned long long)lb + (uint32_t)__popcll(ma) > w.arena_lim) {
             if (lane == leader) {
                 atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
                 c.status = kDone;
@@ -1877,7 +1877,7 @@ __device__ __forceinline__ void gc_prologue(const Work &w, LaneTab &tab, int wha
             const uint32_t n = (uint32_t)pair_at(c.cnt, p);
             const uint32_t win = c.log_cursor > c.sealed ? c.log_cursor - c.sealed : 0u;
             uint32_t items = 0;
-            if (c.gc_on && n <= w.frontier_cap && c.log_cursor <= w.arena)
+            if (c.gc_on && n <= w.frontier_cap && c.log_cursor <= w.arena_lim)
                 items = what == 0 ? n : what == 1 ? win : what == 2 ? c.gc_live : (win + 31u) / 32u;
             units = (items + kWave - 1) / kWave;
             tab.n[L] = items;
@@ -1937,7 +1937,7 @@ __global__ __launch_bounds__(kGcScanBlock) void k_gc_scan(const Work *__restrict
     if (L >= w.max_lanes) return;
     LaneCtl &c = w.ctl[L];
     const int p = lane_par(c, c.last_step + 1);
-    if (!c.gc_on || c.log_cursor > w.arena || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
+    if (!c.gc_on || c.log_cursor > w.arena_lim || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
     const uint32_t win = c.log_cursor > c.sealed ? c.log_cursor - c.sealed : 0u;
     const uint32_t nw = (win + 31u) / 32u;
     const uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
@@ -2098,7 +2098,7 @@ __global__ __launch_bounds__(kWave) void k_gc_end(const Work *__restrict__ wp)
     if (L >= w.max_lanes) return;
     LaneCtl &c = w.ctl[L];
     const int p = lane_par(c, c.last_step + 1);
-    if (!c.gc_on || c.log_cursor > w.arena || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
+    if (!c.gc_on || c.log_cursor > w.arena_lim || (uint32_t)pair_at(c.cnt, p) > w.frontier_cap) return;
     const uint32_t live = c.gc_live;
     uint32_t grow = 0;
     if (c.gc_base_children == 1u && live > 0u) grow = min(c.gc_k, live - 1u) + 1u;
