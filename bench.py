@@ -240,9 +240,11 @@ def main():
                     help="compact the winners log every N steps (and per stream chunk)")
     ap.add_argument("--arena", type=int, default=0, metavar="ENTRIES",
                     help="winners-log entries per lane (0: the decoder's default)")
-    ap.add_argument("--arena-commit", type=int, default=0, metavar="ENTRIES",
-                    help="winners-log entries per lane committed at creation (0: the decoder's "
-                         "lazy default, -1: the whole region)")
+    ap.add_argument("--arena-commit", type=int, default=-1, metavar="ENTRIES",
+                    help="winners-log entries per lane committed at creation (-1, the default "
+                         "here: the whole region, so no warm-up decode is cut short and run again "
+                         "and every counted dispatch belongs to a whole decode; 0: the decoder's "
+                         "lazy default)")
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
