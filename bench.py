@@ -61,6 +61,26 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     return per, path
 
 
+def measure_copy_gbps(dev, mib=1024, reps=5):
+    """Bandwidth of a plain device-to-device copy on this GPU (bytes read plus
+    bytes written per second), the measured companion of the 8 TB/s peak."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(s)
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("wfst_kernels.hip", "wfst_internal.h"):
@@ -296,11 +316,15 @@ def main():
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
+    per_decode = []
     for _ in range(args.steps):
-        res = dec.decode(x, lengths)
+        ta = time.perf_counter()
+        res = dec.decode(x, lengths)      # returns after its stream has finished
+        per_decode.append(time.perf_counter() - ta)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     st = dec.stats()
+    copy_gbps = measure_copy_gbps(dev)
 
     frames = int(np.asarray(lengths).sum())
     ms_per_step = dt / args.steps * 1e3
@@ -358,6 +382,9 @@ def main():
                    **({} if not args.gc_interval else {"gc_interval": args.gc_interval}),
                    **({} if not args.arena else {"arena_entries": args.arena})},
         "arcs_expanded_per_s": round(arcs_ps, 1),
+        "ms_per_decode_median_min_max": [round(float(np.median(per_decode)) * 1e3, 4),
+                                         round(min(per_decode) * 1e3, 4), round(max(per_decode) * 1e3, 4)],
+        "hbm_copy_GBps_measured": copy_gbps,
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
         "parity_meta_ok": ok,

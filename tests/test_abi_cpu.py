@@ -131,3 +131,17 @@ def test_null_arguments(lib):
     assert lib.wfst_decode(None, None, 1, 1, 1, None, None, None, 0, None, None, 0, None, None, None) == WFST_EINVAL
     assert lib.wfst_graph_release(None) == 0
     assert lib.wfst_decoder_destroy(None) == 0
+
+
+def test_graph_from_arrays_validates_before_any_device_call(lib):
+    """Graph.from_arrays marshals plain arrays into the same upload call: a
+    corrupt graph (an arc into a state that does not exist) fails validation,
+    which runs on the host before the device is touched."""
+    rs = np.array([0, 2, 3, 3], np.int32)
+    dest = np.array([1, 5, 2], np.int32)
+    il = np.array([0, -1, -1], np.int32)
+    ol = np.zeros(3, np.int32)
+    w = np.array([-0.5, 0.0, 0.0], np.float32)
+    with pytest.raises(wb.WfstError) as ei:
+        wb.Graph.from_arrays(rs, dest, il, ol, w, start=0, vocab=2)
+    assert ei.value.code == WFST_ECORRUPT

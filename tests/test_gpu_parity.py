@@ -112,6 +112,20 @@ def test_greedy_closed_form_gpu():
         assert r.scores[b] == s
 
 
+def test_graph_from_arrays():
+    """A graph uploaded from plain arrays decodes to the oracle's result."""
+    g = synth.random_graph(77, n=40, deg=(1, 6), vocab=7, self_loop=0.3)
+    lp = synth.random_logprobs(78, 3, 25, g.vocab)
+    L = np.array([25, 11, 0], np.int32)
+    dg = wb.Graph.from_arrays(g.row_splits, g.dest, g.ilabel, g.olabel, g.weight, start=g.start, vocab=g.vocab,
+                              epsilon_id=g.epsilon_id)
+    try:
+        r, steps, _ = gpu_decode(g, lp, L, 8.0, 50, dgraph=dg)
+    finally:
+        dg.release()
+    compare_batch(r, steps, oracle_lanes(g, lp, L, 8.0, 50))
+
+
 # ------------------------------------------------------------- workloads
 
 WORKLOAD_IDS = [1, 2, 5, 4, 3]

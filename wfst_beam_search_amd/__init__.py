@@ -13,6 +13,7 @@ import ctypes
 import os
 import threading
 from dataclasses import dataclass
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -158,6 +159,18 @@ class Graph:
         self.device = device
         self.vocab = int(g.vocab)
         self.epsilon_id = int(g.epsilon_id)
+
+    @classmethod
+    def from_arrays(cls, row_splits, dest, ilabel, olabel, weight, start: int, vocab: int,
+                    epsilon_id: int = -1, device: int = 0) -> "Graph":
+        """Uploads a CSR graph given as plain arrays: row_splits [N + 1] (N states,
+        the last one the super-final state), per arc dest, ilabel (-1 final,
+        epsilon_id, else [0, vocab)), olabel (0 = no word) and weight (float32
+        log-score <= 0); each state's arcs ordered epsilon, emitting, final."""
+        g = SimpleNamespace(num_states=len(row_splits) - 1, start=int(start), vocab=int(vocab),
+                            epsilon_id=int(epsilon_id), row_splits=row_splits, dest=dest, ilabel=ilabel,
+                            olabel=olabel, weight=weight)
+        return cls(g, device=device)
 
     def release(self):
         if self.handle:

@@ -484,8 +484,23 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(const Work *__restrict__ wp)
         // the real steps of the sequence that read a row of this input
         if (c.status != kActive || c.lp_row < 0 || t >= c.T || t >= c.win) continue;
         const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)t * d.stride_t;
+        // 16-byte loads over the row's aligned middle, single elements around it
+        // (the maximum does not depend on the order)
+        constexpr uint32_t kPer = 16 / sizeof(LPT);
+        const uint32_t V = (uint32_t)w.vocab;
+        const uint32_t mis = (uint32_t)(((uintptr_t)row & 15u) / sizeof(LPT));
+        const uint32_t head = min(V, mis ? kPer - mis : 0u);
+        const uint32_t nvec = (V - head) / kPer;
         float m = -__builtin_inff();
-        for (int v = wlane(); v < w.vocab; v += kWave) m = fmaxf(m, lp_at(row, (uint32_t)v));
+        for (uint32_t v = wlane(); v < head; v += kWave) m = fmaxf(m, lp_at(row, v));
+        const uint4 *vp = (const uint4 *)(row + head);
+        for (uint32_t k = wlane(); k < nvec; k += kWave) {
+            const uint4 q = vp[k];
+            const LPT *e = (const LPT *)&q;
+#pragma unroll
+            for (uint32_t j = 0; j < kPer; ++j) m = fmaxf(m, lp_at(e, j));
+        }
+        for (uint32_t v = head + nvec * kPer + wlane(); v < V; v += kWave) m = fmaxf(m, lp_at(row, v));
         m = wave_max(m);
         if (wlane() == 0) w.lpmax[(size_t)L * w.max_frames + t] = m;
     }
