@@ -44,7 +44,8 @@ def algorithmic_bytes(st, elem_bytes, vocab):
                                          next-frontier token 12 B, winners-log entry 8 B)
     Only the admitted candidates C count, not the larger list the slot pass writes
     while the maximum is still being found.
-      eps      16 E + 28 De + 20 Ne     (closure: token + eps arc per relaxation, candidates, changed tokens)
+      eps_expand 16 E, eps_apply 28 De + 20 Ne   (closure: token + eps arc per relaxation; winners'
+                                         candidate and table entry, changed tokens)
       path     12 n + 6 S + 52 C + 28 D + e V F (+ eps terms): the whole step, tokens and arcs counted once
     """
     n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
@@ -54,8 +55,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
         "max": 12 * n + 6 * S + 28 * C + row,
         "finalize": 24 * C + 28 * D,
         "eps_expand": 16 * E,
-        "eps_resolve": 28 * De,
-        "eps_apply": 20 * Ne,
+        "eps_apply": 28 * De + 20 * Ne,
     }
     path = 12 * n + 6 * S + 52 * C + 28 * D + row + 16 * E + 28 * De + 20 * Ne
     return per, path

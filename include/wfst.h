@@ -390,8 +390,8 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_EXPAND       4  /* not launched (its work is part of WFST_K_MAX)            */
 #define WFST_K_FINALIZE     5  /* exact admit, compaction, winners log, next lower bound   */
 #define WFST_K_EPS_EXPAND   6  /* closure pass: relax epsilon arcs                         */
-#define WFST_K_EPS_RESOLVE  7  /* closure pass: append / replace decisions                 */
-#define WFST_K_EPS_APPLY    8  /* closure pass: apply them                                 */
+#define WFST_K_EPS_RESOLVE  7  /* not launched (its work is part of WFST_K_EPS_APPLY)      */
+#define WFST_K_EPS_APPLY    8  /* closure pass: append / replace decisions and their writes */
 #define WFST_K_BACKTRACK    9  /* best path (or a stream's best current token) to arcs, words */
 #define WFST_K_STREAM_BEGIN 10 /* stream call: applies the per-lane plan                   */
 #define WFST_K_STREAM_END  11  /* stream call: commits the chunk's last compaction        */

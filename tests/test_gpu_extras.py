@@ -87,3 +87,42 @@ def test_sparse_final_arcs(keep):
         checked += sum(1 for x in o if x["reached_final"] == 0)
     if keep < 0.5:
         assert checked > 0    # some lanes ended without a final arc
+
+
+def test_largest_vocabulary():
+    """The largest vocabulary the 16-bit labels hold (65534 symbols, labels up to
+    65533 beside the final-arc label): arcs on the top labels, rows the top
+    labels win, results equal to the oracle's."""
+    V = 65534
+    g = synth.random_graph(51, n=25, deg=(1, 5), vocab=V, self_loop=0.3)
+    il = np.asarray(g.ilabel).copy()
+    emit = np.flatnonzero(il >= 0)
+    il[emit[::3]] = V - 1
+    il[emit[1::3]] = V - 2
+    g.ilabel = il
+    lp = synth.random_logprobs(52, 3, 30, V, sigma=2.0)
+    lp[:, ::2, V - 1] = np.float32(-0.05)
+    lp[:, 1::2, V - 2] = np.float32(-0.05)
+    L = np.array([30, 17, 1], np.int32)
+    _say("vocab", V, lp.shape)
+    for dtype in ("f32", "f16"):
+        x = lp if dtype == "f32" else lp.astype(np.float16)
+        r, steps, _ = gpu_decode(g, x, L, 10.0, 200)
+        o = oracle_lanes(g, x, L, 10.0, 200)
+        compare_batch(r, steps, o)
+        assert any((a >= 0).any() and (il[a[a < il.shape[0]]] >= V - 2).any() for a in r.arcs)
+
+
+def test_long_utterance():
+    """3000 frames (a 3008-step graph bucket), with and without compaction
+    rounds: the oracle's path, arc for arc."""
+    g = synth.random_graph(53, n=60, deg=(1, 6), vocab=12, self_loop=0.3)
+    T = 3000
+    lp = synth.random_logprobs(54, 2, T, g.vocab, sigma=2.5)
+    L = np.array([T, 1777], np.int32)
+    o = oracle_lanes(g, lp, L, 8.0, 300)
+    for gi in (0, 64):
+        _say("long", T, "interval", gi)
+        r, steps, st = gpu_decode(g, lp, L, 8.0, 300, gc_interval=gi)
+        compare_batch(r, steps, o)
+        assert len(r.arcs[0]) == T + 1

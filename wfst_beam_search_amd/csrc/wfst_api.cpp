@@ -500,7 +500,6 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     }
     A(&w.best, L * S);
     A(&w.claims, L * CC);
-    if (P > 0) { A(&w.dec, L * CC); A(&w.dec_dest, L * CC); }
     A(&w.res, L * (size_t)w.res_stride);
     A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
     A(&d->d_plan, L * kPlanFields);
@@ -607,7 +606,6 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
     for (int k = 1; k <= d->passes; ++k) {
         if ((e = wrap_clear(d, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
     }
     if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
@@ -619,7 +617,6 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = wrap_clear(d, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
         }
         if (d->w.gc_interval > 0 && (t + 1) % d->w.gc_interval == 0 && t + 1 < steps &&
@@ -821,7 +818,6 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = wrap(-1, k)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsResolve, -1, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
         }
     }
@@ -835,7 +831,6 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = wrap(t, k)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsResolve, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
         }
         // every gc_interval steps and at the end of the chunk

@@ -58,8 +58,9 @@ struct ArcDLW {
     float weight;
 };
 
-// An admitted candidate: destination, arc, source token (position in the
-// frontier being read) and end score. Its key (ordered score << 32 | ~arc) is
+// An admitted candidate: destination, arc, source (the source token's position
+// in the frontier being read; for a closure candidate, the source token's
+// winners-log entry) and end score. Its key (ordered score << 32 | ~arc) is
 // unique per destination, so exactly one candidate of each destination finds
 // its own key in the table once the pass is over: the winner.
 struct alignas(16) Claim {
@@ -105,7 +106,7 @@ struct alignas(128) LaneCtl {
     uint32_t sealed;
     uint32_t gc_on;            // this round compacts the lane
     uint32_t gc_live;          // live entries of the window (after the scan)
-    uint32_t gc_root0;         // local entry of the frontier's first token (epsilon-free lanes)
+    uint32_t eps_n0;           // frontier tokens when the current closure pass began
     alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
                                              //   step's class) << 32
     alignas(128) uint32_t nclaims[2];        // candidate-list length of the slot pass by step parity
@@ -175,8 +176,6 @@ struct Work {
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
     unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed)
     Claim *claims;            // [L][CC]
-    int4 *dec;                // [L][CC] closure decisions {token or -1/-2, score bits, arc, src entry}
-    int32_t *dec_dest;        // [L][CC]
     uint32_t *changed[2];     // [L][CC] closure change lists by pass parity
     int2 *wlog;               // [L][arena] winners log {prev entry, arc}
     int32_t *res;             // [L][res_stride] results

@@ -1191,6 +1191,10 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         // the compaction before this closure (no closure token added yet)
         if (k == 1) commit_log(w, c, L, t, (uint32_t)c.cnt[tab.par[L]]);
         if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
+        // for the apply kernel of this pass, which appends while it reads: the
+        // frontier as the pass found it, and an empty list of changed tokens
+        c.eps_n0 = (uint32_t)c.cnt[tab.par[L]];
+        c.nchanged[(k + 1) & 1] = 0u;
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
@@ -1208,13 +1212,14 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         // the 64 sources of this unit and their epsilon ranges
         const uint32_t tok = (i < tab.n[L])
             ? ((k == 1) ? i : w.changed[k & 1][(size_t)L * w.claims_cap + i]) : 0xFFFFFFFFu;
-        int32_t eb = 0;
+        int32_t eb = 0, ent = -1;
         uint32_t ed = 0;
         float sc = 0.0f;
         if (tok < Q) {
             const size_t q = (size_t)L * Q + tok;
             const StateInfo si = w.sinfo[pick(w.tok_state, fp)[q]];
             sc = pick(w.tok_score, fp)[q];
+            ent = pick(w.tok_entry, fp)[q];
             eb = si.eps_b;
             ed = (uint32_t)(si.emit_b - si.eps_b);
         }
@@ -1232,7 +1237,9 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             }
             const int32_t a = __shfl(eb, src, kWave) + (int32_t)(x - __shfl(dpre, src, kWave));
             const float ssc = __shfl(sc, src, kWave);
-            const uint32_t stk = __shfl(tok, src, kWave);
+            // the source's winners-log entry as this pass found it (the apply
+            // kernel may give the source token a fresh one)
+            const int32_t sen = __shfl(ent, src, kWave);
             bool adm = false;
             int32_t dd = 0;
             float e = 0.0f;
@@ -1246,7 +1253,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                     atomicMax(&tbl[ar.dest], table_key(w, e, a, ep));
                 }
             }
-            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, stk, e);
+            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, (uint32_t)sen, e);
         }
         if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n);
         const uint32_t sd = wave_sum(n_adm);
@@ -1266,8 +1273,14 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ 
     ph_eps_expand(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
 }
 
-// Decides, per claimed destination, append / replace / nothing (reads only).
-__device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, LaneTab &tab)
+// Per claimed destination of the pass: the winner (its key is the table entry)
+// is appended as a new token, replaces the destination's token if its key is
+// greater, or does nothing; then the writes: fresh winners-log entries,
+// appended tokens (with their next-step class and arc offsets), replaced
+// tokens, the next pass's sources. Only a destination's winner reads or writes
+// its token, and the existence test sees only the tokens the pass began with,
+// so the decisions are those of a pass that reads everything before it writes.
+__device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
 {
     const uint32_t ep = round_epoch(w, t, k);
     if (threadIdx.x < kWave) {
@@ -1278,91 +1291,16 @@ __device__ __forceinline__ void ph_eps_resolve(const Work &w, int t, int k, Lane
             const int fp = lane_par(c, t + 1);
             tab.par[L] = fp;
             uint32_t nc = 0;
-            const uint32_t n = (uint32_t)pair_at(c.cnt, fp), nce = c.nclaims_eps[k & 1];
-            if (closure_lane(c, t) && n <= w.frontier_cap) nc = nce;
-            if (nc <= w.claims_cap) units = (nc + kWave - 1) / kWave;
-            tab.n[L] = nc;
-            tab.arcs[L] = n;
-            tab.f1[L] = c.cutoff;
-        }
-        tab_publish(tab, w.max_lanes, units);
-    }
-    __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
-        const int L = (int)threadIdx.x;
-        LaneCtl &c = w.ctl[L];
-        if (tab.n[L] > w.claims_cap) {
-            c.overflow |= kOvfClaims; c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
-        }
-        c.nchanged[(k + 1) & 1] = 0u;
-    }
-    const int nl = w.max_lanes;
-    const uint32_t total = tab.base[nl];
-    const uint32_t Q = w.frontier_cap;
-    uint32_t u_beg, u_end;
-    wave_share(total, &u_beg, &u_end);
-    for (uint32_t u = u_beg; u < u_end; ++u) {
-        const int L = (int)find_lane(tab.base, nl, u);
-        const int fp = upar(tab.par, L);
-        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
-        const bool valid = i < tab.n[L];
-        Claim cl;
-        const bool win = valid && take_winner(w, L, i, ep, cl);
-        const unsigned long long wm = __ballot(win);
-        if (wm && wlane() == __ffsll((long long)__ballot(valid)) - 1)
-            atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
-        if (!valid) continue;
-        const size_t ci = (size_t)L * w.claims_cap + i;
-        const int32_t dst = cl.dest;
-        const float end = __uint_as_float(cl.score);
-        const int32_t arc = cl.arc;
-        const unsigned long long K = cand_key(end, arc);
-        int32_t code = -2;
-        int32_t esrc = -1;
-        if (win && end > tab.f1[L]) {
-            const int32_t stok = (int32_t)cl.tok;
-            esrc = (uint32_t)stok < Q ? pick(w.tok_entry, fp)[(size_t)L * Q + stok] : -1;
-            const int32_t pd = pick(w.pos, fp)[(size_t)L * w.num_states + dst];
-            const bool exists = (uint32_t)pd < tab.arcs[L] && pick(w.tok_state, fp)[(size_t)L * Q + pd] == dst;
-            if (!exists) {
-                code = -1;
-            } else {
-                const size_t q = (size_t)L * Q + pd;
-                if (K > cand_key(pick(w.tok_score, fp)[q], pick(w.tok_last, fp)[q])) code = pd;
-            }
-        }
-        w.dec[ci] = make_int4(code, (int)__float_as_uint(end), arc, esrc);
-        w.dec_dest[ci] = dst;
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_eps_resolve(const Work *__restrict__ wp, int t, int k)
-{
-    const Work &w = *wp;
-    __shared__ LaneTab tab;
-    ph_eps_resolve(w, t, k, tab);
-}
-
-// Applies the decisions: fresh winners-log entries, appended tokens (with their
-// next-step class and arc offsets), replaced tokens, the next pass's sources.
-__device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
-{
-    if (threadIdx.x < kWave) {
-        const int L = (int)threadIdx.x;
-        uint32_t units = 0;
-        if (L < w.max_lanes) {
-            const LaneCtl &c = w.ctl[L];
-            const int fp = lane_par(c, t + 1);
-            tab.par[L] = fp;
-            uint32_t nc = 0;
-            const uint32_t nce = c.nclaims_eps[k & 1];
-            const bool on = closure_lane(c, t) && (uint32_t)pair_at(c.cnt, fp) <= w.frontier_cap;
+            const uint32_t nce = c.nclaims_eps[k & 1], n0 = c.eps_n0;
+            const bool on = closure_lane(c, t) && n0 <= w.frontier_cap;
             if (on) nc = nce;
             // token and log capacity are checked per wavefront as it allocates
             const bool fits = nc <= w.claims_cap;
             if (fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
+            tab.arcs[L] = n0;
             tab.T[L] = c.T;
+            tab.f1[L] = c.cutoff;
             tab.f0[L] = (on && !fits) ? 1.0f : 0.0f;
         }
         tab_publish(tab, w.max_lanes, units);
@@ -1373,7 +1311,9 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         LaneCtl &c = w.ctl[L];
         c.nclaims_eps[(k + 1) & 1] = 0u;
         if (tab.f0[L] != 0.0f) {
-            c.overflow |= kOvfClaims;
+            // candidates past claims_cap were never listed: their table entries
+            // stay set, so the table is cleared before the next decode
+            c.overflow |= kOvfClaims; c.dirty = 1u;
             c.status = kDone; c.phase_final = kPhDead;
         }
     }
@@ -1390,12 +1330,28 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         const bool valid = i < tab.n[L];
         const bool next_final = (t + 1 == tab.T[L]);
         LaneCtl &c = w.ctl[L];
+        // dd = {token replaced (-1: append, -2: nothing), score bits, arc, source entry}
         int4 dd = make_int4(-2, 0, 0, -1);
         int32_t dst = 0;
-        if (valid) {
-            const size_t ci = (size_t)L * w.claims_cap + i;
-            dd = w.dec[ci];
-            dst = w.dec_dest[ci];
+        Claim cl;
+        const bool win = valid && take_winner(w, L, i, ep, cl);
+        const unsigned long long wm = __ballot(win);
+        if (wm && lane == __ffsll((long long)__ballot(valid)) - 1)
+            atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
+        if (win && __uint_as_float(cl.score) > tab.f1[L]) {
+            dst = cl.dest;
+            dd.y = (int)cl.score;
+            dd.z = cl.arc;
+            dd.w = (int32_t)cl.tok;
+            const int32_t pd = pick(w.pos, fp)[(size_t)L * w.num_states + dst];
+            const bool exists = (uint32_t)pd < tab.arcs[L] && pick(w.tok_state, fp)[(size_t)L * Q + pd] == dst;
+            if (!exists) {
+                dd.x = -1;
+            } else {
+                const size_t q = (size_t)L * Q + pd;
+                if (cand_key(__uint_as_float(cl.score), cl.arc) > cand_key(pick(w.tok_score, fp)[q], pick(w.tok_last, fp)[q]))
+                    dd.x = pd;
+            }
         }
         const bool any = dd.x != -2;
         const bool isnew = dd.x == -1;
@@ -2228,7 +2184,6 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         break;
     case kKFinalize: go(k_finalize, G, B, s, e0, e1, dw, t); break;
     case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, dw, t, k); break;
-    case kKEpsResolve: go(k_eps_resolve, G, B, s, e0, e1, dw, t, k); break;
     case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, dw, t, k); break;
     case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
