@@ -483,6 +483,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     w.output_beam = c.lattice ? c.output_beam : 0.0f;
     w.lat_cap = (uint32_t)lat_cap;
     w.gc_interval = c.gc_interval;
+    w.chg_cap = (uint32_t)std::max<uint64_t>(CC, Q);
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
     int r = WFST_OK;
@@ -496,7 +497,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         A(&w.tok_state[p], L * Q); A(&w.tok_score[p], L * Q); A(&w.tok_entry[p], L * Q);
         A(&w.tok_last[p], L * Q); A(&w.tok_off[p], L * Q); A(&w.tok_abeg[p], L * Q);
         A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S); A(&w.strip_tok[p], L * strip_cap);
-        if (P > 0) A(&w.changed[p], L * CC);
+        if (P > 0) A(&w.changed[p], L * std::max<uint64_t>(CC, Q));
     }
     A(&w.best, L * S);
     A(&w.claims, L * CC);

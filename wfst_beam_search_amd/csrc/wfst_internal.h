@@ -116,7 +116,9 @@ struct alignas(128) LaneCtl {
                                              //   (posted by the compaction of the step before)
     alignas(128) uint32_t log_cursor;        // winners-log entries used in this lane's region
     alignas(128) uint32_t nclaims_eps[2];    // admitted candidates of closure pass k at [k & 1]
-    alignas(128) uint32_t nchanged[2];       // changed-token list sizes of closure pass k at [k & 1]
+    alignas(128) unsigned long long nchanged[2];  // closure pass k's sources at [k & 1]: entries of
+                                                  //   its list (low half) | tokens appended or replaced
+                                                  //   by the pass before it (high half; pass 1: unused)
     alignas(128) uint32_t lat_cursor;        // lattice arcs persisted (lattice mode)
     alignas(128) uint32_t lat_out_n;         // lattice records kept by the prune (lattice mode)
     alignas(128) uint32_t gc_base_children;  // live window entries whose predecessor is sealed
@@ -176,7 +178,9 @@ struct Work {
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
     unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed)
     Claim *claims;            // [L][CC]
-    uint32_t *changed[2];     // [L][CC] closure change lists by pass parity
+    int4 *changed[2];         // [L][chg_cap] closure source lists by pass parity: the tokens with
+                              //   epsilon arcs, {first epsilon arc, epsilon arcs, entry, score bits}
+    uint32_t chg_cap;         // max(claims_cap, frontier_cap)
     int2 *wlog;               // [L][arena] winners log {prev entry, arc}
     int32_t *res;             // [L][res_stride] results
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]

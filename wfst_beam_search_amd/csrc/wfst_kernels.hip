@@ -403,8 +403,7 @@ __device__ void init_lane(const Work &w, int L, int T)
     c.final_score = -__builtin_inff();
     c.nclaims_eps[0] = 0u;
     c.nclaims_eps[1] = 0u;
-    c.nchanged[0] = 0u;
-    c.nchanged[1] = 0u;
+    c.nchanged[0] = 0ull;
     c.log_open = 0u;
     c.front_base[0] = 0xFFFFFFFFu;
     c.front_base[1] = 0xFFFFFFFFu;
@@ -430,6 +429,11 @@ __device__ void init_lane(const Work &w, int L, int T)
     w.tok_abeg[0][q] = abeg;
     w.tok_ub[0][q] = ub;
     w.pos[0][(size_t)L * w.num_states + s] = 0;
+    // the start closure's sources: the start token, if it has epsilon arcs
+    const bool eps_src = w.eps_iterations > 0 && si.emit_b > si.eps_b;
+    if (eps_src)
+        w.changed[1][(size_t)L * w.chg_cap] = make_int4(si.eps_b, si.emit_b - si.eps_b, -1, (int)__float_as_uint(0.0f));
+    c.nchanged[1] = eps_src ? 1ull : 0ull;
     uint32_t *st = w.strip_tok[0] + (size_t)L * w.strip_cap;
     for (uint32_t sb = 0; sb * kWave < deg && sb < w.strip_cap; ++sb) st[sb] = 0u;
     c.cnt[0] = 1ull | ((unsigned long long)deg << 32);
@@ -831,6 +835,7 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     c.phase_final = ph;
     c.nclaims[p ^ 1] = 0u;   // this step's list counter was cleared one step ago
     c.cnt[p ^ 1] = 0ull;
+    c.nchanged[1] = 0ull;    // the closure's first sources, listed by this step's compaction
     c.maxkey[p ^ 1] = kOrdNegInf;
     c.lbkey[p ^ 1] = kOrdNegInf;
     if (arcs == 0u) {
@@ -1012,8 +1017,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         const bool next_final = (t + 1 == tab.T[L]);
         LaneCtl &c = w.ctl[L];
         bool keep = false;
-        int32_t dst = 0, arc = 0, esrc = -1, abeg = 0;
-        uint32_t deg = 0;
+        int32_t dst = 0, arc = 0, esrc = -1, abeg = 0, eps_b0 = 0;
+        uint32_t deg = 0, eps_n = 0;
         float end = 0.0f, ub = 0.0f, lbv = -__builtin_inff();
         // the list is a superset: a candidate is admitted iff end > the exact
         // cutoff; the one whose key is its destination's entry owns the entry
@@ -1068,6 +1073,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
                     esrc = w.has_eps ? pick(w.tok_entry, p)[(size_t)L * Q + stok]
                          : fb == 0xFFFFFFFFu ? -1 : (int32_t)((uint32_t)L * w.arena + fb + (uint32_t)stok);
                     class_of(si, next_final, end, &abeg, &deg, &ub);
+                    eps_b0 = si.eps_b;
+                    eps_n = (uint32_t)(si.emit_b - si.eps_b);
                     // (no bound past the sequence's window: its row is not in this input)
                     if (!next_final && deg > 0u && t + 1 < tab.win[L]) {
                         // candidates of the next step through the state's
@@ -1106,11 +1113,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         uint32_t dsum;
         const uint32_t dpre = wave_excl_sum(keep ? deg : 0u, &dsum);
         const int leader = __ffsll((long long)m) - 1;
+        // on epsilon graphs the closure's first sources: the new tokens with
+        // epsilon arcs
+        const unsigned long long ml = (w.eps_iterations > 0) ? __ballot(keep && eps_n > 0u) : 0ull;
         unsigned long long old = 0ull;
+        uint32_t l0 = 0u;
         if (lane == leader) {
             old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
+            if (ml) l0 = (uint32_t)atomicAdd(&c.nchanged[1], (unsigned long long)__popcll(ml));
         }
         old = __shfl(old, leader, kWave);
+        if (ml) l0 = __shfl(l0, leader, kWave);
         const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
         // exact capacity of this wavefront's tokens and winners-log entries: on
         // overflow nothing is written and the lane retires (the frontier count
@@ -1138,6 +1151,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
             pick(w.tok_ub, np)[q] = ub;
             if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
             if (w.lattice) w.lat_score[(size_t)L * w.arena + tab.arcs[L] + pi] = end;
+            if ((ml >> lane) & 1ull)
+                w.changed[1][(size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt())] =
+                    make_int4(eps_b0, (int)eps_n, e, (int)__float_as_uint(end));
         }
         write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
@@ -1175,11 +1191,16 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             const LaneCtl &c = w.ctl[L];
             const int fp = lane_par(c, t + 1);
             tab.par[L] = fp;
-            uint32_t ns = 0;
-            const uint32_t n = (uint32_t)pair_at(c.cnt, fp), nch = c.nchanged[k & 1];
-            if (closure_lane(c, t) && n <= w.frontier_cap) ns = (k == 1) ? n : nch;
+            uint32_t ns = 0, srcs = 0;
+            const uint32_t n = (uint32_t)pair_at(c.cnt, fp);
+            const unsigned long long nch = c.nchanged[k & 1];
+            if (closure_lane(c, t) && n <= w.frontier_cap) {
+                ns = (uint32_t)nch;
+                srcs = (k == 1) ? n : (uint32_t)(nch >> 32);
+            }
             units = (ns + kWave - 1) / kWave;
             tab.n[L] = ns;
+            tab.arcs[L] = srcs;
             tab.f1[L] = c.cutoff;
         }
         tab_publish(tab, w.max_lanes, units);
@@ -1190,38 +1211,34 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         LaneCtl &c = w.ctl[L];
         // the compaction before this closure (no closure token added yet)
         if (k == 1) commit_log(w, c, L, t, (uint32_t)c.cnt[tab.par[L]]);
-        if (tab.n[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;
+        if (tab.arcs[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;   // a pass with sources
         // for the apply kernel of this pass, which appends while it reads: the
         // frontier as the pass found it, and an empty list of changed tokens
         c.eps_n0 = (uint32_t)c.cnt[tab.par[L]];
-        c.nchanged[(k + 1) & 1] = 0u;
+        c.nchanged[(k + 1) & 1] = 0ull;
     }
     const int nl = w.max_lanes;
     const uint32_t total = tab.base[nl];
     const int lane = wlane();
-    const uint32_t Q = w.frontier_cap;
     uint32_t u_beg, u_end;
     wave_share(total, &u_beg, &u_end);
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
-        const int fp = upar(tab.par, L);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
         LaneCtl &c = w.ctl[L];
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
-        // the 64 sources of this unit and their epsilon ranges
-        const uint32_t tok = (i < tab.n[L])
-            ? ((k == 1) ? i : w.changed[k & 1][(size_t)L * w.claims_cap + i]) : 0xFFFFFFFFu;
+        // the 64 sources of this unit: their epsilon ranges, entries and scores
+        // as the kernel that made them wrote them
         int32_t eb = 0, ent = -1;
         uint32_t ed = 0;
         float sc = 0.0f;
-        if (tok < Q) {
-            const size_t q = (size_t)L * Q + tok;
-            const StateInfo si = w.sinfo[pick(w.tok_state, fp)[q]];
-            sc = pick(w.tok_score, fp)[q];
-            ent = pick(w.tok_entry, fp)[q];
-            eb = si.eps_b;
-            ed = (uint32_t)(si.emit_b - si.eps_b);
+        if (i < tab.n[L]) {
+            const int4 ce = w.changed[k & 1][(size_t)L * w.chg_cap + i];
+            eb = ce.x;
+            ed = (uint32_t)ce.y;
+            ent = ce.z;
+            sc = __uint_as_float((uint32_t)ce.w);
         }
         uint32_t dsum;
         const uint32_t dpre = wave_excl_sum(ed, &dsum);
@@ -1356,13 +1373,22 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         const bool any = dd.x != -2;
         const bool isnew = dd.x == -1;
         const float end = __uint_as_float((uint32_t)dd.y);
-        int32_t abeg = 0;
-        uint32_t deg = 0;
+        int32_t abeg = 0, eb = 0;
+        uint32_t deg = 0, ed = 0;
         float ub = 0.0f;
-        if (any) class_of(w.sinfo[dst], next_final, end, &abeg, &deg, &ub);
+        if (any) {
+            const StateInfo si = w.sinfo[dst];
+            class_of(si, next_final, end, &abeg, &deg, &ub);
+            eb = si.eps_b;
+            ed = (uint32_t)(si.emit_b - si.eps_b);
+        }
         const unsigned long long ma = __ballot(any);
         if (ma == 0ull) continue;
         const unsigned long long mn = __ballot(isnew);
+        // the next pass's sources (none after the last pass): the changed tokens
+        // with epsilon arcs, counted apart from all changed tokens
+        const bool more = k < w.eps_iterations;
+        const unsigned long long ml = more ? __ballot(any && ed > 0u) : 0ull;
         const int leader = __ffsll((long long)ma) - 1;
         uint32_t dsum;
         const uint32_t dpre = wave_excl_sum(isnew ? deg : 0u, &dsum);
@@ -1370,7 +1396,9 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         uint32_t lb = 0u, cb = 0u;
         if (lane == leader) {
             lb = atomicAdd(&c.log_cursor, (uint32_t)__popcll(ma));
-            cb = atomicAdd(&c.nchanged[(k + 1) & 1], (uint32_t)__popcll(ma));
+            if (more)
+                cb = (uint32_t)atomicAdd(&c.nchanged[(k + 1) & 1],
+                                         (unsigned long long)__popcll(ml) | ((unsigned long long)__popcll(ma) << 32));
             if (mn) old = atomicAdd(&c.cnt[fp], (unsigned long long)__popcll(mn) | ((unsigned long long)dsum << 32));
             uint32_t *rec = step_rec(w, L, t);
             if (mn) atomicAdd(rec + kRecEpsNew, (uint32_t)__popcll(mn));
@@ -1413,8 +1441,11 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         pick(w.tok_entry, fp)[q] = e;
         pick(w.tok_last, fp)[q] = dd.z;
         pick(w.tok_ub, fp)[q] = ub;
-        const uint32_t ci = cb + ra;
-        if (ci < w.claims_cap) w.changed[(k + 1) & 1][(size_t)L * w.claims_cap + ci] = pi;
+        if ((ml >> lane) & 1ull) {
+            const uint32_t ci = cb + (uint32_t)__popcll(ml & mask_lt());
+            if (ci < w.chg_cap)
+                w.changed[(k + 1) & 1][(size_t)L * w.chg_cap + ci] = make_int4(eb, (int)ed, e, (int)__float_as_uint(end));
+        }
     }
 }
 
