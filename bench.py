@@ -61,6 +61,22 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     return per, path
 
 
+def graph_kind(wl):
+    """What the synthetic graph of workload ``wl`` stands for."""
+    if wl.epsilon:
+        return "synthetic TLG-style graph with epsilon arcs"
+    return "synthetic HLG-scale graph" if wl.num_states >= 1_000_000 else "synthetic HLG-style graph"
+
+
+def degree_kind(wl):
+    kind = wl.degree[0]
+    if kind == "power":
+        return f"power-law out-degree (alpha {wl.degree[1]}, {wl.degree[2]}-{wl.degree[3]})"
+    if kind == "geom":
+        return f"geometric out-degree (p {wl.degree[1]}, cap {wl.degree[2]})"
+    return f"uniform out-degree {wl.degree[1]}-{wl.degree[2]}"
+
+
 def measure_copy_gbps(dev, mib=1024, reps=5):
     """Bandwidth of a plain device-to-device copy on this GPU (bytes read plus
     bytes written per second), the measured companion of the 8 TB/s peak."""
@@ -373,8 +389,8 @@ def main():
         "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl.name}: synthetic HLG-scale graph ({graph.num_states - 1} states, "
-                               f"{graph.num_arcs} arcs, power-law out-degree), log_prob {wl.dtype} "
+        "config": {"workload": f"{wl.name}: {graph_kind(wl)} ({graph.num_states - 1} states, "
+                               f"{graph.num_arcs} arcs, {degree_kind(wl)}), log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
                    "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay",
