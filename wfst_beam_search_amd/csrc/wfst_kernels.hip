@@ -187,7 +187,8 @@ struct LaneTab {
     uint32_t fb[kMaxLanes];        // winners-log base of the sources' compaction
     int32_t par[kMaxLanes];        // parity of the frontier the kernel reads (k_max, k_finalize)
                                    //   or closes (closure passes)
-    int32_t row[kMaxLanes];        // batch row of the lane's log-probs (k_max, k_finalize)
+    int32_t row[kMaxLanes];        // batch row of the lane's log-probs (k_max, k_finalize); in a
+                                   //   compaction round, the frontier's winners-log base (bits)
     int32_t win[kMaxLanes];        // the lane's window of the sequence (k_finalize)
 };
 
@@ -1886,6 +1887,7 @@ __device__ __forceinline__ void gc_prologue(const Work &w, LaneTab &tab, int wha
             tab.arcs[L] = c.sealed;
             tab.par[L] = p;
             tab.fb[L] = c.log_cursor;
+            tab.row[L] = (int32_t)pair_at(c.front_base, p);
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -1900,30 +1902,64 @@ __device__ __forceinline__ uint32_t gc_pos(const uint32_t *mark, const uint32_t 
     return wpre[j >> 5] + (uint32_t)__popc(mark[j >> 5] & ((1u << (j & 31u)) - 1u));
 }
 
-// Marking: every frontier token walks its chain back through the window, setting
-// live bits, and stops at the first entry already marked (or sealed, or -1).
+// Marking: every frontier token marks its own entry, then walks its chain back
+// through the window, setting live bits, and stops at the first entry already
+// marked (or sealed, or -1). Without epsilon arcs the frontier's entries are its
+// compaction's base plus the token's position, so a wavefront's 64 consecutive
+// tokens set their bits with one atomic per 32-entry word; every walk step
+// issues its predecessor load beside its atomic.
 __global__ __launch_bounds__(kBlock) void k_gc_mark(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
     gc_prologue(w, tab, 0);
     const int nl = w.max_lanes;
+    const int lane = wlane();
     uint32_t u_beg, u_end;
     wave_share(tab.base[nl], &u_beg, &u_end);
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         const int p = upar(tab.par, L);
-        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
-        if (i >= tab.n[L]) continue;
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const bool valid = i < tab.n[L];
         const uint32_t sealed = tab.arcs[L], cursor = tab.fb[L];
         uint32_t *mark = w.gc_mark + (size_t)L * gc_words(w);
         const long long lbase = (long long)L * w.arena;
-        const int32_t ge = pick(w.tok_entry, p)[(size_t)L * w.frontier_cap + i];
-        long long e = ge < 0 ? -1 : (long long)ge - lbase;   // the start token has no entry
+        const uint32_t fb = (uint32_t)tab.row[L];
+        long long e = -1;                           // the token's own entry (local), -1: none
+        if (!w.has_eps) {
+            if (valid && fb != 0xFFFFFFFFu) e = (long long)fb + i;   // (the start token has no entry)
+        } else if (valid) {
+            const int32_t ge = pick(w.tok_entry, p)[(size_t)L * w.frontier_cap + i];
+            e = ge < 0 ? -1 : (long long)ge - lbase;
+        }
+        const bool own = e >= (long long)sealed && e < (long long)cursor;
+        const uint32_t j0 = own ? (uint32_t)(e - sealed) : 0u;
+        int32_t prev = own ? w.wlog[lbase + e].x : -1;
+        if (!w.has_eps) {
+            // consecutive tokens own consecutive entries: each word's bits form one
+            // run over a run of lanes
+            const unsigned long long om = __ballot(own);
+            if (om) {
+                const uint32_t wfirst = __shfl(j0 >> 5, __ffsll((long long)om) - 1, kWave);
+#pragma unroll
+                for (uint32_t q = 0; q < 3u; ++q) {
+                    const unsigned long long bm = __ballot(own && (j0 >> 5) == wfirst + q);
+                    if (!bm) continue;
+                    const int la = __ffsll((long long)bm) - 1, lb = 63 - __clzll((long long)bm);
+                    const uint32_t ba = __shfl(j0 & 31u, la, kWave), bb = __shfl(j0 & 31u, lb, kWave);
+                    if (lane == la) atomicOr(&mark[wfirst + q], ((2u << bb) - 1u) & ~((1u << ba) - 1u));
+                }
+            }
+        } else if (own) {
+            atomicOr(&mark[j0 >> 5], 1u << (j0 & 31u));
+        }
+        if (!own) continue;
+        e = prev < 0 ? -1 : (long long)prev - lbase;
         while (e >= (long long)sealed && e < (long long)cursor) {
             const uint32_t j = (uint32_t)(e - sealed), bit = 1u << (j & 31u);
+            prev = w.wlog[lbase + e].x;
             if (atomicOr(&mark[j >> 5], bit) & bit) break;
-            const int32_t prev = w.wlog[lbase + e].x;
             e = prev < 0 ? -1 : (long long)prev - lbase;
         }
     }
