@@ -1788,19 +1788,31 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
             score = __shfl(bs, src, kWave);
         }
     }
+    // The walk goes back entry by entry (newest arc first) until it reaches the
+    // lane's sealed prefix: compaction keeps there the path every live token
+    // shares, one chain in log order (each entry's predecessor is the one
+    // before it, the first one's the start token), so the path ends with
+    // entries tail - 1, ..., 0, read in one sweep.
+    uint32_t tail = 0;
     if (lane == 0 && has_path) {
         const long long limit = (long long)w.max_lanes * w.arena;
+        const long long lbase = (long long)L * w.arena, sb = lbase + c.sealed;
         int32_t e = start;   // -1: the start token (empty path)
         while (e >= 0 && e < limit) {
+            if (e < sb) { tail = (uint32_t)(e - lbase) + 1u; break; }
             const int2 r = w.wlog[e];
             if (len < w.path_cap) arcs[len] = r.y;
             ++len;
             e = r.x;
             if (len > (uint32_t)w.arena) break;
         }
-        if (len > w.path_cap) ovf |= kOvfPath;
     }
     len = __shfl(len, 0, kWave);
+    tail = __shfl(tail, 0, kWave);
+    for (uint32_t x = (uint32_t)lane; x < tail && len + x < w.path_cap; x += kWave)
+        arcs[len + x] = w.wlog[(long long)L * w.arena + (tail - 1u - x)].y;
+    len += tail;
+    if (len > w.path_cap) ovf |= kOvfPath;
     ovf = __shfl(ovf, 0, kWave);
     const uint32_t ns = min(len, w.path_cap);
     __syncthreads();
