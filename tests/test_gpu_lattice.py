@@ -105,6 +105,7 @@ def test_lattice_capacity_and_rejections():
     dec = wb.Decoder(dg, 8.0, 1000, max_lanes=1, max_frames=12, lattice=True, output_beam=5.0, lattice_cap=4)
     r = dec.decode(torch.from_numpy(lp).cuda(), [12])
     assert int(r.meta[0, 2]) & 4 and int(r.meta[0, 0]) == 0      # arena bit: lattice full
+    assert dec.stats()["regrows"] == 0                           # (not the log: no re-run)
     with pytest.raises(wb.WfstError):
         dec.create_stream()                                          # no streams in lattice mode
     dec.close()

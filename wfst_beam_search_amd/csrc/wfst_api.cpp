@@ -771,13 +771,18 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
         for (int32_t b = 0; b < B; ++b)
             grow |= (d->h_res[rs * (size_t)b + kResOverflow] & kOvfArena) != 0;
         if (!grow) break;
-        // the log grows about linearly with the frames: aim at the longest lane's
-        // end from the step where the first one stopped, at least doubling
+        // (the arena bit also reports a full lattice: only lanes the log's bound
+        // stopped count)
         std::vector<LaneCtl> ctl((size_t)c.max_lanes);
         HIP_TRY(hipMemcpy(ctl.data(), d->ctl, sizeof(LaneCtl) * ctl.size(), hipMemcpyDeviceToHost));
+        grow = false;
+        for (int32_t b = 0; b < B; ++b) grow |= ctl[(size_t)b].log_full != 0u;
+        if (!grow) break;
+        // the log grows about linearly with the frames: aim at the longest lane's
+        // end from the step where the first one stopped, at least doubling
         uint64_t want = 2ull * d->log.lim;
         for (int32_t b = 0; b < B; ++b) {
-            if (!(d->h_res[rs * (size_t)b + kResOverflow] & kOvfArena)) continue;
+            if (!ctl[(size_t)b].log_full) continue;
             const uint64_t done = (uint64_t)std::max(ctl[(size_t)b].last_step, 0) + 1;
             want = std::max<uint64_t>(want, (uint64_t)d->log.lim * ((uint64_t)lengths_host[b] + 2) * 5 / (4 * done));
         }

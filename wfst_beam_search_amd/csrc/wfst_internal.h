@@ -107,6 +107,7 @@ struct alignas(128) LaneCtl {
     uint32_t gc_on;            // this round compacts the lane
     uint32_t gc_live;          // live entries of the window (after the scan)
     uint32_t eps_n0;           // frontier tokens when the current closure pass began
+    uint32_t log_full;         // 1: the winners log's committed bound stopped the lane
     alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
                                              //   step's class) << 32
     alignas(128) uint32_t nclaims[2];        // candidate-list length of the slot pass by step parity

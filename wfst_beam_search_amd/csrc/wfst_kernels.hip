@@ -388,6 +388,7 @@ __device__ void init_lane(const Work &w, int L, int T)
     c.T = T;
     c.status = kActive;
     c.overflow = 0u;
+    c.log_full = 0u;
     c.reached_final = 0;
     c.beam[0] = w.beam;
     c.beam[1] = w.beam;
@@ -927,6 +928,7 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
         c.reached_final = 1;
     } else {
         atomicOr(&c.overflow, kOvfArena);
+        c.log_full = 1u;
     }
 }
 
@@ -1133,6 +1135,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena_lim) {
             if (lane == leader) {
                 atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
+                if (pos_ok) c.log_full = 1u;
                 c.status = kDone;
                 c.phase_final = kPhDead;
             }
@@ -1414,6 +1417,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         if (!pos_ok || (unsigned long long)lb + (uint32_t)__popcll(ma) > w.arena_lim) {
             if (lane == leader) {
                 atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
+                if (pos_ok) c.log_full = 1u;
                 c.status = kDone;
                 c.phase_final = kPhDead;
             }
