@@ -258,6 +258,58 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
     dg.release()
 
 
+def blank_skip_bench(args, wl, graph, lp, lengths, dev):
+    """Blank-skip pre-slicing of the whole batch per timed step: the blank column
+    read for every frame, kept rows copied, the rest of the output zeroed."""
+    import numpy as np
+    import torch
+
+    import wfst_beam_search_amd as wb
+    B, T, V = lp.shape
+    dg = wb.Graph(graph, device=0)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
+                     eps_iterations=wl.eps_iterations, arena_entries=1 << 16, arena_commit=-1)
+    x = torch.from_numpy(lp).to(dev)
+    blank = 0
+    for _ in range(args.warmup):
+        dec.blank_skip(x, lengths, blank, args.blank_skip)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(s)
+        _, kept = dec.blank_skip(x, lengths, blank, args.blank_skip)   # returns after its stream finished
+        b.record(s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gpu_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    elem = 2 if wl.dtype == "f16" else 4
+    frames = int(np.asarray(lengths).sum())
+    nk = int(np.asarray(kept).sum())
+    # blank value of every frame, kept rows read and written, the other rows zeroed
+    nbytes = frames * elem + 2 * nk * V * elem + (B * T - nk) * V * elem
+    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
+    line = {
+        "metric": "blank-skip pre-slicing throughput at 1 GPU (frames in per second)",
+        "value": round(frames * args.steps / dt, 1), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name} log_prob {wl.dtype} [{B},{T},{V}], lengths "
+                               f"{wl.lengths[0]}-{wl.lengths[1]}, blank id {blank}, threshold {args.blank_skip}",
+                   "batch": B, "frames": T, "vocab": V},
+        "kept_frames": nk, "input_frames": frames,
+        "gpu_ms_per_call": round(gpu_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "blank_scan + blank_copy (one call)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(nbytes)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    dec.close()
+    dg.release()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +338,9 @@ def main():
                          "release per timed step) instead of one batch decode")
     ap.add_argument("--stream-partial", action="store_true",
                     help="with --stream-chunk: ask for every lane's partial hypothesis after each chunk")
+    ap.add_argument("--blank-skip", type=float, default=None, metavar="THRESHOLD",
+                    help="time blank-skip pre-slicing of the workload's log_prob (frames whose blank "
+                         "probability exceeds THRESHOLD dropped) instead of a decode")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -318,6 +373,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.stream_chunk > 0:
         stream_bench(args, wl, graph, lp, lengths, dev)
+        return
+    if args.blank_skip is not None:
+        blank_skip_bench(args, wl, graph, lp, lengths, dev)
         return
     dg = wb.Graph(graph, device=0)
     lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice)

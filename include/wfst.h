@@ -371,6 +371,18 @@ int wfst_lattice_records(wfst_decoder_t d, int32_t lane, int32_t *out, int64_t c
 int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n);
 
 /*
+ * Device memory of a decoder (page section 6.2, wfst_decoder_mem_stats), bytes:
+ *  out[0] reserved: the fixed workspace plus the winners-log address range,
+ *  out[1] committed: the fixed workspace plus the winners-log memory mapped,
+ *  out[2] fixed: the workspace allocated whole at creation (tokens, tables,
+ *         candidate lists, records, results; not the graph),
+ *  out[3] winners-log high water: the largest lane's log after the last
+ *         decode or stream call (entries x 8).
+ * Errors: WFST_EINVAL (null), WFST_EDEVICE.
+ */
+int wfst_decoder_mem_stats(wfst_decoder_t d, int64_t out[4]);
+
+/*
  * Per-step records of lane `lane` in the last decode or stream call (steps
  * numbered from the call's first), 16 int64 each:
  *  {n, beam bits, max bits, arcs, admitted, distinct, eps arcs, eps admitted,

@@ -20,10 +20,11 @@ def _say(*a):
     print(*a, flush=True)
 
 
+@pytest.mark.parametrize("vocab", [9, 64])      # (rows 16-byte aligned only at 64: the vector copy)
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_blank_skip_matches_oracle(dtype):
+def test_blank_skip_matches_oracle(dtype, vocab):
     import torch
-    g = synth.random_graph(41, n=30, deg=(1, 5), vocab=9, self_loop=0.3)
+    g = synth.random_graph(41, n=30, deg=(1, 5), vocab=vocab, self_loop=0.3)
     dg = wb.Graph(g)
     dec = wb.Decoder(dg, 8.0, 200, max_lanes=6, max_frames=300, lp_dtype=dtype)
     for seed, (B, T, boost, thr) in enumerate([(6, 300, 6.0, 0.98), (3, 77, 4.0, 0.9), (5, 1, 9.0, 0.98),

@@ -147,12 +147,16 @@ def test_lazy_region_commits_on_demand():
         r2 = dec.decode(x, L2)
         s2 = dec.stats()
         steps = [dec.step_stats(b) for b in range(3)]
+        ms = dec.mem_stats()
         dec.close()
         rf, _, sf = gpu_decode(g, lp2, L2, wl.beam, wl.max_active, dgraph=dg, with_steps=False, arena_commit=-1)
     finally:
         dg.release()
     _say("lazy", s1["regrows"], s1["log_committed_bytes"], "of", s1["log_reserved_bytes"], "entries", s1["log_entries"])
     assert s1["regrows"] >= 1 and s2["regrows"] == 0
+    assert ms["reserved"] == ms["fixed"] + s2["log_reserved_bytes"]
+    assert ms["committed"] == ms["fixed"] + s2["log_committed_bytes"] < ms["reserved"]
+    assert 0 < ms["log_high_water"] <= s2["log_committed_bytes"] // 3 and ms["log_high_water"] * 3 >= s2["log_entries"] * 8
     assert s1["log_entries"] * 8 <= s1["log_committed_bytes"] < s1["log_reserved_bytes"]
     assert sf["log_committed_bytes"] >= sf["log_reserved_bytes"] and sf["regrows"] == 0
     compare_batch(r2, steps, oracle_lanes(g, lp2, L2, wl.beam, wl.max_active))

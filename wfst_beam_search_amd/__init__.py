@@ -26,7 +26,7 @@ _LIB_PATH = os.path.join(_HERE, "libwfst_mi355x.so")
 LP_F32, LP_F16 = 0, 1
 EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release",
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
-                    "wfst_decoder_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
+                    "wfst_decoder_stats", "wfst_decoder_mem_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
                     "wfst_finalize_stream", "wfst_release_stream", "wfst_lattice_records",
                     "wfst_blank_skip")
@@ -106,6 +106,7 @@ def load_library():
         lib.wfst_decoder_destroy.argtypes = [vp]
         lib.wfst_decode.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_decoder_stats.argtypes = [vp, vp, i32]
+        lib.wfst_decoder_mem_stats.argtypes = [vp, vp]
         lib.wfst_decoder_step_stats.argtypes = [vp, i32, vp, i32]
         lib.wfst_decoder_profile.argtypes = [vp, i32]
         lib.wfst_decoder_kernel_times.argtypes = [vp, vp, i32]
@@ -347,6 +348,12 @@ class Decoder:
         out = np.zeros(len(STAT_FIELDS), dtype=np.int64)
         _check(_lib.wfst_decoder_stats(self.handle, _ptr(out), len(STAT_FIELDS)))
         return dict(zip(STAT_FIELDS, (int(x) for x in out)))
+
+    def mem_stats(self) -> dict:
+        """Device bytes: reserved, committed, fixed workspace, winners-log high water."""
+        out = np.zeros(4, dtype=np.int64)
+        _check(_lib.wfst_decoder_mem_stats(self.handle, _ptr(out)))
+        return dict(zip(("reserved", "committed", "fixed", "log_high_water"), (int(x) for x in out)))
 
     def step_stats(self, lane: int) -> np.ndarray:
         """Per-step records of ``lane`` in the last decode: int64 [n, 16]

@@ -1082,6 +1082,28 @@ extern "C" int wfst_decoder_stats(wfst_decoder_t d, int64_t *out, int32_t n)
     return WFST_OK;
 }
 
+extern "C" int wfst_decoder_mem_stats(wfst_decoder_t d, int64_t out[4])
+{
+    if (!d || !out) return fail(WFST_EINVAL, "bad arguments");
+    std::lock_guard<std::mutex> lock(d->mu);
+    int64_t hw = 0;
+    bool any = false;
+    for (int32_t x : d->last_len) any |= x >= 0;
+    if (any) {
+        std::vector<LaneCtl> ctl((size_t)d->cfg.max_lanes);
+        HIP_TRY(hipSetDevice(d->g->device));
+        HIP_TRY(hipMemcpy(ctl.data(), d->ctl, sizeof(LaneCtl) * ctl.size(), hipMemcpyDeviceToHost));
+        for (int b = 0; b < d->cfg.max_lanes; ++b)
+            if (d->last_len[(size_t)b] >= 0)
+                hw = std::max<int64_t>(hw, std::min<int64_t>(ctl[(size_t)b].log_cursor, d->w.arena));
+    }
+    out[0] = (int64_t)(d->bytes + d->log.va_bytes);
+    out[1] = (int64_t)(d->bytes + d->log.committed_bytes());
+    out[2] = (int64_t)d->bytes;
+    out[3] = hw * (int64_t)sizeof(int2);
+    return WFST_OK;
+}
+
 extern "C" int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_t steps_cap)
 {
     if (!d || !out || steps_cap < 0) return fail(WFST_EINVAL, "bad arguments");

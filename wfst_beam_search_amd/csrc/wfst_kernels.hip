@@ -2204,7 +2204,8 @@ __global__ __launch_bounds__(kSkipBlock) void k_blank_scan(const Work *__restric
     if (threadIdx.x == 0) w.bs_len[b] = (int32_t)run;
 }
 
-// One wavefront per output row: the kept row's copy, or zeros past the count.
+// One wavefront per output row: the kept row's copy, or zeros past the count;
+// 16-byte accesses when every row of both tensors starts 16-byte aligned.
 template <typename LPT>
 __global__ __launch_bounds__(kBlock) void k_blank_copy(const Work *__restrict__ wp, LPT *__restrict__ out, int T)
 {
@@ -2212,15 +2213,30 @@ __global__ __launch_bounds__(kBlock) void k_blank_copy(const Work *__restrict__ 
     const LpDesc d = *w.lp;
     const int wpb = kBlock / kWave;
     const long long rows = (long long)d.B * T;
+    constexpr uint32_t kPer = 16 / sizeof(LPT);
+    const bool vec = ((uintptr_t)d.base & 15u) == 0 && ((uintptr_t)out & 15u) == 0 && d.stride_t % kPer == 0 &&
+                     d.stride_b % kPer == 0;
+    const uint32_t V = (uint32_t)w.vocab, nvec = vec ? V / kPer : 0u;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     for (long long r = (long long)blockIdx.x * wpb + threadIdx.x / kWave; r < rows; r += (long long)gridDim.x * wpb) {
         const int b = (int)(r / T), i = (int)(r % T);
         LPT *o = out + (long long)b * d.stride_b + (long long)i * d.stride_t;
+        uint4 *o4 = (uint4 *)o;
         if (i < w.bs_len[b]) {
             const LPT *row = (const LPT *)d.base + (long long)b * d.stride_b +
                              (long long)w.bs_src[(size_t)b * w.max_frames + i] * d.stride_t;
-            for (int v = wlane(); v < w.vocab; v += kWave) o[v] = row[v];
+            const uint4 *r4 = (const uint4 *)row;
+            // four loads in flight per lane before their stores
+            uint32_t k = wlane();
+            for (; k + 3u * kWave < nvec; k += 4u * kWave) {
+                const uint4 a0 = r4[k], a1 = r4[k + kWave], a2 = r4[k + 2u * kWave], a3 = r4[k + 3u * kWave];
+                o4[k] = a0; o4[k + kWave] = a1; o4[k + 2u * kWave] = a2; o4[k + 3u * kWave] = a3;
+            }
+            for (; k < nvec; k += kWave) o4[k] = r4[k];
+            for (uint32_t v = nvec * kPer + wlane(); v < V; v += kWave) o[v] = row[v];
         } else {
-            for (int v = wlane(); v < w.vocab; v += kWave) o[v] = (LPT)0.0f;
+            for (uint32_t k = wlane(); k < nvec; k += kWave) o4[k] = z4;
+            for (uint32_t v = nvec * kPer + wlane(); v < V; v += kWave) o[v] = (LPT)0.0f;
         }
     }
 }
