@@ -249,3 +249,49 @@ def test_capacity_overflow_is_flagged(cid, cap, bit):
     for b in range(2):
         compare_lane(b, r2, None, o[b], check_steps=False)
     dec.close(); dg.release()
+
+
+def test_threads_and_streams():
+    """Two threads sharing one decoder (its calls are serial), then two decoders
+    running at once on streams of their own: every result equals a sequential
+    decode's."""
+    import threading
+    import torch
+    cid = 2
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    halves = [(np.ascontiguousarray(lp[:4]), L[:4]), (np.ascontiguousarray(lp[4:]), L[4:])]
+    dg = wb.Graph(g)
+    got, errs = {}, []
+    try:
+        want = [gpu_decode(g, x, n, wl.beam, wl.max_active, dgraph=dg, with_steps=False)[0] for x, n in halves]
+        decs = [wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=4, max_frames=lp.shape[1]) for _ in range(2)]
+        xs = [torch.from_numpy(x).cuda() for x, _ in halves]
+        torch.cuda.synchronize()
+
+        def run(tag, dec, i, stream):
+            try:
+                with torch.cuda.stream(stream):
+                    for rep in range(3):
+                        got[(tag, i, rep)] = dec.decode(xs[i], halves[i][1])
+            except Exception as e:      # reported below, in the test's thread
+                errs.append(e)
+
+        for tag, pick in (("shared", lambda i: decs[0]), ("own", lambda i: decs[i])):
+            _say("threads", tag)
+            ths = [threading.Thread(target=run, args=(tag, pick(i), i, torch.cuda.Stream())) for i in range(2)]
+            for th in ths:
+                th.start()
+            for th in ths:
+                th.join()
+        for dec in decs:
+            dec.close()
+    finally:
+        dg.release()
+    assert not errs, errs
+    assert len(got) == 12
+    for (tag, i, rep), r in got.items():
+        w = want[i]
+        for b in range(4):
+            assert np.array_equal(r.arcs[b], w.arcs[b]) and np.array_equal(r.words[b], w.words[b]), (tag, i, rep, b)
+            assert np.float32(r.scores[b]) == np.float32(w.scores[b]) and np.array_equal(r.meta[b], w.meta[b])
