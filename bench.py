@@ -119,14 +119,17 @@ def traffic_from_profiles(kernel, workload_name):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(graph, lp, lengths, wl, seconds):
+def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None):
+    """The oracle on one pinned core over the batch's first lanes for about
+    ``seconds``; with ``gpu`` (the timed run's last result) each of those lanes
+    is also compared with it: arcs and words equal, score bits equal."""
     import numpy as np
 
     import oracle
     os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     og = oracle.OracleGraph(graph)
     frames = arcs = 0
-    lanes = 0
+    lanes = same = 0
     t0 = time.perf_counter()
     for b in range(lp.shape[0]):
         r = oracle.decode_lane(og, lp[b], int(lengths[b]), wl.beam, wl.max_active,
@@ -134,6 +137,10 @@ def cpu_baseline(graph, lp, lengths, wl, seconds):
         frames += int(lengths[b])
         arcs += int(r["steps"][:, 4].sum() + r["steps"][:, 7].sum())
         lanes += 1
+        if gpu is not None:
+            same += int(np.array_equal(gpu.arcs[b], r["arcs"]) and np.array_equal(gpu.words[b], r["words"]) and
+                        np.float32(gpu.scores[b]).tobytes() == np.float32(r["score"]).tobytes() and
+                        int(gpu.meta[b, 1]) == int(r["reached_final"]))
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
@@ -148,6 +155,7 @@ def cpu_baseline(graph, lp, lengths, wl, seconds):
         pass
     return {"value": frames / dt, "unit": "frames/s", "cores": 1, "kind": "oracle",
             "arcs_per_s": arcs / dt,
+            **({} if gpu is None else {"gpu_lanes_identical": f"{same}/{lanes}"}),
             "sample": f"lanes 0..{lanes - 1} of the {wl.name} batch ({frames} frames, {dt:.1f} s, "
                       f"single-threaded C oracle pinned to one core; host nproc {os.cpu_count()}, {model})"}
 
@@ -440,7 +448,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds)
+        cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds, gpu=res)
 
     line = {
         "metric": "decoded frames/sec and arcs expanded/sec at 1 GPU; % of HBM peak",
