@@ -408,7 +408,7 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_STREAM_BEGIN 10 /* stream call: applies the per-lane plan                   */
 #define WFST_K_STREAM_END  11  /* stream call: commits the chunk's last compaction        */
 #define WFST_K_RECLASS     12  /* stream end: final-step class of the stream's tokens      */
-#define WFST_K_LAT_RESOLVE 13  /* lattice: destination positions of a step's arcs         */
+#define WFST_K_LAT_RESOLVE 13  /* not launched (the next step's WFST_K_FINALIZE does it)  */
 #define WFST_K_LAT_INIT    14  /* lattice: backward scores to -inf                        */
 #define WFST_K_LAT_BACK    15  /* lattice: backward pass and prune of one step's arcs     */
 #define WFST_K_GC_BEGIN    16  /* log compaction round: set-up and commit                 */

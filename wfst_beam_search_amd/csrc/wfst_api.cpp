@@ -614,7 +614,6 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
         if ((e = wrap_clear(d, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
-        if (d->w.lattice && (e = launch(d, kKLatResolve, t, 0, s)) != hipSuccess) return e;
         for (int k = 1; k <= d->passes; ++k) {
             if ((e = wrap_clear(d, t, k, s)) != hipSuccess) return e;
             if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;

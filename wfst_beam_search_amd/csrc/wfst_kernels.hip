@@ -933,10 +933,35 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
 }
 
 
-__device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
+// Lattice mode: the arcs the step before persisted, whose destination states
+// become positions in the frontier that step built. Its position map is still
+// that frontier's here (this compaction writes the other parity's).
+struct LatTab {
+    uint32_t base[kMaxLanes + 1];  // exclusive prefix of work units per lane
+    uint32_t n[kMaxLanes];         // arcs of the step before
+    uint32_t a0[kMaxLanes];        // the first of them
+};
+
+__device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, LatTab &lt)
 {
     const uint32_t ep = round_epoch(w, t, 0);
     const LpDesc lpd = *w.lp;
+    if (w.lattice && threadIdx.x < kWave) {
+        const int L = (int)threadIdx.x;
+        uint32_t n = 0, a0 = 0;
+        // a lane that ran step t - 1 and began step t (whatever step t then did)
+        if (L < w.max_lanes && t >= 1 && w.ctl[L].last_step == t) {
+            const size_t F = (size_t)w.max_frames + 3;
+            a0 = w.lat_aoff[(size_t)L * F + t - 1];
+            const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t], w.lat_cap);
+            n = a1 > a0 ? a1 - a0 : 0u;
+        }
+        if (L < w.max_lanes) { lt.n[L] = n; lt.a0[L] = a0; }
+        uint32_t tot;
+        const uint32_t ex = wave_excl_sum((n + kWave - 1) / kWave, &tot);
+        if (L < w.max_lanes) lt.base[L] = ex;
+        if (L == 0) lt.base[w.max_lanes] = tot;
+    }
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
@@ -1162,13 +1187,29 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab)
         write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
     post_bound(w, lb_lane, lb_np, lb_acc);
+    if (w.lattice) {
+        // the step before's lattice arcs: destination state -> position among the
+        // tokens of frame t (the parity this compaction reads)
+        uint32_t v_beg, v_end;
+        wave_share(lt.base[nl], &v_beg, &v_end);
+        for (uint32_t u = v_beg; u < v_end; ++u) {
+            const int L = find_lane(lt.base, nl, u);
+            const int p = upar(tab.par, L);
+            const uint32_t i = (u - lt.base[L]) * kWave + (uint32_t)lane;
+            if (i >= lt.n[L]) continue;
+            int4 *r = w.lat_arc + (size_t)L * w.lat_cap + lt.a0[L] + i;
+            const int32_t d = r->z;
+            if ((uint32_t)d < (uint32_t)w.num_states) r->z = pick(w.pos, p)[(size_t)L * w.num_states + d];
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
-    ph_finalize(w, t, tab);
+    __shared__ LatTab lt;
+    ph_finalize(w, t, tab, lt);
 }
 
 // ---------------------------------------------------------- epsilon closure
@@ -1470,45 +1511,6 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
 // bwd(token) = max over its arcs of s + bwd(destination) and keeps the arcs with
 // (fwd(source) + s) + bwd(destination) >= best - output_beam, where s is the
 // arc's own score (weight + log-prob; a final arc's weight; 0 for a redirect).
-
-// After finalize of step t: the destination state of each of the step's arcs
-// becomes its token's position at frame t + 1 (the position map of that frame).
-__global__ __launch_bounds__(kBlock) void k_lat_resolve(const Work *__restrict__ wp, int t)
-{
-    const Work &w = *wp;
-    __shared__ LaneTab tab;
-    const size_t F = (size_t)w.max_frames + 3;
-    if (threadIdx.x < kWave) {
-        const int L = (int)threadIdx.x;
-        uint32_t units = 0;
-        if (L < w.max_lanes) {
-            const LaneCtl &c = w.ctl[L];
-            // a real step the lane ran and survived
-            const bool on = c.status == kActive && c.last_step == t && t < c.T;
-            const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
-            const uint32_t a1 = min(c.lat_cursor, w.lat_cap);
-            const uint32_t n = (on && a1 > a0) ? a1 - a0 : 0u;
-            units = (n + kWave - 1) / kWave;
-            tab.n[L] = n;
-            tab.fb[L] = a0;
-            tab.par[L] = lane_par(c, t + 1);
-        }
-        tab_publish(tab, w.max_lanes, units);
-    }
-    __syncthreads();
-    const int nl = w.max_lanes;
-    uint32_t u_beg, u_end;
-    wave_share(tab.base[nl], &u_beg, &u_end);
-    for (uint32_t u = u_beg; u < u_end; ++u) {
-        const int L = find_lane(tab.base, nl, u);
-        const int p = upar(tab.par, L);
-        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
-        if (i >= tab.n[L]) continue;
-        int4 *r = w.lat_arc + (size_t)L * w.lat_cap + tab.fb[L] + i;
-        const int32_t d = r->z;
-        if ((uint32_t)d < (uint32_t)w.num_states) r->z = pick(w.pos, p)[(size_t)L * w.num_states + d];
-    }
-}
 
 // Before the backward pass: every backward score of a lane with a result is
 // -inf (its winners-log entries and the start token's slot).
@@ -2288,7 +2290,6 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamEnd: go(k_stream_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKReclass: go(k_reclass, dim3(w.max_lanes), dim3(kReclassBlock), s, e0, e1, dw); break;
-    case kKLatResolve: go(k_lat_resolve, G, B, s, e0, e1, dw, t); break;
     case kKLatInit: go(k_lat_init, G, B, s, e0, e1, dw); break;
     case kKLatBack:
         if (f16) go(k_lat_back<__half>, G, B, s, e0, e1, dw, t);
