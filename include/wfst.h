@@ -251,8 +251,9 @@ int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *c, wfst_decod
  * the last step without allow_partial) reports ok = 1, reached_final = 0,
  * score -inf and no arcs. The call is idempotent and serial per decoder (an
  * internal mutex); other decoders may run concurrently.
- * Errors: WFST_EINVAL (ranges above, null pointers, V mismatch, or the decoder
- * holds open streams), WFST_EDEVICE.
+ * Errors: WFST_EINVAL (ranges above, null pointers, V mismatch, the decoder
+ * holds open streams, or log_prob is not device memory of the decoder's device
+ * or ends before B * T * V elements), WFST_EDEVICE.
  */
 int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
                 const int32_t *lengths_host, void *stream,
@@ -300,7 +301,8 @@ int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel);
  *                search has died). Otherwise the outputs are not touched and may
  *                be null.
  * Errors: WFST_EINVAL (ranges above, a channel not open or repeated, null
- * pointers), WFST_EDEVICE.
+ * pointers, log_prob not device memory of the decoder's device or shorter than
+ * C * T * V elements), WFST_EDEVICE.
  */
 int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int32_t C, const void *log_prob,
                        int32_t T, int32_t V, const int32_t *lengths_host, void *stream,
@@ -332,7 +334,8 @@ int wfst_release_stream(wfst_decoder_t d, int32_t channel);
  * out_lengths_host [B] the kept counts. Runs on the decoder's device and stream
  * argument like wfst_decode (its scratch is the decoder's); returns after
  * synchronising the stream. Ranges as wfst_decode's, blank_id in [0, V),
- * threshold > 0 finite. Errors: WFST_EINVAL, WFST_EDEVICE.
+ * threshold > 0 finite; both tensors device memory of the decoder's device
+ * holding B * T * V elements. Errors: WFST_EINVAL, WFST_EDEVICE.
  */
 int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, int32_t V,
                     const int32_t *lengths_host, int32_t blank_id, float threshold, void *out_log_prob,

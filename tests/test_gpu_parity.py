@@ -295,3 +295,32 @@ def test_threads_and_streams():
         for b in range(4):
             assert np.array_equal(r.arcs[b], w.arcs[b]) and np.array_equal(r.words[b], w.words[b]), (tag, i, rep, b)
             assert np.float32(r.scores[b]) == np.float32(w.scores[b]) and np.array_equal(r.meta[b], w.meta[b])
+
+
+def test_buffers_not_on_the_device_are_rejected():
+    """log_prob in pinned host memory (readable by the GPU, so no access can
+    fault) is refused by the C ABI with WFST_EINVAL before any launch: decode,
+    blank-skip input and output."""
+    import ctypes
+    import torch
+    g = synth.random_graph(31, n=10, deg=(1, 4), vocab=5)
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, 8.0, 100, max_lanes=2, max_frames=10)
+    host = torch.zeros((2, 10, g.vocab), dtype=torch.float32, pin_memory=True)
+    dev = torch.zeros((2, 10, g.vocab), dtype=torch.float32, device="cuda")
+    lens = np.array([10, 5], np.int32)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out_words, wl, out_arcs, al, sc, meta = dec._outputs(2, 12, 12)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = wb._lib.wfst_decode(dec.handle, ctypes.c_void_p(host.data_ptr()), 2, 10, g.vocab, p(lens), s,
+                             p(out_words), 12, p(wl), p(out_arcs), 12, p(al), p(sc), p(meta))
+    assert rc == -1 and b"device memory" in wb._lib.wfst_last_error()
+    outl = np.zeros(2, np.int32)
+    for src, dst in ((host, dev), (dev, host)):
+        rc = wb._lib.wfst_blank_skip(dec.handle, ctypes.c_void_p(src.data_ptr()), 2, 10, g.vocab, p(lens), 0,
+                                     ctypes.c_float(0.98), ctypes.c_void_p(dst.data_ptr()), p(outl), s)
+        assert rc == -1 and b"device memory" in wb._lib.wfst_last_error()
+    r = dec.decode(dev, lens)                  # the decoder still works
+    assert r.meta.shape == (2, 3)
+    dec.close()
+    dg.release()

@@ -225,6 +225,8 @@ class Decoder:
         import torch
         if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda:
             raise TypeError("log_prob must be a torch tensor on the GPU")
+        if log_prob.device.index != self.graph.device:
+            raise ValueError(f"log_prob must be on cuda:{self.graph.device}, the decoder's device")
         if not log_prob.is_contiguous():
             raise ValueError("log_prob must be packed (contiguous)")
         want = torch.float16 if self.lp_dtype == "f16" else torch.float32

@@ -56,6 +56,30 @@ int dalloc(T **p, size_t count, std::vector<void *> *owned, size_t *bytes)
 }
 
 
+// A caller's buffer of `bytes` bytes at p that the kernels will read or write
+// (page section 4: a bad tensor fails with an error, never an out-of-bounds
+// access): device (or managed) memory of `device`, inside one allocation.
+int check_device_buffer(const void *p, size_t bytes, int device, const char *what)
+{
+    if (bytes == 0) return WFST_OK;
+    hipPointerAttribute_t a{};
+    if (!p || hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(WFST_EINVAL, std::string(what) + " is not device memory");
+    }
+    if (!a.isManaged && (a.type != hipMemoryTypeDevice || a.device != device))
+        return fail(WFST_EINVAL, std::string(what) + " is not device memory of the decoder's device");
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base) {
+        if ((const char *)p + bytes > (const char *)base + size)
+            return fail(WFST_EINVAL, std::string(what) + " ends past its allocation");
+    } else {
+        (void)hipGetLastError();
+    }
+    return WFST_OK;
+}
+
 // The winners log as a lazily committed region (page section 6.2): the whole
 // max_lanes x arena range is reserved as device address space once, so every
 // pointer a kernel or a captured graph holds stays valid, and physical chunks
@@ -722,6 +746,11 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     std::lock_guard<std::mutex> lock(d->mu);
     if (d->open_streams > 0) return fail(WFST_EINVAL, "the decoder has open streams (release them first)");
     HIP_TRY(hipSetDevice(d->g->device));
+    const size_t elem = c.lp_dtype == WFST_LP_F16 ? 2 : 4;
+    if (maxlen > 0) {
+        const int rcb = check_device_buffer(log_prob, (size_t)B * (size_t)T * (size_t)V * elem, d->g->device, "log_prob");
+        if (rcb != WFST_OK) return rcb;
+    }
     hipStream_t s = (hipStream_t)stream;
     const size_t L = (size_t)c.max_lanes;
     int rc0 = set_round_base(d, 0, s);
@@ -972,6 +1001,11 @@ extern "C" int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int
     }
     if (steps > 0 && !log_prob) return fail(WFST_EINVAL, "log_prob is null");
     HIP_TRY(hipSetDevice(d->g->device));
+    if (steps > 0) {
+        const size_t elem = c.lp_dtype == WFST_LP_F16 ? 2 : 4;
+        const int rcb = check_device_buffer(log_prob, (size_t)C * (size_t)T * (size_t)V * elem, d->g->device, "log_prob");
+        if (rcb != WFST_OK) return rcb;
+    }
     hipStream_t s = (hipStream_t)stream;
     LpDesc *hd = (LpDesc *)d->h_in;
     hd->base = log_prob;
@@ -1196,6 +1230,12 @@ extern "C" int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B
         if (lengths_host[b] < 0 || lengths_host[b] > T) return fail(WFST_EINVAL, "lengths must lie in [0, T]");
     std::lock_guard<std::mutex> lock(d->mu);
     HIP_TRY(hipSetDevice(d->g->device));
+    if (T > 0) {
+        const size_t nb = (size_t)B * (size_t)T * (size_t)V * (c.lp_dtype == WFST_LP_F16 ? 2 : 4);
+        int rcb = check_device_buffer(log_prob, nb, d->g->device, "log_prob");
+        if (rcb == WFST_OK) rcb = check_device_buffer(out_log_prob, nb, d->g->device, "out_log_prob");
+        if (rcb != WFST_OK) return rcb;
+    }
     hipStream_t s = (hipStream_t)stream;
     const size_t L = (size_t)c.max_lanes;
     LpDesc *hd = (LpDesc *)d->h_in;
