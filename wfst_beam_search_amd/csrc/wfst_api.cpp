@@ -628,12 +628,13 @@ static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
     d->ev_used = 0;
     if ((e = launch(d, kKClear, 0, 0, s)) != hipSuccess) return e;
     if ((e = launch(d, kKInit, 0, 0, s)) != hipSuccess) return e;
+    // (the row maxima first: the start closure's tokens carry frame 0's in their bound)
+    if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int k = 1; k <= d->passes; ++k) {
         if ((e = wrap_clear(d, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
         if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
     }
-    if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
         if ((e = wrap_clear(d, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;

@@ -182,7 +182,7 @@ struct LaneTab {
     uint32_t arcs[kMaxLanes];      // slots of the step
     int32_t ph[kMaxLanes];
     int32_t T[kMaxLanes];
-    float f0[kMaxLanes];           // max log-prob of the lane's row (0 on the final step)
+    float f0[kMaxLanes];           // finalize: 1 if the candidate list fits; closure apply: 1 if it does not
     float f1[kMaxLanes];           // cutoff, or the running max
     uint32_t fb[kMaxLanes];        // winners-log base of the sources' compaction
     int32_t par[kMaxLanes];        // parity of the frontier the kernel reads (k_max, k_finalize)
@@ -422,6 +422,7 @@ __device__ void init_lane(const Work &w, int L, int T)
     const StateInfo si = w.sinfo[s];
     int32_t abeg; uint32_t deg; float ub;
     class_of(si, T == 0, 0.0f, &abeg, &deg, &ub);
+    if (T != 0) ub = __builtin_inff();   // (its frame's log-probs are not known here)
     const size_t q = (size_t)L * w.frontier_cap;
     w.tok_state[0][q] = s;
     w.tok_score[0][q] = 0.0f;
@@ -539,7 +540,6 @@ struct LaneView {
     const float *score;
     const float *ubv;
     const void *row;      // log-prob row of the step (null on the final step)
-    float lpm;            // its maximum (0 on the final step)
 };
 
 __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab, int t, const LpDesc &d, int L)
@@ -558,15 +558,14 @@ __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab,
     const long long eoff = (long long)tab.row[L] * d.stride_b + (long long)t * d.stride_t;
     v.row = (v.ph == kPhReal)
         ? (const void *)((const char *)d.base + eoff * (w.lp_dtype == 1 ? 2 : 4)) : nullptr;
-    v.lpm = tab.f0[L];
     return v;
 }
 
 // Loads unit u of lane v.L: lane l of the wavefront resolves slots
 // j0 + r*64 + l against register-held windows of 64 token offsets (start token
 // `cur`, moved forward), then issues every arc load of the unit before using
-// any. Tokens whose bound ub + maxlp <= skip are not
-// expanded (exact: no arc of theirs can end above skip).
+// any. Tokens whose bound ub <= skip are not expanded (exact: ub is at least
+// every candidate through the token, so none of its arcs ends above skip).
 template <typename LPT>
 __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
                                           float skip, UnitData &ud)
@@ -626,7 +625,7 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
     for (int r = 0; r < kR; ++r) {
         ud.arc[r] = (uint32_t)ab[r] + (j[r] - toff[r]);
         ud.tok[r] = tok[r];
-        const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] + v.lpm > skip;
+        const bool go = valid[r] && tok[r] < n && ud.arc[r] < (uint32_t)w.num_arcs && ub[r] > skip;
         if (go) ud.live |= 1u << r;
         // {dest, ilabel, weight} in one 12-byte record
         ArcDLW a = {0, 0u, 0.0f};
@@ -787,12 +786,10 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         const unsigned long long cn = pair_at(c.cnt, p);
         const uint32_t lbk = pair_at(c.lbkey, p);
         const float bprev = pair_at(c.beam, p ^ 1);
-        const float lpmt = t < w.max_frames ? w.lpmax[(size_t)L * w.max_frames + t] : 0.0f;
         const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
         if (ph != kPhNone && (n > w.frontier_cap || arcs > w.strip_cap * (uint32_t)kWave)) ph = kPhNone;
-        float lpm = 0.0f, b = 0.0f;
+        float b = 0.0f;
         uint32_t lb = kOrdNegInf;
-        if (ph == kPhReal) lpm = lpmt;
         if (ph != kPhNone && n > 0u && arcs > 0u) {
             units = (arcs + kUnit - 1) / kUnit;
             b = step_beam(w, c.T, bprev, t, ph, n);
@@ -802,7 +799,6 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
         tab.arcs[L] = arcs;
         tab.ph[L] = ph;
         tab.T[L] = c.T;
-        tab.f0[L] = lpm;
         tab.f1[L] = b;
         tab.fb[L] = lb;
         tab.par[L] = p;
@@ -1121,6 +1117,13 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                         }
 #pragma unroll
                         for (int k = 0; k < kTopArcs; ++k) lbv = fmaxf(lbv, (end + si.top_w[k]) + lpk[k]);
+                        // the token's bound for the next step: its exact best candidate
+                        // when these arcs are all it has, else (score + largest weight)
+                        // + the frame's largest log-prob
+                        ub = deg <= (uint32_t)kTopArcs
+                            ? lbv : ub + w.lpmax[(size_t)L * w.max_frames + (size_t)(t + 1)];
+                    } else if (!next_final) {
+                        ub = __builtin_inff();   // (the next frame is not in this input)
                     }
                 }
             }
@@ -1362,6 +1365,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             tab.n[L] = nc;
             tab.arcs[L] = n0;
             tab.T[L] = c.T;
+            tab.win[L] = c.win;
             tab.f1[L] = c.cutoff;
             tab.f0[L] = (on && !fits) ? 1.0f : 0.0f;
         }
@@ -1426,6 +1430,10 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             class_of(si, next_final, end, &abeg, &deg, &ub);
             eb = si.eps_b;
             ed = (uint32_t)(si.emit_b - si.eps_b);
+            // the bound of the next step's skip test: with the frame's largest
+            // log-prob (unknown past the sequence's window)
+            if (!next_final)
+                ub = t + 1 < tab.win[L] ? ub + w.lpmax[(size_t)L * w.max_frames + (size_t)(t + 1)] : __builtin_inff();
         }
         const unsigned long long ma = __ballot(any);
         if (ma == 0ull) continue;
