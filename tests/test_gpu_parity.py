@@ -324,3 +324,28 @@ def test_buffers_not_on_the_device_are_rejected():
     assert r.meta.shape == (2, 3)
     dec.close()
     dg.release()
+
+
+def test_profiled_decode_matches_and_times_every_step_kernel():
+    """With per-launch timing on (plain launches, an event pair per dispatch) a
+    decode returns the same results; every step launches the two step kernels."""
+    import torch
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    lp2, L2 = np.ascontiguousarray(lp[:3]), L[:3]
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=3, max_frames=lp.shape[1])
+    x = torch.from_numpy(lp2).cuda()
+    r0 = dec.decode(x, L2)
+    dec.profile(True)
+    r1 = dec.decode(x, L2)
+    kt = dec.kernel_times()
+    dec.profile(False)
+    r2 = dec.decode(x, L2)
+    dec.close()
+    dg.release()
+    steps = int(L2.max()) + 1
+    assert kt["max"][1] == steps and kt["finalize"][1] == steps and kt["max"][0] > 0.0
+    for r in (r1, r2):
+        for b in range(3):
+            assert np.array_equal(r.arcs[b], r0.arcs[b]) and np.float32(r.scores[b]) == np.float32(r0.scores[b])
