@@ -35,7 +35,8 @@ def _golden_cases():
     for c in load_golden("edge_cases.json")["cases"]:
         g = graph_from_states(c["graph"])
         out.append(("edge_" + c["name"], g,
-                    np.array(c["lp_rows"], np.float32).reshape(c["frames"], g.vocab), c, 0, c["allow_partial"]))
+                    np.array(c["lp_rows"], np.float32).reshape(c["frames"], g.vocab), c, c.get("eps_iterations", 0),
+                    c["allow_partial"]))
     return out
 
 

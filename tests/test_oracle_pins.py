@@ -89,7 +89,7 @@ def test_golden_edge_cases(case):
     g = graph_from_states(case["graph"])
     lp = np.array(case["lp_rows"], dtype=np.float32).reshape(case["frames"], g.vocab)
     r = _decode(g, lp, case["frames"], case["beam"], case["max_active"], case["min_active"],
-                allow_partial=bool(case["allow_partial"]))
+                allow_partial=bool(case["allow_partial"]), eps=case.get("eps_iterations", 0))
     assert list(r["arcs"]) == case["expect_arcs"]
     assert list(r["words"]) == case["expect_words"]
     exp = f32_value(case["expect_score"])
@@ -495,6 +495,35 @@ def test_lattice_at_infinite_beam_is_every_complete_path():
                 judged += 1
             assert kept <= set(through), seed
     assert judged > 500
+
+
+def test_lattice_keep_at_exact_ties():
+    """Section 3 on output_beam (keep at >=, reading R26), where equality
+    happens: with weights and log-probs on a 1/8 grid every sum is exact, so an
+    arc occurrence of a complete path scoring sc has (fwd(src) + s) + bwd(dst) at
+    least sc, with equality on the best such path. Output beam 0 then keeps
+    exactly the arc occurrences of the best-scoring complete paths (ties
+    included), output beam 0.5 those of paths within 0.5 of the best."""
+    judged = 0
+    for seed in range(1100, 1160):
+        g, lp, T = _tiny(seed, False)
+        if T == 0:
+            continue
+        rng = np.random.default_rng(seed)
+        g.weight = (-rng.integers(0, 9, size=len(g.weight)) / 8.0).astype(np.float32)
+        lp = (-rng.integers(0, 17, size=lp.shape) / 8.0).astype(np.float32)
+        paths = complete_paths(g, lp, T)
+        if not paths:
+            continue
+        best = max(p[0] for p in paths)
+        for ob in (0.0, 0.5):
+            r = _lat(g, lp, T, INF_BEAM, 1 << 20, ob)
+            assert r["score"] == best
+            kept = {(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in r["lattice"] if x[LF["keep"]]}
+            want = {(t, a) for sc, arcs in paths if sc >= best - F32(ob) for t, a in enumerate(arcs)}
+            assert kept == want, (seed, ob)
+            judged += len(want)
+    assert judged > 200
 
 
 # ------------------------------------------------------------ blank-skip slicing
