@@ -6,8 +6,10 @@ least one of them must fail. The unmutated copy, built the same way, passes
 them all. The committed oracle is never modified."""
 
 import ctypes
+import inspect
 import os
 import subprocess
+import textwrap
 
 import pytest
 
@@ -55,6 +57,22 @@ MUTANTS = {
     "lattice_keep_strict": [("r[6] = thr >= thresh ? 1 : 0;", "r[6] = thr > thresh ? 1 : 0;", 1)],
     "lattice_backward_drops_arc": [("const float v = sa + bd;", "const float v = bd;", 1)],
 }
+
+
+# the blank-skip slicing (section 3, WeNet-style; reading R27) is numpy: its
+# mutants edit the function's own source
+PY_MUTANTS = {
+    "blank_drop_at_threshold": ("if not (np.float32(lp[b, t, blank_id]) > lthr)",
+                                "if not (np.float32(lp[b, t, blank_id]) >= lthr)"),
+    "blank_threshold_binary64": ("lthr = np.float32(np.log(np.float64(np.float32(threshold))))",
+                                 "lthr = np.float32(np.log(np.float64(threshold)))"),
+}
+
+
+def _blank_pin_calls():
+    return [("blank:" + c["name"], lambda c=c: pins.test_golden_blank_skip(c))
+            for c in load_golden("blank_skip.json")["cases"]] + \
+           [("blank_threshold_one", pins.test_blank_skip_threshold_one_keeps_everything)]
 
 
 def _pin_calls():
@@ -127,3 +145,32 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
 def test_planted_mistake_is_caught(name, tmp_path):
     failed = _failing_pins(_build(str(tmp_path), MUTANTS[name]))
     assert failed, f"mutant {name} passes every pin"
+
+
+def _py_mutant(old, new):
+    src = textwrap.dedent(inspect.getsource(oracle.blank_skip))
+    assert src.count(old) == 1, old
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), "<blank_skip mutant>", "exec"), ns)
+    return ns["blank_skip"]
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_planted_blank_skip_mistake_is_caught(name):
+    saved = oracle.blank_skip
+    oracle.blank_skip = _py_mutant(*PY_MUTANTS[name])
+    failed = []
+    try:
+        for pin, call in _blank_pin_calls():
+            try:
+                call()
+            except AssertionError:
+                failed.append(pin)
+    finally:
+        oracle.blank_skip = saved
+    assert failed, f"mutant {name} passes every pin"
+
+
+def test_unmutated_blank_skip_passes_its_pins():
+    for _, call in _blank_pin_calls():
+        call()
