@@ -175,7 +175,10 @@ struct Work {
     uint32_t *tok_off[2];     // exclusive arc offset of the token in the step's slot space
     uint32_t *strip_tok[2];   // [L][strip_cap] token holding the first slot of each 64-slot strip
     int32_t *tok_abeg[2];     // first arc of the step's class
-    float *tok_ub[2];         // score + largest weight of the step's class
+    float *tok_ub[2];         // bound on every candidate through the token in the step it feeds:
+                              //   its exact best candidate (states with at most kTopArcs emitting
+                              //   arcs), else (score + largest weight) + the frame's largest log-prob;
+                              //   score + largest final weight before a final step; +inf if unknown
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
     unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed)
     Claim *claims;            // [L][CC]

@@ -211,7 +211,9 @@ __device__ __forceinline__ int find_lane(const uint32_t *base, int nl, uint32_t 
     return lo;
 }
 
-// Next-step class of a token at state s: [abeg, abeg + deg) and its upper bound.
+// Next-step class of a token at state s: [abeg, abeg + deg) and score + the
+// class's largest weight (the final class's bound; emitting classes add the
+// frame's largest log-prob, or use the exact best candidate, where known).
 __device__ __forceinline__ void class_of(const StateInfo &si, bool final_step, float score,
                                          int32_t *abeg, uint32_t *deg, float *ub)
 {
