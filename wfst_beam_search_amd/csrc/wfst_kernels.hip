@@ -10,8 +10,9 @@
 //    solution);
 //  * the slot pass (k_max) takes the exact per-lane maximum M with the
 //    per-token upper-bound skip (section 5.3: (s+w)+lp <= (s+maxw)+maxlp holds
-//    in IEEE fp32), its running maximum seeded with a lower bound the previous
-//    compaction posted; in the same walk it lists every candidate with
+//    in IEEE fp32; a token whose state has at most kTopArcs emitting arcs
+//    carries its exact best candidate instead), its running maximum seeded
+//    with a lower bound the previous compaction posted; in the same walk it lists every candidate with
 //    end > running max - b, a superset of the admitted ones (end > M - b), and
 //    recombines them per destination in a direct-mapped per-lane table
 //    best[state] with one posted u64 atomicMax of (ordered score | ~arc), so
@@ -23,7 +24,9 @@
 //    together (tokens in the low half, arcs in the high half), which is the
 //    exclusive degree scan of the next step, done as the frontier is built;
 //    the winners-log entry {source entry, arc} is written;
-//  * epsilon closure passes (expand / resolve / apply) on TLG graphs.
+//  * epsilon closure passes (expand, then decide-and-apply) on TLG graphs;
+//  * around the search: streams, the lattice and its backward prune,
+//    winners-log compaction, blank-skip slicing.
 // All fp32 arithmetic is single operations in the order the page fixes; the
 // file is compiled with -ffp-contract=off.
 #include <hip/hip_ext.h>
@@ -718,7 +721,7 @@ __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t
 
 // Units [s, s_end) of the flattened slot space, in one pass: the exact maximum
 // (running max seeded with the lower bound the compaction posted, tokens whose
-// bound ub + maxlp <= running max - b skipped: exact for both results) and the
+// bound ub <= running max - b skipped: exact for both results) and the
 // superset admission against running max - b.
 template <typename LPT>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
