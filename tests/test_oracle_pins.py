@@ -471,8 +471,8 @@ def test_lattice_at_infinite_beam_is_every_complete_path():
     """At infinite search beam every candidate is admitted; with a wide output beam
     the kept (frame, arc) pairs are exactly the arc occurrences of complete paths,
     and with a narrow one those on a path within output_beam of the best (pairs
-    within 1e-4 of the threshold are not judged)."""
-    judged = 0
+    within 1e-4 of the threshold are not checked)."""
+    checked = 0
     for seed in range(1000, 1060):
         g, lp, T = _tiny(seed, False)
         paths = complete_paths(g, lp, T)
@@ -492,9 +492,9 @@ def test_lattice_at_infinite_beam_is_every_complete_path():
                 if abs(margin) < 1e-4:
                     continue
                 assert (key in kept) == (margin > 0), (seed, ob, key)
-                judged += 1
+                checked += 1
             assert kept <= set(through), seed
-    assert judged > 500
+    assert checked > 500
 
 
 def test_lattice_keep_at_exact_ties():
@@ -504,7 +504,7 @@ def test_lattice_keep_at_exact_ties():
     least sc, with equality on the best such path. Output beam 0 then keeps
     exactly the arc occurrences of the best-scoring complete paths (ties
     included), output beam 0.5 those of paths within 0.5 of the best."""
-    judged = 0
+    checked = 0
     for seed in range(1100, 1160):
         g, lp, T = _tiny(seed, False)
         if T == 0:
@@ -522,8 +522,8 @@ def test_lattice_keep_at_exact_ties():
             kept = {(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in r["lattice"] if x[LF["keep"]]}
             want = {(t, a) for sc, arcs in paths if sc >= best - F32(ob) for t, a in enumerate(arcs)}
             assert kept == want, (seed, ob)
-            judged += len(want)
-    assert judged > 200
+            checked += len(want)
+    assert checked > 200
 
 
 # ------------------------------------------------------------ blank-skip slicing
