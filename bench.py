@@ -201,7 +201,11 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
         for live, xc, lens in chunks:
             dec.advance_chunk([ch[b] for b in live], xc, lens, want_partial=args.stream_partial)
         tc = time.perf_counter()
-        res = [dec.finalize_stream(c) for c in ch]
+        if args.stream_end_together:
+            r = dec.finalize_streams(ch)
+            res = [r.meta[j:j + 1] for j in range(len(ch))]
+        else:
+            res = [dec.finalize_stream(c).meta for c in ch]
         for c in ch:
             dec.release_stream(c)
         td = time.perf_counter()
@@ -220,7 +224,7 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     frames = int(np.asarray(lengths).sum())
-    ok = all(int(r.meta[0, 0]) == 1 and int(r.meta[0, 2]) == 0 for r in res)
+    ok = all(int(m[0, 0]) == 1 and int(m[0, 2]) == 0 for m in res)
     ktimes = {}
     if not args.no_profile_pass:
         dec.profile(True)
@@ -244,7 +248,8 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
         "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name} streamed in chunks of {N} frames"
-                               f"{' with partial hypotheses after each chunk' if args.stream_partial else ''}: "
+                               f"{' with partial hypotheses after each chunk' if args.stream_partial else ''}"
+                               f"{', all ended by one call' if args.stream_end_together else ''}: "
                                f"{graph.num_states - 1} states, {graph.num_arcs} arcs, log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "chunk": N, "chunk_calls_per_step": len(chunks),
@@ -344,6 +349,8 @@ def main():
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
+    ap.add_argument("--stream-end-together", action="store_true",
+                    help="with --stream-chunk: end every stream of the batch with one wfst_finalize_streams call")
     ap.add_argument("--stream-partial", action="store_true",
                     help="with --stream-chunk: ask for every lane's partial hypothesis after each chunk")
     ap.add_argument("--blank-skip", type=float, default=None, metavar="THRESHOLD",

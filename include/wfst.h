@@ -321,6 +321,21 @@ int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_
                          int32_t words_cap, int32_t *out_word_len, int32_t *out_arcs, int32_t arcs_cap,
                          int32_t *out_arc_len, float *out_score, int32_t *out_meta);
 
+/*
+ * End several streams in one call: one device sequence serves them all (the
+ * final step of every listed lane at once, then their paths), which a serving
+ * loop ending many utterances together pays once instead of per stream.
+ * channels[j], j < C, are distinct open channels; row j of the outputs receives
+ * channels[j]'s result exactly as wfst_finalize_stream writes it (words and
+ * arcs rows of words_cap / arcs_cap entries).
+ * Errors: WFST_EINVAL (C outside [1, max_lanes], a channel not open or
+ * repeated, null pointers), WFST_EDEVICE.
+ */
+int wfst_finalize_streams(wfst_decoder_t d, const int32_t *channels, int32_t C, void *stream,
+                          int32_t *out_words, int32_t words_cap, int32_t *out_word_lens,
+                          int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens, float *out_scores,
+                          int32_t *out_meta);
+
 /* Give a stream's lane back (no device work). Errors: WFST_EINVAL (not open). */
 int wfst_release_stream(wfst_decoder_t d, int32_t channel);
 

@@ -51,7 +51,8 @@ def _check_records(tag, got, ost, first, count):
 
 
 def stream_run(g, lp, lengths, chunk, beam, max_active, min_active=0, allow_partial=False, eps=0,
-               partial_every=1, dgraph=None, max_lanes=None, open_at=None, use_graphs=False, **caps):
+               partial_every=1, dgraph=None, max_lanes=None, open_at=None, use_graphs=False, batch_finalize=False,
+               **caps):
     """Streams each lane of ``lp`` [B, T, V] in chunks of ``chunk`` frames (lane b
     opened before chunk open_at[b]); returns (channels, partials, records, finals),
     partials[b] = [(frames so far, words, arcs, score, meta)], records[b] = [(first
@@ -98,7 +99,18 @@ def stream_run(g, lp, lengths, chunk, beam, max_active, min_active=0, allow_part
             if want:
                 partials[b].append((done[b], res.words[j], res.arcs[j], res.scores[j], res.meta[j].copy()))
     finals = []
-    for b in range(B):
+    if batch_finalize:
+        # every stream ended by one call, the channels listed in a scrambled order
+        for b in range(B):
+            if chans[b] < 0:
+                chans[b] = dec.create_stream()
+        order = list(np.random.default_rng(B).permutation(B))
+        r = dec.finalize_streams([chans[b] for b in order])
+        row = {b: j for j, b in enumerate(order)}
+        for b in range(B):
+            j = row[b]
+            finals.append((r.words[j], r.arcs[j], r.scores[j], r.meta[j].copy(), dec.step_stats(chans[b])))
+    for b in range(B if not batch_finalize else 0):
         if chans[b] < 0:
             chans[b] = dec.create_stream()
         r = dec.finalize_stream(chans[b])
@@ -264,3 +276,13 @@ def test_stream_arena_overflow_is_reported():
     dec.release_stream(ch)
     dec.close()
     dg.release()
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_streams_ended_together(eps):
+    """wfst_finalize_streams: every stream of a batch ended by one call, in any
+    channel order, gives each the oracle's online result and final records."""
+    for seed in range(12):
+        g, lp, L, chunk, beam, ma, mi, ap, P = _random_stream_case(seed + (800 if eps else 0), eps)
+        _say("streams ended together", eps, seed, lp.shape, chunk)
+        check_stream(g, lp, L, chunk, beam, ma, mi, ap, P, batch_finalize=True, use_graphs=bool(seed % 2))

@@ -28,7 +28,7 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
                     "wfst_decoder_stats", "wfst_decoder_mem_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
-                    "wfst_finalize_stream", "wfst_release_stream", "wfst_lattice_records",
+                    "wfst_finalize_stream", "wfst_finalize_streams", "wfst_release_stream", "wfst_lattice_records",
                     "wfst_blank_skip")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
            "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
@@ -114,6 +114,7 @@ def load_library():
         lib.wfst_advance_chunk.argtypes = [vp, vp, i32, vp, i32, i32, vp, vp, i32, vp, i32, vp, vp, i32,
                                            vp, vp, vp]
         lib.wfst_finalize_stream.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+        lib.wfst_finalize_streams.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_release_stream.argtypes = [vp, i32]
         lib.wfst_lattice_records.argtypes = [vp, i32, vp, ctypes.c_int64, vp]
         lib.wfst_blank_skip.argtypes = [vp, vp, i32, i32, i32, vp, i32, ctypes.c_float, vp, vp, vp]
@@ -314,6 +315,19 @@ class Decoder:
         _check(_lib.wfst_finalize_stream(self.handle, int(channel), ctypes.c_void_p(int(s)), _ptr(out_words),
                                          words_cap, _ptr(wl), _ptr(out_arcs), arcs_cap, _ptr(al), _ptr(sc),
                                          _ptr(meta)))
+        return self._result(out, words_cap, arcs_cap)
+
+    def finalize_streams(self, channels, stream=None, words_cap: int = 1 << 16,
+                         arcs_cap: int = 1 << 16) -> DecodeResult:
+        """End several streams in one call (row j of the result for channels[j])."""
+        import torch
+        chans = np.ascontiguousarray(np.asarray(channels, dtype=np.int32).reshape(-1))
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        out = self._outputs(chans.shape[0], words_cap, arcs_cap)
+        out_words, wl, out_arcs, al, sc, meta = out
+        _check(_lib.wfst_finalize_streams(self.handle, _ptr(chans), chans.shape[0], ctypes.c_void_p(int(s)),
+                                          _ptr(out_words), words_cap, _ptr(wl), _ptr(out_arcs), arcs_cap, _ptr(al),
+                                          _ptr(sc), _ptr(meta)))
         return self._result(out, words_cap, arcs_cap)
 
     def release_stream(self, channel: int):

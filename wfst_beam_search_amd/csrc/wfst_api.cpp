@@ -1036,26 +1036,59 @@ extern "C" int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int
     return WFST_OK;
 }
 
+// Ends channels[0 .. C) in one finish sequence and copies each result to its row.
+static int finalize_lanes(wfst_decoder_s *d, const int32_t *channels, int32_t C, void *stream, int32_t *out_words,
+                          int32_t words_cap, int32_t *out_word_lens, int32_t *out_arcs, int32_t arcs_cap,
+                          int32_t *out_arc_lens, float *out_scores, int32_t *out_meta)
+{
+    if (!out_word_lens || !out_arc_lens || !out_scores || !out_meta || words_cap < 0 || arcs_cap < 0 ||
+        (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs))
+        return fail(WFST_EINVAL, "an output pointer is null");
+    const int nl = d->cfg.max_lanes;
+    if (!channels || C < 1 || C > nl) return fail(WFST_EINVAL, "C must lie in [1, max_lanes] with channels given");
+    std::lock_guard<std::mutex> lock(d->mu);
+    std::vector<uint8_t> seen((size_t)nl, 0);
+    for (int32_t j = 0; j < C; ++j) {
+        const int32_t ch = channels[j];
+        if (ch < 0 || ch >= nl || !d->chan_open[(size_t)ch]) return fail(WFST_EINVAL, "channel is not an open stream");
+        if (seen[(size_t)ch]) return fail(WFST_EINVAL, "a channel appears twice");
+        seen[(size_t)ch] = 1;
+    }
+    HIP_TRY(hipSetDevice(d->g->device));
+    plan_clear(d);
+    std::vector<int> lanes;
+    for (int32_t j = 0; j < C; ++j) {
+        d->h_plan[channels[j] * kPlanFields + kPlanCmd] = kCmdFinish;
+        lanes.push_back(channels[j]);
+    }
+    int rc = run_stream(d, kSeqFinish, 1, (hipStream_t)stream, lanes);
+    if (rc != WFST_OK) return rc;
+    d->last_len.assign((size_t)nl, -1);
+    for (int32_t j = 0; j < C; ++j) {
+        d->last_len[(size_t)channels[j]] = 0;
+        copy_result(d, channels[j], j, out_words, words_cap, out_word_lens, out_arcs, arcs_cap, out_arc_lens,
+                    out_scores, out_meta);
+    }
+    return WFST_OK;
+}
+
 extern "C" int wfst_finalize_stream(wfst_decoder_t d, int32_t channel, void *stream, int32_t *out_words,
                                     int32_t words_cap, int32_t *out_word_len, int32_t *out_arcs, int32_t arcs_cap,
                                     int32_t *out_arc_len, float *out_score, int32_t *out_meta)
 {
     if (!d) return fail(WFST_EINVAL, "decoder is null");
-    if (!out_word_len || !out_arc_len || !out_score || !out_meta || words_cap < 0 || arcs_cap < 0 ||
-        (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs))
-        return fail(WFST_EINVAL, "an output pointer is null");
-    std::lock_guard<std::mutex> lock(d->mu);
-    if (channel < 0 || channel >= d->cfg.max_lanes || !d->chan_open[(size_t)channel])
-        return fail(WFST_EINVAL, "channel is not an open stream");
-    HIP_TRY(hipSetDevice(d->g->device));
-    plan_clear(d);
-    d->h_plan[channel * kPlanFields + kPlanCmd] = kCmdFinish;
-    int rc = run_stream(d, kSeqFinish, 1, (hipStream_t)stream, {channel});
-    if (rc != WFST_OK) return rc;
-    d->last_len.assign((size_t)d->cfg.max_lanes, -1);
-    d->last_len[(size_t)channel] = 0;
-    copy_result(d, channel, 0, out_words, words_cap, out_word_len, out_arcs, arcs_cap, out_arc_len, out_score, out_meta);
-    return WFST_OK;
+    return finalize_lanes(d, &channel, 1, stream, out_words, words_cap, out_word_len, out_arcs, arcs_cap,
+                          out_arc_len, out_score, out_meta);
+}
+
+extern "C" int wfst_finalize_streams(wfst_decoder_t d, const int32_t *channels, int32_t C, void *stream,
+                                     int32_t *out_words, int32_t words_cap, int32_t *out_word_lens,
+                                     int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens, float *out_scores,
+                                     int32_t *out_meta)
+{
+    if (!d) return fail(WFST_EINVAL, "decoder is null");
+    return finalize_lanes(d, channels, C, stream, out_words, words_cap, out_word_lens, out_arcs, arcs_cap,
+                          out_arc_lens, out_scores, out_meta);
 }
 
 extern "C" int wfst_release_stream(wfst_decoder_t d, int32_t channel)
