@@ -196,12 +196,12 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
 
     def one():
         ta = time.perf_counter()
-        ch = [dec.create_stream() for _ in range(B)]
+        ch = dec.create_streams(B) if args.stream_together else [dec.create_stream() for _ in range(B)]
         tb = time.perf_counter()
         for live, xc, lens in chunks:
             dec.advance_chunk([ch[b] for b in live], xc, lens, want_partial=args.stream_partial)
         tc = time.perf_counter()
-        if args.stream_end_together:
+        if args.stream_together:
             r = dec.finalize_streams(ch)
             res = [r.meta[j:j + 1] for j in range(len(ch))]
         else:
@@ -249,7 +249,7 @@ def stream_bench(args, wl, graph, lp, lengths, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name} streamed in chunks of {N} frames"
                                f"{' with partial hypotheses after each chunk' if args.stream_partial else ''}"
-                               f"{', all ended by one call' if args.stream_end_together else ''}: "
+                               f"{', all opened by one call and ended by one' if args.stream_together else ''}: "
                                f"{graph.num_states - 1} states, {graph.num_arcs} arcs, log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "chunk": N, "chunk_calls_per_step": len(chunks),
@@ -349,8 +349,9 @@ def main():
     ap.add_argument("--stream-chunk", type=int, default=0, metavar="N",
                     help="stream every lane in chunks of N frames (create / advance / finalize / "
                          "release per timed step) instead of one batch decode")
-    ap.add_argument("--stream-end-together", action="store_true",
-                    help="with --stream-chunk: end every stream of the batch with one wfst_finalize_streams call")
+    ap.add_argument("--stream-together", action="store_true",
+                    help="with --stream-chunk: open every stream of the batch with one wfst_create_streams call "
+                         "and end them with one wfst_finalize_streams call")
     ap.add_argument("--stream-partial", action="store_true",
                     help="with --stream-chunk: ask for every lane's partial hypothesis after each chunk")
     ap.add_argument("--blank-skip", type=float, default=None, metavar="THRESHOLD",

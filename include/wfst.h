@@ -285,6 +285,14 @@ int wfst_decoder_destroy(wfst_decoder_t d);
 int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel);
 
 /*
+ * Open up to n streams in one call (one device sequence for all of them):
+ * channels[0 .. *opened) receive their lanes, the lowest free lanes first;
+ * *opened < n when fewer lanes are free (not an error). channels holds n
+ * entries. Errors: WFST_EINVAL (null, n < 0, lattice mode), WFST_EDEVICE.
+ */
+int wfst_create_streams(wfst_decoder_t d, int32_t n, void *stream, int32_t *channels, int32_t *opened);
+
+/*
  * Advance C open streams by one chunk each.
  *  channels      [C] host: distinct open channels, 1 <= C <= max_lanes.
  *  log_prob      device pointer to a packed [C, T, V] tensor of lp_dtype: row j

@@ -52,7 +52,7 @@ def _check_records(tag, got, ost, first, count):
 
 def stream_run(g, lp, lengths, chunk, beam, max_active, min_active=0, allow_partial=False, eps=0,
                partial_every=1, dgraph=None, max_lanes=None, open_at=None, use_graphs=False, batch_finalize=False,
-               **caps):
+               batch_open=False, **caps):
     """Streams each lane of ``lp`` [B, T, V] in chunks of ``chunk`` frames (lane b
     opened before chunk open_at[b]); returns (channels, partials, records, finals),
     partials[b] = [(frames so far, words, arcs, score, meta)], records[b] = [(first
@@ -76,6 +76,12 @@ def stream_run(g, lp, lengths, chunk, beam, max_active, min_active=0, allow_part
     records = [[] for _ in range(B)]
     n_chunks = max(1, -(-max(int(x) for x in lengths) // max(chunk, 1))) + max(open_at)
     for ci in range(n_chunks + 1):
+        if batch_open and ci == 0:
+            first = [b for b in range(B) if open_at[b] == 0]
+            got = dec.create_streams(len(first))
+            assert len(got) == len(first) and len(set(got)) == len(got)
+            for b, ch in zip(first, got):
+                chans[b] = ch
         for b in range(B):
             if open_at[b] == ci and chans[b] < 0:
                 chans[b] = dec.create_stream()
@@ -285,4 +291,23 @@ def test_streams_ended_together(eps):
     for seed in range(12):
         g, lp, L, chunk, beam, ma, mi, ap, P = _random_stream_case(seed + (800 if eps else 0), eps)
         _say("streams ended together", eps, seed, lp.shape, chunk)
-        check_stream(g, lp, L, chunk, beam, ma, mi, ap, P, batch_finalize=True, use_graphs=bool(seed % 2))
+        check_stream(g, lp, L, chunk, beam, ma, mi, ap, P, batch_finalize=True, batch_open=True,
+                     use_graphs=bool(seed % 2))
+
+
+def test_create_streams_grants_the_free_lanes():
+    """wfst_create_streams opens at most the free lanes, lowest first; a full
+    decoder grants none (no error)."""
+    g = synth.random_graph(61, n=8, deg=(1, 3), vocab=4)
+    dg = wb.Graph(g)
+    dec = wb.Decoder(dg, 6.0, 50, max_lanes=4, max_frames=4)
+    a = dec.create_stream()
+    got = dec.create_streams(6)
+    assert a == 0 and got == [1, 2, 3]
+    assert dec.create_streams(2) == [] and dec.create_stream() == -1
+    dec.release_stream(2)
+    assert dec.create_streams(3) == [2]
+    for ch in range(4):
+        dec.release_stream(ch)
+    dec.close()
+    dg.release()

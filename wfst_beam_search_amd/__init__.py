@@ -28,7 +28,7 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
                     "wfst_decoder_create", "wfst_decode", "wfst_decoder_destroy",
                     "wfst_decoder_stats", "wfst_decoder_mem_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
-                    "wfst_finalize_stream", "wfst_finalize_streams", "wfst_release_stream", "wfst_lattice_records",
+                    "wfst_finalize_stream", "wfst_finalize_streams", "wfst_create_streams", "wfst_release_stream", "wfst_lattice_records",
                     "wfst_blank_skip")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
            "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
@@ -115,6 +115,7 @@ def load_library():
                                            vp, vp, vp]
         lib.wfst_finalize_stream.argtypes = [vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
         lib.wfst_finalize_streams.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+        lib.wfst_create_streams.argtypes = [vp, i32, vp, vp, vp]
         lib.wfst_release_stream.argtypes = [vp, i32]
         lib.wfst_lattice_records.argtypes = [vp, i32, vp, ctypes.c_int64, vp]
         lib.wfst_blank_skip.argtypes = [vp, vp, i32, i32, i32, vp, i32, ctypes.c_float, vp, vp, vp]
@@ -284,6 +285,16 @@ class Decoder:
         s = torch.cuda.current_stream().cuda_stream if stream is None else stream
         _check(_lib.wfst_create_stream(self.handle, ctypes.c_void_p(int(s)), ctypes.byref(ch)))
         return int(ch.value)
+
+    def create_streams(self, n: int, stream=None) -> list:
+        """Open up to n streams in one call; returns their channels (fewer when
+        fewer lanes are free)."""
+        import torch
+        out = np.zeros(max(int(n), 1), dtype=np.int32)
+        got = ctypes.c_int32(0)
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        _check(_lib.wfst_create_streams(self.handle, int(n), ctypes.c_void_p(int(s)), _ptr(out), ctypes.byref(got)))
+        return [int(x) for x in out[:got.value]]
 
     def advance_chunk(self, channels, log_prob, lengths, want_partial: bool = False, stream=None,
                       words_cap: int = 4096, arcs_cap: int = 4096):

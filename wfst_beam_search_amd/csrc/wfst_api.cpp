@@ -945,16 +945,17 @@ static void plan_clear(wfst_decoder_s *d)
     std::memset(d->h_plan, 0, 4 * (size_t)d->cfg.max_lanes * kPlanFields);   // kCmdPark
 }
 
-extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel)
+// Opens up to n streams in one open sequence: channels[0 .. *opened) receive
+// the lanes, lowest free lanes first.
+static int open_lanes(wfst_decoder_s *d, int32_t n, void *stream, int32_t *channels, int32_t *opened)
 {
-    if (!d || !channel) return fail(WFST_EINVAL, "decoder or channel is null");
-    *channel = -1;
+    *opened = 0;
     if (d->w.lattice) return fail(WFST_EINVAL, "a lattice-mode decoder does not stream");
     std::lock_guard<std::mutex> lock(d->mu);
-    int lane = -1;
-    for (int L = 0; L < d->cfg.max_lanes; ++L)
-        if (!d->chan_open[(size_t)L]) { lane = L; break; }
-    if (lane < 0) return WFST_OK;   // every lane holds a stream
+    std::vector<int> lanes;
+    for (int L = 0; L < d->cfg.max_lanes && (int32_t)lanes.size() < n; ++L)
+        if (!d->chan_open[(size_t)L]) lanes.push_back(L);
+    if (lanes.empty()) return WFST_OK;   // every lane holds a stream
     HIP_TRY(hipSetDevice(d->g->device));
     // a stream cannot be decoded again: its lane's whole region is committed
     // (streams wait for the device before a commit, see grow_log)
@@ -964,15 +965,33 @@ extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *chann
         if (rc0 != WFST_OK) return rc0;
     }
     plan_clear(d);
-    d->h_plan[lane * kPlanFields + kPlanCmd] = kCmdOpen;
+    for (int L : lanes) d->h_plan[L * kPlanFields + kPlanCmd] = kCmdOpen;
     int rc = run_stream(d, kSeqOpen, 0, (hipStream_t)stream, {});
     if (rc != WFST_OK) return rc;
     d->last_len.assign((size_t)d->cfg.max_lanes, -1);
-    d->last_len[(size_t)lane] = 0;
-    d->chan_open[(size_t)lane] = 1;
-    d->open_streams += 1;
-    *channel = lane;
+    for (int L : lanes) {
+        d->last_len[(size_t)L] = 0;
+        d->chan_open[(size_t)L] = 1;
+        channels[(*opened)++] = L;
+    }
+    d->open_streams += (int)lanes.size();
     return WFST_OK;
+}
+
+extern "C" int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel)
+{
+    if (!d || !channel) return fail(WFST_EINVAL, "decoder or channel is null");
+    *channel = -1;
+    int32_t opened = 0;
+    return open_lanes(d, 1, stream, channel, &opened);
+}
+
+extern "C" int wfst_create_streams(wfst_decoder_t d, int32_t n, void *stream, int32_t *channels, int32_t *opened)
+{
+    if (!d || !channels || !opened || n < 0) return fail(WFST_EINVAL, "bad arguments");
+    *opened = 0;
+    if (n == 0) return WFST_OK;
+    return open_lanes(d, n, stream, channels, opened);
 }
 
 extern "C" int wfst_advance_chunk(wfst_decoder_t d, const int32_t *channels, int32_t C, const void *log_prob,
