@@ -305,6 +305,9 @@ def test_create_streams_grants_the_free_lanes():
     got = dec.create_streams(6)
     assert a == 0 and got == [1, 2, 3]
     assert dec.create_streams(2) == [] and dec.create_stream() == -1
+    assert dec.create_streams(0) == []
+    with pytest.raises(wb.WfstError):
+        dec.create_streams(-1)
     dec.release_stream(2)
     assert dec.create_streams(3) == [2]
     for ch in range(4):
