@@ -280,7 +280,7 @@ int wfst_decoder_destroy(wfst_decoder_t d);
 /*
  * Open a stream: *channel = the lane it holds, or -1 when every lane holds one
  * (not an error). Runs the start frontier's epsilon closure for that lane only.
- * Errors: WFST_EINVAL (null), WFST_EDEVICE.
+ * Errors: WFST_EINVAL (null, lattice mode), WFST_EDEVICE.
  */
 int wfst_create_stream(wfst_decoder_t d, void *stream, int32_t *channel);
 
