@@ -115,13 +115,18 @@ typedef struct wfst_graph_desc {
  *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
  *  slot_cap        candidate arcs (slots) per lane per step (0: 512 * max_active,
  *                  at least 2^16); at most 2^31.
- *  plain_keys      0: on graphs with at most 2^25 arcs the recombination table's
- *                  keys carry the round's epoch in the bits the arc ids leave
- *                  free, so entries are never cleared one by one (the table is
- *                  wiped at the start of a decode and whenever the epoch
- *                  counter wraps: every 2^(32 - ceil(log2 num_arcs)) - 1
- *                  rounds, at least 127); 1: plain keys, each entry cleared by
- *                  its owner (always the case on larger graphs). Same results.
+ *  plain_keys      0: the recombination table's keys carry the round's epoch
+ *                  in the bits their tie part leaves free, so entries are never
+ *                  cleared one by one. The tie part is the arc's rank among its
+ *                  destination's incoming arcs (ordered as the arc ids are)
+ *                  when the graph upload could store the ranks (state id bits +
+ *                  rank bits <= 31), else the arc id (graphs of at most 2^25
+ *                  arcs). Rounds are numbered on across decodes and stream
+ *                  calls, and the table is wiped before the first round past
+ *                  each multiple of the epoch period (epoch_period).
+ *                  2: the same with arc id ties. 1: plain keys, each entry
+ *                  cleared by its owner (also what 0 and 2 fall back to when
+ *                  the tie part needs more than 25 bits). Same results.
  *  path_cap        arcs of a result path kept per lane (0: (max_frames + 2) *
  *                  (1 + eps passes)); in [0, 2^26]. A longer path keeps its
  *                  newest path_cap arcs (its words are those arcs' words) and
@@ -166,6 +171,9 @@ typedef struct wfst_graph_desc {
  *                  on the same inputs, so results are those of a fully committed
  *                  region; wfst_decoder_stats reports the re-runs. Creating a
  *                  stream commits the whole range (a stream cannot run again).
+ *  epoch_period    recombination rounds between table wipes with epoch keys
+ *                  (0: derive: 2^(32 - tie bits) - 1, at most 65535); n in
+ *                  [2, that value]: wipe more often (same results).
  */
 typedef struct wfst_decoder_config {
     float beam;
@@ -189,6 +197,7 @@ typedef struct wfst_decoder_config {
     int64_t lattice_cap;
     int32_t gc_interval;
     int64_t arena_commit;
+    int32_t epoch_period;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays

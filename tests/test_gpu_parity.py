@@ -40,8 +40,11 @@ def _golden_cases():
     return out
 
 
+# table keys: ties by in-rank (default on these graphs), by arc id (plain_keys
+# 2), plain keys (1); epoch wraps forced every few rounds (epoch_period)
 MODES = {"graph": dict(use_graphs=True), "eager": dict(use_graphs=False),
-         "plain": dict(use_graphs=True, plain_keys=True)}
+         "plain": dict(use_graphs=True, plain_keys=1), "arcid": dict(use_graphs=True, plain_keys=2),
+         "wrap": dict(use_graphs=True, epoch_period=3), "wrap_eager": dict(use_graphs=False, epoch_period=2)}
 
 
 @pytest.mark.parametrize("name,g,lp,case,eps,ap", _golden_cases(), ids=lambda x: x if isinstance(x, str) else "")
@@ -91,7 +94,7 @@ def test_random_small_graphs(eps):
     for seed in range(150):
         g, lp, L, beam, ma, mi, ap, P = _random_case(seed + (1000 if eps else 0), eps)
         _say("random", eps, seed, lp.shape, beam, ma, mi, ap, P)
-        mode = ("graph", "eager", "plain")[seed % 3]
+        mode = ("graph", "eager", "plain", "arcid", "wrap", "wrap_eager")[seed % 6]
         r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, **MODES[mode])
         o = oracle_lanes(g, lp, L, beam, ma, mi, ap, P)
         compare_batch(r, steps, o)
@@ -145,7 +148,8 @@ def test_workload_parity(cid, workload_graphs):
     dg = wb.Graph(g)
     runs = {}
     try:
-        for mode in ("graph", "eager") + (("plain",) if cid in (2, 4) else ()):
+        extra = {2: ("plain", "wrap"), 3: ("arcid",), 4: ("plain", "wrap")}.get(cid, ())
+        for mode in ("graph", "eager") + extra:
             runs[mode] = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
                                     dgraph=dg, **MODES[mode])
             _say("  gpu", mode, "done; stats", runs[mode][2])
@@ -169,15 +173,21 @@ def test_graph_replay_equals_eager_and_is_idempotent():
     dg = wb.Graph(g)
     dec_g = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames, use_graphs=True)
     dec_e = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames, use_graphs=False)
+    # rounds number on across decodes; with a period of 500 rounds they pass a
+    # wrap every second decode (then the decode starts at the next multiple
+    # with the table wiped)
+    dec_p = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=wl.batch, max_frames=wl.frames, use_graphs=True,
+                       epoch_period=500)
     x = torch.from_numpy(lp).cuda()
     runs = [dec_g.decode(x, L), dec_g.decode(x, L), dec_e.decode(x, L), dec_g.decode(x, L)]
+    runs += [dec_p.decode(x, L) for _ in range(4)]
     for rr in runs[1:]:
         for b in range(wl.batch):
             assert np.array_equal(rr.arcs[b], runs[0].arcs[b])
             assert np.array_equal(rr.words[b], runs[0].words[b])
         assert np.array_equal(rr.scores.view(np.uint32), runs[0].scores.view(np.uint32))
         assert np.array_equal(rr.meta, runs[0].meta)
-    dec_g.close(); dec_e.close(); dg.release()
+    dec_g.close(); dec_e.close(); dec_p.close(); dg.release()
 
 
 def test_lane_result_independent_of_batchmates():
@@ -221,6 +231,12 @@ def test_decode_argument_errors():
     dec.close(); dg.release()
     with pytest.raises(wb.WfstError):
         wb.Decoder(wb.Graph(g), -1.0, 10)
+    dg = wb.Graph(g)
+    for bad in (dict(plain_keys=3), dict(epoch_period=1), dict(epoch_period=-1), dict(epoch_period=65536)):
+        with pytest.raises(wb.WfstError):
+            wb.Decoder(dg, 10.0, 100, max_lanes=2, max_frames=4, **bad)
+    wb.Decoder(dg, 10.0, 100, max_lanes=2, max_frames=4, epoch_period=2).close()
+    dg.release()
 
 
 @pytest.mark.parametrize("cid,cap,bit", [(2, "frontier_cap", 16), (2, "arena_entries", 4),

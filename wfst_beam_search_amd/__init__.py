@@ -69,7 +69,7 @@ class _Config(ctypes.Structure):
                 ("plain_keys", ctypes.c_int32), ("path_cap", ctypes.c_int32),
                 ("lattice", ctypes.c_int32), ("output_beam", ctypes.c_float),
                 ("lattice_cap", ctypes.c_int64), ("gc_interval", ctypes.c_int32),
-                ("arena_commit", ctypes.c_int64)]
+                ("arena_commit", ctypes.c_int64), ("epoch_period", ctypes.c_int32)]
 
 
 _lib = None
@@ -204,16 +204,16 @@ class Decoder:
                  allow_partial: bool = False, max_lanes: int = 8, max_frames: int = 1024,
                  lp_dtype: str = "f32", eps_iterations: int = 0, use_graphs: bool = True,
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
-                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: bool = False, path_cap: int = 0,
+                 grid_blocks: int = 0, slot_cap: int = 0, plain_keys: int = 0, path_cap: int = 0,
                  lattice: bool = False, output_beam: float = 0.0, lattice_cap: int = 0, gc_interval: int = 0,
-                 arena_commit: int = 0):
+                 arena_commit: int = 0, epoch_period: int = 0):
         lib = load_library()
         cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                       int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                       int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
                       int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
-                      int(bool(plain_keys)), int(path_cap), int(bool(lattice)), float(output_beam),
-                      int(lattice_cap), int(gc_interval), int(arena_commit))
+                      int(plain_keys), int(path_cap), int(bool(lattice)), float(output_beam),
+                      int(lattice_cap), int(gc_interval), int(arena_commit), int(epoch_period))
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h

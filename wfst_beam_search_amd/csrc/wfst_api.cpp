@@ -25,6 +25,8 @@ namespace {
 
 thread_local std::string g_err;
 
+constexpr uint64_t kNoRound = ~0ull;   // no recombination round used since the table was wiped
+
 int fail(int code, const std::string &msg)
 {
     g_err = msg;
@@ -196,6 +198,8 @@ struct wfst_graph_s {
     int device = 0;
     int32_t num_states = 0, num_arcs = 0, start = 0, vocab = 0, eps_id = -1;
     uint32_t max_class_deg = 0;   // most arcs of one class leaving one state
+    uint32_t dest_bits = 0;       // arc records hold the in-rank above this many state id bits (0: no ranks)
+    uint32_t rank_bits = 0;       // bits of the largest in-rank
     std::vector<void *> owned;
     size_t bytes = 0;
     StateInfo *sinfo = nullptr;
@@ -235,9 +239,13 @@ struct wfst_decoder_s {
     int open_streams = 0;
     int32_t *d_plan = nullptr;       // [L][kPlanFields] device copy of the plan
     int32_t *h_plan = nullptr;       // pinned: plan, then the sequence's round base
-    uint64_t round_next = 0;         // first recombination round of the next stream sequence
-                                     //   (counted since the last clear of the whole table)
-    uint32_t dev_round_base = 0;     // round base the device-side Work holds
+    // recombination rounds are numbered on across decodes and stream sequences;
+    // the epoch of round q is 1 + q mod epoch_period, and the table is wiped
+    // before the first round used past a multiple of the period
+    uint64_t round_next = 0;         // round 0 of the next sequence
+    uint64_t round_last = kNoRound;  // last round used since the table was last wiped
+    uint32_t dev_round_base = 0;     // round base and wipe flag the device-side Work holds
+    uint32_t dev_wipe = 0;
     int last_steps = 0;
     bool prof_on = false;            // time every launch with a start / end event pair
     bool last_profiled = false;
@@ -370,9 +378,28 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     std::vector<ArcDLW> dlw((size_t)A);
     for (int32_t s = 0; s < S; ++s)
         for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) src[(size_t)a] = s;
+    // each non-final arc's rank among its destination's incoming non-final arcs,
+    // in arc id order: a table key may break ties by it instead of the arc id
+    // (same order among one destination's candidates, far fewer bits), stored
+    // above the state id when both fit in 31 bits
+    std::vector<uint32_t> rank((size_t)A, 0u);
+    uint32_t max_rank = 0;
+    {
+        std::vector<uint32_t> seen((size_t)S, 0u);
+        for (int32_t a = 0; a < A; ++a) {
+            if (g->ilabel[a] == -1) continue;
+            rank[(size_t)a] = seen[(size_t)g->dest[a]]++;
+            max_rank = std::max(max_rank, rank[(size_t)a]);
+        }
+    }
+    uint32_t db = 1, rb = 1;
+    while ((1ull << db) < (unsigned long long)S) ++db;
+    while ((1ull << rb) <= (unsigned long long)max_rank) ++rb;
+    const bool ranks = db + rb <= 31;
     for (int32_t a = 0; a < A; ++a) {
         const uint32_t il = g->ilabel[a] == -1 ? (uint32_t)kFinalLabel : (uint32_t)g->ilabel[a];
-        dlw[(size_t)a] = ArcDLW{g->dest[a], il, g->weight[a]};
+        const uint32_t dfield = (uint32_t)g->dest[a] | (ranks ? rank[(size_t)a] << db : 0u);
+        dlw[(size_t)a] = ArcDLW{(int32_t)dfield, il, g->weight[a]};
     }
 
     wfst_graph_s *h = new wfst_graph_s();
@@ -383,6 +410,8 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     h->vocab = g->vocab_size;
     h->eps_id = g->epsilon_id;
     h->max_class_deg = md;
+    h->dest_bits = ranks ? db : 0u;
+    h->rank_bits = ranks ? rb : 0u;
     int r = WFST_OK;
     if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->arc_dlw, (size_t)A, &h->owned, &h->bytes)) ||
@@ -429,7 +458,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.frontier_cap < 0 || c.claims_cap < 0 || c.arena_entries < 0 || c.grid_blocks < 0 ||
         c.slot_cap < 0 || c.slot_cap > (1ll << 31))
         return fail(WFST_EINVAL, "capacities must be >= 0");
-    if (c.plain_keys != 0 && c.plain_keys != 1) return fail(WFST_EINVAL, "plain_keys must be 0 or 1");
+    if (c.plain_keys < 0 || c.plain_keys > 2) return fail(WFST_EINVAL, "plain_keys must be 0, 1 or 2");
+    if (c.epoch_period < 0) return fail(WFST_EINVAL, "epoch_period must be >= 0");
     const int P = (g->eps_id >= 0) ? c.eps_iterations : 0;
 
     const uint64_t Q = c.frontier_cap ? (uint64_t)c.frontier_cap : std::min<uint64_t>(64ull * (uint64_t)c.max_active, 1ull << 28);
@@ -492,10 +522,20 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     {
         uint32_t ab = 1;
         while (ab < 31 && (1ll << ab) < (long long)g->num_arcs) ++ab;
-        w.arc_bits = ab;
-        w.epochs = (ab <= kMaxEpochArcBits && !c.plain_keys) ? 1 : 0;
+        const bool ranks = g->dest_bits > 0 && c.plain_keys == 0;
+        const uint32_t tb = ranks ? g->rank_bits : ab;
+        w.tie_bits = tb;
+        w.rank_ties = ranks ? 1u : 0u;
+        w.dest_bits = g->dest_bits;
+        w.dest_mask = g->dest_bits ? (1u << g->dest_bits) - 1u : 0xFFFFFFFFu;
+        w.epochs = (tb <= kMaxEpochArcBits && c.plain_keys != 1) ? 1 : 0;
         // more than 2^16 rounds between clears would gain nothing measurable
-        w.epoch_period = (uint32_t)std::min<uint64_t>((1ull << (32 - ab)) - 1, 65535);
+        const uint32_t pmax = (uint32_t)std::min<uint64_t>((1ull << (32 - tb)) - 1, 65535);
+        if (c.epoch_period != 0 && (c.epoch_period < 2 || (uint32_t)c.epoch_period > pmax)) {
+            delete d;
+            return fail(WFST_EINVAL, "epoch_period must be 0 or lie in [2, 2^(32 - key tie bits) - 1] (at most 65535)");
+        }
+        w.epoch_period = c.epoch_period ? (uint32_t)c.epoch_period : pmax;
     }
     w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
     w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
@@ -558,6 +598,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     }
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
     w.round_base = 0;
+    w.wipe = 0;
     d->chan_open.assign(L, 0);
     d->last_len.assign(L, -1);
 
@@ -567,7 +608,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
-    if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_plan, 4 * (L * kPlanFields + 1), hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_plan, 4 * (L * kPlanFields + 2), hipHostMallocDefault);
     if (e == hipSuccess) e = hipMemset(d->d_plan, 0, 4 * L * kPlanFields);
     if (e == hipSuccess && c.gc_interval > 0) {
         const size_t words = (size_t)arena / 32 + 1;
@@ -601,7 +642,9 @@ static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
 }
 
 // With epoch-tagged table keys the epoch of round (t, k) restarts at 1 every
-// epoch_period rounds: the whole table is cleared before such a round.
+// epoch_period rounds: the whole table is cleared before such a round. (A
+// decode whose rounds pass a multiple of the period starts at one, with the
+// table wiped, and uses every round after its round 0.)
 static hipError_t wrap_clear(wfst_decoder_s *d, int t, int k, hipStream_t s)
 {
     if (!d->w.epochs) return hipSuccess;
@@ -676,15 +719,29 @@ static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)
     return WFST_OK;
 }
 
-// Round base held by the device-side Work (a decode runs with 0).
-static int set_round_base(wfst_decoder_s *d, uint32_t v, hipStream_t s)
+// Round base (the sequence's round 0 modulo the epoch period) and the decode's
+// wipe flag, held by the device-side Work.
+static int set_round_base(wfst_decoder_s *d, uint32_t v, uint32_t wipe, hipStream_t s)
 {
-    if (d->dev_round_base == v) return WFST_OK;
+    static_assert(offsetof(Work, wipe) == offsetof(Work, round_base) + 4, "round_base and wipe are adjacent");
+    if (d->dev_round_base == v && d->dev_wipe == wipe) return WFST_OK;
     uint32_t *h = (uint32_t *)(d->h_plan + (size_t)d->cfg.max_lanes * kPlanFields);
-    *h = v;
-    HIP_TRY(hipMemcpyAsync((char *)d->d_work + offsetof(Work, round_base), h, 4, hipMemcpyHostToDevice, s));
+    h[0] = v;
+    h[1] = wipe;
+    HIP_TRY(hipMemcpyAsync((char *)d->d_work + offsetof(Work, round_base), h, 8, hipMemcpyHostToDevice, s));
     d->dev_round_base = v;
+    d->dev_wipe = wipe;
     return WFST_OK;
+}
+
+// Whether rounds first..last (absolute numbers, in use order) need a table wipe
+// before some of them: the last round used since the last wipe (or, with none,
+// the first of them) lies in an earlier epoch period than the last of them.
+static bool rounds_wrap(const wfst_decoder_s *d, uint64_t first, uint64_t last)
+{
+    const uint64_t P = d->w.epoch_period;
+    const uint64_t ref = d->round_last == kNoRound ? first : d->round_last;
+    return ref / P != last / P;
 }
 
 // Commits n winners-log entries per lane and publishes the bound to the
@@ -754,8 +811,6 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     }
     hipStream_t s = (hipStream_t)stream;
     const size_t L = (size_t)c.max_lanes;
-    int rc0 = set_round_base(d, 0, s);
-    if (rc0 != WFST_OK) return rc0;
     LpDesc *hd = (LpDesc *)d->h_in;
     hd->base = log_prob;
     hd->stride_t = V;
@@ -773,9 +828,28 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     for (;;) {
         // timing events cannot be read back from a replayed graph: a profiled
         // decode runs the same kernels as plain launches
-        if (c.use_graphs && !d->prof_on) {
-            int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
-            bucket = std::min(bucket, c.max_frames + 1);
+        const bool replay = c.use_graphs && !d->prof_on;
+        int bucket = steps <= 256 ? (steps + 31) / 32 * 32 : (steps + 63) / 64 * 64;
+        bucket = std::min(bucket, c.max_frames + 1);
+        const int nsteps = replay ? bucket : steps;
+        // rounds 1 .. R - 1 of the decode are used (round 0 is not). They number
+        // on from the last sequence's unless they would pass an epoch wrap: then
+        // the decode starts at the next multiple of the period with the table
+        // wiped, and clears it again at each later multiple. (A decode run again
+        // after the log grew takes fresh rounds: its first run's entries lose.)
+        const uint64_t R = (uint64_t)(nsteps + 1) * (uint64_t)(1 + d->passes);
+        uint64_t base = d->round_next;
+        uint32_t wipe = 0;
+        if (d->w.epochs) {
+            const uint64_t P = d->w.epoch_period;
+            if (R > P || rounds_wrap(d, base + 1, base + R - 1)) {
+                base = (base + P - 1) / P * P;
+                wipe = 1;
+            }
+        }
+        int rc0 = set_round_base(d, d->w.epochs ? (uint32_t)(base % d->w.epoch_period) : 0u, wipe, s);
+        if (rc0 != WFST_OK) return rc0;
+        if (replay) {
             hipGraphExec_t ex = nullptr;
             int rc = graph_for(d, bucket, &ex);
             if (rc != WFST_OK) return rc;
@@ -786,9 +860,8 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
             if (e != hipSuccess) return hip_fail(e, "kernel launch");
             d->last_steps = steps;
         }
-        // later stream sequences number their rounds on from this decode's (its
-        // entries are still in the table)
-        d->round_next = (uint64_t)(d->last_steps + 1) * (uint64_t)(1 + d->passes);
+        d->round_next = base + R;
+        d->round_last = base + R - 1;
         d->last_profiled = d->prof_on;
         HIP_TRY(hipMemcpyAsync(d->h_res, d->w.res, 4 * rs * (size_t)B, hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
@@ -841,11 +914,17 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
     hipError_t e;
     d->ev_used = 0;
     const uint64_t base = d->round_next;
+    uint64_t last = d->round_last;
+    // before each round it uses: a wipe when the round lies in a later epoch
+    // period than the last round used (a captured sequence has none: see
+    // stream_wraps)
     auto wrap = [&](int t, int k) -> hipError_t {
-        if (!d->w.epochs) return hipSuccess;   // (a captured sequence has no wrap: see stream_wraps)
+        if (!d->w.epochs) return hipSuccess;
         const uint64_t q = base + (uint64_t)((long long)(t + 1) * (1 + d->passes) + k);
-        if (q % d->w.epoch_period != 0) return hipSuccess;
-        return launch(d, kKClear, t, 1, s);
+        const uint64_t P = d->w.epoch_period;
+        const bool clear = last != kNoRound && last / P != q / P;
+        last = q;
+        return clear ? launch(d, kKClear, t, 1, s) : hipSuccess;
     };
     if ((e = launch(d, kKClear, 0, 2, s)) != hipSuccess) return e;
     if ((e = launch(d, kKStreamBegin, 0, 0, s)) != hipSuccess) return e;
@@ -883,13 +962,29 @@ static uint64_t stream_rounds(const wfst_decoder_s *d, int kind, int steps)
     return (uint64_t)((kind == kSeqOpen ? 0 : steps) + 1) * (uint64_t)(1 + d->passes);
 }
 
-// Whether the sequence's rounds pass an epoch wrap (then it clears the table
-// before that round, and runs as plain launches).
+// The first and last rounds a stream sequence uses, as offsets from its round
+// 0 (false when it uses none): the start closure's passes (open), the steps'
+// slot passes and closure passes (advance), the steps' slot passes (finish).
+static bool stream_used(const wfst_decoder_s *d, int kind, int steps, uint64_t *first, uint64_t *last)
+{
+    const uint64_t p1 = 1 + (uint64_t)d->passes;
+    if (kind == kSeqOpen) {
+        *first = 1;
+        *last = (uint64_t)d->passes;
+        return d->passes > 0;
+    }
+    *first = p1;
+    *last = kind == kSeqFinish ? (uint64_t)steps * p1 : (uint64_t)(steps + 1) * p1 - 1;
+    return steps > 0;
+}
+
+// Whether the sequence needs a table wipe before one of its rounds (then it
+// runs as plain launches, with the wipe before that round).
 static bool stream_wraps(const wfst_decoder_s *d, int kind, int steps)
 {
-    if (!d->w.epochs) return false;
-    const uint64_t P = d->w.epoch_period, b = d->round_next;
-    return (b + stream_rounds(d, kind, steps) - 1) / P != b / P;
+    uint64_t f = 0, l = 0;
+    if (!d->w.epochs || !stream_used(d, kind, steps, &f, &l)) return false;
+    return rounds_wrap(d, d->round_next + f, d->round_next + l);
 }
 
 // Runs a stream sequence with the plan in h_plan and waits for it; copies the
@@ -899,7 +994,7 @@ static int run_stream(wfst_decoder_s *d, int kind, int steps, hipStream_t s, con
 {
     const size_t L = (size_t)d->cfg.max_lanes;
     const uint32_t rb = d->w.epochs ? (uint32_t)(d->round_next % d->w.epoch_period) : 0u;
-    int rc = set_round_base(d, rb, s);
+    int rc = set_round_base(d, rb, 0u, s);
     if (rc != WFST_OK) return rc;
     HIP_TRY(hipMemcpyAsync(d->d_plan, d->h_plan, 4 * L * kPlanFields, hipMemcpyHostToDevice, s));
     if (d->cfg.use_graphs && !d->prof_on && !stream_wraps(d, kind, steps)) {
@@ -934,6 +1029,8 @@ static int run_stream(wfst_decoder_s *d, int kind, int steps, hipStream_t s, con
                                hipMemcpyDeviceToHost, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
+    uint64_t uf = 0, ul = 0;
+    if (stream_used(d, kind, steps, &uf, &ul)) d->round_last = d->round_next + ul;
     d->round_next += stream_rounds(d, kind, steps);
     d->last_profiled = d->prof_on;
     d->last_steps = steps;
@@ -1220,7 +1317,7 @@ extern "C" int wfst_decoder_profile(wfst_decoder_t d, int32_t enable)
     HIP_TRY(hipSetDevice(d->g->device));
     if (enable && d->ev.empty()) {
         const size_t rounds = (size_t)(d->cfg.max_frames + 2) * (size_t)(1 + d->passes);
-        const size_t n = 16 + (size_t)(d->cfg.max_frames + 2) * (size_t)(5 + 3 * d->passes + 8) + rounds / d->w.epoch_period;
+        const size_t n = 18 + (size_t)(d->cfg.max_frames + 2) * (size_t)(5 + 3 * d->passes + 8) + rounds / d->w.epoch_period;
         d->ev.resize(2 * n, nullptr);
         d->ev_kind.assign(n, -1);
         for (size_t i = 0; i < 2 * n; ++i) HIP_TRY(hipEventCreateWithFlags(&d->ev[i], hipEventDefault));

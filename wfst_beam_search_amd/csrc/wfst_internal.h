@@ -51,18 +51,21 @@ static_assert(sizeof(StateInfo) == 64, "one state record is one 64-byte line");
 
 // Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR
 // order of the graph), so the fields a pass reads for a token's arcs share
-// cache lines. Final arcs carry kFinalLabel.
+// cache lines. Final arcs carry kFinalLabel. When the graph stores ranks, dest
+// holds the arc's rank among its destination's incoming non-final arcs (in arc
+// id order) above the state id's bits (Work::dest_bits).
 struct ArcDLW {
     int32_t dest;
     uint32_t ilabel;
     float weight;
 };
 
-// An admitted candidate: destination, arc, source (the source token's position
-// in the frontier being read; for a closure candidate, the source token's
-// winners-log entry) and end score. Its key (ordered score << 32 | ~arc) is
-// unique per destination, so exactly one candidate of each destination finds
-// its own key in the table once the pass is over: the winner.
+// An admitted candidate: destination (the arc record's field: the state id,
+// with the arc's rank above it when the graph stores ranks), arc, source (the
+// source token's position in the frontier being read; for a closure candidate,
+// the source token's winners-log entry) and end score. Its key (score, then arc
+// id or rank) is unique per destination, so exactly one candidate of each
+// destination finds its own key in the table once the pass is over: the winner.
 struct alignas(16) Claim {
     int32_t dest;
     int32_t arc;
@@ -146,9 +149,13 @@ struct Work {
     int32_t num_states, num_arcs, start_state, vocab, super_final;
     int32_t has_eps;
     int32_t epochs;           // table keys carry the round's epoch: entries are never cleared singly
-    uint32_t arc_bits;        // arc id bits of an epoch-tagged key (the epoch takes 32 - arc_bits)
+    uint32_t tie_bits;        // tie bits of an epoch-tagged key (the epoch takes 32 - tie_bits)
+    uint32_t rank_ties;       // ties by the arc's rank among its destination's incoming arcs (else arc id)
+    uint32_t dest_bits;       // state id bits of a destination field holding a rank above them (0: none)
+    uint32_t dest_mask;       // state id of a destination field: field & dest_mask
     uint32_t epoch_period;    // rounds between full clears of the table
-    uint32_t round_base;      // rounds of earlier sequences since the table was last cleared
+    uint32_t round_base;      // epoch count of the sequence's round 0 (its rounds' offset into the period)
+    uint32_t wipe;            // 1: the decode's first clear wipes the table (written with round_base)
     // search settings
     float beam;
     int32_t min_active, max_active, allow_partial, eps_iterations;

@@ -68,18 +68,28 @@ __device__ __forceinline__ uint32_t round_epoch(const Work &w, int t, int k)
     return 1u + q % w.epoch_period;
 }
 
-// Key of a candidate in the recombination table. With epochs (arc ids below
-// 2^a, a = arc_bits <= 25): epoch << (32 + a) | ordered score << a |
-// (2^a - 1 - arc), so every key of an earlier round is smaller than every key
-// of the current one: no entry needs clearing (the host wipes the table before
-// the epoch counter wraps); within a round the order is cand_key's: greater
-// score, then smaller arc id.
-__device__ __forceinline__ unsigned long long table_key(const Work &w, float score, int32_t arc, uint32_t ep)
+// State id of a destination field. When the graph stores ranks, arc records
+// (and the candidates made from them) carry, above the state id, the arc's
+// rank among its destination's incoming arcs, counted in arc id order.
+__device__ __forceinline__ uint32_t dest_state(const Work &w, int32_t d) { return (uint32_t)d & w.dest_mask; }
+
+// Key of a candidate (arc, packed destination field pd) in the recombination
+// table. With epochs: epoch << (32 + a) | ordered score << a | (2^a - 1 - tie),
+// a = tie_bits <= 25, where the tie is the arc's rank among its destination's
+// incoming arcs (when the graph stores ranks) or its arc id. Every key of an
+// earlier round is smaller than every key of the current one, so no entry needs
+// clearing (the host wipes the table before the epoch counter wraps). Within a
+// round all keys of one entry share its destination, whose incoming arcs rank
+// in arc id order, so the order is cand_key's either way: greater score, then
+// smaller arc id.
+__device__ __forceinline__ unsigned long long table_key(const Work &w, float score, int32_t arc, int32_t pd,
+                                                        uint32_t ep)
 {
     if (!w.epochs) return cand_key(score, arc);
-    const uint32_t a = w.arc_bits;
+    const uint32_t a = w.tie_bits;
+    const uint32_t tie = w.rank_ties ? (uint32_t)pd >> w.dest_bits : (uint32_t)arc;
     return ((unsigned long long)ep << (32 + a)) | ((unsigned long long)f2ord(score) << a) |
-           (unsigned long long)(((1u << a) - 1u) - (uint32_t)arc);
+           (unsigned long long)(((1u << a) - 1u) - tie);
 }
 
 __device__ __forceinline__ int wlane() { return (int)(threadIdx.x & (kWave - 1)); }
@@ -322,16 +332,19 @@ __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *coun
 __device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, uint32_t ep, Claim &cl)
 {
     cl = w.claims[(size_t)L * w.claims_cap + i];
-    if ((uint32_t)cl.dest >= (uint32_t)w.num_states) return false;
-    unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
-    const bool win = *ent == table_key(w, __uint_as_float(cl.score), cl.arc, ep);
+    const uint32_t ds = dest_state(w, cl.dest);
+    if (ds >= (uint32_t)w.num_states) return false;
+    unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + ds;
+    const bool win = *ent == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
     if (win && !w.epochs) *ent = 0ull;
     return win;
 }
 
 // ---------------------------------------------------------------- k_clear
 // k = 0 (start of a decode): clears the per-step records and the recombination
-// tables — all of them with epoch-tagged keys, else those of lanes whose
+// tables — with epoch-tagged keys all of them when the host asks (the decode's
+// rounds would pass an epoch wrap; otherwise they number on from the last
+// sequence's and every older entry loses), else those of lanes whose
 // candidate list overflowed in an earlier decode (the targeted clears cannot
 // see those entries). k = 1: clears every table (before the epoch counter
 // wraps). k = 2 (start of a stream sequence): the records of the lanes the
@@ -362,6 +375,7 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
     }
     const size_t ns = (size_t)w.num_states;
     if (w.epochs) {
+        if (k == 0 && !w.wipe) return;
         // non-temporal 16-byte stores over the whole [L][num_states] table
         // (hipMalloc'd: 256-byte aligned), an odd last entry singly: the
         // zeros bypass the caches instead of leaving them full of dirty lines
@@ -674,7 +688,7 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
 #pragma unroll
         for (int r = 0; r < kR; ++r)
-            if (adm[r]) atomicMax(&tbl[ud.dst[r]], table_key(w, ud.e[r], (int32_t)ud.arc[r], ep));
+            if (adm[r]) atomicMax(&tbl[dest_state(w, ud.dst[r])], table_key(w, ud.e[r], (int32_t)ud.arc[r], ud.dst[r], ep));
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -1070,7 +1084,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 if (lane == 0) atomicOr(&c.overflow, kOvfArena);
             } else if (adm) {
                 w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
-                    make_int4((int)cl.tok, cl.arc, cl.dest, 0);
+                    make_int4((int)cl.tok, cl.arc, (int32_t)dest_state(w, cl.dest), 0);
             }
         }
         if (tab.ph[L] == kPhFinal) {
@@ -1080,16 +1094,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         }
         // with epochs only admitted candidates need the table (stale entries of
         // earlier rounds always lose); without, every owner clears its entry
-        if (valid && (adm || !w.epochs) && (uint32_t)cl.dest < (uint32_t)w.num_states) {
-            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + (uint32_t)cl.dest;
-            if (*ent == table_key(w, __uint_as_float(cl.score), cl.arc, ep)) {
+        const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
+        if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
+            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + cds;
+            if (*ent == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
                 if (!w.epochs) *ent = 0ull;
                 keep = adm;
             }
         }
         {
             if (keep) {
-                dst = cl.dest;
+                dst = (int32_t)cds;
                 arc = cl.arc;
                 end = __uint_as_float(cl.score);
                 const StateInfo si = w.sinfo[dst];
@@ -1320,7 +1335,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 adm = e > cutoff;
                 if (adm) {
                     ++n_adm;
-                    atomicMax(&tbl[ar.dest], table_key(w, e, a, ep));
+                    atomicMax(&tbl[dest_state(w, ar.dest)], table_key(w, e, a, ar.dest, ep));
                 }
             }
             push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, (uint32_t)sen, e);
@@ -1410,7 +1425,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         if (wm && lane == __ffsll((long long)__ballot(valid)) - 1)
             atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
         if (win && __uint_as_float(cl.score) > tab.f1[L]) {
-            dst = cl.dest;
+            dst = (int32_t)dest_state(w, cl.dest);
             dd.y = (int)cl.score;
             dd.z = cl.arc;
             dd.w = (int32_t)cl.tok;
@@ -1607,10 +1622,10 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
             keep = thr >= tab.f1[L];
             if (keep) {
                 int32_t src_state = w.start_state;
-                if (t > 0) src_state = w.arc_dlw[w.wlog[(size_t)L * w.arena + se].y].dest;
+                if (t > 0) src_state = (int32_t)dest_state(w, w.arc_dlw[w.wlog[(size_t)L * w.arena + se].y].dest);
                 rec[kLatFrame] = t;
                 rec[kLatSrc] = src_state;
-                rec[kLatDst] = (redirect || fin) ? w.super_final : ad.dest;
+                rec[kLatDst] = (redirect || fin) ? w.super_final : (int32_t)dest_state(w, ad.dest);
                 rec[kLatIlabel] = fin ? -1 : (int32_t)ad.ilabel;
                 rec[kLatArc] = arc;
                 rec[kLatScore] = (int32_t)__float_as_uint(sa);
