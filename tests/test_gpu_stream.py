@@ -198,6 +198,25 @@ def test_stream_random_small_graphs(eps):
         check_stream(g, lp, L, chunk, beam, ma, mi, ap, P, use_graphs=graphs, epoch_period=ep)
 
 
+def test_stream_epoch_wrap_on_an_unused_round():
+    """Without epsilon arcs an open uses none of its one round number and a
+    chunk of c frames uses rounds 1..c of its c + 1, so with B streams opened one
+    by one and an epoch period of B + c + 1 the second chunk starts exactly at a
+    multiple of the period, on its unused round 0: the table must still be wiped
+    before its first used round (older entries carry larger epochs)."""
+    B, T = 2, 30
+    for seed, chunk in ((3, 4), (8, 5)):
+        g = synth.random_graph(seed + 900, n=40, deg=(2, 6), vocab=6, self_loop=0.3)
+        lp = synth.random_logprobs(seed + 901, B, T, 6, sigma=1.5)
+        L = np.array([T, T - 3], np.int32)
+        # B opens (one round number each, none used), then chunks of c + 1
+        # rounds: the second chunk begins at round B + chunk + 1
+        _say("stream wrap on an unused round", seed, lp.shape, chunk)
+        for graphs in (False, True):
+            check_stream(g, lp, L, chunk, 8.0, 1000, 0, False, 0, use_graphs=graphs,
+                         epoch_period=B + chunk + 1)
+
+
 def test_stream_staggered_open_with_epsilon():
     """A stream opened while another is mid-utterance: the start closure of the
     new one must not touch the other (page section 8, last paragraphs)."""
