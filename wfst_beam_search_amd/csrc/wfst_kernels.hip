@@ -537,8 +537,9 @@ __global__ __launch_bounds__(kBlock) void k_lpmax(const Work *__restrict__ wp)
 // A wavefront walks its run of the flattened slot space in units of kUnit slots:
 // lane l owns slots j0 + r*64 + l for r < kR, so one window of token offsets and
 // one round of independent arc loads serve kR strips (memory-level parallelism
-// for the latency-bound gathers).
-constexpr int kR = 4;
+// for the latency-bound gathers; two strips balance that against finer units
+// best on the HLG-scale graph).
+constexpr int kR = 2;
 constexpr uint32_t kUnit = kWave * kR;
 
 // Candidates of one unit as seen by one lane of the wavefront.
