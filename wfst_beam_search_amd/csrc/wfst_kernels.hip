@@ -265,8 +265,9 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
 }
 
 // Per-wavefront LDS buffer of the listed candidates of the slot pass and the
-// closure's expand passes (a unit lists at most kUnit of them).
-constexpr uint32_t kClaimBuf = 256;
+// closure's expand passes (a unit lists at most kUnit of them; 8 KB per
+// wavefront, so four units' worth between the flushes' list atomics).
+constexpr uint32_t kClaimBuf = 512;
 
 struct ClaimBuf {
     int32_t dest[kClaimBuf];
