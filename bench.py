@@ -12,7 +12,9 @@ fraction of the HBM roofline for the dominant kernel (algorithmic bytes per
 launch over its average launch time, from hipEvents recorded between the
 decoder's launches in a second, instrumented pass of the same K decodes), and
 the CPU oracle's frames/s on a bounded sample of lanes (test infrastructure,
-single thread).
+single thread). The line's ``configs`` object repeats the measurement for every
+other synthetic workload at full size (frames/s, arcs/s, the method's bytes per
+second against the HBM peak, the oracle on one core beside it).
 """
 
 from __future__ import annotations
@@ -32,33 +34,44 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def algorithmic_bytes(st, elem_bytes, vocab):
-    """Bytes the method must move per decode, per kernel, from the device counters.
+    """Bytes the method must move per decode, from the device step counters.
 
-    Per-unit figures (n tokens expanded, S candidate arcs, C admitted candidates,
-    D distinct destinations, n' survivors = D without epsilon arcs, F lane-frames,
-    E epsilon arcs, e*V log-prob row bytes):
-      max      12 n + 6 S + 28 C + e V F   (the one slot pass: token score + arc range, ilabel u16 +
-                                         weight f32, one row per lane-frame; per admitted candidate
-                                         dest i32, u64 table atomic, 16-byte candidate record)
-      finalize 24 C + 28 D              (candidate + table entry read; per winner: table clear 8 B,
-                                         next-frontier token 12 B, winners-log entry 8 B)
-    Only the admitted candidates C count, not the larger list the slot pass writes
-    while the maximum is still being found.
-      eps_expand 16 E, eps_apply 28 De + 20 Ne   (closure: token + eps arc per relaxation; winners'
-                                         candidate and table entry, changed tokens)
-      path     12 n + 6 S + 52 C + 28 D + e V F (+ eps terms): the whole step, tokens and arcs counted once
+    Per-unit figures (what the method itself reads or writes once, single pass):
+    n tokens expanded, S candidate arcs, C admitted candidates, D distinct
+    admitted destinations (the winners), n' survivors (next-frontier tokens the
+    compaction writes; n' = D), F lane-frames, e*V one log-prob row; on graphs
+    with epsilon arcs E epsilon arcs relaxed, Ce admitted, De distinct, Ne tokens
+    appended or replaced by the closure.
+
+      max       20 n + 6 S + 12 C + e V F   (token state / score / entry 12 B and its arc
+                                             range 8 B; ilabel u16 + weight f32 per arc;
+                                             dest i32 + one u64 recombination atomic per
+                                             admitted candidate; one row per lane-frame)
+      finalize  28 D + 20 n'                (per destination: key 4 B, payload read-back
+                                             12 B, targeted clear 12 B; per survivor the
+                                             token 12 B + winners-log entry 8 B)
+      closure   8 E + 12 Ce + 28 De + 20 Ne (weight + dest per epsilon arc; the same
+                                             per-candidate, per-destination and per-token
+                                             terms as a real step)
+
+    The path figure is their sum. ``design`` counts what this implementation's
+    own choices add on top (the 16-byte candidate record written by the slot
+    pass for every listed candidate and read back by the compaction, the
+    compaction's 64-byte state record per new token, the 16-byte token record
+    the slot pass reads): reported beside the method's bytes, never in them.
     """
     n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
-    E, De, Ne = st["eps_arcs"], st["eps_distinct"], st["eps_changed"]
+    E, Ce, De, Ne = st["eps_arcs"], st["eps_admitted"], st["eps_distinct"], st["eps_changed"]
     row = elem_bytes * vocab * F
     per = {
-        "max": 12 * n + 6 * S + 28 * C + row,
-        "finalize": 24 * C + 28 * D,
-        "eps_expand": 16 * E,
+        "max": 20 * n + 6 * S + 12 * C + row,
+        "finalize": 28 * D + 20 * D,
+        "eps_expand": 8 * E + 12 * Ce,
         "eps_apply": 28 * De + 20 * Ne,
     }
-    path = 12 * n + 6 * S + 52 * C + 28 * D + row + 16 * E + 28 * De + 20 * Ne
-    return per, path
+    path = sum(per.values())
+    design = {"candidate_records": 32 * st["listed"], "state_records": 64 * D, "token_records": 16 * n}
+    return per, path, design
 
 
 def graph_kind(wl):
@@ -126,7 +139,8 @@ def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None):
     import numpy as np
 
     import oracle
-    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    cpus = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {sorted(cpus)[0]})
     og = oracle.OracleGraph(graph)
     frames = arcs = 0
     lanes = same = 0
@@ -144,6 +158,7 @@ def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    os.sched_setaffinity(0, cpus)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -323,6 +338,58 @@ def blank_skip_bench(args, wl, graph, lp, lengths, dev):
     dg.release()
 
 
+def config_summary(wid, steps, warmup, cpu_seconds, dev):
+    """One of the five workloads at full size: decode throughput (captured graph,
+    inputs resident), the method's algorithmic bytes per second against the HBM
+    peak, and the oracle on one core over the batch's first lanes, each of which
+    is compared with the GPU's result."""
+    import numpy as np
+    import torch
+
+    import synth
+    import wfst_beam_search_amd as wb
+
+    wl = synth.WORKLOADS[wid]
+    graph, lp, lengths = synth.workload_inputs(wid)
+    B, T, V = lp.shape
+    dg = wb.Graph(graph, device=0)
+    dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
+                     eps_iterations=wl.eps_iterations, arena_commit=-1)
+    x = torch.from_numpy(lp).to(dev)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        dec.decode(x, lengths)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        res = dec.decode(x, lengths)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = dec.stats()
+    frames = int(np.asarray(lengths).sum())
+    elem = 2 if wl.dtype == "f16" else 4
+    _, path_bytes, _ = algorithmic_bytes(st, elem, V)
+    ok = bool((res.meta[:, 0] == 1).all() and (res.meta[:, 2] == 0).all())
+    dec.close()
+    dg.release()
+    del x
+    torch.cuda.empty_cache()
+    out = {"workload": f"{wl.name}: {graph.num_states - 1} states, {graph.num_arcs} arcs, log_prob {wl.dtype} "
+                       f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}, beam {wl.beam}, "
+                       f"max_active {wl.max_active}" + (f", {wl.eps_iterations} closure passes" if wl.epsilon else ""),
+           "frames_per_s": round(frames * steps / dt, 1),
+           "arcs_expanded_per_s": round((st["arcs"] + st["eps_arcs"]) * steps / dt, 1),
+           "ms_per_decode": round(dt / steps * 1e3, 4),
+           "path_algorithmic_GBps": round(path_bytes * steps / dt / 1e9, 2),
+           "path_hbm_frac": round(path_bytes * steps / dt / 1e9 / HBM_PEAK_GBS, 5),
+           "parity_meta_ok": ok, "steps": steps, "warmup": warmup}
+    if cpu_seconds > 0:
+        cb = cpu_baseline(graph, lp, lengths, wl, cpu_seconds, gpu=res)
+        out["oracle_1core_frames_per_s"] = round(cb["value"], 1)
+        out["oracle_gpu_lanes_identical"] = cb["gpu_lanes_identical"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +424,10 @@ def main():
     ap.add_argument("--blank-skip", type=float, default=None, metavar="THRESHOLD",
                     help="time blank-skip pre-slicing of the workload's log_prob (frames whose blank "
                          "probability exceeds THRESHOLD dropped) instead of a decode")
+    ap.add_argument("--configs", default="1,2,4,5", metavar="IDS",
+                    help="also run these workloads at full size after the headline one (comma list; "
+                         "empty: none) and report them in the line's `configs` object")
+    ap.add_argument("--config-steps", type=int, default=5, help="timed decodes per extra workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE readings to bytes)")
@@ -422,7 +493,7 @@ def main():
     arcs_ps = (st["arcs"] + st["eps_arcs"]) * args.steps / dt
     ok = bool((res.meta[:, 0] == 1).all() and (res.meta[:, 2] == 0).all())
     elem = 2 if wl.dtype == "f16" else 4
-    per_kernel_bytes, path_bytes = algorithmic_bytes(st, elem, V)
+    per_kernel_bytes, path_bytes, design_bytes = algorithmic_bytes(st, elem, V)
 
     roofline = None
     ktimes = {}
@@ -458,15 +529,42 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds, gpu=res)
 
+    configs = {}
+    others = [int(c) for c in args.configs.split(",") if c.strip()] if args.configs else []
+    others = [c for c in others if c != args.workload and c in synth.WORKLOADS]
+    if others and args.lattice is None and not args.gc_interval and not args.eager:
+        # the other workloads (each its own decoder, released before the next)
+        dec.close()
+        dg.release()
+        del x
+        torch.cuda.empty_cache()
+        dec = dg = None
+        cpu_s = {1: 2.0, 2: 3.0, 3: 10.0, 4: 6.0, 5: 4.0}
+        for c in others:
+            configs[str(c)] = config_summary(c, args.config_steps, min(args.warmup, 2),
+                                             0.0 if args.no_cpu_baseline else cpu_s.get(c, 3.0), dev)
+            print(f"bench.py: workload {c} done", file=sys.stderr, flush=True)
+        # the headline workload's own entry, from the run above
+        configs[str(args.workload)] = {
+            "workload": wl.name, "frames_per_s": round(fps, 1), "arcs_expanded_per_s": round(arcs_ps, 1),
+            "ms_per_decode": round(ms_per_step, 4),
+            "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
+            "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
+            "parity_meta_ok": ok, "steps": args.steps, "warmup": args.warmup,
+            **({} if cpu is None else {"oracle_1core_frames_per_s": round(cpu["value"], 1),
+                                       "oracle_gpu_lanes_identical": cpu["gpu_lanes_identical"]})}
+        configs = {k: configs[k] for k in sorted(configs, key=int)}
+
     line = {
         "metric": "decoded frames/sec and arcs expanded/sec at 1 GPU; % of HBM peak",
         "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: {graph_kind(wl)} ({graph.num_states - 1} states, "
                                f"{graph.num_arcs} arcs, {degree_kind(wl)}), log_prob {wl.dtype} "
                                f"[{B},{T},{V}], lengths {wl.lengths[0]}-{wl.lengths[1]}",
                    "batch": B, "frames": T, "vocab": V, "beam": wl.beam, "max_active": wl.max_active,
+                   "log_prob_dtype": wl.dtype, "score_dtype": "f32",
                    "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay",
                    **({} if args.lattice is None else {"lattice_output_beam": args.lattice}),
                    **({} if not args.gc_interval else {"gc_interval": args.gc_interval}),
@@ -477,10 +575,14 @@ def main():
         "hbm_copy_GBps_measured": copy_gbps,
         "path_algorithmic_GBps": round(path_bytes * args.steps / dt / 1e9, 2),
         "path_hbm_frac": round(path_bytes * args.steps / dt / 1e9 / HBM_PEAK_GBS, 5),
+        "path_bytes_per_decode": int(path_bytes),
+        "design_bytes_per_decode": {k: int(v) for k, v in design_bytes.items()},
         "parity_meta_ok": ok,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if configs:
+        line["configs"] = configs
     line["log_entries_at_end"] = int(st["log_entries"])
     line["log_bytes_committed"] = int(st["log_committed_bytes"])
     line["log_bytes_reserved"] = int(st["log_reserved_bytes"])
@@ -493,8 +595,9 @@ def main():
             json.dump({"line": line, "stats": st, "kernels": ktimes, "per_kernel_bytes": per_kernel_bytes,
                        "path_bytes": path_bytes, "profiled_ms_per_step": prof_ms,
                        "kernel_source": kernel_source_hash()}, f, indent=1)
-    dec.close()
-    dg.release()
+    if dec is not None:
+        dec.close()
+        dg.release()
 
 
 if __name__ == "__main__":

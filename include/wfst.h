@@ -273,6 +273,7 @@ int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, in
 /* Free the decoder's workspace and its graph reference. Null is a no-op. */
 int wfst_decoder_destroy(wfst_decoder_t d);
 
+
 /*
  * Streams (page section 8 "Streaming Lifecycle", section 3 on the online beam):
  * a stream decodes one utterance whose frames arrive in chunks. It holds one
@@ -357,8 +358,8 @@ int wfst_finalize_streams(wfst_decoder_t d, const int32_t *channels, int32_t C, 
 int wfst_release_stream(wfst_decoder_t d, int32_t channel);
 
 /*
- * Blank-skip frame pre-slicing before a decode (page section 3: it stays outside
- * the decoder, WeNet-style, threshold 0.98 by default): frame t < lengths[b] of
+ * Blank-skip frame pre-slicing before a decode (page section 3: a step before
+ * the search, as WeNet slices frames, with 0.98 as the usual threshold): frame t < lengths[b] of
  * lane b is dropped iff its blank probability exceeds `threshold`, tested in
  * binary32 as log_prob[b, t, blank_id] > (float) log(threshold); the kept rows
  * keep their order. out_log_prob (device, [B, T, V] packed in lp_dtype, not

@@ -186,8 +186,8 @@ def decode_batch(graph, lp: np.ndarray, lengths, beam: float, max_active: int,
 
 
 def blank_skip(lp: np.ndarray, lengths, blank_id: int, threshold: float):
-    """Blank-skip frame pre-slicing (page section 3, "Blank-skip stays outside the
-    decoder": WeNet-style, threshold 0.98 by default). Reading: frame t < length of
+    """Blank-skip frame pre-slicing (page section 3: a step before the search,
+    as WeNet slices frames, 0.98 the usual threshold). Reading: frame t < length of
     a lane is dropped iff its blank probability exceeds the threshold, tested in
     binary32 as lp[t, blank] > (float32) log(threshold), where the threshold is a
     binary32 value (as the C call takes it) and its log is taken in binary64 and

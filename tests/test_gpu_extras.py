@@ -1,5 +1,5 @@
-"""GPU parity of the steps around the search: blank-skip frame pre-slicing (page
-section 3, "Blank-skip stays outside the decoder") against the oracle's slicing
+"""GPU parity of the steps around the search: blank-skip frame pre-slicing done
+before the decoder runs (page "GPU WFST Beam-Search Decoder", section 3) against the oracle's slicing
 bit for bit, a decode of the sliced frames against the oracle's decode of its
 own slicing, and graphs with sparse final arcs (allow_partial on and off,
 section 3 "Final step") against the oracle, per-step records included."""

@@ -197,6 +197,18 @@ class DecodeResult:
     arc_lens: np.ndarray
 
 
+def _config(beam, max_active, min_active=0, allow_partial=False, max_lanes=8, max_frames=1024, lp_dtype="f32",
+            eps_iterations=0, use_graphs=True, frontier_cap=0, claims_cap=0, arena_entries=0, grid_blocks=0,
+            slot_cap=0, plain_keys=0, path_cap=0, lattice=False, output_beam=0.0, lattice_cap=0, gc_interval=0,
+            arena_commit=0, epoch_period=0) -> _Config:
+    return _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
+                   int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
+                   int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
+                   int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
+                   int(plain_keys), int(path_cap), int(bool(lattice)), float(output_beam),
+                   int(lattice_cap), int(gc_interval), int(arena_commit), int(epoch_period))
+
+
 class Decoder:
     """A decoder instance (workspace on the graph's device)."""
 
@@ -208,12 +220,10 @@ class Decoder:
                  lattice: bool = False, output_beam: float = 0.0, lattice_cap: int = 0, gc_interval: int = 0,
                  arena_commit: int = 0, epoch_period: int = 0):
         lib = load_library()
-        cfg = _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
-                      int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
-                      int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
-                      int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
-                      int(plain_keys), int(path_cap), int(bool(lattice)), float(output_beam),
-                      int(lattice_cap), int(gc_interval), int(arena_commit), int(epoch_period))
+        cfg = _config(beam, max_active, min_active, allow_partial, max_lanes, max_frames, lp_dtype,
+                      eps_iterations, use_graphs, frontier_cap, claims_cap, arena_entries, grid_blocks,
+                      slot_cap, plain_keys, path_cap, lattice, output_beam, lattice_cap, gc_interval,
+                      arena_commit, epoch_period)
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h

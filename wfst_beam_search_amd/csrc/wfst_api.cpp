@@ -443,12 +443,16 @@ extern "C" int wfst_graph_release(wfst_graph_t g)
 
 // ---------------------------------------------------------------- decoder
 
-extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp, wfst_decoder_t *out)
+// Capacities of a decoder's workspace, derived from its config (page section
+// 6.1: every buffer sized once from the configuration).
+struct Sizes {
+    uint64_t Q = 0, slots = 0, strip_cap = 0, CC = 0, arena = 0, lat_cap = 0, path_cap = 0;
+    int P = 0;   // closure passes per step (0 without epsilon arcs)
+};
+
+// Validates a config against graph g and derives the capacities (0 = derive).
+static int derive_sizes(const wfst_graph_s *g, const wfst_decoder_config &c, Sizes *z)
 {
-    if (!out) return fail(WFST_EINVAL, "out is null");
-    *out = nullptr;
-    if (!g || !cp) return fail(WFST_EINVAL, "graph or config is null");
-    wfst_decoder_config c = *cp;
     if (!(c.beam > 0.0f) || std::isinf(c.beam)) return fail(WFST_EINVAL, "beam must be positive and finite");
     if (c.max_active < 1 || c.min_active < 0) return fail(WFST_EINVAL, "max_active must be >= 1 and min_active >= 0");
     if (c.max_lanes < 1 || c.max_lanes > kMaxLanes) return fail(WFST_EINVAL, "max_lanes must lie in [1, 64]");
@@ -493,99 +497,153 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     if (c.gc_interval < 0) return fail(WFST_EINVAL, "gc_interval must be >= 0");
     if (c.arena_commit < -1) return fail(WFST_EINVAL, "arena_commit must be >= -1");
     if (c.gc_interval > 0 && c.lattice) return fail(WFST_EINVAL, "log compaction (gc_interval) does not run in lattice mode");
-    const uint64_t lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
+    z->lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
         : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
                              1ull << 28);
-    const uint64_t path_cap = c.path_cap ? (uint64_t)c.path_cap : (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
+    z->path_cap = c.path_cap ? (uint64_t)c.path_cap : (uint64_t)(c.max_frames + 2) * (uint64_t)(1 + P);
+    z->Q = Q; z->slots = slots; z->strip_cap = strip_cap; z->CC = CC; z->arena = arena; z->P = P;
+    return WFST_OK;
+}
+
+// The scalar fields of a decoder's Work (graph, keys, search settings,
+// capacities); pointers are laid out by lay_out.
+static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &c, const Sizes &z)
+{
+    w = Work{};
+    w.sinfo = g->sinfo; w.arc_dlw = g->arc_dlw;
+    w.olabel = g->olabel; w.arc_src = g->arc_src;
+    w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
+    w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
+    uint32_t ab = 1;
+    while (ab < 31 && (1ll << ab) < (long long)g->num_arcs) ++ab;
+    const bool ranks = g->dest_bits > 0 && c.plain_keys == 0;
+    const uint32_t tb = ranks ? g->rank_bits : ab;
+    w.tie_bits = tb;
+    w.rank_ties = ranks ? 1u : 0u;
+    w.dest_bits = g->dest_bits;
+    w.dest_mask = g->dest_bits ? (1u << g->dest_bits) - 1u : 0xFFFFFFFFu;
+    w.epochs = (tb <= kMaxEpochArcBits && c.plain_keys != 1) ? 1 : 0;
+    // more than 2^16 rounds between clears would gain nothing measurable
+    const uint32_t pmax = (uint32_t)std::min<uint64_t>((1ull << (32 - tb)) - 1, 65535);
+    if (c.epoch_period != 0 && (c.epoch_period < 2 || (uint32_t)c.epoch_period > pmax))
+        return fail(WFST_EINVAL, "epoch_period must be 0 or lie in [2, 2^(32 - key tie bits) - 1] (at most 65535)");
+    w.epoch_period = c.epoch_period ? (uint32_t)c.epoch_period : pmax;
+    w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
+    w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = z.P; w.lp_dtype = c.lp_dtype;
+    w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
+    w.frontier_cap = (uint32_t)z.Q; w.claims_cap = (uint32_t)z.CC;
+    w.arena = (uint32_t)z.arena; w.path_cap = (uint32_t)z.path_cap; w.strip_cap = (uint32_t)z.strip_cap;
+    w.res_stride = (uint32_t)(kResHeader + 2 * z.path_cap);
+    w.lattice = c.lattice;
+    w.output_beam = c.lattice ? c.output_beam : 0.0f;
+    w.lat_cap = (uint32_t)z.lat_cap;
+    w.gc_interval = c.gc_interval;
+    w.chg_cap = (uint32_t)std::max<uint64_t>(z.CC, z.Q);
+    w.round_base = 0;
+    w.wipe = 0;
+    return WFST_OK;
+}
+
+// Device buffers of a decode beside the ones Work points to.
+struct Extra {
+    LaneCtl *ctl = nullptr;
+    Work *d_work = nullptr;
+    LpDesc *d_desc = nullptr;
+    int32_t *d_lengths = nullptr;
+    int32_t *d_plan = nullptr;   // streams only
+};
+
+// Lays out every device buffer a decode touches through take(&ptr, count),
+// called once per buffer in a fixed order. `full`: also the buffers of streams,
+// blank-skip, log compaction and lattices (a decoder's), and the winners log is
+// not taken here (a decoder maps it as a lazily committed region).
+template <typename Take>
+static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes &z, size_t S, bool full, Take &&take)
+{
+    const size_t L = (size_t)c.max_lanes;
+    const uint64_t Q = z.Q;
+    take(&x.ctl, L);
+    take(&x.d_work, 1);
+    take(&x.d_desc, 1);
+    take(&x.d_lengths, L);
+    take(&w.lpmax, L * (size_t)c.max_frames);
+    for (int p = 0; p < 2; ++p) {
+        take(&w.tok_state[p], L * Q); take(&w.tok_score[p], L * Q); take(&w.tok_entry[p], L * Q);
+        take(&w.tok_last[p], L * Q); take(&w.tok_off[p], L * Q); take(&w.tok_abeg[p], L * Q);
+        take(&w.tok_ub[p], L * Q); take(&w.strip_tok[p], L * z.strip_cap);
+        // state -> position maps: read by the closure and the lattice only
+        if (w.has_eps || c.lattice) take(&w.pos[p], L * S);
+        if (z.P > 0) take(&w.changed[p], L * std::max<uint64_t>(z.CC, Q));
+    }
+    take(&w.best, L * S);
+    take(&w.claims, L * z.CC);
+    take(&w.res, L * (size_t)w.res_stride);
+    take(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
+    if (!full) {
+        take(&w.wlog, L * (size_t)z.arena);
+        return;
+    }
+    take(&x.d_plan, L * kPlanFields);
+    take(&w.bs_src, L * (size_t)c.max_frames);
+    take(&w.bs_len, L);
+    if (c.gc_interval > 0) {
+        const size_t words = (size_t)z.arena / 32 + 1;
+        take(&w.gc_mark, L * words);
+        take(&w.gc_wpre, L * words);
+        take(&w.gc_child, L * (size_t)z.arena);
+        take(&w.gc_buf, L * (size_t)z.arena);
+    }
+    if (c.lattice) {
+        const size_t F = (size_t)c.max_frames + 3;
+        take(&w.lat_arc, L * z.lat_cap);
+        take(&w.lat_aoff, L * F);
+        take(&w.lat_fbase, L * F);
+        take(&w.lat_score, L * (size_t)z.arena);
+        take(&w.lat_bwd, L * ((size_t)z.arena + 1));
+        take(&w.lat_out, L * z.lat_cap * kLatFields);
+    }
+}
+
+// Frame-loop grid: every workgroup first builds the lane table, so 4 workgroups
+// per CU (16 wavefronts) is measured best on MI355X.
+static int default_grid(const wfst_decoder_config &c, int device)
+{
+    int ncu = 256;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+        ncu = prop.multiProcessorCount;
+    const long long want = ((long long)c.max_lanes * c.max_active + 127) / 128;
+    return c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
+}
+
+extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp, wfst_decoder_t *out)
+{
+    if (!out) return fail(WFST_EINVAL, "out is null");
+    *out = nullptr;
+    if (!g || !cp) return fail(WFST_EINVAL, "graph or config is null");
+    const wfst_decoder_config c = *cp;
+    Sizes z;
+    int rz = derive_sizes(g, c, &z);
+    if (rz != WFST_OK) return rz;
+    Work w0;
+    rz = init_work(w0, g, c, z);
+    if (rz != WFST_OK) return rz;
     HIP_TRY(hipSetDevice(g->device));
     wfst_decoder_s *d = new wfst_decoder_s();
     d->g = g;
     g->refs.fetch_add(1);
     d->cfg = c;
-    d->passes = P;
-    int ncu = 256;
-    {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, g->device) == hipSuccess && prop.multiProcessorCount > 0)
-            ncu = prop.multiProcessorCount;
-    }
-    const long long want = ((long long)c.max_lanes * c.max_active + 127) / 128;
-    // every workgroup of a frame-loop kernel first builds the lane table, so a
-    // grid of 4 workgroups per CU (16 wavefronts) is measured best on MI355X
-    d->grid = c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
-
+    d->passes = z.P;
+    d->grid = default_grid(c, g->device);
     Work &w = d->w;
-    w.sinfo = g->sinfo; w.arc_dlw = g->arc_dlw;
-    w.olabel = g->olabel; w.arc_src = g->arc_src;
-    w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
-    w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
-    {
-        uint32_t ab = 1;
-        while (ab < 31 && (1ll << ab) < (long long)g->num_arcs) ++ab;
-        const bool ranks = g->dest_bits > 0 && c.plain_keys == 0;
-        const uint32_t tb = ranks ? g->rank_bits : ab;
-        w.tie_bits = tb;
-        w.rank_ties = ranks ? 1u : 0u;
-        w.dest_bits = g->dest_bits;
-        w.dest_mask = g->dest_bits ? (1u << g->dest_bits) - 1u : 0xFFFFFFFFu;
-        w.epochs = (tb <= kMaxEpochArcBits && c.plain_keys != 1) ? 1 : 0;
-        // more than 2^16 rounds between clears would gain nothing measurable
-        const uint32_t pmax = (uint32_t)std::min<uint64_t>((1ull << (32 - tb)) - 1, 65535);
-        if (c.epoch_period != 0 && (c.epoch_period < 2 || (uint32_t)c.epoch_period > pmax)) {
-            delete d;
-            return fail(WFST_EINVAL, "epoch_period must be 0 or lie in [2, 2^(32 - key tie bits) - 1] (at most 65535)");
-        }
-        w.epoch_period = c.epoch_period ? (uint32_t)c.epoch_period : pmax;
-    }
-    w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
-    w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = P; w.lp_dtype = c.lp_dtype;
-    w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
-    w.frontier_cap = (uint32_t)Q; w.claims_cap = (uint32_t)CC;
-    w.arena = (uint32_t)arena; w.path_cap = (uint32_t)path_cap; w.strip_cap = (uint32_t)strip_cap;
-    w.res_stride = (uint32_t)(kResHeader + 2 * path_cap);
-    w.lattice = c.lattice;
-    w.output_beam = c.lattice ? c.output_beam : 0.0f;
-    w.lat_cap = (uint32_t)lat_cap;
-    w.gc_interval = c.gc_interval;
-    w.chg_cap = (uint32_t)std::max<uint64_t>(CC, Q);
+    w = w0;
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
+    const uint64_t arena = z.arena;
     int r = WFST_OK;
-    auto A = [&](auto **p, size_t n) { if (r == WFST_OK) r = dalloc(p, n, &d->owned, &d->bytes); };
-    A(&d->ctl, L);
-    A(&d->d_work, 1);
-    A(&d->d_desc, 1);
-    A(&d->d_lengths, L);
-    A(&w.lpmax, L * (size_t)c.max_frames);
-    for (int p = 0; p < 2; ++p) {
-        A(&w.tok_state[p], L * Q); A(&w.tok_score[p], L * Q); A(&w.tok_entry[p], L * Q);
-        A(&w.tok_last[p], L * Q); A(&w.tok_off[p], L * Q); A(&w.tok_abeg[p], L * Q);
-        A(&w.tok_ub[p], L * Q); A(&w.pos[p], L * S); A(&w.strip_tok[p], L * strip_cap);
-        if (P > 0) A(&w.changed[p], L * std::max<uint64_t>(CC, Q));
-    }
-    A(&w.best, L * S);
-    A(&w.claims, L * CC);
-    A(&w.res, L * (size_t)w.res_stride);
-    A(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
-    A(&d->d_plan, L * kPlanFields);
-    A(&w.bs_src, L * (size_t)c.max_frames);
-    A(&w.bs_len, L);
-    if (c.gc_interval > 0) {
-        const size_t words = (size_t)arena / 32 + 1;
-        A(&w.gc_mark, L * words);
-        A(&w.gc_wpre, L * words);
-        A(&w.gc_child, L * (size_t)arena);
-        A(&w.gc_buf, L * (size_t)arena);
-    }
-    if (c.lattice) {
-        const size_t F = (size_t)c.max_frames + 3;
-        A(&w.lat_arc, L * lat_cap);
-        A(&w.lat_aoff, L * F);
-        A(&w.lat_fbase, L * F);
-        A(&w.lat_score, L * (size_t)arena);
-        A(&w.lat_bwd, L * ((size_t)arena + 1));
-        A(&w.lat_out, L * lat_cap * kLatFields);
-    }
+    Extra x;
+    lay_out(w, x, c, z, S, true, [&](auto **p, size_t n) { if (r == WFST_OK) r = dalloc(p, n, &d->owned, &d->bytes); });
+    d->ctl = x.ctl; d->d_work = x.d_work; d->d_desc = x.d_desc; d->d_lengths = x.d_lengths; d->d_plan = x.d_plan;
     if (r != WFST_OK) { delete d; return r; }
     {
         const uint64_t lim0 = c.arena_commit < 0 ? arena
@@ -597,15 +655,13 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         w.arena_lim = d->log.lim;
     }
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
-    w.round_base = 0;
-    w.wipe = 0;
     d->chan_open.assign(L, 0);
     d->last_len.assign(L, -1);
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
     if (e == hipSuccess) e = hipMemcpy(d->d_work, &w, sizeof(Work), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
-    for (int p = 0; p < 2 && e == hipSuccess; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
+    for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_plan, 4 * (L * kPlanFields + 2), hipHostMallocDefault);
@@ -641,16 +697,51 @@ static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
     return launch_kernel(id, d->w, d->d_work, t, k, d->grid, s);
 }
 
-// With epoch-tagged table keys the epoch of round (t, k) restarts at 1 every
-// epoch_period rounds: the whole table is cleared before such a round. (A
+// Queue one whole decode of `steps` frame-loop steps: go(id, t, k) launches one
+// kernel. With epoch-tagged table keys the epoch of round (t, k) restarts at 1
+// every epoch_period rounds: the whole table is cleared before such a round (a
 // decode whose rounds pass a multiple of the period starts at one, with the
-// table wiped, and uses every round after its round 0.)
-static hipError_t wrap_clear(wfst_decoder_s *d, int t, int k, hipStream_t s)
+// table wiped, and uses every round after its round 0).
+template <typename Go>
+static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &&go)
 {
-    if (!d->w.epochs) return hipSuccess;
-    const long long q = (long long)(t + 1) * (1 + d->passes) + k;
-    if (q <= 0 || q % d->w.epoch_period != 0) return hipSuccess;
-    return launch(d, kKClear, t, 1, s);
+    hipError_t e;
+    auto wrap_clear = [&](int t, int k) -> hipError_t {
+        if (!w.epochs) return hipSuccess;
+        const long long q = (long long)(t + 1) * (1 + passes) + k;
+        if (q <= 0 || q % w.epoch_period != 0) return hipSuccess;
+        return go(kKClear, t, 1);
+    };
+    if ((e = go(kKClear, 0, 0)) != hipSuccess) return e;
+    if ((e = go(kKInit, 0, 0)) != hipSuccess) return e;
+    // (the row maxima first: the start closure's tokens carry frame 0's in their bound)
+    if ((e = go(kKLpmax, 0, 0)) != hipSuccess) return e;
+    for (int k = 1; k <= passes; ++k) {
+        if ((e = wrap_clear(-1, k)) != hipSuccess) return e;
+        if ((e = go(kKEpsExpand, -1, k)) != hipSuccess) return e;
+        if ((e = go(kKEpsApply, -1, k)) != hipSuccess) return e;
+    }
+    for (int t = 0; t < steps; ++t) {
+        if ((e = wrap_clear(t, 0)) != hipSuccess) return e;
+        if ((e = go(kKMax, t, 0)) != hipSuccess) return e;
+        if ((e = go(kKFinalize, t, 0)) != hipSuccess) return e;
+        for (int k = 1; k <= passes; ++k) {
+            if ((e = wrap_clear(t, k)) != hipSuccess) return e;
+            if ((e = go(kKEpsExpand, t, k)) != hipSuccess) return e;
+            if ((e = go(kKEpsApply, t, k)) != hipSuccess) return e;
+        }
+        if (w.gc_interval > 0 && (t + 1) % w.gc_interval == 0 && t + 1 < steps) {
+            static const int ids[] = {kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd};
+            for (int id : ids)
+                if ((e = go(id, 0, 0)) != hipSuccess) return e;
+        }
+    }
+    if (w.lattice) {
+        if ((e = go(kKLatInit, 0, 0)) != hipSuccess) return e;
+        for (int t = steps - 1; t >= 0; --t)
+            if ((e = go(kKLatBack, t, 0)) != hipSuccess) return e;
+    }
+    return go(kKBacktrack, 0, 0);
 }
 
 // One winners-log compaction round (lanes that ran a real step).
@@ -667,36 +758,8 @@ static hipError_t gc_round(wfst_decoder_s *d, hipStream_t s)
 // Queue one whole decode of `steps` frame-loop steps on stream s.
 static hipError_t enqueue_decode(wfst_decoder_s *d, int steps, hipStream_t s)
 {
-    hipError_t e;
     d->ev_used = 0;
-    if ((e = launch(d, kKClear, 0, 0, s)) != hipSuccess) return e;
-    if ((e = launch(d, kKInit, 0, 0, s)) != hipSuccess) return e;
-    // (the row maxima first: the start closure's tokens carry frame 0's in their bound)
-    if ((e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
-    for (int k = 1; k <= d->passes; ++k) {
-        if ((e = wrap_clear(d, -1, k, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
-    }
-    for (int t = 0; t < steps; ++t) {
-        if ((e = wrap_clear(d, t, 0, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
-        if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
-        for (int k = 1; k <= d->passes; ++k) {
-            if ((e = wrap_clear(d, t, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
-        }
-        if (d->w.gc_interval > 0 && (t + 1) % d->w.gc_interval == 0 && t + 1 < steps &&
-            (e = gc_round(d, s)) != hipSuccess) return e;
-    }
-    if (d->w.lattice) {
-        if ((e = launch(d, kKLatInit, 0, 0, s)) != hipSuccess) return e;
-        for (int t = steps - 1; t >= 0; --t)
-            if ((e = launch(d, kKLatBack, t, 0, s)) != hipSuccess) return e;
-    }
-    if ((e = launch(d, kKBacktrack, 0, 0, s)) != hipSuccess) return e;
-    return hipSuccess;
+    return enqueue_decode_with(d->w, d->passes, steps, [&](int id, int t, int k) { return launch(d, id, t, k, s); });
 }
 
 static int graph_for(wfst_decoder_s *d, int steps, hipGraphExec_t *exec)

@@ -451,7 +451,8 @@ __device__ void init_lane(const Work &w, int L, int T)
     w.tok_off[0][q] = 0u;
     w.tok_abeg[0][q] = abeg;
     w.tok_ub[0][q] = ub;
-    w.pos[0][(size_t)L * w.num_states + s] = 0;
+    // (the position map exists only where a kernel reads it: epsilon graphs, lattices)
+    if (w.has_eps || w.lattice) w.pos[0][(size_t)L * w.num_states + s] = 0;
     // the start closure's sources: the start token, if it has epsilon arcs
     const bool eps_src = w.eps_iterations > 0 && si.emit_b > si.eps_b;
     if (eps_src)
@@ -1542,8 +1543,15 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
 // (fwd(source) + s) + bwd(destination) >= best - output_beam, where s is the
 // arc's own score (weight + log-prob; a final arc's weight; 0 for a redirect).
 
-// Before the backward pass: every backward score of a lane with a result is
-// -inf (its winners-log entries and the start token's slot).
+// Whether lane c's lattice holds every arc its search persisted: appends past
+// lat_cap were dropped whole (arena bit) while the cursor still counted them,
+// so a lane past its capacity has ranges with records never written; it gets
+// no backward pass and no kept records.
+__device__ __forceinline__ bool lat_complete(const Work &w, const LaneCtl &c) { return c.lat_cursor <= w.lat_cap; }
+
+// Before the backward pass: every backward score of a lane with a result (and
+// a complete lattice) is -inf (its winners-log entries and the start token's
+// slot).
 __global__ __launch_bounds__(kBlock) void k_lat_init(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
@@ -1551,7 +1559,7 @@ __global__ __launch_bounds__(kBlock) void k_lat_init(const Work *__restrict__ wp
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (int L = 0; L < w.max_lanes; ++L) {
         const LaneCtl &c = w.ctl[L];
-        if (!lane_has_result(c)) continue;
+        if (!lane_has_result(c) || !lat_complete(w, c)) continue;
         const size_t n = min(c.log_cursor, w.arena);
         uint32_t *b = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
         for (size_t i = tid; i < n; i += stride) b[i] = kOrdNegInf;
@@ -1572,10 +1580,10 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
         uint32_t units = 0;
         if (L < w.max_lanes) {
             const LaneCtl &c = w.ctl[L];
-            const bool on = lane_has_result(c) && t <= c.last_step;
+            const bool on = lane_has_result(c) && t <= c.last_step && lat_complete(w, c);
             const bool fin = t == c.last_step;   // the lane's final step (or its redirect)
             const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
-            const uint32_t a1 = fin ? min(c.lat_cursor, w.lat_cap) : w.lat_aoff[(size_t)L * F + t + 1];
+            const uint32_t a1 = min(fin ? c.lat_cursor : w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
             const uint32_t n = (on && a1 > a0) ? a1 - a0 : 0u;
             units = (n + kWave - 1) / kWave;
             tab.n[L] = n;
@@ -2194,8 +2202,8 @@ __global__ __launch_bounds__(kWave) void k_gc_end(const Work *__restrict__ wp)
 }
 
 // -------------------------------------------------------- blank-skip slicing
-// Frame pre-slicing before a decode (page section 3: blank-skip stays outside
-// the decoder, WeNet-style): a frame t < length is dropped iff its blank
+// Frame pre-slicing before a decode (page section 3: the search itself never
+// skips frames; the caller slices them first, as WeNet does): a frame t < length is dropped iff its blank
 // log-prob exceeds lthr = log(threshold); the kept frames keep their order.
 
 // One workgroup per lane: keep flags, a workgroup scan in frame order, the
