@@ -273,6 +273,44 @@ int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T, in
 /* Free the decoder's workspace and its graph reference. Null is a no-op. */
 int wfst_decoder_destroy(wfst_decoder_t d);
 
+/*
+ * For callers that cannot allocate device memory (code that runs under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * decode, as wfst_decode, of the batch with the decoder configuration *c, that
+ * calls no hipMalloc, hipFree or other allocating routine. There is no decoder
+ * object: every workspace buffer of the decode (control blocks, frontiers,
+ * candidate list, recombination table, winners log, results) is laid out in a
+ * static device scratch of WFST_NOALLOC_SCRATCH_BYTES (64 MiB) per device,
+ * which each device the library runs on holds until the process ends.
+ *
+ *  g             an uploaded graph (wfst_graph_upload), on the device the call
+ *                runs on; the call takes no reference.
+ *  c             the same fields as wfst_decoder_create's (0 = derive a
+ *                capacity the same way); lattice and gc_interval must be 0,
+ *                use_graphs and arena_commit are ignored (plain launches, the
+ *                whole winners-log region backed). The workspace these sizes
+ *                give must fit the scratch, else WFST_EINVAL with the bytes
+ *                needed: the derived defaults suit decoder objects and are far
+ *                larger, so callers set frontier_cap, claims_cap, slot_cap,
+ *                arena_entries (and path_cap) for their batches.
+ *  log_prob ...  as wfst_decode (B <= max_lanes, T <= max_frames). A lane whose
+ *                winners log outgrows arena_entries reports WFST_OVF_ARENA (no
+ *                region can grow here). In out_words / out_arcs, entries past a
+ *                row's length (up to its cap) are unspecified.
+ * Results equal wfst_decode's for the same graph, config and inputs. Calls on
+ * one device share its scratch and its contents from the previous call: they
+ * run one at a time (a process-wide lock per device; the call returns after
+ * synchronising `stream`), and every call clears what must start empty. Calls
+ * from separate processes use separate scratch copies.
+ * Errors: WFST_EINVAL (as wfst_decode, lattice or gc_interval set, workspace
+ * larger than the scratch), WFST_EDEVICE.
+ */
+#define WFST_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int wfst_decode_noalloc(wfst_graph_t g, const wfst_decoder_config *c, const void *log_prob, int32_t B, int32_t T,
+                        int32_t V, const int32_t *lengths_host, void *stream,
+                        int32_t *out_words, int32_t words_cap, int32_t *out_word_lens,
+                        int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens,
+                        float *out_scores, int32_t *out_meta);
 
 /*
  * Streams (page section 8 "Streaming Lifecycle", section 3 on the online beam):

@@ -17,7 +17,7 @@ from types import SimpleNamespace
 
 import numpy as np
 
-__all__ = ["Graph", "Decoder", "DecodeResult", "WfstError", "library_path", "load_library",
+__all__ = ["Graph", "Decoder", "DecodeResult", "WfstError", "library_path", "load_library", "decode_noalloc",
            "EXPORTED_SYMBOLS", "LP_F32", "LP_F16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = ("wfst_last_error", "wfst_graph_upload", "wfst_graph_release"
                     "wfst_decoder_stats", "wfst_decoder_mem_stats", "wfst_decoder_step_stats", "wfst_decoder_profile",
                     "wfst_decoder_kernel_times", "wfst_create_stream", "wfst_advance_chunk",
                     "wfst_finalize_stream", "wfst_finalize_streams", "wfst_create_streams", "wfst_release_stream", "wfst_lattice_records",
-                    "wfst_blank_skip")
+                    "wfst_blank_skip", "wfst_decode_noalloc")
 KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", "eps_resolve",
            "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
            "lat_back", "gc_begin", "gc_mark", "gc_scan", "gc_compact", "gc_commit", "gc_roots", "gc_clear",
@@ -119,6 +119,8 @@ def load_library():
         lib.wfst_release_stream.argtypes = [vp, i32]
         lib.wfst_lattice_records.argtypes = [vp, i32, vp, ctypes.c_int64, vp]
         lib.wfst_blank_skip.argtypes = [vp, vp, i32, i32, i32, vp, i32, ctypes.c_float, vp, vp, vp]
+        lib.wfst_decode_noalloc.argtypes = [vp, ctypes.POINTER(_Config), vp, i32, i32, i32, vp, vp, vp, i32, vp,
+                                            vp, i32, vp, vp, vp]
         for name in EXPORTED_SYMBOLS:
             if name != "wfst_last_error":
                 getattr(lib, name).restype = ctypes.c_int
@@ -207,6 +209,38 @@ def _config(beam, max_active, min_active=0, allow_partial=False, max_lanes=8, ma
                    int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
                    int(plain_keys), int(path_cap), int(bool(lattice)), float(output_beam),
                    int(lattice_cap), int(gc_interval), int(arena_commit), int(epoch_period))
+
+
+def decode_noalloc(graph: "Graph", log_prob, lengths, beam: float, max_active: int, stream=None,
+                   words_cap: int | None = None, arcs_cap: int | None = None, **config) -> "DecodeResult":
+    """One decode through ``wfst_decode_noalloc``: no decoder object, the whole
+    workspace in the library's static device scratch (no device allocation).
+    ``config`` takes Decoder's keyword arguments (capacities must fit the
+    scratch); ``log_prob`` and ``lengths`` as Decoder.decode."""
+    import torch
+    lib = load_library()
+    cfg = _config(beam, max_active, **config)
+    if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda or not log_prob.is_contiguous():
+        raise TypeError("log_prob must be a packed torch tensor on the GPU")
+    if log_prob.device.index != graph.device:
+        raise ValueError(f"log_prob must be on cuda:{graph.device}, the graph's device")
+    want = torch.float16 if config.get("lp_dtype", "f32") == "f16" else torch.float32
+    if log_prob.dtype != want or log_prob.dim() != 3:
+        raise TypeError(f"log_prob must be a [B, T, V] {want} tensor")
+    B, T, V = (int(x) for x in log_prob.shape)
+    lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
+    if lens.shape[0] != B:
+        raise ValueError("lengths must have B entries")
+    stream = Decoder._stream(stream, log_prob.device)
+    P = int(config.get("eps_iterations", 0))
+    wcap = int(words_cap) if words_cap is not None else T + 2
+    acap = int(arcs_cap) if arcs_cap is not None else (T + 2) * (1 + max(0, P))
+    out = Decoder._outputs(B, wcap, acap)
+    out_words, wl, out_arcs, al, sc, meta = out
+    _check(lib.wfst_decode_noalloc(graph.handle, ctypes.byref(cfg), ctypes.c_void_p(log_prob.data_ptr()), B, T, V,
+                                   _ptr(lens), ctypes.c_void_p(int(stream)), _ptr(out_words), wcap, _ptr(wl),
+                                   _ptr(out_arcs), acap, _ptr(al), _ptr(sc), _ptr(meta)))
+    return Decoder._result(out, wcap, acap)
 
 
 class Decoder:

@@ -14,6 +14,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "wfst.h"
@@ -960,6 +961,130 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     for (int32_t b = 0; b < B; ++b) d->last_len[(size_t)b] = lengths_host[b];
     for (int32_t b = 0; b < B; ++b)
         copy_result(d, b, b, out_words, words_cap, out_word_lens, out_arcs, arcs_cap, out_arc_lens, out_scores, out_meta);
+    return WFST_OK;
+}
+
+// ------------------------------------------------------ allocation-free decode
+
+static_assert(kScratchBytes == (size_t)WFST_NOALLOC_SCRATCH_BYTES, "one scratch size in the header and the library");
+
+extern "C" int wfst_decode_noalloc(wfst_graph_t g, const wfst_decoder_config *cp, const void *log_prob, int32_t B,
+                                   int32_t T, int32_t V, const int32_t *lengths_host, void *stream,
+                                   int32_t *out_words, int32_t words_cap, int32_t *out_word_lens,
+                                   int32_t *out_arcs, int32_t arcs_cap, int32_t *out_arc_lens, float *out_scores,
+                                   int32_t *out_meta)
+{
+    if (!g || !cp) return fail(WFST_EINVAL, "graph or config is null");
+    const wfst_decoder_config &c = *cp;
+    if (c.lattice) return fail(WFST_EINVAL, "the allocation-free decode has no lattice mode");
+    if (c.gc_interval > 0) return fail(WFST_EINVAL, "the allocation-free decode runs without log compaction (gc_interval 0)");
+    Sizes z;
+    int rc = derive_sizes(g, c, &z);
+    if (rc != WFST_OK) return rc;
+    if (B < 1 || B > c.max_lanes) return fail(WFST_EINVAL, "B must lie in [1, max_lanes]");
+    if (T < 0 || T > c.max_frames) return fail(WFST_EINVAL, "T must lie in [0, max_frames]");
+    if (V != g->vocab) return fail(WFST_EINVAL, "V differs from the graph's vocab_size");
+    if (!lengths_host || !out_word_lens || !out_arc_lens || !out_scores || !out_meta)
+        return fail(WFST_EINVAL, "an output or lengths pointer is null");
+    if (words_cap < 0 || arcs_cap < 0 || (words_cap > 0 && !out_words) || (arcs_cap > 0 && !out_arcs))
+        return fail(WFST_EINVAL, "bad words/arcs buffer");
+    int32_t maxlen = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        if (lengths_host[b] < 0 || lengths_host[b] > T) return fail(WFST_EINVAL, "lengths must lie in [0, T]");
+        maxlen = std::max(maxlen, lengths_host[b]);
+    }
+    if (maxlen > 0 && !log_prob) return fail(WFST_EINVAL, "log_prob is null");
+    Work w;
+    rc = init_work(w, g, c, z);
+    if (rc != WFST_OK) return rc;
+
+    // the workspace, laid out in the device's scratch (256-byte aligned pieces)
+    const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
+    size_t need = 0;
+    bool over = false;
+    auto place = [&](char *base) {
+        need = 0;
+        Extra x;
+        lay_out(w, x, c, z, S, false, [&](auto **p, size_t n) {
+            using E = std::remove_pointer_t<std::remove_pointer_t<decltype(p)>>;
+            const size_t nb = std::max<size_t>(n, 1) * sizeof(E);
+            need = (need + 255) & ~(size_t)255;
+            if (nb > kScratchBytes || need > kScratchBytes - nb) over = true;
+            *p = (base && !over) ? (E *)(base + need) : nullptr;
+            need += nb;
+        });
+        return x;
+    };
+    place(nullptr);
+    if (over || need > kScratchBytes)
+        return fail(WFST_EINVAL, "the workspace needs " + std::to_string(need) + " bytes; the allocation-free decode has " +
+                                     std::to_string(kScratchBytes) +
+                                     " (lower max_lanes, frontier_cap, claims_cap, slot_cap, arena_entries or path_cap)");
+    HIP_TRY(hipSetDevice(g->device));
+    const size_t elem = c.lp_dtype == WFST_LP_F16 ? 2 : 4;
+    if (maxlen > 0) {
+        const int rcb = check_device_buffer(log_prob, (size_t)B * (size_t)T * (size_t)V * elem, g->device, "log_prob");
+        if (rcb != WFST_OK) return rcb;
+    }
+    void *base = nullptr;
+    HIP_TRY(scratch_region(g->device, &base));
+    std::lock_guard<std::mutex> lock(scratch_call_mutex(g->device));
+    const Extra x = place((char *)base);
+    w.ctl = x.ctl; w.lp = x.d_desc; w.lengths = x.d_lengths; w.plan = nullptr;
+    w.arena_lim = w.arena;   // the whole region is backed: nothing to commit later
+    hipStream_t s = (hipStream_t)stream;
+    LpDesc hd{};
+    hd.base = log_prob;
+    hd.stride_t = V;
+    hd.stride_b = (long long)T * V;
+    hd.B = B;
+    hd.dtype = c.lp_dtype;
+    int32_t lens[kMaxLanes] = {0};
+    for (int32_t b = 0; b < B; ++b) lens[b] = lengths_host[b];
+    const int grid = default_grid(c, g->device);
+    const int steps = maxlen + 1;
+    // the scratch holds whatever the last call left: the control blocks and the
+    // recombination table start at zero, the position maps at -1
+    auto run = [&]() -> hipError_t {
+        hipError_t e = hipMemsetAsync(x.ctl, 0, sizeof(LaneCtl) * L, s);
+        if (e == hipSuccess) e = hipMemsetAsync(w.best, 0, sizeof(unsigned long long) * L * S, s);
+        for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemsetAsync(w.pos[p], 0xFF, 4 * L * S, s);
+        if (e == hipSuccess) e = launch_noalloc_put(w, hd, lens, (int)L, x.d_work, x.d_desc, x.d_lengths, s);
+        if (e == hipSuccess)
+            e = enqueue_decode_with(w, z.P, steps, [&](int id, int t, int k) {
+                return launch_kernel(id, w, x.d_work, t, k, grid, s);
+            });
+        return e;
+    };
+    hipError_t e = run();
+    // result headers, then each lane's arcs and words straight into the
+    // caller's rows (entries past a row's length are unspecified)
+    int32_t hdr[kMaxLanes][kResHeader];
+    const size_t rs = 4 * (size_t)w.res_stride;
+    if (e == hipSuccess) e = hipMemcpy2DAsync(hdr, sizeof(hdr[0]), w.res, rs, sizeof(hdr[0]), (size_t)B, hipMemcpyDeviceToHost, s);
+    const size_t acopy = std::min<size_t>((size_t)arcs_cap, w.path_cap), wcopy = std::min<size_t>((size_t)words_cap, w.path_cap);
+    if (e == hipSuccess && acopy > 0)
+        e = hipMemcpy2DAsync(out_arcs, 4 * (size_t)arcs_cap, w.res + kResHeader, rs, 4 * acopy, (size_t)B,
+                             hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && wcopy > 0)
+        e = hipMemcpy2DAsync(out_words, 4 * (size_t)words_cap, w.res + kResHeader + w.path_cap, rs, 4 * wcopy, (size_t)B,
+                             hipMemcpyDeviceToHost, s);
+    // (also on failure: no work of this call may still run when the next one starts)
+    const hipError_t es = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "allocation-free decode");
+    if (es != hipSuccess) return hip_fail(es, "hipStreamSynchronize");
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t *R = hdr[b];
+        out_meta[3 * b + 0] = R[kResOk];
+        out_meta[3 * b + 1] = R[kResReached];
+        out_meta[3 * b + 2] = R[kResOverflow];
+        uint32_t sb = (uint32_t)R[kResScore];
+        float sc;
+        std::memcpy(&sc, &sb, 4);
+        out_scores[b] = sc;
+        out_arc_lens[b] = R[kResArcLen];
+        out_word_lens[b] = R[kResWordLen];
+    }
     return WFST_OK;
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace wfst {
 
 constexpr int kWave = 64;           // CDNA wavefront width
@@ -245,6 +247,17 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
 // log-prob exceeds lthr are dropped, the kept rows packed first, zeros after.
 hipError_t launch_blank_skip(const Work &w, const Work *dw, void *out, float lthr, int blank, int B, int T,
                              int grid, hipStream_t s);
+
+// Allocation-free decode (wfst_noalloc.hip): the per-device static
+// scratch every such call lays its workspace out in, its address on `device`
+// (looked up once per device, with the device current), the mutex that keeps
+// those calls one at a time per device, and the kernel that writes a call's
+// Work, log-prob descriptor and lengths (n <= kMaxLanes) into the scratch.
+constexpr size_t kScratchBytes = 64ull << 20;   // WFST_NOALLOC_SCRATCH_BYTES
+hipError_t scratch_region(int device, void **ptr);
+std::mutex &scratch_call_mutex(int device);
+hipError_t launch_noalloc_put(const Work &w, const LpDesc &d, const int32_t *lengths, int n, Work *dw, LpDesc *dd,
+                              int32_t *dl, hipStream_t s);
 
 // Result buffer header (int32 per lane, then arcs[path_cap], words[path_cap]).
 enum : int { kResOk = 0, kResReached, kResOverflow, kResArcLen, kResWordLen, kResScore, kResHeader = 8 };
