@@ -117,9 +117,10 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
     ``online``: streaming semantics (no "last ~5 frames" raise of min_active).
     ``partial``: stop after the ``length`` real steps; the result is the path of the
     best current token (no final step).
-    ``output_beam``: also build the lattice (epsilon-free search) and prune it;
-    adds ``lattice`` (int32 [n, 8], fields ``LAT_FIELDS``, every admitted arc with
-    its keep bit) and ``lattice_vals`` (float32 [n, 3]: fwd(src), arc score, bwd(dst)).
+    ``output_beam``: also build the lattice and prune it; adds ``lattice`` (int32
+    [n, 8], fields ``LAT_FIELDS``, every admitted arc with its keep bit; on graphs
+    with epsilon arcs also every epsilon arc a closure admitted, flags 4, once per
+    frame) and ``lattice_vals`` (float32 [n, 3]: fwd(src), arc score, bwd(dst)).
 
     Returns a dict: score (float32), reached_final, dead, arcs, words (int32 arrays),
     steps (int64 [n_steps, 16], fields ``FIELDS``), start_closure, log_entries.

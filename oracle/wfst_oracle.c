@@ -84,7 +84,14 @@ typedef struct {
  * {frame, src state, dst state, ilabel (-1 final), arc id, score bits, keep, flags}
  * with the arc's own score s (weight + log-prob, one binary32 addition; a final
  * arc's weight; 0 for the redirect's virtual arc, flags 2; final arcs flags 1),
- * and vals {fwd(src), s, bwd(dst)}. keep is the output_beam prune. */
+ * and vals {fwd(src), s, bwd(dst)}. keep is the output_beam prune.
+ * On graphs with epsilon arcs (section 5.5: the candidate set is persisted
+ * after the closure, epsilon arcs tagged) every epsilon candidate a closure
+ * admitted is also a lattice arc, from its source's token to its destination's
+ * token within the same frame: frame f is the frame the closure prepared
+ * (0 for the start closure, t + 1 after step t), ilabel the epsilon id, s the
+ * arc's weight, flags 4. An epsilon arc admitted by several passes of one
+ * closure (its source improved in between) is one lattice arc. */
 typedef struct {
     float output_beam;   /* finite, >= 0 */
     int64_t cap;         /* records rec / vals hold */
@@ -211,6 +218,12 @@ typedef struct {
     uint64_t *best_key;     /* state -> best candidate key this step, 0 if none     */
     int32_t *best_src;      /* state -> winners-log entry of that candidate's source */
     wo_ivec touched;        /* states with best_key != 0                            */
+    /* lattice mode on epsilon graphs: the admitted epsilon arcs of each closure
+     * (source token index in its frontier, arc), one entry per arc and frame */
+    int lat;                /* 1: record them                                        */
+    int32_t *eps_seen;      /* arc -> 1 + the frame whose closure last recorded it   */
+    int32_t frame;          /* frame the running closure prepares                    */
+    wo_ivec le_src, le_arc;
 } wo_scratch;
 
 /* Offer candidate (dest d, score end, arc a, source entry e) to recombination:
@@ -269,6 +282,11 @@ static int wo_closure(const wo_graph *g, int32_t passes_max, float cutoff, wo_fr
                 if (end > cutoff) {
                     stat[1]++;
                     if (wo_offer(sc, g->dest[a], end, a, snap_e[j])) goto out;
+                    if (sc->lat && sc->eps_seen[a] != sc->frame + 1) {
+                        /* a lattice arc of this frame (once, whichever pass admits it first) */
+                        sc->eps_seen[a] = sc->frame + 1;
+                        if (wo_ivec_push(&sc->le_src, src.v[j]) || wo_ivec_push(&sc->le_arc, a)) goto out;
+                    }
                 }
             }
         }
@@ -355,6 +373,7 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     wo_ivec lt_state = {0}, la_src = {0}, la_arc = {0};
     wo_fvec lt_score = {0}, la_s = {0};
     int64_t *lt_off = NULL, *la_off = NULL;
+    int64_t *le_beg = NULL, *le_end = NULL;   /* epsilon lattice arcs of frame f: [le_beg[f], le_end[f]) */
     int32_t lat_steps = 0;
     int rc = -1;
     int32_t final_entry = -1;
@@ -364,14 +383,25 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     memset(res, 0, sizeof(*res));
     res->score = -INFINITY;
     if (!g || !cfg || T < 0 || (T > 0 && !lp)) return -2;
-    /* lattice mode: epsilon-free search only (no closure), not with partial results */
-    if (lat && ((g->epsilon_id >= 0 && cfg->eps_iterations > 0) || cfg->partial ||
-                !(lat->output_beam >= 0.0f) || isinf(lat->output_beam))) return -2;
+    /* lattice mode: not with partial results; on epsilon graphs every epsilon
+     * weight must be <= 0 (reading: then a token's best continuation inside its
+     * frame exists, since no epsilon cycle can raise it) */
+    if (lat && (cfg->partial || !(lat->output_beam >= 0.0f) || isinf(lat->output_beam))) return -2;
+    if (lat && g->epsilon_id >= 0 && cfg->eps_iterations > 0)
+        for (int32_t a = 0; a < g->num_arcs; a++)
+            if (g->ilabel[a] == g->epsilon_id && g->weight[a] > 0.0f) return -2;
     if (lat) {
         lat->n = 0;
         lt_off = malloc(((size_t)T + 3) * 8);
         la_off = malloc(((size_t)T + 3) * 8);
-        if (!lt_off || !la_off) goto out;
+        le_beg = calloc((size_t)T + 3, 8);
+        le_end = calloc((size_t)T + 3, 8);
+        if (!lt_off || !la_off || !le_beg || !le_end) goto out;
+        if (g->epsilon_id >= 0 && cfg->eps_iterations > 0) {
+            sc.lat = 1;
+            sc.eps_seen = calloc((size_t)(g->num_arcs > 0 ? g->num_arcs : 1), 4);
+            if (!sc.eps_seen) goto out;
+        }
     }
     sc.tok_of_state = malloc((size_t)g->num_states * 4);
     sc.best_key = calloc((size_t)g->num_states, 8);
@@ -383,7 +413,10 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     sc.tok_of_state[g->start] = 0;
     if (g->epsilon_id >= 0 && cfg->eps_iterations > 0) {
         float cut0 = 0.0f - cfg->beam;
+        sc.frame = 0;
+        if (lat) le_beg[0] = sc.le_src.n;
         if (wo_closure(g, cfg->eps_iterations, cut0, &cur, &lg, &sc, res->start_closure)) goto out;
+        if (lat) le_end[0] = sc.le_src.n;
     }
 
     for (int32_t t = 0; t <= T; t++) {
@@ -542,7 +575,10 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
         }
         if (g->epsilon_id >= 0 && cfg->eps_iterations > 0) {
             int64_t st[8] = {0};
+            sc.frame = t + 1;
+            if (lat) le_beg[t + 1] = sc.le_src.n;
             if (wo_closure(g, cfg->eps_iterations, cutoff, &cur, &lg, &sc, st)) goto out;
+            if (lat) le_end[t + 1] = sc.le_src.n;
             rec[WO_EPS_ARCS] = st[0]; rec[WO_EPS_ADMITTED] = st[1]; rec[WO_EPS_DISTINCT] = st[2];
             rec[WO_EPS_NEW] = st[3]; rec[WO_EPS_REPLACED] = st[4]; rec[WO_EPS_PASSES] = st[5];
         }
@@ -605,6 +641,52 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
             }
             if (!last)
                 for (int64_t j = lt_off[t + 1]; j < lt_off[t + 2]; j++) sc.tok_of_state[lt_state.v[j]] = -1;
+            /*
+             * Epsilon arcs of frame t (reading): bwd(token) also takes the best of
+             * w + bwd(dst) over its epsilon arcs, whose destinations lie in the
+             * same frame, so frame t's scores are the least fixpoint of those
+             * relaxations on top of the step's own arcs: relaxed until nothing
+             * changes (every epsilon weight is <= 0, so this ends, and the result
+             * is the best right-folded continuation whatever the order). Then the
+             * same keep test, with fwd(src) the source token's score after the
+             * closure and s the arc's weight.
+             */
+            if (le_end[t] > le_beg[t]) {
+                for (int64_t j = t0; j < t0 + nt; j++) sc.tok_of_state[lt_state.v[j]] = (int32_t)(j - t0);
+                for (int changed = 1; changed;) {
+                    changed = 0;
+                    for (int64_t k = le_beg[t]; k < le_end[t]; k++) {
+                        const int32_t i = sc.le_src.v[k], a = sc.le_arc.v[k];
+                        const float v = g->weight[a] + b[sc.tok_of_state[g->dest[a]]];
+                        if (v > b[i]) { b[i] = v; changed = 1; }
+                    }
+                }
+                for (int64_t k = le_beg[t]; k < le_end[t]; k++) {
+                    const int32_t i = sc.le_src.v[k], a = sc.le_arc.v[k];
+                    const float sa = g->weight[a];
+                    const float bd = b[sc.tok_of_state[g->dest[a]]];
+                    const float fwd = lt_score.v[t0 + i];
+                    const float thr = (fwd + sa) + bd;
+                    if (lat->n < lat->cap) {
+                        int32_t *r = lat->rec + lat->n * 8;
+                        uint32_t u;
+                        memcpy(&u, &sa, 4);
+                        r[0] = t;
+                        r[1] = lt_state.v[t0 + i];
+                        r[2] = g->dest[a];
+                        r[3] = g->epsilon_id;
+                        r[4] = a;
+                        r[5] = (int32_t)u;
+                        r[6] = thr >= thresh ? 1 : 0;
+                        r[7] = 4;
+                        lat->vals[lat->n * 3 + 0] = fwd;
+                        lat->vals[lat->n * 3 + 1] = sa;
+                        lat->vals[lat->n * 3 + 2] = bd;
+                    }
+                    lat->n++;
+                }
+                for (int64_t j = t0; j < t0 + nt; j++) sc.tok_of_state[lt_state.v[j]] = -1;
+            }
             free(bnext);
             bnext = b;
             (void)bcur;
@@ -649,7 +731,8 @@ out:
     free(lg.prev); free(lg.arc);
     free(sc.tok_of_state); free(sc.best_key); free(sc.best_src); free(sc.touched.v);
     free(lt_state.v); free(la_src.v); free(la_arc.v); free(lt_score.v); free(la_s.v);
-    free(lt_off); free(la_off);
+    free(lt_off); free(la_off); free(le_beg); free(le_end);
+    free(sc.eps_seen); free(sc.le_src.v); free(sc.le_arc.v);
     return rc;
 }
 

@@ -15,6 +15,10 @@ their weight).
   score (the lattice pins compare kept arcs with them).
 * ``enumerate_paths``: lists every path (at most ``max_eps`` epsilon arcs
   between frames) and takes the maximum.
+* ``complete_paths_framed``: every complete path (at most ``max_eps`` epsilon
+  arcs between frames) with its score and each arc tagged with the frame it
+  runs in (an epsilon arc: the number of emitting arcs before it; an emitting
+  arc: its frame; the final arc: T).
 """
 
 from __future__ import annotations
@@ -165,4 +169,26 @@ def complete_paths(g, lp, T):
                 out.append((F32(sc + g.weight[a]), arcs + [a]))
 
     rec(g.start, 0, F32(0.0), [])
+    return out
+
+
+def complete_paths_framed(g, lp, T, max_eps):
+    """Every path e* (x e*)^T f from the start state, at most ``max_eps`` epsilon
+    arcs per e* run: a list of (score, [(frame, arc), ...]) with the fp32
+    left-to-right score of section 5.3."""
+    final, eps, emit = _classes(g)
+    rs = g.row_splits
+    out = []
+
+    def rec(s, t, sc, arcs, eps_left):
+        for a in range(rs[s], rs[s + 1]):
+            if eps[a] and eps_left > 0:
+                rec(int(g.dest[a]), t, F32(sc + g.weight[a]), arcs + [(t, int(a))], eps_left - 1)
+            elif emit[a] and t < T:
+                c = F32(F32(sc + g.weight[a]) + F32(lp[t, g.ilabel[a]]))
+                rec(int(g.dest[a]), t + 1, c, arcs + [(t, int(a))], max_eps)
+            elif final[a] and t == T:
+                out.append((F32(sc + g.weight[a]), arcs + [(t, int(a))]))
+
+    rec(g.start, 0, F32(0.0), [], max_eps)
     return out

@@ -54,8 +54,12 @@ MUTANTS = {
     "final_weight_dropped": [(_CAND, "float end = is_final ? cur.score[i] : cur.score[i] + g->weight[a];\n"
                                      "                if (!is_final) end = end + row[g->ilabel[a]];", 2)],
     # section 3 on output_beam: keep at >=, and the backward score adds the arc's
-    "lattice_keep_strict": [("r[6] = thr >= thresh ? 1 : 0;", "r[6] = thr > thresh ? 1 : 0;", 1)],
+    "lattice_keep_strict": [("r[6] = thr >= thresh ? 1 : 0;", "r[6] = thr > thresh ? 1 : 0;", 2)],
     "lattice_backward_drops_arc": [("const float v = sa + bd;", "const float v = bd;", 1)],
+    # section 5.5 lattice persistence, reading R31: a frame's epsilon arcs relaxed
+    # to a fixpoint, each recorded once per frame
+    "lattice_eps_one_round": [("for (int changed = 1; changed;) {", "for (int changed = 1; changed; changed = 0) {", 1)],
+    "lattice_eps_no_dedupe": [("if (sc->lat && sc->eps_seen[a] != sc->frame + 1) {", "if (sc->lat) {", 1)],
 }
 
 
@@ -100,6 +104,8 @@ def _pin_calls():
         ("lattice_keep", pins.test_lattice_keep_rule_and_best_path),
         ("lattice_paths", pins.test_lattice_at_infinite_beam_is_every_complete_path),
         ("lattice_ties", pins.test_lattice_keep_at_exact_ties),
+        ("eps_lattice_paths", pins.test_eps_lattice_at_infinite_beam_is_every_path_within_output_beam),
+        ("eps_lattice_bwd", pins.test_eps_lattice_backward_scores_are_best_continuations),
     ]
     return calls
 

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from bruteforce import complete_paths, enumerate_paths, viterbi_exact, viterbi_partial
+from bruteforce import complete_paths, complete_paths_framed, enumerate_paths, viterbi_exact, viterbi_partial
 from cases import check_path, f32_value, graph_from_states, load_golden
 
 F32 = np.float32
@@ -393,6 +393,16 @@ def _lat(g, lp, T, beam, max_active, output_beam, **kw):
     return oracle.decode_lane(g, lp, T, beam, max_active, output_beam=output_beam, **kw)
 
 
+EPS_FLAG = 4    # lattice record flag of an epsilon arc (it stays in its frame)
+
+
+def _next_node(r):
+    """The lattice node an arc record enters: (frame + 1, dst), or (frame, dst)
+    for an epsilon arc, which runs inside its frame."""
+    f = int(r[LF["frame"]])
+    return (f if int(r[LF["flags"]]) == EPS_FLAG else f + 1, int(r[LF["dst"]]))
+
+
 def _continuations(lat, sf):
     """Best right-folded continuation score of every lattice node (frame, state),
     by listing every continuation path to the super-final state explicitly."""
@@ -409,7 +419,7 @@ def _continuations(lat, sf):
             if int(r[LF["dst"]]) == sf:
                 res.append([s])
             else:
-                for p in paths((int(r[LF["frame"]]) + 1, int(r[LF["dst"]]))):
+                for p in paths(_next_node(r)):
                     res.append([s] + p)
         return res
 
@@ -524,6 +534,83 @@ def test_lattice_keep_at_exact_ties():
             assert kept == want, (seed, ob)
             checked += len(want)
     assert checked > 200
+
+
+def _grid(g, lp, seed):
+    """Weights and log-probs on a 1/8 grid (every fp32 sum of a tiny case exact)."""
+    rng = np.random.default_rng(seed)
+    g.weight = (-rng.integers(0, 9, size=len(g.weight)) / 8.0).astype(np.float32)
+    return g, (-rng.integers(0, 17, size=lp.shape) / 8.0).astype(np.float32)
+
+
+def test_eps_lattice_at_infinite_beam_is_every_path_within_output_beam():
+    """Section 5.5 (the candidate set persisted after the closure, epsilon arcs
+    tagged), reading R31: at infinite search beam every candidate of every step
+    and closure pass is admitted, and with epsilon chains at most P arcs long P
+    passes reach every state an epsilon path reaches. With weights and
+    log-probs on a 1/8 grid every sum is exact, so the kept (frame, arc) pairs at
+    output beam ob are exactly the arc occurrences of complete paths scoring at
+    least best - ob, epsilon arcs counted in the frame they run in; each epsilon
+    arc is one record per frame (never repeated when several passes admit it),
+    tagged with the epsilon id and flag 4."""
+    checked = 0
+    for seed in range(1200, 1290):
+        g, lp, T = _tiny(seed, True)
+        if T == 0 or g.epsilon_id < 0:
+            continue
+        g, lp = _grid(g, lp, seed)
+        P = 2   # _tiny's epsilon levels: chains of at most 2 arcs
+        paths = complete_paths_framed(g, lp, T, P)
+        if not paths:
+            continue
+        best = max(p[0] for p in paths)
+        for ob in (0.0, 0.5, 1e6):
+            r = _lat(g, lp, T, INF_BEAM, 1 << 20, ob, eps_iterations=P)
+            assert r["score"] == best, seed
+            recs = r["lattice"]
+            keys = [(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in recs]
+            assert len(keys) == len(set(keys)), f"seed {seed}: an arc recorded twice in one frame"
+            epsr = recs[recs[:, LF["flags"]] == EPS_FLAG]
+            assert np.all(g.ilabel[epsr[:, LF["arc"]]] == g.epsilon_id)
+            assert np.all(epsr[:, LF["ilabel"]] == g.epsilon_id)
+            kept = {k for k, x in zip(keys, recs) if x[LF["keep"]]}
+            want = {fa for sc, arcs in paths if sc >= best - F32(ob) for fa in arcs}
+            assert kept == want, (seed, ob)
+            checked += sum(1 for f, a in want if g.ilabel[a] == g.epsilon_id)
+    assert checked > 100
+
+
+def test_eps_lattice_backward_scores_are_best_continuations():
+    """Reading R31: an epsilon arc's backward term is its destination's best
+    continuation inside the same frame (epsilon arcs again, then the frame's step)
+    and an emitting arc's that of its destination in the next frame, each
+    continuation folded from its last arc back; pruned search (finite beam),
+    listing every continuation explicitly."""
+    checked = 0
+    for seed in range(1300, 1380):
+        g, lp, T = _tiny(seed, True)
+        r = _lat(g, lp, T, 3.0, 50, 2.0, eps_iterations=2)
+        if r["reached_final"] != 1:
+            continue
+        sf = g.num_states - 1
+        best = _continuations(r, sf)
+        for k, rr in enumerate(r["lattice"]):
+            dst = int(rr[LF["dst"]])
+            want = F32(0.0) if dst == sf else best.get(_next_node(rr), F32(-np.inf))
+            assert r["lattice_vals"][k, 2] == want, (seed, k)
+            checked += int(rr[LF["flags"]]) == EPS_FLAG
+    assert checked > 100
+
+
+def test_eps_lattice_refuses_positive_epsilon_weights():
+    """Reading R31: a best continuation needs epsilon weights <= 0 (a positive
+    epsilon cycle would raise it without bound), so lattice mode refuses them."""
+    g, lp, T = _tiny(1201, True)
+    eps = g.ilabel == g.epsilon_id
+    assert eps.any()
+    g.weight = np.where(eps, np.float32(0.25), g.weight).astype(np.float32)
+    with pytest.raises(RuntimeError):
+        _lat(g, lp, max(T, 1), 5.0, 50, 1.0, eps_iterations=2)
 
 
 # ------------------------------------------------------------ blank-skip slicing
