@@ -134,17 +134,23 @@ typedef struct wfst_graph_desc {
  *                  (section 8): size this for the longest stream.
  *  lattice         1: lattice mode (section 1 "Lattice mode", section 7
  *                  "Lattice"): every admitted candidate of every step is kept
- *                  as a lattice arc, and after the decode a backward pass
- *                  prunes them with output_beam (section 3); read the result
- *                  with wfst_lattice_records. Needs an epsilon-free search
- *                  (no epsilon arcs, or eps_iterations 0); no streams.
+ *                  as a lattice arc, and on graphs with epsilon arcs every
+ *                  epsilon candidate a closure pass admits (section 5.5: the
+ *                  candidate set persisted after the closure, epsilon arcs
+ *                  tagged), as an arc inside the frame the closure prepares;
+ *                  after the decode a backward pass prunes them with
+ *                  output_beam (section 3); read the result with
+ *                  wfst_lattice_records. On graphs with epsilon arcs every
+ *                  epsilon weight must be <= 0. No streams.
  *  output_beam     the lattice prune's beam (finite, >= 0): an arc survives iff
  *                  (fwd(src) + s) + bwd(dst) >= best - output_beam, with s the
- *                  arc's own score (weight + log-prob; a final arc's weight; 0 for
- *                  the redirect's virtual arc), fwd the search score of its source
- *                  token, bwd(token) the best continuation to the super-final
- *                  state (s + bwd(dst) maximised over its arcs, last step first),
- *                  best the lane's result score; binary32, in that order.
+ *                  arc's own score (weight + log-prob; a final or epsilon arc's
+ *                  weight; 0 for the redirect's virtual arc), fwd the score of
+ *                  its source token after the frame's closure, bwd(token) the
+ *                  best continuation to the super-final state (s + bwd(dst)
+ *                  maximised over its arcs, last frame first; inside a frame,
+ *                  over its epsilon arcs, to a fixpoint), best the lane's result
+ *                  score; binary32, in that order.
  *  lattice_cap     lattice arcs (and kept records) per lane per decode
  *                  (0: 2 * max_active * (max_frames + 2), at least 2^20); in
  *                  [0, 2^28]. More sets WFST_OVF_ARENA (the 1-best result is
@@ -417,11 +423,13 @@ int wfst_blank_skip(wfst_decoder_t d, const void *log_prob, int32_t B, int32_t T
  * "Lattice": flat records). *n = the number of kept arcs; the first min(*n, cap)
  * records are written to out, 8 int32 each, in no particular order:
  *   {frame t, source state, destination state (the super-final state for final
- *    and redirect arcs), ilabel (-1 final), arc id (num_arcs + state for the
- *    redirect's virtual arc), arc score bits (binary32 s), lane, flags (1 final
- *    arc, 2 redirect)}
+ *    and redirect arcs), ilabel (-1 final, the epsilon id for an epsilon arc),
+ *    arc id (num_arcs + state for the redirect's virtual arc), arc score bits
+ *    (binary32 s), lane, flags (1 final arc, 2 redirect, 4 epsilon arc)}
  * A source is the token of its state at frame t, an emitting arc's destination
- * the token of its state at frame t + 1. A lane with no result has no arcs.
+ * the token of its state at frame t + 1, an epsilon arc's the token of its
+ * state at frame t (each epsilon arc appears once per frame). A lane with no
+ * result, or whose lattice overflowed lattice_cap, has no arcs.
  * Errors: WFST_EINVAL (not lattice mode, lane outside the last decode, null),
  * WFST_EDEVICE.
  */
@@ -493,7 +501,8 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_GC_ROOTS    21  /* log compaction: the frontier's entries renumbered       */
 #define WFST_K_GC_CLEAR    22  /* log compaction: live map and counts cleared             */
 #define WFST_K_GC_END      23  /* log compaction: log end and the sealed prefix           */
-#define WFST_K_COUNT       24
+#define WFST_K_LAT_EPS_BACK 24 /* lattice: one frame's epsilon arcs, backward and prune   */
+#define WFST_K_COUNT       25
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

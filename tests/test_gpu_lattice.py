@@ -1,7 +1,9 @@
 """GPU parity of lattice mode (page section 1 "Lattice mode", section 3 on
-output_beam, section 7 "Lattice"): the kept lattice arcs of every lane, as flat
-records, equal the oracle's kept arcs bit for bit (frame, states, labels, arc
-ids, arc-score bits, flags); the 1-best results stay those of a plain decode."""
+output_beam, section 5.5 on the candidate set persisted after the closure with
+epsilon arcs tagged, section 7 "Lattice"): the kept lattice arcs of every lane,
+as flat records, equal the oracle's kept arcs bit for bit (frame, states,
+labels, arc ids, arc-score bits, flags), on epsilon-free graphs and on graphs
+with epsilon arcs; the 1-best results stay those of a plain decode."""
 
 import numpy as np
 import pytest
@@ -20,9 +22,9 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob, lane):
+def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob, lane, eps_iterations=0):
     r = oracle.decode_lane(g, lp_lane.astype(np.float32), T, beam, max_active, min_active, allow_partial,
-                           output_beam=ob)
+                           eps_iterations=eps_iterations, output_beam=ob)
     lat = r["lattice"]
     k = lat[lat[:, OF["keep"]] == 1]
     out = np.stack([k[:, OF["frame"]], k[:, OF["src"]], k[:, OF["dst"]], k[:, OF["ilabel"]], k[:, OF["arc"]],
@@ -32,23 +34,25 @@ def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob,
     return out[np.lexsort((out[:, 4], out[:, 1], out[:, 0]))] if out.shape[0] else out, r
 
 
-def lattice_case(g, lp, L, beam, ma, mi, ap, ob, dgraph=None, **caps):
+def lattice_case(g, lp, L, beam, ma, mi, ap, ob, dgraph=None, eps_iterations=0, lanes=None, **caps):
     import torch
     B, T, V = lp.shape
     own = dgraph is None
     dg = wb.Graph(g) if own else dgraph
     dec = wb.Decoder(dg, beam, ma, min_active=mi, allow_partial=ap, max_lanes=B, max_frames=max(T, 1),
-                     lp_dtype="f16" if lp.dtype == np.float16 else "f32", lattice=True, output_beam=ob, **caps)
+                     lp_dtype="f16" if lp.dtype == np.float16 else "f32", lattice=True, output_beam=ob,
+                     eps_iterations=eps_iterations, **caps)
     r = dec.decode(torch.from_numpy(np.ascontiguousarray(lp)).cuda(), L)
-    lats = [dec.lattice(b) for b in range(B)]
+    lanes = list(range(B)) if lanes is None else list(lanes)
+    lats = [dec.lattice(b) for b in lanes]
     dec.close()
     if own:
         dg.release()
-    o = oracle_lanes(g, lp, L, beam, ma, mi, ap)
-    compare_batch(r, None, o, check_steps=False)
-    for b in range(B):
-        want, _ = _oracle_kept(g, lp[b], int(L[b]), beam, ma, mi, ap, ob, b)
-        got = lats[b]
+    o = oracle_lanes(g, lp, L, beam, ma, mi, ap, eps_iterations=eps_iterations, lanes=lanes)
+    compare_batch(r, None, o, lanes=lanes, check_steps=False)
+    for j, b in enumerate(lanes):
+        want, _ = _oracle_kept(g, lp[b], int(L[b]), beam, ma, mi, ap, ob, b, eps_iterations)
+        got = lats[j]
         assert got.shape == want.shape, f"lane {b}: {got.shape[0]} kept arcs vs {want.shape[0]}"
         assert np.array_equal(got, want), f"lane {b}: lattice records differ"
     return r, lats
@@ -97,6 +101,54 @@ def test_lattice_workload(ob):
     assert all(x.shape[0] > L2[b] for b, x in enumerate(lats))
 
 
+def _random_tlg_case(seed):
+    rng = np.random.default_rng(71_000 + seed)
+    n = int(rng.integers(3, 40))
+    vocab = int(rng.integers(3, 10))
+    levels = int(rng.integers(2, 5))
+    g = synth.random_graph(seed + 13, n=n, deg=(1, int(rng.integers(2, 8))), vocab=vocab, epsilon=True,
+                           eps_levels=levels, eps_share=float(rng.choice([0.2, 0.4])))
+    B = int(rng.integers(1, 5))
+    T = int(rng.integers(0, 20))
+    lp = synth.random_logprobs(seed + 6, B, max(T, 1), vocab, sigma=float(rng.uniform(0.5, 3.0)))
+    if T == 0:
+        lp = lp[:, :0, :]
+    L = rng.integers(0, T + 1, size=B).astype(np.int32)
+    beam = float(rng.choice([1.0, 3.0, 8.0, 1e10]))
+    ma = int(rng.choice([2, 5, 50, 1000]))
+    mi = int(rng.choice([0, 0, 3]))
+    ap = bool(rng.integers(0, 2))
+    ob = float(rng.choice([0.0, 0.5, 2.0, 10.0]))
+    P = int(rng.integers(1, 5))
+    return g, lp, L, beam, ma, mi, ap, ob, P
+
+
+def test_lattice_random_tlg_graphs():
+    """Graphs with epsilon arcs (levels 2-4, 1-4 closure passes): epsilon arcs
+    persisted by every closure pass, kept records equal the oracle's."""
+    kept = eps_kept = 0
+    for seed in range(60):
+        g, lp, L, beam, ma, mi, ap, ob, P = _random_tlg_case(seed)
+        _say("lattice tlg random", seed, lp.shape, beam, ma, mi, ap, ob, P)
+        _, lats = lattice_case(g, lp, L, beam, ma, mi, ap, ob, eps_iterations=P)
+        kept += sum(x.shape[0] for x in lats)
+        eps_kept += sum(int((x[:, 7] == 4).sum()) for x in lats)
+    assert kept > 500 and eps_kept > 100
+
+
+def test_lattice_tlg_workload_full_size():
+    """The TLG workload at full size (1M states, 16 x 400 frames, 4 closure
+    passes), lattice mode with output beam 4: every lane's 1-best result and,
+    on sampled lanes, the kept records equal the oracle's bit for bit."""
+    cid = 4
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    _say("lattice tlg workload", lp.shape)
+    _, lats = lattice_case(g, lp, L, wl.beam, wl.max_active, 0, False, 4.0, eps_iterations=wl.eps_iterations,
+                           lanes=[0, 9], arena_entries=16 << 20)
+    assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
 def test_lattice_capacity_and_rejections():
     import torch
     g, lp, L, beam, ma, mi, ap, _ = _random_case(3)
@@ -111,9 +163,14 @@ def test_lattice_capacity_and_rejections():
     dec.close()
     with pytest.raises(wb.WfstError):
         wb.Decoder(dg, 8.0, 100, lattice=True, output_beam=float("inf"))
+    # a positive epsilon weight: no best continuation inside a frame
     eg = synth.random_graph(4, n=6, deg=(1, 3), vocab=4, epsilon=True, eps_levels=3)
+    eps = eg.ilabel == eg.epsilon_id
+    assert eps.any()
+    eg.weight = np.where(eps, np.float32(0.5), eg.weight).astype(np.float32)
     deg_ = wb.Graph(eg)
-    with pytest.raises(wb.WfstError):
+    with pytest.raises(wb.WfstError, match="epsilon weight"):
         wb.Decoder(deg_, 8.0, 100, eps_iterations=2, lattice=True, output_beam=1.0)
+    wb.Decoder(deg_, 8.0, 100, eps_iterations=2).close()       # (1-best decoding takes it)
     deg_.release()
     dg.release()

@@ -201,6 +201,7 @@ struct wfst_graph_s {
     uint32_t max_class_deg = 0;   // most arcs of one class leaving one state
     uint32_t dest_bits = 0;       // arc records hold the in-rank above this many state id bits (0: no ranks)
     uint32_t rank_bits = 0;       // bits of the largest in-rank
+    bool eps_positive = false;    // some epsilon arc has a weight > 0 (lattice mode refuses the graph)
     std::vector<void *> owned;
     size_t bytes = 0;
     StateInfo *sinfo = nullptr;
@@ -413,6 +414,9 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     h->max_class_deg = md;
     h->dest_bits = ranks ? db : 0u;
     h->rank_bits = ranks ? rb : 0u;
+    if (g->epsilon_id >= 0)
+        for (int32_t a = 0; a < A; ++a)
+            if (g->ilabel[a] == g->epsilon_id && g->weight[a] > 0.0f) { h->eps_positive = true; break; }
     int r = WFST_OK;
     if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
         (r = dalloc(&h->arc_dlw, (size_t)A, &h->owned, &h->bytes)) ||
@@ -492,7 +496,9 @@ static int derive_sizes(const wfst_graph_s *g, const wfst_decoder_config &c, Siz
     }
     if (c.path_cap < 0 || c.path_cap > (1 << 26)) return fail(WFST_EINVAL, "path_cap must lie in [0, 2^26]");
     if (c.lattice != 0 && c.lattice != 1) return fail(WFST_EINVAL, "lattice must be 0 or 1");
-    if (c.lattice && P > 0) return fail(WFST_EINVAL, "lattice mode needs an epsilon-free search (eps_iterations 0 or no epsilon arcs)");
+    if (c.lattice && P > 0 && g->eps_positive)
+        return fail(WFST_EINVAL, "lattice mode on a graph with epsilon arcs needs every epsilon weight <= 0 "
+                                 "(a frame's backward scores are a fixpoint over its epsilon arcs)");
     if (c.lattice && (!(c.output_beam >= 0.0f) || std::isinf(c.output_beam))) return fail(WFST_EINVAL, "output_beam must be finite and >= 0");
     if (c.lattice_cap < 0 || c.lattice_cap > (1ll << 28)) return fail(WFST_EINVAL, "lattice_cap must lie in [0, 2^28]");
     if (c.gc_interval < 0) return fail(WFST_EINVAL, "gc_interval must be >= 0");
@@ -538,6 +544,7 @@ static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &
     w.lattice = c.lattice;
     w.output_beam = c.lattice ? c.output_beam : 0.0f;
     w.lat_cap = (uint32_t)z.lat_cap;
+    w.lat_nodes = c.lattice ? (uint32_t)(z.arena + 1) : 0u;
     w.gc_interval = c.gc_interval;
     w.chg_cap = (uint32_t)std::max<uint64_t>(z.CC, z.Q);
     w.round_base = 0;
@@ -595,13 +602,17 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
         take(&w.gc_buf, L * (size_t)z.arena);
     }
     if (c.lattice) {
-        const size_t F = (size_t)c.max_frames + 3;
+        const size_t F = (size_t)c.max_frames + 3, nodes = (size_t)z.arena + 1;
         take(&w.lat_arc, L * z.lat_cap);
         take(&w.lat_aoff, L * F);
-        take(&w.lat_fbase, L * F);
-        take(&w.lat_score, L * (size_t)z.arena);
-        take(&w.lat_bwd, L * ((size_t)z.arena + 1));
+        take(&w.lat_nbase, L * F);
+        take(&w.lat_score, L * nodes);
+        take(&w.lat_state, L * nodes);
+        take(&w.lat_bwd, L * nodes);
+        take(&w.lat_epass, L * nodes);
         take(&w.lat_out, L * z.lat_cap * kLatFields);
+        if (z.P > 0)
+            for (int p = 0; p < 2; ++p) take(&w.chg_pos[p], L * std::max<uint64_t>(z.CC, Q));
     }
 }
 
@@ -739,8 +750,10 @@ static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &
     }
     if (w.lattice) {
         if ((e = go(kKLatInit, 0, 0)) != hipSuccess) return e;
-        for (int t = steps - 1; t >= 0; --t)
+        for (int t = steps - 1; t >= 0; --t) {
             if ((e = go(kKLatBack, t, 0)) != hipSuccess) return e;
+            if (passes > 0 && (e = go(kKLatEpsBack, t, 0)) != hipSuccess) return e;
+        }
     }
     return go(kKBacktrack, 0, 0);
 }

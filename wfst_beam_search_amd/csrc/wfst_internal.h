@@ -198,16 +198,24 @@ struct Work {
     int32_t *res;             // [L][res_stride] results
     uint32_t *steps;          // [L][max_frames + 2][kStepFields]
     const int32_t *plan;      // [L][kPlanFields] stream commands of the next sequence
-    // lattice mode (epsilon-free search): every admitted candidate of every step
+    // lattice mode: every admitted candidate of every step and closure pass. A
+    // lattice node is a token of one frame (after the frame's closure): node id
+    // = the frame's first node + the token's position in that frame's frontier.
     int32_t lattice;          // 1: persist and prune the lattice
     float output_beam;        // the prune's beam
     uint32_t lat_cap;         // lattice arcs (and kept records) per lane
-    int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position, 0}
-    uint32_t *lat_aoff;       // [L][max_frames + 3] first lattice arc of each step
-    uint32_t *lat_fbase;      // [L][max_frames + 3] winners-log base of each frame's tokens
-    float *lat_score;         // [L][arena] score of each winners-log entry's token
-    uint32_t *lat_bwd;        // [L][arena + 1] ordered backward score by entry (+ the start token)
+    uint32_t lat_nodes;       // lattice nodes per lane (arena + 1: every token but the start one has an entry)
+    int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position, closure pass
+                              //   (0: an arc of the step itself)}
+    uint32_t *lat_aoff;       // [L][max_frames + 3] first lattice arc of step t at [t + 1] (t = -1: the
+                              //   start closure); step t's arcs are followed by its closure's
+    uint32_t *lat_nbase;      // [L][max_frames + 3] first node of each frame
+    float *lat_score;         // [L][lat_nodes] token score of each node (after its frame's closure)
+    int32_t *lat_state;       // [L][lat_nodes] state of each node
+    uint32_t *lat_bwd;        // [L][lat_nodes] ordered backward score of each node
+    uint8_t *lat_epass;       // [L][lat_nodes] last closure pass whose sources included the node
     int32_t *lat_out;         // [L][lat_cap][kLatFields] kept records
+    int32_t *chg_pos[2];      // [L][chg_cap] frontier position of each closure source (lattice mode)
     // blank-skip pre-slicing
     int32_t *bs_src;          // [L][max_frames] source frame of each kept row
     int32_t *bs_len;          // [L] kept rows
@@ -232,7 +240,7 @@ enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
     kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
-    kKCount
+    kKLatEpsBack, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -455,9 +455,20 @@ __device__ void init_lane(const Work &w, int L, int T)
     if (w.has_eps || w.lattice) w.pos[0][(size_t)L * w.num_states + s] = 0;
     // the start closure's sources: the start token, if it has epsilon arcs
     const bool eps_src = w.eps_iterations > 0 && si.emit_b > si.eps_b;
-    if (eps_src)
+    if (eps_src) {
         w.changed[1][(size_t)L * w.chg_cap] = make_int4(si.eps_b, si.emit_b - si.eps_b, -1, (int)__float_as_uint(0.0f));
+        if (w.lattice) w.chg_pos[1][(size_t)L * w.chg_cap] = 0;
+    }
     c.nchanged[1] = eps_src ? 1ull : 0ull;
+    if (w.lattice) {
+        // frame 0's first node is the start token; the start closure's arcs
+        // open the lattice (step -1)
+        const size_t F = (size_t)w.max_frames + 3;
+        w.lat_nbase[(size_t)L * F] = 0u;
+        w.lat_aoff[(size_t)L * F] = 0u;
+        w.lat_score[(size_t)L * w.lat_nodes] = 0.0f;
+        w.lat_state[(size_t)L * w.lat_nodes] = s;
+    }
     uint32_t *st = w.strip_tok[0] + (size_t)L * w.strip_cap;
     for (uint32_t sb = 0; sb * kWave < deg && sb < w.strip_cap; ++sb) st[sb] = 0u;
     c.cnt[0] = 1ull | ((unsigned long long)deg << 32);
@@ -842,12 +853,17 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     if (ph == kPhNone) return;
     uint32_t *rec = step_rec(w, L, t);
     c.last_step = t;
-    if (w.lattice) w.lat_aoff[(size_t)L * (w.max_frames + 3) + t] = c.lat_cursor;
+    if (w.lattice) w.lat_aoff[(size_t)L * (w.max_frames + 3) + t + 1] = c.lat_cursor;
     rec[kRecN] = n;
     rec[kRecArcs] = arcs;
     if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
     if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    if (w.lattice) {
+        // frame t holds n tokens (its closure is done): frame t + 1's first node
+        const size_t F = (size_t)w.max_frames + 3;
+        w.lat_nbase[(size_t)L * F + t + 1] = w.lat_nbase[(size_t)L * F + t] + n;
+    }
     const float b = step_beam(w, c.T, c.beam[p ^ 1], t, ph, n);
     c.beam[p] = b;
     rec[kRecBeam] = __float_as_uint(b);
@@ -951,13 +967,15 @@ __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, in
 }
 
 
-// Lattice mode: the arcs the step before persisted, whose destination states
-// become positions in the frontier that step built. Its position map is still
-// that frontier's here (this compaction writes the other parity's).
+// Lattice mode: the arcs the step before persisted (its own, then its
+// closure's; the start closure's at step 0), whose destination states become
+// positions in the frontier that step built. Its position map is still that
+// frontier's here (this compaction writes the other parity's).
 struct LatTab {
     uint32_t base[kMaxLanes + 1];  // exclusive prefix of work units per lane
-    uint32_t n[kMaxLanes];         // arcs of the step before
+    uint32_t n[kMaxLanes];         // arcs of the step before (and of its closure)
     uint32_t a0[kMaxLanes];        // the first of them
+    uint32_t nb[kMaxLanes];        // first lattice node of the frame this compaction builds
 };
 
 __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, LatTab &lt)
@@ -966,15 +984,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     const LpDesc lpd = *w.lp;
     if (w.lattice && threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
-        uint32_t n = 0, a0 = 0;
-        // a lane that ran step t - 1 and began step t (whatever step t then did)
-        if (L < w.max_lanes && t >= 1 && w.ctl[L].last_step == t) {
+        uint32_t n = 0, a0 = 0, nb = 0;
+        // a lane that began step t (whatever step t then did): the arcs of step
+        // t - 1 (slot t of the offsets; step -1 is the start closure)
+        if (L < w.max_lanes && w.ctl[L].last_step == t) {
             const size_t F = (size_t)w.max_frames + 3;
-            a0 = w.lat_aoff[(size_t)L * F + t - 1];
-            const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t], w.lat_cap);
+            a0 = w.lat_aoff[(size_t)L * F + t];
+            const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
             n = a1 > a0 ? a1 - a0 : 0u;
+            nb = w.lat_nbase[(size_t)L * F + t + 1];
         }
-        if (L < w.max_lanes) { lt.n[L] = n; lt.a0[L] = a0; }
+        if (L < w.max_lanes) { lt.n[L] = n; lt.a0[L] = a0; lt.nb[L] = nb; }
         uint32_t tot;
         const uint32_t ex = wave_excl_sum((n + kWave - 1) / kWave, &tot);
         if (L < w.max_lanes) lt.base[L] = ex;
@@ -1031,7 +1051,6 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
                 c.front_base[np] = tab.arcs[L];
-                if (w.lattice) w.lat_fbase[(size_t)L * (w.max_frames + 3) + t + 1] = tab.arcs[L];
                 c.log_open = 1u;   // entries added to log_cursor by the next kernel
             }
             c.nclaims_eps[1] = 0u;
@@ -1205,10 +1224,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             pick(w.tok_abeg, np)[q] = abeg;
             pick(w.tok_ub, np)[q] = ub;
             if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
-            if (w.lattice) w.lat_score[(size_t)L * w.arena + tab.arcs[L] + pi] = end;
-            if ((ml >> lane) & 1ull)
-                w.changed[1][(size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt())] =
-                    make_int4(eps_b0, (int)eps_n, e, (int)__float_as_uint(end));
+            if (w.lattice) {
+                // the token's lattice node (its closure may still raise the score)
+                const size_t nd = (size_t)L * w.lat_nodes + lt.nb[L] + pi;
+                w.lat_score[nd] = end;
+                w.lat_state[nd] = dst;
+            }
+            if ((ml >> lane) & 1ull) {
+                const size_t ci = (size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt());
+                w.changed[1][ci] = make_int4(eps_b0, (int)eps_n, e, (int)__float_as_uint(end));
+                if (w.lattice) w.chg_pos[1][ci] = (int32_t)pi;
+            }
         }
         write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
@@ -1273,6 +1299,8 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             tab.n[L] = ns;
             tab.arcs[L] = srcs;
             tab.f1[L] = c.cutoff;
+            // lattice mode: first node of the frame being closed
+            tab.fb[L] = w.lattice ? w.lat_nbase[(size_t)L * ((size_t)w.max_frames + 3) + (size_t)(t + 1)] : 0u;
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -1301,7 +1329,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
         // the 64 sources of this unit: their epsilon ranges, entries and scores
         // as the kernel that made them wrote them
-        int32_t eb = 0, ent = -1;
+        int32_t eb = 0, ent = -1, spos = 0;
         uint32_t ed = 0;
         float sc = 0.0f;
         if (i < tab.n[L]) {
@@ -1310,6 +1338,13 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
             ed = (uint32_t)ce.y;
             ent = ce.z;
             sc = __uint_as_float((uint32_t)ce.w);
+            if (w.lattice) {
+                // the source's node: this pass relaxes its epsilon arcs (a later
+                // pass that relaxes them again admits a superset: the source's
+                // score only grows)
+                spos = w.chg_pos[k & 1][(size_t)L * w.chg_cap + i];
+                w.lat_epass[(size_t)L * w.lat_nodes + tab.fb[L] + (uint32_t)spos] = (uint8_t)k;
+            }
         }
         uint32_t dsum;
         const uint32_t dpre = wave_excl_sum(ed, &dsum);
@@ -1339,6 +1374,25 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 if (adm) {
                     ++n_adm;
                     atomicMax(&tbl[dest_state(w, ar.dest)], table_key(w, e, a, ar.dest, ep));
+                }
+            }
+            if (w.lattice) {
+                // every admitted epsilon candidate is a lattice arc of the frame
+                // being closed: {source position, arc, destination state (its
+                // position once the next compaction resolves it), pass}
+                const int32_t sps = __shfl(spos, src, kWave);
+                const unsigned long long am = __ballot(adm);
+                if (am) {
+                    const int lead = __ffsll((long long)am) - 1;
+                    uint32_t lb0 = 0u;
+                    if (lane == lead) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
+                    lb0 = __shfl(lb0, lead, kWave);
+                    if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
+                        if (lane == lead) atomicOr(&c.overflow, kOvfArena);
+                    } else if (adm) {
+                        w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
+                            make_int4(sps, a, (int32_t)dest_state(w, dd), k);
+                    }
                 }
             }
             push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, (uint32_t)sen, e);
@@ -1391,6 +1445,8 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             tab.win[L] = c.win;
             tab.f1[L] = c.cutoff;
             tab.f0[L] = (on && !fits) ? 1.0f : 0.0f;
+            // lattice mode: first node of the frame being closed
+            tab.fb[L] = w.lattice ? w.lat_nbase[(size_t)L * ((size_t)w.max_frames + 3) + (size_t)(t + 1)] : 0u;
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -1518,10 +1574,18 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         pick(w.tok_entry, fp)[q] = e;
         pick(w.tok_last, fp)[q] = dd.z;
         pick(w.tok_ub, fp)[q] = ub;
+        if (w.lattice) {
+            // the token's node (appended: a new one; replaced: its score rises)
+            const size_t nd = (size_t)L * w.lat_nodes + tab.fb[L] + pi;
+            w.lat_score[nd] = end;
+            if (isnew) w.lat_state[nd] = dst;
+        }
         if ((ml >> lane) & 1ull) {
             const uint32_t ci = cb + (uint32_t)__popcll(ml & mask_lt());
-            if (ci < w.chg_cap)
+            if (ci < w.chg_cap) {
                 w.changed[(k + 1) & 1][(size_t)L * w.chg_cap + ci] = make_int4(eb, (int)ed, e, (int)__float_as_uint(end));
+                if (w.lattice) w.chg_pos[(k + 1) & 1][(size_t)L * w.chg_cap + ci] = (int32_t)pi;
+            }
         }
     }
 }
@@ -1535,13 +1599,17 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
 
 // ------------------------------------------------------------------ lattice
 // Lattice mode (page section 1 "Lattice mode", section 3 on output_beam,
-// section 7 "Lattice"; epsilon-free search): finalize persists every admitted
-// candidate as a lattice arc {source position at frame t, arc, destination
-// state}, every winner's score by winners-log entry, and each frame's log base.
-// After the decode a backward pass over the steps (last to first) computes
-// bwd(token) = max over its arcs of s + bwd(destination) and keeps the arcs with
-// (fwd(source) + s) + bwd(destination) >= best - output_beam, where s is the
-// arc's own score (weight + log-prob; a final arc's weight; 0 for a redirect).
+// section 5.5 on persisting candidates after the closure, section 7
+// "Lattice"): finalize persists every admitted candidate of a step, each closure
+// pass every admitted epsilon candidate (tagged with its pass), as lattice arcs
+// {source position, arc, destination}; a node is a frame's token (first node of
+// the frame + its position), with its score after the frame's closure and its
+// state. After the decode a backward pass over the frames (last to first)
+// computes bwd(node) = the best s + bwd(destination) over its arcs, epsilon
+// arcs staying inside their frame (a fixpoint per frame), and keeps the arcs
+// with (fwd(source) + s) + bwd(destination) >= best - output_beam, where s is
+// the arc's own score (weight + log-prob; a final or epsilon arc's weight; 0 for
+// a redirect).
 
 // Whether lane c's lattice holds every arc its search persisted: appends past
 // lat_cap were dropped whole (arena bit) while the cursor still counted them,
@@ -1550,24 +1618,24 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
 __device__ __forceinline__ bool lat_complete(const Work &w, const LaneCtl &c) { return c.lat_cursor <= w.lat_cap; }
 
 // Before the backward pass: every backward score of a lane with a result (and
-// a complete lattice) is -inf (its winners-log entries and the start token's
-// slot).
+// a complete lattice) is -inf (nodes of frames 0 .. its last step).
 __global__ __launch_bounds__(kBlock) void k_lat_init(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t F = (size_t)w.max_frames + 3;
     for (int L = 0; L < w.max_lanes; ++L) {
         const LaneCtl &c = w.ctl[L];
-        if (!lane_has_result(c) || !lat_complete(w, c)) continue;
-        const size_t n = min(c.log_cursor, w.arena);
-        uint32_t *b = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
+        if (!lane_has_result(c) || !lat_complete(w, c) || c.last_step < 0) continue;
+        const size_t n = min(w.lat_nbase[(size_t)L * F + (size_t)c.last_step + 1], w.lat_nodes);
+        uint32_t *b = w.lat_bwd + (size_t)L * w.lat_nodes;
         for (size_t i = tid; i < n; i += stride) b[i] = kOrdNegInf;
-        if (tid == 0) b[w.arena] = kOrdNegInf;
     }
 }
 
-// Backward pass over the arcs of step t (launched for t = last .. 0).
+// Backward pass over the arcs of step t itself (launched for t = last .. 0;
+// the epsilon arcs of its closure belong to frame t + 1, done before).
 template <typename LPT>
 __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp, int t)
 {
@@ -1582,8 +1650,8 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
             const LaneCtl &c = w.ctl[L];
             const bool on = lane_has_result(c) && t <= c.last_step && lat_complete(w, c);
             const bool fin = t == c.last_step;   // the lane's final step (or its redirect)
-            const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
-            const uint32_t a1 = min(fin ? c.lat_cursor : w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
+            const uint32_t a0 = w.lat_aoff[(size_t)L * F + t + 1];
+            const uint32_t a1 = min(fin ? c.lat_cursor : w.lat_aoff[(size_t)L * F + t + 2], w.lat_cap);
             const uint32_t n = (on && a1 > a0) ? a1 - a0 : 0u;
             units = (n + kWave - 1) / kWave;
             tab.n[L] = n;
@@ -1591,8 +1659,8 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
             tab.ph[L] = fin ? 1 : 0;
             tab.f1[L] = c.final_score - w.output_beam;
             tab.row[L] = c.lp_row;
-            tab.arcs[L] = t > 0 ? w.lat_fbase[(size_t)L * F + t] : 0u;                 // frame t's log base
-            tab.win[L] = (int32_t)(fin ? 0u : w.lat_fbase[(size_t)L * F + t + 1]);    // frame t + 1's
+            tab.arcs[L] = on ? w.lat_nbase[(size_t)L * F + t] : 0u;                      // frame t's first node
+            tab.win[L] = (int32_t)((on && !fin) ? w.lat_nbase[(size_t)L * F + t + 1] : 0u);   // frame t + 1's
         }
         tab_publish(tab, w.max_lanes, units);
     }
@@ -1604,13 +1672,13 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
-        const bool valid = i < tab.n[L];
         const bool fin = tab.ph[L] != 0;
-        uint32_t *bwd = w.lat_bwd + (size_t)L * ((size_t)w.arena + 1);
+        uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes;
         bool keep = false;
         int32_t rec[kLatFields];
-        if (valid) {
-            const int4 r = w.lat_arc[(size_t)L * w.lat_cap + tab.fb[L] + i];
+        int4 r = make_int4(0, 0, 0, 1);
+        if (i < tab.n[L]) r = w.lat_arc[(size_t)L * w.lat_cap + tab.fb[L] + i];
+        if (r.w == 0) {   // (epsilon arcs of the step's closure, and lanes past their arcs, skip)
             const int32_t arc = r.y;
             const bool redirect = (uint32_t)arc >= (uint32_t)w.num_arcs;
             ArcDLW ad = {0, 0u, 0.0f};
@@ -1622,19 +1690,16 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
                 const LPT *row = (const LPT *)d.base + (long long)tab.row[L] * d.stride_b + (long long)t * d.stride_t;
                 sa = ad.weight + lp_at(row, ad.ilabel);
             }
-            const uint32_t srcpos = (uint32_t)r.x;
-            const size_t se = t > 0 ? (size_t)tab.arcs[L] + srcpos : (size_t)w.arena;   // source slot
+            const size_t se = (size_t)tab.arcs[L] + (uint32_t)r.x;   // source node
             const float bd = fin ? 0.0f : ord2f(bwd[(uint32_t)tab.win[L] + (uint32_t)r.z]);
             const float v = sa + bd;
             if (v > -__builtin_inff()) atomicMax(&bwd[se], f2ord(v));
-            const float fwd = t > 0 ? w.lat_score[(size_t)L * w.arena + se] : 0.0f;
+            const float fwd = w.lat_score[(size_t)L * w.lat_nodes + se];
             const float thr = (fwd + sa) + bd;
             keep = thr >= tab.f1[L];
             if (keep) {
-                int32_t src_state = w.start_state;
-                if (t > 0) src_state = (int32_t)dest_state(w, w.arc_dlw[w.wlog[(size_t)L * w.arena + se].y].dest);
                 rec[kLatFrame] = t;
-                rec[kLatSrc] = src_state;
+                rec[kLatSrc] = w.lat_state[(size_t)L * w.lat_nodes + se];
                 rec[kLatDst] = (redirect || fin) ? w.super_final : (int32_t)dest_state(w, ad.dest);
                 rec[kLatIlabel] = fin ? -1 : (int32_t)ad.ilabel;
                 rec[kLatArc] = arc;
@@ -1658,6 +1723,79 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
                 for (int f = 0; f < kLatFields; ++f) o[f] = rec[f];
             }
         }
+    }
+}
+
+// Backward pass over frame t's epsilon arcs (its closure's: stored after step
+// t - 1's own arcs, or first of all for frame 0), launched after k_lat_back(t):
+// one workgroup per lane relaxes bwd(src) = max(bwd(src), w + bwd(dst)) over
+// them in rounds until a round changes nothing (the least fixpoint: epsilon
+// weights are <= 0 in lattice mode, so it exists and rounds end; a bound of one
+// round per arc + 1 ends them in any case), then keeps each arc once: from the
+// pass that last relaxed its source (that pass admitted every arc an earlier
+// one did, the source's score having only grown).
+constexpr int kLatEpsBlock = 1024;
+
+__device__ __forceinline__ uint32_t load_bwd(const uint32_t *p)
+{
+    // (other threads of the workgroup raise these with atomics: read past L1)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kLatEpsBlock) void k_lat_eps_back(const Work *__restrict__ wp, int t)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    if (!lane_has_result(c) || t > c.last_step || !lat_complete(w, c)) return;
+    const size_t F = (size_t)w.max_frames + 3;
+    const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
+    const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
+    if (a1 <= a0) return;
+    const uint32_t n = a1 - a0;
+    const uint32_t nb = w.lat_nbase[(size_t)L * F + t];
+    const int4 *rec = w.lat_arc + (size_t)L * w.lat_cap + a0;
+    uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes;
+    __shared__ int changed;
+    for (uint32_t round = 0; round <= n + 1u; ++round) {
+        if (threadIdx.x == 0) changed = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const int4 r = rec[i];
+            if (r.w == 0) continue;
+            const float v = w.arc_dlw[r.y].weight + ord2f(load_bwd(&bwd[nb + (uint32_t)r.z]));
+            if (!(v > -__builtin_inff())) continue;
+            const uint32_t o = f2ord(v);
+            if (atomicMax(&bwd[nb + (uint32_t)r.x], o) < o) changed = 1;
+        }
+        __syncthreads();
+        const int ch = changed;
+        __syncthreads();
+        if (!ch) break;
+    }
+    const float thr_min = c.final_score - w.output_beam;
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int4 r = rec[i];
+        if (r.w == 0) continue;
+        const size_t se = (size_t)L * w.lat_nodes + nb + (uint32_t)r.x;
+        if ((int)w.lat_epass[se] != r.w) continue;   // (a repeat of the source's last relaxation)
+        const ArcDLW ad = w.arc_dlw[r.y];
+        const float sa = ad.weight;
+        const float bd = ord2f(load_bwd(&bwd[nb + (uint32_t)r.z]));
+        const float thr = (w.lat_score[se] + sa) + bd;
+        if (!(thr >= thr_min)) continue;
+        const uint32_t oi = atomicAdd(&c.lat_out_n, 1u);
+        if (oi >= w.lat_cap) continue;
+        int32_t *o = w.lat_out + ((size_t)L * w.lat_cap + oi) * kLatFields;
+        o[kLatFrame] = t;
+        o[kLatSrc] = w.lat_state[se];
+        o[kLatDst] = (int32_t)dest_state(w, ad.dest);
+        o[kLatIlabel] = (int32_t)ad.ilabel;
+        o[kLatArc] = r.y;
+        o[kLatScore] = (int32_t)__float_as_uint(sa);
+        o[kLatLane] = L;
+        o[kLatFlags] = 4;
     }
 }
 
@@ -2341,6 +2479,7 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKGcRoots: go(k_gc_roots, G, B, s, e0, e1, dw); break;
     case kKGcClear: go(k_gc_clear, G, B, s, e0, e1, dw); break;
     case kKGcEnd: go(k_gc_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
+    case kKLatEpsBack: go(k_lat_eps_back, dim3(w.max_lanes), dim3(kLatEpsBlock), s, e0, e1, dw, t); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
