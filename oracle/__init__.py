@@ -49,7 +49,8 @@ class _Config(ctypes.Structure):
 
 class _Lattice(ctypes.Structure):
     _fields_ = [("output_beam", ctypes.c_float), ("cap", ctypes.c_int64), ("n", ctypes.c_int64),
-                ("rec", ctypes.c_void_p), ("vals", ctypes.c_void_p)]
+                ("rec", ctypes.c_void_p), ("vals", ctypes.c_void_p), ("prune_interval", ctypes.c_int32),
+                ("max_live", ctypes.c_int64)]
 
 
 LAT_FIELDS = ("frame", "src", "dst", "ilabel", "arc", "score_bits", "keep", "flags")
@@ -111,7 +112,7 @@ class OracleGraph:
 
 def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active: int,
                 min_active: int = 0, allow_partial: bool = False, eps_iterations: int = 0,
-                online: bool = False, partial: bool = False, output_beam=None):
+                online: bool = False, partial: bool = False, output_beam=None, lat_prune_interval: int = 0):
     """Decode one utterance. ``lp_lane`` is [T, V] (float32, or float16 widened exactly).
 
     ``online``: streaming semantics (no "last ~5 frames" raise of min_active).
@@ -121,6 +122,8 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
     [n, 8], fields ``LAT_FIELDS``, every admitted arc with its keep bit; on graphs
     with epsilon arcs also every epsilon arc a closure admitted, flags 4, once per
     frame) and ``lattice_vals`` (float32 [n, 3]: fwd(src), arc score, bwd(dst)).
+    ``lat_prune_interval``: N > 0 prunes the lattice every N steps (window-loose,
+    section 7); adds ``lattice_max_live``, the most arcs held at once.
 
     Returns a dict: score (float32), reached_final, dead, arcs, words (int32 arrays),
     steps (int64 [n_steps, 16], fields ``FIELDS``), start_closure, log_entries.
@@ -147,7 +150,7 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
         if output_beam is not None:
             rec = np.zeros((max(cap, 1), 8), dtype=np.int32)
             vals = np.zeros((max(cap, 1), 3), dtype=np.float32)
-            lat = _Lattice(float(output_beam), cap, 0, rec.ctypes.data, vals.ctypes.data)
+            lat = _Lattice(float(output_beam), cap, 0, rec.ctypes.data, vals.ctypes.data, int(lat_prune_interval), 0)
         rc = lib.wo_decode(ctypes.byref(og.c), ctypes.byref(cfg), lp.ctypes.data if lp.size else None,
                            length, int(lp.shape[1]), arcs.ctypes.data, arcs_cap, words.ctypes.data,
                            arcs_cap, steps.ctypes.data, steps_cap, ctypes.byref(res),
@@ -161,7 +164,7 @@ def decode_lane(graph, lp_lane: np.ndarray, length: int, beam: float, max_active
         raise RuntimeError("oracle output larger than its buffers")
     extra = {}
     if lat is not None:
-        extra = dict(lattice=rec[:lat.n].copy(), lattice_vals=vals[:lat.n].copy())
+        extra = dict(lattice=rec[:lat.n].copy(), lattice_vals=vals[:lat.n].copy(), lattice_max_live=int(lat.max_live))
     return dict(**extra, score=np.float32(res.score), reached_final=int(res.reached_final),
                 dead=int(res.dead), arcs=arcs[:res.n_arcs].copy(),
                 words=words[:res.n_words].copy(), steps=steps[:res.n_steps].copy(),

@@ -98,6 +98,8 @@ typedef struct {
     int64_t n;           /* lattice arcs (true count, may exceed cap) */
     int32_t *rec;        /* [cap][8] */
     float *vals;         /* [cap][3] */
+    int32_t prune_interval; /* > 0: the interval prune of section 7 every that many steps (wo_decode) */
+    int64_t max_live;    /* out: most lattice arcs held at once during the search */
 } wo_lattice;
 
 /* ---- ordering key: greater = better (higher score, then smaller arc id) ---- */
@@ -374,6 +376,7 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
     wo_fvec lt_score = {0}, la_s = {0};
     int64_t *lt_off = NULL, *la_off = NULL;
     int64_t *le_beg = NULL, *le_end = NULL;   /* epsilon lattice arcs of frame f: [le_beg[f], le_end[f]) */
+    int32_t *pmap = NULL;                     /* interval prune: state -> token index of one frame */
     int32_t lat_steps = 0;
     int rc = -1;
     int32_t final_entry = -1;
@@ -401,6 +404,13 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
             sc.lat = 1;
             sc.eps_seen = calloc((size_t)(g->num_arcs > 0 ? g->num_arcs : 1), 4);
             if (!sc.eps_seen) goto out;
+        }
+        lat->max_live = 0;
+        if (lat->prune_interval < 0) { rc = -2; goto out; }
+        if (lat->prune_interval > 0) {
+            pmap = malloc((size_t)g->num_states * 4);
+            if (!pmap) goto out;
+            for (int32_t st = 0; st < g->num_states; st++) pmap[st] = -1;
         }
     }
     sc.tok_of_state = malloc((size_t)g->num_states * 4);
@@ -585,7 +595,111 @@ int wo_decode(const wo_graph *g, const wo_config *cfg, const float *lp, int32_t 
         rec[WO_N_NEXT] = cur.n;
         if (res->n_steps < steps_cap) memcpy(steps + (int64_t)res->n_steps * WO_FIELDS, rec, sizeof(rec));
         res->n_steps++;
+        if (lat && la_src.n + sc.le_src.n > lat->max_live) lat->max_live = la_src.n + sc.le_src.n;
+
+        /*
+         * Interval prune (section 7: lat_prune_interval = N, a window-loose
+         * prune that bounds the lattice while the exact final pass stays as it
+         * is). Reading: after every N-th real step that is not the last one,
+         * with F = t + 1 the frontier's frame and W = max(0, F - 2N), backward
+         * scores over frames W .. F - 1 are computed as in the final pass but
+         * from bwd(u) = -fwd(u) for every frontier token u (no complete path
+         * through u can score more than the final best, so fwd(u) + bwd(u) is
+         * at most best - fwd(u) + fwd(u)); the arcs of steps W .. F - 1 and the
+         * epsilon arcs of frames W .. F - 1 with (fwd(src) + s) + bwd(dst) <
+         * 0 - output_beam are removed: the final test, which subtracts the
+         * same output beam from the best, could not keep them (exactly so in
+         * exact arithmetic). Survivors keep their order.
+         */
+        if (lat && lat->prune_interval > 0 && (t + 1) % lat->prune_interval == 0 && t + 1 < T) {
+            const int32_t F = t + 1;
+            const int32_t W = F - 2 * lat->prune_interval > 0 ? F - 2 * lat->prune_interval : 0;
+            const float thr_loose = 0.0f - lat->output_beam;
+            const int64_t ea0 = la_off[W], ea1 = la_src.n;
+            const int64_t xa0 = sc.lat ? le_beg[W] : 0, xa1 = sc.lat ? sc.le_src.n : 0;
+            uint8_t *keep_e = malloc((size_t)(ea1 - ea0 + 1));
+            uint8_t *keep_x = malloc((size_t)(xa1 - xa0 + 1));
+            float *bnext = malloc((size_t)(cur.n > 0 ? cur.n : 1) * 4);
+            if (!keep_e || !keep_x || !bnext) { free(keep_e); free(keep_x); free(bnext); goto out; }
+            memset(keep_e, 1, (size_t)(ea1 - ea0 + 1));
+            memset(keep_x, 1, (size_t)(xa1 - xa0 + 1));
+            for (int64_t i = 0; i < cur.n; i++) bnext[i] = -cur.score[i];
+            for (int32_t f = F - 1; f >= W; f--) {
+                const int64_t fa = lt_off[f], fb = (f + 1 <= t) ? lt_off[f + 1] : lt_state.n;
+                const int64_t nf = fb - fa;
+                const int64_t k0 = la_off[f], k1 = (f + 1 <= t) ? la_off[f + 1] : la_src.n;
+                float *b = malloc((size_t)(nf > 0 ? nf : 1) * 4);
+                if (!b) { free(keep_e); free(keep_x); free(bnext); goto out; }
+                for (int64_t i = 0; i < nf; i++) b[i] = -INFINITY;
+                /* destinations: frame f + 1's tokens (the frontier's own map at F) */
+                if (f + 1 < F)
+                    for (int64_t j = lt_off[f + 1]; j < ((f + 2 <= t) ? lt_off[f + 2] : lt_state.n); j++)
+                        pmap[lt_state.v[j]] = (int32_t)(j - lt_off[f + 1]);
+                for (int64_t k = k0; k < k1; k++) {
+                    const int32_t i = la_src.v[k], a = la_arc.v[k];
+                    const float sa = la_s.v[k];
+                    const float bd = bnext[f + 1 < F ? pmap[g->dest[a]] : sc.tok_of_state[g->dest[a]]];
+                    const float v = sa + bd;
+                    if (v > b[i]) b[i] = v;
+                    keep_e[k - ea0] = ((lt_score.v[fa + i] + sa) + bd) >= thr_loose;
+                }
+                if (f + 1 < F)
+                    for (int64_t j = lt_off[f + 1]; j < ((f + 2 <= t) ? lt_off[f + 2] : lt_state.n); j++)
+                        pmap[lt_state.v[j]] = -1;
+                if (sc.lat && le_end[f] > le_beg[f]) {
+                    for (int64_t j = fa; j < fb; j++) pmap[lt_state.v[j]] = (int32_t)(j - fa);
+                    for (int changed = 1; changed;) {
+                        changed = 0;
+                        for (int64_t k = le_beg[f]; k < le_end[f]; k++) {
+                            const int32_t i = sc.le_src.v[k], a = sc.le_arc.v[k];
+                            const float v = g->weight[a] + b[pmap[g->dest[a]]];
+                            if (v > b[i]) { b[i] = v; changed = 1; }
+                        }
+                    }
+                    for (int64_t k = le_beg[f]; k < le_end[f]; k++) {
+                        const int32_t i = sc.le_src.v[k], a = sc.le_arc.v[k];
+                        keep_x[k - xa0] = ((lt_score.v[fa + i] + g->weight[a]) + b[pmap[g->dest[a]]]) >= thr_loose;
+                    }
+                    for (int64_t j = fa; j < fb; j++) pmap[lt_state.v[j]] = -1;
+                }
+                free(bnext);
+                bnext = b;
+            }
+            free(bnext);
+            /* compaction: the steps' own arcs, then the epsilon arcs (frame F's
+             * all stay: its closure belongs to the next window) */
+            {
+                int64_t o = ea0;
+                for (int32_t f = W; f < F; f++) {
+                    const int64_t k0 = la_off[f], k1 = (f + 1 <= t) ? la_off[f + 1] : ea1;
+                    la_off[f] = o;
+                    for (int64_t k = k0; k < k1; k++)
+                        if (keep_e[k - ea0]) {
+                            la_src.v[o] = la_src.v[k]; la_arc.v[o] = la_arc.v[k]; la_s.v[o] = la_s.v[k];
+                            o++;
+                        }
+                }
+                la_src.n = la_arc.n = la_s.n = o;
+            }
+            if (sc.lat) {
+                int64_t o = xa0;
+                for (int32_t f = W; f <= F; f++) {
+                    const int64_t k0 = le_beg[f], k1 = le_end[f];
+                    le_beg[f] = o;
+                    for (int64_t k = k0; k < k1; k++)
+                        if (f == F || keep_x[k - xa0]) {
+                            sc.le_src.v[o] = sc.le_src.v[k]; sc.le_arc.v[o] = sc.le_arc.v[k];
+                            o++;
+                        }
+                    le_end[f] = o;
+                }
+                sc.le_src.n = sc.le_arc.n = o;
+            }
+            free(keep_e);
+            free(keep_x);
+        }
     }
+    if (lat && la_src.n + sc.le_src.n > lat->max_live) lat->max_live = la_src.n + sc.le_src.n;
 
     /*
      * Lattice backward pass and output_beam prune (section 3: forward[src] + arc +
@@ -732,7 +846,7 @@ out:
     free(sc.tok_of_state); free(sc.best_key); free(sc.best_src); free(sc.touched.v);
     free(lt_state.v); free(la_src.v); free(la_arc.v); free(lt_score.v); free(la_s.v);
     free(lt_off); free(la_off); free(le_beg); free(le_end);
-    free(sc.eps_seen); free(sc.le_src.v); free(sc.le_arc.v);
+    free(sc.eps_seen); free(sc.le_src.v); free(sc.le_arc.v); free(pmap);
     return rc;
 }
 

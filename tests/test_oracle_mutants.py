@@ -60,6 +60,12 @@ MUTANTS = {
     # to a fixpoint, each recorded once per frame
     "lattice_eps_one_round": [("for (int changed = 1; changed;) {", "for (int changed = 1; changed; changed = 0) {", 1)],
     "lattice_eps_no_dedupe": [("if (sc->lat && sc->eps_seen[a] != sc->frame + 1) {", "if (sc->lat) {", 1)],
+    # section 7 interval prune, reading R32: the frontier's continuation bound is
+    # -fwd, and an arc exactly at the loose threshold stays
+    "interval_prune_zero_bound": [("for (int64_t i = 0; i < cur.n; i++) bnext[i] = -cur.score[i];",
+                                   "for (int64_t i = 0; i < cur.n; i++) bnext[i] = 0.0f;", 1)],
+    "interval_prune_strict": [("keep_e[k - ea0] = ((lt_score.v[fa + i] + sa) + bd) >= thr_loose;",
+                               "keep_e[k - ea0] = ((lt_score.v[fa + i] + sa) + bd) > thr_loose;", 1)],
 }
 
 
@@ -106,6 +112,8 @@ def _pin_calls():
         ("lattice_ties", pins.test_lattice_keep_at_exact_ties),
         ("eps_lattice_paths", pins.test_eps_lattice_at_infinite_beam_is_every_path_within_output_beam),
         ("eps_lattice_bwd", pins.test_eps_lattice_backward_scores_are_best_continuations),
+        ("interval_prune", lambda: pins.test_interval_prune_keeps_the_final_keep_set(False)),
+        ("interval_prune_eps", lambda: pins.test_interval_prune_keeps_the_final_keep_set(True)),
     ]
     return calls
 

@@ -613,6 +613,63 @@ def test_eps_lattice_refuses_positive_epsilon_weights():
         _lat(g, lp, max(T, 1), 5.0, 50, 1.0, eps_iterations=2)
 
 
+def _kept(r):
+    return {(int(x[LF["frame"]]), int(x[LF["arc"]])) for x in r["lattice"] if x[LF["keep"]]}
+
+
+@pytest.mark.parametrize("eps", [False, True])
+def test_interval_prune_keeps_the_final_keep_set(eps):
+    """Section 7 (lat_prune_interval: a window-loose interval prune, the exact
+    final pass unchanged), reading R32: on a 1/8 grid every sum is exact, so an
+    arc the interval prune removes fails the final test whatever the future
+    holds; the final kept set, records and values included, is the same with
+    pruning every 1, 2 or 3 steps as without, on pruned searches (finite beam)
+    and at every output beam tried; arcs are only ever removed."""
+    compared = 0
+    for seed in range(1400, 1480):
+        g, lp, T = _tiny(seed, eps)
+        if T < 2:
+            continue
+        g, lp = _grid(g, lp, seed)
+        P = 2 if eps else 0
+        for beam, ob in ((2.0, 0.0), (4.0, 0.5), (INF_BEAM, 1.0)):
+            base = _lat(g, lp, T, beam, 50, ob, eps_iterations=P)
+            if base["reached_final"] != 1:
+                continue
+            keep0 = base["lattice"][base["lattice"][:, LF["keep"]] == 1]
+            for n in (1, 2, 3):
+                r = _lat(g, lp, T, beam, 50, ob, eps_iterations=P, lat_prune_interval=n)
+                assert r["score"] == base["score"] and np.array_equal(r["arcs"], base["arcs"])
+                keep = r["lattice"][r["lattice"][:, LF["keep"]] == 1]
+                o0 = np.lexsort((keep0[:, LF["arc"]], keep0[:, LF["frame"]]))
+                o1 = np.lexsort((keep[:, LF["arc"]], keep[:, LF["frame"]]))
+                assert np.array_equal(keep[o1], keep0[o0]), (seed, beam, ob, n)
+                assert r["lattice"].shape[0] <= base["lattice"].shape[0]
+                compared += keep.shape[0]
+    assert compared > 300
+
+
+def test_interval_prune_bounds_the_live_lattice():
+    """Reading R32: with pruning every N steps the arcs held at once grow with
+    the utterance only about as fast as the arcs within output_beam of the
+    local best do, a fraction of the growth without pruning (every admitted
+    arc); the kept set is the same (pruned search on random graphs, lanes of 200
+    and 400 frames)."""
+    for gs in (5, 7):
+        g = synth.random_graph(gs, n=30, deg=(1, 6), vocab=6, self_loop=0.3)
+        lp = synth.random_logprobs(6, 1, 400, g.vocab, sigma=2.0)[0]
+        live = {}
+        for T in (200, 400):
+            for n in (0, 8):
+                r = _lat(g, lp, T, 6.0, 100, 2.0, lat_prune_interval=n)
+                assert r["reached_final"] == 1
+                live[T, n] = r["lattice_max_live"]
+                if n:
+                    assert _kept(r) == _kept(_lat(g, lp, T, 6.0, 100, 2.0)), (gs, T)
+        assert live[400, 8] < live[400, 0] / 4, gs
+        assert live[400, 8] - live[200, 8] < (live[400, 0] - live[200, 0]) / 4, gs
+
+
 # ------------------------------------------------------------ blank-skip slicing
 
 def _blank_lp(case, V=3):
