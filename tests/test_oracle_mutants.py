@@ -55,10 +55,10 @@ MUTANTS = {
                                      "                if (!is_final) end = end + row[g->ilabel[a]];", 2)],
     # section 3 on output_beam: keep at >=, and the backward score adds the arc's
     "lattice_keep_strict": [("r[6] = thr >= thresh ? 1 : 0;", "r[6] = thr > thresh ? 1 : 0;", 2)],
-    "lattice_backward_drops_arc": [("const float v = sa + bd;", "const float v = bd;", 1)],
+    "lattice_backward_drops_arc": [("const float v = sa + bd;", "const float v = bd;", 2)],
     # section 5.5 lattice persistence, reading R31: a frame's epsilon arcs relaxed
     # to a fixpoint, each recorded once per frame
-    "lattice_eps_one_round": [("for (int changed = 1; changed;) {", "for (int changed = 1; changed; changed = 0) {", 1)],
+    "lattice_eps_one_round": [("for (int changed = 1; changed;) {", "for (int changed = 1; changed; changed = 0) {", 2)],
     "lattice_eps_no_dedupe": [("if (sc->lat && sc->eps_seen[a] != sc->frame + 1) {", "if (sc->lat) {", 1)],
     # section 7 interval prune, reading R32: the frontier's continuation bound is
     # -fwd, and an arc exactly at the loose threshold stays
