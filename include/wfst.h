@@ -151,10 +151,21 @@ typedef struct wfst_graph_desc {
  *                  maximised over its arcs, last frame first; inside a frame,
  *                  over its epsilon arcs, to a fixpoint), best the lane's result
  *                  score; binary32, in that order.
- *  lattice_cap     lattice arcs (and kept records) per lane per decode
+ *  lattice_cap     lattice arcs held (and kept records) per lane per decode
  *                  (0: 2 * max_active * (max_frames + 2), at least 2^20); in
  *                  [0, 2^28]. More sets WFST_OVF_ARENA (the 1-best result is
- *                  still exact).
+ *                  still exact). A lattice also holds max(arena_entries,
+ *                  lattice_cap) + 1 nodes (tokens) per lane; more (possible
+ *                  only with gc_interval > 0) sets the same bit.
+ *  lat_prune_interval  0: none. N in [1, 512] (lattice mode): section 7's
+ *                  interval prune, window-loose: after every N steps that are
+ *                  not a lane's last, backward scores over the last 2N frames
+ *                  are computed from -fwd at the frontier (no complete path
+ *                  through a frontier token can beat the final best), and arcs
+ *                  with (fwd(src) + s) + bwd(dst) < 0 - output_beam are dropped
+ *                  (the final test could not keep them, in exact arithmetic);
+ *                  lattice_cap then bounds the arcs held at once, not all
+ *                  admitted ones. The final pass is unchanged.
  *  gc_interval     0: the winners log keeps every entry of a decode (arena_entries
  *                  per lane must hold them all). n > 0: after every n steps, and
  *                  at the end of each stream chunk, a compaction round keeps only
@@ -162,7 +173,8 @@ typedef struct wfst_graph_desc {
  *                  the log then holds the path all tokens share (about one entry
  *                  per frame) plus the recent tree, so a small arena_entries
  *                  serves long utterances and streams. Results are identical.
- *                  Not with lattice mode. With n > 0 arena_entries defaults to
+ *                  Lattice mode may use it (lattice nodes are frame positions,
+ *                  never log entries). With n > 0 arena_entries defaults to
  *                  max(2^20, 8 * max_active * (n + 2) * (1 + eps passes)).
  *  arena_commit    how much of the winners-log regions is backed by memory
  *                  (page section 6.2, lazily committed regions): the whole
@@ -204,6 +216,7 @@ typedef struct wfst_decoder_config {
     int32_t gc_interval;
     int64_t arena_commit;
     int32_t epoch_period;
+    int32_t lat_prune_interval;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -502,7 +515,8 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_GC_CLEAR    22  /* log compaction: live map and counts cleared             */
 #define WFST_K_GC_END      23  /* log compaction: log end and the sealed prefix           */
 #define WFST_K_LAT_EPS_BACK 24 /* lattice: one frame's epsilon arcs, backward and prune   */
-#define WFST_K_COUNT       25
+#define WFST_K_LAT_PRUNE   25  /* lattice: interval prune of the last 2N frames's arcs     */
+#define WFST_K_COUNT       26
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

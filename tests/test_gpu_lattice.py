@@ -22,9 +22,10 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob, lane, eps_iterations=0):
+def _oracle_kept(g, lp_lane, T, beam, max_active, min_active, allow_partial, ob, lane, eps_iterations=0,
+                 lat_prune_interval=0):
     r = oracle.decode_lane(g, lp_lane.astype(np.float32), T, beam, max_active, min_active, allow_partial,
-                           eps_iterations=eps_iterations, output_beam=ob)
+                           eps_iterations=eps_iterations, output_beam=ob, lat_prune_interval=lat_prune_interval)
     lat = r["lattice"]
     k = lat[lat[:, OF["keep"]] == 1]
     out = np.stack([k[:, OF["frame"]], k[:, OF["src"]], k[:, OF["dst"]], k[:, OF["ilabel"]], k[:, OF["arc"]],
@@ -51,7 +52,8 @@ def lattice_case(g, lp, L, beam, ma, mi, ap, ob, dgraph=None, eps_iterations=0, 
     o = oracle_lanes(g, lp, L, beam, ma, mi, ap, eps_iterations=eps_iterations, lanes=lanes)
     compare_batch(r, None, o, lanes=lanes, check_steps=False)
     for j, b in enumerate(lanes):
-        want, _ = _oracle_kept(g, lp[b], int(L[b]), beam, ma, mi, ap, ob, b, eps_iterations)
+        want, _ = _oracle_kept(g, lp[b], int(L[b]), beam, ma, mi, ap, ob, b, eps_iterations,
+                               caps.get("lat_prune_interval", 0))
         got = lats[j]
         assert got.shape == want.shape, f"lane {b}: {got.shape[0]} kept arcs vs {want.shape[0]}"
         assert np.array_equal(got, want), f"lane {b}: lattice records differ"
@@ -147,6 +149,63 @@ def test_lattice_tlg_workload_full_size():
     _, lats = lattice_case(g, lp, L, wl.beam, wl.max_active, 0, False, 4.0, eps_iterations=wl.eps_iterations,
                            lanes=[0, 9], arena_entries=16 << 20)
     assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
+def test_lattice_interval_prune_random():
+    """Section 7's interval prune (reading R32), every 1, 2, 3 or 5 steps, on
+    random epsilon-free and TLG graphs: the kept records equal the oracle's with
+    the same interval bit for bit."""
+    kept = 0
+    for seed in range(40):
+        n = (1, 2, 3, 5)[seed % 4]
+        if seed % 2:
+            g, lp, L, beam, ma, mi, ap, ob, P = _random_tlg_case(200 + seed)
+        else:
+            g, lp, L, beam, ma, mi, ap, ob = _random_case(200 + seed)
+            P = 0
+        _say("lattice interval prune", seed, n, lp.shape, beam, ma, ob, P)
+        _, lats = lattice_case(g, lp, L, beam, ma, mi, ap, ob, eps_iterations=P, lat_prune_interval=n)
+        kept += sum(x.shape[0] for x in lats)
+    assert kept > 300
+
+
+def _long_case():
+    g = synth.random_graph(5, n=30, deg=(1, 6), vocab=6, self_loop=0.3)
+    lp = synth.random_logprobs(6, 2, 400, g.vocab, sigma=2.0)
+    return g, lp, np.array([400, 371], dtype=np.int32)
+
+
+def test_lattice_interval_prune_bounds_the_arena():
+    """A 400-frame lane admits ~11k lattice arcs; with lattice_cap 4000 the
+    lattice overflows without the interval prune (arena bit, no records) and
+    fits with a prune every 8 steps, its kept records equal to the oracle's."""
+    import torch
+    g, lp, L = _long_case()
+    dg = wb.Graph(g)
+    try:
+        dec = wb.Decoder(dg, 6.0, 100, max_lanes=2, max_frames=400, lattice=True, output_beam=2.0, lattice_cap=4000)
+        r = dec.decode(torch.from_numpy(lp).cuda(), L)
+        assert all(int(r.meta[b, 2]) & 4 for b in range(2)) and dec.lattice(0).shape[0] == 0
+        dec.close()
+        _, lats = lattice_case(g, lp, L, 6.0, 100, 0, False, 2.0, dgraph=dg, lattice_cap=4000, lat_prune_interval=8)
+        assert all(x.shape[0] > 400 for x in lats)
+    finally:
+        dg.release()
+
+
+def test_lattice_with_log_compaction():
+    """Log compaction rounds in lattice mode (section 6.3): lattice nodes are
+    frame positions, never winners-log entries, so rounds every 16 steps leave
+    the kept records and the 1-best results those of the oracle, with and
+    without the interval prune, while a winners log of 3000 entries per lane
+    (the whole decode appends about 6300) suffices."""
+    g, lp, L = _long_case()
+    for n in (0, 8):
+        _say("lattice with compaction", n)
+        r, lats = lattice_case(g, lp, L, 6.0, 100, 0, False, 2.0, gc_interval=16, arena_entries=3000,
+                               lat_prune_interval=n)
+        assert all(int(r.meta[b, 2]) == 0 for b in range(2))
+        assert all(x.shape[0] > 400 for x in lats)
 
 
 def test_lattice_capacity_and_rejections():

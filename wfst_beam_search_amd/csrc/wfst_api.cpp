@@ -503,7 +503,8 @@ static int derive_sizes(const wfst_graph_s *g, const wfst_decoder_config &c, Siz
     if (c.lattice_cap < 0 || c.lattice_cap > (1ll << 28)) return fail(WFST_EINVAL, "lattice_cap must lie in [0, 2^28]");
     if (c.gc_interval < 0) return fail(WFST_EINVAL, "gc_interval must be >= 0");
     if (c.arena_commit < -1) return fail(WFST_EINVAL, "arena_commit must be >= -1");
-    if (c.gc_interval > 0 && c.lattice) return fail(WFST_EINVAL, "log compaction (gc_interval) does not run in lattice mode");
+    if (c.lat_prune_interval < 0 || c.lat_prune_interval > 512 || (c.lat_prune_interval > 0 && !c.lattice))
+        return fail(WFST_EINVAL, "lat_prune_interval must lie in [0, 512] and needs lattice mode");
     z->lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
         : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
                              1ull << 28);
@@ -544,7 +545,8 @@ static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &
     w.lattice = c.lattice;
     w.output_beam = c.lattice ? c.output_beam : 0.0f;
     w.lat_cap = (uint32_t)z.lat_cap;
-    w.lat_nodes = c.lattice ? (uint32_t)(z.arena + 1) : 0u;
+    w.lat_nodes = c.lattice ? (uint32_t)(std::max(z.arena, z.lat_cap) + 1) : 0u;
+    w.lat_prune_interval = c.lattice ? c.lat_prune_interval : 0;
     w.gc_interval = c.gc_interval;
     w.chg_cap = (uint32_t)std::max<uint64_t>(z.CC, z.Q);
     w.round_base = 0;
@@ -602,7 +604,7 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
         take(&w.gc_buf, L * (size_t)z.arena);
     }
     if (c.lattice) {
-        const size_t F = (size_t)c.max_frames + 3, nodes = (size_t)z.arena + 1;
+        const size_t F = (size_t)c.max_frames + 3, nodes = (size_t)std::max(z.arena, z.lat_cap) + 1;
         take(&w.lat_arc, L * z.lat_cap);
         take(&w.lat_aoff, L * F);
         take(&w.lat_nbase, L * F);
@@ -742,6 +744,8 @@ static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &
             if ((e = go(kKEpsExpand, t, k)) != hipSuccess) return e;
             if ((e = go(kKEpsApply, t, k)) != hipSuccess) return e;
         }
+        if (w.lat_prune_interval > 0 && (t + 1) % w.lat_prune_interval == 0 && t + 1 < steps &&
+            (e = go(kKLatPrune, t, 0)) != hipSuccess) return e;
         if (w.gc_interval > 0 && (t + 1) % w.gc_interval == 0 && t + 1 < steps) {
             static const int ids[] = {kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd};
             for (int id : ids)

@@ -203,8 +203,11 @@ struct Work {
     // = the frame's first node + the token's position in that frame's frontier.
     int32_t lattice;          // 1: persist and prune the lattice
     float output_beam;        // the prune's beam
+    int32_t lat_prune_interval;  // > 0: the interval prune runs after every that many steps
     uint32_t lat_cap;         // lattice arcs (and kept records) per lane
-    uint32_t lat_nodes;       // lattice nodes per lane (arena + 1: every token but the start one has an entry)
+    uint32_t lat_nodes;       // lattice nodes per lane: max(arena, lat_cap) + 1 (without log compaction every
+                              //   token but the start one has its own entry, so arena + 1 suffice; a lane
+                              //   past it has an incomplete lattice)
     int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position, closure pass
                               //   (0: an arc of the step itself)}
     uint32_t *lat_aoff;       // [L][max_frames + 3] first lattice arc of step t at [t + 1] (t = -1: the
@@ -240,7 +243,7 @@ enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
     kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
-    kKLatEpsBack, kKCount
+    kKLatEpsBack, kKLatPrune, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -148,6 +148,16 @@ __device__ __forceinline__ bool lane_has_result(const LaneCtl &c)
     return c.final_entry >= 0 || c.final_score > -__builtin_inff();
 }
 
+// A lattice node past the lane's node capacity (possible only with log
+// compaction, which lets a lane hold more tokens over a decode than log
+// entries): the lane's lattice is marked incomplete (its cursor past
+// lat_cap, the arena bit) and gets no backward pass.
+__device__ __forceinline__ void lat_node_overflow(const Work &w, LaneCtl &c)
+{
+    atomicOr(&c.overflow, kOvfArena);
+    atomicMax(&c.lat_cursor, w.lat_cap + 1u);
+}
+
 // Parity of the frontier that feeds lane c's step t of the sequence.
 __device__ __forceinline__ int lane_par(const LaneCtl &c, int t) { return (c.base + t) & 1; }
 
@@ -1226,9 +1236,13 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
             if (w.lattice) {
                 // the token's lattice node (its closure may still raise the score)
-                const size_t nd = (size_t)L * w.lat_nodes + lt.nb[L] + pi;
-                w.lat_score[nd] = end;
-                w.lat_state[nd] = dst;
+                const uint32_t ni = lt.nb[L] + pi;
+                if (ni < w.lat_nodes) {
+                    w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
+                    w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
+                } else {
+                    lat_node_overflow(w, c);
+                }
             }
             if ((ml >> lane) & 1ull) {
                 const size_t ci = (size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt());
@@ -1343,7 +1357,8 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 // pass that relaxes them again admits a superset: the source's
                 // score only grows)
                 spos = w.chg_pos[k & 1][(size_t)L * w.chg_cap + i];
-                w.lat_epass[(size_t)L * w.lat_nodes + tab.fb[L] + (uint32_t)spos] = (uint8_t)k;
+                const uint32_t ni = tab.fb[L] + (uint32_t)spos;
+                if (ni < w.lat_nodes) w.lat_epass[(size_t)L * w.lat_nodes + ni] = (uint8_t)k;
             }
         }
         uint32_t dsum;
@@ -1576,9 +1591,13 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         pick(w.tok_ub, fp)[q] = ub;
         if (w.lattice) {
             // the token's node (appended: a new one; replaced: its score rises)
-            const size_t nd = (size_t)L * w.lat_nodes + tab.fb[L] + pi;
-            w.lat_score[nd] = end;
-            if (isnew) w.lat_state[nd] = dst;
+            const uint32_t ni = tab.fb[L] + pi;
+            if (ni < w.lat_nodes) {
+                w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
+                if (isnew) w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
+            } else {
+                lat_node_overflow(w, c);
+            }
         }
         if ((ml >> lane) & 1ull) {
             const uint32_t ci = cb + (uint32_t)__popcll(ml & mask_lt());
@@ -1797,6 +1816,140 @@ __global__ __launch_bounds__(kLatEpsBlock) void k_lat_eps_back(const Work *__res
         o[kLatLane] = L;
         o[kLatFlags] = 4;
     }
+}
+
+// Interval prune (page section 7, lat_prune_interval = N: a window-loose prune
+// that bounds the lattice, the exact final pass unchanged), after real step t
+// with (t + 1) % N == 0 for lanes with more real steps, one workgroup per lane.
+// With F = t + 1 the frontier's frame and W = max(0, F - 2N): backward scores of
+// frames F - 1 .. W from bwd(u) = -fwd(u) at every frontier token u (no
+// complete path through u can score more than the final best), the step's own
+// arcs then the frame's epsilon arcs to a fixpoint, as the final pass does; an
+// arc of steps W .. F - 1 or an epsilon arc of frames W .. F - 1 with
+// (fwd(src) + s) + bwd(dst) < 0 - output_beam is marked (pass field -1), and
+// the records from step W - 1's first to the cursor are compacted in place,
+// in order, with the step offsets rewritten. Step t's own arcs still hold
+// destination states (the next compaction resolves them): their destination
+// nodes come from the position map of frame F.
+constexpr int kLatPruneBlock = 1024;
+constexpr int kMaxPruneInterval = 512;   // 2N + 1 step offsets fit the workgroup's table
+
+template <typename LPT>
+__global__ __launch_bounds__(kLatPruneBlock) void k_lat_prune(const Work *__restrict__ wp, int t)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    const int F = t + 1;
+    if (c.status != kActive || c.last_step != t || F >= c.T || !lat_complete(w, c)) return;
+    const int W = max(0, F - 2 * w.lat_prune_interval);
+    const size_t FF = (size_t)w.max_frames + 3;
+    uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+    const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
+    int4 *rec = w.lat_arc + (size_t)L * w.lat_cap;
+    uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes;
+    const size_t nodes = (size_t)L * w.lat_nodes;
+    const int pF = lane_par(c, F);
+    const uint32_t nF = (uint32_t)c.cnt[pF];
+    const int32_t *posF = pick(w.pos, pF) + (size_t)L * w.num_states;
+    const uint32_t cursor = c.lat_cursor;
+    const float thr = 0.0f - w.output_beam;
+    const LpDesc d = *w.lp;
+    const int tid = (int)threadIdx.x;
+    __shared__ uint32_t off0[2 * kMaxPruneInterval + 2];   // offsets of slots W .. F (old)
+    __shared__ uint32_t wtot[kLatPruneBlock / kWave];
+    __shared__ uint32_t exs[kLatPruneBlock];
+    __shared__ int changed;
+    const int nslot = F - W + 1;
+    for (int i = tid; i < nslot; i += blockDim.x) off0[i] = aoff[W + i];
+    // bwd: frames W .. F - 1 at -inf, the frontier's nodes at -fwd
+    const uint32_t n0 = nbase[W], nf0 = nbase[F];
+    for (uint32_t i = n0 + (uint32_t)tid; i < nf0 + nF; i += blockDim.x)
+        bwd[i] = i < nf0 ? kOrdNegInf : f2ord(0.0f - w.lat_score[nodes + i]);
+    __syncthreads();
+    for (int f = F - 1; f >= W; --f) {
+        // the arcs of step f (slot f + 1; its epsilon part belongs to frame f + 1)
+        const uint32_t a0 = off0[f + 1 - W], a1 = (f + 1 < F) ? off0[f + 2 - W] : cursor;
+        const uint32_t ns = nbase[f], nd = nbase[f + 1];
+        const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)f * d.stride_t;
+        for (uint32_t i = a0 + (uint32_t)tid; i < a1; i += blockDim.x) {
+            const int4 r = rec[i];
+            if (r.w != 0) continue;
+            const ArcDLW ad = w.arc_dlw[r.y];
+            const float sa = ad.weight + lp_at(row, ad.ilabel);
+            const uint32_t dn = nd + (uint32_t)((f + 1 < F) ? r.z : posF[r.z]);
+            const float bd = ord2f(load_bwd(&bwd[dn]));
+            const float v = sa + bd;
+            const uint32_t sn = ns + (uint32_t)r.x;
+            if (v > -__builtin_inff()) atomicMax(&bwd[sn], f2ord(v));
+            if (!(((w.lat_score[nodes + sn] + sa) + bd) >= thr)) rec[i].w = -1;
+        }
+        __syncthreads();
+        // the epsilon arcs of frame f (slot f, after step f - 1's own)
+        const uint32_t e0 = off0[f - W], e1 = off0[f + 1 - W];
+        bool any = false;
+        for (uint32_t i = e0 + (uint32_t)tid; i < e1 && !any; i += blockDim.x) any = rec[i].w > 0;
+        if (__syncthreads_or(any)) {
+            for (uint32_t round = 0; round <= e1 - e0 + 1u; ++round) {
+                if (tid == 0) changed = 0;
+                __syncthreads();
+                for (uint32_t i = e0 + (uint32_t)tid; i < e1; i += blockDim.x) {
+                    const int4 r = rec[i];
+                    if (r.w <= 0) continue;
+                    const float v = w.arc_dlw[r.y].weight + ord2f(load_bwd(&bwd[ns + (uint32_t)r.z]));
+                    if (!(v > -__builtin_inff())) continue;
+                    const uint32_t o = f2ord(v);
+                    if (atomicMax(&bwd[ns + (uint32_t)r.x], o) < o) changed = 1;
+                }
+                __syncthreads();
+                const int ch = changed;
+                __syncthreads();
+                if (!ch) break;
+            }
+            for (uint32_t i = e0 + (uint32_t)tid; i < e1; i += blockDim.x) {
+                const int4 r = rec[i];
+                if (r.w <= 0) continue;
+                const float v = (w.lat_score[nodes + ns + (uint32_t)r.x] + w.arc_dlw[r.y].weight) +
+                                ord2f(load_bwd(&bwd[ns + (uint32_t)r.z]));
+                if (!(v >= thr)) rec[i].w = -1;
+            }
+            __syncthreads();
+        }
+    }
+    // in-place compaction of [off0[0], cursor), 1024 records at a time: every
+    // record of a chunk is read before any is written, and survivors only move
+    // down, so no unread record is overwritten
+    uint32_t out = off0[0];
+    for (uint32_t b0 = off0[0]; b0 < cursor; b0 += blockDim.x) {
+        const uint32_t i = b0 + (uint32_t)tid;
+        int4 r = make_int4(0, 0, 0, -1);
+        if (i < cursor) r = rec[i];
+        const bool keep = r.w != -1;
+        __syncthreads();
+        uint32_t tot;
+        const uint32_t ex = wave_excl_sum(keep ? 1u : 0u, &tot);
+        if (wlane() == 0) wtot[tid / kWave] = tot;
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (int x = 0; x < kLatPruneBlock / kWave; ++x) {
+            if (x < tid / kWave) before += wtot[x];
+            all += wtot[x];
+        }
+        exs[tid] = before + ex;
+        if (keep) rec[out + before + ex] = r;
+        __syncthreads();
+        // slots whose first record lies in this chunk start at its survivors' place
+        for (int sl = 1 + tid; sl < nslot; sl += blockDim.x) {
+            const uint32_t p = off0[sl];
+            if (p >= b0 && p < b0 + blockDim.x && p < cursor) aoff[W + sl] = out + exs[p - b0];
+        }
+        out += all;
+        __syncthreads();
+    }
+    for (int sl = 1 + tid; sl < nslot; sl += blockDim.x)
+        if (off0[sl] >= cursor) aoff[W + sl] = out;
+    if (tid == 0) c.lat_cursor = out;
 }
 
 // ---------------------------------------------------------- stream sequences
@@ -2035,11 +2188,12 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
 // sealed + j; a live entry's compacted position is the count of live bits before
 // it. Kernels, in order: begin, mark, scan, compact, commit, roots, clear, end.
 
-// Whether lane c's round runs: it ran a real step in this sequence, is active,
-// and is not in lattice mode (lattice arrays index entries).
+// Whether lane c's round runs: it ran a real step in this sequence and is
+// active (lattice nodes are frame positions, never log entries, so lattices
+// do not hold the log back).
 __device__ __forceinline__ bool gc_due(const Work &w, const LaneCtl &c)
 {
-    return !w.lattice && c.status == kActive && c.last_step >= 0 && c.last_step < c.T;
+    return c.status == kActive && c.last_step >= 0 && c.last_step < c.T;
 }
 
 // Round set-up, one thread per lane: the compaction of the lane's last step is
@@ -2480,6 +2634,11 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKGcClear: go(k_gc_clear, G, B, s, e0, e1, dw); break;
     case kKGcEnd: go(k_gc_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKLatEpsBack: go(k_lat_eps_back, dim3(w.max_lanes), dim3(kLatEpsBlock), s, e0, e1, dw, t); break;
+    case kKLatPrune:
+        if (w.lat_prune_interval < 1 || w.lat_prune_interval > kMaxPruneInterval) return hipErrorInvalidValue;
+        if (f16) go(k_lat_prune<__half>, dim3(w.max_lanes), dim3(kLatPruneBlock), s, e0, e1, dw, t);
+        else go(k_lat_prune<float>, dim3(w.max_lanes), dim3(kLatPruneBlock), s, e0, e1, dw, t);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
