@@ -132,7 +132,7 @@ def traffic_from_profiles(kernel, workload_name):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None):
+def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None, allow_partial=False):
     """The oracle on one pinned core over the batch's first lanes for about
     ``seconds``; with ``gpu`` (the timed run's last result) each of those lanes
     is also compared with it: arcs and words equal, score bits equal."""
@@ -147,7 +147,7 @@ def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None):
     t0 = time.perf_counter()
     for b in range(lp.shape[0]):
         r = oracle.decode_lane(og, lp[b], int(lengths[b]), wl.beam, wl.max_active,
-                               eps_iterations=wl.eps_iterations)
+                               allow_partial=allow_partial, eps_iterations=wl.eps_iterations)
         frames += int(lengths[b])
         arcs += int(r["steps"][:, 4].sum() + r["steps"][:, 7].sum())
         lanes += 1
@@ -404,6 +404,14 @@ def main():
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
     ap.add_argument("--lattice", type=float, default=None, metavar="OUTPUT_BEAM",
                     help="lattice mode: keep every admitted arc and prune with this output beam")
+    ap.add_argument("--lat-prune-interval", type=int, default=0, metavar="N",
+                    help="with --lattice: the interval prune every N steps")
+    ap.add_argument("--sparse-finals", type=float, default=None, metavar="KEEP",
+                    help="keep each state's final arc with probability KEEP (allow_partial on: lanes "
+                         "without a final arc at their end redirect to their best token)")
+    ap.add_argument("--recomb-slots", type=int, default=0, metavar="SLOTS",
+                    help="recombination through a per-lane open-addressing hash of SLOTS slots "
+                         "(power of 2) instead of the direct-mapped per-state table")
     ap.add_argument("--gc-interval", type=int, default=0, metavar="N",
                     help="compact the winners log every N steps (and per stream chunk)")
     ap.add_argument("--arena", type=int, default=0, metavar="ENTRIES",
@@ -456,6 +464,10 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     graph, lp, lengths = synth.workload_inputs(args.workload)
+    if args.sparse_finals is not None:
+        # keep each state's final arc with this probability; lanes that end
+        # without one redirect to their best token (allow_partial)
+        graph = synth.drop_finals(graph, 4000 + args.workload, args.sparse_finals)
     B, T, V = lp.shape
     dev = torch.device("cuda:0")
     if args.stream_chunk > 0:
@@ -465,11 +477,13 @@ def main():
         blank_skip_bench(args, wl, graph, lp, lengths, dev)
         return
     dg = wb.Graph(graph, device=0)
-    lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice)
+    lat = {} if args.lattice is None else dict(lattice=True, output_beam=args.lattice,
+                                               lat_prune_interval=args.lat_prune_interval)
     lat.update(gc_interval=args.gc_interval, arena_entries=args.arena, arena_commit=args.arena_commit)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=B, max_frames=T, lp_dtype=wl.dtype,
                      eps_iterations=wl.eps_iterations, use_graphs=not args.eager,
-                     grid_blocks=args.grid, **lat)
+                     grid_blocks=args.grid, allow_partial=args.sparse_finals is not None,
+                     recomb_slots=args.recomb_slots, **lat)
     x = torch.from_numpy(lp).to(dev)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -527,12 +541,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds, gpu=res)
+        cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds, gpu=res,
+                           allow_partial=args.sparse_finals is not None)
 
     configs = {}
     others = [int(c) for c in args.configs.split(",") if c.strip()] if args.configs else []
     others = [c for c in others if c != args.workload and c in synth.WORKLOADS]
-    if others and args.lattice is None and not args.gc_interval and not args.eager:
+    if (others and args.lattice is None and not args.gc_interval and not args.eager and args.sparse_finals is None
+            and not args.recomb_slots):
         # the other workloads (each its own decoder, released before the next)
         dec.close()
         dg.release()
@@ -567,6 +583,10 @@ def main():
                    "log_prob_dtype": wl.dtype, "score_dtype": "f32",
                    "execution": "per-phase kernels, eager" if args.eager else "per-phase kernels, hipGraph replay",
                    **({} if args.lattice is None else {"lattice_output_beam": args.lattice}),
+                   **({} if not args.lat_prune_interval else {"lat_prune_interval": args.lat_prune_interval}),
+                   **({} if args.sparse_finals is None else {"final_arc_keep": args.sparse_finals,
+                                                             "allow_partial": True}),
+                   **({} if not args.recomb_slots else {"recombination": f"hash, {args.recomb_slots} slots per lane"}),
                    **({} if not args.gc_interval else {"gc_interval": args.gc_interval}),
                    **({} if not args.arena else {"arena_entries": args.arena})},
         "arcs_expanded_per_s": round(arcs_ps, 1),

@@ -40,7 +40,7 @@ extern "C" {
 /* out_meta[b * 3 + 2] bits (section 7 of the page): a non-zero value means the
  * lane's result may be degraded; such a lane also reports ok = 0. */
 #define WFST_OVF_SLOTS    1   /* a lane's candidate arcs in one step exceed slot_cap       */
-#define WFST_OVF_HASH     2   /* reserved: recombination is direct-mapped and never overflows */
+#define WFST_OVF_HASH     2   /* recomb_slots > 0: more distinct destinations in one pass than the hash holds */
 #define WFST_OVF_ARENA    4   /* the lane's winners-log region is full                     */
 #define WFST_OVF_CLAIMS   8   /* more admitted candidates in one pass than claims_cap      */
 #define WFST_OVF_FRONTIER 16  /* more surviving tokens than frontier_cap                   */
@@ -189,6 +189,15 @@ typedef struct wfst_graph_desc {
  *                  on the same inputs, so results are those of a fully committed
  *                  region; wfst_decoder_stats reports the re-runs. Creating a
  *                  stream commits the whole range (a stream cannot run again).
+ *  recomb_slots    0: recombination through a direct-mapped table of one 8-byte
+ *                  key per state and lane (max_lanes * num_states * 8 bytes; no
+ *                  probing, never full). n > 0, a power of 2 in [64, 2^28]: a
+ *                  per-lane open-addressing hash of n 16-byte slots keyed on the
+ *                  destination state (page section 5.3's hash; memory
+ *                  max_lanes * n * 16 bytes, independent of the graph), claimed
+ *                  with a CAS and resolved with the same 64-bit atomicMax; a pass
+ *                  with more distinct destinations than n retires the lane with
+ *                  WFST_OVF_HASH. Same results. Needs epoch keys (plain_keys != 1).
  *  epoch_period    recombination rounds between table wipes with epoch keys
  *                  (0: derive: 2^(32 - tie bits) - 1, at most 65535); n in
  *                  [2, that value]: wipe more often (same results).
@@ -217,6 +226,7 @@ typedef struct wfst_decoder_config {
     int64_t arena_commit;
     int32_t epoch_period;
     int32_t lat_prune_interval;
+    int64_t recomb_slots;
 } wfst_decoder_config;
 
 /* Message of the last failed call on this thread ("" if none). The pointer stays
@@ -246,7 +256,8 @@ int wfst_graph_release(wfst_graph_t g);
  * result buffers) and takes a graph reference (page section 6.1 "Workspace",
  * section 10). The recombination table holds one 8-byte entry per state and
  * lane (max_lanes * num_states * 8 bytes), so destinations are resolved with
- * one atomic each and never overflow. Errors: WFST_EINVAL (bad config),
+ * one atomic each and never overflow (or, with recomb_slots, a per-lane hash).
+ * Errors: WFST_EINVAL (bad config),
  * WFST_ENOMEM, WFST_EDEVICE.
  */
 int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *c, wfst_decoder_t *out);

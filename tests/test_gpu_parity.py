@@ -41,10 +41,15 @@ def _golden_cases():
 
 
 # table keys: ties by in-rank (default on these graphs), by arc id (plain_keys
-# 2), plain keys (1); epoch wraps forced every few rounds (epoch_period)
+# 2), plain keys (1); epoch wraps forced every few rounds (epoch_period);
+# recombination through the open-addressing hash (recomb_slots: 64 slots on the
+# small graphs, so probe chains run long, a quarter million on the workloads)
 MODES = {"graph": dict(use_graphs=True), "eager": dict(use_graphs=False),
          "plain": dict(use_graphs=True, plain_keys=1), "arcid": dict(use_graphs=True, plain_keys=2),
-         "wrap": dict(use_graphs=True, epoch_period=3), "wrap_eager": dict(use_graphs=False, epoch_period=2)}
+         "wrap": dict(use_graphs=True, epoch_period=3), "wrap_eager": dict(use_graphs=False, epoch_period=2),
+         "hash": dict(use_graphs=True, recomb_slots=64), "hash_wrap": dict(use_graphs=False, recomb_slots=64,
+                                                                            epoch_period=3, plain_keys=2),
+         "hash_big": dict(use_graphs=True, recomb_slots=1 << 18)}
 
 
 @pytest.mark.parametrize("name,g,lp,case,eps,ap", _golden_cases(), ids=lambda x: x if isinstance(x, str) else "")
@@ -94,7 +99,7 @@ def test_random_small_graphs(eps):
     for seed in range(150):
         g, lp, L, beam, ma, mi, ap, P = _random_case(seed + (1000 if eps else 0), eps)
         _say("random", eps, seed, lp.shape, beam, ma, mi, ap, P)
-        mode = ("graph", "eager", "plain", "arcid", "wrap", "wrap_eager")[seed % 6]
+        mode = ("graph", "eager", "plain", "arcid", "wrap", "wrap_eager", "hash", "hash_wrap")[seed % 8]
         r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, **MODES[mode])
         o = oracle_lanes(g, lp, L, beam, ma, mi, ap, P)
         compare_batch(r, steps, o)
@@ -148,7 +153,8 @@ def test_workload_parity(cid, workload_graphs):
     dg = wb.Graph(g)
     runs = {}
     try:
-        extra = {2: ("plain", "wrap"), 3: ("arcid",), 4: ("plain", "wrap")}.get(cid, ())
+        extra = {2: ("plain", "wrap", "hash_big"), 3: ("arcid", "hash_big"), 4: ("plain", "wrap", "hash_big"),
+                 5: ("hash_big",)}.get(cid, ())
         for mode in ("graph", "eager") + extra:
             runs[mode] = gpu_decode(g, lp, L, wl.beam, wl.max_active, 0, False, wl.eps_iterations,
                                     dgraph=dg, **MODES[mode])
@@ -240,8 +246,8 @@ def test_decode_argument_errors():
 
 
 @pytest.mark.parametrize("cid,cap,bit", [(2, "frontier_cap", 16), (2, "arena_entries", 4),
-                                         (2, "claims_cap", 8), (2, "slot_cap", 1),
-                                         (4, "frontier_cap", 16), (4, "arena_entries", 4)])
+                                         (2, "claims_cap", 8), (2, "slot_cap", 1), (2, "recomb_slots", 2),
+                                         (4, "frontier_cap", 16), (4, "arena_entries", 4), (4, "recomb_slots", 2)])
 def test_capacity_overflow_is_flagged(cid, cap, bit):
     import torch
     g, lp, L = synth.workload_inputs(cid)
@@ -250,7 +256,8 @@ def test_capacity_overflow_is_flagged(cid, cap, bit):
     caps = {"frontier_cap": {"frontier_cap": 2000 if cid == 4 else 64, "claims_cap": 1000000},
             "arena_entries": {"arena_entries": 40000 if cid == 4 else 4096},
             "claims_cap": {"frontier_cap": 100000, "claims_cap": 64},
-            "slot_cap": {"slot_cap": 256}}[cap]
+            "slot_cap": {"slot_cap": 256},
+            "recomb_slots": {"recomb_slots": 64}}[cap]
     dg = wb.Graph(g)
     dec = wb.Decoder(dg, wl.beam, wl.max_active, max_lanes=2, max_frames=wl.frames,
                      eps_iterations=wl.eps_iterations, **caps)

@@ -70,7 +70,7 @@ class _Config(ctypes.Structure):
                 ("lattice", ctypes.c_int32), ("output_beam", ctypes.c_float),
                 ("lattice_cap", ctypes.c_int64), ("gc_interval", ctypes.c_int32),
                 ("arena_commit", ctypes.c_int64), ("epoch_period", ctypes.c_int32),
-                ("lat_prune_interval", ctypes.c_int32)]
+                ("lat_prune_interval", ctypes.c_int32), ("recomb_slots", ctypes.c_int64)]
 
 
 _lib = None
@@ -203,14 +203,14 @@ class DecodeResult:
 def _config(beam, max_active, min_active=0, allow_partial=False, max_lanes=8, max_frames=1024, lp_dtype="f32",
             eps_iterations=0, use_graphs=True, frontier_cap=0, claims_cap=0, arena_entries=0, grid_blocks=0,
             slot_cap=0, plain_keys=0, path_cap=0, lattice=False, output_beam=0.0, lattice_cap=0, gc_interval=0,
-            arena_commit=0, epoch_period=0, lat_prune_interval=0) -> _Config:
+            arena_commit=0, epoch_period=0, lat_prune_interval=0, recomb_slots=0) -> _Config:
     return _Config(float(beam), int(min_active), int(max_active), int(bool(allow_partial)),
                    int(max_lanes), int(max_frames), LP_F16 if lp_dtype == "f16" else LP_F32,
                    int(eps_iterations), int(bool(use_graphs)), int(frontier_cap),
                    int(claims_cap), int(grid_blocks), int(arena_entries), int(slot_cap),
                    int(plain_keys), int(path_cap), int(bool(lattice)), float(output_beam),
                    int(lattice_cap), int(gc_interval), int(arena_commit), int(epoch_period),
-                   int(lat_prune_interval))
+                   int(lat_prune_interval), int(recomb_slots))
 
 
 def decode_noalloc(graph: "Graph", log_prob, lengths, beam: float, max_active: int, stream=None,
@@ -254,12 +254,13 @@ class Decoder:
                  frontier_cap: int = 0, claims_cap: int = 0, arena_entries: int = 0,
                  grid_blocks: int = 0, slot_cap: int = 0, plain_keys: int = 0, path_cap: int = 0,
                  lattice: bool = False, output_beam: float = 0.0, lattice_cap: int = 0, gc_interval: int = 0,
-                 arena_commit: int = 0, epoch_period: int = 0, lat_prune_interval: int = 0):
+                 arena_commit: int = 0, epoch_period: int = 0, lat_prune_interval: int = 0,
+                 recomb_slots: int = 0):
         lib = load_library()
         cfg = _config(beam, max_active, min_active, allow_partial, max_lanes, max_frames, lp_dtype,
                       eps_iterations, use_graphs, frontier_cap, claims_cap, arena_entries, grid_blocks,
                       slot_cap, plain_keys, path_cap, lattice, output_beam, lattice_cap, gc_interval,
-                      arena_commit, epoch_period, lat_prune_interval)
+                      arena_commit, epoch_period, lat_prune_interval, recomb_slots)
         h = ctypes.c_void_p()
         _check(lib.wfst_decoder_create(graph.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h

@@ -505,6 +505,9 @@ static int derive_sizes(const wfst_graph_s *g, const wfst_decoder_config &c, Siz
     if (c.arena_commit < -1) return fail(WFST_EINVAL, "arena_commit must be >= -1");
     if (c.lat_prune_interval < 0 || c.lat_prune_interval > 512 || (c.lat_prune_interval > 0 && !c.lattice))
         return fail(WFST_EINVAL, "lat_prune_interval must lie in [0, 512] and needs lattice mode");
+    if (c.recomb_slots != 0 && (c.recomb_slots < 64 || c.recomb_slots > (1ll << 28) ||
+                                (c.recomb_slots & (c.recomb_slots - 1)) != 0))
+        return fail(WFST_EINVAL, "recomb_slots must be 0 (direct-mapped table) or a power of 2 in [64, 2^28]");
     z->lat_cap = !c.lattice ? 0 : c.lattice_cap ? (uint64_t)c.lattice_cap
         : std::min<uint64_t>(std::max<uint64_t>(2ull * (uint64_t)c.max_active * (uint64_t)(c.max_frames + 2), 1ull << 20),
                              1ull << 28);
@@ -536,6 +539,14 @@ static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &
     if (c.epoch_period != 0 && (c.epoch_period < 2 || (uint32_t)c.epoch_period > pmax))
         return fail(WFST_EINVAL, "epoch_period must be 0 or lie in [2, 2^(32 - key tie bits) - 1] (at most 65535)");
     w.epoch_period = c.epoch_period ? (uint32_t)c.epoch_period : pmax;
+    if (c.recomb_slots > 0) {
+        // the hash's claims carry the round's epoch: it needs epoch-tagged keys
+        if (!w.epochs)
+            return fail(WFST_EINVAL, "recomb_slots needs epoch-tagged table keys (plain_keys != 1 and key ties of at most 25 bits)");
+        uint32_t hb = 0;
+        while ((1ll << hb) < c.recomb_slots) ++hb;
+        w.hash_bits = hb;
+    }
     w.beam = c.beam; w.min_active = c.min_active; w.max_active = c.max_active;
     w.allow_partial = c.allow_partial ? 1 : 0; w.eps_iterations = z.P; w.lp_dtype = c.lp_dtype;
     w.max_lanes = c.max_lanes; w.max_frames = c.max_frames;
@@ -585,7 +596,8 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
         if (w.has_eps || c.lattice) take(&w.pos[p], L * S);
         if (z.P > 0) take(&w.changed[p], L * std::max<uint64_t>(z.CC, Q));
     }
-    take(&w.best, L * S);
+    if (w.hash_bits) take(&w.hash, L << w.hash_bits);
+    else take(&w.best, L * S);
     take(&w.claims, L * z.CC);
     take(&w.res, L * (size_t)w.res_stride);
     take(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
@@ -674,7 +686,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
     if (e == hipSuccess) e = hipMemcpy(d->d_work, &w, sizeof(Work), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
+    if (e == hipSuccess) e = w.hash_bits ? hipMemset(w.hash, 0, sizeof(HSlot) * (L << w.hash_bits))
+                                          : hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
     for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
@@ -1064,7 +1077,9 @@ extern "C" int wfst_decode_noalloc(wfst_graph_t g, const wfst_decoder_config *cp
     // recombination table start at zero, the position maps at -1
     auto run = [&]() -> hipError_t {
         hipError_t e = hipMemsetAsync(x.ctl, 0, sizeof(LaneCtl) * L, s);
-        if (e == hipSuccess) e = hipMemsetAsync(w.best, 0, sizeof(unsigned long long) * L * S, s);
+        if (e == hipSuccess)
+            e = w.hash_bits ? hipMemsetAsync(w.hash, 0, sizeof(HSlot) * (L << w.hash_bits), s)
+                            : hipMemsetAsync(w.best, 0, sizeof(unsigned long long) * L * S, s);
         for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemsetAsync(w.pos[p], 0xFF, 4 * L * S, s);
         if (e == hipSuccess) e = launch_noalloc_put(w, hd, lens, (int)L, x.d_work, x.d_desc, x.d_lengths, s);
         if (e == hipSuccess)

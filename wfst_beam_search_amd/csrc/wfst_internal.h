@@ -75,6 +75,14 @@ struct alignas(16) Claim {
     uint32_t score;   // binary32 bits of the end score
 };
 
+// A slot of the per-lane open-addressing recombination hash (the alternative to
+// the direct-mapped table): claim = epoch << 32 | destination state (a slot of
+// an earlier round counts as empty), key = the table key of its best candidate.
+struct alignas(16) HSlot {
+    unsigned long long claim;
+    unsigned long long key;
+};
+
 // Per-lane control block. Device-scope atomics on one 128-byte line serialize
 // even on different words, so every counter that many wavefronts of one kernel
 // update atomically has a line of its own; the first line holds the fields the
@@ -189,7 +197,9 @@ struct Work {
                               //   arcs), else (score + largest weight) + the frame's largest log-prob;
                               //   score + largest final weight before a final step; +inf if unknown
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
-    unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed)
+    unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed); null with the hash
+    HSlot *hash;              // [L][1 << hash_bits] recombination hash (hash_bits > 0), else null
+    uint32_t hash_bits;       // 0: the direct-mapped table; else log2 of the hash slots per lane
     Claim *claims;            // [L][CC]
     int4 *changed[2];         // [L][chg_cap] closure source lists by pass parity: the tokens with
                               //   epsilon arcs, {first epsilon arc, epsilon arcs, entry, score bits}

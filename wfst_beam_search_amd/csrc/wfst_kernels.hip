@@ -92,6 +92,56 @@ __device__ __forceinline__ unsigned long long table_key(const Work &w, float sco
            (unsigned long long)(((1u << a) - 1u) - tie);
 }
 
+// ------------------------------------------- recombination: table or hash
+// Where the candidates of destination state ds (lane L, round epoch ep) meet:
+// the direct-mapped table's entry best[L][ds], or a slot of the lane's
+// open-addressing hash (page section 5.3: a hash keyed on the destination,
+// one 64-bit atomicMax per candidate): linear probing from a multiplicative
+// hash of ds; a slot whose claim is of an earlier round is empty, and the
+// first candidate of ds to reach one claims it with a CAS. Every slot between
+// ds's first probe and its slot belongs to another destination of this round,
+// so a lookup stops at the first slot of an earlier round. Null: the hash is
+// full (the lane retires with the hash bit).
+__device__ __forceinline__ uint32_t hash_first(const Work &w, uint32_t ds)
+{
+    return (ds * 0x9E3779B1u) >> (32u - w.hash_bits);
+}
+
+__device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int L, uint32_t ds, uint32_t ep)
+{
+    if (!w.hash_bits) return w.best + (size_t)L * (size_t)w.num_states + ds;
+    HSlot *h = w.hash + ((size_t)L << w.hash_bits);
+    const uint32_t mask = (1u << w.hash_bits) - 1u;
+    const unsigned long long want = ((unsigned long long)ep << 32) | ds;
+    uint32_t i = hash_first(w, ds);
+    for (uint32_t n = 0; n <= mask; ++n, i = (i + 1u) & mask) {
+        const unsigned long long c = __hip_atomic_load(&h[i].claim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (c == want) return &h[i].key;
+        if ((uint32_t)(c >> 32) == ep) continue;   // another destination's, this round
+        const unsigned long long old = atomicCAS(&h[i].claim, c, want);
+        if (old == c || old == want) return &h[i].key;
+        // (claimed meanwhile for another destination: the next slot)
+    }
+    return nullptr;
+}
+
+// The key recorded for destination ds in round ep after the round's atomics
+// (0 when none: a table entry of an earlier round never equals a key of this one).
+__device__ __forceinline__ unsigned long long recomb_key(const Work &w, int L, uint32_t ds, uint32_t ep)
+{
+    if (!w.hash_bits) return w.best[(size_t)L * (size_t)w.num_states + ds];
+    const HSlot *h = w.hash + ((size_t)L << w.hash_bits);
+    const uint32_t mask = (1u << w.hash_bits) - 1u;
+    const unsigned long long want = ((unsigned long long)ep << 32) | ds;
+    uint32_t i = hash_first(w, ds);
+    for (uint32_t n = 0; n <= mask; ++n, i = (i + 1u) & mask) {
+        const HSlot v = h[i];
+        if (v.claim == want) return v.key;
+        if ((uint32_t)(v.claim >> 32) != ep) return 0ull;
+    }
+    return 0ull;
+}
+
 __device__ __forceinline__ int wlane() { return (int)(threadIdx.x & (kWave - 1)); }
 
 __device__ __forceinline__ unsigned long long mask_lt() { return (1ull << wlane()) - 1ull; }
@@ -345,9 +395,8 @@ __device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, ui
     cl = w.claims[(size_t)L * w.claims_cap + i];
     const uint32_t ds = dest_state(w, cl.dest);
     if (ds >= (uint32_t)w.num_states) return false;
-    unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + ds;
-    const bool win = *ent == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
-    if (win && !w.epochs) *ent = 0ull;
+    const bool win = recomb_key(w, L, ds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
+    if (win && !w.epochs) w.best[(size_t)L * (size_t)w.num_states + ds] = 0ull;
     return win;
 }
 
@@ -392,11 +441,13 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
         // zeros bypass the caches instead of leaving them full of dirty lines
         // that later kernels would have to write back
         typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-        const size_t n = (size_t)w.max_lanes * ns;
-        v4u *t4 = (v4u *)w.best;
+        // (the hash: two u64 per slot)
+        unsigned long long *base = w.hash_bits ? (unsigned long long *)w.hash : w.best;
+        const size_t n = w.hash_bits ? ((size_t)w.max_lanes << w.hash_bits) * 2u : (size_t)w.max_lanes * ns;
+        v4u *t4 = (v4u *)base;
         const v4u z = {0u, 0u, 0u, 0u};
         for (size_t i = tid; i < n / 2; i += stride) __builtin_nontemporal_store(z, &t4[i]);
-        if (tid == 0 && (n & 1)) w.best[n - 1] = 0ull;
+        if (tid == 0 && (n & 1)) base[n - 1] = 0ull;
         return;
     }
     if (k != 0) return;
@@ -709,10 +760,13 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
 #pragma unroll
     for (int r = 0; r < kR; ++r) adm[r] = ((ud.live >> r) & 1u) && ud.e[r] > cut;
     if (ph == kPhReal) {
-        unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
 #pragma unroll
-        for (int r = 0; r < kR; ++r)
-            if (adm[r]) atomicMax(&tbl[dest_state(w, ud.dst[r])], table_key(w, ud.e[r], (int32_t)ud.arc[r], ud.dst[r], ep));
+        for (int r = 0; r < kR; ++r) {
+            if (!adm[r]) continue;
+            unsigned long long *ent = recomb_entry(w, L, dest_state(w, ud.dst[r]), ep);
+            if (ent) atomicMax(ent, table_key(w, ud.e[r], (int32_t)ud.arc[r], ud.dst[r], ep));
+            else atomicOr(&c.overflow, kOvfHash);
+        }
     } else {
         unsigned long long fkey = 0ull;
 #pragma unroll
@@ -851,8 +905,10 @@ __device__ __forceinline__ void slot_prologue(const Work &w, LaneTab &tab, int t
 }
 
 // Step bookkeeping done once per step by thread L of workgroup 0 of k_max:
-// retire overflowed / dead lanes, the dynamic beam, the redirect, resets.
-__device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
+// retire overflowed / dead lanes, the dynamic beam, resets. Returns true when
+// the lane's final step found no final arc and allow_partial asks for the
+// redirect (done by a whole wavefront afterwards: redirect_lane).
+__device__ __forceinline__ bool step_begin_lane(const Work &w, int t, int L)
 {
     LaneCtl &c = w.ctl[L];
     const int p = lane_par(c, t);
@@ -860,15 +916,15 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
     const uint32_t n = (uint32_t)cn, arcs = (uint32_t)(cn >> 32);
     commit_log(w, c, L, t - 1, n);
     const int ph = lane_phase(c, t);
-    if (ph == kPhNone) return;
+    if (ph == kPhNone) return false;
     uint32_t *rec = step_rec(w, L, t);
     c.last_step = t;
     if (w.lattice) w.lat_aoff[(size_t)L * (w.max_frames + 3) + t + 1] = c.lat_cursor;
     rec[kRecN] = n;
     rec[kRecArcs] = arcs;
-    if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
-    if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
-    if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return; }
+    if (n > w.frontier_cap) { c.overflow |= kOvfFrontier; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return false; }
+    if (arcs > w.strip_cap * (uint32_t)kWave) { c.overflow |= kOvfSlots; c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return false; }
+    if (n == 0u) { c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead; return false; }
     if (w.lattice) {
         // frame t holds n tokens (its closure is done): frame t + 1's first node
         const size_t F = (size_t)w.max_frames + 3;
@@ -888,38 +944,57 @@ __device__ __forceinline__ void step_begin_lane(const Work &w, int t, int L)
         if (ph == kPhReal) {
             c.status = kDone; c.phase_final = kPhDead; rec[kRecPhase] = kPhDead;
         } else {
-            if (w.allow_partial) {
-                // redirect: each token offers a virtual weight-0 arc num_arcs + state
-                const size_t qo = (size_t)L * w.frontier_cap;
-                unsigned long long bk = 0ull;
-                uint32_t bi = 0;
-                for (uint32_t i = 0; i < n; ++i) {
-                    const float e = w.tok_score[p][qo + i] + 0.0f;
-                    const unsigned long long k =
-                        cand_key(e, (int32_t)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + i]));
-                    if (i == 0 || k > bk) { bk = k; bi = i; }
-                }
-                c.final_entry = w.tok_entry[p][qo + bi];
-                c.final_score = w.tok_score[p][qo + bi] + 0.0f;
-                c.reached_final = 0;
-                rec[kRecPhase] = kPhRedirect;
-                if (w.lattice) {
-                    // the redirect's virtual arc is the lattice's one final arc
-                    const uint32_t li = c.lat_cursor;
-                    if (li < w.lat_cap) {
-                        w.lat_arc[(size_t)L * w.lat_cap + li] =
-                            make_int4((int)bi, (int)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + bi]),
-                                      w.super_final, 0);
-                        c.lat_cursor = li + 1u;
-                    } else {
-                        c.overflow |= kOvfArena;
-                    }
-                }
-                c.phase_final = kPhRedirect;
-            }
             c.status = kDone;
+            if (w.allow_partial) return true;
         }
     }
+    return false;
+}
+
+// The redirect of a final step without final arcs (page section 3, allow_partial;
+// reading R10), by one wavefront: each token offers a virtual weight-0 arc
+// num_arcs + state, and the greatest key(score, arc) wins (keys are unique: one
+// token per state); a strided scan of the frontier, then a wavefront reduction.
+__device__ __forceinline__ void redirect_lane(const Work &w, int t, int L)
+{
+    LaneCtl &c = w.ctl[L];
+    const int p = lane_par(c, t);
+    const uint32_t n = (uint32_t)pair_at(c.cnt, p);
+    const size_t qo = (size_t)L * w.frontier_cap;
+    unsigned long long bk = 0ull;
+    uint32_t bi = 0xFFFFFFFFu;
+    for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave) {
+        const float e = w.tok_score[p][qo + i] + 0.0f;
+        const unsigned long long k = cand_key(e, (int32_t)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + i]));
+        if (bi == 0xFFFFFFFFu || k > bk) { bk = k; bi = i; }
+    }
+    unsigned long long m = bi == 0xFFFFFFFFu ? 0ull : bk;
+#pragma unroll
+    for (int dd = kWave / 2; dd >= 1; dd >>= 1) {
+        const unsigned long long o = __shfl_xor(m, dd, kWave);
+        m = o > m ? o : m;
+    }
+    const unsigned long long who = __ballot(bi != 0xFFFFFFFFu && bk == m);
+    if (!who) return;
+    const int src = __ffsll((long long)who) - 1;
+    if (wlane() != src) return;
+    uint32_t *rec = step_rec(w, L, t);
+    c.final_entry = w.tok_entry[p][qo + bi];
+    c.final_score = w.tok_score[p][qo + bi] + 0.0f;
+    c.reached_final = 0;
+    rec[kRecPhase] = kPhRedirect;
+    if (w.lattice) {
+        // the redirect's virtual arc is the lattice's one final arc
+        const uint32_t li = c.lat_cursor;
+        if (li < w.lat_cap) {
+            w.lat_arc[(size_t)L * w.lat_cap + li] =
+                make_int4((int)bi, (int)((uint32_t)w.num_arcs + (uint32_t)w.tok_state[p][qo + bi]), w.super_final, 0);
+            c.lat_cursor = li + 1u;
+        } else {
+            c.overflow |= kOvfArena;
+        }
+    }
+    c.phase_final = kPhRedirect;
 }
 
 // Start of a step: the lane table of the step's slot space, then workgroup 0
@@ -929,7 +1004,16 @@ __device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
 {
     slot_prologue(w, tab, t);
     __syncthreads();
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) step_begin_lane(w, t, (int)threadIdx.x);
+    if (blockIdx.x == 0) {
+        // (block-uniform: the whole workgroup takes part in the barrier)
+        __shared__ int32_t redir[kMaxLanes];
+        if (threadIdx.x < (unsigned)w.max_lanes)
+            redir[threadIdx.x] = step_begin_lane(w, t, (int)threadIdx.x) ? 1 : 0;
+        __syncthreads();
+        // one wavefront per lane that redirects
+        for (int L = (int)(threadIdx.x / kWave); L < w.max_lanes; L += kBlock / kWave)
+            if (redir[L]) redirect_lane(w, t, L);
+    }
 }
 
 // The slot pass of step t: exact maximum and superset admission in one walk.
@@ -1021,9 +1105,10 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             const uint32_t mk = pair_at(c.maxkey, p);
             const float bt = pair_at(c.beam, p);
             const uint32_t fbase = pair_at(c.front_base, p);
-            // candidates past claims_cap were never written: the lane cannot be
-            // compacted (token and log capacity are checked per wavefront)
-            const bool fits = nc <= w.claims_cap;
+            // candidates past claims_cap were never written, or a full hash lost
+            // some: the lane cannot be compacted (token and log capacity are
+            // checked per wavefront)
+            const bool fits = nc <= w.claims_cap && !(c.overflow & kOvfHash);
             if ((ph == kPhReal || ph == kPhFinal) && fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = c.log_cursor;          // winners-log base of this compaction
@@ -1054,10 +1139,10 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         }
         if (ph == kPhReal) {
             if (tab.f0[L] == 0.0f) {
-                // the candidate list overflowed: retire the lane before writing
-                // any token; its table entries stay set, so the table is cleared
-                // before the next decode
-                c.overflow |= kOvfClaims;
+                // the candidate list overflowed (or the hash was full): retire the
+                // lane before writing any token; its table entries stay set, so
+                // the table is cleared before the next decode
+                if (tab.n[L] > w.claims_cap) c.overflow |= kOvfClaims;
                 c.dirty = 1u; c.status = kDone; c.phase_final = kPhDead;
             } else {
                 c.front_base[np] = tab.arcs[L];
@@ -1069,7 +1154,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             const unsigned long long fk = c.final_key;
             const bool got = fk != 0ull && ord2f((uint32_t)(fk >> 32)) > tab.f1[L] && tab.f0[L] != 0.0f;
             step_rec(w, L, t)[kRecDistinct] = got ? 1u : 0u;
-            if (tab.f0[L] == 0.0f) c.overflow |= kOvfClaims;
+            if (tab.f0[L] == 0.0f && tab.n[L] > w.claims_cap) c.overflow |= kOvfClaims;
             c.status = kDone;
         }
     }
@@ -1128,9 +1213,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         // earlier rounds always lose); without, every owner clears its entry
         const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
         if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
-            unsigned long long *ent = w.best + (size_t)L * (size_t)w.num_states + cds;
-            if (*ent == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
-                if (!w.epochs) *ent = 0ull;
+            if (recomb_key(w, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
+                if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
                 keep = adm;
             }
         }
@@ -1340,7 +1424,6 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
         const float cutoff = tab.f1[L];
         LaneCtl &c = w.ctl[L];
-        unsigned long long *tbl = w.best + (size_t)L * (size_t)w.num_states;
         // the 64 sources of this unit: their epsilon ranges, entries and scores
         // as the kernel that made them wrote them
         int32_t eb = 0, ent = -1, spos = 0;
@@ -1388,7 +1471,9 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 adm = e > cutoff;
                 if (adm) {
                     ++n_adm;
-                    atomicMax(&tbl[dest_state(w, ar.dest)], table_key(w, e, a, ar.dest, ep));
+                    unsigned long long *ent = recomb_entry(w, L, dest_state(w, ar.dest), ep);
+                    if (ent) atomicMax(ent, table_key(w, e, a, ar.dest, ep));
+                    else atomicOr(&c.overflow, kOvfHash);
                 }
             }
             if (w.lattice) {
@@ -1451,8 +1536,9 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             const uint32_t nce = c.nclaims_eps[k & 1], n0 = c.eps_n0;
             const bool on = closure_lane(c, t) && n0 <= w.frontier_cap;
             if (on) nc = nce;
-            // token and log capacity are checked per wavefront as it allocates
-            const bool fits = nc <= w.claims_cap;
+            // token and log capacity are checked per wavefront as it allocates;
+            // a full hash lost candidates
+            const bool fits = nc <= w.claims_cap && !(c.overflow & kOvfHash);
             if (fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
             tab.arcs[L] = n0;
@@ -1471,9 +1557,11 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         LaneCtl &c = w.ctl[L];
         c.nclaims_eps[(k + 1) & 1] = 0u;
         if (tab.f0[L] != 0.0f) {
-            // candidates past claims_cap were never listed: their table entries
-            // stay set, so the table is cleared before the next decode
-            c.overflow |= kOvfClaims; c.dirty = 1u;
+            // candidates past claims_cap were never listed (or the hash was
+            // full): their table entries stay set, so the table is cleared
+            // before the next decode
+            if (tab.n[L] > w.claims_cap) c.overflow |= kOvfClaims;
+            c.dirty = 1u;
             c.status = kDone; c.phase_final = kPhDead;
         }
     }
