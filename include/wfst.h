@@ -188,7 +188,9 @@ typedef struct wfst_graph_desc {
  *                  least double, aimed at the longest lane's end) and runs again
  *                  on the same inputs, so results are those of a fully committed
  *                  region; wfst_decoder_stats reports the re-runs. Creating a
- *                  stream commits the whole range (a stream cannot run again).
+ *                  stream commits its own lane's whole region when it opens (it
+ *                  cannot run again), so committed memory grows with the
+ *                  streams opened; chunks stay mapped after release.
  *  recomb_slots    0: recombination through a direct-mapped table of one 8-byte
  *                  key per state and lane (max_lanes * num_states * 8 bytes; no
  *                  probing, never full). n > 0, a power of 2 in [64, 2^28]: a

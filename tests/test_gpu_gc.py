@@ -174,3 +174,44 @@ def test_lazy_region_streams(gi):
         g, lp, L, beam, ma, ap, P, _ = _case(seed + 900, bool(seed % 2))
         _say("lazy stream", seed, lp.shape, "interval", gi)
         check_stream(g, lp, L, 5, beam, ma, 0, ap, P, gc_interval=gi, arena_commit=2048)
+
+
+def test_stream_commit_tracks_open_channels():
+    """Page section 6.2 (a channel's slice committed at CreateStream): with
+    lazily committed regions of 2^21 entries per lane (16 MiB, 4 MiB chunks), each
+    stream opened commits its own lane's region, the same amount per lane, and
+    nothing when a released channel opens again; a decode after the streams
+    (kernels' bound back to the decode's committed size) equals the oracle."""
+    import torch
+    g = synth.random_graph(2024, n=50, deg=(1, 6), vocab=8, self_loop=0.3)
+    lp = synth.random_logprobs(2025, 4, 30, g.vocab, sigma=2.0)
+    L = np.array([30, 22, 17, 30], dtype=np.int32)
+    dg = wb.Graph(g)
+    try:
+        dec = wb.Decoder(dg, 8.0, 200, max_lanes=8, max_frames=30, arena_entries=1 << 21, arena_commit=4096)
+        m0 = dec.mem_stats()
+        chans, seen = [], [m0["committed"]]
+        for k in range(3):
+            chans.append(dec.create_stream())
+            seen.append(dec.mem_stats()["committed"])
+        per = seen[1] - seen[0]
+        _say("committed per opened stream", per, seen)
+        assert per >= (1 << 21) * 8 - (4 << 20)
+        assert all(seen[k + 1] - seen[k] == per for k in range(3))
+        assert dec.mem_stats()["reserved"] == m0["reserved"]
+        # a stream on those lanes decodes (its whole region is usable)
+        x = torch.from_numpy(np.ascontiguousarray(lp[:1])).cuda()
+        dec.advance_chunk([chans[0]], x, [30])
+        fin = dec.finalize_stream(chans[0])
+        o = oracle.decode_lane(g, lp[0], 30, 8.0, 200, online=True)
+        assert np.array_equal(fin.arcs[0], o["arcs"]) and np.float32(fin.scores[0]) == np.float32(o["score"])
+        for c in chans:
+            dec.release_stream(c)
+        again = dec.create_stream()
+        assert again in chans and dec.mem_stats()["committed"] == seen[-1]
+        dec.release_stream(again)
+        r = dec.decode(torch.from_numpy(lp).cuda(), L)
+        compare_batch(r, None, oracle_lanes(g, lp, L, 8.0, 200), check_steps=False)
+        dec.close()
+    finally:
+        dg.release()

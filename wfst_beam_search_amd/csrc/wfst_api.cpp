@@ -174,6 +174,31 @@ struct LogRegion {
         return hipSuccess;
     }
 
+    // Maps the chunks covering lane L's whole region (a stream's: it cannot
+    // grow and run again). Other lanes' bounds stay as they are.
+    hipError_t commit_lane(uint32_t L)
+    {
+        if (!vmm || lim >= arena) return hipSuccess;
+        const hipMemAllocationProp prop = props();
+        hipMemAccessDesc acc{};
+        acc.location = prop.location;
+        acc.flags = hipMemAccessFlagsProtReadWrite;
+        const size_t b0 = (size_t)L * arena * sizeof(int2), b1 = ((size_t)L + 1) * arena * sizeof(int2);
+        for (size_t k = b0 / chunk; k < (b1 + chunk - 1) / chunk; ++k) {
+            if (h[k]) continue;
+            hipMemGenericAllocationHandle_t x{};
+            hipError_t e = hipMemCreate(&x, chunk, &prop, 0);
+            if (e != hipSuccess) return e;
+            e = hipMemMap(va + k * chunk, chunk, 0, x, 0);
+            if (e != hipSuccess) { (void)hipMemRelease(x); return e; }
+            h[k] = x;
+            ++mapped;
+            e = hipMemSetAccess(va + k * chunk, chunk, &acc, 1);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+
     size_t committed_bytes() const { return vmm ? mapped * chunk : va_bytes; }
 
     void release()
@@ -255,6 +280,8 @@ struct wfst_decoder_s {
     std::vector<int> ev_kind;
     size_t ev_used = 0;
     LogRegion log;                   // the winners log (w.wlog)
+    uint32_t dev_arena_lim = 0;      // append bound the device-side Work holds (log.lim, or the whole region
+                                     //   while streams are open: only their lanes append, each fully mapped)
     int last_regrows = 0;            // re-decodes of the last decode after the log grew
 
     ~wfst_decoder_s()
@@ -679,6 +706,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
         if (e != hipSuccess) { delete d; return hip_fail(e, "winners-log region"); }
         w.wlog = (int2 *)d->log.va;
         w.arena_lim = d->log.lim;
+        d->dev_arena_lim = d->log.lim;
     }
     w.ctl = d->ctl; w.lp = d->d_desc; w.lengths = d->d_lengths; w.plan = d->d_plan;
     d->chan_open.assign(L, 0);
@@ -838,17 +866,25 @@ static bool rounds_wrap(const wfst_decoder_s *d, uint64_t first, uint64_t last)
     return ref / P != last / P;
 }
 
+// Publishes append bound v to the kernels (their Work copy). The caller has no
+// kernel of this decoder in flight that the bound could matter to.
+static int set_arena_lim(wfst_decoder_s *d, uint32_t v)
+{
+    if (d->dev_arena_lim == v) return WFST_OK;
+    d->w.arena_lim = v;
+    HIP_TRY(hipMemcpy((char *)d->d_work + offsetof(Work, arena_lim), &v, 4, hipMemcpyHostToDevice));
+    d->dev_arena_lim = v;
+    return WFST_OK;
+}
+
 // Commits n winners-log entries per lane and publishes the bound to the
-// kernels (their Work copy). The caller has no kernel of this decoder in flight
-// that the new bound could matter to.
+// kernels. Same precondition.
 static int grow_log(wfst_decoder_s *d, uint32_t n)
 {
-    if (n <= d->log.lim) return WFST_OK;
+    if (n <= d->log.lim) return set_arena_lim(d, d->log.lim);
     hipError_t e = d->log.commit(n);
     if (e != hipSuccess) return hip_fail(e, "winners-log commit");
-    d->w.arena_lim = d->log.lim;
-    HIP_TRY(hipMemcpy((char *)d->d_work + offsetof(Work, arena_lim), &d->w.arena_lim, 4, hipMemcpyHostToDevice));
-    return WFST_OK;
+    return set_arena_lim(d, d->log.lim);
 }
 
 // Copies result block `lane` (already in h_res) to output row j.
@@ -898,6 +934,11 @@ extern "C" int wfst_decode(wfst_decoder_t d, const void *log_prob, int32_t B, in
     std::lock_guard<std::mutex> lock(d->mu);
     if (d->open_streams > 0) return fail(WFST_EINVAL, "the decoder has open streams (release them first)");
     HIP_TRY(hipSetDevice(d->g->device));
+    {
+        // (streams left the kernels' bound at their lanes' whole regions)
+        const int rcl = set_arena_lim(d, d->log.lim);
+        if (rcl != WFST_OK) return rcl;
+    }
     const size_t elem = c.lp_dtype == WFST_LP_F16 ? 2 : 4;
     if (maxlen > 0) {
         const int rcb = check_device_buffer(log_prob, (size_t)B * (size_t)T * (size_t)V * elem, d->g->device, "log_prob");
@@ -1274,11 +1315,19 @@ static int open_lanes(wfst_decoder_s *d, int32_t n, void *stream, int32_t *chann
         if (!d->chan_open[(size_t)L]) lanes.push_back(L);
     if (lanes.empty()) return WFST_OK;   // every lane holds a stream
     HIP_TRY(hipSetDevice(d->g->device));
-    // a stream cannot be decoded again: its lane's whole region is committed
-    // (streams wait for the device before a commit, see grow_log)
-    if (d->log.lim < d->w.arena) {
+    // a stream cannot be decoded again: the whole region of each lane that
+    // opens one is committed now (page section 6.2: a channel's slice at
+    // CreateStream), and while streams are open the kernels' bound is the
+    // whole region (only open streams' lanes append); the chunks stay mapped
+    // after release, for the lane's next stream (streams wait for the device
+    // before a commit, see grow_log)
+    if (d->log.lim < d->w.arena || d->dev_arena_lim != d->w.arena) {
         HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
-        int rc0 = grow_log(d, d->w.arena);
+        for (int L : lanes) {
+            const hipError_t e = d->log.commit_lane((uint32_t)L);
+            if (e != hipSuccess) return hip_fail(e, "winners-log commit");
+        }
+        int rc0 = set_arena_lim(d, d->w.arena);
         if (rc0 != WFST_OK) return rc0;
     }
     plan_clear(d);
