@@ -107,9 +107,12 @@ __device__ __forceinline__ uint32_t hash_first(const Work &w, uint32_t ds)
     return (ds * 0x9E3779B1u) >> (32u - w.hash_bits);
 }
 
+// (HASH: the kernels are compiled once per recombination structure, so the
+// default table path carries no probing code)
+template <bool HASH>
 __device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int L, uint32_t ds, uint32_t ep)
 {
-    if (!w.hash_bits) return w.best + (size_t)L * (size_t)w.num_states + ds;
+    if (!HASH) return w.best + (size_t)L * (size_t)w.num_states + ds;
     HSlot *h = w.hash + ((size_t)L << w.hash_bits);
     const uint32_t mask = (1u << w.hash_bits) - 1u;
     const unsigned long long want = ((unsigned long long)ep << 32) | ds;
@@ -127,9 +130,10 @@ __device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int L
 
 // The key recorded for destination ds in round ep after the round's atomics
 // (0 when none: a table entry of an earlier round never equals a key of this one).
+template <bool HASH>
 __device__ __forceinline__ unsigned long long recomb_key(const Work &w, int L, uint32_t ds, uint32_t ep)
 {
-    if (!w.hash_bits) return w.best[(size_t)L * (size_t)w.num_states + ds];
+    if (!HASH) return w.best[(size_t)L * (size_t)w.num_states + ds];
     const HSlot *h = w.hash + ((size_t)L << w.hash_bits);
     const uint32_t mask = (1u << w.hash_bits) - 1u;
     const unsigned long long want = ((unsigned long long)ep << 32) | ds;
@@ -390,12 +394,13 @@ __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *coun
 // its destination in round epoch ep: its key is the table entry after the
 // closure's expand pass. Without epochs the winner clears the entry (a loser
 // reading after that sees 0, never its key).
+template <bool HASH>
 __device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, uint32_t ep, Claim &cl)
 {
     cl = w.claims[(size_t)L * w.claims_cap + i];
     const uint32_t ds = dest_state(w, cl.dest);
     if (ds >= (uint32_t)w.num_states) return false;
-    const bool win = recomb_key(w, L, ds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
+    const bool win = recomb_key<HASH>(w, L, ds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
     if (win && !w.epochs) w.best[(size_t)L * (size_t)w.num_states + ds] = 0ull;
     return win;
 }
@@ -751,6 +756,7 @@ __device__ __forceinline__ float unit_max(const UnitData &ud)
 // candidate on the lane's direct-mapped table, on the final step with one
 // wavefront-reduced atomicMax of the lane's final key. Every candidate of the
 // superset goes to the wavefront's LDS buffer, then to the lane's list.
+template <bool HASH>
 __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float cut, uint32_t ep,
                                            const UnitData &ud, uint32_t *counter, ClaimBuf *cb, uint32_t &cb_n)
 {
@@ -763,7 +769,7 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
             if (!adm[r]) continue;
-            unsigned long long *ent = recomb_entry(w, L, dest_state(w, ud.dst[r]), ep);
+            unsigned long long *ent = recomb_entry<HASH>(w, L, dest_state(w, ud.dst[r]), ep);
             if (ent) atomicMax(ent, table_key(w, ud.e[r], (int32_t)ud.arc[r], ud.dst[r], ep));
             else atomicOr(&c.overflow, kOvfHash);
         }
@@ -815,7 +821,7 @@ __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t
 // (running max seeded with the lower bound the compaction posted, tokens whose
 // bound ub <= running max - b skipped: exact for both results) and the
 // superset admission against running max - b.
-template <typename LPT>
+template <typename LPT, bool HASH>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            uint32_t s, uint32_t s_end, ClaimBuf *cbuf)
 {
@@ -836,7 +842,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
             UnitData ud;
             load_unit<LPT>(w, v, s - tab.base[L], cur, run - b, ud);
             run = fmaxf(run, unit_max(ud));
-            admit_unit(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
+            admit_unit<HASH>(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
         }
         if (cb_n) flush_claims(w, L, &c.nclaims[p], *cbuf, cb_n);
         cb_n = 0;
@@ -844,13 +850,13 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
     }
 }
 
-template <typename LPT>
+template <typename LPT, bool HASH>
 __device__ __forceinline__ void walk_slots(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            ClaimBuf *cbuf)
 {
     uint32_t s, s_end;
     wave_share(tab.base[w.max_lanes], &s, &s_end);
-    walk_range<LPT>(w, tab, t, d, s, s_end, cbuf);
+    walk_range<LPT, HASH>(w, tab, t, d, s, s_end, cbuf);
 }
 
 // Dynamic beam b_t of a lane (page section 3), every operation one fp32
@@ -1017,7 +1023,7 @@ __device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
 }
 
 // The slot pass of step t: exact maximum and superset admission in one walk.
-template <typename LPT>
+template <typename LPT, bool HASH>
 __global__ __launch_bounds__(kBlock) void k_max(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
@@ -1025,7 +1031,7 @@ __global__ __launch_bounds__(kBlock) void k_max(const Work *__restrict__ wp, int
     __shared__ ClaimBuf cbufs[kBlock / kWave];
     step_open(w, t, tab);
     const LpDesc d = *w.lp;
-    walk_slots<LPT>(w, tab, t, d, &cbufs[threadIdx.x / kWave]);
+    walk_slots<LPT, HASH>(w, tab, t, d, &cbufs[threadIdx.x / kWave]);
 }
 
 // -------------------------------------------------------------- k_finalize
@@ -1072,6 +1078,7 @@ struct LatTab {
     uint32_t nb[kMaxLanes];        // first lattice node of the frame this compaction builds
 };
 
+template <bool HASH>
 __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, LatTab &lt)
 {
     const uint32_t ep = round_epoch(w, t, 0);
@@ -1213,7 +1220,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         // earlier rounds always lose); without, every owner clears its entry
         const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
         if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
-            if (recomb_key(w, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
+            if (recomb_key<HASH>(w, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
                 if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
                 keep = adm;
             }
@@ -1354,12 +1361,13 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     }
 }
 
+template <bool HASH>
 __global__ __launch_bounds__(kBlock) void k_finalize(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
     __shared__ LatTab lt;
-    ph_finalize(w, t, tab, lt);
+    ph_finalize<HASH>(w, t, tab, lt);
 }
 
 // ---------------------------------------------------------- epsilon closure
@@ -1376,6 +1384,7 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
     return c.status == kActive && t < c.win && (t < 0 || t < c.T);
 }
 
+template <bool HASH>
 __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
     const uint32_t ep = round_epoch(w, t, k);
@@ -1471,7 +1480,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                 adm = e > cutoff;
                 if (adm) {
                     ++n_adm;
-                    unsigned long long *ent = recomb_entry(w, L, dest_state(w, ar.dest), ep);
+                    unsigned long long *ent = recomb_entry<HASH>(w, L, dest_state(w, ar.dest), ep);
                     if (ent) atomicMax(ent, table_key(w, e, a, ar.dest, ep));
                     else atomicOr(&c.overflow, kOvfHash);
                 }
@@ -1507,12 +1516,13 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     }
 }
 
+template <bool HASH>
 __global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ wp, int t, int k)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
     __shared__ ClaimBuf cbufs[kBlock / kWave];
-    ph_eps_expand(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
+    ph_eps_expand<HASH>(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
 }
 
 // Per claimed destination of the pass: the winner (its key is the table entry)
@@ -1522,6 +1532,7 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ 
 // tokens, the next pass's sources. Only a destination's winner reads or writes
 // its token, and the existence test sees only the tokens the pass began with,
 // so the decisions are those of a pass that reads everything before it writes.
+template <bool HASH>
 __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
 {
     const uint32_t ep = round_epoch(w, t, k);
@@ -1582,7 +1593,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         int4 dd = make_int4(-2, 0, 0, -1);
         int32_t dst = 0;
         Claim cl;
-        const bool win = valid && take_winner(w, L, i, ep, cl);
+        const bool win = valid && take_winner<HASH>(w, L, i, ep, cl);
         const unsigned long long wm = __ballot(win);
         if (wm && lane == __ffsll((long long)__ballot(valid)) - 1)
             atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
@@ -1697,11 +1708,12 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
     }
 }
 
+template <bool HASH>
 __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ wp, int t, int k)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
-    ph_eps_apply(w, t, k, tab);
+    ph_eps_apply<HASH>(w, t, k, tab);
 }
 
 // ------------------------------------------------------------------ lattice
@@ -2689,6 +2701,7 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
                          hipEvent_t e0, hipEvent_t e1)
 {
     const bool f16 = w.lp_dtype == 1;
+    const bool hash = w.hash_bits != 0;
     const dim3 G(grid), B(kBlock);
     switch (id) {
     case kKClear: go(k_clear, G, B, s, e0, e1, dw, k); break;
@@ -2698,12 +2711,26 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         else go(k_lpmax<float>, G, B, s, e0, e1, dw);
         break;
     case kKMax:
-        if (f16) go(k_max<__half>, G, B, s, e0, e1, dw, t);
-        else go(k_max<float>, G, B, s, e0, e1, dw, t);
+        if (hash) {
+            if (f16) go(k_max<__half, true>, G, B, s, e0, e1, dw, t);
+            else go(k_max<float, true>, G, B, s, e0, e1, dw, t);
+        } else {
+            if (f16) go(k_max<__half, false>, G, B, s, e0, e1, dw, t);
+            else go(k_max<float, false>, G, B, s, e0, e1, dw, t);
+        }
         break;
-    case kKFinalize: go(k_finalize, G, B, s, e0, e1, dw, t); break;
-    case kKEpsExpand: go(k_eps_expand, G, B, s, e0, e1, dw, t, k); break;
-    case kKEpsApply: go(k_eps_apply, G, B, s, e0, e1, dw, t, k); break;
+    case kKFinalize:
+        if (hash) go(k_finalize<true>, G, B, s, e0, e1, dw, t);
+        else go(k_finalize<false>, G, B, s, e0, e1, dw, t);
+        break;
+    case kKEpsExpand:
+        if (hash) go(k_eps_expand<true>, G, B, s, e0, e1, dw, t, k);
+        else go(k_eps_expand<false>, G, B, s, e0, e1, dw, t, k);
+        break;
+    case kKEpsApply:
+        if (hash) go(k_eps_apply<true>, G, B, s, e0, e1, dw, t, k);
+        else go(k_eps_apply<false>, G, B, s, e0, e1, dw, t, k);
+        break;
     case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamEnd: go(k_stream_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
