@@ -169,6 +169,27 @@ def test_lattice_interval_prune_random():
     assert kept > 300
 
 
+def _large_frame_case():
+    g = synth.random_graph(77, n=60000, deg=(4, 14), vocab=8, epsilon=True, eps_levels=4, eps_share=0.3)
+    lp = synth.random_logprobs(78, 2, 5, g.vocab, sigma=1.0)
+    return g, lp, np.array([5, 4], dtype=np.int32)
+
+
+@pytest.mark.parametrize("interval", [0, 2])
+def test_lattice_large_epsilon_frames(interval):
+    """Frames of up to 60k tokens with up to 160k epsilon records (an unbounded
+    beam on a 60k-state graph with epsilon arcs): the epsilon fixpoint of a frame
+    whose nodes or records pass the workgroup's on-chip capacity runs on the
+    scores in memory, a smaller frame's in LDS; the kept records equal the
+    oracle's, with and without the interval prune."""
+    g, lp, L = _large_frame_case()
+    _say("lattice large epsilon frames", interval, lp.shape)
+    _, lats = lattice_case(g, lp, L, 1e10, 10**6, 0, False, 2.0, eps_iterations=3, frontier_cap=1 << 17,
+                           slot_cap=1 << 21, claims_cap=1 << 21, arena_entries=4 << 20, lattice_cap=4 << 20,
+                           lat_prune_interval=interval)
+    assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
 def _long_case():
     g = synth.random_graph(5, n=30, deg=(1, 6), vocab=6, self_loop=0.3)
     lp = synth.random_logprobs(6, 2, 400, g.vocab, sigma=2.0)

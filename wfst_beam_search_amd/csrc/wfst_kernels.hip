@@ -1845,15 +1845,54 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
     }
 }
 
-// Backward pass over frame t's epsilon arcs (its closure's: stored after step
-// t - 1's own arcs, or first of all for frame 0), launched after k_lat_back(t):
-// one workgroup per lane relaxes bwd(src) = max(bwd(src), w + bwd(dst)) over
-// them in rounds until a round changes nothing (the least fixpoint: epsilon
-// weights are <= 0 in lattice mode, so it exists and rounds end; a bound of one
-// round per arc + 1 ends them in any case), then keeps each arc once: from the
-// pass that last relaxed its source (that pass admitted every arc an earlier
-// one did, the source's score having only grown).
-constexpr int kLatEpsBlock = 1024;
+// Backward sweeps of one workgroup per lane. The interval prune (k_lat_prune:
+// the last 2N frames of a running lane) walks frames from the last to the
+// first; for each frame f:
+//  1. frame f's nodes start at -inf;
+//  2. the arcs of step f (records of slot f + 1 with pass 0; their destinations
+//     lie in frame f + 1, whose backward scores are final by now) raise
+//     bwd(source) with one atomicMax each and are marked at once;
+//  3. frame f's epsilon arcs (records of slot f with a pass > 0; both ends in
+//     frame f) relax bwd(source) to the least fixpoint, then are marked.
+// The final pass runs step 2 flat over lanes (k_lat_back, above) and step 3 per
+// lane (k_lat_eps_back). A sweep runs on as many workgroups as lanes, so its
+// speed is set by the memory-level parallelism inside a workgroup: each thread
+// issues the loads of a batch of records before it uses any. Epsilon fixpoints
+// run in LDS when the frame's nodes and records fit, else on the scores in
+// memory.
+constexpr int kLatSweepBlock = 1024;
+constexpr int kLatBatch = 8;                  // step-arc records per thread per load round
+constexpr int kLatEpsRegs = 8;                // epsilon-slot records per thread per load round (half in the prune)
+constexpr uint32_t kLatEpsLdsNodes = 35840;   // frame nodes whose backward scores fit in LDS (140 KiB)
+constexpr int kMaxPruneInterval = 512;        // 2N + 1 step offsets fit the workgroup's table
+
+struct SweepShared {
+    uint32_t bwd[kLatEpsLdsNodes];               // one frame's backward scores (epsilon fixpoint)
+    uint32_t off0[2 * kMaxPruneInterval + 2];    // prune: step offsets of slots W .. F before compaction
+    uint32_t nb0[2 * kMaxPruneInterval + 2];     // prune: first nodes of frames W .. F
+    uint32_t exs[kLatSweepBlock];                // compaction: survivors before each thread's records
+    uint32_t kmask[kLatSweepBlock];              // compaction: each thread's survivor bits
+    uint32_t wtot[kLatSweepBlock / kWave];       // compaction: survivors per wavefront
+};
+
+// One lane's lattice arrays, and the keep threshold of the sweep: an arc is
+// kept when (fwd(source) + s) + bwd(destination) >= thr.
+struct SweepLane {
+    int L;
+    int4 *rec;
+    uint32_t *bwd;
+    const float *fwd;
+    const int32_t *state;
+    const uint8_t *epass;
+    float thr;
+};
+
+__device__ __forceinline__ SweepLane sweep_lane(const Work &w, int L, float thr)
+{
+    const size_t nodes = (size_t)L * w.lat_nodes;
+    return SweepLane{L, w.lat_arc + (size_t)L * w.lat_cap, w.lat_bwd + nodes, w.lat_score + nodes,
+                     w.lat_state + nodes, w.lat_epass + nodes, thr};
+}
 
 __device__ __forceinline__ uint32_t load_bwd(const uint32_t *p)
 {
@@ -1861,81 +1900,240 @@ __device__ __forceinline__ uint32_t load_bwd(const uint32_t *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kLatEpsBlock) void k_lat_eps_back(const Work *__restrict__ wp, int t)
+// Appends a wavefront's kept records (final pass) to lane L's output, one
+// atomicAdd per wavefront. Every thread of the wavefront calls it.
+__device__ __forceinline__ void lat_emit(const Work &w, LaneCtl &c, int L, bool keep, const int32_t (&o)[kLatFields])
+{
+    const unsigned long long m = __ballot(keep);
+    if (m == 0ull) return;
+    const int leader = __ffsll((long long)m) - 1;
+    uint32_t ob = 0u;
+    if (wlane() == leader) ob = atomicAdd(&c.lat_out_n, (uint32_t)__popcll(m));
+    ob = __shfl(ob, leader, kWave);
+    if (!keep) return;
+    const uint32_t oi = ob + (uint32_t)__popcll(m & mask_lt());
+    if (oi >= w.lat_cap) return;
+    int32_t *dst = w.lat_out + ((size_t)L * w.lat_cap + oi) * kLatFields;
+#pragma unroll
+    for (int f = 0; f < kLatFields; ++f) dst[f] = o[f];
+}
+
+// Frame f's nodes [n0, n1) at -inf.
+__device__ __forceinline__ void sweep_clear(const SweepLane &s, uint32_t n0, uint32_t n1)
+{
+    for (uint32_t i = n0 + threadIdx.x; i < n1; i += kLatSweepBlock) s.bwd[i] = kOrdNegInf;
+}
+
+// Step f's arcs in the prune: records [a0, a1), those with pass 0 (step 2 of
+// the sweep). Sources are nodes ns + position, destinations nd + position;
+// dpos: non-null when the destination fields still hold states (the newest
+// step of a running lane), mapped to positions by it.
+template <typename LPT>
+__device__ __forceinline__ void sweep_step(const Work &w, const SweepLane &s, uint32_t a0, uint32_t a1,
+                                           uint32_t ns, uint32_t nd, const int32_t *dpos, const LPT *row)
+{
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t b0 = a0; b0 < a1; b0 += (uint32_t)kLatBatch * kLatSweepBlock) {
+        int4 r[kLatBatch];
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatSweepBlock + tid;
+            r[k] = i < a1 ? s.rec[i] : make_int4(0, 0, 0, 1);
+        }
+        ArcDLW ad[kLatBatch];
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            ad[k] = ArcDLW{0, 0u, 0.0f};
+            if (r[k].w == 0) ad[k] = w.arc_dlw[r[k].y];
+        }
+        float sa[kLatBatch], bd[kLatBatch], fw[kLatBatch];
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            sa[k] = 0.0f;
+            bd[k] = 0.0f;
+            fw[k] = 0.0f;
+            if (r[k].w != 0) continue;
+            sa[k] = ad[k].weight + lp_at(row, ad[k].ilabel);
+            const uint32_t dn = nd + (uint32_t)(dpos ? dpos[r[k].z] : r[k].z);
+            bd[k] = ord2f(load_bwd(&s.bwd[dn]));
+            fw[k] = s.fwd[ns + (uint32_t)r[k].x];
+        }
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            if (r[k].w != 0) continue;   // (positions past a1 carry pass 1)
+            const float v = sa[k] + bd[k];
+            if (v > -__builtin_inff()) atomicMax(&s.bwd[ns + (uint32_t)r[k].x], f2ord(v));
+            if (!(((fw[k] + sa[k]) + bd[k]) >= s.thr)) s.rec[b0 + (uint32_t)k * kLatSweepBlock + tid].w = -1;
+        }
+    }
+}
+
+// Keeps (final pass) or marks (prune) one epsilon record of frame f with
+// weight wt, source node se, the destination's backward score bd; fw = fwd(se),
+// ep = the pass that last relaxed the source (final pass: a record is kept
+// once, from that pass, which admitted every arc an earlier pass did, the
+// source's score having only grown). Every thread of the wavefront calls it.
+template <bool PRUNE>
+__device__ __forceinline__ void eps_keep(const Work &w, LaneCtl &c, const SweepLane &s, int f, bool on,
+                                         const int4 &r, uint32_t i, uint32_t se, float wt, float fw, float bd, int ep)
+{
+    const bool pass = on && ((fw + wt) + bd) >= s.thr;
+    if (PRUNE) {
+        if (on && !pass) s.rec[i].w = -1;
+        return;
+    }
+    const bool keep = pass && ep == r.w;
+    int32_t o[kLatFields] = {};
+    if (keep) {
+        const ArcDLW ad = w.arc_dlw[r.y];
+        o[kLatFrame] = f;
+        o[kLatSrc] = s.state[se];
+        o[kLatDst] = (int32_t)dest_state(w, ad.dest);
+        o[kLatIlabel] = (int32_t)ad.ilabel;
+        o[kLatArc] = r.y;
+        o[kLatScore] = (int32_t)__float_as_uint(wt);
+        o[kLatLane] = s.L;
+        o[kLatFlags] = 4;
+    }
+    lat_emit(w, c, s.L, keep, o);
+}
+
+// Frame f's epsilon arcs: records [e0, e1) of slot f, those with a pass > 0,
+// over nodes ns .. ns + nn - 1 (step 3 of the sweep). The fixpoint
+// bwd(src) = max(bwd(src), weight + bwd(dst)) runs in rounds until one changes
+// nothing (the least fixpoint: epsilon weights are <= 0 in lattice mode; a
+// bound of one round per record + 1 ends them in any case). A round visits
+// the records from the last to the first, a barrier after each 1024, so that
+// later closure passes go first and most chains settle in one round. The
+// scores live in LDS when the frame's nodes fit (bw = the LDS copy, indexed by
+// position), else in memory (bw = the frame's first node); each round loads
+// kLatEpsRegs records per thread at a time, or keeps them in registers when
+// the frame has no more.
+template <bool PRUNE, bool LDS, int R>
+__device__ __forceinline__ void eps_fix(const Work &w, LaneCtl &c, const SweepLane &s, uint32_t *bw, int f,
+                                        uint32_t e0, uint32_t e1, uint32_t ns, uint32_t nn)
+{
+    const uint32_t tid = threadIdx.x;
+    constexpr uint32_t kSuper = (uint32_t)R * kLatSweepBlock;
+    const uint32_t n = e1 - e0;
+    const uint32_t nsup = (n + kSuper - 1) / kSuper;
+    auto get = [&](uint32_t x) -> uint32_t { return LDS ? bw[x] : load_bwd(&bw[x]); };
+    int4 r[R];
+    float wt[R];
+    auto load = [&](uint32_t q) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const uint32_t i = e0 + q * kSuper + (uint32_t)k * kLatSweepBlock + tid;
+            r[k] = i < e1 ? s.rec[i] : make_int4(0, 0, 0, 0);
+            if (!(r[k].w > 0 && (uint32_t)r[k].x < nn && (uint32_t)r[k].z < nn)) r[k].w = 0;
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) wt[k] = r[k].w > 0 ? w.arc_dlw[r[k].y].weight : 0.0f;
+    };
+    // relaxes the loaded records, last first; the number of 1024-record
+    // groups present (kn) is workgroup-uniform
+    auto relax = [&](uint32_t q) -> int {
+        const uint32_t left = e1 - (e0 + q * kSuper);
+        const int kn = (int)min((left + kLatSweepBlock - 1) / kLatSweepBlock, (uint32_t)R);
+        int ch = 0;
+#pragma unroll
+        for (int k = R - 1; k >= 0; --k) {
+            if (k >= kn) continue;
+            if (r[k].w > 0) {
+                const float v = wt[k] + ord2f(get((uint32_t)r[k].z));
+                if (v > -__builtin_inff()) {
+                    const uint32_t o = f2ord(v);
+                    if (atomicMax(&bw[(uint32_t)r[k].x], o) < o) ch = 1;
+                }
+            }
+            __syncthreads();
+        }
+        return ch;
+    };
+    if (nsup == 1) load(0);
+    for (uint32_t round = 0; round <= n + 1u; ++round) {
+        int ch = 0;
+        if (nsup == 1) {
+            ch = relax(0);
+        } else {
+            for (uint32_t q = nsup; q-- > 0;) {
+                load(q);
+                ch |= relax(q);
+            }
+        }
+        if (!__syncthreads_or(ch)) break;
+    }
+    // keep (final pass) or mark (prune)
+    for (uint32_t q = 0; q < nsup; ++q) {
+        if (nsup > 1) load(q);
+        float fw[R];
+        int ep[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const bool on = r[k].w > 0;
+            fw[k] = on ? s.fwd[ns + (uint32_t)r[k].x] : 0.0f;
+            ep[k] = (!PRUNE && on) ? (int)s.epass[ns + (uint32_t)r[k].x] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const uint32_t i = e0 + q * kSuper + (uint32_t)k * kLatSweepBlock;
+            if (i >= e1) continue;   // (workgroup-uniform)
+            const bool on = r[k].w > 0;
+            const float bd = on ? ord2f(get((uint32_t)r[k].z)) : 0.0f;
+            eps_keep<PRUNE>(w, c, s, f, on, r[k], i + tid, ns + (uint32_t)r[k].x, wt[k], fw[k], bd, ep[k]);
+        }
+    }
+}
+
+template <bool PRUNE, int R>
+__device__ void sweep_eps(const Work &w, LaneCtl &c, const SweepLane &s, SweepShared &sh, int f,
+                          uint32_t e0, uint32_t e1, uint32_t ns, uint32_t nn)
+{
+    if (e1 <= e0) return;
+    const uint32_t tid = threadIdx.x;
+    if (nn <= kLatEpsLdsNodes) {
+        for (uint32_t i = tid; i < nn; i += kLatSweepBlock) sh.bwd[i] = load_bwd(&s.bwd[ns + i]);
+        __syncthreads();
+        eps_fix<PRUNE, true, R>(w, c, s, sh.bwd, f, e0, e1, ns, nn);
+        for (uint32_t i = tid; i < nn; i += kLatSweepBlock) s.bwd[ns + i] = sh.bwd[i];
+    } else {
+        eps_fix<PRUNE, false, R>(w, c, s, s.bwd + ns, f, e0, e1, ns, nn);
+    }
+}
+
+// The final backward pass over frame t's epsilon arcs (records of slot t with
+// a pass > 0), launched after k_lat_back(t) on graphs with epsilon arcs: one
+// workgroup per lane with a result and a complete lattice (step 3 of the
+// sweep above, threshold best - output_beam).
+__global__ __launch_bounds__(kLatSweepBlock) void k_lat_eps_back(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     const int L = (int)blockIdx.x;
     if (L >= w.max_lanes) return;
     LaneCtl &c = w.ctl[L];
     if (!lane_has_result(c) || t > c.last_step || !lat_complete(w, c)) return;
-    const size_t F = (size_t)w.max_frames + 3;
-    const uint32_t a0 = w.lat_aoff[(size_t)L * F + t];
-    const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
-    if (a1 <= a0) return;
-    const uint32_t n = a1 - a0;
-    const uint32_t nb = w.lat_nbase[(size_t)L * F + t];
-    const int4 *rec = w.lat_arc + (size_t)L * w.lat_cap + a0;
-    uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes;
-    __shared__ int changed;
-    for (uint32_t round = 0; round <= n + 1u; ++round) {
-        if (threadIdx.x == 0) changed = 0;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-            const int4 r = rec[i];
-            if (r.w == 0) continue;
-            const float v = w.arc_dlw[r.y].weight + ord2f(load_bwd(&bwd[nb + (uint32_t)r.z]));
-            if (!(v > -__builtin_inff())) continue;
-            const uint32_t o = f2ord(v);
-            if (atomicMax(&bwd[nb + (uint32_t)r.x], o) < o) changed = 1;
-        }
-        __syncthreads();
-        const int ch = changed;
-        __syncthreads();
-        if (!ch) break;
-    }
-    const float thr_min = c.final_score - w.output_beam;
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-        const int4 r = rec[i];
-        if (r.w == 0) continue;
-        const size_t se = (size_t)L * w.lat_nodes + nb + (uint32_t)r.x;
-        if ((int)w.lat_epass[se] != r.w) continue;   // (a repeat of the source's last relaxation)
-        const ArcDLW ad = w.arc_dlw[r.y];
-        const float sa = ad.weight;
-        const float bd = ord2f(load_bwd(&bwd[nb + (uint32_t)r.z]));
-        const float thr = (w.lat_score[se] + sa) + bd;
-        if (!(thr >= thr_min)) continue;
-        const uint32_t oi = atomicAdd(&c.lat_out_n, 1u);
-        if (oi >= w.lat_cap) continue;
-        int32_t *o = w.lat_out + ((size_t)L * w.lat_cap + oi) * kLatFields;
-        o[kLatFrame] = t;
-        o[kLatSrc] = w.lat_state[se];
-        o[kLatDst] = (int32_t)dest_state(w, ad.dest);
-        o[kLatIlabel] = (int32_t)ad.ilabel;
-        o[kLatArc] = r.y;
-        o[kLatScore] = (int32_t)__float_as_uint(sa);
-        o[kLatLane] = L;
-        o[kLatFlags] = 4;
-    }
+    __shared__ SweepShared sh;
+    const size_t FF = (size_t)w.max_frames + 3;
+    const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+    const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
+    const SweepLane s = sweep_lane(w, L, c.final_score - w.output_beam);
+    sweep_eps<false, kLatEpsRegs>(w, c, s, sh, t, aoff[t], min(aoff[t + 1], w.lat_cap), nbase[t], nbase[t + 1] - nbase[t]);
 }
 
 // Interval prune (page section 7, lat_prune_interval = N: a window-loose prune
 // that bounds the lattice, the exact final pass unchanged), after real step t
 // with (t + 1) % N == 0 for lanes with more real steps, one workgroup per lane.
-// With F = t + 1 the frontier's frame and W = max(0, F - 2N): backward scores of
-// frames F - 1 .. W from bwd(u) = -fwd(u) at every frontier token u (no
-// complete path through u can score more than the final best), the step's own
-// arcs then the frame's epsilon arcs to a fixpoint, as the final pass does; an
-// arc of steps W .. F - 1 or an epsilon arc of frames W .. F - 1 with
-// (fwd(src) + s) + bwd(dst) < 0 - output_beam is marked (pass field -1), and
-// the records from step W - 1's first to the cursor are compacted in place,
-// in order, with the step offsets rewritten. Step t's own arcs still hold
-// destination states (the next compaction resolves them): their destination
-// nodes come from the position map of frame F.
-constexpr int kLatPruneBlock = 1024;
-constexpr int kMaxPruneInterval = 512;   // 2N + 1 step offsets fit the workgroup's table
-
+// With F = t + 1 the frontier's frame and W = max(0, F - 2N): the sweep over
+// frames F - 1 .. W starts from bwd(u) = -fwd(u) at every frontier token u (no
+// complete path through u can score more than the final best) and marks (pass
+// field -1) the arcs of steps W .. F - 1 and the epsilon arcs of frames
+// W .. F - 1 with (fwd(src) + s) + bwd(dst) < 0 - output_beam; then the records
+// from step W - 1's first to the cursor are compacted in place, in order, with
+// the step offsets rewritten. Step t's own arcs still hold destination states
+// (the next compaction resolves them): their destination nodes come from the
+// position map of frame F.
 template <typename LPT>
-__global__ __launch_bounds__(kLatPruneBlock) void k_lat_prune(const Work *__restrict__ wp, int t)
+__global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     const int L = (int)blockIdx.x;
@@ -1943,112 +2141,95 @@ __global__ __launch_bounds__(kLatPruneBlock) void k_lat_prune(const Work *__rest
     LaneCtl &c = w.ctl[L];
     const int F = t + 1;
     if (c.status != kActive || c.last_step != t || F >= c.T || !lat_complete(w, c)) return;
+    __shared__ SweepShared sh;
     const int W = max(0, F - 2 * w.lat_prune_interval);
     const size_t FF = (size_t)w.max_frames + 3;
     uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
     const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
-    int4 *rec = w.lat_arc + (size_t)L * w.lat_cap;
-    uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes;
-    const size_t nodes = (size_t)L * w.lat_nodes;
+    const SweepLane s = sweep_lane(w, L, 0.0f - w.output_beam);
     const int pF = lane_par(c, F);
     const uint32_t nF = (uint32_t)c.cnt[pF];
     const int32_t *posF = pick(w.pos, pF) + (size_t)L * w.num_states;
     const uint32_t cursor = c.lat_cursor;
-    const float thr = 0.0f - w.output_beam;
     const LpDesc d = *w.lp;
-    const int tid = (int)threadIdx.x;
-    __shared__ uint32_t off0[2 * kMaxPruneInterval + 2];   // offsets of slots W .. F (old)
-    __shared__ uint32_t wtot[kLatPruneBlock / kWave];
-    __shared__ uint32_t exs[kLatPruneBlock];
-    __shared__ int changed;
+    const uint32_t tid = threadIdx.x;
     const int nslot = F - W + 1;
-    for (int i = tid; i < nslot; i += blockDim.x) off0[i] = aoff[W + i];
-    // bwd: frames W .. F - 1 at -inf, the frontier's nodes at -fwd
-    const uint32_t n0 = nbase[W], nf0 = nbase[F];
-    for (uint32_t i = n0 + (uint32_t)tid; i < nf0 + nF; i += blockDim.x)
-        bwd[i] = i < nf0 ? kOrdNegInf : f2ord(0.0f - w.lat_score[nodes + i]);
+    for (int i = (int)tid; i < nslot; i += kLatSweepBlock) {
+        sh.off0[i] = aoff[W + i];
+        sh.nb0[i] = nbase[W + i];
+    }
+    const uint32_t nf0 = nbase[F];
+    for (uint32_t i = nf0 + tid; i < nf0 + nF; i += kLatSweepBlock) s.bwd[i] = f2ord(0.0f - s.fwd[i]);
     __syncthreads();
     for (int f = F - 1; f >= W; --f) {
-        // the arcs of step f (slot f + 1; its epsilon part belongs to frame f + 1)
-        const uint32_t a0 = off0[f + 1 - W], a1 = (f + 1 < F) ? off0[f + 2 - W] : cursor;
-        const uint32_t ns = nbase[f], nd = nbase[f + 1];
-        const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)f * d.stride_t;
-        for (uint32_t i = a0 + (uint32_t)tid; i < a1; i += blockDim.x) {
-            const int4 r = rec[i];
-            if (r.w != 0) continue;
-            const ArcDLW ad = w.arc_dlw[r.y];
-            const float sa = ad.weight + lp_at(row, ad.ilabel);
-            const uint32_t dn = nd + (uint32_t)((f + 1 < F) ? r.z : posF[r.z]);
-            const float bd = ord2f(load_bwd(&bwd[dn]));
-            const float v = sa + bd;
-            const uint32_t sn = ns + (uint32_t)r.x;
-            if (v > -__builtin_inff()) atomicMax(&bwd[sn], f2ord(v));
-            if (!(((w.lat_score[nodes + sn] + sa) + bd) >= thr)) rec[i].w = -1;
-        }
+        const uint32_t ns = sh.nb0[f - W], nd = sh.nb0[f + 1 - W];
+        sweep_clear(s, ns, nd);
         __syncthreads();
-        // the epsilon arcs of frame f (slot f, after step f - 1's own)
-        const uint32_t e0 = off0[f - W], e1 = off0[f + 1 - W];
-        bool any = false;
-        for (uint32_t i = e0 + (uint32_t)tid; i < e1 && !any; i += blockDim.x) any = rec[i].w > 0;
-        if (__syncthreads_or(any)) {
-            for (uint32_t round = 0; round <= e1 - e0 + 1u; ++round) {
-                if (tid == 0) changed = 0;
-                __syncthreads();
-                for (uint32_t i = e0 + (uint32_t)tid; i < e1; i += blockDim.x) {
-                    const int4 r = rec[i];
-                    if (r.w <= 0) continue;
-                    const float v = w.arc_dlw[r.y].weight + ord2f(load_bwd(&bwd[ns + (uint32_t)r.z]));
-                    if (!(v > -__builtin_inff())) continue;
-                    const uint32_t o = f2ord(v);
-                    if (atomicMax(&bwd[ns + (uint32_t)r.x], o) < o) changed = 1;
-                }
-                __syncthreads();
-                const int ch = changed;
-                __syncthreads();
-                if (!ch) break;
-            }
-            for (uint32_t i = e0 + (uint32_t)tid; i < e1; i += blockDim.x) {
-                const int4 r = rec[i];
-                if (r.w <= 0) continue;
-                const float v = (w.lat_score[nodes + ns + (uint32_t)r.x] + w.arc_dlw[r.y].weight) +
-                                ord2f(load_bwd(&bwd[ns + (uint32_t)r.z]));
-                if (!(v >= thr)) rec[i].w = -1;
-            }
+        const uint32_t a0 = sh.off0[f + 1 - W], a1 = (f + 1 < F) ? sh.off0[f + 2 - W] : cursor;
+        const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)f * d.stride_t;
+        sweep_step<LPT>(w, s, a0, a1, ns, nd, (f + 1 < F) ? nullptr : posF, row);
+        __syncthreads();
+        if (w.has_eps) {
+            sweep_eps<true, kLatEpsRegs / 2>(w, c, s, sh, f, sh.off0[f - W], sh.off0[f + 1 - W], ns, nd - ns);
             __syncthreads();
         }
     }
-    // in-place compaction of [off0[0], cursor), 1024 records at a time: every
-    // record of a chunk is read before any is written, and survivors only move
-    // down, so no unread record is overwritten
-    uint32_t out = off0[0];
-    for (uint32_t b0 = off0[0]; b0 < cursor; b0 += blockDim.x) {
-        const uint32_t i = b0 + (uint32_t)tid;
-        int4 r = make_int4(0, 0, 0, -1);
-        if (i < cursor) r = rec[i];
-        const bool keep = r.w != -1;
+    // in-place compaction of [off0[0], cursor), kLatBatch records per thread (a
+    // contiguous run) per chunk: every record of a chunk is read before any is
+    // written, and survivors only move down, so no unread record is overwritten;
+    // the next chunk's records are loaded while this one's are written (they lie
+    // past every position this chunk writes)
+    constexpr uint32_t kChunk = (uint32_t)kLatBatch * kLatSweepBlock;
+    const uint32_t wv = tid / kWave;
+    uint32_t out = sh.off0[0];
+    int4 r[kLatBatch];
+    auto load_chunk = [&](uint32_t b, int4 (&x)[kLatBatch]) {
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            const uint32_t i = b + tid * (uint32_t)kLatBatch + (uint32_t)k;
+            x[k] = i < cursor ? s.rec[i] : make_int4(0, 0, 0, -1);
+        }
+    };
+    load_chunk(sh.off0[0], r);
+    for (uint32_t b0 = sh.off0[0]; b0 < cursor; b0 += kChunk) {
+        uint32_t km = 0u;
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k)
+            if (r[k].w != -1) km |= 1u << k;
         __syncthreads();
+        int4 nx[kLatBatch];
+        load_chunk(b0 + kChunk, nx);
         uint32_t tot;
-        const uint32_t ex = wave_excl_sum(keep ? 1u : 0u, &tot);
-        if (wlane() == 0) wtot[tid / kWave] = tot;
+        const uint32_t ex = wave_excl_sum((uint32_t)__popc(km), &tot);
+        if (wlane() == 0) sh.wtot[wv] = tot;
         __syncthreads();
         uint32_t before = 0, all = 0;
-        for (int x = 0; x < kLatPruneBlock / kWave; ++x) {
-            if (x < tid / kWave) before += wtot[x];
-            all += wtot[x];
+        for (uint32_t x = 0; x < (uint32_t)(kLatSweepBlock / kWave); ++x) {
+            if (x < wv) before += sh.wtot[x];
+            all += sh.wtot[x];
         }
-        exs[tid] = before + ex;
-        if (keep) rec[out + before + ex] = r;
+        sh.exs[tid] = before + ex;
+        sh.kmask[tid] = km;
+        uint32_t o = out + before + ex;
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k)
+            if ((km >> k) & 1u) s.rec[o++] = r[k];
         __syncthreads();
         // slots whose first record lies in this chunk start at its survivors' place
-        for (int sl = 1 + tid; sl < nslot; sl += blockDim.x) {
-            const uint32_t p = off0[sl];
-            if (p >= b0 && p < b0 + blockDim.x && p < cursor) aoff[W + sl] = out + exs[p - b0];
+        for (int sl = 1 + (int)tid; sl < nslot; sl += kLatSweepBlock) {
+            const uint32_t p = sh.off0[sl];
+            if (p >= b0 && p < b0 + kChunk && p < cursor) {
+                const uint32_t j = p - b0, th = j / (uint32_t)kLatBatch, q = j % (uint32_t)kLatBatch;
+                aoff[W + sl] = out + sh.exs[th] + (uint32_t)__popc(sh.kmask[th] & ((1u << q) - 1u));
+            }
         }
         out += all;
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) r[k] = nx[k];
         __syncthreads();
     }
-    for (int sl = 1 + tid; sl < nslot; sl += blockDim.x)
-        if (off0[sl] >= cursor) aoff[W + sl] = out;
+    for (int sl = 1 + (int)tid; sl < nslot; sl += kLatSweepBlock)
+        if (sh.off0[sl] >= cursor) aoff[W + sl] = out;
     if (tid == 0) c.lat_cursor = out;
 }
 
@@ -2740,6 +2921,7 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         if (f16) go(k_lat_back<__half>, G, B, s, e0, e1, dw, t);
         else go(k_lat_back<float>, G, B, s, e0, e1, dw, t);
         break;
+    case kKLatEpsBack: go(k_lat_eps_back, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t); break;
     case kKGcBegin: go(k_gc_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKGcMark: go(k_gc_mark, G, B, s, e0, e1, dw); break;
     case kKGcScan: go(k_gc_scan, dim3(w.max_lanes), dim3(kGcScanBlock), s, e0, e1, dw); break;
@@ -2748,11 +2930,10 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKGcRoots: go(k_gc_roots, G, B, s, e0, e1, dw); break;
     case kKGcClear: go(k_gc_clear, G, B, s, e0, e1, dw); break;
     case kKGcEnd: go(k_gc_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
-    case kKLatEpsBack: go(k_lat_eps_back, dim3(w.max_lanes), dim3(kLatEpsBlock), s, e0, e1, dw, t); break;
     case kKLatPrune:
         if (w.lat_prune_interval < 1 || w.lat_prune_interval > kMaxPruneInterval) return hipErrorInvalidValue;
-        if (f16) go(k_lat_prune<__half>, dim3(w.max_lanes), dim3(kLatPruneBlock), s, e0, e1, dw, t);
-        else go(k_lat_prune<float>, dim3(w.max_lanes), dim3(kLatPruneBlock), s, e0, e1, dw, t);
+        if (f16) go(k_lat_prune<__half>, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
+        else go(k_lat_prune<float>, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
         break;
     default: return hipErrorInvalidValue;
     }
