@@ -527,9 +527,10 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_GC_ROOTS    21  /* log compaction: the frontier's entries renumbered       */
 #define WFST_K_GC_CLEAR    22  /* log compaction: live map and counts cleared             */
 #define WFST_K_GC_END      23  /* log compaction: log end and the sealed prefix           */
-#define WFST_K_LAT_EPS_BACK 24 /* lattice: one frame's epsilon arcs, backward and prune   */
+#define WFST_K_LAT_EPS_BACK 24 /* lattice: a frame's epsilon arcs, fixpoint end and prune */
 #define WFST_K_LAT_PRUNE   25  /* lattice: interval prune of the last 2N frames's arcs     */
-#define WFST_K_COUNT       26
+#define WFST_K_LAT_EPS_ROUND 26 /* lattice: one flat relaxation round of a frame's epsilon arcs */
+#define WFST_K_COUNT       27
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

@@ -169,25 +169,46 @@ def test_lattice_interval_prune_random():
     assert kept > 300
 
 
-def _large_frame_case():
-    g = synth.random_graph(77, n=60000, deg=(4, 14), vocab=8, epsilon=True, eps_levels=4, eps_share=0.3)
+def _large_frame_case(levels):
+    g = synth.random_graph(77, n=60000, deg=(4, 14), vocab=8, epsilon=True, eps_levels=levels, eps_share=0.3)
     lp = synth.random_logprobs(78, 2, 5, g.vocab, sigma=1.0)
     return g, lp, np.array([5, 4], dtype=np.int32)
 
 
-@pytest.mark.parametrize("interval", [0, 2])
-def test_lattice_large_epsilon_frames(interval):
+@pytest.mark.parametrize("interval,levels,passes", [(0, 4, 3), (2, 4, 3), (0, 8, 1), (2, 8, 2)])
+def test_lattice_large_epsilon_frames(interval, levels, passes):
     """Frames of up to 60k tokens with up to 160k epsilon records (an unbounded
-    beam on a 60k-state graph with epsilon arcs): the epsilon fixpoint of a frame
-    whose nodes or records pass the workgroup's on-chip capacity runs on the
-    scores in memory, a smaller frame's in LDS; the kept records equal the
-    oracle's, with and without the interval prune."""
-    g, lp, L = _large_frame_case()
-    _say("lattice large epsilon frames", interval, lp.shape)
-    _, lats = lattice_case(g, lp, L, 1e10, 10**6, 0, False, 2.0, eps_iterations=3, frontier_cap=1 << 17,
+    beam on a 60k-state graph with epsilon arcs): the final pass's flat epsilon
+    rounds, and, with epsilon chains longer than the rounds settle (8 levels, 1
+    or 2 closure passes), the per-lane finish of the fixpoint, in LDS for a
+    small frame and on the scores in memory for a large one; the interval
+    prune's per-lane fixpoint likewise. The kept records equal the oracle's."""
+    g, lp, L = _large_frame_case(levels)
+    _say("lattice large epsilon frames", interval, levels, passes, lp.shape)
+    _, lats = lattice_case(g, lp, L, 1e10, 10**6, 0, False, 2.0, eps_iterations=passes, frontier_cap=1 << 17,
                            slot_cap=1 << 21, claims_cap=1 << 21, arena_entries=4 << 20, lattice_cap=4 << 20,
                            lat_prune_interval=interval)
     assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
+def test_lattice_deep_epsilon_chains():
+    """Small graphs whose epsilon chains run up to 7 arcs, 1 or 2 closure passes:
+    the final pass's flat rounds leave chains unsettled, and the per-lane finish
+    of the fixpoint completes them; kept records equal the oracle's."""
+    kept = eps_kept = 0
+    for seed in range(30):
+        rng = np.random.default_rng(72_000 + seed)
+        g = synth.random_graph(seed + 900, n=int(rng.integers(20, 60)), deg=(1, int(rng.integers(3, 8))),
+                               vocab=int(rng.integers(3, 8)), epsilon=True, eps_levels=8, eps_share=0.5)
+        B, T = int(rng.integers(1, 4)), int(rng.integers(1, 12))
+        lp = synth.random_logprobs(seed + 901, B, T, g.vocab, sigma=float(rng.uniform(0.5, 2.0)))
+        L = rng.integers(1, T + 1, size=B).astype(np.int32)
+        P = int(rng.integers(1, 3))
+        _say("lattice deep epsilon", seed, lp.shape, P)
+        _, lats = lattice_case(g, lp, L, 1e10, 1000, 0, True, float(rng.choice([1.0, 5.0])), eps_iterations=P)
+        kept += sum(x.shape[0] for x in lats)
+        eps_kept += sum(int((x[:, 7] == 4).sum()) for x in lats)
+    assert kept > 100 and eps_kept > 50
 
 
 def _long_case():

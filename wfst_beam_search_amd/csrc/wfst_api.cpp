@@ -651,6 +651,7 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
         take(&w.lat_state, L * nodes);
         take(&w.lat_bwd, L * nodes);
         take(&w.lat_epass, L * nodes);
+        take(&w.lat_chg, L);
         take(&w.lat_out, L * z.lat_cap * kLatFields);
         if (z.P > 0)
             for (int p = 0; p < 2; ++p) take(&w.chg_pos[p], L * std::max<uint64_t>(z.CC, Q));
@@ -797,7 +798,11 @@ static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &
         if ((e = go(kKLatInit, 0, 0)) != hipSuccess) return e;
         for (int t = steps - 1; t >= 0; --t) {
             if ((e = go(kKLatBack, t, 0)) != hipSuccess) return e;
-            if (passes > 0 && (e = go(kKLatEpsBack, t, 0)) != hipSuccess) return e;
+            if (passes <= 0) continue;
+            const int rounds = std::min(passes, 3) + 1;
+            for (int k = 1; k <= rounds; ++k)
+                if ((e = go(kKLatEpsRound, t, k == rounds ? 1 : 0)) != hipSuccess) return e;
+            if ((e = go(kKLatEpsBack, t, 0)) != hipSuccess) return e;
         }
     }
     return go(kKBacktrack, 0, 0);

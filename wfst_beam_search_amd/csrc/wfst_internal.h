@@ -227,6 +227,7 @@ struct Work {
     int32_t *lat_state;       // [L][lat_nodes] state of each node
     uint32_t *lat_bwd;        // [L][lat_nodes] ordered backward score of each node
     uint8_t *lat_epass;       // [L][lat_nodes] last closure pass whose sources included the node
+    uint32_t *lat_chg;        // [L] the last flat epsilon round of the final pass raised a score
     int32_t *lat_out;         // [L][lat_cap][kLatFields] kept records
     int32_t *chg_pos[2];      // [L][chg_cap] frontier position of each closure source (lattice mode)
     // blank-skip pre-slicing
@@ -253,7 +254,7 @@ enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
     kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
-    kKLatEpsBack, kKLatPrune, kKCount
+    kKLatEpsBack, kKLatPrune, kKLatEpsRound, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

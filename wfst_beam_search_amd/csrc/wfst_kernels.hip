@@ -1783,6 +1783,8 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
         }
         tab_publish(tab, w.max_lanes, units);
     }
+    // (the flags of the frame's flat epsilon rounds start clear)
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes && w.lat_chg) w.lat_chg[threadIdx.x] = 0u;
     __syncthreads();
     const int nl = w.max_lanes;
     const int lane = wlane();
@@ -1865,6 +1867,7 @@ constexpr int kLatBatch = 8;                  // step-arc records per thread per
 constexpr int kLatEpsRegs = 8;                // epsilon-slot records per thread per load round (half in the prune)
 constexpr uint32_t kLatEpsLdsNodes = 35840;   // frame nodes whose backward scores fit in LDS (140 KiB)
 constexpr int kMaxPruneInterval = 512;        // 2N + 1 step offsets fit the workgroup's table
+constexpr int kLatKeepBlocks = 256;           // workgroups of the final pass's flat epsilon keep
 
 struct SweepShared {
     uint32_t bwd[kLatEpsLdsNodes];               // one frame's backward scores (epsilon fixpoint)
@@ -2101,23 +2104,127 @@ __device__ void sweep_eps(const Work &w, LaneCtl &c, const SweepLane &s, SweepSh
     }
 }
 
-// The final backward pass over frame t's epsilon arcs (records of slot t with
-// a pass > 0), launched after k_lat_back(t) on graphs with epsilon arcs: one
-// workgroup per lane with a result and a complete lattice (step 3 of the
-// sweep above, threshold best - output_beam).
+// The final pass over frame t's epsilon arcs (records of slot t with a pass
+// > 0) on graphs with epsilon arcs, after k_lat_back(t): R flat rounds over
+// every lane's records (k_lat_eps_round: each record once per round,
+// bwd(src) = max(bwd(src), weight + bwd(dst)), any order; the last round
+// records per lane whether it raised a score), then k_lat_eps_back: a lane
+// whose last round raised nothing has reached the least fixpoint (no record can
+// raise a score: each was tried against scores no one changed) and its records
+// are kept flat over the grid; a lane whose last round raised a score gets a
+// workgroup that runs the fixpoint to its end and keeps its records itself.
+// Frames of tens of thousands of records (the largest lane's sets the time of
+// a per-lane pass) are so spread over every CU; R = min(passes, 3) + 1 rounds
+// settle chains of up to R - 1 epsilon arcs without a finishing workgroup.
+
+// Lane table of the flat epsilon passes of frame t: records [aoff[t],
+// aoff[t + 1]) of lanes with a result and a complete lattice (and, for the
+// keep, whose last round raised no score); tab.fb = first record, tab.arcs =
+// the frame's first node, tab.win = its node count, tab.f1 = the threshold.
+__device__ __forceinline__ void eps_tab(const Work &w, LaneTab &tab, int t, bool keep)
+{
+    if (threadIdx.x >= kWave) return;
+    const int L = (int)threadIdx.x;
+    const size_t F = (size_t)w.max_frames + 3;
+    uint32_t units = 0;
+    if (L < w.max_lanes) {
+        const LaneCtl &c = w.ctl[L];
+        bool on = lane_has_result(c) && t <= c.last_step && lat_complete(w, c);
+        if (keep && on) on = w.lat_chg[L] == 0u;
+        const uint32_t a0 = on ? w.lat_aoff[(size_t)L * F + t] : 0u;
+        const uint32_t a1 = on ? min(w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap) : 0u;
+        const uint32_t n = a1 > a0 ? a1 - a0 : 0u;
+        const uint32_t nb = on ? w.lat_nbase[(size_t)L * F + t] : 0u;
+        units = (n + kWave - 1) / kWave;
+        tab.n[L] = n;
+        tab.fb[L] = a0;
+        tab.arcs[L] = nb;
+        tab.win[L] = on ? (int32_t)(w.lat_nbase[(size_t)L * F + t + 1] - nb) : 0;
+        tab.f1[L] = c.final_score - w.output_beam;
+    }
+    tab_publish(tab, w.max_lanes, units);
+}
+
+__global__ __launch_bounds__(kBlock) void k_lat_eps_round(const Work *__restrict__ wp, int t, int last)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    eps_tab(w, tab, t, false);
+    __syncthreads();
+    const int nl = w.max_lanes;
+    uint32_t u_beg, u_end;
+    wave_share(tab.base[nl], &u_beg, &u_end);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        const uint32_t nn = (uint32_t)tab.win[L];
+        int4 r = make_int4(0, 0, 0, 0);
+        if (i < tab.n[L]) r = w.lat_arc[(size_t)L * w.lat_cap + tab.fb[L] + i];
+        if (!(r.w > 0 && (uint32_t)r.x < nn && (uint32_t)r.z < nn)) continue;
+        uint32_t *bwd = w.lat_bwd + (size_t)L * w.lat_nodes + tab.arcs[L];
+        const float v = w.arc_dlw[r.y].weight + ord2f(load_bwd(&bwd[(uint32_t)r.z]));
+        if (!(v > -__builtin_inff())) continue;
+        const uint32_t o = f2ord(v);
+        if (last) {
+            if (atomicMax(&bwd[(uint32_t)r.x], o) < o) w.lat_chg[L] = 1u;
+        } else {
+            atomicMax(&bwd[(uint32_t)r.x], o);
+        }
+    }
+}
+
+// Workgroups 0 .. max_lanes - 1: the finishing workgroup of lane blockIdx.x
+// (when its last round raised a score); the rest: the flat keep of every other
+// lane's records.
 __global__ __launch_bounds__(kLatSweepBlock) void k_lat_eps_back(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
-    const int L = (int)blockIdx.x;
-    if (L >= w.max_lanes) return;
-    LaneCtl &c = w.ctl[L];
-    if (!lane_has_result(c) || t > c.last_step || !lat_complete(w, c)) return;
-    __shared__ SweepShared sh;
-    const size_t FF = (size_t)w.max_frames + 3;
-    const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
-    const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
-    const SweepLane s = sweep_lane(w, L, c.final_score - w.output_beam);
-    sweep_eps<false, kLatEpsRegs>(w, c, s, sh, t, aoff[t], min(aoff[t + 1], w.lat_cap), nbase[t], nbase[t + 1] - nbase[t]);
+    __shared__ union {
+        SweepShared sweep;
+        LaneTab tab;
+    } sh;
+    const int nl = w.max_lanes;
+    if ((int)blockIdx.x < nl) {
+        const int L = (int)blockIdx.x;
+        LaneCtl &c = w.ctl[L];
+        if (w.lat_chg[L] == 0u || !lane_has_result(c) || t > c.last_step || !lat_complete(w, c)) return;
+        const size_t FF = (size_t)w.max_frames + 3;
+        const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+        const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
+        const SweepLane s = sweep_lane(w, L, c.final_score - w.output_beam);
+        sweep_eps<false, kLatEpsRegs>(w, c, s, sh.sweep, t, aoff[t], min(aoff[t + 1], w.lat_cap), nbase[t],
+                                      nbase[t + 1] - nbase[t]);
+        return;
+    }
+    LaneTab &tab = sh.tab;
+    eps_tab(w, tab, t, true);
+    __syncthreads();
+    // this wavefront's equal share of the keep blocks' units
+    const uint32_t wpb = kLatSweepBlock / kWave;
+    const uint32_t nwaves = (gridDim.x - (uint32_t)nl) * wpb;
+    const uint32_t wid = (blockIdx.x - (uint32_t)nl) * wpb + threadIdx.x / kWave;
+    const uint32_t total = tab.base[nl];
+    const uint32_t u_beg = (uint32_t)(((unsigned long long)total * wid) / nwaves);
+    const uint32_t u_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
+    for (uint32_t u = u_beg; u < u_end; ++u) {
+        const int L = find_lane(tab.base, nl, u);
+        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)wlane();
+        const uint32_t nn = (uint32_t)tab.win[L];
+        const SweepLane s = sweep_lane(w, L, tab.f1[L]);
+        int4 r = make_int4(0, 0, 0, 0);
+        if (i < tab.n[L]) r = s.rec[tab.fb[L] + i];
+        const bool on = r.w > 0 && (uint32_t)r.x < nn && (uint32_t)r.z < nn;
+        const uint32_t se = tab.arcs[L] + (uint32_t)r.x;
+        float wt = 0.0f, fw = 0.0f, bd = 0.0f;
+        int ep = 0;
+        if (on) {
+            wt = w.arc_dlw[r.y].weight;
+            fw = s.fwd[se];
+            ep = (int)s.epass[se];
+            bd = ord2f(s.bwd[tab.arcs[L] + (uint32_t)r.z]);
+        }
+        eps_keep<false>(w, w.ctl[L], s, t, on, r, tab.fb[L] + i, se, wt, fw, bd, ep);
+    }
 }
 
 // Interval prune (page section 7, lat_prune_interval = N: a window-loose prune
@@ -2921,7 +3028,10 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         if (f16) go(k_lat_back<__half>, G, B, s, e0, e1, dw, t);
         else go(k_lat_back<float>, G, B, s, e0, e1, dw, t);
         break;
-    case kKLatEpsBack: go(k_lat_eps_back, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t); break;
+    case kKLatEpsRound: go(k_lat_eps_round, G, B, s, e0, e1, dw, t, k); break;
+    case kKLatEpsBack:
+        go(k_lat_eps_back, dim3(w.max_lanes + kLatKeepBlocks), dim3(kLatSweepBlock), s, e0, e1, dw, t);
+        break;
     case kKGcBegin: go(k_gc_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
     case kKGcMark: go(k_gc_mark, G, B, s, e0, e1, dw); break;
     case kKGcScan: go(k_gc_scan, dim3(w.max_lanes), dim3(kGcScanBlock), s, e0, e1, dw); break;
