@@ -390,6 +390,33 @@ def config_summary(wid, steps, warmup, cpu_seconds, dev):
     return out
 
 
+def run_probes() -> dict:
+    """Machine probes (libwfst_probe.so, built with the decoder): the random-line
+    rate, the latency of a dependent load, posted 64-bit atomics and the launch
+    floor on this GPU."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(os.path.join(ROOT, "wfst_beam_search_amd", "libwfst_probe.so"))
+    out = (ctypes.c_double * 24)()
+    rc = lib.wfst_probe_run(out, 24)
+    if rc != 0:
+        raise RuntimeError(f"wfst_probe_run failed ({rc})")
+    v = list(out)
+    res = {"gather": [], "atomic_max_u64": []}
+    for j, mb in enumerate((4, 32, 128, 512, 1024, 4096)):
+        us, glines, lvl = v[3 * j: 3 * j + 3]
+        res["gather"].append({"footprint_mib": mb, "us_per_launch": round(us, 2),
+                              "random_lines_per_s_G": round(glines, 2), "dependent_level_us": round(lvl, 3),
+                              "loads_per_launch": 1024 * 256 * 4})
+    for j, mb in enumerate((8, 512)):
+        us, gat = v[18 + 2 * j: 20 + 2 * j]
+        res["atomic_max_u64"].append({"table_mib": mb, "us_per_launch": round(us, 2),
+                                      "atomics_per_s_G": round(gat, 2), "atomics_per_launch": 1024 * 256})
+    res["launch_floor_us"] = {"eager": round(v[22], 3), "graph_replay": round(v[23], 3)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,10 +463,16 @@ def main():
                     help="also run these workloads at full size after the headline one (comma list; "
                          "empty: none) and report them in the line's `configs` object")
     ap.add_argument("--config-steps", type=int, default=5, help="timed decodes per extra workload")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the machine probes (random gathers over 4 MiB - 4 GiB, dependent "
+                         "load chains, posted 64-bit atomics, the launch floor) and print them as JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE readings to bytes)")
     args = ap.parse_args()
+    if args.probe:
+        print(json.dumps(run_probes()))
+        return
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20

@@ -25,15 +25,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# machine probes (random gathers, dependent chains, atomics, launch floor) for
+# bench.py --probe: a library of their own, not part of the decoder
+PROBE_LIB = os.path.join(HERE, "libwfst_probe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "wfst_probe.hip")]
+
+
+def _compile(out: str, sources, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *SOURCES]
+           "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(LIB, SOURCES, verbose)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 
