@@ -218,7 +218,8 @@ struct Work {
     uint32_t lat_nodes;       // lattice nodes per lane: max(arena, lat_cap) + 1 (without log compaction every
                               //   token but the start one has its own entry, so arena + 1 suffice; a lane
                               //   past it has an incomplete lattice)
-    int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position, closure pass
+    int4 *lat_arc;            // [L][lat_cap] {source position, arc, destination position (its state |
+                              //   kLatUnresolved until the next compaction maps it), closure pass
                               //   (0: an arc of the step itself)}
     uint32_t *lat_aoff;       // [L][max_frames + 3] first lattice arc of step t at [t + 1] (t = -1: the
                               //   start closure); step t's arcs are followed by its closure's
@@ -244,6 +245,10 @@ struct Work {
 // Fields of a kept lattice record (int32 each).
 enum : int32_t { kLatFrame = 0, kLatSrc, kLatDst, kLatIlabel, kLatArc, kLatScore, kLatLane, kLatFlags,
                  kLatFields = 8 };
+
+// A persisted lattice arc's destination field while it still holds a state
+// (state | kLatUnresolved) rather than the destination's frontier position.
+constexpr uint32_t kLatUnresolved = 0x80000000u;
 
 // Per-lane stream command of a launch sequence (written by the host).
 enum : int32_t { kPlanCmd = 0, kPlanLen, kPlanRow, kPlanWant, kPlanFields = 4 };

@@ -1198,27 +1198,35 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         }
         const unsigned long long am = __ballot(adm);
         if (lane == 0 && am) atomicAdd(step_rec(w, L, t) + kRecAdmitted, (uint32_t)__popcll(am));
+        // lattice mode: every admitted candidate is a lattice arc {source
+        // position, arc, destination, pass 0}, its record written once the
+        // destination is known: a winner's position in the new frontier, else
+        // (recombination losers, final arcs) its state marked unresolved
+        // (kLatUnresolved), mapped to the position by the next compaction
+        uint32_t lat_i = 0xFFFFFFFFu;
         if (w.lattice && am) {
-            // lattice mode: every admitted candidate is a lattice arc (source
-            // position, arc, destination state: resolved to its position later)
             uint32_t lb0 = 0u;
             if (lane == 0) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
             lb0 = __shfl(lb0, 0, kWave);
             if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
                 if (lane == 0) atomicOr(&c.overflow, kOvfArena);
             } else if (adm) {
-                w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
-                    make_int4((int)cl.tok, cl.arc, (int32_t)dest_state(w, cl.dest), 0);
+                lat_i = lb0 + (uint32_t)__popcll(am & mask_lt());
             }
         }
+        const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
+        int32_t lat_z = (int32_t)(cds | kLatUnresolved);
+        auto lat_put = [&]() {
+            if (lat_i != 0xFFFFFFFFu) w.lat_arc[(size_t)L * w.lat_cap + lat_i] = make_int4((int)cl.tok, cl.arc, lat_z, 0);
+        };
         if (tab.ph[L] == kPhFinal) {
+            lat_put();
             if (adm && cand_key(__uint_as_float(cl.score), cl.arc) == c.final_key)
                 final_entry(w, c, L, p, c.final_key, (int32_t)cl.tok);
             continue;
         }
         // with epochs only admitted candidates need the table (stale entries of
         // earlier rounds always lose); without, every owner clears its entry
-        const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
         if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
             if (recomb_key<HASH>(w, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
                 if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
@@ -1281,7 +1289,10 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         }
         lb_acc = fmaxf(lb_acc, lbv);
         const unsigned long long m = __ballot(keep);
-        if (m == 0ull) continue;
+        if (m == 0ull) {
+            lat_put();
+            continue;
+        }
         const uint32_t nkeep = (uint32_t)__popcll(m);
         const uint32_t rank = (uint32_t)__popcll(m & mask_lt());
         uint32_t dsum;
@@ -1310,10 +1321,12 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 c.status = kDone;
                 c.phase_final = kPhDead;
             }
+            lat_put();
             continue;
         }
         if (keep) {
             const uint32_t pi = p0 + rank;
+            lat_z = (int32_t)pi;
             const size_t q = (size_t)L * Q + pi;
             const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
             w.wlog[e] = make_int2(esrc, arc);
@@ -1341,11 +1354,13 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 if (w.lattice) w.chg_pos[1][ci] = (int32_t)pi;
             }
         }
+        lat_put();
         write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
     }
     post_bound(w, lb_lane, lb_np, lb_acc);
     if (w.lattice) {
-        // the step before's lattice arcs: destination state -> position among the
+        // the step before's unresolved lattice arcs (its recombination losers and
+        // its closure's epsilon arcs): destination state -> position among the
         // tokens of frame t (the parity this compaction reads)
         uint32_t v_beg, v_end;
         wave_share(lt.base[nl], &v_beg, &v_end);
@@ -1355,8 +1370,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             const uint32_t i = (u - lt.base[L]) * kWave + (uint32_t)lane;
             if (i >= lt.n[L]) continue;
             int4 *r = w.lat_arc + (size_t)L * w.lat_cap + lt.a0[L] + i;
-            const int32_t d = r->z;
-            if ((uint32_t)d < (uint32_t)w.num_states) r->z = pick(w.pos, p)[(size_t)L * w.num_states + d];
+            const uint32_t d = (uint32_t)r->z;
+            if ((d & kLatUnresolved) && (d & ~kLatUnresolved) < (uint32_t)w.num_states)
+                r->z = pick(w.pos, p)[(size_t)L * w.num_states + (d & ~kLatUnresolved)];
         }
     }
 }
@@ -1500,7 +1516,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
                         if (lane == lead) atomicOr(&c.overflow, kOvfArena);
                     } else if (adm) {
                         w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
-                            make_int4(sps, a, (int32_t)dest_state(w, dd), k);
+                            make_int4(sps, a, (int32_t)(dest_state(w, dd) | kLatUnresolved), k);
                     }
                 }
             }
@@ -1957,7 +1973,8 @@ __device__ __forceinline__ void sweep_step(const Work &w, const SweepLane &s, ui
             fw[k] = 0.0f;
             if (r[k].w != 0) continue;
             sa[k] = ad[k].weight + lp_at(row, ad[k].ilabel);
-            const uint32_t dn = nd + (uint32_t)(dpos ? dpos[r[k].z] : r[k].z);
+            const uint32_t dz = (uint32_t)r[k].z;
+            const uint32_t dn = nd + ((dpos && (dz & kLatUnresolved)) ? (uint32_t)dpos[dz & ~kLatUnresolved] : dz);
             bd[k] = ord2f(load_bwd(&s.bwd[dn]));
             fw[k] = s.fwd[ns + (uint32_t)r[k].x];
         }
