@@ -1943,22 +1943,30 @@ __device__ __forceinline__ void sweep_clear(const SweepLane &s, uint32_t n0, uin
     for (uint32_t i = n0 + threadIdx.x; i < n1; i += kLatSweepBlock) s.bwd[i] = kOrdNegInf;
 }
 
+// One batch of step-arc records of the prune, [b0, a1) strided over the
+// workgroup (positions past a1 read as pass 1, so they are skipped).
+__device__ __forceinline__ void load_batch(const SweepLane &s, uint32_t b0, uint32_t a1, int4 (&r)[kLatBatch])
+{
+#pragma unroll
+    for (int k = 0; k < kLatBatch; ++k) {
+        const uint32_t i = b0 + (uint32_t)k * kLatSweepBlock + threadIdx.x;
+        r[k] = i < a1 ? s.rec[i] : make_int4(0, 0, 0, 1);
+    }
+}
+
 // Step f's arcs in the prune: records [a0, a1), those with pass 0 (step 2 of
 // the sweep). Sources are nodes ns + position, destinations nd + position;
-// dpos: non-null when the destination fields still hold states (the newest
-// step of a running lane), mapped to positions by it.
+// dpos: non-null when the destination fields may still hold states (the
+// newest step of a running lane), mapped to positions by it. r holds the first
+// batch, loaded ahead by the caller.
 template <typename LPT>
 __device__ __forceinline__ void sweep_step(const Work &w, const SweepLane &s, uint32_t a0, uint32_t a1,
-                                           uint32_t ns, uint32_t nd, const int32_t *dpos, const LPT *row)
+                                           uint32_t ns, uint32_t nd, const int32_t *dpos, const LPT *row,
+                                           int4 (&r)[kLatBatch])
 {
     const uint32_t tid = threadIdx.x;
     for (uint32_t b0 = a0; b0 < a1; b0 += (uint32_t)kLatBatch * kLatSweepBlock) {
-        int4 r[kLatBatch];
-#pragma unroll
-        for (int k = 0; k < kLatBatch; ++k) {
-            const uint32_t i = b0 + (uint32_t)k * kLatSweepBlock + tid;
-            r[k] = i < a1 ? s.rec[i] : make_int4(0, 0, 0, 1);
-        }
+        if (b0 != a0) load_batch(s, b0, a1, r);
         ArcDLW ad[kLatBatch];
 #pragma unroll
         for (int k = 0; k < kLatBatch; ++k) {
@@ -2285,18 +2293,28 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
     const uint32_t nf0 = nbase[F];
     for (uint32_t i = nf0 + tid; i < nf0 + nF; i += kLatSweepBlock) s.bwd[i] = f2ord(0.0f - s.fwd[i]);
     __syncthreads();
+    int4 r[kLatBatch];
+    load_batch(s, sh.off0[F - W], cursor, r);   // the newest step's first batch
     for (int f = F - 1; f >= W; --f) {
         const uint32_t ns = sh.nb0[f - W], nd = sh.nb0[f + 1 - W];
         sweep_clear(s, ns, nd);
         __syncthreads();
         const uint32_t a0 = sh.off0[f + 1 - W], a1 = (f + 1 < F) ? sh.off0[f + 2 - W] : cursor;
+        // the next frame's step arcs (none after frame W): their first batch is
+        // loaded as soon as this frame no longer needs r, so the loads overlap
+        // the rest of the frame (which changes no pass-0 record of them: it
+        // marks this frame's own records and its epsilon records only)
+        const uint32_t n0 = f > W ? sh.off0[f - W] : 0u, n1 = f > W ? sh.off0[f + 1 - W] : 0u;
         const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)f * d.stride_t;
-        sweep_step<LPT>(w, s, a0, a1, ns, nd, (f + 1 < F) ? nullptr : posF, row);
-        __syncthreads();
+        sweep_step<LPT>(w, s, a0, a1, ns, nd, (f + 1 < F) ? nullptr : posF, row, r);
         if (w.has_eps) {
-            sweep_eps<true, kLatEpsRegs / 2>(w, c, s, sh, f, sh.off0[f - W], sh.off0[f + 1 - W], ns, nd - ns);
             __syncthreads();
+            sweep_eps<true, kLatEpsRegs / 2>(w, c, s, sh, f, sh.off0[f - W], sh.off0[f + 1 - W], ns, nd - ns);
+            load_batch(s, n0, n1, r);
+        } else {
+            load_batch(s, n0, n1, r);
         }
+        __syncthreads();
     }
     // in-place compaction of [off0[0], cursor), kLatBatch records per thread (a
     // contiguous run) per chunk: every record of a chunk is read before any is
@@ -2306,7 +2324,6 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
     constexpr uint32_t kChunk = (uint32_t)kLatBatch * kLatSweepBlock;
     const uint32_t wv = tid / kWave;
     uint32_t out = sh.off0[0];
-    int4 r[kLatBatch];
     auto load_chunk = [&](uint32_t b, int4 (&x)[kLatBatch]) {
 #pragma unroll
         for (int k = 0; k < kLatBatch; ++k) {
