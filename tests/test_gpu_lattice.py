@@ -275,3 +275,48 @@ def test_lattice_capacity_and_rejections():
     wb.Decoder(deg_, 8.0, 100, eps_iterations=2).close()       # (1-best decoding takes it)
     deg_.release()
     dg.release()
+
+
+def test_lattice_with_the_recombination_hash():
+    """Lattice mode over the open-addressing recombination hash (64 slots per
+    lane: long probe chains) on random epsilon-free and TLG graphs, with and
+    without the interval prune: kept records equal the oracle's."""
+    kept = 0
+    for seed in range(24):
+        if seed % 2:
+            g, lp, L, beam, ma, mi, ap, ob, P = _random_tlg_case(400 + seed)
+        else:
+            g, lp, L, beam, ma, mi, ap, ob = _random_case(400 + seed)
+            P = 0
+        n = (0, 2, 0, 3)[seed % 4]
+        _say("lattice hash", seed, lp.shape, P, n)
+        _, lats = lattice_case(g, lp, L, beam, ma, mi, ap, ob, eps_iterations=P, recomb_slots=64,
+                               lat_prune_interval=n)
+        kept += sum(x.shape[0] for x in lats)
+    assert kept > 100
+
+
+def test_lattice_tlg_workload_interval_prune():
+    """The TLG workload at full size with the interval prune every 32 steps
+    (output beam 4): sampled lanes' kept records equal the oracle's with the
+    same interval, epsilon records among them."""
+    cid = 4
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    _say("lattice tlg workload prune", lp.shape)
+    _, lats = lattice_case(g, lp, L, wl.beam, wl.max_active, 0, False, 4.0, eps_iterations=wl.eps_iterations,
+                           lanes=[3, 12], arena_entries=16 << 20, lat_prune_interval=32)
+    assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
+def test_lattice_epsilon_graph_with_log_compaction():
+    """A 300-frame TLG-style decode in lattice mode with log compaction every
+    16 steps and the interval prune every 8: kept records and 1-best results
+    equal the oracle's while a winners log of 4000 entries per lane suffices."""
+    g = synth.random_graph(7, n=40, deg=(1, 6), vocab=6, epsilon=True, eps_levels=3, eps_share=0.3)
+    lp = synth.random_logprobs(8, 2, 300, g.vocab, sigma=2.0)
+    L = np.array([300, 277], dtype=np.int32)
+    r, lats = lattice_case(g, lp, L, 6.0, 100, 0, False, 2.0, eps_iterations=2, gc_interval=16,
+                           arena_entries=4000, lat_prune_interval=8)
+    assert all(int(r.meta[b, 2]) == 0 for b in range(2))
+    assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)

@@ -2613,7 +2613,7 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
 // Whether lane c's round runs: it ran a real step in this sequence and is
 // active (lattice nodes are frame positions, never log entries, so lattices
 // do not hold the log back).
-__device__ __forceinline__ bool gc_due(const Work &w, const LaneCtl &c)
+__device__ __forceinline__ bool gc_due(const LaneCtl &c)
 {
     return c.status == kActive && c.last_step >= 0 && c.last_step < c.T;
 }
@@ -2626,7 +2626,7 @@ __global__ __launch_bounds__(kWave) void k_gc_begin(const Work *__restrict__ wp)
     const int L = (int)threadIdx.x;
     if (L >= w.max_lanes) return;
     LaneCtl &c = w.ctl[L];
-    const bool on = gc_due(w, c);
+    const bool on = gc_due(c);
     c.gc_on = on ? 1u : 0u;
     if (!on) return;
     const int p = lane_par(c, c.last_step + 1);
