@@ -33,6 +33,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# kernels of the epsilon closure, timed and charged as one group
+CLOSURE_KERNELS = ("eps_expand", "eps_apply", "eps_apply_expand")
+
+
 def algorithmic_bytes(st, elem_bytes, vocab):
     """Bytes the method must move per decode, from the device step counters.
 
@@ -66,8 +70,9 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     per = {
         "max": 20 * n + 6 * S + 12 * C + row,
         "finalize": 28 * D + 20 * D,
-        "eps_expand": 8 * E + 12 * Ce,
-        "eps_apply": 28 * De + 20 * Ne,
+        # the closure's kernels (a pass's relaxation, its resolution, and the
+        # launches that resolve pass k while they relax pass k + 1) as one group
+        "closure": 8 * E + 12 * Ce + 28 * De + 20 * Ne,
     }
     path = sum(per.values())
     design = {"candidate_records": 32 * st["listed"], "state_records": 64 * D, "token_records": 16 * n}
@@ -562,6 +567,12 @@ def main():
         dec.profile(False)
         ktimes = {k: {"total_ms_per_decode": v[0] / args.steps, "launches_per_decode": v[1] // args.steps,
                       "avg_launch_us": (v[0] / v[1] * 1e3) if v[1] else 0.0} for k, v in acc.items()}
+        cl = [ktimes[k] for k in CLOSURE_KERNELS if k in ktimes and ktimes[k]["launches_per_decode"]]
+        if cl:
+            tot = sum(x["total_ms_per_decode"] for x in cl)
+            nl = sum(x["launches_per_decode"] for x in cl)
+            ktimes["closure"] = {"total_ms_per_decode": tot, "launches_per_decode": nl,
+                                 "avg_launch_us": tot / nl * 1e3 if nl else 0.0}
         dom = max((k for k in ktimes if k in per_kernel_bytes), key=lambda k: ktimes[k]["total_ms_per_decode"])
         launches = ktimes[dom]["launches_per_decode"]
         avg_s = ktimes[dom]["avg_launch_us"] * 1e-6

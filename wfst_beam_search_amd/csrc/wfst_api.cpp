@@ -587,6 +587,9 @@ static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &
     w.lat_prune_interval = c.lattice ? c.lat_prune_interval : 0;
     w.gc_interval = c.gc_interval;
     w.chg_cap = (uint32_t)std::max<uint64_t>(z.CC, z.Q);
+    // two recombination tables and candidate lists where closure passes run
+    // (a kernel resolves pass k from one while it relaxes pass k + 1 into the other)
+    w.ntab = z.P > 0 ? 2 : 1;
     w.round_base = 0;
     w.wipe = 0;
     return WFST_OK;
@@ -619,13 +622,15 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
         take(&w.tok_state[p], L * Q); take(&w.tok_score[p], L * Q); take(&w.tok_entry[p], L * Q);
         take(&w.tok_last[p], L * Q); take(&w.tok_off[p], L * Q); take(&w.tok_abeg[p], L * Q);
         take(&w.tok_ub[p], L * Q); take(&w.strip_tok[p], L * z.strip_cap);
+        if (z.P > 0) take(&w.tok_tag[p], L * Q);
         // state -> position maps: read by the closure and the lattice only
         if (w.has_eps || c.lattice) take(&w.pos[p], L * S);
         if (z.P > 0) take(&w.changed[p], L * std::max<uint64_t>(z.CC, Q));
     }
-    if (w.hash_bits) take(&w.hash, L << w.hash_bits);
-    else take(&w.best, L * S);
-    take(&w.claims, L * z.CC);
+    const size_t nt = (size_t)w.ntab;
+    if (w.hash_bits) take(&w.hash, nt * (L << w.hash_bits));
+    else take(&w.best, nt * L * S);
+    take(&w.claims, nt * L * z.CC);
     take(&w.res, L * (size_t)w.res_stride);
     take(&w.steps, L * (size_t)(c.max_frames + 2) * kStepFields);
     if (!full) {
@@ -715,8 +720,8 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
 
     hipError_t e = hipMemset(d->ctl, 0, sizeof(LaneCtl) * L);
     if (e == hipSuccess) e = hipMemcpy(d->d_work, &w, sizeof(Work), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = w.hash_bits ? hipMemset(w.hash, 0, sizeof(HSlot) * (L << w.hash_bits))
-                                          : hipMemset(w.best, 0, sizeof(unsigned long long) * L * S);
+    if (e == hipSuccess) e = w.hash_bits ? hipMemset(w.hash, 0, sizeof(HSlot) * w.ntab * (L << w.hash_bits))
+                                          : hipMemset(w.best, 0, sizeof(unsigned long long) * w.ntab * L * S);
     for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemset(w.pos[p], 0xFF, 4 * L * S);
     if (e == hipSuccess) e = hipHostMalloc(&d->h_in, sizeof(LpDesc) + 4 * L, hipHostMallocDefault);
     if (e == hipSuccess) e = hipHostMalloc((void **)&d->h_res, 4 * L * (size_t)w.res_stride, hipHostMallocDefault);
@@ -758,34 +763,51 @@ static hipError_t launch(wfst_decoder_s *d, int id, int t, int k, hipStream_t s)
 // every epoch_period rounds: the whole table is cleared before such a round (a
 // decode whose rounds pass a multiple of the period starts at one, with the
 // table wiped, and uses every round after its round 0).
+// Closure passes 1..P of step t (t = -1: the start closure). Pass k + 1's
+// relaxation runs in pass k's resolving launch (kKEpsApplyExpand) unless a
+// table clear is due before round (t, k + 1): the clear must fall between the
+// two. clear(t, k) enqueues the clear due before round (t, k), if any;
+// clear_due(t, k) says whether one is.
+template <typename Go, typename Due, typename Clear>
+static hipError_t enqueue_closure(int t, int P, Go &&go, Due &&clear_due, Clear &&clear)
+{
+    hipError_t e;
+    bool relaxed = false;   // pass k's relaxation ran in the launch before
+    for (int k = 1; k <= P; ++k) {
+        if (!relaxed) {
+            if ((e = clear(t, k)) != hipSuccess) return e;
+            if ((e = go(kKEpsExpand, t, k)) != hipSuccess) return e;
+        }
+        const bool fuse = k < P && !clear_due(t, k + 1);
+        if (fuse && (e = clear(t, k + 1)) != hipSuccess) return e;   // (none due: bookkeeping only)
+        if ((e = go(fuse ? kKEpsApplyExpand : kKEpsApply, t, k)) != hipSuccess) return e;
+        relaxed = fuse;
+    }
+    return hipSuccess;
+}
+
 template <typename Go>
 static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &&go)
 {
     hipError_t e;
-    auto wrap_clear = [&](int t, int k) -> hipError_t {
-        if (!w.epochs) return hipSuccess;
+    auto clear_due = [&](int t, int k) -> bool {
+        if (!w.epochs) return false;
         const long long q = (long long)(t + 1) * (1 + passes) + k;
-        if (q <= 0 || q % w.epoch_period != 0) return hipSuccess;
-        return go(kKClear, t, 1);
+        return q > 0 && q % w.epoch_period == 0;
+    };
+    auto wrap_clear = [&](int t, int k) -> hipError_t {
+        return clear_due(t, k) ? go(kKClear, t, 1) : hipSuccess;
     };
     if ((e = go(kKClear, 0, 0)) != hipSuccess) return e;
     if ((e = go(kKInit, 0, 0)) != hipSuccess) return e;
     // (the row maxima first: the start closure's tokens carry frame 0's in their bound)
     if ((e = go(kKLpmax, 0, 0)) != hipSuccess) return e;
-    for (int k = 1; k <= passes; ++k) {
-        if ((e = wrap_clear(-1, k)) != hipSuccess) return e;
-        if ((e = go(kKEpsExpand, -1, k)) != hipSuccess) return e;
-        if ((e = go(kKEpsApply, -1, k)) != hipSuccess) return e;
-    }
+    if ((e = enqueue_closure(-1, passes, go, clear_due, wrap_clear)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
         if ((e = wrap_clear(t, 0)) != hipSuccess) return e;
         if ((e = go(kKMax, t, 0)) != hipSuccess) return e;
         if ((e = go(kKFinalize, t, 0)) != hipSuccess) return e;
-        for (int k = 1; k <= passes; ++k) {
-            if ((e = wrap_clear(t, k)) != hipSuccess) return e;
-            if ((e = go(kKEpsExpand, t, k)) != hipSuccess) return e;
-            if ((e = go(kKEpsApply, t, k)) != hipSuccess) return e;
-        }
+        if ((e = enqueue_closure(t, passes, go, clear_due, wrap_clear)) != hipSuccess) return e;
         if (w.lat_prune_interval > 0 && (t + 1) % w.lat_prune_interval == 0 && t + 1 < steps &&
             (e = go(kKLatPrune, t, 0)) != hipSuccess) return e;
         if (w.gc_interval > 0 && (t + 1) % w.gc_interval == 0 && t + 1 < steps) {
@@ -1124,8 +1146,8 @@ extern "C" int wfst_decode_noalloc(wfst_graph_t g, const wfst_decoder_config *cp
     auto run = [&]() -> hipError_t {
         hipError_t e = hipMemsetAsync(x.ctl, 0, sizeof(LaneCtl) * L, s);
         if (e == hipSuccess)
-            e = w.hash_bits ? hipMemsetAsync(w.hash, 0, sizeof(HSlot) * (L << w.hash_bits), s)
-                            : hipMemsetAsync(w.best, 0, sizeof(unsigned long long) * L * S, s);
+            e = w.hash_bits ? hipMemsetAsync(w.hash, 0, sizeof(HSlot) * w.ntab * (L << w.hash_bits), s)
+                            : hipMemsetAsync(w.best, 0, sizeof(unsigned long long) * w.ntab * L * S, s);
         for (int p = 0; p < 2 && e == hipSuccess && w.pos[p]; ++p) e = hipMemsetAsync(w.pos[p], 0xFF, 4 * L * S, s);
         if (e == hipSuccess) e = launch_noalloc_put(w, hd, lens, (int)L, x.d_work, x.d_desc, x.d_lengths, s);
         if (e == hipSuccess)
@@ -1184,23 +1206,22 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
     // before each round it uses: a wipe when the round lies in a later epoch
     // period than the last round used (a captured sequence has none: see
     // stream_wraps)
-    auto wrap = [&](int t, int k) -> hipError_t {
-        if (!d->w.epochs) return hipSuccess;
+    auto wrap_due = [&](int t, int k) -> bool {
+        if (!d->w.epochs) return false;
         const uint64_t q = base + (uint64_t)((long long)(t + 1) * (1 + d->passes) + k);
         const uint64_t P = d->w.epoch_period;
-        const bool clear = last != kNoRound && last / P != q / P;
-        last = q;
+        return last != kNoRound && last / P != q / P;
+    };
+    auto wrap = [&](int t, int k) -> hipError_t {
+        if (!d->w.epochs) return hipSuccess;
+        const bool clear = wrap_due(t, k);
+        last = base + (uint64_t)((long long)(t + 1) * (1 + d->passes) + k);
         return clear ? launch(d, kKClear, t, 1, s) : hipSuccess;
     };
+    auto go = [&](int id, int t, int k) -> hipError_t { return launch(d, id, t, k, s); };
     if ((e = launch(d, kKClear, 0, 2, s)) != hipSuccess) return e;
     if ((e = launch(d, kKStreamBegin, 0, 0, s)) != hipSuccess) return e;
-    if (kind == kSeqOpen) {
-        for (int k = 1; k <= d->passes; ++k) {
-            if ((e = wrap(-1, k)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsExpand, -1, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsApply, -1, k, s)) != hipSuccess) return e;
-        }
-    }
+    if (kind == kSeqOpen && (e = enqueue_closure(-1, d->passes, go, wrap_due, wrap)) != hipSuccess) return e;
     if (kind == kSeqFinish && (e = launch(d, kKReclass, 0, 0, s)) != hipSuccess) return e;
     if (kind == kSeqAdvance && steps > 0 && (e = launch(d, kKLpmax, 0, 0, s)) != hipSuccess) return e;
     for (int t = 0; t < steps; ++t) {
@@ -1208,11 +1229,7 @@ static hipError_t enqueue_stream(wfst_decoder_s *d, int kind, int steps, hipStre
         if ((e = launch(d, kKMax, t, 0, s)) != hipSuccess) return e;
         if ((e = launch(d, kKFinalize, t, 0, s)) != hipSuccess) return e;
         if (kind != kSeqAdvance) continue;
-        for (int k = 1; k <= d->passes; ++k) {
-            if ((e = wrap(t, k)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsExpand, t, k, s)) != hipSuccess) return e;
-            if ((e = launch(d, kKEpsApply, t, k, s)) != hipSuccess) return e;
-        }
+        if ((e = enqueue_closure(t, d->passes, go, wrap_due, wrap)) != hipSuccess) return e;
         // every gc_interval steps and at the end of the chunk
         if (d->w.gc_interval > 0 && ((t + 1) % d->w.gc_interval == 0 || t + 1 == steps) &&
             (e = gc_round(d, s)) != hipSuccess) return e;

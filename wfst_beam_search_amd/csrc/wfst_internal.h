@@ -119,7 +119,6 @@ struct alignas(128) LaneCtl {
     uint32_t sealed;
     uint32_t gc_on;            // this round compacts the lane
     uint32_t gc_live;          // live entries of the window (after the scan)
-    uint32_t eps_n0;           // frontier tokens when the current closure pass began
     uint32_t log_full;         // 1: the winners log's committed bound stopped the lane
     alignas(128) unsigned long long cnt[2];  // frontier counter by parity: tokens | (arcs of the
                                              //   step's class) << 32
@@ -129,7 +128,9 @@ struct alignas(128) LaneCtl {
                                              //   candidate through each token's largest-weight arcs
                                              //   (posted by the compaction of the step before)
     alignas(128) uint32_t log_cursor;        // winners-log entries used in this lane's region
-    alignas(128) uint32_t nclaims_eps[2];    // admitted candidates of closure pass k at [k & 1]
+    alignas(128) uint32_t nclaims_eps[3];    // listed candidates of closure pass k at [k % 3] (three,
+                                             //   so a kernel that reads pass k's and appends pass
+                                             //   k + 1's can clear pass k + 2's)
     alignas(128) unsigned long long nchanged[2];  // closure pass k's sources at [k & 1]: entries of
                                                   //   its list (low half) | tokens appended or replaced
                                                   //   by the pass before it (high half; pass 1: unused)
@@ -186,6 +187,8 @@ struct Work {
     const int32_t *lengths;   // [L] device copy of the batch lengths
     float *lpmax;             // [L][max_frames]
     int32_t *tok_state[2];    // [L][Q] by parity
+    uint32_t *tok_tag[2];     // [L][Q] (graphs with epsilon arcs) the round that made the token:
+                              //   (the lane's frame << 5) | closure pass (0: the compaction)
     float *tok_score[2];
     int32_t *tok_entry[2];
     int32_t *tok_last[2];
@@ -197,10 +200,14 @@ struct Work {
                               //   arcs), else (score + largest weight) + the frame's largest log-prob;
                               //   score + largest final weight before a final step; +inf if unknown
     int32_t *pos[2];          // [L][num_states] state -> token index (validated on read)
-    unsigned long long *best; // [L][num_states] recombination keys (0 = unclaimed); null with the hash
-    HSlot *hash;              // [L][1 << hash_bits] recombination hash (hash_bits > 0), else null
+    unsigned long long *best; // [ntab][L][num_states] recombination keys (0 = unclaimed); null with
+                              //   the hash; round (t, k) uses table k & (ntab - 1)
+    HSlot *hash;              // [ntab][L][1 << hash_bits] recombination hash (hash_bits > 0), else null
     uint32_t hash_bits;       // 0: the direct-mapped table; else log2 of the hash slots per lane
-    Claim *claims;            // [L][CC]
+    Claim *claims;            // [ntab][L][CC] candidate lists: round (t, k) uses list k & (ntab - 1)
+    int32_t ntab;             // recombination tables and candidate lists: 2 on graphs with epsilon
+                              //   arcs (a kernel that resolves closure pass k while it relaxes pass
+                              //   k + 1 reads one and fills the other), else 1
     int4 *changed[2];         // [L][chg_cap] closure source lists by pass parity: the tokens with
                               //   epsilon arcs, {first epsilon arc, epsilon arcs, entry, score bits}
     uint32_t chg_cap;         // max(claims_cap, frontier_cap)
@@ -259,7 +266,7 @@ enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
     kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
-    kKLatEpsBack, kKLatPrune, kKLatEpsRound, kKCount
+    kKLatEpsBack, kKLatPrune, kKLatEpsRound, kKEpsApplyExpand, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

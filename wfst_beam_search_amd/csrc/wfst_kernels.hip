@@ -107,13 +107,24 @@ __device__ __forceinline__ uint32_t hash_first(const Work &w, uint32_t ds)
     return (ds * 0x9E3779B1u) >> (32u - w.hash_bits);
 }
 
+// On graphs with epsilon arcs there are two tables (and two candidate lists):
+// round (t, k) uses table k & 1, so a kernel that resolves closure pass k can
+// relax pass k + 1 into the other one. (One table otherwise: k is always 0.)
+__device__ __forceinline__ int round_tab(const Work &w, int k) { return k & (w.ntab - 1); }
+
+// Lane L's row of table tb.
+__device__ __forceinline__ size_t tab_row(const Work &w, int tb, int L)
+{
+    return (size_t)tb * (size_t)w.max_lanes + (size_t)L;
+}
+
 // (HASH: the kernels are compiled once per recombination structure, so the
 // default table path carries no probing code)
 template <bool HASH>
-__device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int L, uint32_t ds, uint32_t ep)
+__device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int tb, int L, uint32_t ds, uint32_t ep)
 {
-    if (!HASH) return w.best + (size_t)L * (size_t)w.num_states + ds;
-    HSlot *h = w.hash + ((size_t)L << w.hash_bits);
+    if (!HASH) return w.best + tab_row(w, tb, L) * (size_t)w.num_states + ds;
+    HSlot *h = w.hash + (tab_row(w, tb, L) << w.hash_bits);
     const uint32_t mask = (1u << w.hash_bits) - 1u;
     const unsigned long long want = ((unsigned long long)ep << 32) | ds;
     uint32_t i = hash_first(w, ds);
@@ -131,10 +142,10 @@ __device__ __forceinline__ unsigned long long *recomb_entry(const Work &w, int L
 // The key recorded for destination ds in round ep after the round's atomics
 // (0 when none: a table entry of an earlier round never equals a key of this one).
 template <bool HASH>
-__device__ __forceinline__ unsigned long long recomb_key(const Work &w, int L, uint32_t ds, uint32_t ep)
+__device__ __forceinline__ unsigned long long recomb_key(const Work &w, int tb, int L, uint32_t ds, uint32_t ep)
 {
-    if (!HASH) return w.best[(size_t)L * (size_t)w.num_states + ds];
-    const HSlot *h = w.hash + ((size_t)L << w.hash_bits);
+    if (!HASH) return w.best[tab_row(w, tb, L) * (size_t)w.num_states + ds];
+    const HSlot *h = w.hash + (tab_row(w, tb, L) << w.hash_bits);
     const uint32_t mask = (1u << w.hash_bits) - 1u;
     const unsigned long long want = ((unsigned long long)ep << 32) | ds;
     uint32_t i = hash_first(w, ds);
@@ -214,6 +225,15 @@ __device__ __forceinline__ void lat_node_overflow(const Work &w, LaneCtl &c)
 
 // Parity of the frontier that feeds lane c's step t of the sequence.
 __device__ __forceinline__ int lane_par(const LaneCtl &c, int t) { return (c.base + t) & 1; }
+
+// Tag of the tokens a round makes: (the lane's frame << 5) | closure pass, the
+// frame being the one step t builds (its closure included); the lane's frames
+// count on across a stream's calls. Passes are at most 16, frames wrap at 2^27.
+__device__ __forceinline__ uint32_t frame_tag(const LaneCtl &c, int t)
+{
+    return ((uint32_t)(c.base + t + 1) & ((1u << 27) - 1u)) << 5;
+}
+
 
 // Buffer of parity p (wavefront-uniform) out of a pair: a select between the two
 // pointers, which a kernel loads once, instead of an indexed load per use.
@@ -349,14 +369,14 @@ __device__ __forceinline__ void wave_lds_sync()
 
 // Appends the wave's n buffered candidates to lane L's list: one atomic, then a
 // coalesced copy out of LDS.
-__device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
+__device__ __forceinline__ void flush_claims(const Work &w, int tb, int L, uint32_t *counter, ClaimBuf &cb,
                                              uint32_t n)
 {
     wave_lds_sync();
     uint32_t base = 0;
     if (wlane() == 0) base = atomicAdd(counter, n);
     base = __shfl(base, 0, kWave);
-    Claim *dst = w.claims + (size_t)L * w.claims_cap;
+    Claim *dst = w.claims + tab_row(w, tb, L) * w.claims_cap;
     for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave) {
         Claim c;
         c.dest = cb.dest[i];
@@ -370,14 +390,14 @@ __device__ __forceinline__ void flush_claims(const Work &w, int L, uint32_t *cou
 
 // Buffers the candidates of one round of a wavefront (lanes with `adm` set),
 // flushing first if the round might not fit.
-__device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *counter, ClaimBuf &cb,
+__device__ __forceinline__ void push_claims(const Work &w, int tb, int L, uint32_t *counter, ClaimBuf &cb,
                                             uint32_t &cb_n, bool adm, int32_t dest, int32_t arc,
                                             uint32_t tok, float score)
 {
     const unsigned long long fm = __ballot(adm);
     if (!fm) return;
     if (cb_n + kWave > kClaimBuf) {
-        flush_claims(w, L, counter, cb, cb_n);
+        flush_claims(w, tb, L, counter, cb, cb_n);
         cb_n = 0;
     }
     if (adm) {
@@ -395,13 +415,13 @@ __device__ __forceinline__ void push_claims(const Work &w, int L, uint32_t *coun
 // closure's expand pass. Without epochs the winner clears the entry (a loser
 // reading after that sees 0, never its key).
 template <bool HASH>
-__device__ __forceinline__ bool take_winner(const Work &w, int L, uint32_t i, uint32_t ep, Claim &cl)
+__device__ __forceinline__ bool take_winner(const Work &w, int tb, int L, uint32_t i, uint32_t ep, Claim &cl)
 {
-    cl = w.claims[(size_t)L * w.claims_cap + i];
+    cl = w.claims[tab_row(w, tb, L) * w.claims_cap + i];
     const uint32_t ds = dest_state(w, cl.dest);
     if (ds >= (uint32_t)w.num_states) return false;
-    const bool win = recomb_key<HASH>(w, L, ds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
-    if (win && !w.epochs) w.best[(size_t)L * (size_t)w.num_states + ds] = 0ull;
+    const bool win = recomb_key<HASH>(w, tb, L, ds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep);
+    if (win && !w.epochs) w.best[tab_row(w, tb, L) * (size_t)w.num_states + ds] = 0ull;
     return win;
 }
 
@@ -428,8 +448,10 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
             if (cmd == kCmdPark) continue;
             for (size_t i = tid; i < per; i += stride) w.steps[(size_t)L * per + i] = 0u;
             if (cmd == kCmdOpen && !w.epochs && w.ctl[L].dirty) {
-                unsigned long long *tbl = w.best + (size_t)L * ns;
-                for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
+                for (int tb = 0; tb < w.ntab; ++tb) {
+                    unsigned long long *tbl = w.best + tab_row(w, tb, L) * ns;
+                    for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
+                }
             }
         }
         return;
@@ -448,7 +470,8 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
         typedef unsigned int v4u __attribute__((ext_vector_type(4)));
         // (the hash: two u64 per slot)
         unsigned long long *base = w.hash_bits ? (unsigned long long *)w.hash : w.best;
-        const size_t n = w.hash_bits ? ((size_t)w.max_lanes << w.hash_bits) * 2u : (size_t)w.max_lanes * ns;
+        const size_t n = (size_t)w.ntab * (w.hash_bits ? ((size_t)w.max_lanes << w.hash_bits) * 2u
+                                                       : (size_t)w.max_lanes * ns);
         v4u *t4 = (v4u *)base;
         const v4u z = {0u, 0u, 0u, 0u};
         for (size_t i = tid; i < n / 2; i += stride) __builtin_nontemporal_store(z, &t4[i]);
@@ -458,8 +481,10 @@ __global__ __launch_bounds__(kBlock) void k_clear(const Work *__restrict__ wp, i
     if (k != 0) return;
     for (int L = 0; L < w.max_lanes; ++L) {
         if (!w.ctl[L].dirty) continue;
-        unsigned long long *tbl = w.best + (size_t)L * ns;
-        for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
+        for (int tb = 0; tb < w.ntab; ++tb) {
+            unsigned long long *tbl = w.best + tab_row(w, tb, L) * ns;
+            for (size_t i = tid; i < ns; i += stride) tbl[i] = 0ull;
+        }
     }
 }
 
@@ -491,6 +516,7 @@ __device__ void init_lane(const Work &w, int L, int T)
     c.final_score = -__builtin_inff();
     c.nclaims_eps[0] = 0u;
     c.nclaims_eps[1] = 0u;
+    c.nclaims_eps[2] = 0u;
     c.nchanged[0] = 0ull;
     c.log_open = 0u;
     c.front_base[0] = 0xFFFFFFFFu;
@@ -511,6 +537,7 @@ __device__ void init_lane(const Work &w, int L, int T)
     if (T != 0) ub = __builtin_inff();   // (its frame's log-probs are not known here)
     const size_t q = (size_t)L * w.frontier_cap;
     w.tok_state[0][q] = s;
+    if (w.eps_iterations > 0) w.tok_tag[0][q] = 0u;   // frame 0 of the lane, made before any pass
     w.tok_score[0][q] = 0.0f;
     w.tok_entry[0][q] = -1;
     w.tok_last[0][q] = -1;
@@ -769,7 +796,7 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
             if (!adm[r]) continue;
-            unsigned long long *ent = recomb_entry<HASH>(w, L, dest_state(w, ud.dst[r]), ep);
+            unsigned long long *ent = recomb_entry<HASH>(w, 0, L, dest_state(w, ud.dst[r]), ep);
             if (ent) atomicMax(ent, table_key(w, ud.e[r], (int32_t)ud.arc[r], ud.dst[r], ep));
             else atomicOr(&c.overflow, kOvfHash);
         }
@@ -791,7 +818,7 @@ __device__ __forceinline__ void admit_unit(const Work &w, int L, int ph, float c
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r)
-        push_claims(w, L, counter, *cb, cb_n, adm[r], ud.dst[r], (int32_t)ud.arc[r], ud.tok[r], ud.e[r]);
+        push_claims(w, 0, L, counter, *cb, cb_n, adm[r], ud.dst[r], (int32_t)ud.arc[r], ud.tok[r], ud.e[r]);
 }
 
 // XCD-aware block order: workgroups are dealt to the 8 XCDs round-robin
@@ -844,7 +871,7 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
             run = fmaxf(run, unit_max(ud));
             admit_unit<HASH>(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
         }
-        if (cb_n) flush_claims(w, L, &c.nclaims[p], *cbuf, cb_n);
+        if (cb_n) flush_claims(w, 0, L, &c.nclaims[p], *cbuf, cb_n);
         cb_n = 0;
         if (run > -__builtin_inff() && wlane() == 0) atomicMax(&c.maxkey[p], f2ord(run));
     }
@@ -1155,7 +1182,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 c.front_base[np] = tab.arcs[L];
                 c.log_open = 1u;   // entries added to log_cursor by the next kernel
             }
-            c.nclaims_eps[1] = 0u;
+            c.nclaims_eps[1] = 0u;   // (the closure's first two passes' lists)
+            c.nclaims_eps[2] = 0u;
         } else if (ph == kPhFinal) {
             // the final key is the best of the superset: a result iff admitted
             const unsigned long long fk = c.final_key;
@@ -1193,7 +1221,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         Claim cl;
         bool adm = false;
         if (valid) {
-            cl = w.claims[(size_t)L * w.claims_cap + i];
+            cl = w.claims[tab_row(w, 0, L) * w.claims_cap + i];
             adm = __uint_as_float(cl.score) > cutoff;
         }
         const unsigned long long am = __ballot(adm);
@@ -1228,7 +1256,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         // with epochs only admitted candidates need the table (stale entries of
         // earlier rounds always lose); without, every owner clears its entry
         if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
-            if (recomb_key<HASH>(w, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
+            if (recomb_key<HASH>(w, 0, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
                 if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
                 keep = adm;
             }
@@ -1331,6 +1359,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
             w.wlog[e] = make_int2(esrc, arc);
             pick(w.tok_state, np)[q] = dst;
+            if (w.eps_iterations > 0) pick(w.tok_tag, np)[q] = frame_tag(c, t);   // made by the compaction
             pick(w.tok_score, np)[q] = end;
             pick(w.tok_entry, np)[q] = e;
             pick(w.tok_last, np)[q] = arc;
@@ -1400,6 +1429,94 @@ __device__ __forceinline__ bool closure_lane(const LaneCtl &c, int t)
     return c.status == kActive && t < c.win && (t < 0 || t < c.T);
 }
 
+// Relaxes the epsilon arcs of a wavefront's sources in closure pass k of step
+// t, at most one source per lane (src: first epsilon arc eb, ed arcs, winners-
+// log entry ent, score sc, frontier position spos) of lane L: all their arcs, 64
+// at a time (balanced within the wave), each admitted candidate posting its
+// key to round (t, k)'s table and joining its list; in lattice mode each
+// admitted one is a lattice arc of the frame being closed (nb: its first
+// node), tagged with the pass. ep: the round's epoch.
+template <bool HASH>
+__device__ __forceinline__ void relax_sources(const Work &w, int L, int t, int k, uint32_t ep, float cutoff,
+                                              uint32_t nb, bool src, int32_t eb, uint32_t ed, int32_t ent,
+                                              float sc, int32_t spos, ClaimBuf *cbuf)
+{
+    LaneCtl &c = w.ctl[L];
+    const int lane = wlane();
+    const int tb = round_tab(w, k);
+    uint32_t *counter = &c.nclaims_eps[k % 3];
+    if (!src) ed = 0u;
+    if (w.lattice && src) {
+        // the source's node: this pass relaxes its epsilon arcs (a later pass
+        // that relaxes them again admits a superset: the source's score only
+        // grows)
+        const uint32_t ni = nb + (uint32_t)spos;
+        if (ni < w.lat_nodes) w.lat_epass[(size_t)L * w.lat_nodes + ni] = (uint8_t)k;
+    }
+    uint32_t dsum;
+    const uint32_t dpre = wave_excl_sum(ed, &dsum);
+    uint32_t n_adm = 0, cb_n = 0;
+    for (uint32_t x0 = 0; x0 < dsum; x0 += kWave) {
+        const uint32_t x = x0 + (uint32_t)lane;
+        int sl = 0;
+#pragma unroll
+        for (int st = 32; st >= 1; st >>= 1) {
+            const uint32_t v = __shfl(dpre, sl + st, kWave);
+            if (v <= x) sl += st;
+        }
+        const int32_t a = __shfl(eb, sl, kWave) + (int32_t)(x - __shfl(dpre, sl, kWave));
+        const float ssc = __shfl(sc, sl, kWave);
+        // the source's winners-log entry as this pass found it (the resolving
+        // kernel may give the source token a fresh one)
+        const int32_t sen = __shfl(ent, sl, kWave);
+        bool adm = false;
+        int32_t dd = 0;
+        float e = 0.0f;
+        if (x < dsum) {
+            const ArcDLW ar = w.arc_dlw[a];
+            e = ssc + ar.weight;
+            dd = ar.dest;
+            adm = e > cutoff;
+            if (adm) {
+                ++n_adm;
+                unsigned long long *slot = recomb_entry<HASH>(w, tb, L, dest_state(w, ar.dest), ep);
+                if (slot) atomicMax(slot, table_key(w, e, a, ar.dest, ep));
+                else atomicOr(&c.overflow, kOvfHash);
+            }
+        }
+        if (w.lattice) {
+            // every admitted epsilon candidate is a lattice arc of the frame
+            // being closed: {source position, arc, destination state (unresolved
+            // until the next compaction maps it), pass}
+            const int32_t sps = __shfl(spos, sl, kWave);
+            const unsigned long long am = __ballot(adm);
+            if (am) {
+                const int lead = __ffsll((long long)am) - 1;
+                uint32_t lb0 = 0u;
+                if (lane == lead) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
+                lb0 = __shfl(lb0, lead, kWave);
+                if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
+                    if (lane == lead) atomicOr(&c.overflow, kOvfArena);
+                } else if (adm) {
+                    w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
+                        make_int4(sps, a, (int32_t)(dest_state(w, dd) | kLatUnresolved), k);
+                }
+            }
+        }
+        push_claims(w, tb, L, counter, *cbuf, cb_n, adm, dd, a, (uint32_t)sen, e);
+    }
+    if (cb_n) flush_claims(w, tb, L, counter, *cbuf, cb_n);
+    const uint32_t sd = wave_sum(n_adm);
+    if (lane == 0 && dsum) {
+        uint32_t *rec = step_rec(w, L, t);
+        atomicAdd(rec + kRecEpsArcs, dsum);
+        if (sd) atomicAdd(rec + kRecEpsAdmitted, sd);
+    }
+}
+
+// Closure pass k's relaxation from the source list the kernel before wrote
+// (pass 1: the compaction's new tokens with epsilon arcs; a pass after a
+// resolving kernel that did not relax it itself: that kernel's changed tokens).
 template <bool HASH>
 __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
@@ -1434,9 +1551,7 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
         // the compaction before this closure (no closure token added yet)
         if (k == 1) commit_log(w, c, L, t, (uint32_t)c.cnt[tab.par[L]]);
         if (tab.arcs[L] > 0u) step_rec(w, L, t)[kRecEpsPasses] += 1u;   // a pass with sources
-        // for the apply kernel of this pass, which appends while it reads: the
-        // frontier as the pass found it, and an empty list of changed tokens
-        c.eps_n0 = (uint32_t)c.cnt[tab.par[L]];
+        // for the resolving kernel of this pass: an empty list of changed tokens
         c.nchanged[(k + 1) & 1] = 0ull;
     }
     const int nl = w.max_lanes;
@@ -1447,88 +1562,21 @@ __device__ __forceinline__ void ph_eps_expand(const Work &w, int t, int k, LaneT
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
-        const float cutoff = tab.f1[L];
-        LaneCtl &c = w.ctl[L];
         // the 64 sources of this unit: their epsilon ranges, entries and scores
         // as the kernel that made them wrote them
         int32_t eb = 0, ent = -1, spos = 0;
         uint32_t ed = 0;
         float sc = 0.0f;
-        if (i < tab.n[L]) {
+        const bool src = i < tab.n[L];
+        if (src) {
             const int4 ce = w.changed[k & 1][(size_t)L * w.chg_cap + i];
             eb = ce.x;
             ed = (uint32_t)ce.y;
             ent = ce.z;
             sc = __uint_as_float((uint32_t)ce.w);
-            if (w.lattice) {
-                // the source's node: this pass relaxes its epsilon arcs (a later
-                // pass that relaxes them again admits a superset: the source's
-                // score only grows)
-                spos = w.chg_pos[k & 1][(size_t)L * w.chg_cap + i];
-                const uint32_t ni = tab.fb[L] + (uint32_t)spos;
-                if (ni < w.lat_nodes) w.lat_epass[(size_t)L * w.lat_nodes + ni] = (uint8_t)k;
-            }
+            if (w.lattice) spos = w.chg_pos[k & 1][(size_t)L * w.chg_cap + i];
         }
-        uint32_t dsum;
-        const uint32_t dpre = wave_excl_sum(ed, &dsum);
-        // all epsilon arcs of the unit, 64 at a time (balanced within the wave)
-        uint32_t n_adm = 0, cb_n = 0;
-        for (uint32_t x0 = 0; x0 < dsum; x0 += kWave) {
-            const uint32_t x = x0 + (uint32_t)lane;
-            int src = 0;
-#pragma unroll
-            for (int st = 32; st >= 1; st >>= 1) {
-                const uint32_t v = __shfl(dpre, src + st, kWave);
-                if (v <= x) src += st;
-            }
-            const int32_t a = __shfl(eb, src, kWave) + (int32_t)(x - __shfl(dpre, src, kWave));
-            const float ssc = __shfl(sc, src, kWave);
-            // the source's winners-log entry as this pass found it (the apply
-            // kernel may give the source token a fresh one)
-            const int32_t sen = __shfl(ent, src, kWave);
-            bool adm = false;
-            int32_t dd = 0;
-            float e = 0.0f;
-            if (x < dsum) {
-                const ArcDLW ar = w.arc_dlw[a];
-                e = ssc + ar.weight;
-                dd = ar.dest;
-                adm = e > cutoff;
-                if (adm) {
-                    ++n_adm;
-                    unsigned long long *ent = recomb_entry<HASH>(w, L, dest_state(w, ar.dest), ep);
-                    if (ent) atomicMax(ent, table_key(w, e, a, ar.dest, ep));
-                    else atomicOr(&c.overflow, kOvfHash);
-                }
-            }
-            if (w.lattice) {
-                // every admitted epsilon candidate is a lattice arc of the frame
-                // being closed: {source position, arc, destination state (its
-                // position once the next compaction resolves it), pass}
-                const int32_t sps = __shfl(spos, src, kWave);
-                const unsigned long long am = __ballot(adm);
-                if (am) {
-                    const int lead = __ffsll((long long)am) - 1;
-                    uint32_t lb0 = 0u;
-                    if (lane == lead) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
-                    lb0 = __shfl(lb0, lead, kWave);
-                    if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
-                        if (lane == lead) atomicOr(&c.overflow, kOvfArena);
-                    } else if (adm) {
-                        w.lat_arc[(size_t)L * w.lat_cap + lb0 + (uint32_t)__popcll(am & mask_lt())] =
-                            make_int4(sps, a, (int32_t)(dest_state(w, dd) | kLatUnresolved), k);
-                    }
-                }
-            }
-            push_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n, adm, dd, a, (uint32_t)sen, e);
-        }
-        if (cb_n) flush_claims(w, L, &c.nclaims_eps[k & 1], *cbuf, cb_n);
-        const uint32_t sd = wave_sum(n_adm);
-        if (lane == 0 && dsum) {
-            uint32_t *rec = step_rec(w, L, t);
-            atomicAdd(rec + kRecEpsArcs, dsum);
-            if (sd) atomicAdd(rec + kRecEpsAdmitted, sd);
-        }
+        relax_sources<HASH>(w, L, t, k, ep, tab.f1[L], tab.fb[L], src, eb, ed, ent, sc, spos, cbuf);
     }
 }
 
@@ -1541,17 +1589,23 @@ __global__ __launch_bounds__(kBlock) void k_eps_expand(const Work *__restrict__ 
     ph_eps_expand<HASH>(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
 }
 
-// Per claimed destination of the pass: the winner (its key is the table entry)
+// Per claimed destination of pass k: the winner (its key is the table entry)
 // is appended as a new token, replaces the destination's token if its key is
 // greater, or does nothing; then the writes: fresh winners-log entries,
 // appended tokens (with their next-step class and arc offsets), replaced
-// tokens, the next pass's sources. Only a destination's winner reads or writes
-// its token, and the existence test sees only the tokens the pass began with,
-// so the decisions are those of a pass that reads everything before it writes.
-template <bool HASH>
-__device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab)
+// tokens. Only a destination's winner reads or writes its token, and the
+// existence test sees only the tokens of rounds before this pass (their tag:
+// the frame's compaction or an earlier pass), so the decisions are those of a
+// pass that reads everything before it writes. RELAX (k < passes): each
+// wavefront then relaxes its changed tokens' epsilon arcs as pass k + 1 (into
+// the other table and list: pass k's stay untouched); otherwise it lists them
+// for the kernel of pass k + 1.
+template <bool HASH, bool RELAX>
+__device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTab &tab, ClaimBuf *cbuf)
 {
     const uint32_t ep = round_epoch(w, t, k);
+    const uint32_t ep_next = RELAX ? round_epoch(w, t, k + 1) : 0u;
+    const int tb = round_tab(w, k);
     if (threadIdx.x < kWave) {
         const int L = (int)threadIdx.x;
         uint32_t units = 0;
@@ -1560,15 +1614,16 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             const int fp = lane_par(c, t + 1);
             tab.par[L] = fp;
             uint32_t nc = 0;
-            const uint32_t nce = c.nclaims_eps[k & 1], n0 = c.eps_n0;
-            const bool on = closure_lane(c, t) && n0 <= w.frontier_cap;
+            const uint32_t nce = c.nclaims_eps[k % 3];
+            // (a frontier past its capacity belongs to a lane that is retiring)
+            const bool on = closure_lane(c, t) && (uint32_t)pair_at(c.cnt, fp) <= w.frontier_cap;
             if (on) nc = nce;
             // token and log capacity are checked per wavefront as it allocates;
             // a full hash lost candidates
             const bool fits = nc <= w.claims_cap && !(c.overflow & kOvfHash);
             if (fits) units = (nc + kWave - 1) / kWave;
             tab.n[L] = nc;
-            tab.arcs[L] = n0;
+            tab.arcs[L] = frame_tag(c, t);
             tab.T[L] = c.T;
             tab.win[L] = c.win;
             tab.f1[L] = c.cutoff;
@@ -1582,7 +1637,14 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
     if (blockIdx.x == 0 && threadIdx.x < (unsigned)w.max_lanes) {
         const int L = (int)threadIdx.x;
         LaneCtl &c = w.ctl[L];
-        c.nclaims_eps[(k + 1) & 1] = 0u;
+        // the list counters this launch does not fill and no later kernel has
+        // filled yet: pass k + 2's (read last by pass k - 1), and when this
+        // launch only lists pass k + 1's sources, pass k + 1's as well (its
+        // relaxation runs next). A launch that relaxes pass k + 1 itself also
+        // clears the source count a listing launch for pass k + 1 would add to.
+        c.nclaims_eps[(k + 2) % 3] = 0u;
+        if (!RELAX) c.nclaims_eps[(k + 1) % 3] = 0u;
+        if (RELAX) c.nchanged[k & 1] = 0ull;
         if (tab.f0[L] != 0.0f) {
             // candidates past claims_cap were never listed (or the hash was
             // full): their table entries stay set, so the table is cleared
@@ -1609,7 +1671,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         int4 dd = make_int4(-2, 0, 0, -1);
         int32_t dst = 0;
         Claim cl;
-        const bool win = valid && take_winner<HASH>(w, L, i, ep, cl);
+        const bool win = valid && take_winner<HASH>(w, tb, L, i, ep, cl);
         const unsigned long long wm = __ballot(win);
         if (wm && lane == __ffsll((long long)__ballot(valid)) - 1)
             atomicAdd(step_rec(w, L, t) + kRecEpsDistinct, (uint32_t)__popcll(wm));
@@ -1618,8 +1680,14 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
             dd.y = (int)cl.score;
             dd.z = cl.arc;
             dd.w = (int32_t)cl.tok;
+            // the destination's token, if a round before this pass made it
             const int32_t pd = pick(w.pos, fp)[(size_t)L * w.num_states + dst];
-            const bool exists = (uint32_t)pd < tab.arcs[L] && pick(w.tok_state, fp)[(size_t)L * Q + pd] == dst;
+            bool exists = false;
+            if ((uint32_t)pd < Q) {
+                const size_t q = (size_t)L * Q + (uint32_t)pd;
+                const uint32_t tg = pick(w.tok_tag, fp)[q];
+                exists = pick(w.tok_state, fp)[q] == dst && tg >= tab.arcs[L] && tg < tab.arcs[L] + (uint32_t)k;
+            }
             if (!exists) {
                 dd.x = -1;
             } else {
@@ -1648,7 +1716,7 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         if (ma == 0ull) continue;
         const unsigned long long mn = __ballot(isnew);
         // the next pass's sources (none after the last pass): the changed tokens
-        // with epsilon arcs, counted apart from all changed tokens
+        // with epsilon arcs
         const bool more = k < w.eps_iterations;
         const unsigned long long ml = more ? __ballot(any && ed > 0u) : 0ull;
         const int leader = __ffsll((long long)ma) - 1;
@@ -1658,9 +1726,15 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         uint32_t lb = 0u, cb = 0u;
         if (lane == leader) {
             lb = atomicAdd(&c.log_cursor, (uint32_t)__popcll(ma));
-            if (more)
+            if (RELAX) {
+                // pass k + 1 has sources (the passes with sources are the first
+                // few: one that changes nothing leaves the next none)
+                atomicMax(step_rec(w, L, t) + kRecEpsPasses, (uint32_t)(k + 1));
+            } else if (more) {
+                // the list of pass k + 1 (low half), and the changed tokens (high)
                 cb = (uint32_t)atomicAdd(&c.nchanged[(k + 1) & 1],
                                          (unsigned long long)__popcll(ml) | ((unsigned long long)__popcll(ma) << 32));
+            }
             if (mn) old = atomicAdd(&c.cnt[fp], (unsigned long long)__popcll(mn) | ((unsigned long long)dsum << 32));
             uint32_t *rec = step_rec(w, L, t);
             if (mn) atomicAdd(rec + kRecEpsNew, (uint32_t)__popcll(mn));
@@ -1668,14 +1742,17 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         }
         old = __shfl(old, leader, kWave);
         lb = __shfl(lb, leader, kWave);
-        cb = __shfl(cb, leader, kWave);
+        if (!RELAX) cb = __shfl(cb, leader, kWave);
         // exact capacity of this wavefront's appends and winners-log entries: on
-        // overflow nothing is written and the lane retires
+        // overflow nothing is written and the lane retires (its table entries may
+        // stay set by the relaxation of pass k + 1: the table is cleared before
+        // the next decode)
         const bool pos_ok = (unsigned long long)(uint32_t)old + (uint32_t)__popcll(mn) <= Q;
         if (!pos_ok || (unsigned long long)lb + (uint32_t)__popcll(ma) > w.arena_lim) {
             if (lane == leader) {
                 atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
                 if (pos_ok) c.log_full = 1u;
+                if (RELAX) c.dirty = 1u;
                 c.status = kDone;
                 c.phase_final = kPhDead;
             }
@@ -1683,38 +1760,43 @@ __device__ __forceinline__ void ph_eps_apply(const Work &w, int t, int k, LaneTa
         }
         if (mn) write_strips(pick(w.strip_tok, fp) + (size_t)L * w.strip_cap, w.strip_cap, (uint32_t)old,
                              (uint32_t)(old >> 32), dpre, dsum, mn);
-        if (!any) continue;
         const uint32_t ra = (uint32_t)__popcll(ma & mask_lt());
         const uint32_t le = lb + ra;
         const int32_t e = (int32_t)((uint32_t)L * w.arena + le);
-        w.wlog[e] = make_int2(dd.w, dd.z);
-        uint32_t pi;
-        if (isnew) {
-            pi = (uint32_t)old + (uint32_t)__popcll(mn & mask_lt());
-            const size_t q = (size_t)L * Q + pi;
-            pick(w.tok_state, fp)[q] = dst;
-            pick(w.tok_off, fp)[q] = (uint32_t)(old >> 32) + dpre;
-            pick(w.tok_abeg, fp)[q] = abeg;
-            pick(w.pos, fp)[(size_t)L * w.num_states + dst] = (int32_t)pi;
-        } else {
-            pi = (uint32_t)dd.x;
-        }
-        const size_t q = (size_t)L * Q + pi;
-        pick(w.tok_score, fp)[q] = end;
-        pick(w.tok_entry, fp)[q] = e;
-        pick(w.tok_last, fp)[q] = dd.z;
-        pick(w.tok_ub, fp)[q] = ub;
-        if (w.lattice) {
-            // the token's node (appended: a new one; replaced: its score rises)
-            const uint32_t ni = tab.fb[L] + pi;
-            if (ni < w.lat_nodes) {
-                w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
-                if (isnew) w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
+        uint32_t pi = 0u;
+        if (any) {
+            w.wlog[e] = make_int2(dd.w, dd.z);
+            if (isnew) {
+                pi = (uint32_t)old + (uint32_t)__popcll(mn & mask_lt());
+                const size_t q = (size_t)L * Q + pi;
+                pick(w.tok_state, fp)[q] = dst;
+                pick(w.tok_tag, fp)[q] = tab.arcs[L] | (uint32_t)k;
+                pick(w.tok_off, fp)[q] = (uint32_t)(old >> 32) + dpre;
+                pick(w.tok_abeg, fp)[q] = abeg;
+                pick(w.pos, fp)[(size_t)L * w.num_states + dst] = (int32_t)pi;
             } else {
-                lat_node_overflow(w, c);
+                pi = (uint32_t)dd.x;
+            }
+            const size_t q = (size_t)L * Q + pi;
+            pick(w.tok_score, fp)[q] = end;
+            pick(w.tok_entry, fp)[q] = e;
+            pick(w.tok_last, fp)[q] = dd.z;
+            pick(w.tok_ub, fp)[q] = ub;
+            if (w.lattice) {
+                // the token's node (appended: a new one; replaced: its score rises)
+                const uint32_t ni = tab.fb[L] + pi;
+                if (ni < w.lat_nodes) {
+                    w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
+                    if (isnew) w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
+                } else {
+                    lat_node_overflow(w, c);
+                }
             }
         }
-        if ((ml >> lane) & 1ull) {
+        const bool src = (ml >> lane) & 1ull;
+        if (RELAX) {
+            relax_sources<HASH>(w, L, t, k + 1, ep_next, tab.f1[L], tab.fb[L], src, eb, ed, e, end, (int32_t)pi, cbuf);
+        } else if (src) {
             const uint32_t ci = cb + (uint32_t)__popcll(ml & mask_lt());
             if (ci < w.chg_cap) {
                 w.changed[(k + 1) & 1][(size_t)L * w.chg_cap + ci] = make_int4(eb, (int)ed, e, (int)__float_as_uint(end));
@@ -1729,7 +1811,17 @@ __global__ __launch_bounds__(kBlock) void k_eps_apply(const Work *__restrict__ w
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
-    ph_eps_apply<HASH>(w, t, k, tab);
+    ph_eps_apply<HASH, false>(w, t, k, tab, nullptr);
+}
+
+// Pass k's resolution and pass k + 1's relaxation in one launch (k < passes).
+template <bool HASH>
+__global__ __launch_bounds__(kBlock) void k_eps_apply_expand(const Work *__restrict__ wp, int t, int k)
+{
+    const Work &w = *wp;
+    __shared__ LaneTab tab;
+    __shared__ ClaimBuf cbufs[kBlock / kWave];
+    ph_eps_apply<HASH, true>(w, t, k, tab, &cbufs[threadIdx.x / kWave]);
 }
 
 // ------------------------------------------------------------------ lattice
@@ -3052,6 +3144,11 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKEpsApply:
         if (hash) go(k_eps_apply<true>, G, B, s, e0, e1, dw, t, k);
         else go(k_eps_apply<false>, G, B, s, e0, e1, dw, t, k);
+        break;
+    case kKEpsApplyExpand:
+        if (k < 1 || k >= w.eps_iterations || w.ntab != 2) return hipErrorInvalidValue;
+        if (hash) go(k_eps_apply_expand<true>, G, B, s, e0, e1, dw, t, k);
+        else go(k_eps_apply_expand<false>, G, B, s, e0, e1, dw, t, k);
         break;
     case kKBacktrack: go(k_backtrack, dim3(w.max_lanes), dim3(kWave), s, e0, e1, dw); break;
     case kKStreamBegin: go(k_stream_begin, dim3(1), dim3(kWave), s, e0, e1, dw); break;
