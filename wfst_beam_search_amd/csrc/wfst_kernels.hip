@@ -2743,9 +2743,10 @@ __device__ __forceinline__ void gc_prologue(const Work &w, LaneTab &tab, int wha
             const uint32_t win = c.log_cursor > c.sealed ? c.log_cursor - c.sealed : 0u;
             uint32_t items = 0;
             if (c.gc_on && n <= w.frontier_cap && c.log_cursor <= w.arena_lim)
-                items = what == 0 ? n : what == 1 ? win : what == 2 ? c.gc_live : (win + 31u) / 32u;
+                items = what == 0 ? n : what == 1 ? win : what == 2 ? c.gc_live : max((win + 31u) / 32u, c.gc_live);
             units = (items + kWave - 1) / kWave;
             tab.n[L] = items;
+            tab.win[L] = (int32_t)c.gc_live;
             tab.arcs[L] = c.sealed;
             tab.par[L] = p;
             tab.fb[L] = c.log_cursor;
@@ -2966,7 +2967,9 @@ __global__ __launch_bounds__(kBlock) void k_gc_roots(const Work *__restrict__ wp
     }
 }
 
-// Clears the round's live map and child counts.
+// Clears the round's live map (the window's words) and child counts (set only
+// at the live entries' compacted positions), each with one coalesced store per
+// item.
 __global__ __launch_bounds__(kBlock) void k_gc_clear(const Work *__restrict__ wp)
 {
     const Work &w = *wp;
@@ -2979,12 +2982,9 @@ __global__ __launch_bounds__(kBlock) void k_gc_clear(const Work *__restrict__ wp
         const int L = find_lane(tab.base, nl, u);
         const uint32_t x = (u - tab.base[L]) * kWave + (uint32_t)wlane();
         if (x >= tab.n[L]) continue;
-        w.gc_mark[(size_t)L * gc_words(w) + x] = 0u;
-        // the child counts of positions 32x .. 32x + 31
-        for (uint32_t k = 0; k < 32u; ++k) {
-            const size_t q = (size_t)x * 32u + k;
-            if (q < (size_t)w.arena) w.gc_child[(size_t)L * w.arena + q] = 0u;
-        }
+        const uint32_t win = tab.fb[L] > tab.arcs[L] ? tab.fb[L] - tab.arcs[L] : 0u;
+        if (x < (win + 31u) / 32u) w.gc_mark[(size_t)L * gc_words(w) + x] = 0u;
+        if (x < (uint32_t)tab.win[L] && x < w.arena) w.gc_child[(size_t)L * w.arena + x] = 0u;
     }
 }
 
