@@ -1964,12 +1964,13 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
 //     bwd(source) with one atomicMax each and are marked at once;
 //  3. frame f's epsilon arcs (records of slot f with a pass > 0; both ends in
 //     frame f) relax bwd(source) to the least fixpoint, then are marked.
-// The final pass runs step 2 flat over lanes (k_lat_back, above) and step 3 per
-// lane (k_lat_eps_back). A sweep runs on as many workgroups as lanes, so its
-// speed is set by the memory-level parallelism inside a workgroup: each thread
-// issues the loads of a batch of records before it uses any. Epsilon fixpoints
-// run in LDS when the frame's nodes and records fit, else on the scores in
-// memory.
+// The final pass runs step 2 flat over lanes (k_lat_back, above) and step 3 as
+// flat rounds over all lanes' records, finishing per lane only where a chain is
+// still open (k_lat_eps_round, k_lat_eps_back, below). A sweep runs on as many
+// workgroups as lanes, so its speed is set by the memory-level parallelism
+// inside a workgroup: each thread issues the loads of a batch of records before
+// it uses any. A per-lane epsilon fixpoint runs in LDS when the frame's nodes
+// fit, else on the scores in memory.
 constexpr int kLatSweepBlock = 1024;
 constexpr int kLatBatch = 8;                  // step-arc records per thread per load round
 constexpr int kLatEpsRegs = 8;                // epsilon-slot records per thread per load round (half in the prune)
