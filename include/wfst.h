@@ -192,11 +192,14 @@ typedef struct wfst_graph_desc {
  *                  cannot run again), so committed memory grows with the
  *                  streams opened; chunks stay mapped after release.
  *  recomb_slots    0: recombination through a direct-mapped table of one 8-byte
- *                  key per state and lane (max_lanes * num_states * 8 bytes; no
- *                  probing, never full). n > 0, a power of 2 in [64, 2^28]: a
- *                  per-lane open-addressing hash of n 16-byte slots keyed on the
- *                  destination state (page section 5.3's hash; memory
- *                  max_lanes * n * 16 bytes, independent of the graph), claimed
+ *                  key per state and lane (max_lanes * num_states * 8 bytes,
+ *                  twice on graphs with epsilon arcs and eps_iterations > 0: a
+ *                  closure pass resolves from one while the next relaxes into
+ *                  the other; no probing, never full). n > 0, a power of 2 in
+ *                  [64, 2^28]: a per-lane open-addressing hash of n 16-byte
+ *                  slots keyed on the destination state (page section 5.3's
+ *                  hash; memory max_lanes * n * 16 bytes, twice likewise,
+ *                  independent of the graph's size), claimed
  *                  with a CAS and resolved with the same 64-bit atomicMax; a pass
  *                  with more distinct destinations than n retires the lane with
  *                  WFST_OVF_HASH. Same results. Needs epoch keys (plain_keys != 1).
@@ -257,8 +260,9 @@ int wfst_graph_release(wfst_graph_t g);
  * (frontiers, per-lane recombination tables, claims lists, winners-log regions,
  * result buffers) and takes a graph reference (page section 6.1 "Workspace",
  * section 10). The recombination table holds one 8-byte entry per state and
- * lane (max_lanes * num_states * 8 bytes), so destinations are resolved with
- * one atomic each and never overflow (or, with recomb_slots, a per-lane hash).
+ * lane (max_lanes * num_states * 8 bytes; two tables when closure passes run),
+ * so destinations are resolved with one atomic each and never overflow (or,
+ * with recomb_slots, a per-lane hash).
  * Errors: WFST_EINVAL (bad config),
  * WFST_ENOMEM, WFST_EDEVICE.
  */
