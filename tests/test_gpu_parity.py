@@ -232,6 +232,8 @@ def test_decode_argument_errors():
         dec.decode(torch.zeros((1, 5, g.vocab), device="cuda"), [1])         # T > max_frames
     with pytest.raises(wb.WfstError):
         dec.decode(torch.zeros((1, 4, g.vocab + 1), device="cuda"), [1])     # V mismatch
+    with pytest.raises(wb.WfstError):
+        dec.decode(torch.zeros((0, 4, g.vocab), device="cuda"), [])          # an empty batch
     r = dec.decode(x, [0, 3])
     assert r.meta[0, 0] == 1
     dec.close(); dg.release()
