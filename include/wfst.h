@@ -532,10 +532,11 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_GC_CLEAR    22  /* log compaction: live map and counts cleared             */
 #define WFST_K_GC_END      23  /* log compaction: log end and the sealed prefix           */
 #define WFST_K_LAT_EPS_BACK 24 /* lattice: a frame's epsilon arcs, fixpoint end and prune */
-#define WFST_K_LAT_PRUNE   25  /* lattice: interval prune of the last 2N frames's arcs     */
+#define WFST_K_LAT_PRUNE   25  /* lattice: interval prune of the last 2N frames' arcs      */
 #define WFST_K_LAT_EPS_ROUND 26 /* lattice: one flat relaxation round of a frame's epsilon arcs */
 #define WFST_K_EPS_APPLY_EXPAND 27 /* closure: pass k's decisions and writes, then pass k + 1's relaxation */
-#define WFST_K_COUNT       28
+#define WFST_K_LAT_PREP    28  /* lattice: the interval prune's arc scores, flat over lanes */
+#define WFST_K_COUNT       29
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

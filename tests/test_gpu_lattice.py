@@ -191,6 +191,23 @@ def test_lattice_large_epsilon_frames(interval, levels, passes):
     assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
 
 
+@pytest.mark.parametrize("interval", [0, 3])
+def test_lattice_large_frames(interval):
+    """Frames growing to 60k tokens and 530k lattice arcs on an epsilon-free
+    graph (an unbounded beam on a 60k-state graph): with the interval prune
+    every 3 steps, the second prune's sweep holds its small frames' backward
+    scores in LDS and its large ones in memory, with a step between the two.
+    The kept records equal the oracle's."""
+    g = synth.random_graph(79, n=60000, deg=(4, 14), vocab=8)
+    lp = synth.random_logprobs(80, 2, 7, g.vocab, sigma=1.0)
+    L = np.array([7, 6], dtype=np.int32)
+    _say("lattice large frames", interval, lp.shape)
+    _, lats = lattice_case(g, lp, L, 1e10, 10**6, 0, False, 2.0, frontier_cap=1 << 17, slot_cap=1 << 21,
+                           claims_cap=1 << 21, arena_entries=4 << 20, lattice_cap=4 << 20,
+                           lat_prune_interval=interval)
+    assert all(x.shape[0] > 0 for x in lats)
+
+
 def test_lattice_deep_epsilon_chains():
     """Small graphs whose epsilon chains run up to 7 arcs, 1 or 2 closure passes:
     the final pass's flat rounds leave chains unsettled, and the per-lane finish
@@ -307,6 +324,19 @@ def test_lattice_tlg_workload_interval_prune():
     _, lats = lattice_case(g, lp, L, wl.beam, wl.max_active, 0, False, 4.0, eps_iterations=wl.eps_iterations,
                            lanes=[3, 12], arena_entries=16 << 20, lat_prune_interval=32)
     assert all(int((x[:, 7] == 4).sum()) > 0 for x in lats)
+
+
+def test_lattice_hlg_workload_interval_prune():
+    """The HLG workload at full size in lattice mode with output beam 8 and the
+    interval prune every 64 steps, as its benchmark runs it: sampled lanes'
+    kept records equal the oracle's with the same interval."""
+    cid = 3
+    g, lp, L = synth.workload_inputs(cid)
+    wl = synth.WORKLOADS[cid]
+    _say("lattice hlg workload prune", lp.shape)
+    _, lats = lattice_case(g, lp, L, wl.beam, wl.max_active, 0, False, 8.0, lanes=[1, 17, 30],
+                           lat_prune_interval=64)
+    assert all(x.shape[0] > 0 for x in lats)
 
 
 def test_lattice_epsilon_graph_with_log_compaction():

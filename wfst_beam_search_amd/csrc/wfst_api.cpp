@@ -809,7 +809,7 @@ static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &
         if ((e = go(kKFinalize, t, 0)) != hipSuccess) return e;
         if ((e = enqueue_closure(t, passes, go, clear_due, wrap_clear)) != hipSuccess) return e;
         if (w.lat_prune_interval > 0 && (t + 1) % w.lat_prune_interval == 0 && t + 1 < steps &&
-            (e = go(kKLatPrune, t, 0)) != hipSuccess) return e;
+            ((e = go(kKLatPrep, t, 0)) != hipSuccess || (e = go(kKLatPrune, t, 0)) != hipSuccess)) return e;
         if (w.gc_interval > 0 && (t + 1) % w.gc_interval == 0 && t + 1 < steps) {
             static const int ids[] = {kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd};
             for (int id : ids)

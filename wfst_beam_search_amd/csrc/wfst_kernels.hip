@@ -1967,19 +1967,27 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
 // The final pass runs step 2 flat over lanes (k_lat_back, above) and step 3 as
 // flat rounds over all lanes' records, finishing per lane only where a chain is
 // still open (k_lat_eps_round, k_lat_eps_back, below). A sweep runs on as many
-// workgroups as lanes, so its speed is set by the memory-level parallelism
-// inside a workgroup: each thread issues the loads of a batch of records before
-// it uses any. A per-lane epsilon fixpoint runs in LDS when the frame's nodes
-// fit, else on the scores in memory.
+// workgroups as lanes, so its speed is set by the memory latency of each frame
+// inside a workgroup. The prune's sweep therefore waits on no gather: a flat
+// kernel over the whole chip (k_lat_prep) first turns every step arc of the
+// window into a work record (positions, arc score, forward score of the
+// source), and the sweep keeps the backward scores of the frames it works on
+// in LDS (three frames' worth, frames with more nodes in memory), so a frame
+// costs one coalesced load of its work records, issued a frame ahead, and LDS
+// operations. The final pass's per-lane epsilon fixpoint runs in LDS when the
+// frame's nodes fit, else on the scores in memory.
 constexpr int kLatSweepBlock = 1024;
-constexpr int kLatBatch = 8;                  // step-arc records per thread per load round
+constexpr int kLatBatch = 8;                  // records per thread per load round
 constexpr int kLatEpsRegs = 8;                // epsilon-slot records per thread per load round (half in the prune)
 constexpr uint32_t kLatEpsLdsNodes = 35840;   // frame nodes whose backward scores fit in LDS (140 KiB)
+constexpr uint32_t kLatPruneLdsNodes = kLatEpsLdsNodes / 3;   // prune: one frame of three in LDS
 constexpr int kMaxPruneInterval = 512;        // 2N + 1 step offsets fit the workgroup's table
 constexpr int kLatKeepBlocks = 256;           // workgroups of the final pass's flat epsilon keep
+constexpr int kLatPrepBlock = 256;
+constexpr int kLatPrepRecs = 4;              // prune work records per thread per load round
 
 struct SweepShared {
-    uint32_t bwd[kLatEpsLdsNodes];               // one frame's backward scores (epsilon fixpoint)
+    uint32_t bwd[kLatEpsLdsNodes];               // final pass: one frame's backward scores; prune: three frames'
     uint32_t off0[2 * kMaxPruneInterval + 2];    // prune: step offsets of slots W .. F before compaction
     uint32_t nb0[2 * kMaxPruneInterval + 2];     // prune: first nodes of frames W .. F
     uint32_t exs[kLatSweepBlock];                // compaction: survivors before each thread's records
@@ -2034,59 +2042,6 @@ __device__ __forceinline__ void lat_emit(const Work &w, LaneCtl &c, int L, bool 
 __device__ __forceinline__ void sweep_clear(const SweepLane &s, uint32_t n0, uint32_t n1)
 {
     for (uint32_t i = n0 + threadIdx.x; i < n1; i += kLatSweepBlock) s.bwd[i] = kOrdNegInf;
-}
-
-// One batch of step-arc records of the prune, [b0, a1) strided over the
-// workgroup (positions past a1 read as pass 1, so they are skipped).
-__device__ __forceinline__ void load_batch(const SweepLane &s, uint32_t b0, uint32_t a1, int4 (&r)[kLatBatch])
-{
-#pragma unroll
-    for (int k = 0; k < kLatBatch; ++k) {
-        const uint32_t i = b0 + (uint32_t)k * kLatSweepBlock + threadIdx.x;
-        r[k] = i < a1 ? s.rec[i] : make_int4(0, 0, 0, 1);
-    }
-}
-
-// Step f's arcs in the prune: records [a0, a1), those with pass 0 (step 2 of
-// the sweep). Sources are nodes ns + position, destinations nd + position;
-// dpos: non-null when the destination fields may still hold states (the
-// newest step of a running lane), mapped to positions by it. r holds the first
-// batch, loaded ahead by the caller.
-template <typename LPT>
-__device__ __forceinline__ void sweep_step(const Work &w, const SweepLane &s, uint32_t a0, uint32_t a1,
-                                           uint32_t ns, uint32_t nd, const int32_t *dpos, const LPT *row,
-                                           int4 (&r)[kLatBatch])
-{
-    const uint32_t tid = threadIdx.x;
-    for (uint32_t b0 = a0; b0 < a1; b0 += (uint32_t)kLatBatch * kLatSweepBlock) {
-        if (b0 != a0) load_batch(s, b0, a1, r);
-        ArcDLW ad[kLatBatch];
-#pragma unroll
-        for (int k = 0; k < kLatBatch; ++k) {
-            ad[k] = ArcDLW{0, 0u, 0.0f};
-            if (r[k].w == 0) ad[k] = w.arc_dlw[r[k].y];
-        }
-        float sa[kLatBatch], bd[kLatBatch], fw[kLatBatch];
-#pragma unroll
-        for (int k = 0; k < kLatBatch; ++k) {
-            sa[k] = 0.0f;
-            bd[k] = 0.0f;
-            fw[k] = 0.0f;
-            if (r[k].w != 0) continue;
-            sa[k] = ad[k].weight + lp_at(row, ad[k].ilabel);
-            const uint32_t dz = (uint32_t)r[k].z;
-            const uint32_t dn = nd + ((dpos && (dz & kLatUnresolved)) ? (uint32_t)dpos[dz & ~kLatUnresolved] : dz);
-            bd[k] = ord2f(load_bwd(&s.bwd[dn]));
-            fw[k] = s.fwd[ns + (uint32_t)r[k].x];
-        }
-#pragma unroll
-        for (int k = 0; k < kLatBatch; ++k) {
-            if (r[k].w != 0) continue;   // (positions past a1 carry pass 1)
-            const float v = sa[k] + bd[k];
-            if (v > -__builtin_inff()) atomicMax(&s.bwd[ns + (uint32_t)r[k].x], f2ord(v));
-            if (!(((fw[k] + sa[k]) + bd[k]) >= s.thr)) s.rec[b0 + (uint32_t)k * kLatSweepBlock + tid].w = -1;
-        }
-    }
 }
 
 // Keeps (final pass) or marks (prune) one epsilon record of frame f with
@@ -2345,38 +2300,179 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_eps_back(const Work *__r
     }
 }
 
+// Lanes the interval prune after real step t works on: running lanes with more
+// real steps whose lattice has not overflowed.
+__device__ __forceinline__ bool prune_lane(const Work &w, const LaneCtl &c, int t)
+{
+    return c.status == kActive && c.last_step == t && t + 1 < c.T && lat_complete(w, c);
+}
+
+// The prune's work records of lane L: its output area, unused until the final
+// pass (which runs after every prune), holds one int4 per record index.
+__device__ __forceinline__ int4 *lat_work(const Work &w, int L)
+{
+    return reinterpret_cast<int4 *>(w.lat_out + (size_t)L * w.lat_cap * kLatFields);
+}
+
+// Work records of the interval prune after real step t, flat over lanes and
+// slots (blockIdx.y = lane, blockIdx.x = slot W + 1 + x, whose records hold
+// step x + W's arcs and frame x + W + 1's epsilon arcs): for each record of the
+// slot, {source position, destination position, s = weight + log-prob, fwd of
+// the source} for a step arc (pass 0), y = -1 for any other. Step t's own arcs
+// still hold destination states: their positions come from frame F's map.
+template <typename LPT>
+__global__ __launch_bounds__(kLatPrepBlock) void k_lat_prep(const Work *__restrict__ wp, int t)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.y;
+    if (L >= w.max_lanes) return;
+    const LaneCtl &c = w.ctl[L];
+    if (!prune_lane(w, c, t)) return;
+    const int F = t + 1, W = max(0, F - 2 * w.lat_prune_interval);
+    const int sl = W + 1 + (int)blockIdx.x;
+    if (sl > F) return;
+    const size_t FF = (size_t)w.max_frames + 3;
+    const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+    const uint32_t a0 = aoff[sl], a1 = sl < F ? aoff[sl + 1] : c.lat_cursor;
+    const uint32_t ns = w.lat_nbase[(size_t)L * FF + (size_t)(sl - 1)];
+    const int32_t *dpos = sl == F ? pick(w.pos, lane_par(c, F)) + (size_t)L * w.num_states : nullptr;
+    const LpDesc d = *w.lp;
+    const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)(sl - 1) * d.stride_t;
+    const int4 *rec = w.lat_arc + (size_t)L * w.lat_cap;
+    const float *fwd = w.lat_score + (size_t)L * w.lat_nodes;
+    int4 *work = lat_work(w, L);
+    // kLatPrepRecs records per thread at a time, each level of loads issued
+    // for all of them before any is used
+    constexpr uint32_t kStride = (uint32_t)kLatPrepRecs * kLatPrepBlock;
+    for (uint32_t b0 = a0; b0 < a1; b0 += kStride) {
+        int4 r[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatPrepBlock + threadIdx.x;
+            r[k] = i < a1 ? rec[i] : make_int4(0, 0, 0, 1);
+        }
+        ArcDLW ad[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) ad[k] = r[k].w == 0 ? w.arc_dlw[r[k].y] : ArcDLW{0, 0u, 0.0f};
+        int4 o[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            o[k] = make_int4(0, -1, 0, 0);
+            if (r[k].w != 0) continue;
+            const float sa = ad[k].weight + lp_at(row, ad[k].ilabel);
+            const uint32_t dz = (uint32_t)r[k].z;
+            const uint32_t dp = (dpos && (dz & kLatUnresolved)) ? (uint32_t)dpos[dz & ~kLatUnresolved] : dz;
+            o[k] = make_int4(r[k].x, (int)dp, (int)__float_as_uint(sa),
+                             (int)__float_as_uint(fwd[ns + (uint32_t)r[k].x]));
+        }
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatPrepBlock + threadIdx.x;
+            if (i < a1) work[i] = o[k];
+        }
+    }
+}
+
+// The prune's backward sweep over frames F - 1 .. W (steps 1-3 above) on the
+// work records; frame F's scores are set. A frame with at most
+// kLatPruneLdsNodes nodes keeps its scores in LDS buffer f % 3 (a buffer is
+// cleared two frames after its last reader), a larger one in memory. Without
+// epsilon arcs the next frame's first batch of work records is loaded as this
+// frame starts; with them, after the frame's fixpoint (whose loads need the
+// registers).
+template <bool EPS>
+__device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const SweepLane &s, SweepShared &sh,
+                                            const int4 *__restrict__ work, int F, int W, uint32_t nF,
+                                            uint32_t cursor, int4 (&r)[kLatBatch])
+{
+    const uint32_t tid = threadIdx.x;
+    auto nodes = [&](int f) -> uint32_t { return f == F ? nF : sh.nb0[f + 1 - W] - sh.nb0[f - W]; };
+    auto lbase = [&](int f) -> uint32_t { return (uint32_t)(f % 3) * kLatPruneLdsNodes; };
+    auto load_work = [&](uint32_t b0, uint32_t a1, int4 (&x)[kLatBatch]) {
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatSweepBlock + tid;
+            x[k] = i < a1 ? work[i] : make_int4(0, -1, 0, 0);
+        }
+    };
+    load_work(sh.off0[F - W], cursor, r);   // step F - 1's first batch
+    for (int f = F - 1; f >= W; --f) {
+        const uint32_t ns = sh.nb0[f - W], nd = sh.nb0[f + 1 - W], nn = nodes(f);
+        const bool ls = nn <= kLatPruneLdsNodes, ld = nodes(f + 1) <= kLatPruneLdsNodes;
+        const uint32_t os = lbase(f), od = lbase(f + 1);
+        if (ls)
+            for (uint32_t i = tid; i < nn; i += kLatSweepBlock) sh.bwd[os + i] = kOrdNegInf;
+        else
+            for (uint32_t i = tid; i < nn; i += kLatSweepBlock) s.bwd[ns + i] = kOrdNegInf;
+        __syncthreads();
+        const uint32_t a0 = sh.off0[f + 1 - W], a1 = (f + 1 < F) ? sh.off0[f + 2 - W] : cursor;
+        const uint32_t n0 = f > W ? sh.off0[f - W] : 0u, n1 = f > W ? sh.off0[f + 1 - W] : 0u;
+        int4 nx[kLatBatch];
+        if (!EPS) load_work(n0, n1, nx);
+        for (uint32_t b0 = a0; b0 < a1; b0 += (uint32_t)kLatBatch * kLatSweepBlock) {
+            if (b0 != a0) load_work(b0, a1, r);
+            float bv[kLatBatch];
+            if (ld) {
+#pragma unroll
+                for (int k = 0; k < kLatBatch; ++k) bv[k] = r[k].y != -1 ? ord2f(sh.bwd[od + (uint32_t)r[k].y]) : 0.0f;
+            } else {
+#pragma unroll
+                for (int k = 0; k < kLatBatch; ++k)
+                    bv[k] = r[k].y != -1 ? ord2f(load_bwd(&s.bwd[nd + (uint32_t)r[k].y])) : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kLatBatch; ++k) {
+                if (r[k].y == -1) continue;   // (also positions past a1)
+                const float sa = __int_as_float(r[k].z), fw = __int_as_float(r[k].w);
+                const float v = sa + bv[k];
+                if (v > -__builtin_inff()) {
+                    if (ls) atomicMax(&sh.bwd[os + (uint32_t)r[k].x], f2ord(v));
+                    else atomicMax(&s.bwd[ns + (uint32_t)r[k].x], f2ord(v));
+                }
+                if (!(((fw + sa) + bv[k]) >= s.thr)) s.rec[b0 + (uint32_t)k * kLatSweepBlock + tid].w = -1;
+            }
+        }
+        if (EPS) {
+            __syncthreads();
+            const uint32_t e0 = sh.off0[f - W], e1 = sh.off0[f + 1 - W];
+            if (e1 > e0) {
+                if (ls) eps_fix<true, true, kLatEpsRegs / 2>(w, c, s, sh.bwd + os, f, e0, e1, ns, nn);
+                else eps_fix<true, false, kLatEpsRegs / 2>(w, c, s, s.bwd + ns, f, e0, e1, ns, nn);
+            }
+            load_work(n0, n1, nx);
+        }
+#pragma unroll
+        for (int k = 0; k < kLatBatch; ++k) r[k] = nx[k];
+    }
+}
+
 // Interval prune (page section 7, lat_prune_interval = N: a window-loose prune
 // that bounds the lattice, the exact final pass unchanged), after real step t
-// with (t + 1) % N == 0 for lanes with more real steps, one workgroup per lane.
-// With F = t + 1 the frontier's frame and W = max(0, F - 2N): the sweep over
-// frames F - 1 .. W starts from bwd(u) = -fwd(u) at every frontier token u (no
-// complete path through u can score more than the final best) and marks (pass
-// field -1) the arcs of steps W .. F - 1 and the epsilon arcs of frames
-// W .. F - 1 with (fwd(src) + s) + bwd(dst) < 0 - output_beam; then the records
-// from step W - 1's first to the cursor are compacted in place, in order, with
-// the step offsets rewritten. Step t's own arcs still hold destination states
-// (the next compaction resolves them): their destination nodes come from the
-// position map of frame F.
-template <typename LPT>
+// with (t + 1) % N == 0 for lanes with more real steps, one workgroup per lane,
+// after k_lat_prep(t). With F = t + 1 the frontier's frame and
+// W = max(0, F - 2N): the sweep over frames F - 1 .. W starts from
+// bwd(u) = -fwd(u) at every frontier token u (no complete path through u can
+// score more than the final best) and marks (pass field -1) the arcs of steps
+// W .. F - 1 and the epsilon arcs of frames W .. F - 1 with
+// (fwd(src) + s) + bwd(dst) < 0 - output_beam; then the records from step
+// W - 1's first to the cursor are compacted in place, in order, with the step
+// offsets rewritten.
 __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     const int L = (int)blockIdx.x;
     if (L >= w.max_lanes) return;
     LaneCtl &c = w.ctl[L];
-    const int F = t + 1;
-    if (c.status != kActive || c.last_step != t || F >= c.T || !lat_complete(w, c)) return;
+    if (!prune_lane(w, c, t)) return;
     __shared__ SweepShared sh;
+    const int F = t + 1;
     const int W = max(0, F - 2 * w.lat_prune_interval);
     const size_t FF = (size_t)w.max_frames + 3;
     uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
     const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
     const SweepLane s = sweep_lane(w, L, 0.0f - w.output_beam);
-    const int pF = lane_par(c, F);
-    const uint32_t nF = (uint32_t)c.cnt[pF];
-    const int32_t *posF = pick(w.pos, pF) + (size_t)L * w.num_states;
+    const uint32_t nF = (uint32_t)c.cnt[lane_par(c, F)];
     const uint32_t cursor = c.lat_cursor;
-    const LpDesc d = *w.lp;
     const uint32_t tid = threadIdx.x;
     const int nslot = F - W + 1;
     for (int i = (int)tid; i < nslot; i += kLatSweepBlock) {
@@ -2384,31 +2480,16 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
         sh.nb0[i] = nbase[W + i];
     }
     const uint32_t nf0 = nbase[F];
-    for (uint32_t i = nf0 + tid; i < nf0 + nF; i += kLatSweepBlock) s.bwd[i] = f2ord(0.0f - s.fwd[i]);
+    if (nF <= kLatPruneLdsNodes) {
+        const uint32_t o = (uint32_t)(F % 3) * kLatPruneLdsNodes;
+        for (uint32_t i = tid; i < nF; i += kLatSweepBlock) sh.bwd[o + i] = f2ord(0.0f - s.fwd[nf0 + i]);
+    } else {
+        for (uint32_t i = nf0 + tid; i < nf0 + nF; i += kLatSweepBlock) s.bwd[i] = f2ord(0.0f - s.fwd[i]);
+    }
     __syncthreads();
     int4 r[kLatBatch];
-    load_batch(s, sh.off0[F - W], cursor, r);   // the newest step's first batch
-    for (int f = F - 1; f >= W; --f) {
-        const uint32_t ns = sh.nb0[f - W], nd = sh.nb0[f + 1 - W];
-        sweep_clear(s, ns, nd);
-        __syncthreads();
-        const uint32_t a0 = sh.off0[f + 1 - W], a1 = (f + 1 < F) ? sh.off0[f + 2 - W] : cursor;
-        // the next frame's step arcs (none after frame W): their first batch is
-        // loaded as soon as this frame no longer needs r, so the loads overlap
-        // the rest of the frame (which changes no pass-0 record of them: it
-        // marks this frame's own records and its epsilon records only)
-        const uint32_t n0 = f > W ? sh.off0[f - W] : 0u, n1 = f > W ? sh.off0[f + 1 - W] : 0u;
-        const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)f * d.stride_t;
-        sweep_step<LPT>(w, s, a0, a1, ns, nd, (f + 1 < F) ? nullptr : posF, row, r);
-        if (w.has_eps) {
-            __syncthreads();
-            sweep_eps<true, kLatEpsRegs / 2>(w, c, s, sh, f, sh.off0[f - W], sh.off0[f + 1 - W], ns, nd - ns);
-            load_batch(s, n0, n1, r);
-        } else {
-            load_batch(s, n0, n1, r);
-        }
-        __syncthreads();
-    }
+    if (w.has_eps) prune_sweep<true>(w, c, s, sh, lat_work(w, L), F, W, nF, cursor, r);
+    else prune_sweep<false>(w, c, s, sh, lat_work(w, L), F, W, nF, cursor, r);
     // in-place compaction of [off0[0], cursor), kLatBatch records per thread (a
     // contiguous run) per chunk: every record of a chunk is read before any is
     // written, and survivors only move down, so no unread record is overwritten;
@@ -3172,10 +3253,14 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKGcRoots: go(k_gc_roots, G, B, s, e0, e1, dw); break;
     case kKGcClear: go(k_gc_clear, G, B, s, e0, e1, dw); break;
     case kKGcEnd: go(k_gc_end, dim3(1), dim3(kWave), s, e0, e1, dw); break;
+    case kKLatPrep:
+        if (w.lat_prune_interval < 1 || w.lat_prune_interval > kMaxPruneInterval) return hipErrorInvalidValue;
+        if (f16) go(k_lat_prep<__half>, dim3(2 * w.lat_prune_interval, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw, t);
+        else go(k_lat_prep<float>, dim3(2 * w.lat_prune_interval, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw, t);
+        break;
     case kKLatPrune:
         if (w.lat_prune_interval < 1 || w.lat_prune_interval > kMaxPruneInterval) return hipErrorInvalidValue;
-        if (f16) go(k_lat_prune<__half>, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
-        else go(k_lat_prune<float>, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
+        go(k_lat_prune, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
         break;
     default: return hipErrorInvalidValue;
     }
