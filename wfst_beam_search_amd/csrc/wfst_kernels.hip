@@ -1971,8 +1971,8 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
 // inside a workgroup. The prune's sweep therefore waits on no gather: a flat
 // kernel over the whole chip (k_lat_prep) first turns every step arc of the
 // window into a work record (positions, arc score, forward score of the
-// source), and the sweep keeps the backward scores of the frames it works on
-// in LDS (three frames' worth, frames with more nodes in memory), so a frame
+// source), and the sweep keeps the backward scores of the two frames it works
+// on in LDS (a frame that does not fit beside the other in memory), so a frame
 // costs one coalesced load of its work records, issued a frame ahead, and LDS
 // operations. The final pass's per-lane epsilon fixpoint runs in LDS when the
 // frame's nodes fit, else on the scores in memory.
@@ -1980,14 +1980,13 @@ constexpr int kLatSweepBlock = 1024;
 constexpr int kLatBatch = 8;                  // records per thread per load round
 constexpr int kLatEpsRegs = 8;                // epsilon-slot records per thread per load round (half in the prune)
 constexpr uint32_t kLatEpsLdsNodes = 35840;   // frame nodes whose backward scores fit in LDS (140 KiB)
-constexpr uint32_t kLatPruneLdsNodes = kLatEpsLdsNodes / 3;   // prune: one frame of three in LDS
 constexpr int kMaxPruneInterval = 512;        // 2N + 1 step offsets fit the workgroup's table
 constexpr int kLatKeepBlocks = 256;           // workgroups of the final pass's flat epsilon keep
 constexpr int kLatPrepBlock = 256;
 constexpr int kLatPrepRecs = 4;              // prune work records per thread per load round
 
 struct SweepShared {
-    uint32_t bwd[kLatEpsLdsNodes];               // final pass: one frame's backward scores; prune: three frames'
+    uint32_t bwd[kLatEpsLdsNodes];               // backward scores of one frame (final pass) or two (prune)
     uint32_t off0[2 * kMaxPruneInterval + 2];    // prune: step offsets of slots W .. F before compaction
     uint32_t nb0[2 * kMaxPruneInterval + 2];     // prune: first nodes of frames W .. F
     uint32_t exs[kLatSweepBlock];                // compaction: survivors before each thread's records
@@ -2107,17 +2106,37 @@ __device__ __forceinline__ void eps_fix(const Work &w, LaneCtl &c, const SweepLa
         for (int k = 0; k < R; ++k) wt[k] = r[k].w > 0 ? w.arc_dlw[r[k].y].weight : 0.0f;
     };
     // relaxes the loaded records, last first; the number of 1024-record
-    // groups present (kn) is workgroup-uniform
-    auto relax = [&](uint32_t q) -> int {
+    // groups present (kn) is workgroup-uniform. With `each`, a barrier follows
+    // every group (a later group's raises are seen by the earlier ones: most
+    // chains settle in one round); without, the loads of every group are
+    // issued before any atomic and one barrier ends the batch (scores in
+    // memory: one load and one atomic latency per batch instead of per group)
+    auto relax = [&](uint32_t q, bool each) -> int {
         const uint32_t left = e1 - (e0 + q * kSuper);
         const int kn = (int)min((left + kLatSweepBlock - 1) / kLatSweepBlock, (uint32_t)R);
         int ch = 0;
+        if (each) {
 #pragma unroll
-        for (int k = R - 1; k >= 0; --k) {
-            if (k >= kn) continue;
-            if (r[k].w > 0) {
-                const float v = wt[k] + ord2f(get((uint32_t)r[k].z));
-                if (v > -__builtin_inff()) {
+            for (int k = R - 1; k >= 0; --k) {
+                if (k >= kn) continue;
+                if (r[k].w > 0) {
+                    const float v = wt[k] + ord2f(get((uint32_t)r[k].z));
+                    if (v > -__builtin_inff()) {
+                        const uint32_t o = f2ord(v);
+                        if (atomicMax(&bw[(uint32_t)r[k].x], o) < o) ch = 1;
+                    }
+                }
+                __syncthreads();
+            }
+        } else {
+            float bd[R];
+#pragma unroll
+            for (int k = R - 1; k >= 0; --k)
+                bd[k] = (k < kn && r[k].w > 0) ? ord2f(get((uint32_t)r[k].z)) : -__builtin_inff();
+#pragma unroll
+            for (int k = R - 1; k >= 0; --k) {
+                const float v = wt[k] + bd[k];
+                if (k < kn && r[k].w > 0 && v > -__builtin_inff()) {
                     const uint32_t o = f2ord(v);
                     if (atomicMax(&bw[(uint32_t)r[k].x], o) < o) ch = 1;
                 }
@@ -2128,13 +2147,16 @@ __device__ __forceinline__ void eps_fix(const Work &w, LaneCtl &c, const SweepLa
     };
     if (nsup == 1) load(0);
     for (uint32_t round = 0; round <= n + 1u; ++round) {
+        // scores in LDS: a barrier per group in every round; in memory: in the
+        // first round only (it settles most chains), later rounds batched
+        const bool each = LDS || round == 0;
         int ch = 0;
         if (nsup == 1) {
-            ch = relax(0);
+            ch = relax(0, each);
         } else {
             for (uint32_t q = nsup; q-- > 0;) {
                 load(q);
-                ch |= relax(q);
+                ch |= relax(q, each);
             }
         }
         if (!__syncthreads_or(ch)) break;
@@ -2373,21 +2395,32 @@ __global__ __launch_bounds__(kLatPrepBlock) void k_lat_prep(const Work *__restri
     }
 }
 
+// LDS place of the prune sweep's frame of n nodes beside the live frame at
+// [po, po + pn) (po == kNoLds: that one is in memory): right after it, else
+// before it, else kNoLds (the frame's scores stay in memory).
+constexpr uint32_t kNoLds = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t lds_place(uint32_t n, uint32_t po, uint32_t pn)
+{
+    if (n > kLatEpsLdsNodes) return kNoLds;
+    if (po == kNoLds) return 0u;
+    if (po + pn + n <= kLatEpsLdsNodes) return po + pn;
+    return n <= po ? 0u : kNoLds;
+}
+
 // The prune's backward sweep over frames F - 1 .. W (steps 1-3 above) on the
-// work records; frame F's scores are set. A frame with at most
-// kLatPruneLdsNodes nodes keeps its scores in LDS buffer f % 3 (a buffer is
-// cleared two frames after its last reader), a larger one in memory. Without
+// work records; frame F's scores are set, at LDS offset oF (or in memory). Two
+// frames are live at a time, f + 1 (read) and f (raised): each gets a place in
+// the LDS array beside the other (lds_place) or stays in memory. Without
 // epsilon arcs the next frame's first batch of work records is loaded as this
 // frame starts; with them, after the frame's fixpoint (whose loads need the
 // registers).
 template <bool EPS>
 __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const SweepLane &s, SweepShared &sh,
-                                            const int4 *__restrict__ work, int F, int W, uint32_t nF,
+                                            const int4 *__restrict__ work, int F, int W, uint32_t nF, uint32_t oF,
                                             uint32_t cursor, int4 (&r)[kLatBatch])
 {
     const uint32_t tid = threadIdx.x;
     auto nodes = [&](int f) -> uint32_t { return f == F ? nF : sh.nb0[f + 1 - W] - sh.nb0[f - W]; };
-    auto lbase = [&](int f) -> uint32_t { return (uint32_t)(f % 3) * kLatPruneLdsNodes; };
     auto load_work = [&](uint32_t b0, uint32_t a1, int4 (&x)[kLatBatch]) {
 #pragma unroll
         for (int k = 0; k < kLatBatch; ++k) {
@@ -2395,16 +2428,21 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
             x[k] = i < a1 ? work[i] : make_int4(0, -1, 0, 0);
         }
     };
+    // frame g's nodes at -inf, at LDS offset o or in memory
+    auto clear = [&](int g, uint32_t o) {
+        const uint32_t n = nodes(g);
+        if (o != kNoLds)
+            for (uint32_t i = tid; i < n; i += kLatSweepBlock) sh.bwd[o + i] = kOrdNegInf;
+        else
+            for (uint32_t i = tid; i < n; i += kLatSweepBlock) s.bwd[sh.nb0[g - W] + i] = kOrdNegInf;
+    };
+    uint32_t od = oF, os = lds_place(nodes(F - 1), oF, nF);
+    clear(F - 1, os);
     load_work(sh.off0[F - W], cursor, r);   // step F - 1's first batch
+    __syncthreads();
     for (int f = F - 1; f >= W; --f) {
         const uint32_t ns = sh.nb0[f - W], nd = sh.nb0[f + 1 - W], nn = nodes(f);
-        const bool ls = nn <= kLatPruneLdsNodes, ld = nodes(f + 1) <= kLatPruneLdsNodes;
-        const uint32_t os = lbase(f), od = lbase(f + 1);
-        if (ls)
-            for (uint32_t i = tid; i < nn; i += kLatSweepBlock) sh.bwd[os + i] = kOrdNegInf;
-        else
-            for (uint32_t i = tid; i < nn; i += kLatSweepBlock) s.bwd[ns + i] = kOrdNegInf;
-        __syncthreads();
+        const bool ls = os != kNoLds, ld = od != kNoLds;
         const uint32_t a0 = sh.off0[f + 1 - W], a1 = (f + 1 < F) ? sh.off0[f + 2 - W] : cursor;
         const uint32_t n0 = f > W ? sh.off0[f - W] : 0u, n1 = f > W ? sh.off0[f + 1 - W] : 0u;
         int4 nx[kLatBatch];
@@ -2443,6 +2481,14 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
         }
 #pragma unroll
         for (int k = 0; k < kLatBatch; ++k) r[k] = nx[k];
+        if (f > W) {
+            __syncthreads();   // frame f final, frame f + 1 no longer read
+            const uint32_t o = lds_place(nodes(f - 1), os, nn);
+            clear(f - 1, o);
+            od = os;
+            os = o;
+            __syncthreads();
+        }
     }
 }
 
@@ -2479,17 +2525,15 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
         sh.off0[i] = aoff[W + i];
         sh.nb0[i] = nbase[W + i];
     }
-    const uint32_t nf0 = nbase[F];
-    if (nF <= kLatPruneLdsNodes) {
-        const uint32_t o = (uint32_t)(F % 3) * kLatPruneLdsNodes;
-        for (uint32_t i = tid; i < nF; i += kLatSweepBlock) sh.bwd[o + i] = f2ord(0.0f - s.fwd[nf0 + i]);
-    } else {
+    const uint32_t nf0 = nbase[F], oF = lds_place(nF, kNoLds, 0u);
+    if (oF != kNoLds)
+        for (uint32_t i = tid; i < nF; i += kLatSweepBlock) sh.bwd[oF + i] = f2ord(0.0f - s.fwd[nf0 + i]);
+    else
         for (uint32_t i = nf0 + tid; i < nf0 + nF; i += kLatSweepBlock) s.bwd[i] = f2ord(0.0f - s.fwd[i]);
-    }
-    __syncthreads();
+    __syncthreads();   // (sh.nb0 and sh.off0 too)
     int4 r[kLatBatch];
-    if (w.has_eps) prune_sweep<true>(w, c, s, sh, lat_work(w, L), F, W, nF, cursor, r);
-    else prune_sweep<false>(w, c, s, sh, lat_work(w, L), F, W, nF, cursor, r);
+    if (w.has_eps) prune_sweep<true>(w, c, s, sh, lat_work(w, L), F, W, nF, oF, cursor, r);
+    else prune_sweep<false>(w, c, s, sh, lat_work(w, L), F, W, nF, oF, cursor, r);
     // in-place compaction of [off0[0], cursor), kLatBatch records per thread (a
     // contiguous run) per chunk: every record of a chunk is read before any is
     // written, and survivors only move down, so no unread record is overwritten;
