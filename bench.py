@@ -180,6 +180,32 @@ def cpu_baseline(graph, lp, lengths, wl, seconds, gpu=None, allow_partial=False)
                       f"single-threaded C oracle pinned to one core; host nproc {os.cpu_count()}, {model})"}
 
 
+def cpu_baseline_all_cores(graph, lp, lengths, wl, allow_partial=False, threads=16):
+    """The oracle over every lane of the batch, one lane per thread at a time on
+    up to ``threads`` of the host's cores (the oracle is plain C called through
+    ctypes, which releases the interpreter lock, and keeps no global state):
+    the host's throughput with lanes in parallel, beside the one-core figure."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    og = oracle.OracleGraph(graph)
+    n = max(1, min(threads, len(os.sched_getaffinity(0))))
+
+    def one(b):
+        oracle.decode_lane(og, lp[b], int(lengths[b]), wl.beam, wl.max_active,
+                           allow_partial=allow_partial, eps_iterations=wl.eps_iterations)
+        return int(lengths[b])
+
+    one(0)   # (loads the library before the threads start)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        frames = sum(ex.map(one, range(lp.shape[0])))
+    dt = time.perf_counter() - t0
+    return {"value": frames / dt, "unit": "frames/s", "cores": n, "kind": "oracle",
+            "sample": f"all {lp.shape[0]} lanes of the {wl.name} batch ({frames} frames, {dt:.1f} s), "
+                      f"{n} threads, lanes in parallel"}
+
+
 def stream_bench(args, wl, graph, lp, lengths, dev):
     """Streams the workload's utterances (one stream per lane, all lanes advanced
     together chunk by chunk, then finalized): a step is the whole batch streamed.
@@ -431,6 +457,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="plain launches instead of the captured graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-all-cores", type=int, default=1,
+                    help="1: also time the oracle over every lane with lanes in parallel on up to 16 cores")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per frame-loop launch (0: derive)")
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--report", default="", help="also write a detailed JSON report here")
@@ -583,10 +611,12 @@ def main():
                     "traffic": traffic_from_profiles(dom, wl.name),
                     "bytes_per_launch": int(bpl), "avg_launch_us": round(ktimes[dom]["avg_launch_us"], 3)}
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(graph, lp, lengths, wl, args.cpu_seconds, gpu=res,
                            allow_partial=args.sparse_finals is not None)
+        if args.cpu_all_cores:
+            cpu_all = cpu_baseline_all_cores(graph, lp, lengths, wl, allow_partial=args.sparse_finals is not None)
 
     configs = {}
     others = [int(c) for c in args.configs.split(",") if c.strip()] if args.configs else []
@@ -645,6 +675,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if cpu_all is not None:
+        line["cpu_baseline_all_cores"] = cpu_all
     if configs:
         line["configs"] = configs
     line["log_entries_at_end"] = int(st["log_entries"])
