@@ -252,6 +252,19 @@ def test_lattice_interval_prune_bounds_the_arena():
         dg.release()
 
 
+def test_lattice_interval_prune_longest_window():
+    """The largest interval (512 steps): 1100-frame lanes pruned after steps
+    511 and 1023 over windows reaching back to frame 0 (1025 step offsets in
+    the sweep's table, 1024 slots in the work-record pass); kept records equal
+    the oracle's with the same interval."""
+    g = synth.random_graph(15, n=30, deg=(1, 5), vocab=6, self_loop=0.3)
+    lp = synth.random_logprobs(16, 2, 1100, g.vocab, sigma=2.0)
+    L = np.array([1100, 1030], dtype=np.int32)
+    _say("lattice longest prune window", lp.shape)
+    _, lats = lattice_case(g, lp, L, 6.0, 100, 0, False, 2.0, lattice_cap=1 << 16, lat_prune_interval=512)
+    assert all(x.shape[0] > 1000 for x in lats)
+
+
 def test_lattice_with_log_compaction():
     """Log compaction rounds in lattice mode (section 6.3): lattice nodes are
     frame positions, never winners-log entries, so rounds every 16 steps leave
