@@ -2534,6 +2534,7 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
     int4 r[kLatBatch];
     if (w.has_eps) prune_sweep<true>(w, c, s, sh, lat_work(w, L), F, W, nF, oF, cursor, r);
     else prune_sweep<false>(w, c, s, sh, lat_work(w, L), F, W, nF, oF, cursor, r);
+    __syncthreads();   // the last frame's marks (slots W and W + 1) before any is read
     // in-place compaction of [off0[0], cursor), kLatBatch records per thread (a
     // contiguous run) per chunk: every record of a chunk is read before any is
     // written, and survivors only move down, so no unread record is overwritten;
