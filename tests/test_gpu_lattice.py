@@ -265,6 +265,22 @@ def test_lattice_interval_prune_longest_window():
     assert all(x.shape[0] > 1000 for x in lats)
 
 
+@pytest.mark.parametrize("grid", [1, 7])
+def test_lattice_grid_sizes(grid):
+    """Lattice mode with one and with seven workgroups per frame-loop launch
+    (grid_blocks), with and without the interval prune, on random
+    epsilon-free and TLG graphs: kept records equal the oracle's."""
+    for seed in range(8):
+        if seed % 2:
+            g, lp, L, beam, ma, mi, ap, ob, P = _random_tlg_case(600 + seed)
+        else:
+            g, lp, L, beam, ma, mi, ap, ob = _random_case(600 + seed)
+            P = 0
+        n = (0, 0, 2, 3)[seed % 4]
+        _say("lattice grid", grid, seed, lp.shape, P, n)
+        lattice_case(g, lp, L, beam, ma, mi, ap, ob, eps_iterations=P, grid_blocks=grid, lat_prune_interval=n)
+
+
 def test_lattice_with_log_compaction():
     """Log compaction rounds in lattice mode (section 6.3): lattice nodes are
     frame positions, never winners-log entries, so rounds every 16 steps leave

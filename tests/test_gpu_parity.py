@@ -105,6 +105,28 @@ def test_random_small_graphs(eps):
         compare_batch(r, steps, o)
 
 
+@pytest.mark.parametrize("grid", [1, 3, 8, 1000])
+def test_grid_sizes(grid):
+    """Any workgroup count of the frame-loop kernels (grid_blocks): one, a
+    prime, a multiple of the XCD count, more workgroups than work. The
+    per-wavefront shares, the bookkeeping of workgroup 0 and the XCD-aware
+    block order change with it; random graphs with and without epsilon arcs
+    and the mid-size workload's first lanes equal the oracle's results and
+    per-step records."""
+    for seed in range(12):
+        eps = bool(seed % 2)
+        g, lp, L, beam, ma, mi, ap, P = _random_case(3000 + seed, eps)
+        _say("grid", grid, seed, lp.shape, P)
+        r, steps, _ = gpu_decode(g, lp, L, beam, ma, mi, ap, P, grid_blocks=grid)
+        compare_batch(r, steps, oracle_lanes(g, lp, L, beam, ma, mi, ap, P))
+    g, lp, L = synth.workload_inputs(2)
+    wl = synth.WORKLOADS[2]
+    lp2 = np.ascontiguousarray(lp[:3, :60])
+    L2 = np.minimum(L[:3], 60).astype(np.int32)
+    r, steps, _ = gpu_decode(g, lp2, L2, wl.beam, wl.max_active, grid_blocks=grid)
+    compare_batch(r, steps, oracle_lanes(g, lp2, L2, wl.beam, wl.max_active))
+
+
 def test_greedy_closed_form_gpu():
     V, T = 500, 60
     spec = {"start": 0, "vocab": V, "epsilon_id": -1,
