@@ -2410,7 +2410,8 @@ __device__ __forceinline__ uint32_t lds_place(uint32_t n, uint32_t po, uint32_t 
 // The prune's backward sweep over frames F - 1 .. W (steps 1-3 above) on the
 // work records; frame F's scores are set, at LDS offset oF (or in memory). Two
 // frames are live at a time, f + 1 (read) and f (raised): each gets a place in
-// the LDS array beside the other (lds_place) or stays in memory. Without
+// the LDS array beside the other (lds_place), or the whole array when it fits
+// alone (the other's scores then move to memory), or stays in memory. Without
 // epsilon arcs the next frame's first batch of work records is loaded as this
 // frame starts; with them, after the frame's fixpoint (whose loads need the
 // registers).
@@ -2436,7 +2437,19 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
         else
             for (uint32_t i = tid; i < n; i += kLatSweepBlock) s.bwd[sh.nb0[g - W] + i] = kOrdNegInf;
     };
+    // a frame that fits the LDS array alone but not beside the frame it reads
+    // takes the whole array; that frame's scores move to memory first (the
+    // step that reads them, the next one, gathers them there)
+    auto evict = [&](uint32_t o, uint32_t n, uint32_t nbase) {
+        for (uint32_t i = tid; i < n; i += kLatSweepBlock) s.bwd[nbase + i] = sh.bwd[o + i];
+        __syncthreads();
+    };
     uint32_t od = oF, os = lds_place(nodes(F - 1), oF, nF);
+    if (os == kNoLds && od != kNoLds && nodes(F - 1) <= kLatEpsLdsNodes) {
+        evict(od, nF, sh.nb0[F - W]);
+        od = kNoLds;
+        os = 0u;
+    }
     clear(F - 1, os);
     load_work(sh.off0[F - W], cursor, r);   // step F - 1's first batch
     __syncthreads();
@@ -2483,7 +2496,12 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
         for (int k = 0; k < kLatBatch; ++k) r[k] = nx[k];
         if (f > W) {
             __syncthreads();   // frame f final, frame f + 1 no longer read
-            const uint32_t o = lds_place(nodes(f - 1), os, nn);
+            uint32_t o = lds_place(nodes(f - 1), os, nn);
+            if (o == kNoLds && ls && nodes(f - 1) <= kLatEpsLdsNodes) {
+                evict(os, nn, ns);
+                os = kNoLds;
+                o = 0u;
+            }
             clear(f - 1, o);
             od = os;
             os = o;
