@@ -1110,17 +1110,24 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
 {
     const uint32_t ep = round_epoch(w, t, 0);
     const LpDesc lpd = *w.lp;
-    if (w.lattice && threadIdx.x < kWave) {
-        const int L = (int)threadIdx.x;
+    // (the second wavefront builds the lattice table beside the first's lane
+    // table; every load of a lane is issued before any decision)
+    if (w.lattice && threadIdx.x >= kWave && threadIdx.x < 2 * kWave) {
+        const int L = (int)threadIdx.x - kWave;
         uint32_t n = 0, a0 = 0, nb = 0;
         // a lane that began step t (whatever step t then did): the arcs of step
         // t - 1 (slot t of the offsets; step -1 is the start closure)
-        if (L < w.max_lanes && w.ctl[L].last_step == t) {
+        if (L < w.max_lanes) {
             const size_t F = (size_t)w.max_frames + 3;
-            a0 = w.lat_aoff[(size_t)L * F + t];
+            const int ls = w.ctl[L].last_step;
+            const uint32_t b0 = w.lat_aoff[(size_t)L * F + t];
             const uint32_t a1 = min(w.lat_aoff[(size_t)L * F + t + 1], w.lat_cap);
-            n = a1 > a0 ? a1 - a0 : 0u;
-            nb = w.lat_nbase[(size_t)L * F + t + 1];
+            const uint32_t nb0 = w.lat_nbase[(size_t)L * F + t + 1];
+            if (ls == t) {
+                a0 = b0;
+                n = a1 > a0 ? a1 - a0 : 0u;
+                nb = nb0;
+            }
         }
         if (L < w.max_lanes) { lt.n[L] = n; lt.a0[L] = a0; lt.nb[L] = nb; }
         uint32_t tot;
