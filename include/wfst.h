@@ -521,8 +521,8 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_STREAM_END  11  /* stream call: commits the chunk's last compaction        */
 #define WFST_K_RECLASS     12  /* stream end: final-step class of the stream's tokens      */
 #define WFST_K_LAT_RESOLVE 13  /* not launched (the next step's WFST_K_FINALIZE does it)  */
-#define WFST_K_LAT_INIT    14  /* lattice: backward scores to -inf                        */
-#define WFST_K_LAT_BACK    15  /* lattice: backward pass and prune of one step's arcs     */
+#define WFST_K_LAT_INIT    14  /* lattice with closure: backward scores to -inf           */
+#define WFST_K_LAT_BACK    15  /* lattice with closure: backward pass and prune of a step */
 #define WFST_K_GC_BEGIN    16  /* log compaction round: set-up and commit                 */
 #define WFST_K_GC_MARK     17  /* log compaction: live entries from the frontier          */
 #define WFST_K_GC_SCAN     18  /* log compaction: positions of live entries               */
@@ -536,7 +536,10 @@ int wfst_decoder_step_stats(wfst_decoder_t d, int32_t lane, int64_t *out, int32_
 #define WFST_K_LAT_EPS_ROUND 26 /* lattice: one flat relaxation round of a frame's epsilon arcs */
 #define WFST_K_EPS_APPLY_EXPAND 27 /* closure: pass k's decisions and writes, then pass k + 1's relaxation */
 #define WFST_K_LAT_PREP    28  /* lattice: the interval prune's arc scores, flat over lanes */
-#define WFST_K_COUNT       29
+#define WFST_K_LAT_FPREP   29  /* lattice without closure: the final pass's arc scores, flat */
+#define WFST_K_LAT_SWEEP   30  /* lattice without closure: backward sweep and prune per lane */
+#define WFST_K_LAT_EMIT    31  /* lattice without closure: the kept arcs written out        */
+#define WFST_K_COUNT       32
 
 /*
  * Turn per-kernel timing on (enable != 0) or off. While on, each decode runs its

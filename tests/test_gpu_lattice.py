@@ -265,6 +265,19 @@ def test_lattice_interval_prune_longest_window():
     assert all(x.shape[0] > 1000 for x in lats)
 
 
+def test_lattice_final_pass_windows():
+    """Lanes of 2100, 1500, 1025 and 1024 frames on an epsilon-free graph
+    without the interval prune: the final pass's sweep walks each lane in
+    windows of 1024 frames, each starting from the scores the one above left;
+    kept records equal the oracle's."""
+    g = synth.random_graph(17, n=30, deg=(1, 5), vocab=6, self_loop=0.3)
+    lp = synth.random_logprobs(18, 4, 2100, g.vocab, sigma=2.0)
+    L = np.array([2100, 1500, 1025, 1024], dtype=np.int32)
+    _say("lattice final-pass windows", lp.shape)
+    _, lats = lattice_case(g, lp, L, 6.0, 100, 0, False, 2.0, lattice_cap=1 << 18)
+    assert all(x.shape[0] > L[b] for b, x in enumerate(lats))
+
+
 @pytest.mark.parametrize("grid", [1, 7])
 def test_lattice_grid_sizes(grid):
     """Lattice mode with one and with seven workgroups per frame-loop launch

@@ -34,7 +34,7 @@ KERNELS = ("clear", "init", "lpmax", "max", "expand", "finalize", "eps_expand", 
            "eps_apply", "backtrack", "stream_begin", "stream_end", "reclass", "lat_resolve", "lat_init",
            "lat_back", "gc_begin", "gc_mark", "gc_scan", "gc_compact", "gc_commit", "gc_roots", "gc_clear",
            "gc_end", "lat_eps_back", "lat_prune", "lat_eps_round", "eps_apply_expand",
-           "lat_prep")
+           "lat_prep", "lat_fprep", "lat_sweep", "lat_emit")
 LATTICE_FIELDS = ("frame", "src", "dst", "ilabel", "arc", "score_bits", "lane", "flags")
 STEP_FIELDS = ("n", "beam", "max", "arcs", "admitted", "distinct", "eps_arcs", "eps_admitted",
                "eps_distinct", "eps_new", "eps_replaced", "eps_passes", "phase", "listed", "_14", "_15")

@@ -816,7 +816,12 @@ static hipError_t enqueue_decode_with(const Work &w, int passes, int steps, Go &
                 if ((e = go(id, 0, 0)) != hipSuccess) return e;
         }
     }
-    if (w.lattice) {
+    if (w.lattice && passes <= 0) {
+        // without a closure every lattice arc is a step arc: work records, one
+        // backward sweep per lane over all its frames, the kept arcs
+        if (steps > 0 && ((e = go(kKLatFPrep, steps, 0)) != hipSuccess || (e = go(kKLatSweep, 0, 0)) != hipSuccess ||
+                          (e = go(kKLatEmit, steps, 0)) != hipSuccess)) return e;
+    } else if (w.lattice) {
         if ((e = go(kKLatInit, 0, 0)) != hipSuccess) return e;
         for (int t = steps - 1; t >= 0; --t) {
             if ((e = go(kKLatBack, t, 0)) != hipSuccess) return e;

@@ -266,7 +266,8 @@ enum : int {
     kKClear = 0, kKInit, kKLpmax, kKMax, kKExpand, kKFinalize, kKEpsExpand, kKEpsResolve,
     kKEpsApply, kKBacktrack, kKStreamBegin, kKStreamEnd, kKReclass, kKLatResolve, kKLatInit,
     kKLatBack, kKGcBegin, kKGcMark, kKGcScan, kKGcCompact, kKGcCommit, kKGcRoots, kKGcClear, kKGcEnd,
-    kKLatEpsBack, kKLatPrune, kKLatEpsRound, kKEpsApplyExpand, kKLatPrep, kKCount
+    kKLatEpsBack, kKLatPrune, kKLatEpsRound, kKEpsApplyExpand, kKLatPrep, kKLatFPrep, kKLatSweep,
+    kKLatEmit, kKCount
 };
 
 // Host-side launchers (wfst_kernels.hip): t = step (-1 before step 0), k = closure pass.

@@ -2044,12 +2044,6 @@ __device__ __forceinline__ void lat_emit(const Work &w, LaneCtl &c, int L, bool 
     for (int f = 0; f < kLatFields; ++f) dst[f] = o[f];
 }
 
-// Frame f's nodes [n0, n1) at -inf.
-__device__ __forceinline__ void sweep_clear(const SweepLane &s, uint32_t n0, uint32_t n1)
-{
-    for (uint32_t i = n0 + threadIdx.x; i < n1; i += kLatSweepBlock) s.bwd[i] = kOrdNegInf;
-}
-
 // Keeps (final pass) or marks (prune) one epsilon record of frame f with
 // weight wt, source node se, the destination's backward score bd; fw = fwd(se),
 // ep = the pass that last relaxed the source (final pass: a record is kept
@@ -2406,6 +2400,9 @@ __global__ __launch_bounds__(kLatPrepBlock) void k_lat_prep(const Work *__restri
 // [po, po + pn) (po == kNoLds: that one is in memory): right after it, else
 // before it, else kNoLds (the frame's scores stay in memory).
 constexpr uint32_t kNoLds = 0xFFFFFFFFu;
+// Pass field of an arc the final pass keeps (it runs only without closure
+// passes, so every other arc still holds pass 0).
+constexpr int32_t kFinalKept = 1;
 __device__ __forceinline__ uint32_t lds_place(uint32_t n, uint32_t po, uint32_t pn)
 {
     if (n > kLatEpsLdsNodes) return kNoLds;
@@ -2415,15 +2412,18 @@ __device__ __forceinline__ uint32_t lds_place(uint32_t n, uint32_t po, uint32_t 
 }
 
 // The prune's backward sweep over frames F - 1 .. W (steps 1-3 above) on the
-// work records; frame F's scores are set, at LDS offset oF (or in memory). Two
+// work records of slots W + 1 .. F (slot F's ending at `cursor`); frame F's
+// scores are set, at LDS offset oF (or in memory). Returns frame W's LDS offset
+// (kNoLds: its scores are in memory). The prune marks the arcs it drops (pass
+// field -1), the final pass (FINAL) the ones it keeps (kFinalKept). Two
 // frames are live at a time, f + 1 (read) and f (raised): each gets a place in
 // the LDS array beside the other (lds_place), or the whole array when it fits
 // alone (the other's scores then move to memory), or stays in memory. Without
 // epsilon arcs the next frame's first batch of work records is loaded as this
 // frame starts; with them, after the frame's fixpoint (whose loads need the
 // registers).
-template <bool EPS>
-__device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const SweepLane &s, SweepShared &sh,
+template <bool EPS, bool FINAL = false>
+__device__ __forceinline__ uint32_t prune_sweep(const Work &w, LaneCtl &c, const SweepLane &s, SweepShared &sh,
                                             const int4 *__restrict__ work, int F, int W, uint32_t nF, uint32_t oF,
                                             uint32_t cursor, int4 (&r)[kLatBatch])
 {
@@ -2487,7 +2487,8 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
                     if (ls) atomicMax(&sh.bwd[os + (uint32_t)r[k].x], f2ord(v));
                     else atomicMax(&s.bwd[ns + (uint32_t)r[k].x], f2ord(v));
                 }
-                if (!(((fw + sa) + bv[k]) >= s.thr)) s.rec[b0 + (uint32_t)k * kLatSweepBlock + tid].w = -1;
+                const bool kept = ((fw + sa) + bv[k]) >= s.thr;
+                if (FINAL ? kept : !kept) s.rec[b0 + (uint32_t)k * kLatSweepBlock + tid].w = FINAL ? kFinalKept : -1;
             }
         }
         if (EPS) {
@@ -2515,6 +2516,7 @@ __device__ __forceinline__ void prune_sweep(const Work &w, LaneCtl &c, const Swe
             __syncthreads();
         }
     }
+    return os;
 }
 
 // Interval prune (page section 7, lat_prune_interval = N: a window-loose prune
@@ -2616,6 +2618,197 @@ __global__ __launch_bounds__(kLatSweepBlock) void k_lat_prune(const Work *__rest
     for (int sl = 1 + (int)tid; sl < nslot; sl += kLatSweepBlock)
         if (sh.off0[sl] >= cursor) aoff[W + sl] = out;
     if (tid == 0) c.lat_cursor = out;
+}
+
+// Final pass on a graph without closure passes, as three launches instead of
+// one per frame: every persisted arc is a step arc, so the backward scores
+// follow from one sweep over the frames per lane (the interval prune's sweep,
+// prune_sweep, over the whole lattice), fed by work records a flat kernel
+// makes first, and a flat kernel then writes the kept arcs out. The arcs kept,
+// their fields and their scores are those of k_lat_back.
+
+// A lane that gets the final pass: it has a result, every arc it persisted was
+// written, and it ran a step.
+__device__ __forceinline__ bool lat_final_lane(const Work &w, const LaneCtl &c)
+{
+    return lane_has_result(c) && lat_complete(w, c) && c.last_step >= 0;
+}
+
+// Records of step ts of lane L: [a0, a1) of its lattice arcs; fin: ts is the
+// lane's final step (its arcs are final arcs, or the redirect).
+struct FinalStep {
+    uint32_t a0, a1, ns;   // ns: first node of frame ts (the sources)
+    bool fin;
+};
+
+__device__ __forceinline__ FinalStep final_step(const Work &w, const LaneCtl &c, int L, int ts)
+{
+    const size_t FF = (size_t)w.max_frames + 3;
+    const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+    const bool fin = ts == c.last_step;
+    return FinalStep{aoff[ts + 1], min(fin ? c.lat_cursor : aoff[ts + 2], w.lat_cap),
+                     w.lat_nbase[(size_t)L * FF + (size_t)ts], fin};
+}
+
+// s of an arc of step ts as the backward pass adds it: weight + log-prob of
+// frame ts; on the final step the final arc's weight, 0 for the redirect.
+template <typename LPT>
+__device__ __forceinline__ float final_arc_score(bool fin, bool redirect, const ArcDLW &ad, const LPT *row)
+{
+    if (fin) return redirect ? 0.0f : ad.weight;
+    return ad.weight + lp_at(row, ad.ilabel);
+}
+
+// Work records of the final pass (blockIdx.y = lane, blockIdx.x = step ts):
+// for each arc of step ts, {source position, destination position, s, fwd of
+// the source}; the final step's arcs (and the redirect) all lead to the
+// super-final node (position 0, unused).
+template <typename LPT>
+__global__ __launch_bounds__(kLatPrepBlock) void k_lat_fprep(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.y;
+    if (L >= w.max_lanes) return;
+    const LaneCtl &c = w.ctl[L];
+    const int ts = (int)blockIdx.x;
+    if (!lat_final_lane(w, c) || ts > c.last_step) return;
+    const FinalStep st = final_step(w, c, L, ts);
+    const LpDesc d = *w.lp;
+    const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)ts * d.stride_t;
+    const int4 *rec = w.lat_arc + (size_t)L * w.lat_cap;
+    const float *fwd = w.lat_score + (size_t)L * w.lat_nodes;
+    int4 *work = lat_work(w, L);
+    constexpr uint32_t kStride = (uint32_t)kLatPrepRecs * kLatPrepBlock;
+    for (uint32_t b0 = st.a0; b0 < st.a1; b0 += kStride) {
+        int4 r[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatPrepBlock + threadIdx.x;
+            r[k] = i < st.a1 ? rec[i] : make_int4(0, 0, 0, 1);
+        }
+        ArcDLW ad[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k)
+            ad[k] = (r[k].w == 0 && (uint32_t)r[k].y < (uint32_t)w.num_arcs) ? w.arc_dlw[r[k].y] : ArcDLW{0, 0u, 0.0f};
+        int4 o[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            o[k] = make_int4(0, -1, 0, 0);
+            if (r[k].w != 0) continue;
+            const bool redirect = (uint32_t)r[k].y >= (uint32_t)w.num_arcs;
+            const float sa = final_arc_score(st.fin, redirect, ad[k], row);
+            o[k] = make_int4(r[k].x, st.fin ? 0 : r[k].z, (int)__float_as_uint(sa),
+                             (int)__float_as_uint(fwd[st.ns + (uint32_t)r[k].x]));
+        }
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatPrepBlock + threadIdx.x;
+            if (i < st.a1) work[i] = o[k];
+        }
+    }
+}
+
+// The final pass's backward sweep, one workgroup per lane (after k_lat_fprep),
+// with the keep threshold final_score - output_beam: the final step's arcs set
+// the scores of frame last_step (bwd(u) = the best s of u's final arcs; their
+// destination, the super-final node, scores 0), then prune_sweep walks frames
+// last_step - 1 .. 0; every arc kept is marked (kFinalKept). Frames go
+// in windows of at most 2 * kMaxPruneInterval (the workgroup's table of step
+// offsets and first nodes), each starting from the scores the window above
+// left (in LDS or in memory).
+__global__ __launch_bounds__(kLatSweepBlock) void k_lat_fsweep(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.x;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    if (!lat_final_lane(w, c)) return;
+    __shared__ SweepShared sh;
+    const size_t FF = (size_t)w.max_frames + 3;
+    const uint32_t *aoff = w.lat_aoff + (size_t)L * FF;
+    const uint32_t *nbase = w.lat_nbase + (size_t)L * FF;
+    const SweepLane s = sweep_lane(w, L, c.final_score - w.output_beam);
+    const int4 *work = lat_work(w, L);
+    const uint32_t tid = threadIdx.x;
+    int F = c.last_step;
+    const FinalStep st = final_step(w, c, L, F);
+    const uint32_t nF = nbase[F + 1] - st.ns, oF = lds_place(nF, kNoLds, 0u);
+    uint32_t *bf = oF != kNoLds ? sh.bwd + oF : s.bwd + st.ns;
+    for (uint32_t i = tid; i < nF; i += kLatSweepBlock) bf[i] = kOrdNegInf;
+    __syncthreads();
+    for (uint32_t i = st.a0 + tid; i < st.a1; i += kLatSweepBlock) {
+        const int4 r = work[i];
+        if (r.y == -1) continue;
+        const float sa = __int_as_float(r.z), fw = __int_as_float(r.w);
+        const float v = sa + 0.0f;
+        if (v > -__builtin_inff()) atomicMax(&bf[(uint32_t)r.x], f2ord(v));
+        if (((fw + sa) + 0.0f) >= s.thr) s.rec[i].w = kFinalKept;
+    }
+    uint32_t o = oF, end = st.a0;
+    while (F > 0) {
+        const int W = max(0, F - 2 * kMaxPruneInterval);
+        __syncthreads();   // (frame F's scores; the window above no longer reads the table)
+        for (int i = (int)tid; i <= F - W; i += kLatSweepBlock) {
+            sh.off0[i] = aoff[W + i];
+            sh.nb0[i] = nbase[W + i];
+        }
+        __syncthreads();
+        const uint32_t n = nbase[F + 1] - nbase[F];
+        int4 r[kLatBatch];
+        o = prune_sweep<false, true>(w, c, s, sh, work, F, W, n, o, end, r);
+        end = sh.off0[1];
+        F = W;
+    }
+}
+
+// The final pass's output (after k_lat_fsweep): every arc of step ts
+// (blockIdx.x) of lane blockIdx.y that the sweep kept, written as k_lat_back
+// writes it.
+template <typename LPT>
+__global__ __launch_bounds__(kLatPrepBlock) void k_lat_femit(const Work *__restrict__ wp)
+{
+    const Work &w = *wp;
+    const int L = (int)blockIdx.y;
+    if (L >= w.max_lanes) return;
+    LaneCtl &c = w.ctl[L];
+    const int ts = (int)blockIdx.x;
+    if (!lat_final_lane(w, c) || ts > c.last_step) return;
+    const FinalStep st = final_step(w, c, L, ts);
+    const LpDesc d = *w.lp;
+    const LPT *row = (const LPT *)d.base + (long long)c.lp_row * d.stride_b + (long long)ts * d.stride_t;
+    const int4 *rec = w.lat_arc + (size_t)L * w.lat_cap;
+    const int32_t *state = w.lat_state + (size_t)L * w.lat_nodes;
+    constexpr uint32_t kStride = (uint32_t)kLatPrepRecs * kLatPrepBlock;
+    // (the block's loop count is uniform: every wavefront takes part in each
+    // lat_emit)
+    for (uint32_t b0 = st.a0; b0 < st.a1; b0 += kStride) {
+        int4 r[kLatPrepRecs];
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const uint32_t i = b0 + (uint32_t)k * kLatPrepBlock + threadIdx.x;
+            r[k] = i < st.a1 ? rec[i] : make_int4(0, 0, 0, -1);
+        }
+#pragma unroll
+        for (int k = 0; k < kLatPrepRecs; ++k) {
+            const bool keep = r[k].w == kFinalKept;
+            int32_t o[kLatFields];
+            if (keep) {
+                const int32_t arc = r[k].y;
+                const bool redirect = (uint32_t)arc >= (uint32_t)w.num_arcs;
+                ArcDLW ad = {0, 0u, 0.0f};
+                if (!redirect) ad = w.arc_dlw[arc];
+                o[kLatFrame] = ts;
+                o[kLatSrc] = state[st.ns + (uint32_t)r[k].x];
+                o[kLatDst] = (redirect || st.fin) ? w.super_final : (int32_t)dest_state(w, ad.dest);
+                o[kLatIlabel] = st.fin ? -1 : (int32_t)ad.ilabel;
+                o[kLatArc] = arc;
+                o[kLatScore] = (int32_t)__float_as_uint(final_arc_score(st.fin, redirect, ad, row));
+                o[kLatLane] = L;
+                o[kLatFlags] = redirect ? 2 : (st.fin ? 1 : 0);
+            }
+            lat_emit(w, c, L, keep, o);
+        }
+    }
 }
 
 // ---------------------------------------------------------- stream sequences
@@ -3331,6 +3524,17 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
     case kKLatPrune:
         if (w.lat_prune_interval < 1 || w.lat_prune_interval > kMaxPruneInterval) return hipErrorInvalidValue;
         go(k_lat_prune, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw, t);
+        break;
+    case kKLatFPrep:   // t: the decode's steps
+        if (t < 1 || t > w.max_frames + 1) return hipErrorInvalidValue;
+        if (f16) go(k_lat_fprep<__half>, dim3(t, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw);
+        else go(k_lat_fprep<float>, dim3(t, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw);
+        break;
+    case kKLatSweep: go(k_lat_fsweep, dim3(w.max_lanes), dim3(kLatSweepBlock), s, e0, e1, dw); break;
+    case kKLatEmit:
+        if (t < 1 || t > w.max_frames + 1) return hipErrorInvalidValue;
+        if (f16) go(k_lat_femit<__half>, dim3(t, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw);
+        else go(k_lat_femit<float>, dim3(t, w.max_lanes), dim3(kLatPrepBlock), s, e0, e1, dw);
         break;
     default: return hipErrorInvalidValue;
     }
