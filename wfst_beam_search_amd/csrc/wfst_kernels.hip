@@ -1209,6 +1209,33 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     wave_share(total, &u_beg, &u_end);
     int lb_lane = -1, lb_np = 0;
     float lb_acc = -__builtin_inff();
+    // lattice mode: the step before's unresolved arcs (its recombination losers
+    // and its closure's epsilon arcs) get their destination's position among
+    // the tokens of frame t (the parity this compaction reads). The wavefront's
+    // first unit of them is read, and its position gathers issued, before the
+    // compaction's own loads; the positions are written after them.
+    uint32_t v_beg = 0, v_end = 0;
+    int mL = -1;
+    uint32_t mi = 0;
+    int4 mr = make_int4(0, 0, 0, 0);
+    int32_t mpos = 0;
+    bool mpend = false, mun = false;
+    if (w.lattice) {
+        wave_share(lt.base[nl], &v_beg, &v_end);
+        if (v_beg < v_end) {
+            mL = find_lane(lt.base, nl, v_beg);
+            mi = (v_beg - lt.base[mL]) * kWave + (uint32_t)lane;
+            if (mi < lt.n[mL]) mr = w.lat_arc[(size_t)mL * w.lat_cap + lt.a0[mL] + mi];
+            mpend = true;
+        }
+    }
+    if (mpend) {
+        const uint32_t d = (uint32_t)mr.z;
+        if (mi < lt.n[mL] && (d & kLatUnresolved) && (d & ~kLatUnresolved) < (uint32_t)w.num_states) {
+            mun = true;
+            mpos = pick(w.pos, upar(tab.par, mL))[(size_t)mL * w.num_states + (d & ~kLatUnresolved)];
+        }
+    }
     for (uint32_t u = u_beg; u < u_end; ++u) {
         const int L = find_lane(tab.base, nl, u);
         const int p = upar(tab.par, L), np = p ^ 1;
@@ -1395,12 +1422,9 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     }
     post_bound(w, lb_lane, lb_np, lb_acc);
     if (w.lattice) {
-        // the step before's unresolved lattice arcs (its recombination losers and
-        // its closure's epsilon arcs): destination state -> position among the
-        // tokens of frame t (the parity this compaction reads)
-        uint32_t v_beg, v_end;
-        wave_share(lt.base[nl], &v_beg, &v_end);
-        for (uint32_t u = v_beg; u < v_end; ++u) {
+        if (mun) w.lat_arc[(size_t)mL * w.lat_cap + lt.a0[mL] + mi].z = mpos;
+        // (the wavefront's other units, if any)
+        for (uint32_t u = v_beg + 1; u < v_end; ++u) {
             const int L = find_lane(lt.base, nl, u);
             const int p = upar(tab.par, L);
             const uint32_t i = (u - lt.base[L]) * kWave + (uint32_t)lane;
