@@ -223,6 +223,7 @@ struct wfst_graph_s {
     std::atomic<int> refs{1};
     int device = 0;
     int32_t num_states = 0, num_arcs = 0, start = 0, vocab = 0, eps_id = -1;
+    int32_t num_records = 0;      // arc records on the device, padding included
     uint32_t max_class_deg = 0;   // most arcs of one class leaving one state
     uint32_t dest_bits = 0;       // arc records hold the in-rank above this many state id bits (0: no ranks)
     uint32_t rank_bits = 0;       // bits of the largest in-rank
@@ -231,7 +232,7 @@ struct wfst_graph_s {
     size_t bytes = 0;
     StateInfo *sinfo = nullptr;
     ArcDLW *arc_dlw = nullptr;
-    int32_t *olabel = nullptr, *arc_src = nullptr;
+    int32_t *olabel = nullptr, *arc_uid = nullptr;
 
     ~wfst_graph_s()
     {
@@ -402,11 +403,34 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
 
     const int32_t S = g->num_states, A = g->num_arcs;
     // interleaved arc records in CSR order (section 4's split, regrouped so that
-    // the fields a pass reads for one arc share a cache line)
-    std::vector<int32_t> src((size_t)A);
-    std::vector<ArcDLW> dlw((size_t)A);
-    for (int32_t s = 0; s < S; ++s)
-        for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) src[(size_t)a] = s;
+    // the fields a pass reads for one arc share a cache line). State s's run
+    // starts k <= 31 records after the one before ends, k the least that puts
+    // its emitting arcs on the fewest 128-byte lines (12-byte records: a run
+    // can start at a line's start only every 32 records); without such a k, or
+    // if the records would pass 2^31 - 1, k = 0.
+    std::vector<int64_t> first((size_t)S + 1);
+    auto lay = [&](bool pad) {
+        int64_t p = 0;
+        for (int32_t s = 0; s < S; ++s) {
+            const StateInfo &si = info[(size_t)s];
+            const int64_t ne = si.emit_b - si.eps_b, n = si.fin_b - si.emit_b;
+            int k = 0;
+            if (pad && n > 0) {
+                const int64_t need = (12 * n + 127) / 128 * 128;
+                while (k < 32 && (12 * (p + k + ne)) % 128 + 12 * n > need) ++k;
+                if (k == 32) k = 0;
+            }
+            first[(size_t)s] = p + k;
+            p += k + (si.end - si.eps_b);
+        }
+        first[(size_t)S] = p;
+        return p;
+    };
+    if (lay(true) >= INT32_MAX) lay(false);
+    const int32_t R = (int32_t)first[(size_t)S];
+    auto pos_of = [&](int32_t s, int32_t a) -> int32_t { return (int32_t)(first[(size_t)s] + (a - g->row_splits[s])); };
+    std::vector<ArcDLW> dlw((size_t)R, ArcDLW{0, 0u, 0.0f});
+    std::vector<int32_t> ol((size_t)R, 0), uid((size_t)R, -1);
     // each non-final arc's rank among its destination's incoming non-final arcs,
     // in arc id order: a table key may break ties by it instead of the arc id
     // (same order among one destination's candidates, far fewer bits), stored
@@ -425,16 +449,26 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
     while ((1ull << db) < (unsigned long long)S) ++db;
     while ((1ull << rb) <= (unsigned long long)max_rank) ++rb;
     const bool ranks = db + rb <= 31;
-    for (int32_t a = 0; a < A; ++a) {
-        const uint32_t il = g->ilabel[a] == -1 ? (uint32_t)kFinalLabel : (uint32_t)g->ilabel[a];
-        const uint32_t dfield = (uint32_t)g->dest[a] | (ranks ? rank[(size_t)a] << db : 0u);
-        dlw[(size_t)a] = ArcDLW{(int32_t)dfield, il, g->weight[a]};
+    for (int32_t s = 0; s < S; ++s) {
+        for (int32_t a = g->row_splits[s]; a < g->row_splits[s + 1]; ++a) {
+            const uint32_t il = g->ilabel[a] == -1 ? (uint32_t)kFinalLabel : (uint32_t)g->ilabel[a];
+            const uint32_t dfield = (uint32_t)g->dest[a] | (ranks ? rank[(size_t)a] << db : 0u);
+            const int32_t q = pos_of(s, a);
+            dlw[(size_t)q] = ArcDLW{(int32_t)dfield, il, g->weight[a]};
+            ol[(size_t)q] = g->olabel[a];
+            uid[(size_t)q] = a;
+        }
+        // the state's class ranges, as record positions
+        StateInfo &si = info[(size_t)s];
+        const int32_t d = (int32_t)(first[(size_t)s] - g->row_splits[s]);
+        si.eps_b += d; si.emit_b += d; si.fin_b += d; si.end += d;
     }
 
     wfst_graph_s *h = new wfst_graph_s();
     h->device = device;
     h->num_states = S;
     h->num_arcs = A;
+    h->num_records = R;
     h->start = g->start_state;
     h->vocab = g->vocab_size;
     h->eps_id = g->epsilon_id;
@@ -446,18 +480,18 @@ extern "C" int wfst_graph_upload(const wfst_graph_desc *g, int device, wfst_grap
             if (g->ilabel[a] == g->epsilon_id && g->weight[a] > 0.0f) { h->eps_positive = true; break; }
     int r = WFST_OK;
     if ((r = dalloc(&h->sinfo, (size_t)S, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->arc_dlw, (size_t)A, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->olabel, (size_t)A, &h->owned, &h->bytes)) ||
-        (r = dalloc(&h->arc_src, (size_t)A, &h->owned, &h->bytes))) {
+        (r = dalloc(&h->arc_dlw, (size_t)R, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->olabel, (size_t)R, &h->owned, &h->bytes)) ||
+        (r = dalloc(&h->arc_uid, (size_t)R, &h->owned, &h->bytes))) {
         delete h;
         return r;
     }
     hipError_t e = hipSuccess;
     if (e == hipSuccess) e = hipMemcpy(h->sinfo, info.data(), sizeof(StateInfo) * (size_t)S, hipMemcpyHostToDevice);
-    if (A > 0) {
-        if (e == hipSuccess) e = hipMemcpy(h->arc_dlw, dlw.data(), sizeof(ArcDLW) * (size_t)A, hipMemcpyHostToDevice);
-        if (e == hipSuccess) e = hipMemcpy(h->olabel, g->olabel, 4 * (size_t)A, hipMemcpyHostToDevice);
-        if (e == hipSuccess) e = hipMemcpy(h->arc_src, src.data(), 4 * (size_t)A, hipMemcpyHostToDevice);
+    if (R > 0) {
+        if (e == hipSuccess) e = hipMemcpy(h->arc_dlw, dlw.data(), sizeof(ArcDLW) * (size_t)R, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->olabel, ol.data(), 4 * (size_t)R, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemcpy(h->arc_uid, uid.data(), 4 * (size_t)R, hipMemcpyHostToDevice);
     }
     if (e != hipSuccess) {
         delete h;
@@ -549,11 +583,12 @@ static int init_work(Work &w, const wfst_graph_s *g, const wfst_decoder_config &
 {
     w = Work{};
     w.sinfo = g->sinfo; w.arc_dlw = g->arc_dlw;
-    w.olabel = g->olabel; w.arc_src = g->arc_src;
-    w.num_states = g->num_states; w.num_arcs = g->num_arcs; w.start_state = g->start;
+    w.olabel = g->olabel; w.arc_uid = g->arc_uid;
+    w.num_states = g->num_states; w.num_arcs = g->num_records; w.num_arcs_user = g->num_arcs;
+    w.start_state = g->start;
     w.vocab = g->vocab; w.super_final = g->num_states - 1; w.has_eps = g->eps_id >= 0;
     uint32_t ab = 1;
-    while (ab < 31 && (1ll << ab) < (long long)g->num_arcs) ++ab;
+    while (ab < 31 && (1ll << ab) < (long long)g->num_records) ++ab;
     const bool ranks = g->dest_bits > 0 && c.plain_keys == 0;
     const uint32_t tb = ranks ? g->rank_bits : ab;
     w.tie_bits = tb;

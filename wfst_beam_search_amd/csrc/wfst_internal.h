@@ -53,7 +53,12 @@ static_assert(sizeof(StateInfo) == 64, "one state record is one 64-byte line");
 
 // Arc records {dest, ilabel, weight}, one contiguous run per state (the CSR
 // order of the graph), so the fields a pass reads for a token's arcs share
-// cache lines. Final arcs carry kFinalLabel. When the graph stores ranks, dest
+// cache lines; each state's run starts after up to 31 padding records, placed
+// so that its emitting arcs span the fewest 128-byte lines. On the device an
+// arc is named by its record's position, which grows with the graph's arc id
+// (a tie between arcs resolves the same on either); results and lattice
+// records carry the graph's ids (Work::arc_uid). Final arcs carry kFinalLabel.
+// When the graph stores ranks, dest
 // holds the arc's rank among its destination's incoming non-final arcs (in arc
 // id order) above the state id's bits (Work::dest_bits).
 struct ArcDLW {
@@ -155,9 +160,10 @@ struct Work {
     // graph (read-only)
     const StateInfo *sinfo;
     const ArcDLW *arc_dlw;
-    const int32_t *olabel;
-    const int32_t *arc_src;
-    int32_t num_states, num_arcs, start_state, vocab, super_final;
+    const int32_t *olabel;        // by record position
+    const int32_t *arc_uid;       // record position -> the graph's arc id (-1: padding)
+    int32_t num_states, num_arcs, start_state, vocab, super_final;   // num_arcs: records, padding included
+    int32_t num_arcs_user;        // the graph's arcs
     int32_t has_eps;
     int32_t epochs;           // table keys carry the round's epoch: entries are never cleared singly
     uint32_t tie_bits;        // tie bits of an epoch-tagged key (the epoch takes 32 - tie_bits)

@@ -73,6 +73,14 @@ __device__ __forceinline__ uint32_t round_epoch(const Work &w, int t, int k)
 // rank among its destination's incoming arcs, counted in arc id order.
 __device__ __forceinline__ uint32_t dest_state(const Work &w, int32_t d) { return (uint32_t)d & w.dest_mask; }
 
+// The graph's id of the arc at record position a; a redirect's virtual arc
+// (num_arcs + state) keeps its offset past the graph's arcs.
+__device__ __forceinline__ int32_t user_arc(const Work &w, int32_t a)
+{
+    if (a < 0) return a;
+    return a < w.num_arcs ? w.arc_uid[a] : w.num_arcs_user + (a - w.num_arcs);
+}
+
 // Key of a candidate (arc, packed destination field pd) in the recombination
 // table. With epochs: epoch << (32 + a) | ordered score << a | (2^a - 1 - tie),
 // a = tie_bits <= 25, where the tie is the arc's rank among its destination's
@@ -1962,7 +1970,7 @@ __global__ __launch_bounds__(kBlock) void k_lat_back(const Work *__restrict__ wp
                 rec[kLatSrc] = w.lat_state[(size_t)L * w.lat_nodes + se];
                 rec[kLatDst] = (redirect || fin) ? w.super_final : (int32_t)dest_state(w, ad.dest);
                 rec[kLatIlabel] = fin ? -1 : (int32_t)ad.ilabel;
-                rec[kLatArc] = arc;
+                rec[kLatArc] = user_arc(w, arc);
                 rec[kLatScore] = (int32_t)__float_as_uint(sa);
                 rec[kLatLane] = L;
                 rec[kLatFlags] = redirect ? 2 : (fin ? 1 : 0);
@@ -2090,7 +2098,7 @@ __device__ __forceinline__ void eps_keep(const Work &w, LaneCtl &c, const SweepL
         o[kLatSrc] = s.state[se];
         o[kLatDst] = (int32_t)dest_state(w, ad.dest);
         o[kLatIlabel] = (int32_t)ad.ilabel;
-        o[kLatArc] = r.y;
+        o[kLatArc] = user_arc(w, r.y);
         o[kLatScore] = (int32_t)__float_as_uint(wt);
         o[kLatLane] = s.L;
         o[kLatFlags] = 4;
@@ -2825,7 +2833,7 @@ __global__ __launch_bounds__(kLatPrepBlock) void k_lat_femit(const Work *__restr
                 o[kLatSrc] = state[st.ns + (uint32_t)r[k].x];
                 o[kLatDst] = (redirect || st.fin) ? w.super_final : (int32_t)dest_state(w, ad.dest);
                 o[kLatIlabel] = st.fin ? -1 : (int32_t)ad.ilabel;
-                o[kLatArc] = arc;
+                o[kLatArc] = user_arc(w, arc);
                 o[kLatScore] = (int32_t)__float_as_uint(final_arc_score(st.fin, redirect, ad, row));
                 o[kLatLane] = L;
                 o[kLatFlags] = redirect ? 2 : (st.fin ? 1 : 0);
@@ -3044,7 +3052,10 @@ __global__ __launch_bounds__(kWave) void k_backtrack(const Work *__restrict__ wp
     for (uint32_t i0 = 0; i0 < ns; i0 += kWave) {
         const uint32_t i = i0 + (uint32_t)lane;
         int32_t ol = 0;
-        if (i < ns) ol = w.olabel[arcs[i]];
+        if (i < ns) {
+            ol = w.olabel[arcs[i]];
+            arcs[i] = user_arc(w, arcs[i]);   // (the graph's arc ids in the result)
+        }
         const unsigned long long m = __ballot(ol != 0);
         if (ol != 0) words[nw + (uint32_t)__popcll(m & mask_lt())] = ol;
         nw += (uint32_t)__popcll(m);
