@@ -120,8 +120,10 @@ typedef struct wfst_graph_desc {
  *                  cleared one by one. The tie part is the arc's rank among its
  *                  destination's incoming arcs (ordered as the arc ids are)
  *                  when the graph upload could store the ranks (state id bits +
- *                  rank bits <= 31), else the arc id (graphs of at most 2^25
- *                  arcs). Rounds are numbered on across decodes and stream
+ *                  rank bits <= 31), else the arc's record position on the
+ *                  device (graphs of at most 2^25 arc records: the arcs and up
+ *                  to 31 padding records per state, which order arcs as their
+ *                  ids do). Rounds are numbered on across decodes and stream
  *                  calls, and the table is wiped before the first round past
  *                  each multiple of the epoch period (epoch_period).
  *                  2: the same with arc id ties. 1: plain keys, each entry
