@@ -61,7 +61,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
     The path figure is their sum. ``design`` counts what this implementation's
     own choices add on top (the 16-byte candidate record written by the slot
     pass for every listed candidate and read back by the compaction, the
-    compaction's 64-byte state record per new token, the 16-byte token record
+    compaction's 128-byte state record per new token, the 16-byte token record
     the slot pass reads): reported beside the method's bytes, never in them.
     """
     n, S, C, D, F = st["tokens"], st["arcs"], st["admitted"], st["distinct"], st["lane_frames"]
@@ -75,7 +75,7 @@ def algorithmic_bytes(st, elem_bytes, vocab):
         "closure": 8 * E + 12 * Ce + 28 * De + 20 * Ne,
     }
     path = sum(per.values())
-    design = {"candidate_records": 32 * st["listed"], "state_records": 64 * D, "token_records": 16 * n}
+    design = {"candidate_records": 32 * st["listed"], "state_records": 128 * D, "token_records": 16 * n}
     return per, path, design
 
 

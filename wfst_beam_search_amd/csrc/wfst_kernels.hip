@@ -1071,6 +1071,28 @@ __global__ __launch_bounds__(kBlock) void k_max(const Work *__restrict__ wp, int
 
 // -------------------------------------------------------------- k_finalize
 
+// The best next-step candidate through the state's kTopArcs largest-weight
+// emitting arcs, (score + weight) + lp as the maximum pass adds them (unused
+// entries weigh -inf); row = element offset of the next frame's log-prob row.
+__device__ __forceinline__ float top_bound(const Work &w, const LpDesc &lpd, const StateInfo &si, float end,
+                                           long long row)
+{
+    float lpk[kTopArcs];
+    if (w.lp_dtype == 1) {
+        const __half *r = (const __half *)lpd.base + row;
+#pragma unroll
+        for (int k = 0; k < kTopArcs; ++k) lpk[k] = __half2float(r[si.top_il[k]]);
+    } else {
+        const float *r = (const float *)lpd.base + row;
+#pragma unroll
+        for (int k = 0; k < kTopArcs; ++k) lpk[k] = r[si.top_il[k]];
+    }
+    float lbv = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < kTopArcs; ++k) lbv = fmaxf(lbv, (end + si.top_w[k]) + lpk[k]);
+    return lbv;
+}
+
 // Posts a wavefront's lower bound of lane L's next-step maximum (L < 0: none).
 __device__ __forceinline__ void post_bound(const Work &w, int L, int np, float v)
 {
@@ -1325,19 +1347,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                         // candidates of the next step through the state's
                         // largest-weight arcs, (score + weight) + lp as the
                         // maximum pass adds them (unused entries weigh -inf)
-                        const long long row = (long long)tab.row[L] * lpd.stride_b + (long long)(t + 1) * lpd.stride_t;
-                        float lpk[kTopArcs];
-                        if (w.lp_dtype == 1) {
-                            const __half *r = (const __half *)lpd.base + row;
-#pragma unroll
-                            for (int k = 0; k < kTopArcs; ++k) lpk[k] = __half2float(r[si.top_il[k]]);
-                        } else {
-                            const float *r = (const float *)lpd.base + row;
-#pragma unroll
-                            for (int k = 0; k < kTopArcs; ++k) lpk[k] = r[si.top_il[k]];
-                        }
-#pragma unroll
-                        for (int k = 0; k < kTopArcs; ++k) lbv = fmaxf(lbv, (end + si.top_w[k]) + lpk[k]);
+                        lbv = top_bound(w, lpd, si, end, (long long)tab.row[L] * lpd.stride_b + (long long)(t + 1) * lpd.stride_t);
                         // the token's bound for the next step: its exact best candidate
                         // when these arcs are all it has, else (score + largest weight)
                         // + the frame's largest log-prob
