@@ -852,10 +852,62 @@ __device__ __forceinline__ void wave_share(uint32_t total, uint32_t *s, uint32_t
     *s_end = (uint32_t)(((unsigned long long)total * (wid + 1)) / nwaves);
 }
 
+// The end of the walk for the whole workgroup: each wavefront's last lane
+// segment (lane L, n buffered candidates, running max run; L < 0: none) is
+// posted with one list allocation and one maximum atomic per lane of the
+// workgroup instead of one per wavefront, then every wavefront copies its
+// buffer to its part of the allocation.
+__device__ __forceinline__ void wg_post(const Work &w, const LaneTab &tab, int L, float run, uint32_t n,
+                                        ClaimBuf *cb)
+{
+    constexpr int kW = kBlock / kWave;
+    __shared__ int32_t agL[kW];
+    __shared__ uint32_t agN[kW], agB[kW];
+    __shared__ float agR[kW];
+    const int wv = (int)(threadIdx.x / kWave);
+    if (wlane() == 0) { agL[wv] = L; agN[wv] = n; agR[wv] = run; }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)kW) {
+        const int i = (int)threadIdx.x;
+        const int Li = agL[i];
+        bool first = Li >= 0;
+        for (int j = 0; j < i; ++j) first = first && agL[j] != Li;
+        if (first) {
+            uint32_t tot = 0;
+            float r = -__builtin_inff();
+            for (int j = i; j < kW; ++j)
+                if (agL[j] == Li) { tot += agN[j]; r = fmaxf(r, agR[j]); }
+            const int p = tab.par[Li];
+            LaneCtl &c = w.ctl[Li];
+            uint32_t base = tot ? atomicAdd(&c.nclaims[p], tot) : 0u;
+            if (r > -__builtin_inff()) atomicMax(&c.maxkey[p], f2ord(r));
+            for (int j = i; j < kW; ++j)
+                if (agL[j] == Li) { agB[j] = base; base += agN[j]; }
+        }
+    }
+    __syncthreads();
+    if (L >= 0 && n) {
+        const uint32_t base = agB[wv];
+        Claim *dst = w.claims + tab_row(w, 0, L) * w.claims_cap;
+        for (uint32_t i = (uint32_t)wlane(); i < n; i += kWave) {
+            Claim c;
+            c.dest = cb->dest[i];
+            c.arc = cb->arc[i];
+            c.tok = cb->tok[i];
+            c.score = cb->score[i];
+            if (base + i < w.claims_cap) dst[base + i] = c;
+        }
+    }
+}
+
 // Units [s, s_end) of the flattened slot space, in one pass: the exact maximum
 // (running max seeded with the lower bound the compaction posted, tokens whose
 // bound ub <= running max - b skipped: exact for both results) and the
-// superset admission against running max - b.
+// superset admission against running max - b. Every thread of the workgroup
+// calls it (the last segments are posted together, behind a barrier): per-lane
+// counters that every wavefront hit with its own atomic serialize at the
+// memory side (about 12 ns each on one address), so a lane's list allocation
+// and maximum take one atomic per workgroup instead.
 template <typename LPT, bool HASH>
 __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, int t, const LpDesc &d,
                                            uint32_t s, uint32_t s_end, ClaimBuf *cbuf)
@@ -863,6 +915,8 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
     const int nl = w.max_lanes;
     const uint32_t ep = round_epoch(w, t, 0);
     uint32_t cb_n = 0;
+    int lastL = -1;
+    float lastRun = -__builtin_inff();
     while (s < s_end) {
         const int L = find_lane(tab.base, nl, s);
         const int p = upar(tab.par, L);
@@ -879,10 +933,13 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
             run = fmaxf(run, unit_max(ud));
             admit_unit<HASH>(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
         }
+        // (the wavefront's last segment is posted by the whole workgroup)
+        if (s >= s_end) { lastL = L; lastRun = run; break; }
         if (cb_n) flush_claims(w, 0, L, &c.nclaims[p], *cbuf, cb_n);
         cb_n = 0;
         if (run > -__builtin_inff() && wlane() == 0) atomicMax(&c.maxkey[p], f2ord(run));
     }
+    wg_post(w, tab, lastL, lastRun, cb_n, cbuf);
 }
 
 template <typename LPT, bool HASH>
