@@ -900,6 +900,16 @@ __device__ __forceinline__ void wg_post(const Work &w, const LaneTab &tab, int L
     }
 }
 
+// The workgroup's contiguous share [s, s_end) of `total` units: the union of
+// its wavefronts' wave_share runs.
+__device__ __forceinline__ void wg_share(uint32_t total, uint32_t *s, uint32_t *s_end)
+{
+    const uint32_t wpb = kBlock / kWave;
+    const unsigned long long nwaves = (unsigned long long)gridDim.x * wpb;
+    *s = (uint32_t)(((unsigned long long)total * (vblock() * wpb)) / nwaves);
+    *s_end = (uint32_t)(((unsigned long long)total * (vblock() * wpb + wpb)) / nwaves);
+}
+
 // Units [s, s_end) of the flattened slot space, in one pass: the exact maximum
 // (running max seeded with the lower bound the compaction posted, tokens whose
 // bound ub <= running max - b skipped: exact for both results) and the
@@ -1150,13 +1160,6 @@ __device__ __forceinline__ float top_bound(const Work &w, const LpDesc &lpd, con
     return lbv;
 }
 
-// Posts a wavefront's lower bound of lane L's next-step maximum (L < 0: none).
-__device__ __forceinline__ void post_bound(const Work &w, int L, int np, float v)
-{
-    const float m = wave_max(v);
-    if (L >= 0 && wlane() == 0 && m > -__builtin_inff()) atomicMax(&w.ctl[L].lbkey[np], f2ord(m));
-}
-
 // Result of the final step: the winners-log entry of the best final arc (key
 // fk, source token stok of frontier parity p). Written by exactly one thread.
 __device__ __forceinline__ void final_entry(const Work &w, LaneCtl &c, int L, int p,
@@ -1292,10 +1295,23 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     const uint32_t total = tab.base[nl];
     const int lane = wlane();
     const uint32_t Q = w.frontier_cap;
-    uint32_t u_beg, u_end;
-    wave_share(total, &u_beg, &u_end);
-    int lb_lane = -1, lb_np = 0;
-    float lb_acc = -__builtin_inff();
+    // the workgroup's units, dealt round-robin to its wavefronts so that every
+    // wavefront takes the same rounds: a round's lane counters (positions and
+    // slot offsets, closure sources, admitted count, lower bound of the next
+    // maximum) take one atomic per lane of the round instead of one per
+    // wavefront (same-address atomics serialize at the memory side)
+    constexpr int kW = kBlock / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    uint32_t g_beg, g_end;
+    wg_share(total, &g_beg, &g_end);
+    // (bounds, wavefront index and allocated bases as scalars: the loop holds
+    // barriers, so the compiler must see it as uniform)
+    g_beg = __builtin_amdgcn_readfirstlane(g_beg);
+    g_end = __builtin_amdgcn_readfirstlane(g_end);
+    __shared__ int32_t agL[kW];
+    __shared__ uint32_t agA[kW], agN[kW], agD[kW], agE[kW], agPE[kW];
+    __shared__ unsigned long long agP[kW];
+    __shared__ float agLB[kW];
     // lattice mode: the step before's unresolved arcs (its recombination losers
     // and its closure's epsilon arcs) get their destination's position among
     // the tokens of frame t (the parity this compaction reads). The wavefront's
@@ -1323,14 +1339,17 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             mpos = pick(w.pos, upar(tab.par, mL))[(size_t)mL * w.num_states + (d & ~kLatUnresolved)];
         }
     }
-    for (uint32_t u = u_beg; u < u_end; ++u) {
-        const int L = find_lane(tab.base, nl, u);
+    for (uint32_t ur = g_beg; ur < g_end; ur += (uint32_t)kW) {
+        const uint32_t u = ur + (uint32_t)wv;
+        const bool has = u < g_end;                       // (wavefront-uniform)
+        const int L = has ? find_lane(tab.base, nl, u) : 0;
         const int p = upar(tab.par, L), np = p ^ 1;
-        const uint32_t nc = tab.n[L];
-        const uint32_t i = (u - tab.base[L]) * kWave + (uint32_t)lane;
+        const uint32_t nc = has ? tab.n[L] : 0u;
+        const uint32_t i = has ? (u - tab.base[L]) * kWave + (uint32_t)lane : 0u;
         const bool valid = i < nc;
         const float cutoff = tab.f1[L];
         const bool next_final = (t + 1 == tab.T[L]);
+        const bool fin = has && tab.ph[L] == kPhFinal;
         LaneCtl &c = w.ctl[L];
         bool keep = false;
         int32_t dst = 0, arc = 0, esrc = -1, abeg = 0, eps_b0 = 0;
@@ -1346,7 +1365,6 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
             adm = __uint_as_float(cl.score) > cutoff;
         }
         const unsigned long long am = __ballot(adm);
-        if (lane == 0 && am) atomicAdd(step_rec(w, L, t) + kRecAdmitted, (uint32_t)__popcll(am));
         // lattice mode: every admitted candidate is a lattice arc {source
         // position, arc, destination, pass 0}, its record written once the
         // destination is known: a winner's position in the new frontier, else
@@ -1365,24 +1383,18 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         }
         const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
         int32_t lat_z = (int32_t)(cds | kLatUnresolved);
-        auto lat_put = [&]() {
-            if (lat_i != 0xFFFFFFFFu) w.lat_arc[(size_t)L * w.lat_cap + lat_i] = make_int4((int)cl.tok, cl.arc, lat_z, 0);
-        };
-        if (tab.ph[L] == kPhFinal) {
-            lat_put();
+        if (fin) {
             if (adm && cand_key(__uint_as_float(cl.score), cl.arc) == c.final_key)
                 final_entry(w, c, L, p, c.final_key, (int32_t)cl.tok);
-            continue;
-        }
-        // with epochs only admitted candidates need the table (stale entries of
-        // earlier rounds always lose); without, every owner clears its entry
-        if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
-            if (recomb_key<HASH>(w, 0, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
-                if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
-                keep = adm;
+        } else if (has) {
+            // with epochs only admitted candidates need the table (stale entries of
+            // earlier rounds always lose); without, every owner clears its entry
+            if (valid && (adm || !w.epochs) && cds < (uint32_t)w.num_states) {
+                if (recomb_key<HASH>(w, 0, L, cds, ep) == table_key(w, __uint_as_float(cl.score), cl.arc, cl.dest, ep)) {
+                    if (!w.epochs) w.best[(size_t)L * (size_t)w.num_states + cds] = 0ull;
+                    keep = adm;
+                }
             }
-        }
-        {
             if (keep) {
                 dst = (int32_t)cds;
                 arc = cl.arc;
@@ -1416,86 +1428,111 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 }
             }
         }
-        // lower bound of the next step's maximum (posted per lane after the
-        // loop, so its log-prob load overlaps the allocation below)
-        if (L != lb_lane) {
-            post_bound(w, lb_lane, lb_np, lb_acc);
-            lb_lane = L;
-            lb_np = np;
-            lb_acc = -__builtin_inff();
-        }
-        lb_acc = fmaxf(lb_acc, lbv);
         const unsigned long long m = __ballot(keep);
-        if (m == 0ull) {
-            lat_put();
-            continue;
-        }
         const uint32_t nkeep = (uint32_t)__popcll(m);
         const uint32_t rank = (uint32_t)__popcll(m & mask_lt());
         uint32_t dsum;
         const uint32_t dpre = wave_excl_sum(keep ? deg : 0u, &dsum);
-        const int leader = __ffsll((long long)m) - 1;
         // on epsilon graphs the closure's first sources: the new tokens with
         // epsilon arcs
         const unsigned long long ml = (w.eps_iterations > 0) ? __ballot(keep && eps_n > 0u) : 0ull;
-        unsigned long long old = 0ull;
-        uint32_t l0 = 0u;
-        if (lane == leader) {
-            old = atomicAdd(&c.cnt[np], (unsigned long long)nkeep | ((unsigned long long)dsum << 32));
-            if (ml) l0 = (uint32_t)atomicAdd(&c.nchanged[1], (unsigned long long)__popcll(ml));
+        // the round's allocation: per lane one 64-bit atomicAdd of positions
+        // (low half) and slot offsets (high half), the wavefronts of the lane
+        // taking consecutive parts in wavefront order
+        // lower bound of the next step's maximum: the wavefront's best, posted
+        // with the round's allocation
+        const float lbw = wave_max(lbv);
+        if (lane == 0) {
+            agLB[wv] = lbw;
+            agL[wv] = has ? L : -1;
+            agA[wv] = (uint32_t)__popcll(am);
+            agN[wv] = nkeep;
+            agD[wv] = dsum;
+            agE[wv] = (uint32_t)__popcll(ml);
         }
-        old = __shfl(old, leader, kWave);
-        if (ml) l0 = __shfl(l0, leader, kWave);
-        const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
-        // exact capacity of this wavefront's tokens and winners-log entries: on
-        // overflow nothing is written and the lane retires (the frontier count
-        // past frontier_cap keeps every later kernel off its tokens)
-        const bool pos_ok = (unsigned long long)p0 + nkeep <= Q;
-        if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena_lim) {
-            if (lane == leader) {
-                atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
-                if (pos_ok) c.log_full = 1u;
-                c.status = kDone;
-                c.phase_final = kPhDead;
+        __syncthreads();
+        if (threadIdx.x < (unsigned)kW) {
+            const int k = (int)threadIdx.x;
+            const int Lk = agL[k];
+            bool first = Lk >= 0;
+            for (int j = 0; j < k; ++j) first = first && agL[j] != Lk;
+            if (first) {
+                uint32_t tA = 0, tN = 0, tD = 0, tE = 0;
+                float tB = -__builtin_inff();
+                for (int j = k; j < kW; ++j)
+                    if (agL[j] == Lk) { tA += agA[j]; tN += agN[j]; tD += agD[j]; tE += agE[j]; tB = fmaxf(tB, agLB[j]); }
+                LaneCtl &ck = w.ctl[Lk];
+                const int npk = tab.par[Lk] ^ 1;
+                unsigned long long old = 0ull;
+                uint32_t e0 = 0u;
+                if (tA) atomicAdd(step_rec(w, Lk, t) + kRecAdmitted, tA);
+                if (tB > -__builtin_inff()) atomicMax(&ck.lbkey[npk], f2ord(tB));
+                if (tN) old = atomicAdd(&ck.cnt[npk], (unsigned long long)tN | ((unsigned long long)tD << 32));
+                if (tE) e0 = (uint32_t)atomicAdd(&ck.nchanged[1], (unsigned long long)tE);
+                for (int j = k; j < kW; ++j)
+                    if (agL[j] == Lk) {
+                        agP[j] = old;
+                        agPE[j] = e0;
+                        old += (unsigned long long)agN[j] | ((unsigned long long)agD[j] << 32);
+                        e0 += agE[j];
+                    }
             }
-            lat_put();
-            continue;
         }
-        if (keep) {
-            const uint32_t pi = p0 + rank;
-            lat_z = (int32_t)pi;
-            const size_t q = (size_t)L * Q + pi;
-            const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
-            w.wlog[e] = make_int2(esrc, arc);
-            pick(w.tok_state, np)[q] = dst;
-            if (w.eps_iterations > 0) pick(w.tok_tag, np)[q] = frame_tag(c, t);   // made by the compaction
-            pick(w.tok_score, np)[q] = end;
-            pick(w.tok_entry, np)[q] = e;
-            pick(w.tok_last, np)[q] = arc;
-            pick(w.tok_off, np)[q] = a0 + dpre;
-            pick(w.tok_abeg, np)[q] = abeg;
-            pick(w.tok_ub, np)[q] = ub;
-            if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
-            if (w.lattice) {
-                // the token's lattice node (its closure may still raise the score)
-                const uint32_t ni = lt.nb[L] + pi;
-                if (ni < w.lat_nodes) {
-                    w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
-                    w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
-                } else {
-                    lat_node_overflow(w, c);
+        __syncthreads();
+        if (m != 0ull) {
+            const unsigned long long old = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(agP[wv] >> 32)) << 32)
+                                         | (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)agP[wv]);
+            const uint32_t l0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)agPE[wv]);
+            const int leader = __ffsll((long long)m) - 1;
+            const uint32_t p0 = (uint32_t)old, a0 = (uint32_t)(old >> 32);
+            // exact capacity of this wavefront's tokens and winners-log entries: on
+            // overflow nothing is written and the lane retires (the frontier count
+            // past frontier_cap keeps every later kernel off its tokens)
+            const bool pos_ok = (unsigned long long)p0 + nkeep <= Q;
+            if (!pos_ok || (unsigned long long)tab.arcs[L] + p0 + nkeep > w.arena_lim) {
+                if (lane == leader) {
+                    atomicOr(&c.overflow, pos_ok ? kOvfArena : kOvfFrontier);
+                    if (pos_ok) c.log_full = 1u;
+                    c.status = kDone;
+                    c.phase_final = kPhDead;
                 }
-            }
-            if ((ml >> lane) & 1ull) {
-                const size_t ci = (size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt());
-                w.changed[1][ci] = make_int4(eps_b0, (int)eps_n, e, (int)__float_as_uint(end));
-                if (w.lattice) w.chg_pos[1][ci] = (int32_t)pi;
+            } else {
+                if (keep) {
+                    const uint32_t pi = p0 + rank;
+                    lat_z = (int32_t)pi;
+                    const size_t q = (size_t)L * Q + pi;
+                    const int32_t e = (int32_t)((uint32_t)L * w.arena + tab.arcs[L] + pi);
+                    w.wlog[e] = make_int2(esrc, arc);
+                    pick(w.tok_state, np)[q] = dst;
+                    if (w.eps_iterations > 0) pick(w.tok_tag, np)[q] = frame_tag(c, t);   // made by the compaction
+                    pick(w.tok_score, np)[q] = end;
+                    pick(w.tok_entry, np)[q] = e;
+                    pick(w.tok_last, np)[q] = arc;
+                    pick(w.tok_off, np)[q] = a0 + dpre;
+                    pick(w.tok_abeg, np)[q] = abeg;
+                    pick(w.tok_ub, np)[q] = ub;
+                    if (w.has_eps || w.lattice) pick(w.pos, np)[(size_t)L * w.num_states + dst] = (int32_t)pi;
+                    if (w.lattice) {
+                        // the token's lattice node (its closure may still raise the score)
+                        const uint32_t ni = lt.nb[L] + pi;
+                        if (ni < w.lat_nodes) {
+                            w.lat_score[(size_t)L * w.lat_nodes + ni] = end;
+                            w.lat_state[(size_t)L * w.lat_nodes + ni] = dst;
+                        } else {
+                            lat_node_overflow(w, c);
+                        }
+                    }
+                    if ((ml >> lane) & 1ull) {
+                        const size_t ci = (size_t)L * w.chg_cap + l0 + (uint32_t)__popcll(ml & mask_lt());
+                        w.changed[1][ci] = make_int4(eps_b0, (int)eps_n, e, (int)__float_as_uint(end));
+                        if (w.lattice) w.chg_pos[1][ci] = (int32_t)pi;
+                    }
+                }
+                write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
             }
         }
-        lat_put();
-        write_strips(pick(w.strip_tok, np) + (size_t)L * w.strip_cap, w.strip_cap, p0, a0, dpre, dsum, m);
+        if (lat_i != 0xFFFFFFFFu) w.lat_arc[(size_t)L * w.lat_cap + lat_i] = make_int4((int)cl.tok, cl.arc, lat_z, 0);
     }
-    post_bound(w, lb_lane, lb_np, lb_acc);
     if (w.lattice) {
         if (mun) w.lat_arc[(size_t)mL * w.lat_cap + lt.a0[mL] + mi].z = mpos;
         // (the wavefront's other units, if any)
