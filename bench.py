@@ -423,14 +423,14 @@ def config_summary(wid, steps, warmup, cpu_seconds, dev):
 
 def run_probes() -> dict:
     """Machine probes (libwfst_probe.so, built with the decoder): the random-line
-    rate, the latency of a dependent load, posted 64-bit atomics and the launch
-    floor on this GPU."""
+    rate, the latency of a dependent load, posted 64-bit atomics, the launch
+    floor, and returning atomics on few hot counters on this GPU."""
     import ctypes
     import torch
     torch.cuda.init()
     lib = ctypes.CDLL(os.path.join(ROOT, "wfst_beam_search_amd", "libwfst_probe.so"))
-    out = (ctypes.c_double * 24)()
-    rc = lib.wfst_probe_run(out, 24)
+    out = (ctypes.c_double * 32)()
+    rc = lib.wfst_probe_run(out, 32)
     if rc != 0:
         raise RuntimeError(f"wfst_probe_run failed ({rc})")
     v = list(out)
@@ -445,6 +445,8 @@ def run_probes() -> dict:
         res["atomic_max_u64"].append({"table_mib": mb, "us_per_launch": round(us, 2),
                                       "atomics_per_s_G": round(gat, 2), "atomics_per_launch": 1024 * 256})
     res["launch_floor_us"] = {"eager": round(v[22], 3), "graph_replay": round(v[23], 3)}
+    res["hot_counter_atomic_us"] = [{"counters": nc, "wavefronts": 4096, "mean": round(v[24 + 2 * j], 3),
+                                     "max": round(v[25 + 2 * j], 3)} for j, nc in enumerate((1, 8, 32, 4096))]
     return res
 
 

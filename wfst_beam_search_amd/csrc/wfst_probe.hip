@@ -6,13 +6,16 @@
 //   - dependent load chains (x = a[x]): the latency of one level;
 //   - posted 64-bit atomicMax on random slots of a small and a large table;
 //   - the launch floor: empty kernels back to back, eager and replayed from a
-//     captured graph.
+//     captured graph;
+//   - hot counters: one returning 64-bit atomicAdd per wavefront on few
+//     addresses (as per-lane counters are), timed inside the kernel.
 // Every index is masked into its array; every kernel is a plain grid with no
 // waits between workgroups.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 
 namespace {
 
@@ -60,6 +63,24 @@ __global__ __launch_bounds__(256) void p_atomic_max(unsigned long long *slots, u
     atomicMax(&slots[mix(gid + seed) & mask], (unsigned long long)gid * 7u + seed);
 }
 
+// one returning u64 atomicAdd per wavefront (lane 0) on counter (wave % nctr),
+// counters 256 bytes apart; each wavefront records the wall-clock ticks its
+// atomic took (out[3 * wave]), its start tick and the value the atomic returned
+__global__ __launch_bounds__(256) void p_hot(unsigned long long *ctr, unsigned long long *out, uint32_t nctr)
+{
+    const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) / 64u;
+    const unsigned long long t0 = wall_clock64();
+    unsigned long long v = 0;
+    if ((threadIdx.x & 63u) == 0u) v = atomicAdd(&ctr[(size_t)(wave % nctr) * 32u], 1ull);
+    v = __shfl(v, 0, 64);
+    const unsigned long long t1 = wall_clock64();
+    if ((threadIdx.x & 63u) == 0u) {
+        out[3 * (size_t)wave] = t1 - t0;
+        out[3 * (size_t)wave + 1] = t0;
+        out[3 * (size_t)wave + 2] = v;
+    }
+}
+
 __global__ __launch_bounds__(64) void p_empty(uint32_t *out)
 {
     if (threadIdx.x == 1000u) out[0] = 1u;
@@ -82,11 +103,13 @@ __global__ __launch_bounds__(64) void p_empty(uint32_t *out)
 //     microseconds per chain level (chain of 4 minus chain of 1, over 3);
 //   posted atomicMax on 8 MiB of slots: us per launch (262144 atomics), G atomics/s;
 //   the same on 512 MiB;
-//   launch floor: us per empty launch eager, us per empty launch in a graph replay.
-// Returns 0 on success, 1 on a HIP error, 2 if n is too small (n >= 24).
+//   launch floor: us per empty launch eager, us per empty launch in a graph replay;
+//   hot counters, 4096 wavefronts on 1, 8, 32 and 4096 counters (4 x 2 values):
+//     mean and largest latency of the wavefronts' returning atomics (us).
+// Returns 0 on success, 1 on a HIP error, 2 if n is too small (n >= 32).
 extern "C" int wfst_probe_run(double *out, int n)
 {
-    if (!out || n < 24) return 2;
+    if (!out || n < 32) return 2;
     const size_t maxb = (size_t)4 << 30;
     uint32_t *a = nullptr, *sink = nullptr;
     unsigned long long *slots = nullptr;
@@ -164,6 +187,36 @@ extern "C" int wfst_probe_run(double *out, int n)
         out[o++] = (double)ms * 1000.0 / nl;
         PCK(hipGraphExecDestroy(ge));
         PCK(hipGraphDestroy(gr));
+    }
+    {
+        // hot counters: 1024 workgroups of 4 wavefronts, one atomic each
+        const uint32_t nw = G * 4u;
+        unsigned long long *ctr = nullptr, *lat = nullptr;
+        PCK(hipMalloc(&ctr, (size_t)4096 * 32 * 8));
+        PCK(hipMalloc(&lat, (size_t)nw * 3 * 8));
+        PCK(hipMemset(ctr, 0, (size_t)4096 * 32 * 8));
+        int khz = 0;
+        PCK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, 0));
+        const double us_per_tick = khz > 0 ? 1000.0 / (double)khz : 0.01;
+        unsigned long long *h = (unsigned long long *)malloc((size_t)nw * 3 * 8);
+        if (!h) return 1;
+        for (uint32_t nc : {1u, 8u, 32u, 4096u}) {
+            for (int r = 0; r < 3; ++r) p_hot<<<G, 256, 0, s>>>(ctr, lat, nc);
+            PCK(hipGetLastError());
+            PCK(hipStreamSynchronize(s));
+            PCK(hipMemcpy(h, lat, (size_t)nw * 3 * 8, hipMemcpyDeviceToHost));
+            double sum = 0.0, mx = 0.0;
+            for (uint32_t wv = 0; wv < nw; ++wv) {
+                const double d = (double)h[3 * (size_t)wv] * us_per_tick;
+                sum += d;
+                if (d > mx) mx = d;
+            }
+            out[o++] = sum / nw;
+            out[o++] = mx;
+        }
+        free(h);
+        PCK(hipFree(lat));
+        PCK(hipFree(ctr));
     }
     PCK(hipEventDestroy(e0));
     PCK(hipEventDestroy(e1));
