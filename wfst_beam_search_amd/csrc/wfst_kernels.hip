@@ -1309,7 +1309,7 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
     g_beg = __builtin_amdgcn_readfirstlane(g_beg);
     g_end = __builtin_amdgcn_readfirstlane(g_end);
     __shared__ int32_t agL[kW];
-    __shared__ uint32_t agA[kW], agN[kW], agD[kW], agE[kW], agPE[kW];
+    __shared__ uint32_t agA[kW], agN[kW], agD[kW], agE[kW], agPE[kW], agPR[kW];
     __shared__ unsigned long long agP[kW];
     __shared__ float agLB[kW];
     // lattice mode: the step before's unresolved arcs (its recombination losers
@@ -1370,17 +1370,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
         // destination is known: a winner's position in the new frontier, else
         // (recombination losers, final arcs) its state marked unresolved
         // (kLatUnresolved), mapped to the position by the next compaction
+        // (their positions are allocated with the round's counters below)
         uint32_t lat_i = 0xFFFFFFFFu;
-        if (w.lattice && am) {
-            uint32_t lb0 = 0u;
-            if (lane == 0) lb0 = atomicAdd(&c.lat_cursor, (uint32_t)__popcll(am));
-            lb0 = __shfl(lb0, 0, kWave);
-            if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
-                if (lane == 0) atomicOr(&c.overflow, kOvfArena);
-            } else if (adm) {
-                lat_i = lb0 + (uint32_t)__popcll(am & mask_lt());
-            }
-        }
         const uint32_t cds = valid ? dest_state(w, cl.dest) : 0u;
         int32_t lat_z = (int32_t)(cds | kLatUnresolved);
         if (fin) {
@@ -1466,6 +1457,8 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                 unsigned long long old = 0ull;
                 uint32_t e0 = 0u;
                 if (tA) atomicAdd(step_rec(w, Lk, t) + kRecAdmitted, tA);
+                uint32_t r0 = 0u;
+                if (w.lattice && tA) r0 = atomicAdd(&ck.lat_cursor, tA);
                 if (tB > -__builtin_inff()) atomicMax(&ck.lbkey[npk], f2ord(tB));
                 if (tN) old = atomicAdd(&ck.cnt[npk], (unsigned long long)tN | ((unsigned long long)tD << 32));
                 if (tE) e0 = (uint32_t)atomicAdd(&ck.nchanged[1], (unsigned long long)tE);
@@ -1473,12 +1466,22 @@ __device__ __forceinline__ void ph_finalize(const Work &w, int t, LaneTab &tab, 
                     if (agL[j] == Lk) {
                         agP[j] = old;
                         agPE[j] = e0;
+                        agPR[j] = r0;
+                        r0 += agA[j];
                         old += (unsigned long long)agN[j] | ((unsigned long long)agD[j] << 32);
                         e0 += agE[j];
                     }
             }
         }
         __syncthreads();
+        if (w.lattice && am) {
+            const uint32_t lb0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)agPR[wv]);
+            if ((unsigned long long)lb0 + (uint32_t)__popcll(am) > w.lat_cap) {
+                if (lane == 0) atomicOr(&c.overflow, kOvfArena);
+            } else if (adm) {
+                lat_i = lb0 + (uint32_t)__popcll(am & mask_lt());
+            }
+        }
         if (m != 0ull) {
             const unsigned long long old = ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(agP[wv] >> 32)) << 32)
                                          | (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)agP[wv]);
