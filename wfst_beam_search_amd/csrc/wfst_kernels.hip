@@ -700,9 +700,20 @@ __device__ __forceinline__ LaneView lane_view(const Work &w, const LaneTab &tab,
 // `cur`, moved forward), then issues every arc load of the unit before using
 // any. Tokens whose bound ub <= skip are not expanded (exact: ub is at least
 // every candidate through the token, so none of its arcs ends above skip).
+// The window of 64 token offsets a wavefront last loaded (lane l: token wb + l),
+// kept across the units of a lane segment: consecutive units continue in token
+// order, so a unit whose slots lie within the window resolves them without a
+// load (at HLG scale a window covers several units' slots).
+struct SlotWin {
+    bool valid;
+    uint32_t wb, o, o_next;
+    int32_t ab;
+    float sc, ub;
+};
+
 template <typename LPT>
 __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint32_t u, uint32_t &cur,
-                                          float skip, UnitData &ud)
+                                          float skip, UnitData &ud, SlotWin &sw)
 {
     const int lane = wlane();
     const uint32_t n = v.n;
@@ -718,15 +729,23 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
         resolved[r] = !valid[r];
         tok[r] = cur; toff[r] = 0; ab[r] = 0; sc[r] = 0.0f; ub[r] = 0.0f;
     }
-    uint32_t wb = cur;
+    // (a carried window starts at or before cur, the token of the last slot before this unit)
+    bool have = sw.valid;
+    uint32_t wb = have ? sw.wb : cur;
+    uint32_t o = sw.o, o_next = sw.o_next;
+    int32_t ab_l = sw.ab;
+    float sc_l = sw.sc, ub_l = sw.ub;
     for (;;) {
-        const uint32_t idx = wb + (uint32_t)lane;
-        const bool in = idx < n;
-        const uint32_t o = in ? v.off[idx] : 0xFFFFFFFFu;
-        const int32_t ab_l = in ? v.abeg[idx] : 0;
-        const float sc_l = in ? v.score[idx] : 0.0f;
-        const float ub_l = in ? v.ubv[idx] : 0.0f;
-        const uint32_t o_next = (wb + kWave < n) ? v.off[wb + kWave] : 0xFFFFFFFFu;
+        if (!have) {
+            const uint32_t idx = wb + (uint32_t)lane;
+            const bool in = idx < n;
+            o = in ? v.off[idx] : 0xFFFFFFFFu;
+            ab_l = in ? v.abeg[idx] : 0;
+            sc_l = in ? v.score[idx] : 0.0f;
+            ub_l = in ? v.ubv[idx] : 0.0f;
+            o_next = (wb + kWave < n) ? v.off[wb + kWave] : 0xFFFFFFFFu;
+        }
+        have = false;
         bool pending = false;
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
@@ -749,6 +768,8 @@ __device__ __forceinline__ void load_unit(const Work &w, const LaneView &v, uint
         if (__ballot(pending) == 0ull) break;
         wb += kWave;
     }
+    sw.valid = true;
+    sw.wb = wb; sw.o = o; sw.o_next = o_next; sw.ab = ab_l; sw.sc = sc_l; sw.ub = ub_l;
     cur = __shfl(tok[kR - 1], kWave - 1, kWave);
 
     const LPT *row = (const LPT *)v.row;
@@ -937,9 +958,12 @@ __device__ __forceinline__ void walk_range(const Work &w, const LaneTab &tab, in
         if (cur >= v.n) cur = 0;
         float run = ord2f(tab.fb[L]);
         const float b = tab.f1[L];
+        SlotWin sw;
+        sw.valid = false;
+        sw.wb = 0u; sw.o = 0u; sw.o_next = 0u; sw.ab = 0; sw.sc = 0.0f; sw.ub = 0.0f;
         for (; s < seg_end; ++s) {
             UnitData ud;
-            load_unit<LPT>(w, v, s - tab.base[L], cur, run - b, ud);
+            load_unit<LPT>(w, v, s - tab.base[L], cur, run - b, ud, sw);
             run = fmaxf(run, unit_max(ud));
             admit_unit<HASH>(w, L, v.ph, run - b, ep, ud, &c.nclaims[p], cbuf, cb_n);
         }
