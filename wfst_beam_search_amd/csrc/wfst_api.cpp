@@ -699,15 +699,18 @@ static void lay_out(Work &w, Extra &x, const wfst_decoder_config &c, const Sizes
 }
 
 // Frame-loop grid: every workgroup first builds the lane table, so 4 workgroups
-// per CU (16 wavefronts) is measured best on MI355X.
-static int default_grid(const wfst_decoder_config &c, int device)
+// per CU (16 wavefronts) is measured best on MI355X for most kernels; the slot
+// walk (per = 5) fits five per CU (its register budget is held to five
+// wavefronts per SIMD, its candidate buffers to 24 KiB per workgroup) and
+// gains from the fifth on the HLG-scale batch.
+static int default_grid(const wfst_decoder_config &c, int device, int per = 4)
 {
     int ncu = 256;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
         ncu = prop.multiProcessorCount;
     const long long want = ((long long)c.max_lanes * c.max_active + 127) / 128;
-    return c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), 4LL * ncu);
+    return c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), (long long)per * ncu);
 }
 
 extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp, wfst_decoder_t *out)
@@ -731,6 +734,7 @@ extern "C" int wfst_decoder_create(wfst_graph_t g, const wfst_decoder_config *cp
     d->grid = default_grid(c, g->device);
     Work &w = d->w;
     w = w0;
+    w.walk_grid = default_grid(c, g->device, 5);
 
     const size_t L = (size_t)c.max_lanes, S = (size_t)g->num_states;
     const uint64_t arena = z.arena;
@@ -1180,6 +1184,7 @@ extern "C" int wfst_decode_noalloc(wfst_graph_t g, const wfst_decoder_config *cp
     int32_t lens[kMaxLanes] = {0};
     for (int32_t b = 0; b < B; ++b) lens[b] = lengths_host[b];
     const int grid = default_grid(c, g->device);
+    w.walk_grid = default_grid(c, g->device, 5);
     const int steps = maxlen + 1;
     // the scratch holds whatever the last call left: the control blocks and the
     // recombination table start at zero, the position maps at -1

@@ -256,6 +256,8 @@ struct Work {
     uint32_t *gc_wpre;        // [L][arena / 32 + 1] live entries before each 32-entry word
     uint32_t *gc_child;       // [L][arena] live children by compacted position
     int2 *gc_buf;             // [L][arena] compacted entries
+    // launch shape (host side): workgroups of the slot walk (0: the frame-loop grid)
+    int32_t walk_grid;
 };
 
 // Fields of a kept lattice record (int32 each).

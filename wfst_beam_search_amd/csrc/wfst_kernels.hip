@@ -359,7 +359,7 @@ __device__ __forceinline__ void write_strips(uint32_t *strip_tok, uint32_t strip
 // Per-wavefront LDS buffer of the listed candidates of the slot pass and the
 // closure's expand passes (a unit lists at most kUnit of them; 8 KB per
 // wavefront, so four units' worth between the flushes' list atomics).
-constexpr uint32_t kClaimBuf = 512;
+constexpr uint32_t kClaimBuf = 384;
 
 struct ClaimBuf {
     int32_t dest[kClaimBuf];
@@ -1149,8 +1149,9 @@ __device__ __forceinline__ void step_open(const Work &w, int t, LaneTab &tab)
 }
 
 // The slot pass of step t: exact maximum and superset admission in one walk.
+// (five workgroups per CU: the register budget is held to five wavefronts per SIMD)
 template <typename LPT, bool HASH>
-__global__ __launch_bounds__(kBlock) void k_max(const Work *__restrict__ wp, int t)
+__global__ __launch_bounds__(kBlock, 5) void k_max(const Work *__restrict__ wp, int t)
 {
     const Work &w = *wp;
     __shared__ LaneTab tab;
@@ -3635,15 +3636,17 @@ hipError_t launch_kernel(int id, const Work &w, const Work *dw, int t, int k, in
         if (f16) go(k_lpmax<__half>, G, B, s, e0, e1, dw);
         else go(k_lpmax<float>, G, B, s, e0, e1, dw);
         break;
-    case kKMax:
+    case kKMax: {
+        const dim3 GW(w.walk_grid > 0 ? w.walk_grid : grid);
         if (hash) {
-            if (f16) go(k_max<__half, true>, G, B, s, e0, e1, dw, t);
-            else go(k_max<float, true>, G, B, s, e0, e1, dw, t);
+            if (f16) go(k_max<__half, true>, GW, B, s, e0, e1, dw, t);
+            else go(k_max<float, true>, GW, B, s, e0, e1, dw, t);
         } else {
-            if (f16) go(k_max<__half, false>, G, B, s, e0, e1, dw, t);
-            else go(k_max<float, false>, G, B, s, e0, e1, dw, t);
+            if (f16) go(k_max<__half, false>, GW, B, s, e0, e1, dw, t);
+            else go(k_max<float, false>, GW, B, s, e0, e1, dw, t);
         }
         break;
+    }
     case kKFinalize:
         if (hash) go(k_finalize<true>, G, B, s, e0, e1, dw, t);
         else go(k_finalize<false>, G, B, s, e0, e1, dw, t);
