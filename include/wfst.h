@@ -112,7 +112,8 @@ typedef struct wfst_graph_desc {
  *  arena_entries   winners-log entries per lane per decode
  *                  (0: 4 * max_active * (max_frames + 2) * (1 + eps passes),
  *                  at least 2^20); max_lanes * arena_entries < 2^31.
- *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive).
+ *  grid_blocks     workgroups per launch of the frame-loop kernels (0: derive: up to
+ *                  4 per CU, the slot walk up to 5 per CU, fewer for small batches).
  *  slot_cap        candidate arcs (slots) per lane per step (0: 512 * max_active,
  *                  at least 2^16); at most 2^31.
  *  plain_keys      0: the recombination table's keys carry the round's epoch
