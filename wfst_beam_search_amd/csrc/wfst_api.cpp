@@ -709,7 +709,8 @@ static int default_grid(const wfst_decoder_config &c, int device, int per = 4)
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
         ncu = prop.multiProcessorCount;
-    const long long want = ((long long)c.max_lanes * c.max_active + 127) / 128;
+    // (a multiple of 8: the kernels deal workgroups to the 8 XCDs in equal runs)
+    const long long want = (((long long)c.max_lanes * c.max_active + 127) / 128 + 7) / 8 * 8;
     return c.grid_blocks ? c.grid_blocks : (int)std::min<long long>(std::max<long long>(want, 8), (long long)per * ncu);
 }
 
